@@ -1,0 +1,321 @@
+"""fp64 reference implementation of the S4 DPLR convolution-mode forward pass.
+
+TEST INFRASTRUCTURE ONLY: this module is the oracle that the GPU library is
+checked against.  It is imported by the tests, by the smoke check and by the
+CPU-baseline leg of the benchmark, and by nothing else.  It shares no code,
+tables or constants with the HIP path; both sides only share the seeded input
+generator in ``synth/``.
+
+Everything here is written for a reader to check against the pages by eye:
+plain NumPy in float64/complex128, no blocking or fusion, library routines
+(matrix products, solves, eigh, FFT) only as whole steps.
+
+Pages cited (by title and section):
+  [scratch]   "The S4 kernel, from scratch" -- section 1 (continuous SSM),
+              2 (HiPPO initialization -> DPLR form), 3 (Discretization),
+              4 (The convolutional kernel via the generating function, with
+              its "Aliasing" paragraph), 5 (Two views, kept in sync),
+              6 (Trainable layer).
+  [wiki]      "S4" wiki page -- "Structured Transition Matrix", "S4D".
+  [glossary]  "Structured state-space sequence model and S4" -- "One linear
+              layer, two computational views", "Follow one input through
+              memory" (worked-example table).
+  [kronos]    "Structured State-Space Models (S4)" -- "A linear system as a
+              layer", "Recurrence and convolution duality".
+
+Readings of points the pages leave open (numbered as in the design notes):
+  R1  the HiPPO-LegS entries are not printed; the standard LegS matrix is used.
+  R2  the rank-1 NPLR factor is P_n = sqrt(n + 1/2).
+  R3  eigh is taken of -i*T (T the skew part); eigenvalues ascending; each
+      eigenvector rephased so that (V^* P)_n is real and >= 0.
+  R5  the kernel is the real part of the inverse FFT (C is complex).
+  R6  C-bar = C: the length-L inverse FFT yields the *aliased* kernel.
+  R7  bilinear B-bar = (I - dt/2 A)^{-1} dt B.
+  R8  z_l = exp(-2 pi i l / L); inverse FFT scaled by 1/L (NumPy convention).
+  R9  at z = -1 (l = L/2) the generating function takes its limit
+      (dt/2) * sum_n C_n B_n.
+  R10 y_t = sum_{j<=t} K_j u_{t-j} + D u_t (no one-step delay).
+  R12 the causal convolution is zero-padded to exactly 2L.
+  R13 ZOH uses the expm1 form (limit dt*b at a = 0); the pages' Taylor
+      threshold is not reproduced (parity unpinned for that threshold, which
+      no hot-path result depends on).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "hippo_legs", "nplr_legs", "dplr_legs",
+    "dense_state_matrix", "discretize_bilinear", "discretize_zoh_scalar",
+    "kernel_truncated", "kernel_aliased_dense", "generating_function",
+    "kernel_cauchy", "conv_direct", "conv_direct_at", "conv_fft",
+    "recurrence", "forward",
+]
+
+
+# ---------------------------------------------------------------------------
+# Initialization: HiPPO-LegS -> NPLR -> DPLR   ([scratch] section 2;
+# [wiki] "Structured Transition Matrix")
+# ---------------------------------------------------------------------------
+
+def hippo_legs(N: int):
+    """HiPPO-LegS state matrix A (N x N, real) and input vector B (N).
+
+    [scratch] section 2 names the matrix but does not print it (reading R1):
+    A[n,k] = -sqrt((2n+1)(2k+1)) below the diagonal, -(n+1) on it, 0 above;
+    B[n] = sqrt(2n+1).
+    """
+    n = np.arange(N, dtype=np.float64)
+    A = np.zeros((N, N), dtype=np.float64)
+    for i in range(N):
+        for k in range(N):
+            if i > k:
+                A[i, k] = -np.sqrt((2 * n[i] + 1) * (2 * n[k] + 1))
+            elif i == k:
+                A[i, k] = -(n[i] + 1)
+    B = np.sqrt(2 * n + 1)
+    return A, B
+
+
+def nplr_legs(N: int):
+    """Normal-plus-low-rank split A = A_normal - P P^T ([scratch] section 2).
+
+    Returns (A, P, B, S) with S = A + P P^T the normal part (reading R2:
+    P_n = sqrt(n + 1/2), which makes S = -I/2 + skew-symmetric).
+    """
+    A, B = hippo_legs(N)
+    P = np.sqrt(np.arange(N, dtype=np.float64) + 0.5)
+    S = A + np.outer(P, P)
+    return A, P, B, S
+
+
+def dplr_legs(N: int):
+    """DPLR parameters (Lambda, P~, B~, V) with A = V (Lambda - P~ P~^*) V^*.
+
+    [scratch] section 2: diagonalize the normal part with a Hermitian eigh and
+    rotate P and B into the eigenbasis; Q = P.  Reading R3 fixes the basis:
+    eigh of -i*T, ascending eigenvalues, eigenvectors rephased so that every
+    P~_n is real and non-negative.
+    """
+    A, P, B, S = nplr_legs(N)
+    T = S + 0.5 * np.eye(N)                 # skew-symmetric part of S
+    mu, V = np.linalg.eigh(-1j * T)         # -iT is Hermitian; mu ascending
+    Pt = V.conj().T @ P
+    phase = np.exp(1j * np.angle(Pt))
+    phase[np.abs(Pt) == 0] = 1.0
+    V = V * phase[None, :]                  # column n times e^{i arg P~_n}
+    lam = -0.5 + 1j * mu                    # eigenvalues of S = -I/2 + T
+    Pt = V.conj().T @ P
+    Bt = V.conj().T @ B
+    return lam, Pt, Bt, V
+
+
+# ---------------------------------------------------------------------------
+# Dense system and discretization   ([scratch] sections 1 and 3)
+# ---------------------------------------------------------------------------
+
+def dense_state_matrix(lam, P, Q):
+    """A = diag(Lambda) - P Q^*  ([scratch] section 2; [wiki] eq. A = Lambda - PQ^*)."""
+    lam = np.asarray(lam, dtype=np.complex128)
+    return np.diag(lam) - np.outer(np.asarray(P, np.complex128),
+                                   np.conj(np.asarray(Q, np.complex128)))
+
+
+def discretize_bilinear(A, B, dt):
+    """Bilinear (Tustin) discretization ([scratch] section 3; reading R7).
+
+    A-bar = (I - dt/2 A)^{-1} (I + dt/2 A),  B-bar = (I - dt/2 A)^{-1} dt B.
+    """
+    A = np.asarray(A, dtype=np.complex128)
+    I = np.eye(A.shape[0], dtype=np.complex128)
+    M = I - (dt / 2.0) * A
+    Abar = np.linalg.solve(M, I + (dt / 2.0) * A)
+    Bbar = np.linalg.solve(M, dt * np.asarray(B, dtype=np.complex128))
+    return Abar, Bbar
+
+
+def discretize_zoh_scalar(a, b, dt):
+    """Zero-order hold for a scalar system: A-bar = exp(dt a),
+    B-bar = (exp(dt a) - 1)/a * b  ([scratch] section 3; [glossary] "Follow one
+    input through memory").  Reading R13: expm1 form, limit dt*b at a = 0."""
+    if a == 0:
+        return 1.0, dt * b
+    return np.exp(dt * a), np.expm1(dt * a) / a * b
+
+
+# ---------------------------------------------------------------------------
+# Convolution kernel: plain definition   ([scratch] section 4)
+# ---------------------------------------------------------------------------
+
+def kernel_truncated(Abar, Bbar, C, L):
+    """K_k = Re(C A-bar^k B-bar), k < L: the first L Markov parameters
+    ([scratch] section 4 kernel definition; [glossary] k_j = C A-bar^j B-bar).
+    Computed by repeated multiplication, one power at a time."""
+    C = np.asarray(C, dtype=np.complex128)
+    x = np.asarray(Bbar, dtype=np.complex128).copy()
+    K = np.empty(L, dtype=np.float64)
+    for k in range(L):
+        K[k] = (C @ x).real
+        x = Abar @ x
+    return K
+
+
+def kernel_aliased_dense(Abar, Bbar, C, L):
+    """The aliased kernel sum_j K_{k+jL} = Re(C A-bar^k (I - A-bar^L)^{-1} B-bar).
+
+    [scratch] section 4, "Aliasing": the length-L inverse FFT of the generating
+    function returns the kernel summed over all periods.  The geometric series
+    over periods is summed in closed form with one linear solve (readings R5,
+    R6), then the powers are taken one at a time as in ``kernel_truncated``.
+    """
+    Abar = np.asarray(Abar, dtype=np.complex128)
+    N = Abar.shape[0]
+    AL = np.linalg.matrix_power(Abar, L)
+    x0 = np.linalg.solve(np.eye(N) - AL, np.asarray(Bbar, dtype=np.complex128))
+    return kernel_truncated(Abar, x0, C, L)
+
+
+# ---------------------------------------------------------------------------
+# Convolution kernel: the pages' method   ([scratch] section 4)
+# ---------------------------------------------------------------------------
+
+def generating_function(lam, P, Q, B, C, dt, L):
+    """K-hat at the L roots of unity by four Cauchy sums and a rank-1
+    Woodbury correction ([scratch] section 4 equations; [wiki] "Structured
+    Transition Matrix").
+
+    z_l = exp(-2 pi i l/L) (reading R8); g = (2/dt)(1-z)/(1+z);
+    k_ab = sum_n w_n / (g - Lambda_n) with weights C*B, C*P, conj(Q)*B,
+    conj(Q)*P; K-hat = 2/(1+z) * (k00 - k01 k10 / (1 + k11)).
+    At l = L/2 (z = -1) the limit (dt/2) sum_n C_n B_n is used (reading R9).
+    """
+    lam = np.asarray(lam, np.complex128)
+    P = np.asarray(P, np.complex128)
+    Q = np.asarray(Q, np.complex128)
+    B = np.asarray(B, np.complex128)
+    C = np.asarray(C, np.complex128)
+    ell = np.arange(L)
+    Khat = np.empty(L, dtype=np.complex128)
+    regular = np.ones(L, dtype=bool)
+    if L % 2 == 0:
+        regular[L // 2] = False
+    z = np.exp(-2j * np.pi * ell[regular] / L)
+    g = (2.0 / dt) * (1.0 - z) / (1.0 + z)
+    r = 1.0 / (g[:, None] - lam[None, :])          # Cauchy matrix [l, n]
+    k00 = r @ (C * B)
+    k01 = r @ (C * P)
+    k10 = r @ (np.conj(Q) * B)
+    k11 = r @ (np.conj(Q) * P)
+    Khat[regular] = (2.0 / (1.0 + z)) * (k00 - k01 * k10 / (1.0 + k11))
+    if L % 2 == 0:
+        Khat[L // 2] = (dt / 2.0) * np.sum(C * B)
+    return Khat
+
+
+def kernel_cauchy(lam, P, Q, B, C, dt, L):
+    """Time-domain kernel K = Re(ifft(K-hat)) ([scratch] section 4: "an
+    inverse FFT returns the time-domain kernel"; readings R5, R8)."""
+    return np.fft.ifft(generating_function(lam, P, Q, B, C, dt, L)).real
+
+
+# ---------------------------------------------------------------------------
+# The two views   ([scratch] section 5; [glossary] "One linear layer, two
+# computational views"; [kronos] "Recurrence and convolution duality")
+# ---------------------------------------------------------------------------
+
+def conv_direct(u, K, D):
+    """y_t = sum_{j=0}^{t} K_j u_{t-j} + D u_t, summed directly (O(L^2)).
+
+    [scratch] section 1 (feed-through D) and section 4 (y = K * u); reading R10.
+    """
+    u = np.asarray(u, np.float64)
+    K = np.asarray(K, np.float64)
+    L = u.shape[0]
+    y = np.empty(L, dtype=np.float64)
+    for t in range(L):
+        y[t] = np.dot(K[: t + 1], u[t::-1]) + D * u[t]
+    return y
+
+
+def conv_direct_at(u, K, D, t):
+    """One output sample y_t of ``conv_direct``."""
+    u = np.asarray(u, np.float64)
+    K = np.asarray(K, np.float64)
+    return float(np.dot(K[: t + 1], u[t::-1]) + D * u[t])
+
+
+def conv_fft(u, K, D):
+    """Causal convolution by an FFT zero-padded to 2L ([scratch] section 5,
+    "zero-padded to avoid circular wrap-around"; reading R12), plus D u.
+
+    ``u`` may be [..., L]; ``K`` broadcasts against it; ``D`` likewise
+    (shape [..., 1] or scalar).
+    """
+    u = np.asarray(u, np.float64)
+    K = np.asarray(K, np.float64)
+    L = u.shape[-1]
+    n = 2 * L
+    y = np.fft.irfft(np.fft.rfft(u, n) * np.fft.rfft(K, n), n)[..., :L]
+    return y + np.asarray(D, np.float64) * u
+
+
+def recurrence(Abar, Bbar, C, D, u):
+    """Recurrent view x_t = A-bar x_{t-1} + B-bar u_t, y_t = Re(C x_t) + D u_t,
+    with x_{-1} = 0 ([scratch] section 5; [glossary] h_t = A-bar h_{t-1} + B-bar u_t)."""
+    Abar = np.asarray(Abar, np.complex128)
+    Bbar = np.asarray(Bbar, np.complex128)
+    C = np.asarray(C, np.complex128)
+    x = np.zeros(Abar.shape[0], dtype=np.complex128)
+    y = np.empty(len(u), dtype=np.float64)
+    for t, ut in enumerate(np.asarray(u, np.float64)):
+        x = Abar @ x + Bbar * ut
+        y[t] = (C @ x).real + D * ut
+    return y
+
+
+# ---------------------------------------------------------------------------
+# Whole forward pass over channels and batch
+# ---------------------------------------------------------------------------
+
+def _as_complex(a):
+    """(..., 2) float -> complex128 (the interleaved layout of [scratch]
+    section 6: complex parameters stored as real (..., 2) tensors)."""
+    a = np.asarray(a, dtype=np.float64)
+    return a[..., 0] + 1j * a[..., 1]
+
+
+def forward(lam, P, Q, B, C, dt, D, u, method="cauchy", diagonal=False):
+    """K [H, L] and y [batch, H, L] for H independent channels
+    ([scratch] section 1: one SSM per feature channel).
+
+    Complex inputs are (H, N, 2) float arrays; dt, D are (H,); u is
+    (batch, H, L).  ``method`` selects the kernel: "cauchy" (the pages'
+    generating-function method) or "dense" (the aliased plain definition).
+    ``diagonal`` drops the low-rank term (S4D, [wiki] "S4D": P = Q = 0).
+    """
+    lam_c = _as_complex(lam)
+    H, N = lam_c.shape
+    u = np.asarray(u, np.float64)
+    L = u.shape[-1]
+    if diagonal:
+        P_c = np.zeros((H, N), np.complex128)
+        Q_c = P_c
+    else:
+        P_c = _as_complex(P)
+        Q_c = P_c if Q is None else _as_complex(Q)
+    B_c = _as_complex(B)
+    C_c = _as_complex(C)
+    dt = np.asarray(dt, np.float64)
+    D = np.zeros(H) if D is None else np.asarray(D, np.float64)
+    K = np.empty((H, L), dtype=np.float64)
+    for h in range(H):
+        if method == "cauchy":
+            K[h] = kernel_cauchy(lam_c[h], P_c[h], Q_c[h], B_c[h], C_c[h], dt[h], L)
+        elif method == "dense":
+            A = dense_state_matrix(lam_c[h], P_c[h], Q_c[h])
+            Abar, Bbar = discretize_bilinear(A, B_c[h], dt[h])
+            K[h] = kernel_aliased_dense(Abar, Bbar, C_c[h], L)
+        else:
+            raise ValueError(method)
+    y = conv_fft(u, K[None, :, :], D[None, :, None])
+    return K, y

@@ -1,0 +1,344 @@
+"""Pins for the fp64 oracle: values and identities fixed by the pages and by
+mathematics, chosen so that a dropped term, a wrong sign or index, or a
+transposed operand anywhere in ``oracle/`` fails at least one of them.
+
+Pages: "The S4 kernel, from scratch" ([scratch]); "S4" wiki ([wiki]);
+"Structured state-space sequence model and S4" ([glossary]).
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle as o
+from synth import load_dplr_table, make_generic_inputs, make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = line.split()
+            vals[k] = float(v)
+    return vals
+
+
+def _cn(rng, *shape):
+    return rng.normal(size=shape) + 1j * rng.normal(size=shape)
+
+
+# --- P1: the worked example of [glossary] "Follow one input through memory" --
+
+def test_worked_example_zoh_values():
+    g = _golden("worked_example_zoh.txt")
+    Abar, Bbar = o.discretize_zoh_scalar(g["a"], g["b"], g["dt"])
+    assert abs(Abar - g["Abar"]) < 1e-10
+    assert abs(Bbar - g["Bbar"]) < 1e-10
+
+
+def test_worked_example_recurrence_and_convolution():
+    g = _golden("worked_example_zoh.txt")
+    Abar, Bbar = o.discretize_zoh_scalar(g["a"], g["b"], g["dt"])
+    A1, B1, C1 = np.array([[Abar]]), np.array([Bbar]), np.array([g["c"]])
+    u = np.array([1.0, 0.0])
+    y_rec = o.recurrence(A1, B1, C1, 0.0, u)
+    assert abs(y_rec[0] - g["h1"]) < 1e-10 and abs(y_rec[1] - g["h2"]) < 1e-10
+    K = o.kernel_truncated(A1, B1, C1, 2)
+    assert abs(K[0] - g["k0"]) < 1e-10 and abs(K[1] - g["k1"]) < 1e-10
+    y_conv = o.conv_direct(u, K, 0.0)
+    np.testing.assert_allclose(y_conv, [g["h1"], g["h2"]], atol=1e-10)
+    np.testing.assert_allclose(o.conv_fft(u, K, 0.0), [g["h1"], g["h2"]], atol=1e-10)
+
+
+def test_zoh_limit_at_zero_pole():
+    # a -> 0: exp(dt a) -> 1 and (exp(dt a) - 1)/a * b -> dt b.
+    Abar, Bbar = o.discretize_zoh_scalar(0.0, 3.0, 0.25)
+    assert Abar == 1.0 and Bbar == 0.75
+    # near a = 0 the series b (dt + a dt^2 / 2 + ...) holds
+    A2, B2 = o.discretize_zoh_scalar(-1e-9, 3.0, 0.25)
+    assert abs(B2 - 3.0 * (0.25 - 1e-9 * 0.25 ** 2 / 2)) < 1e-15
+
+
+# --- P2: scalar bilinear closed form ---------------------------------------
+
+@pytest.mark.parametrize("L", [2, 4, 16, 256])
+def test_scalar_bilinear_closed_form(L):
+    # Lambda = -1, B = C = 1, dt = 1, no low-rank term:
+    # A-bar = 1/3, B-bar = 2/3, K-hat(z) = 2/(3 - z), K_k = (2/3) 3^-k / (1 - 3^-L).
+    Abar, Bbar = o.discretize_bilinear(np.array([[-1.0]]), np.array([1.0]), 1.0)
+    assert abs(Abar[0, 0] - 1.0 / 3.0) < 1e-15 and abs(Bbar[0] - 2.0 / 3.0) < 1e-15
+    lam, z0, one = np.array([-1.0 + 0j]), np.array([0j]), np.array([1.0 + 0j])
+    k = np.arange(L)
+    ref = (2.0 / 3.0) * 3.0 ** (-k) / (1.0 - 3.0 ** (-L))
+    Kh = o.generating_function(lam, z0, z0, one, one, 1.0, L)
+    z = np.exp(-2j * np.pi * k / L)
+    np.testing.assert_allclose(Kh, 2.0 / (3.0 - z), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(o.kernel_cauchy(lam, z0, z0, one, one, 1.0, L), ref, rtol=1e-12, atol=1e-16)
+    np.testing.assert_allclose(o.kernel_aliased_dense(Abar, Bbar, one, L), ref, rtol=1e-12, atol=1e-16)
+    np.testing.assert_allclose(o.kernel_truncated(Abar, Bbar, one, L), (2.0 / 3.0) * 3.0 ** (-k), rtol=1e-12, atol=1e-16)
+
+
+# --- P3: rank-1 Woodbury with N = 1 equals a shifted diagonal pole ----------
+
+def test_scalar_woodbury_equals_shifted_pole():
+    rng = np.random.default_rng(1)
+    for _ in range(5):
+        lam = np.array([-rng.uniform(0.1, 2.0) + 1j * rng.uniform(-5, 5)])
+        p, b, c = _cn(rng, 1), _cn(rng, 1), _cn(rng, 1)
+        dt, L = rng.uniform(0.01, 0.5), 64
+        K_dplr = o.kernel_cauchy(lam, p, p, b, c, dt, L)
+        a = lam - np.abs(p) ** 2
+        K_diag = o.kernel_cauchy(a, 0 * p, 0 * p, b, c, dt, L)
+        np.testing.assert_allclose(K_dplr, K_diag, rtol=1e-11, atol=1e-13)
+        # closed form of the scalar bilinear system, summed over all periods
+        Ab = (1 + dt * a[0] / 2) / (1 - dt * a[0] / 2)
+        Bb = dt * b[0] / (1 - dt * a[0] / 2)
+        k = np.arange(L)
+        ref = (c[0] * Bb * Ab ** k / (1 - Ab ** L)).real
+        np.testing.assert_allclose(K_dplr, ref, rtol=1e-10, atol=1e-12)
+
+
+# --- Woodbury/Cauchy sums against a direct linear solve of the resolvent ----
+
+def test_generating_function_matches_resolvent_solve():
+    rng = np.random.default_rng(2)
+    N, L, dt = 6, 32, 0.07
+    lam = -rng.uniform(0.1, 1.0, N) + 1j * rng.uniform(-10, 10, N)
+    P, Q, B, C = _cn(rng, N), 0.5 * _cn(rng, N), _cn(rng, N), _cn(rng, N)
+    Kh = o.generating_function(lam, P, Q, B, C, dt, L)
+    A = np.diag(lam) - np.outer(P, Q.conj())      # A = Lambda - P Q^*
+    for l in range(L):
+        if l == L // 2:
+            continue
+        z = np.exp(-2j * np.pi * l / L)
+        g = (2 / dt) * (1 - z) / (1 + z)
+        ref = (2 / (1 + z)) * (C @ np.linalg.solve(g * np.eye(N) - A, B))
+        assert abs(Kh[l] - ref) <= 1e-11 * max(1.0, abs(ref))
+
+
+def test_generating_function_is_power_series_of_markov_parameters():
+    # K-hat(z) = sum_k (C A-bar^k B-bar) z^k for the bilinear system, summed
+    # until the terms have decayed (Delta large enough for fast decay).
+    rng = np.random.default_rng(3)
+    N, L, dt = 5, 16, 0.5
+    lam = -rng.uniform(0.5, 1.5, N) + 1j * rng.uniform(-3, 3, N)
+    P, B, C = 0.3 * _cn(rng, N), _cn(rng, N), _cn(rng, N)
+    Kh = o.generating_function(lam, P, P, B, C, dt, L)
+    Abar, Bbar = o.discretize_bilinear(o.dense_state_matrix(lam, P, P), B, dt)
+    z = np.exp(-2j * np.pi * np.arange(L) / L)
+    acc = np.zeros(L, complex)
+    x = Bbar.copy()
+    zk = np.ones(L, complex)
+    for _ in range(4000):
+        acc += (C @ x) * zk
+        x = Abar @ x
+        zk = zk * z
+    assert np.abs(C @ x) < 1e-14
+    np.testing.assert_allclose(Kh, acc, rtol=1e-10, atol=1e-12)
+
+
+# --- P4: DC and Nyquist closed forms ---------------------------------------
+
+@pytest.mark.parametrize("L", [8, 256, 1024])
+def test_dc_and_nyquist_sums(L):
+    lam, P, B = load_dplr_table(16)
+    rng = np.random.default_rng(4)
+    C = _cn(rng, 16)
+    dt = 0.03
+    K = o.kernel_cauchy(lam, P, P, B, C, dt, L)
+    A = o.dense_state_matrix(lam, P, P)
+    dc = (-C @ np.linalg.solve(A, B)).real           # K-hat at z = 1
+    nyq = (dt / 2 * np.sum(C * B)).real                # K-hat at z = -1
+    s = np.abs(K).sum()
+    assert abs(K.sum() - dc) <= 1e-12 * s
+    assert abs((K * (-1.0) ** np.arange(L)).sum() - nyq) <= 1e-12 * s
+
+
+# --- P5 / P6: HiPPO-LegS -> NPLR -> DPLR invariants --------------------------
+
+@pytest.mark.parametrize("N", [4, 16, 64])
+def test_hippo_nplr_dplr_invariants(N):
+    A, P, B, S = o.nplr_legs(N)
+    # the normal part is normal: S S^T = S^T S, with diagonal -1/2 and a skew rest
+    nS = np.linalg.norm(S)
+    assert np.linalg.norm(S @ S.T - S.T @ S) <= 1e-12 * nS ** 2
+    np.testing.assert_allclose(np.diag(S), -0.5, atol=1e-14)
+    T = S + 0.5 * np.eye(N)
+    assert np.abs(T + T.T).max() <= 1e-13
+    lam, Pt, Bt, V = o.dplr_legs(N)
+    assert np.linalg.norm(V.conj().T @ V - np.eye(N)) <= 1e-12
+    Ad = o.dense_state_matrix(lam, Pt, Pt)
+    assert np.linalg.norm(V @ Ad @ V.conj().T - A) <= 1e-13 * np.linalg.norm(A)
+    np.testing.assert_allclose(lam.real, -0.5, atol=1e-13)
+    assert np.all(np.diff(lam.imag) >= 0)
+    assert np.abs(Pt.imag).max() <= 1e-12 and Pt.real.min() >= 0
+    # B = sqrt(2) P holds for LegS before and after the change of basis
+    np.testing.assert_allclose(B, np.sqrt(2) * P, rtol=1e-15)
+    np.testing.assert_allclose(Bt, np.sqrt(2) * Pt, atol=1e-12 * np.abs(Bt).max())
+
+
+def test_stored_tables_match_oracle():
+    for N in (16, 64):
+        lam, P, B = load_dplr_table(N)
+        lam2, P2, B2, _ = o.dplr_legs(N)
+        np.testing.assert_allclose(lam, lam2, atol=1e-12 * np.abs(lam2).max())
+        np.testing.assert_allclose(P, P2, atol=1e-12 * np.abs(P2).max())
+        np.testing.assert_allclose(B, B2, atol=1e-12 * np.abs(B2).max())
+
+
+# --- P7: the Woodbury denominator stays away from zero when Q = P ----------
+
+def test_woodbury_denominator_bound():
+    lam, P, B = load_dplr_table(64)
+    for dt in (1e-4, 1e-2, 1e-1):
+        L = 4096
+        l = np.arange(L)
+        l = l[l != L // 2]
+        z = np.exp(-2j * np.pi * l / L)
+        g = (2 / dt) * (1 - z) / (1 + z)
+        k11 = (1 / (g[:, None] - lam[None, :])) @ (np.conj(P) * P)
+        assert np.abs(1 + k11).min() >= 1 - 1e-12
+
+
+# --- P8: aliasing identity (Cauchy method == dense aliased definition) ------
+
+@pytest.mark.parametrize("N,L,dt", [(16, 256, 1e-3), (16, 256, 1e-1), (64, 1024, 1e-2), (64, 512, 1e-4)])
+def test_cauchy_equals_dense_aliased_hippo(N, L, dt):
+    lam, P, B = load_dplr_table(N)
+    C = _cn(np.random.default_rng(N + L), N) * np.sqrt(0.5)
+    K1 = o.kernel_cauchy(lam, P, P, B, C, dt, L)
+    Abar, Bbar = o.discretize_bilinear(o.dense_state_matrix(lam, P, P), B, dt)
+    K2 = o.kernel_aliased_dense(Abar, Bbar, C, L)
+    assert np.abs(K1 - K2).max() <= 1e-10 * np.abs(K2).max()
+
+
+def test_cauchy_equals_dense_aliased_generic_distinct_q():
+    x = make_generic_inputs(H=3, N=8, L=128, batch=1, seed=5, distinct_q=True)
+    K1, _ = o.forward(x["lam"], x["P"], x["Q"], x["B"], x["C"], x["dt"], x["D"], x["u"], method="cauchy")
+    K2, _ = o.forward(x["lam"], x["P"], x["Q"], x["B"], x["C"], x["dt"], x["D"], x["u"], method="dense")
+    assert np.abs(K1 - K2).max() <= 1e-10 * np.abs(K2).max()
+
+
+def test_aliased_kernel_is_sum_over_periods():
+    # [scratch] section 4, "Aliasing": the kernel matches a dense system summed
+    # over many periods (the page's tolerance: < 1e-4).
+    lam, P, B = load_dplr_table(16)
+    C = _cn(np.random.default_rng(7), 16) * np.sqrt(0.5)
+    dt, L, periods = 1e-2, 128, 200
+    K = o.kernel_cauchy(lam, P, P, B, C, dt, L)
+    Abar, Bbar = o.discretize_bilinear(o.dense_state_matrix(lam, P, P), B, dt)
+    Kt = o.kernel_truncated(Abar, Bbar, C, L * periods).reshape(periods, L).sum(0)
+    assert np.abs(K - Kt).max() / np.abs(Kt).max() < 1e-4
+
+
+# --- P9: decayed kernel equals the exact recurrence -------------------------
+
+def test_decayed_kernel_matches_recurrence():
+    lam, P, B = load_dplr_table(16)
+    C = _cn(np.random.default_rng(8), 16) * np.sqrt(0.5)
+    dt, L = 0.1, 1024
+    Abar, Bbar = o.discretize_bilinear(o.dense_state_matrix(lam, P, P), B, dt)
+    assert np.abs(np.linalg.eigvals(Abar)).max() ** L < 1e-8
+    K = o.kernel_cauchy(lam, P, P, B, C, dt, L)
+    Kt = o.kernel_truncated(Abar, Bbar, C, L)
+    assert np.abs(K - Kt).max() / np.abs(Kt).max() < 1e-7      # page: ~1e-7
+    u = np.random.default_rng(9).standard_normal(L)
+    y_rec = o.recurrence(Abar, Bbar, C, 0.3, u)
+    y_conv = o.conv_fft(u, K, 0.3)
+    assert np.abs(y_rec - y_conv).max() / np.abs(y_rec).max() < 1e-7
+
+
+# --- P10: diagonal (S4D) Vandermonde closed form ----------------------------
+
+def test_s4d_lin_vandermonde_closed_form():
+    x = make_inputs("s4d_lin", H=2, batch=1, L=4096)
+    lam = x["lam"][..., 0].astype(np.float64) + 1j * x["lam"][..., 1]
+    C = x["C"][..., 0].astype(np.float64) + 1j * x["C"][..., 1]
+    Bv = x["B"][..., 0].astype(np.float64) + 1j * x["B"][..., 1]
+    L = 4096
+    K, _ = o.forward(x["lam"], None, None, x["B"], x["C"], x["dt"], x["D"], x["u"], diagonal=True)
+    k = np.arange(L)
+    for h in range(2):
+        dt = float(x["dt"][h])
+        Ab = (1 + dt * lam[h] / 2) / (1 - dt * lam[h] / 2)
+        Bb = dt * Bv[h] / (1 - dt * lam[h] / 2)
+        ref = ((C[h] * Bb / (1 - Ab ** L))[None, :] * Ab[None, :] ** k[:, None]).sum(1).real
+        assert np.abs(K[h] - ref).max() <= 1e-11 * np.abs(ref).max()
+
+
+# --- P11 / P12: brute force on tiny inputs ----------------------------------
+
+@pytest.mark.parametrize("N,L", [(1, 4), (2, 8), (4, 16), (3, 16)])
+def test_recurrence_equals_convolution_bruteforce(N, L):
+    rng = np.random.default_rng(10 + N)
+    lam = -rng.uniform(0.1, 1, N) + 1j * rng.uniform(-2, 2, N)
+    P, B, C = 0.5 * _cn(rng, N), _cn(rng, N), _cn(rng, N)
+    dt, D = 0.2, rng.normal()
+    Abar, Bbar = o.discretize_bilinear(o.dense_state_matrix(lam, P, P), B, dt)
+    Kt = o.kernel_truncated(Abar, Bbar, C, L)
+    for trial in range(3):
+        u = rng.standard_normal(L)
+        y1 = o.recurrence(Abar, Bbar, C, D, u)
+        y2 = o.conv_direct(u, Kt, D)
+        y3 = o.conv_fft(u, Kt, D)
+        np.testing.assert_allclose(y1, y2, atol=1e-13 * np.abs(y1).max())
+        np.testing.assert_allclose(y1, y3, atol=1e-13 * np.abs(y1).max())
+    for t0 in range(L):             # unit impulses: the response is the shifted kernel
+        u = np.zeros(L)
+        u[t0] = 1.0
+        y = o.recurrence(Abar, Bbar, C, D, u)
+        ref = np.zeros(L)
+        ref[t0:] = Kt[: L - t0]
+        ref[t0] += D
+        np.testing.assert_allclose(y, ref, atol=1e-13)
+
+
+@pytest.mark.parametrize("L", [1, 2, 4, 8, 32, 128])
+def test_fft_convolution_equals_direct(L):
+    rng = np.random.default_rng(L)
+    u, K, D = rng.standard_normal(L), rng.standard_normal(L), rng.normal()
+    y = o.conv_fft(u, K, D)
+    np.testing.assert_allclose(y, o.conv_direct(u, K, D), atol=1e-12 * max(1, np.abs(y).max()))
+    for t in range(L):
+        assert abs(o.conv_direct_at(u, K, D, t) - y[t]) < 1e-12 * max(1, np.abs(y).max())
+    # causality: changing a later input does not change earlier outputs
+    if L > 1:
+        u2 = u.copy()
+        u2[L // 2:] += 1.0
+        np.testing.assert_allclose(o.conv_fft(u2, K, D)[: L // 2], y[: L // 2], atol=1e-12)
+    # broadcasting over (batch, H) rows equals the per-row result
+    U = rng.standard_normal((2, 3, L))
+    Ks = rng.standard_normal((3, L))
+    Ds = rng.standard_normal(3)
+    Y = o.conv_fft(U, Ks[None], Ds[None, :, None])
+    for b in range(2):
+        for h in range(3):
+            np.testing.assert_allclose(Y[b, h], o.conv_direct(U[b, h], Ks[h], Ds[h]), atol=1e-11)
+
+
+# --- P13: discrete stability ------------------------------------------------
+
+def test_discrete_poles_inside_unit_circle():
+    for N in (16, 64):
+        lam, P, B = load_dplr_table(N)
+        for dt in (1e-4, 1e-2, 1e-1):
+            Abar, _ = o.discretize_bilinear(o.dense_state_matrix(lam, P, P), B, dt)
+            assert np.abs(np.linalg.eigvals(Abar)).max() < 1.0
+
+
+def test_forward_tiny_cauchy_vs_dense():
+    x = make_inputs("tiny")
+    K1, y1 = o.forward(x["lam"], x["P"], x["Q"], x["B"], x["C"], x["dt"], x["D"], x["u"], method="cauchy")
+    K2, y2 = o.forward(x["lam"], x["P"], x["Q"], x["B"], x["C"], x["dt"], x["D"], x["u"], method="dense")
+    assert np.abs(K1 - K2).max() <= 1e-10 * np.abs(K2).max()
+    assert np.abs(y1 - y2).max() <= 1e-10 * np.abs(y2).max()
+    # y against the direct sum on every row
+    for b in range(y1.shape[0]):
+        for h in range(y1.shape[1]):
+            yd = o.conv_direct(x["u"][b, h], K2[h], float(x["D"][h]))
+            assert np.abs(yd - y1[b, h]).max() <= 1e-11 * np.abs(yd).max()
