@@ -1,0 +1,151 @@
+/*
+ * s4dplr -- S4 DPLR convolution-mode forward pass on AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libs4dplr.so.  Plain pointers and sizes only.  Every device buffer
+ * is owned by the caller; the library never allocates device memory.  All
+ * launches are asynchronous on the caller's HIP stream; a device fault
+ * surfaces at the caller's next synchronisation.
+ *
+ * What is computed (pages cited by title and section):
+ *   "The S4 kernel, from scratch", section 1: H independent single-input
+ *   single-output state-space systems x' = A x + B u, y = C x + D u, one per
+ *   channel, with complex A (N x N), B, C (N) and a real feed-through D.
+ *   Section 2 / "S4" wiki, "Structured Transition Matrix": A = Lambda - P Q^*
+ *   with Lambda complex diagonal and P, Q rank 1 (Q = P at initialization).
+ *   Section 3: bilinear discretization with step dt.
+ *   Section 4: the kernel's generating function at the L roots of unity,
+ *   z_l = exp(-2 pi i l / L), is
+ *       Khat(z) = 2/(1+z) * (k00 - k01 k10 / (1 + k11)),
+ *       k_ab    = sum_n w_ab,n / (g(z) - Lambda_n),  g(z) = (2/dt)(1-z)/(1+z),
+ *   with weights w00 = C B, w01 = C P, w10 = conj(Q) B, w11 = conj(Q) P
+ *   (elementwise); at z = -1 its limit (dt/2) sum_n C_n B_n.  The inverse FFT
+ *   of length L returns the aliased kernel (section 4, "Aliasing"); the
+ *   time-domain kernel is its real part:  K[h][k] = Re((1/L) sum_l Khat_l z_l^-k).
+ *   Section 5: the causal convolution y = K * u + D u, evaluated by an FFT
+ *   zero-padded to 2L:  y[b][h][t] = sum_{j<=t} K[h][j] u[b][h][t-j] + D[h] u[b][h][t].
+ *   "S4" wiki, section "S4D": with the diagonal flag the low-rank term is
+ *   dropped (P = Q = 0) and only k00 is formed.
+ *
+ * Layouts (all contiguous, row-major, last index fastest):
+ *   lambda, P, Q, B, C : [H][N] complex, interleaved float32 (re, im) -- the
+ *                        "(..., 2) real tensor" storage of complex parameters
+ *                        ("The S4 kernel, from scratch", section 6).
+ *   dt, D              : [H] float32.
+ *   K                  : [H][L] float32.
+ *   u, y               : [batch][H][L] float32.
+ *
+ * Limits: L a power of two in [2, 65536] (so 2L <= 131072); 1 <= N <= 256;
+ * H >= 1; batch >= 1; batch * H * L < 2^31.  The workspace is at least
+ * s4dplr_plan_workspace_bytes() bytes and 256-byte aligned.
+ *
+ * Preconditions not checked on the device: Re(Lambda_n) < 0 (a stable
+ * system), dt > 0, all values finite.
+ *
+ * Errors: every entry point returns a status code and never aborts or prints.
+ * Host-side validation runs before any launch; on a validation error nothing
+ * is enqueued.  S4DPLR_ERR_HIP reports a HIP runtime error raised while
+ * enqueueing; s4dplr_last_hip_error() returns its hipError_t value.
+ */
+#ifndef S4DPLR_H
+#define S4DPLR_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define S4DPLR_ABI_VERSION 1
+
+typedef enum s4dplr_status {
+  S4DPLR_OK = 0,
+  S4DPLR_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  S4DPLR_ERR_SHAPE = 2,       /* a size is outside the limits above              */
+  S4DPLR_ERR_WORKSPACE = 3,   /* workspace NULL-sized or not 256-byte aligned    */
+  S4DPLR_ERR_UNSUPPORTED = 4, /* unknown flag bits                               */
+  S4DPLR_ERR_HIP = 5,         /* HIP runtime error while enqueueing              */
+  S4DPLR_ERR_ALIAS = 6        /* output buffer overlaps an input it must not     */
+} s4dplr_status;
+
+/* Plan flag: diagonal state matrix (S4D).  P and Q are ignored (may be NULL). */
+#define S4DPLR_DIAGONAL 1u
+
+typedef struct s4dplr_plan s4dplr_plan;
+
+/* ABI version of the loaded library (S4DPLR_ABI_VERSION it was built with). */
+int s4dplr_abi_version(void);
+
+/* Static English description of a status code; never NULL. */
+const char* s4dplr_status_string(s4dplr_status status);
+
+/* hipError_t of the most recent S4DPLR_ERR_HIP on the calling thread (0 if none). */
+int s4dplr_last_hip_error(void);
+
+/*
+ * Create a plan for H channels of N poles, sequence length L and `batch`
+ * input rows per channel.  Host-only: allocates host memory for the plan and
+ * its fp64-derived tables, touches no device.  *out receives the plan, or NULL
+ * on error.  Errors: ERR_NULL (out), ERR_SHAPE (sizes), ERR_UNSUPPORTED (flags).
+ * The plan is immutable after creation and may be used concurrently from
+ * several threads and streams, each with its own workspace.
+ */
+s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int batch,
+                                 unsigned flags);
+
+/* Bytes of device workspace the plan needs.  Errors: ERR_NULL. */
+s4dplr_status s4dplr_plan_workspace_bytes(const s4dplr_plan* plan, size_t* bytes);
+
+/*
+ * Copy the plan's constant tables (frequency nodes, FFT twiddles, real-FFT
+ * weights; computed in fp64 on the host, rounded to fp32) into the head of
+ * the workspace `ws` on `stream`.  Call once per workspace before the compute
+ * entry points; those leave the table region untouched, so the workspace can
+ * be reused for any number of calls with the same plan.
+ * Errors: ERR_NULL, ERR_WORKSPACE (alignment), ERR_HIP.
+ */
+s4dplr_status s4dplr_plan_init(const s4dplr_plan* plan, void* ws, hipStream_t stream);
+
+/*
+ * Kernel generation ("The S4 kernel, from scratch", sections 3-4): write the
+ * time-domain kernel K [H][L] for the DPLR parameters.  lambda, P, Q, B, C
+ * are [H][N] interleaved complex; dt is [H].  Q == NULL means Q = P.  With
+ * S4DPLR_DIAGONAL, P and Q are ignored.  Device pointers.  K must not overlap
+ * the workspace.  Also leaves the kernel's padded spectrum in the workspace
+ * (with D = 0).
+ * Errors: ERR_NULL, ERR_WORKSPACE, ERR_HIP.
+ */
+s4dplr_status s4dplr_kernel_gen(const s4dplr_plan* plan, const float* lambda, const float* P,
+                                const float* Q, const float* B, const float* C,
+                                const float* dt, float* K, void* ws, hipStream_t stream);
+
+/*
+ * Causal convolution ("The S4 kernel, from scratch", sections 1 and 5):
+ * y[b][h][t] = sum_{j<=t} K[h][j] u[b][h][t-j] + D[h] u[b][h][t], by an FFT
+ * zero-padded to 2L.  u, y: [batch][H][L]; K: [H][L]; D: [H] or NULL (D = 0).
+ * Device pointers.  y must not overlap u or K (ERR_ALIAS).
+ * Errors: ERR_NULL, ERR_ALIAS, ERR_WORKSPACE, ERR_HIP.
+ */
+s4dplr_status s4dplr_conv_fwd(const s4dplr_plan* plan, const float* u, const float* K,
+                              const float* D, float* y, void* ws, hipStream_t stream);
+
+/*
+ * The whole convolution-mode forward pass: kernel generation followed by the
+ * causal convolution, y = K * u + D u.  Arguments as above; K may be NULL, in
+ * which case the time-domain kernel is not written out.  D may be NULL (D = 0).
+ * y must not overlap u (ERR_ALIAS).
+ * Errors: ERR_NULL, ERR_ALIAS, ERR_WORKSPACE, ERR_HIP.
+ */
+s4dplr_status s4dplr_forward(const s4dplr_plan* plan, const float* lambda, const float* P,
+                             const float* Q, const float* B, const float* C, const float* dt,
+                             const float* D, const float* u, float* K, float* y, void* ws,
+                             hipStream_t stream);
+
+/* Release a plan (NULL is ignored).  Host-only. */
+void s4dplr_plan_destroy(s4dplr_plan* plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* S4DPLR_H */

@@ -1,0 +1,194 @@
+"""Python binding of libs4dplr (S4 DPLR convolution-mode forward on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libs4dplr.so``.  The functions carry the names of the C entry
+points in ``include/s4dplr.h`` (without the ``s4dplr_`` prefix).  Tensors are
+float32, contiguous and on the GPU; complex parameters are [H, N, 2]
+(interleaved re, im).  PyTorch supplies device memory and the current stream.
+
+There is no fallback: if the library is missing or fails to load, importing
+this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime that libs4dplr then shares
+
+__all__ = [
+    "S4DPLRError", "DIAGONAL", "abi_version", "status_string", "plan_create",
+    "plan_workspace_bytes", "plan_init", "kernel_gen", "conv_fwd", "forward",
+    "plan_destroy", "Plan", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libs4dplr.so")
+DIAGONAL = 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m structured_state_space_dplr_amd.build` "
+        "(or __graft_entry__.build()) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_p = ctypes.c_void_p
+_lib.s4dplr_abi_version.restype = ctypes.c_int
+_lib.s4dplr_abi_version.argtypes = []
+_lib.s4dplr_status_string.restype = ctypes.c_char_p
+_lib.s4dplr_status_string.argtypes = [ctypes.c_int]
+_lib.s4dplr_last_hip_error.restype = ctypes.c_int
+_lib.s4dplr_last_hip_error.argtypes = []
+_lib.s4dplr_plan_create.restype = ctypes.c_int
+_lib.s4dplr_plan_create.argtypes = [ctypes.POINTER(_p), ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_uint]
+_lib.s4dplr_plan_workspace_bytes.restype = ctypes.c_int
+_lib.s4dplr_plan_workspace_bytes.argtypes = [_p, ctypes.POINTER(ctypes.c_size_t)]
+_lib.s4dplr_plan_init.restype = ctypes.c_int
+_lib.s4dplr_plan_init.argtypes = [_p, _p, _p]
+_lib.s4dplr_kernel_gen.restype = ctypes.c_int
+_lib.s4dplr_kernel_gen.argtypes = [_p] * 10
+_lib.s4dplr_conv_fwd.restype = ctypes.c_int
+_lib.s4dplr_conv_fwd.argtypes = [_p] * 7
+_lib.s4dplr_forward.restype = ctypes.c_int
+_lib.s4dplr_forward.argtypes = [_p] * 13
+_lib.s4dplr_plan_destroy.restype = None
+_lib.s4dplr_plan_destroy.argtypes = [_p]
+
+
+class S4DPLRError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = status_string(status)
+        if status == 5:
+            msg += f" (hipError_t {_lib.s4dplr_last_hip_error()})"
+        super().__init__(f"{where}: status {status}: {msg}")
+        self.status = status
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise S4DPLRError(status, where)
+
+
+def abi_version() -> int:
+    return _lib.s4dplr_abi_version()
+
+
+def status_string(status: int) -> str:
+    return _lib.s4dplr_status_string(status).decode()
+
+
+def plan_create(H: int, N: int, L: int, batch: int, flags: int = 0) -> int:
+    h = _p()
+    _check(_lib.s4dplr_plan_create(ctypes.byref(h), H, N, L, batch, flags), "plan_create")
+    return h.value
+
+
+def plan_workspace_bytes(plan: int) -> int:
+    n = ctypes.c_size_t()
+    _check(_lib.s4dplr_plan_workspace_bytes(plan, ctypes.byref(n)), "plan_workspace_bytes")
+    return n.value
+
+
+def plan_destroy(plan: int) -> None:
+    _lib.s4dplr_plan_destroy(plan)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t, name, shape=None):
+    """Device pointer of a float32 contiguous GPU tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name}: must be float32, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _ws_ptr(ws) -> int:
+    if isinstance(ws, torch.Tensor):
+        return ws.data_ptr()
+    return int(ws)
+
+
+def plan_init(plan: int, ws, stream=None) -> None:
+    _check(_lib.s4dplr_plan_init(plan, _ws_ptr(ws), _stream(stream)), "plan_init")
+
+
+def kernel_gen(plan: "Plan | int", lam, P, Q, B, C, dt, K, ws, stream=None) -> None:
+    p, (H, N, L, _) = _dims(plan)
+    cplx = (H, N, 2)
+    _check(_lib.s4dplr_kernel_gen(
+        p, _ptr(lam, "lam", cplx), _ptr(P, "P", cplx), _ptr(Q, "Q", cplx), _ptr(B, "B", cplx),
+        _ptr(C, "C", cplx), _ptr(dt, "dt", (H,)), _ptr(K, "K", (H, L)), _ws_ptr(ws),
+        _stream(stream)), "kernel_gen")
+
+
+def conv_fwd(plan: "Plan | int", u, K, D, y, ws, stream=None) -> None:
+    p, (H, N, L, batch) = _dims(plan)
+    _check(_lib.s4dplr_conv_fwd(
+        p, _ptr(u, "u", (batch, H, L)), _ptr(K, "K", (H, L)), _ptr(D, "D", (H,)),
+        _ptr(y, "y", (batch, H, L)), _ws_ptr(ws), _stream(stream)), "conv_fwd")
+
+
+def forward(plan: "Plan | int", lam, P, Q, B, C, dt, D, u, K, y, ws, stream=None) -> None:
+    p, (H, N, L, batch) = _dims(plan)
+    cplx = (H, N, 2)
+    _check(_lib.s4dplr_forward(
+        p, _ptr(lam, "lam", cplx), _ptr(P, "P", cplx), _ptr(Q, "Q", cplx), _ptr(B, "B", cplx),
+        _ptr(C, "C", cplx), _ptr(dt, "dt", (H,)), _ptr(D, "D", (H,)),
+        _ptr(u, "u", (batch, H, L)), _ptr(K, "K", (H, L)), _ptr(y, "y", (batch, H, L)),
+        _ws_ptr(ws), _stream(stream)), "forward")
+
+
+def _dims(plan):
+    if isinstance(plan, Plan):
+        return plan.handle, (plan.H, plan.N, plan.L, plan.batch)
+    raise TypeError("pass a Plan (its sizes are needed to check tensor shapes)")
+
+
+class Plan:
+    """Owns a plan handle and (optionally) a workspace tensor on one device."""
+
+    def __init__(self, H: int, N: int, L: int, batch: int, diagonal: bool = False,
+                 device=None):
+        self.H, self.N, self.L, self.batch = H, N, L, batch
+        self.diagonal = diagonal
+        self.handle = plan_create(H, N, L, batch, DIAGONAL if diagonal else 0)
+        self.workspace_bytes = plan_workspace_bytes(self.handle)
+        self.device = torch.device("cuda" if device is None else device)
+        self._ws_store = None
+        self._ws = None
+
+    def workspace(self, stream=None):
+        """A 256-byte aligned workspace tensor with the tables already written."""
+        if self._ws is None:
+            store = torch.empty(self.workspace_bytes + 256, dtype=torch.uint8, device=self.device)
+            off = (-store.data_ptr()) % 256
+            self._ws_store = store
+            self._ws = store[off: off + self.workspace_bytes]
+            plan_init(self.handle, self._ws, stream)
+        return self._ws
+
+    def close(self) -> None:
+        if self.handle:
+            plan_destroy(self.handle)
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

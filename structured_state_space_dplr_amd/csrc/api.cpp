@@ -1,0 +1,228 @@
+// Host side of libs4dplr: argument validation, plans, workspace layout, the
+// fp64 constant tables, and the order of kernel launches.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "fft_sched.h"
+#include "internal.h"
+#include "s4dplr.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool is_pow2(long v) { return v > 0 && (v & (v - 1)) == 0; }
+int ilog2(long v) {
+  int r = 0;
+  while ((1L << r) < v) ++r;
+  return r;
+}
+
+s4dplr_status hip_fail(hipError_t e) {
+  g_last_hip_error = static_cast<int>(e);
+  return S4DPLR_ERR_HIP;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Twiddles of the workgroup FFT of 2^log2n points, pass by pass, as the
+// schedule in fft_sched.h lays them out: W_{Ns R}^{r k} = e^{-2 pi i r k/(Ns R)}.
+void fft_twiddles(int log2n, float* out) {
+  const int P = s4::fft_num_passes(log2n);
+  for (int p = 1; p < P; ++p) {
+    const int ns = 1 << s4::fft_ns_log(log2n, p);
+    const int R = 1 << s4::fft_radix_log(log2n, p);
+    const long span = (long)ns * R;
+    float* t = out + 2 * s4::fft_tw_offset(log2n, p);
+    for (int k = 0; k < ns; ++k)
+      for (int r = 0; r < R; ++r) {
+        const long m = ((long)r * k) % span;
+        const double ang = -2.0 * M_PI * (double)m / (double)span;
+        t[2 * (k * R + r) + 0] = (float)std::cos(ang);
+        t[2 * (k * R + r) + 1] = (float)std::sin(ang);
+      }
+  }
+}
+
+bool valid_plan(const s4dplr_plan* p) { return p != nullptr; }
+
+}  // namespace
+
+extern "C" {
+
+int s4dplr_abi_version(void) { return S4DPLR_ABI_VERSION; }
+
+int s4dplr_last_hip_error(void) { return g_last_hip_error; }
+
+const char* s4dplr_status_string(s4dplr_status s) {
+  switch (s) {
+    case S4DPLR_OK: return "success";
+    case S4DPLR_ERR_NULL: return "a required pointer is NULL";
+    case S4DPLR_ERR_SHAPE: return "a size is outside the supported limits";
+    case S4DPLR_ERR_WORKSPACE: return "workspace missing or not 256-byte aligned";
+    case S4DPLR_ERR_UNSUPPORTED: return "unsupported flags";
+    case S4DPLR_ERR_HIP: return "HIP runtime error while enqueueing";
+    case S4DPLR_ERR_ALIAS: return "an output buffer overlaps an input or the workspace";
+  }
+  return "unknown status";
+}
+
+s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int batch,
+                                 unsigned flags) {
+  if (!out) return S4DPLR_ERR_NULL;
+  *out = nullptr;
+  if (flags & ~S4DPLR_DIAGONAL) return S4DPLR_ERR_UNSUPPORTED;
+  if (H < 1 || batch < 1 || N < 1 || N > 256) return S4DPLR_ERR_SHAPE;
+  if (!is_pow2(L) || L < 2 || L > 65536) return S4DPLR_ERR_SHAPE;
+  if ((long long)batch * H * L >= (1LL << 31)) return S4DPLR_ERR_SHAPE;
+  const int log2L = ilog2(L);
+  if (log2L > S4DPLR_LDS_MAX_LOG2L) return S4DPLR_ERR_SHAPE;  // multi-pass path not built yet
+
+  s4dplr_plan* p = new (std::nothrow) s4dplr_plan();
+  if (!p) return S4DPLR_ERR_SHAPE;
+  p->H = H;
+  p->N = N;
+  p->L = L;
+  p->log2L = log2L;
+  p->batch = batch;
+  p->flags = flags;
+
+  // Table region.
+  size_t off = 0;
+  p->off_tan = off;
+  off = align_up(off + sizeof(float) * L);
+  p->off_cs = off;
+  off = align_up(off + 2 * sizeof(float) * (L + 1));
+  p->off_twL = off;
+  off = align_up(off + 2 * sizeof(float) * (size_t)s4::fft_tw_size(log2L));
+  p->off_twH = off;
+  off = align_up(off + 2 * sizeof(float) * (size_t)s4::fft_tw_size(log2L - 1));
+  p->off_tw4 = off;
+  p->tables_bytes = off;
+  // Scratch region.
+  p->off_poles = off;
+  off = align_up(off + sizeof(float) * 12 * (size_t)H * N);
+  p->off_chan = off;
+  off = align_up(off + sizeof(float) * 4 * (size_t)H);
+  p->off_khat = off;
+  off = align_up(off + sizeof(float) * 2 * (size_t)H * L);
+  p->off_coef = off;
+  off = align_up(off + sizeof(float) * 4 * (size_t)H * L);
+  p->off_big = off;
+  p->total = off;
+
+  // fp64 tables, rounded once to fp32.
+  p->tables.assign(p->tables_bytes, 0);
+  float* tanT = reinterpret_cast<float*>(p->tables.data() + p->off_tan);
+  for (int l = 0; l < L; ++l)
+    tanT[l] = (2 * l == L) ? 0.0f : (float)std::tan(M_PI * (double)l / (double)L);
+  float* cs = reinterpret_cast<float*>(p->tables.data() + p->off_cs);
+  for (int j = 0; j <= L; ++j) {
+    cs[2 * j + 0] = (float)std::cos(M_PI * (double)j / (double)L);
+    cs[2 * j + 1] = (float)std::sin(M_PI * (double)j / (double)L);
+  }
+  cs[2 * L + 1] = 0.0f;      // sin(pi) exactly
+  if (L % 2 == 0) cs[L + 0] = 0.0f;  // cos(pi/2) exactly, at j = L/2
+  fft_twiddles(log2L, reinterpret_cast<float*>(p->tables.data() + p->off_twL));
+  fft_twiddles(log2L - 1, reinterpret_cast<float*>(p->tables.data() + p->off_twH));
+  *out = p;
+  return S4DPLR_OK;
+}
+
+void s4dplr_plan_destroy(s4dplr_plan* p) { delete p; }
+
+s4dplr_status s4dplr_plan_workspace_bytes(const s4dplr_plan* p, size_t* bytes) {
+  if (!valid_plan(p) || !bytes) return S4DPLR_ERR_NULL;
+  *bytes = p->total;
+  return S4DPLR_OK;
+}
+
+static s4dplr_status check_ws(const void* ws) {
+  if (!ws) return S4DPLR_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return S4DPLR_ERR_WORKSPACE;
+  return S4DPLR_OK;
+}
+
+s4dplr_status s4dplr_plan_init(const s4dplr_plan* p, void* ws, hipStream_t stream) {
+  if (!valid_plan(p)) return S4DPLR_ERR_NULL;
+  if (s4dplr_status st = check_ws(ws)) return st;
+  hipError_t e = hipMemcpyAsync(ws, p->tables.data(), p->tables_bytes, hipMemcpyHostToDevice,
+                                stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return S4DPLR_OK;
+}
+
+static s4dplr_status check_params(const s4dplr_plan* p, const float* lambda, const float* P,
+                                  const float* B, const float* C, const float* dt) {
+  if (!lambda || !B || !C || !dt) return S4DPLR_ERR_NULL;
+  if (!(p->flags & S4DPLR_DIAGONAL) && !P) return S4DPLR_ERR_NULL;
+  return S4DPLR_OK;
+}
+
+s4dplr_status s4dplr_kernel_gen(const s4dplr_plan* p, const float* lambda, const float* P,
+                                const float* Q, const float* B, const float* C,
+                                const float* dt, float* K, void* ws, hipStream_t stream) {
+  if (!valid_plan(p)) return S4DPLR_ERR_NULL;
+  if (s4dplr_status st = check_params(p, lambda, P, B, C, dt)) return st;
+  if (!K) return S4DPLR_ERR_NULL;
+  if (s4dplr_status st = check_ws(ws)) return st;
+  const size_t kb = sizeof(float) * (size_t)p->H * p->L;
+  if (overlaps(K, kb, ws, p->total)) return S4DPLR_ERR_ALIAS;
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  hipError_t e;
+  if ((e = s4::launch_pack(p, lambda, P, Q, B, C, dt, w, stream)) != hipSuccess) return hip_fail(e);
+  if ((e = s4::launch_cauchy(p, w, stream)) != hipSuccess) return hip_fail(e);
+  if ((e = s4::launch_kspec(p, nullptr, nullptr, K, w, stream)) != hipSuccess) return hip_fail(e);
+  return S4DPLR_OK;
+}
+
+s4dplr_status s4dplr_conv_fwd(const s4dplr_plan* p, const float* u, const float* K,
+                              const float* D, float* y, void* ws, hipStream_t stream) {
+  if (!valid_plan(p)) return S4DPLR_ERR_NULL;
+  if (!u || !K || !y) return S4DPLR_ERR_NULL;
+  if (s4dplr_status st = check_ws(ws)) return st;
+  const size_t ub = sizeof(float) * (size_t)p->batch * p->H * p->L;
+  const size_t kb = sizeof(float) * (size_t)p->H * p->L;
+  if (overlaps(y, ub, u, ub) || overlaps(y, ub, K, kb) || overlaps(y, ub, ws, p->total))
+    return S4DPLR_ERR_ALIAS;
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  hipError_t e;
+  if ((e = s4::launch_kspec(p, K, D, nullptr, w, stream)) != hipSuccess) return hip_fail(e);
+  if ((e = s4::launch_conv(p, u, y, w, stream)) != hipSuccess) return hip_fail(e);
+  return S4DPLR_OK;
+}
+
+s4dplr_status s4dplr_forward(const s4dplr_plan* p, const float* lambda, const float* P,
+                             const float* Q, const float* B, const float* C, const float* dt,
+                             const float* D, const float* u, float* K, float* y, void* ws,
+                             hipStream_t stream) {
+  if (!valid_plan(p)) return S4DPLR_ERR_NULL;
+  if (s4dplr_status st = check_params(p, lambda, P, B, C, dt)) return st;
+  if (!u || !y) return S4DPLR_ERR_NULL;
+  if (s4dplr_status st = check_ws(ws)) return st;
+  const size_t ub = sizeof(float) * (size_t)p->batch * p->H * p->L;
+  const size_t kb = sizeof(float) * (size_t)p->H * p->L;
+  if (overlaps(y, ub, u, ub) || overlaps(y, ub, ws, p->total)) return S4DPLR_ERR_ALIAS;
+  if (K && (overlaps(K, kb, u, ub) || overlaps(K, kb, y, ub) || overlaps(K, kb, ws, p->total)))
+    return S4DPLR_ERR_ALIAS;
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  hipError_t e;
+  if ((e = s4::launch_pack(p, lambda, P, Q, B, C, dt, w, stream)) != hipSuccess) return hip_fail(e);
+  if ((e = s4::launch_cauchy(p, w, stream)) != hipSuccess) return hip_fail(e);
+  if ((e = s4::launch_kspec(p, nullptr, D, K, w, stream)) != hipSuccess) return hip_fail(e);
+  if ((e = s4::launch_conv(p, u, y, w, stream)) != hipSuccess) return hip_fail(e);
+  return S4DPLR_OK;
+}
+
+}  // extern "C"

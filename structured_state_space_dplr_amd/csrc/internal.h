@@ -1,0 +1,51 @@
+// Internal plan structure and kernel launchers of libs4dplr.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "s4dplr.h"
+
+// Largest L handled by the single-workgroup (LDS-resident) kernels; longer
+// sequences use the multi-pass path.
+#define S4DPLR_LDS_MAX_LOG2L 14
+
+struct s4dplr_plan {
+  int H, N, L, log2L, batch;
+  unsigned flags;
+  // Workspace layout, byte offsets from the 256-byte aligned base.
+  size_t off_tan;    // [L] float: tan(pi l / L), 0 at l = L/2
+  size_t off_cs;     // [L+1] float2: (cos(pi j / L), sin(pi j / L))
+  size_t off_twL;    // FFT twiddles for transforms of L points
+  size_t off_twH;    // FFT twiddles for transforms of L/2 points
+  size_t off_tw4;    // multi-pass path: four-step twiddles (0 bytes otherwise)
+  size_t tables_bytes;
+  size_t off_poles;  // [H][N][3] float4 packed pole records
+  size_t off_chan;   // [H] float4: (2/dt, (dt/2) sum C B re, im, 0)
+  size_t off_khat;   // [H][L] float2: generating function at the roots of unity
+  size_t off_coef;   // [H][2][L/2] float4: spectral weights (alpha, beta) per bin
+  size_t off_big;    // multi-pass path: [batch*H][L] float2 intermediate (0 bytes otherwise)
+  size_t total;
+  std::vector<unsigned char> tables;  // exact bytes of the table region
+};
+
+namespace s4 {
+
+bool lds_path(const s4dplr_plan* p);
+
+hipError_t launch_pack(const s4dplr_plan* p, const float* lam, const float* P, const float* Q,
+                       const float* B, const float* C, const float* dt, unsigned char* ws,
+                       hipStream_t s);
+hipError_t launch_cauchy(const s4dplr_plan* p, unsigned char* ws, hipStream_t s);
+// Kernel spectrum: from the generating function in the workspace (Ktime ==
+// nullptr; writes the time-domain kernel to Kout if not null) or from a
+// time-domain kernel Ktime.  Folds D (may be null) into the weights.
+hipError_t launch_kspec(const s4dplr_plan* p, const float* Ktime, const float* D, float* Kout,
+                        unsigned char* ws, hipStream_t s);
+hipError_t launch_conv(const s4dplr_plan* p, const float* u, float* y, unsigned char* ws,
+                       hipStream_t s);
+
+}  // namespace s4

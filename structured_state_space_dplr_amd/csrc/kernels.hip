@@ -1,0 +1,422 @@
+// HIP kernels (gfx950) of the S4 DPLR convolution-mode forward pass.
+//
+// Pages cited: "The S4 kernel, from scratch" (sections 3-5), "S4" wiki
+// ("Structured Transition Matrix", "S4D").
+//
+// Stage 1 (kernel generation):
+//   pack    -- per (channel, pole): weights C B, C P, conj(Q) B, conj(Q) P and
+//              the pole's Re^2, Im; per channel 2/dt and the z = -1 limit.
+//   cauchy  -- per (channel, frequency): the four Cauchy sums over the poles,
+//              the rank-1 Woodbury correction and the 2/(1+z) factor.
+//   kspec   -- per channel: inverse FFT of length L, real part -> K; then the
+//              spectrum of (K + D delta) zero-padded to 2L, stored as the two
+//              complex weights per bin that the convolution applies.
+// Stage 2 (convolution):
+//   conv    -- per (batch, channel) row: real FFT of length 2L of the
+//              zero-padded input, spectral product, inverse, first L outputs.
+//
+// Frequency-node algebra (exact rewrites of section 4's formulas): with
+// theta = 2 pi l / L and z = e^{-i theta},
+//   g(z) = (2/dt) (1-z)/(1+z) = i (2/dt) tan(theta/2),
+//   2/(1+z) = 1 + i tan(theta/2),
+// so every Cauchy term is 1/(i G - Lambda_n) with a real G per frequency.
+//
+// Real FFT of length 2L in halves: the zero-padded input x (2L reals) is
+// packed as z_k = x_2k + i x_2k+1 (M = L complex points, the upper half zero).
+// The even bins of its M-point DFT are the (M/2)-point DFT of a_k = z_k, the
+// odd bins that of b_k = z_k W_M^k.  The real-FFT pairing of bins j and M-j
+// never mixes the two halves, and the inverse of the spectral product is
+// z'_k = IDFT(a')_k + W_M^-k IDFT(b')_k for the first M/2 points, which are
+// exactly the L outputs kept.  So each row is two independent transforms of
+// L/2 points forward and two back, joined only at the ends.
+#include <hip/hip_runtime.h>
+
+#include "device_fft.h"
+#include "internal.h"
+
+namespace s4 {
+
+// ---------------------------------------------------------------------------
+// Stage 1a: pack pole records and channel constants
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_kernel(
+    const float2* __restrict__ lam, const float2* __restrict__ P, const float2* __restrict__ Q,
+    const float2* __restrict__ B, const float2* __restrict__ C, const float* __restrict__ dt,
+    float4* __restrict__ poles, float4* __restrict__ chan, int H, int N, int diag) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx < H * N) {
+    const float2 l = lam[idx], b = B[idx], c = C[idx];
+    const float2 p = diag ? make_float2(0.f, 0.f) : P[idx];
+    const float2 q = diag ? make_float2(0.f, 0.f) : (Q ? Q[idx] : p);
+    const float2 w00 = cmul(c, b), w01 = cmul(c, p);
+    const float2 w10 = cmul(cconj(q), b), w11 = cmul(cconj(q), p);
+    poles[3 * idx + 0] = make_float4(l.y, l.x * l.x, -l.x, 0.f);
+    poles[3 * idx + 1] = make_float4(w00.x, w00.y, w01.x, w01.y);
+    poles[3 * idx + 2] = make_float4(w10.x, w10.y, w11.x, w11.y);
+  }
+  if (idx < H) {
+    const float d = dt[idx];
+    float2 s = make_float2(0.f, 0.f);
+    for (int n = 0; n < N; ++n) s = cadd(s, cmul(C[idx * N + n], B[idx * N + n]));
+    // limit of the generating function at z = -1: (dt/2) sum_n C_n B_n
+    chan[idx] = make_float4(2.0f / d, 0.5f * d * s.x, 0.5f * d * s.y, 0.f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 1b: Cauchy sums + Woodbury + 2/(1+z) at the L roots of unity
+// ---------------------------------------------------------------------------
+// Each thread evaluates F frequencies of one channel; the pole loop reads
+// wave-uniform records (scalar loads) so every term is pure VALU work:
+//   y = G - Im(Lambda), d = Re(Lambda)^2 + y^2, rho = (-Re(Lambda) - i y)/d,
+//   k_ab += w_ab * rho.
+constexpr int kCauchyThreads = 256;
+
+template <int F, bool DIAG>
+__global__ __launch_bounds__(kCauchyThreads) void cauchy_kernel(
+    const float4* __restrict__ poles, const float4* __restrict__ chan,
+    const float* __restrict__ tanT, float2* __restrict__ khat, int N, int L) {
+  const int h = blockIdx.y;
+  const float4 ch = chan[h];
+  const float4* __restrict__ pr = poles + (size_t)h * N * 3;
+  int l[F];
+  float T[F], G[F];
+  float acc[F][8];
+#pragma unroll
+  for (int f = 0; f < F; ++f) {
+    l[f] = (blockIdx.x * F + f) * kCauchyThreads + threadIdx.x;
+    T[f] = l[f] < L ? tanT[l[f]] : 0.f;
+    G[f] = ch.x * T[f];
+#pragma unroll
+    for (int a = 0; a < 8; ++a) acc[f][a] = 0.f;
+  }
+  for (int n = 0; n < N; ++n) {
+    const float4 p0 = pr[3 * n + 0];
+    const float4 p1 = pr[3 * n + 1];
+    float4 p2 = make_float4(0.f, 0.f, 0.f, 0.f);
+    if constexpr (!DIAG) p2 = pr[3 * n + 2];
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      const float yv = G[f] - p0.x;
+      const float d = fmaf(yv, yv, p0.y);
+      const float r = __builtin_amdgcn_rcpf(d);
+      const float qr = p0.z * r;
+      const float qi = -yv * r;
+      acc[f][0] = fmaf(p1.x, qr, acc[f][0]);
+      acc[f][0] = fmaf(-p1.y, qi, acc[f][0]);
+      acc[f][1] = fmaf(p1.x, qi, acc[f][1]);
+      acc[f][1] = fmaf(p1.y, qr, acc[f][1]);
+      if constexpr (!DIAG) {
+        acc[f][2] = fmaf(p1.z, qr, acc[f][2]);
+        acc[f][2] = fmaf(-p1.w, qi, acc[f][2]);
+        acc[f][3] = fmaf(p1.z, qi, acc[f][3]);
+        acc[f][3] = fmaf(p1.w, qr, acc[f][3]);
+        acc[f][4] = fmaf(p2.x, qr, acc[f][4]);
+        acc[f][4] = fmaf(-p2.y, qi, acc[f][4]);
+        acc[f][5] = fmaf(p2.x, qi, acc[f][5]);
+        acc[f][5] = fmaf(p2.y, qr, acc[f][5]);
+        acc[f][6] = fmaf(p2.z, qr, acc[f][6]);
+        acc[f][6] = fmaf(-p2.w, qi, acc[f][6]);
+        acc[f][7] = fmaf(p2.z, qi, acc[f][7]);
+        acc[f][7] = fmaf(p2.w, qr, acc[f][7]);
+      }
+    }
+  }
+#pragma unroll
+  for (int f = 0; f < F; ++f) {
+    if (l[f] >= L) continue;
+    float2 kv = make_float2(acc[f][0], acc[f][1]);
+    if constexpr (!DIAG) {
+      // Woodbury: k00 - k01 k10 / (1 + k11)
+      const float2 k01 = make_float2(acc[f][2], acc[f][3]);
+      const float2 k10 = make_float2(acc[f][4], acc[f][5]);
+      const float2 den = make_float2(1.0f + acc[f][6], acc[f][7]);
+      const float2 num = cmul(k01, k10);
+      const float inv = 1.0f / fmaf(den.x, den.x, den.y * den.y);
+      const float2 t = cmulc(num, den);
+      kv = make_float2(fmaf(-t.x, inv, kv.x), fmaf(-t.y, inv, kv.y));
+    }
+    float2 kh = cmul(make_float2(1.0f, T[f]), kv);       // times 2/(1+z)
+    if (2 * l[f] == L) kh = make_float2(ch.y, ch.z);      // z = -1: the limit
+    khat[(size_t)h * L + l[f]] = kh;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 1c: time-domain kernel and its zero-padded spectrum (LDS-resident)
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+template <int LOG2L>
+struct KspecShape {
+  static constexpr int L = 1 << LOG2L, H2 = L / 2, LOG2H2 = LOG2L - 1;
+  static constexpr int EL = 1 << fft_elems_log(LOG2L);
+  static constexpr int EH = 1 << fft_elems_log(LOG2H2);
+  static constexpr int NTL = L / EL;       // threads of the length-L transform
+  static constexpr int TPH = H2 / EH;      // threads per half transform
+  static constexpr int NT = cmax(NTL, 2 * TPH);
+  static constexpr int HP = lds_padded_size(H2);
+  static constexpr int BUF = cmax(lds_padded_size(L), 2 * HP);
+  static constexpr int ZPT = (H2 + NT - 1) / NT;
+};
+
+// (1 -+ i W_{2M}^j)/2 with W_{2M}^j = e^{-i pi j / M} given as (cos, sin) of pi j / M:
+//   p = ((1 - s) - i c)/2,  q = ((1 + s) + i c)/2.
+__device__ __forceinline__ float2 rfft_x(float2 zj, float2 zmj, float2 csj) {
+  // X_j = p_j Z_j + q_j conj(Z_{M-j})
+  const float2 p = make_float2(0.5f * (1.0f - csj.y), -0.5f * csj.x);
+  const float2 q = make_float2(0.5f * (1.0f + csj.y), 0.5f * csj.x);
+  return cadd(cmul(p, zj), cmul(q, cconj(zmj)));
+}
+
+template <int LOG2L, bool FROM_TIME>
+__global__ __launch_bounds__(KspecShape<LOG2L>::NT) void kspec_kernel(
+    const float2* __restrict__ khat, const float* __restrict__ Kin, const float* __restrict__ D,
+    float* __restrict__ Kout, float4* __restrict__ coef, const float2* __restrict__ twL,
+    const float2* __restrict__ twH, const float2* __restrict__ cs) {
+  using S = KspecShape<LOG2L>;
+  constexpr int L = S::L, H2 = S::H2, NT = S::NT;
+  __shared__ float2 buf[S::BUF];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  float2 z[S::ZPT];
+  if constexpr (!FROM_TIME) {
+    for (int k = tid; k < L; k += NT) buf[lds_pad(k)] = khat[(size_t)h * L + k];
+    __syncthreads();
+    lds_fft<LOG2L, true>(buf, tid, tid < S::NTL, twL);
+    const float invL = 1.0f / (float)L;
+#pragma unroll
+    for (int i = 0; i < S::ZPT; ++i) {
+      const int k = tid + i * NT;
+      if (k < H2) {
+        z[i] = make_float2(buf[lds_pad(2 * k)].x * invL, buf[lds_pad(2 * k + 1)].x * invL);
+        if (Kout) reinterpret_cast<float2*>(Kout + (size_t)h * L)[k] = z[i];
+      }
+    }
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int i = 0; i < S::ZPT; ++i) {
+      const int k = tid + i * NT;
+      if (k < H2) z[i] = reinterpret_cast<const float2*>(Kin + (size_t)h * L)[k];
+    }
+  }
+  float2* A = buf;
+  float2* Bq = buf + S::HP;
+#pragma unroll
+  for (int i = 0; i < S::ZPT; ++i) {
+    const int k = tid + i * NT;
+    if (k < H2) {
+      const float2 c = cs[2 * k];                        // W_L^k = cos - i sin of 2 pi k / L
+      A[lds_pad(k)] = z[i];
+      Bq[lds_pad(k)] = cmul(z[i], make_float2(c.x, -c.y));
+    }
+  }
+  __syncthreads();
+  {
+    const int half = tid / S::TPH, lt = tid % S::TPH;
+    lds_fft<S::LOG2H2, false>(half ? Bq : A, lt, tid < 2 * S::TPH, twH);
+  }
+  // Spectrum S_j = X_j + D of (K + D delta) padded to 2L, for bins j in
+  // [0, L]; weights for the convolution's pairing step (scaled by 1/(2L)):
+  //   alpha_j = ((1 - s_j) S_j + (1 + s_j) conj(S_{L-j})) / (2L)
+  //   beta_j  = i c_j (S_j - conj(S_{L-j})) / (2L)
+  const float Dh = D ? D[h] : 0.f;
+  const float sc = 0.5f / (float)L;
+  float4* cf = coef + (size_t)h * L;
+  auto zget = [&](int j) -> float2 { return (j & 1) ? Bq[lds_pad(j >> 1)] : A[lds_pad(j >> 1)]; };
+  auto cidx = [&](int j) -> int { return (j & 1) * H2 + (j >> 1); };
+  for (int j = tid; j <= L / 2; j += NT) {
+    const int jm = L - j;
+    const float2 zj = zget(j), zm = zget(jm & (L - 1));
+    const float2 csj = cs[j], csm = cs[jm];
+    float2 sj = rfft_x(zj, zm, csj), sm = rfft_x(zm, zj, csm);
+    sj.x += Dh;
+    sm.x += Dh;
+    {
+      const float a = sc * (1.0f - csj.y), b = sc * (1.0f + csj.y), c = sc * csj.x;
+      const float2 al = make_float2(fmaf(a, sj.x, b * sm.x), fmaf(a, sj.y, -b * sm.y));
+      const float2 df = make_float2(sj.x - sm.x, sj.y + sm.y);   // S_j - conj(S_m)
+      cf[cidx(j)] = make_float4(al.x, al.y, -c * df.y, c * df.x);
+    }
+    if (j != 0 && jm != j) {
+      const float a = sc * (1.0f - csm.y), b = sc * (1.0f + csm.y), c = sc * csm.x;
+      const float2 al = make_float2(fmaf(a, sm.x, b * sj.x), fmaf(a, sm.y, -b * sj.y));
+      const float2 df = make_float2(sm.x - sj.x, sm.y + sj.y);
+      cf[cidx(jm)] = make_float4(al.x, al.y, -c * df.y, c * df.x);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 2: fused causal convolution, one row per thread group (LDS-resident)
+// ---------------------------------------------------------------------------
+template <int LOG2L>
+struct ConvShape {
+  static constexpr int L = 1 << LOG2L, H2 = L / 2, LOG2H2 = LOG2L - 1;
+  static constexpr int E = 1 << fft_elems_log(LOG2H2);
+  static constexpr int TPH = H2 / E;
+  static constexpr int TPR = 2 * TPH;                      // threads per row
+  static constexpr int NTHR = TPR > 256 ? TPR : 256;
+  static constexpr int RPW = NTHR / TPR;                   // rows per workgroup
+  static constexpr int HP = lds_padded_size(H2);
+};
+
+template <int LOG2L>
+__global__ __launch_bounds__(ConvShape<LOG2L>::NTHR) void conv_kernel(
+    const float* __restrict__ u, float* __restrict__ y, const float4* __restrict__ coef,
+    const float2* __restrict__ twH, const float2* __restrict__ cs, int H, int batch) {
+  using S = ConvShape<LOG2L>;
+  constexpr int L = S::L, H2 = S::H2, TPR = S::TPR, TPH = S::TPH;
+  __shared__ float2 lds[S::RPW * 2 * S::HP];
+  const int tid = threadIdx.x;
+  const int rloc = tid / TPR, t = tid % TPR;
+  const int half = t / TPH, lt = t % TPH;
+  const int lblk = xcd_remap(blockIdx.x, gridDim.x);
+  const int lrow = lblk * S::RPW + rloc;          // logical row: channel-major
+  const int rows = batch * H;
+  const bool active = lrow < rows;
+  const int h = active ? lrow / batch : 0;
+  const int b = active ? lrow - h * batch : 0;
+  const size_t roff = ((size_t)b * H + h) * L;
+  float2* A = lds + rloc * 2 * S::HP;
+  float2* Bq = A + S::HP;
+  // 1. load the row as z_k = (u_2k, u_2k+1); a = z, b = z W_L^k
+  for (int k = t; k < H2; k += TPR) {
+    const float2 zk = active ? reinterpret_cast<const float2*>(u + roff)[k] : make_float2(0.f, 0.f);
+    const float2 c = cs[2 * k];
+    A[lds_pad(k)] = zk;
+    Bq[lds_pad(k)] = cmul(zk, make_float2(c.x, -c.y));
+  }
+  __syncthreads();
+  float2* mine = half ? Bq : A;
+  // 2. forward transforms of L/2 points
+  lds_fft<S::LOG2H2, false>(mine, lt, true, twH);
+  // 3. spectral step on bin pairs (j, L-j): Z'_j = alpha_j Z_j + beta_j conj(Z_{L-j})
+  const float4* __restrict__ cf = coef + (size_t)h * L + half * H2;
+  if (half == 0) {
+    for (int m = lt; m <= H2 / 2; m += TPH) {
+      const int mp = (H2 - m) & (H2 - 1);
+      const float2 z1 = A[lds_pad(m)], z2 = A[lds_pad(mp)];
+      const float4 c1 = cf[m], c2 = cf[mp];
+      const float2 o1 = cadd(cmul(make_float2(c1.x, c1.y), z1), cmul(make_float2(c1.z, c1.w), cconj(z2)));
+      const float2 o2 = cadd(cmul(make_float2(c2.x, c2.y), z2), cmul(make_float2(c2.z, c2.w), cconj(z1)));
+      A[lds_pad(m)] = o1;
+      if (mp != m) A[lds_pad(mp)] = o2;
+    }
+  } else {
+    for (int m = lt; m < (H2 + 1) / 2; m += TPH) {
+      const int mp = H2 - 1 - m;
+      const float2 z1 = Bq[lds_pad(m)], z2 = Bq[lds_pad(mp)];
+      const float4 c1 = cf[m], c2 = cf[mp];
+      const float2 o1 = cadd(cmul(make_float2(c1.x, c1.y), z1), cmul(make_float2(c1.z, c1.w), cconj(z2)));
+      const float2 o2 = cadd(cmul(make_float2(c2.x, c2.y), z2), cmul(make_float2(c2.z, c2.w), cconj(z1)));
+      Bq[lds_pad(m)] = o1;
+      if (mp != m) Bq[lds_pad(mp)] = o2;
+    }
+  }
+  __syncthreads();
+  // 4. inverse transforms
+  lds_fft<S::LOG2H2, true>(mine, lt, true, twH);
+  // 5. join the halves: z'_k = a'_k + W_L^-k b'_k -> (y_2k, y_2k+1)
+  for (int k = t; k < H2; k += TPR) {
+    const float2 c = cs[2 * k];
+    const float2 zz = cadd(A[lds_pad(k)], cmul(Bq[lds_pad(k)], c));
+    if (active) reinterpret_cast<float2*>(y + roff)[k] = zz;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+bool lds_path(const s4dplr_plan* p) { return p->log2L <= S4DPLR_LDS_MAX_LOG2L; }
+
+template <typename T>
+static T* at(unsigned char* ws, size_t off) { return reinterpret_cast<T*>(ws + off); }
+
+hipError_t launch_pack(const s4dplr_plan* p, const float* lam, const float* P, const float* Q,
+                       const float* B, const float* C, const float* dt, unsigned char* ws,
+                       hipStream_t s) {
+  const int n = p->H * p->N;
+  const int blocks = (n + 255) / 256;
+  const int diag = (p->flags & S4DPLR_DIAGONAL) ? 1 : 0;
+  pack_kernel<<<blocks, 256, 0, s>>>(
+      reinterpret_cast<const float2*>(lam), reinterpret_cast<const float2*>(P),
+      reinterpret_cast<const float2*>(Q), reinterpret_cast<const float2*>(B),
+      reinterpret_cast<const float2*>(C), dt, at<float4>(ws, p->off_poles),
+      at<float4>(ws, p->off_chan), p->H, p->N, diag);
+  return hipGetLastError();
+}
+
+hipError_t launch_cauchy(const s4dplr_plan* p, unsigned char* ws, hipStream_t s) {
+  constexpr int F = 2;
+  const int per_block = F * kCauchyThreads;
+  dim3 grid((p->L + per_block - 1) / per_block, p->H);
+  const float4* poles = at<const float4>(ws, p->off_poles);
+  const float4* chan = at<const float4>(ws, p->off_chan);
+  const float* tanT = at<const float>(ws, p->off_tan);
+  float2* khat = at<float2>(ws, p->off_khat);
+  if (p->flags & S4DPLR_DIAGONAL)
+    cauchy_kernel<F, true><<<grid, kCauchyThreads, 0, s>>>(poles, chan, tanT, khat, p->N, p->L);
+  else
+    cauchy_kernel<F, false><<<grid, kCauchyThreads, 0, s>>>(poles, chan, tanT, khat, p->N, p->L);
+  return hipGetLastError();
+}
+
+template <int LOG2L>
+static void kspec_launch(const s4dplr_plan* p, const float* Ktime, const float* D, float* Kout,
+                         unsigned char* ws, hipStream_t s) {
+  using S = KspecShape<LOG2L>;
+  const float2* khat = at<const float2>(ws, p->off_khat);
+  float4* coef = at<float4>(ws, p->off_coef);
+  const float2* twL = at<const float2>(ws, p->off_twL);
+  const float2* twH = at<const float2>(ws, p->off_twH);
+  const float2* cs = at<const float2>(ws, p->off_cs);
+  if (Ktime)
+    kspec_kernel<LOG2L, true><<<p->H, S::NT, 0, s>>>(khat, Ktime, D, Kout, coef, twL, twH, cs);
+  else
+    kspec_kernel<LOG2L, false><<<p->H, S::NT, 0, s>>>(khat, Ktime, D, Kout, coef, twL, twH, cs);
+}
+
+template <int LOG2L>
+static void conv_launch(const s4dplr_plan* p, const float* u, float* y, unsigned char* ws,
+                        hipStream_t s) {
+  using S = ConvShape<LOG2L>;
+  const int rows = p->batch * p->H;
+  const int blocks = (rows + S::RPW - 1) / S::RPW;
+  conv_kernel<LOG2L><<<blocks, S::NTHR, 0, s>>>(u, y, at<const float4>(ws, p->off_coef),
+                                                at<const float2>(ws, p->off_twH),
+                                                at<const float2>(ws, p->off_cs), p->H, p->batch);
+}
+
+#define S4_DISPATCH_LOG2L(fn, ...)          \
+  switch (p->log2L) {                       \
+    case 1: fn<1>(__VA_ARGS__); break;      \
+    case 2: fn<2>(__VA_ARGS__); break;      \
+    case 3: fn<3>(__VA_ARGS__); break;      \
+    case 4: fn<4>(__VA_ARGS__); break;      \
+    case 5: fn<5>(__VA_ARGS__); break;      \
+    case 6: fn<6>(__VA_ARGS__); break;      \
+    case 7: fn<7>(__VA_ARGS__); break;      \
+    case 8: fn<8>(__VA_ARGS__); break;      \
+    case 9: fn<9>(__VA_ARGS__); break;      \
+    case 10: fn<10>(__VA_ARGS__); break;    \
+    case 11: fn<11>(__VA_ARGS__); break;    \
+    case 12: fn<12>(__VA_ARGS__); break;    \
+    case 13: fn<13>(__VA_ARGS__); break;    \
+    case 14: fn<14>(__VA_ARGS__); break;    \
+    default: return hipErrorInvalidValue;   \
+  }
+
+hipError_t launch_kspec(const s4dplr_plan* p, const float* Ktime, const float* D, float* Kout,
+                        unsigned char* ws, hipStream_t s) {
+  S4_DISPATCH_LOG2L(kspec_launch, p, Ktime, D, Kout, ws, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_conv(const s4dplr_plan* p, const float* u, float* y, unsigned char* ws,
+                       hipStream_t s) {
+  S4_DISPATCH_LOG2L(conv_launch, p, u, y, ws, s);
+  return hipGetLastError();
+}
+
+}  // namespace s4

@@ -1,0 +1,173 @@
+"""CPU tests of the C ABI: the library loads, exports every entry point the
+header declares, and rejects bad arguments with the documented status codes
+before touching any device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "s4dplr.h")
+LIB = os.path.join(ROOT, "structured_state_space_dplr_amd", "libs4dplr.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP, ERR_ALIAS = range(7)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from structured_state_space_dplr_amd.build import build
+        build()
+    import torch  # noqa: F401  (the HIP runtime the library shares)
+    L = ctypes.CDLL(LIB)
+    vp = ctypes.c_void_p
+    L.s4dplr_plan_create.argtypes = [ctypes.POINTER(vp), ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_uint]
+    L.s4dplr_plan_workspace_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t)]
+    L.s4dplr_plan_init.argtypes = [vp, vp, vp]
+    L.s4dplr_kernel_gen.argtypes = [vp] * 10
+    L.s4dplr_conv_fwd.argtypes = [vp] * 7
+    L.s4dplr_forward.argtypes = [vp] * 13
+    L.s4dplr_plan_destroy.argtypes = [vp]
+    L.s4dplr_status_string.restype = ctypes.c_char_p
+    return L
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(s4dplr_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["s4dplr_abi_version", "s4dplr_status_string", "s4dplr_plan_create",
+              "s4dplr_plan_workspace_bytes", "s4dplr_plan_init", "s4dplr_kernel_gen",
+              "s4dplr_conv_fwd", "s4dplr_forward", "s4dplr_plan_destroy",
+              "s4dplr_last_hip_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.s4dplr_abi_version() == 1
+    for s in range(7):
+        assert len(lib.s4dplr_status_string(s)) > 0
+    assert lib.s4dplr_status_string(99) == b"unknown status"
+
+
+def _create(lib, H, N, L, B, flags=0):
+    h = ctypes.c_void_p()
+    st = lib.s4dplr_plan_create(ctypes.byref(h), H, N, L, B, flags)
+    return st, h
+
+
+@pytest.mark.parametrize("H,N,L,B,flags,expect", [
+    (4, 16, 256, 2, 0, OK),
+    (1, 1, 2, 1, 0, OK),
+    (3, 256, 64, 5, 1, OK),
+    (1, 64, 16384, 1, 0, OK),
+    (0, 16, 256, 2, 0, ERR_SHAPE),
+    (4, 0, 256, 2, 0, ERR_SHAPE),
+    (4, 257, 256, 2, 0, ERR_SHAPE),
+    (4, 16, 255, 2, 0, ERR_SHAPE),
+    (4, 16, 1, 2, 0, ERR_SHAPE),
+    (4, 16, 131072, 2, 0, ERR_SHAPE),
+    (4, 16, 256, 0, 0, ERR_SHAPE),
+    (4096, 16, 65536, 16, 0, ERR_SHAPE),     # batch*H*L >= 2^31
+    (4, 16, 256, 2, 2, ERR_UNSUPPORTED),
+])
+def test_plan_create_validation(lib, H, N, L, B, flags, expect):
+    st, h = _create(lib, H, N, L, B, flags)
+    assert st == expect
+    if st == OK:
+        n = ctypes.c_size_t()
+        assert lib.s4dplr_plan_workspace_bytes(h, ctypes.byref(n)) == OK
+        assert n.value > 0 and n.value % 256 == 0
+        lib.s4dplr_plan_destroy(h)
+    else:
+        assert h.value is None
+
+
+def test_null_arguments(lib):
+    assert lib.s4dplr_plan_create(None, 4, 16, 256, 2, 0) == ERR_NULL
+    assert lib.s4dplr_plan_workspace_bytes(None, None) == ERR_NULL
+    st, h = _create(lib, 4, 16, 256, 2)
+    n = ctypes.c_size_t()
+    assert lib.s4dplr_plan_workspace_bytes(h, None) == ERR_NULL
+    lib.s4dplr_plan_workspace_bytes(h, ctypes.byref(n))
+    fake = 1 << 20          # an aligned, never-dereferenced address
+    ws = 1 << 30
+    # plan_init
+    assert lib.s4dplr_plan_init(None, ws, None) == ERR_NULL
+    assert lib.s4dplr_plan_init(h, None, None) == ERR_NULL
+    assert lib.s4dplr_plan_init(h, ws + 16, None) == ERR_WORKSPACE
+    # kernel_gen: lambda, P, Q, B, C, dt, K required except Q
+    args = [fake] * 7
+    for i in [0, 1, 3, 4, 5, 6]:
+        a = list(args)
+        a[i] = None
+        assert lib.s4dplr_kernel_gen(h, *a, ws, None) == ERR_NULL
+    assert lib.s4dplr_kernel_gen(h, *args, None, None) == ERR_NULL
+    assert lib.s4dplr_kernel_gen(h, *args, ws + 8, None) == ERR_WORKSPACE
+    # conv_fwd: u, K, y required; D optional
+    assert lib.s4dplr_conv_fwd(h, None, fake, None, fake + 4096, ws, None) == ERR_NULL
+    assert lib.s4dplr_conv_fwd(h, fake, None, None, fake + 4096, ws, None) == ERR_NULL
+    assert lib.s4dplr_conv_fwd(h, fake, fake, None, None, ws, None) == ERR_NULL
+    # forward: K and D optional
+    assert lib.s4dplr_forward(h, None, fake, None, fake, fake, fake, None, fake, None, fake, ws, None) == ERR_NULL
+    assert lib.s4dplr_forward(h, fake, fake, None, fake, fake, fake, None, None, None, fake, ws, None) == ERR_NULL
+    lib.s4dplr_plan_destroy(h)
+    lib.s4dplr_plan_destroy(None)
+
+
+def test_diagonal_plan_needs_no_P(lib):
+    st, h = _create(lib, 2, 8, 64, 1, flags=1)
+    assert st == OK
+    ws = 1 << 30
+    # P missing is fine for the diagonal flag; the remaining NULL checks still apply
+    assert lib.s4dplr_kernel_gen(h, None, None, None, 1 << 20, 1 << 20, 1 << 20, 1 << 21, ws, None) == ERR_NULL
+    st2, h2 = _create(lib, 2, 8, 64, 1, flags=0)
+    assert lib.s4dplr_kernel_gen(h2, 1 << 20, None, None, 1 << 20, 1 << 20, 1 << 20, 1 << 21, ws, None) == ERR_NULL
+    lib.s4dplr_plan_destroy(h)
+    lib.s4dplr_plan_destroy(h2)
+
+
+def test_aliasing_is_rejected_before_launch(lib):
+    H, N, L, B = 4, 16, 256, 2
+    st, h = _create(lib, H, N, L, B)
+    n = ctypes.c_size_t()
+    lib.s4dplr_plan_workspace_bytes(h, ctypes.byref(n))
+    ws = 1 << 32
+    u = 1 << 24
+    ub = 4 * B * H * L
+    K = u + 4 * ub
+    # y == u, y overlapping the tail of u, y overlapping K, y inside the workspace
+    for y in (u, u + ub - 4, K, ws + 256):
+        assert lib.s4dplr_conv_fwd(h, u, K, None, y, ws, None) == ERR_ALIAS
+    # forward: y over u; K over y; K inside the workspace
+    y = K + 4 * 4 * H * L
+    assert lib.s4dplr_forward(h, 1, 1, None, 1, 1, 1, None, u, None, u, ws, None) == ERR_ALIAS
+    assert lib.s4dplr_forward(h, 1, 1, None, 1, 1, 1, None, u, y, y, ws, None) == ERR_ALIAS
+    assert lib.s4dplr_forward(h, 1, 1, None, 1, 1, 1, None, u, ws, y, ws, None) == ERR_ALIAS
+    assert lib.s4dplr_kernel_gen(h, 1, 1, None, 1, 1, 1, ws + 512, ws, None) == ERR_ALIAS
+    lib.s4dplr_plan_destroy(h)
+
+
+def test_hip_error_is_reported_without_a_device(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; the no-device error path cannot be forced")
+    st, h = _create(lib, 4, 16, 256, 2)
+    assert lib.s4dplr_plan_init(h, 1 << 30, None) == ERR_HIP
+    assert lib.s4dplr_last_hip_error() != 0
+    lib.s4dplr_plan_destroy(h)

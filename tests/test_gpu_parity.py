@@ -1,0 +1,194 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.  Gate: max|gpu - oracle| / max|oracle| <= 1e-4 for both
+the kernel K and the output y, the tolerance the task sets for fp32 against
+fp64 (the derivation of the expected fp32 error is in the design notes)."""
+import numpy as np
+import pytest
+
+import oracle as o
+from synth import WORKLOADS, make_generic_inputs, make_inputs
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def s4():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import structured_state_space_dplr_amd as s4
+    return s4
+
+
+def _dev(a):
+    import torch
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _rel(gpu, ref):
+    return float(np.abs(gpu.astype(np.float64) - ref).max() / max(np.abs(ref).max(), 1e-300))
+
+
+def run_forward(s4, x, diagonal=False, with_D=True, write_K=True, stream=None):
+    import torch
+    H, N = x["lam"].shape[:2]
+    batch, _, L = x["u"].shape
+    plan = s4.Plan(H, N, L, batch, diagonal=diagonal)
+    ws = plan.workspace(stream)
+    t = {k: _dev(x[k]) for k in ("lam", "P", "Q", "B", "C", "dt", "D", "u")}
+    if not with_D:
+        t["D"] = None
+    K = torch.empty((H, L), dtype=torch.float32, device="cuda") if write_K else None
+    y = torch.empty((batch, H, L), dtype=torch.float32, device="cuda")
+    s4.forward(plan, t["lam"], None if diagonal else t["P"], t["Q"], t["B"], t["C"], t["dt"],
+               t["D"], t["u"], K, y, ws, stream)
+    torch.cuda.synchronize()
+    out = (None if K is None else K.cpu().numpy(), y.cpu().numpy())
+    plan.close()
+    return out
+
+
+def oracle_forward(x, diagonal=False, with_D=True):
+    D = x["D"] if with_D else np.zeros_like(x["D"])
+    return o.forward(x["lam"], x["P"], x["Q"], x["B"], x["C"], x["dt"], D, x["u"],
+                     method="cauchy", diagonal=diagonal)
+
+
+# ---- the five workloads at their full sizes --------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "long", "s4d_lin"])
+def test_workload_parity(s4, name):
+    w = WORKLOADS[name]
+    print(f"case: workload {w.describe()}", flush=True)
+    x = make_inputs(name)
+    K, y = run_forward(s4, x, diagonal=w.diagonal)
+    Kr, yr = oracle_forward(x, diagonal=w.diagonal)
+    eK, ey = _rel(K, Kr), _rel(y, yr)
+    print(f"  rel err K {eK:.3e}  y {ey:.3e}", flush=True)
+    assert eK <= TOL and ey <= TOL
+    # the plain definitions on a sample: dense aliased kernel on two channels,
+    # the direct causal sum at a few output samples
+    rng = np.random.default_rng(0)
+    lam = x["lam"][..., 0].astype(np.float64) + 1j * x["lam"][..., 1]
+    B = x["B"][..., 0].astype(np.float64) + 1j * x["B"][..., 1]
+    C = x["C"][..., 0].astype(np.float64) + 1j * x["C"][..., 1]
+    P = np.zeros_like(lam) if w.diagonal else x["P"][..., 0].astype(np.float64) + 1j * x["P"][..., 1]
+    for h in rng.choice(w.H, size=2, replace=False):
+        A = o.dense_state_matrix(lam[h], P[h], P[h])
+        Abar, Bbar = o.discretize_bilinear(A, B[h], float(x["dt"][h]))
+        Kd = o.kernel_aliased_dense(Abar, Bbar, C[h], w.L)
+        assert _rel(K[h], Kd) <= TOL
+    for _ in range(6):
+        b, h, t = rng.integers(w.batch), rng.integers(w.H), rng.integers(w.L)
+        ref = o.conv_direct_at(x["u"][b, h], Kr[h], float(x["D"][h]), int(t))
+        assert abs(y[b, h, t] - ref) <= TOL * np.abs(yr).max()
+
+
+# ---- every sequence length, generic DPLR parameters ------------------------
+
+@pytest.mark.parametrize("L", [2 ** k for k in range(1, 15)])
+def test_all_lengths_generic(s4, L):
+    print(f"case: generic H=3 N=8 L={L} batch=2", flush=True)
+    x = make_generic_inputs(H=3, N=8, L=L, batch=2, seed=L)
+    K, y = run_forward(s4, x)
+    Kr, yr = oracle_forward(x)
+    assert _rel(K, Kr) <= TOL and _rel(y, yr) <= TOL
+
+
+@pytest.mark.parametrize("L", [2, 16, 256, 4096])
+def test_diagonal_generic(s4, L):
+    print(f"case: diagonal generic L={L}", flush=True)
+    x = make_generic_inputs(H=5, N=16, L=L, batch=3, seed=7, diagonal=True)
+    K, y = run_forward(s4, x, diagonal=True)
+    Kr, yr = oracle_forward(x, diagonal=True)
+    assert _rel(K, Kr) <= TOL and _rel(y, yr) <= TOL
+
+
+def test_distinct_q(s4):
+    x = make_generic_inputs(H=4, N=16, L=512, batch=2, seed=11, distinct_q=True)
+    K, y = run_forward(s4, x)
+    Kr, yr = oracle_forward(x)
+    assert _rel(K, Kr) <= TOL and _rel(y, yr) <= TOL
+
+
+def test_no_D_and_no_K_output(s4):
+    x = make_generic_inputs(H=2, N=8, L=1024, batch=3, seed=12)
+    K, y = run_forward(s4, x, with_D=False, write_K=False)
+    assert K is None
+    _, yr = oracle_forward(x, with_D=False)
+    assert _rel(y, yr) <= TOL
+
+
+def test_single_channel_single_row_many_poles(s4):
+    x = make_generic_inputs(H=1, N=256, L=2048, batch=1, seed=13)
+    K, y = run_forward(s4, x)
+    Kr, yr = oracle_forward(x)
+    assert _rel(K, Kr) <= TOL and _rel(y, yr) <= TOL
+
+
+# ---- the two halves separately ---------------------------------------------
+
+@pytest.mark.parametrize("L", [2, 8, 64, 1024, 16384])
+def test_conv_fwd_random_kernel(s4, L):
+    import torch
+    print(f"case: conv_fwd random K L={L}", flush=True)
+    rng = np.random.default_rng(L + 1)
+    H, batch = 3, 2
+    u = rng.standard_normal((batch, H, L)).astype(np.float32)
+    K = (rng.standard_normal((H, L)) * np.exp(-np.arange(L) / (L / 4))).astype(np.float32)
+    D = rng.standard_normal(H).astype(np.float32)
+    plan = s4.Plan(H, 4, L, batch)
+    ws = plan.workspace()
+    y = torch.empty((batch, H, L), dtype=torch.float32, device="cuda")
+    s4.conv_fwd(plan, _dev(u), _dev(K), _dev(D), y, ws)
+    torch.cuda.synchronize()
+    yr = o.conv_fft(u, K[None], D[None, :, None])
+    assert _rel(y.cpu().numpy(), yr) <= TOL
+    plan.close()
+
+
+def test_kernel_gen_matches_forward_kernel(s4):
+    import torch
+    x = make_inputs("tiny")
+    plan = s4.Plan(4, 16, 256, 2)
+    ws = plan.workspace()
+    K = torch.empty((4, 256), dtype=torch.float32, device="cuda")
+    s4.kernel_gen(plan, _dev(x["lam"]), _dev(x["P"]), None, _dev(x["B"]), _dev(x["C"]),
+                  _dev(x["dt"]), K, ws)
+    torch.cuda.synchronize()
+    Kf, _ = run_forward(s4, x)
+    assert np.array_equal(K.cpu().numpy(), Kf)
+    plan.close()
+
+
+# ---- determinism and streams -------------------------------------------------
+
+def test_bitwise_repeatable_and_nondefault_stream(s4):
+    import torch
+    x = make_inputs("mid", H=32, batch=4)
+    K1, y1 = run_forward(s4, x)
+    K2, y2 = run_forward(s4, x)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        K3, y3 = run_forward(s4, x, stream=s)
+    assert np.array_equal(K1, K2) and np.array_equal(y1, y2)
+    assert np.array_equal(K1, K3) and np.array_equal(y1, y3)
+
+
+def test_workspace_reuse_across_calls(s4):
+    import torch
+    x1 = make_generic_inputs(H=4, N=8, L=512, batch=2, seed=21)
+    x2 = make_generic_inputs(H=4, N=8, L=512, batch=2, seed=22)
+    plan = s4.Plan(4, 8, 512, 2)
+    ws = plan.workspace()
+    outs = []
+    for x in (x1, x2, x1):
+        y = torch.empty((2, 4, 512), dtype=torch.float32, device="cuda")
+        t = {k: _dev(x[k]) for k in ("lam", "P", "B", "C", "dt", "D", "u")}
+        s4.forward(plan, t["lam"], t["P"], None, t["B"], t["C"], t["dt"], t["D"], t["u"], None, y, ws)
+        torch.cuda.synchronize()
+        outs.append(y.cpu().numpy())
+    assert np.array_equal(outs[0], outs[2])
+    assert _rel(outs[1], oracle_forward(x2)[1]) <= TOL
+    plan.close()
