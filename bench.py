@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Throughput of the S4 DPLR convolution-mode forward pass on one MI355X.
+
+One step = one call of the library's fused forward entry point over one batch
+of synthetic input: pole packing, the Cauchy/Woodbury kernel generation, the
+kernel spectrum (inverse FFT to K, which is written out, and the zero-padded
+2L spectrum) and the causal FFT convolution with the D skip, y = K * u + D u.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mid]
+
+Inputs are resident in HBM before the timed region.  The timed steps rotate
+over several input/output buffer sets whose total exceeds 512 MB so that the
+256 MB last-level cache does not hold a step's data from the previous step.
+After the K timed steps the two stages are timed separately with HIP events
+on the launch stream: kernel generation alone, and the convolution kernel
+alone (``conv_apply``: one launch of the convolution kernel per step) -- the
+latter gives the roofline figure.  The CPU baseline runs the fp64 oracle on
+the host (one thread) on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "S4 conv fwd samples/s (B·H·L/s) + Cauchy kernel-gen GFLOP/s vs fp32 peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector, published (packed issue)
+FP32_UNPACKED_TFLOPS = 78.6    # 256 CU x 4 SIMD x 16 lanes x 2 flop (FMA) x 2.4 GHz
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv_traffic.json")
+KERNEL_SOURCES = ["kernels.hip", "device_fft.h", "fft_sched.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "structured_state_space_dplr_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_counts(w):
+    """Algorithmic work of one forward pass (not the work the method avoids).
+
+    F1: Cauchy stage flops, H*L*N*(8 + 8*S) with S = 4 sums (DPLR) or 1
+        (diagonal): 8 flops per complex reciprocal, 8 per complex
+        multiply-accumulate.
+    Q2: convolution bytes, 4 B*H*L (read u) + 4 B*H*L (write y) + 4 H*L
+        (the kernel) + 4 H (D).
+    """
+    S = 1 if w.diagonal else 4
+    F1 = w.H * w.L * w.N * (8 + 8 * S)
+    Q2 = 8 * w.batch * w.H * w.L + 4 * w.H * w.L + 4 * w.H
+    return F1, Q2
+
+
+def read_traffic(workload_name: str):
+    """HBM bytes per convolution launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload_name or t.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(x, K_gpu, y_gpu, min_seconds: float):
+    """The fp64 oracle (the pages' Cauchy/Woodbury method and an fp64 FFT
+    convolution) on the whole workload, one BLAS thread, repeated until
+    `min_seconds` of CPU work; also the GPU result's error against it."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    w = x["workload"]
+    times = []
+    with threadpool_limits(1):
+        t_start = time.perf_counter()
+        while True:
+            t0 = time.perf_counter()
+            K, y = oracle.forward(x["lam"], x["P"], x["Q"], x["B"], x["C"], x["dt"], x["D"],
+                                  x["u"], method="cauchy", diagonal=w.diagonal)
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() - t_start >= min_seconds and len(times) >= 3:
+                break
+    t = statistics.median(times)
+    samples = w.batch * w.H * w.L
+    eK = float(np.abs(K_gpu - K).max() / np.abs(K).max())
+    ey = float(np.abs(y_gpu - y).max() / np.abs(y).max())
+    return {
+        "value": samples / t, "unit": "samples/s", "cores": 1, "kind": "oracle",
+        "sample": (f"whole {w.name} workload (H={w.H}, N={w.N}, L={w.L}, batch={w.batch}), "
+                   f"fp64 NumPy oracle: Cauchy/Woodbury kernel + rfft convolution; "
+                   f"median of {len(times)} runs, 1 thread"),
+        "seconds_per_forward": t,
+    }, {"K_max_rel_err": eK, "y_max_rel_err": ey, "tolerance": 1e-4,
+        "reference": "fp64 oracle, same seeded inputs"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mid",
+                    help="tiny | mid | long | s4d_lin | waveform (default: mid)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration runs)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported: the channels shard across GPUs with no exchange, so the figure of "
+              "interest is the one-GPU throughput at the full workload shape.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import structured_state_space_dplr_amd as s4
+    from synth import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        return 1
+    w = WORKLOADS[args.workload]
+    log(f"[bench] workload {w.describe()}; generating inputs")
+    x = make_inputs(w.name)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def g(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    params = {k: g(x[k]) for k in ("lam", "P", "Q", "B", "C", "dt", "D")}
+    u0 = g(x["u"])
+    row_bytes = 4 * w.batch * w.H * w.L
+    nsets = max(2, -(-(512 << 20) // (2 * row_bytes)) + 1)
+    us = [u0] + [u0.clone() for _ in range(nsets - 1)]
+    ys = [torch.empty_like(u0) for _ in range(nsets)]
+    K = torch.empty((w.H, w.L), dtype=torch.float32, device=dev)
+    plan = s4.Plan(w.H, w.N, w.L, w.batch, diagonal=w.diagonal, device=dev)
+    ws = plan.workspace()
+    stream = torch.cuda.current_stream()
+    P = None if w.diagonal else params["P"]
+
+    def step(i):
+        s4.forward(plan, params["lam"], P, params["Q"], params["B"], params["C"], params["dt"],
+                   params["D"], us[i % nsets], K, ys[i % nsets], ws, stream)
+
+    log(f"[bench] {nsets} buffer sets of {2 * row_bytes / 2**20:.1f} MiB; warmup {args.warmup}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # ---- timed region: exactly K forward steps ---------------------------------
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms_events = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = 1e3 * wall / args.steps
+    samples = w.batch * w.H * w.L
+    value = samples / (wall / args.steps)
+    log(f"[bench] forward: {ms_per_step * 1e3:.1f} us/step (events {fwd_ms_events * 1e3:.1f} us)")
+
+    # keep the first set's outputs for the parity check against the oracle
+    step(0)
+    torch.cuda.synchronize()
+    K_gpu = K.cpu().numpy().astype(np.float64)
+    y_gpu = ys[0].cpu().numpy().astype(np.float64)
+
+    # ---- stage 1 alone: kernel generation (pack, Cauchy, kernel spectrum) ------
+    def timed(fn, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(n):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e-3       # seconds per call
+
+    t_gen = timed(lambda i: s4.kernel_gen(plan, params["lam"], P, params["Q"], params["B"],
+                                          params["C"], params["dt"], K, ws, stream), args.steps)
+    # ---- stage 2 alone: one convolution-kernel launch per call ------------------
+    step(0)    # leaves the spectrum of this layer (with D) in the workspace
+    t_conv = timed(lambda i: s4.conv_apply(plan, us[i % nsets], ys[i % nsets], ws, stream),
+                   args.steps)
+    F1, Q2 = algorithmic_counts(w)
+    log(f"[bench] kernel_gen {t_gen * 1e6:.1f} us ({F1 / t_gen / 1e9:.0f} GFLOP/s), "
+        f"conv {t_conv * 1e6:.1f} us ({Q2 / t_conv / 1e9:.0f} GB/s)")
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 5 copies of 1 GiB done")
+
+    traffic = read_traffic(w.name)
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "samples/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "H": w.H, "N": w.N, "L": w.L, "batch": w.batch,
+                   "init": w.init, "u": w.u_kind, "seed": 0},
+        "roofline": {
+            "kernel": "conv_kernel (fused causal FFT convolution, one launch per step)",
+            "bound": "hbm",
+            "achieved": Q2 / t_conv / 1e9,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": Q2 / t_conv / 1e9 / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": Q2,
+            "launch_us": t_conv * 1e6,
+        },
+        "kernel_gen": {
+            "us": t_gen * 1e6,
+            "gflops": F1 / t_gen / 1e9,
+            "frac_fp32_peak": F1 / t_gen / 1e12 / FP32_PEAK_TFLOPS,
+            "frac_fp32_unpacked_peak": F1 / t_gen / 1e12 / FP32_UNPACKED_TFLOPS,
+            "algorithmic_flops": F1,
+            "note": "pack + Cauchy/Woodbury + kernel spectrum; flops counted for the Cauchy sums",
+        },
+        "forward_us_events": fwd_ms_events * 1e3,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU baseline: fp64 oracle, >= {args.cpu_seconds:.0f} s")
+        cb, parity = cpu_baseline(x, K_gpu, y_gpu, args.cpu_seconds)
+        result["cpu_baseline"] = cb
+        result["parity"] = parity
+        log(f"[bench] oracle {cb['value']:.3g} samples/s; parity K {parity['K_max_rel_err']:.2e} "
+            f"y {parity['y_max_rel_err']:.2e}")
+    plan.close()
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

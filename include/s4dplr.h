@@ -141,6 +141,20 @@ s4dplr_status s4dplr_forward(const s4dplr_plan* plan, const float* lambda, const
                              const float* D, const float* u, float* K, float* y, void* ws,
                              hipStream_t stream);
 
+/*
+ * Apply the convolution with the kernel spectrum already in the workspace:
+ * y = K * u + D u for the K and D of the most recent s4dplr_kernel_gen
+ * (which uses D = 0), s4dplr_conv_fwd or s4dplr_forward call made with this
+ * plan on this workspace and stream order.  For running one layer's kernel
+ * over several input batches without generating it again ("The S4 kernel,
+ * from scratch", section 5: the kernel is computed once and applied as one
+ * long convolution).  Without such a prior call the results are unspecified
+ * (every access stays inside the workspace).  u, y: [batch][H][L].
+ * Errors: ERR_NULL, ERR_ALIAS, ERR_WORKSPACE, ERR_HIP.
+ */
+s4dplr_status s4dplr_conv_apply(const s4dplr_plan* plan, const float* u, float* y, void* ws,
+                                hipStream_t stream);
+
 /* Release a plan (NULL is ignored).  Host-only. */
 void s4dplr_plan_destroy(s4dplr_plan* plan);
 

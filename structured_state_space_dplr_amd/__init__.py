@@ -19,7 +19,7 @@ import torch  # loads the HIP runtime that libs4dplr then shares
 __all__ = [
     "S4DPLRError", "DIAGONAL", "abi_version", "status_string", "plan_create",
     "plan_workspace_bytes", "plan_init", "kernel_gen", "conv_fwd", "forward",
-    "plan_destroy", "Plan", "LIB_PATH",
+    "conv_apply", "plan_destroy", "Plan", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libs4dplr.so")
@@ -27,7 +27,7 @@ DIAGONAL = 1
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m structured_state_space_dplr_amd.build` "
+        f"{LIB_PATH} is not built; run `python structured_state_space_dplr_amd/build.py` "
         "(or __graft_entry__.build()) first")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -52,6 +52,8 @@ _lib.s4dplr_conv_fwd.restype = ctypes.c_int
 _lib.s4dplr_conv_fwd.argtypes = [_p] * 7
 _lib.s4dplr_forward.restype = ctypes.c_int
 _lib.s4dplr_forward.argtypes = [_p] * 13
+_lib.s4dplr_conv_apply.restype = ctypes.c_int
+_lib.s4dplr_conv_apply.argtypes = [_p] * 5
 _lib.s4dplr_plan_destroy.restype = None
 _lib.s4dplr_plan_destroy.argtypes = [_p]
 
@@ -151,6 +153,13 @@ def forward(plan: "Plan | int", lam, P, Q, B, C, dt, D, u, K, y, ws, stream=None
         _ptr(C, "C", cplx), _ptr(dt, "dt", (H,)), _ptr(D, "D", (H,)),
         _ptr(u, "u", (batch, H, L)), _ptr(K, "K", (H, L)), _ptr(y, "y", (batch, H, L)),
         _ws_ptr(ws), _stream(stream)), "forward")
+
+
+def conv_apply(plan: "Plan | int", u, y, ws, stream=None) -> None:
+    p, (H, N, L, batch) = _dims(plan)
+    _check(_lib.s4dplr_conv_apply(
+        p, _ptr(u, "u", (batch, H, L)), _ptr(y, "y", (batch, H, L)), _ws_ptr(ws),
+        _stream(stream)), "conv_apply")
 
 
 def _dims(plan):

@@ -1,6 +1,8 @@
 """Build libs4dplr.so in-tree with hipcc for gfx950.
 
-    python -m structured_state_space_dplr_amd.build
+    python structured_state_space_dplr_amd/build.py
+
+(run as a file so that the stale library is not loaded by the package import)
 """
 from __future__ import annotations
 

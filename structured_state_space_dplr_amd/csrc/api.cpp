@@ -93,6 +93,7 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
   if (!p) return S4DPLR_ERR_SHAPE;
   p->H = H;
   p->N = N;
+  p->NP = (N + 3) / 4 * 4;
   p->L = L;
   p->log2L = log2L;
   p->batch = batch;
@@ -112,7 +113,7 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
   p->tables_bytes = off;
   // Scratch region.
   p->off_poles = off;
-  off = align_up(off + sizeof(float) * 12 * (size_t)H * N);
+  off = align_up(off + sizeof(float) * 12 * (size_t)H * p->NP);
   p->off_chan = off;
   off = align_up(off + sizeof(float) * 4 * (size_t)H);
   p->off_khat = off;
@@ -222,6 +223,18 @@ s4dplr_status s4dplr_forward(const s4dplr_plan* p, const float* lambda, const fl
   if ((e = s4::launch_cauchy(p, w, stream)) != hipSuccess) return hip_fail(e);
   if ((e = s4::launch_kspec(p, nullptr, D, K, w, stream)) != hipSuccess) return hip_fail(e);
   if ((e = s4::launch_conv(p, u, y, w, stream)) != hipSuccess) return hip_fail(e);
+  return S4DPLR_OK;
+}
+
+s4dplr_status s4dplr_conv_apply(const s4dplr_plan* p, const float* u, float* y, void* ws,
+                                hipStream_t stream) {
+  if (!valid_plan(p)) return S4DPLR_ERR_NULL;
+  if (!u || !y) return S4DPLR_ERR_NULL;
+  if (s4dplr_status st = check_ws(ws)) return st;
+  const size_t ub = sizeof(float) * (size_t)p->batch * p->H * p->L;
+  if (overlaps(y, ub, u, ub) || overlaps(y, ub, ws, p->total)) return S4DPLR_ERR_ALIAS;
+  hipError_t e = s4::launch_conv(p, u, y, static_cast<unsigned char*>(ws), stream);
+  if (e != hipSuccess) return hip_fail(e);
   return S4DPLR_OK;
 }
 

@@ -144,6 +144,102 @@ __device__ __forceinline__ void lds_fft(float2* __restrict__ buf, int lt, bool o
   if constexpr (LOG2N > 0) FftPass<LOG2N, 0, INV>::run(buf, lt, on, tw);
 }
 
+// ---------------------------------------------------------------------------
+// Wave-resident transforms: a transform of M = 2^LOG2M points (32 <= M <=
+// 1024) is held by T = M/16 lanes of one wavefront, 16 points per lane, and
+// the passes exchange data through a wave-private LDS region, so only
+// wave-level ordering is needed between passes (no workgroup barrier).
+// ---------------------------------------------------------------------------
+
+// pad(x + c) - pad(x) for a compile-time c: exactly c + c/16 when c is a
+// multiple of 16; otherwise computed from x.
+__device__ __forceinline__ int pad_shift(int x, int c) {
+  if ((c & 15) == 0) return c + (c >> 4);
+  return lds_pad(x + c) - lds_pad(x);
+}
+
+// Orders this wave's LDS accesses before and after the call.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int LOG2M, int P>
+struct WPass {
+  static constexpr int M = 1 << LOG2M;
+  static constexpr int T = M / 16;
+  static constexpr int RL = fft_radix_log(LOG2M, P);
+  static constexpr int R = 1 << RL;
+  static constexpr int NB = 16 / R;
+  static constexpr int NSL = fft_ns_log(LOG2M, P);
+  static constexpr int NS = 1 << NSL;
+  static constexpr int STRIDE = M / R;
+  static constexpr int TWOFF = fft_tw_offset(LOG2M, P);
+
+  // v[q*R + r] = x[j + r*STRIDE], j = lt + q*T
+  static __device__ __forceinline__ void load(float2 (&v)[16], const float2* __restrict__ buf, int lt) {
+    const float2* __restrict__ b0 = buf + lds_pad(lt);
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+#pragma unroll
+      for (int r = 0; r < R; ++r) v[q * R + r] = b0[pad_shift(lt, q * T + r * STRIDE)];
+  }
+  // this pass's twiddles for the lane (entries r = 0 are 1 and unused)
+  static __device__ __forceinline__ void load_tw(float2 (&w)[16], const float2* __restrict__ tw, int lt) {
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int k = (lt + q * T) & (NS - 1);
+      const float4* t4 = reinterpret_cast<const float4*>(tw + TWOFF + k * R);
+#pragma unroll
+      for (int r2 = 0; r2 < R / 2; ++r2) {
+        const float4 x = t4[r2];
+        w[q * R + 2 * r2] = make_float2(x.x, x.y);
+        w[q * R + 2 * r2 + 1] = make_float2(x.z, x.w);
+      }
+    }
+  }
+  template <bool INV>
+  static __device__ __forceinline__ void compute(float2 (&v)[16], const float2 (&w)[16]) {
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      if constexpr (NS > 1) {
+#pragma unroll
+        for (int r = 1; r < R; ++r) v[q * R + r] = cmulw<INV>(v[q * R + r], w[q * R + r]);
+      }
+      dft_dif<R, INV>(&v[q * R]);
+    }
+  }
+  // y[base(j) + s*NS] = X_s of butterfly j (X_s sits in v[q*R + bitrev(s)]).
+  // base is a multiple of 16 when NS = 1 and s*NS is one when NS >= 16, so
+  // pad(base + s*NS) = pad(base) + s*NS + (s*NS >> 4) in both cases.
+  static __device__ __forceinline__ void store(const float2 (&v)[16], float2* __restrict__ buf, int lt) {
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int j = lt + q * T;
+      const int k = j & (NS - 1);
+      const int base = ((j >> NSL) << (NSL + RL)) + k;
+      float2* __restrict__ b0 = buf + lds_pad(base);
+#pragma unroll
+      for (int s = 0; s < R; ++s) b0[s * NS + ((s * NS) >> 4)] = v[q * R + bitrev<RL>(s)];
+    }
+  }
+};
+
+// First forward pass (radix 16, span 1) when the upper half of the input is
+// zero: the first DIF stage reduces to v[i+8] = v[i] W_16^i.
+__device__ __forceinline__ void dft16_fwd_half_input(float2 (&v)[16]) {
+  v[8] = v[0];
+  v[9] = rot16<1, false>(v[1]);
+  v[10] = rot16<2, false>(v[2]);
+  v[11] = rot16<3, false>(v[3]);
+  v[12] = rot16<4, false>(v[4]);
+  v[13] = rot16<5, false>(v[5]);
+  v[14] = rot16<6, false>(v[6]);
+  v[15] = rot16<7, false>(v[7]);
+  dif_all<16, 4, false>(v);   // the remaining stages over all 16 points
+}
+
 // Blocks are placed on the 8 XCDs round-robin by block id.  Map block ids to
 // logical tiles so that each XCD gets one contiguous range of tiles, which
 // keeps the rows of one channel (sharing its spectrum) in one L2.

@@ -14,7 +14,7 @@
 #define S4DPLR_LDS_MAX_LOG2L 14
 
 struct s4dplr_plan {
-  int H, N, L, log2L, batch;
+  int H, N, NP, L, log2L, batch;   // NP: N rounded up to the Cauchy loop unroll (4)
   unsigned flags;
   // Workspace layout, byte offsets from the 256-byte aligned base.
   size_t off_tan;    // [L] float: tan(pi l / L), 0 at l = L/2
@@ -23,10 +23,10 @@ struct s4dplr_plan {
   size_t off_twH;    // FFT twiddles for transforms of L/2 points
   size_t off_tw4;    // multi-pass path: four-step twiddles (0 bytes otherwise)
   size_t tables_bytes;
-  size_t off_poles;  // [H][N][3] float4 packed pole records
+  size_t off_poles;  // [H][NP][3] float4 packed pole records
   size_t off_chan;   // [H] float4: (2/dt, (dt/2) sum C B re, im, 0)
   size_t off_khat;   // [H][L] float2: generating function at the roots of unity
-  size_t off_coef;   // [H][2][L/2] float4: spectral weights (alpha, beta) per bin
+  size_t off_coef;   // [H][L] float4: spectral weights (alpha, beta) of bin j
   size_t off_big;    // multi-pass path: [batch*H][L] float2 intermediate (0 bytes otherwise)
   size_t total;
   std::vector<unsigned char> tables;  // exact bytes of the table region

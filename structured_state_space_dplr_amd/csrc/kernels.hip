@@ -39,27 +39,45 @@ namespace s4 {
 // ---------------------------------------------------------------------------
 // Stage 1a: pack pole records and channel constants
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void pack_kernel(
+// One wave per channel.  Pole records are padded to a multiple of
+// kPoleUnroll with inert poles (zero weights, Lambda = -1) so that the Cauchy
+// loop runs in whole unrolled blocks.
+constexpr int kPoleUnroll = 4;
+
+__global__ __launch_bounds__(64) void pack_kernel(
     const float2* __restrict__ lam, const float2* __restrict__ P, const float2* __restrict__ Q,
     const float2* __restrict__ B, const float2* __restrict__ C, const float* __restrict__ dt,
-    float4* __restrict__ poles, float4* __restrict__ chan, int H, int N, int diag) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx < H * N) {
-    const float2 l = lam[idx], b = B[idx], c = C[idx];
-    const float2 p = diag ? make_float2(0.f, 0.f) : P[idx];
-    const float2 q = diag ? make_float2(0.f, 0.f) : (Q ? Q[idx] : p);
-    const float2 w00 = cmul(c, b), w01 = cmul(c, p);
-    const float2 w10 = cmul(cconj(q), b), w11 = cmul(cconj(q), p);
-    poles[3 * idx + 0] = make_float4(l.y, l.x * l.x, -l.x, 0.f);
-    poles[3 * idx + 1] = make_float4(w00.x, w00.y, w01.x, w01.y);
-    poles[3 * idx + 2] = make_float4(w10.x, w10.y, w11.x, w11.y);
+    float4* __restrict__ poles, float4* __restrict__ chan, int N, int NP, int diag) {
+  const int h = blockIdx.x, lane = threadIdx.x;
+  float2 s = make_float2(0.f, 0.f);
+  for (int n = lane; n < NP; n += 64) {
+    float4* rec = poles + 3 * ((size_t)h * NP + n);
+    if (n < N) {
+      const size_t idx = (size_t)h * N + n;
+      const float2 l = lam[idx], b = B[idx], c = C[idx];
+      const float2 p = diag ? make_float2(0.f, 0.f) : P[idx];
+      const float2 q = diag ? make_float2(0.f, 0.f) : (Q ? Q[idx] : p);
+      const float2 w00 = cmul(c, b), w01 = cmul(c, p);
+      const float2 w10 = cmul(cconj(q), b), w11 = cmul(cconj(q), p);
+      rec[0] = make_float4(l.y, l.x * l.x, -l.x, 0.f);
+      rec[1] = make_float4(w00.x, w00.y, w01.x, w01.y);
+      rec[2] = make_float4(w10.x, w10.y, w11.x, w11.y);
+      s = cadd(s, w00);
+    } else {
+      rec[0] = make_float4(0.f, 1.f, 1.f, 0.f);
+      rec[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      rec[2] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   }
-  if (idx < H) {
-    const float d = dt[idx];
-    float2 s = make_float2(0.f, 0.f);
-    for (int n = 0; n < N; ++n) s = cadd(s, cmul(C[idx * N + n], B[idx * N + n]));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    s.x += __shfl_xor(s.x, off);
+    s.y += __shfl_xor(s.y, off);
+  }
+  if (lane == 0) {
+    const float d = dt[h];
     // limit of the generating function at z = -1: (dt/2) sum_n C_n B_n
-    chan[idx] = make_float4(2.0f / d, 0.5f * d * s.x, 0.5f * d * s.y, 0.f);
+    chan[h] = make_float4(2.0f / d, 0.5f * d * s.x, 0.5f * d * s.y, 0.f);
   }
 }
 
@@ -75,10 +93,10 @@ constexpr int kCauchyThreads = 256;
 template <int F, bool DIAG>
 __global__ __launch_bounds__(kCauchyThreads) void cauchy_kernel(
     const float4* __restrict__ poles, const float4* __restrict__ chan,
-    const float* __restrict__ tanT, float2* __restrict__ khat, int N, int L) {
+    const float* __restrict__ tanT, float2* __restrict__ khat, int NP, int L) {
   const int h = blockIdx.y;
   const float4 ch = chan[h];
-  const float4* __restrict__ pr = poles + (size_t)h * N * 3;
+  const float4* __restrict__ pr = poles + (size_t)h * NP * 3;
   int l[F];
   float T[F], G[F];
   float acc[F][8];
@@ -90,7 +108,9 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_kernel(
 #pragma unroll
     for (int a = 0; a < 8; ++a) acc[f][a] = 0.f;
   }
-  for (int n = 0; n < N; ++n) {
+  for (int n0 = 0; n0 < NP; n0 += kPoleUnroll) {
+#pragma unroll
+  for (int n = n0; n < n0 + kPoleUnroll; ++n) {
     const float4 p0 = pr[3 * n + 0];
     const float4 p1 = pr[3 * n + 1];
     float4 p2 = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -121,6 +141,7 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_kernel(
         acc[f][7] = fmaf(p2.w, qr, acc[f][7]);
       }
     }
+  }
   }
 #pragma unroll
   for (int f = 0; f < F; ++f) {
@@ -224,7 +245,6 @@ __global__ __launch_bounds__(KspecShape<LOG2L>::NT) void kspec_kernel(
   const float sc = 0.5f / (float)L;
   float4* cf = coef + (size_t)h * L;
   auto zget = [&](int j) -> float2 { return (j & 1) ? Bq[lds_pad(j >> 1)] : A[lds_pad(j >> 1)]; };
-  auto cidx = [&](int j) -> int { return (j & 1) * H2 + (j >> 1); };
   for (int j = tid; j <= L / 2; j += NT) {
     const int jm = L - j;
     const float2 zj = zget(j), zm = zget(jm & (L - 1));
@@ -236,13 +256,13 @@ __global__ __launch_bounds__(KspecShape<LOG2L>::NT) void kspec_kernel(
       const float a = sc * (1.0f - csj.y), b = sc * (1.0f + csj.y), c = sc * csj.x;
       const float2 al = make_float2(fmaf(a, sj.x, b * sm.x), fmaf(a, sj.y, -b * sm.y));
       const float2 df = make_float2(sj.x - sm.x, sj.y + sm.y);   // S_j - conj(S_m)
-      cf[cidx(j)] = make_float4(al.x, al.y, -c * df.y, c * df.x);
+      cf[j] = make_float4(al.x, al.y, -c * df.y, c * df.x);
     }
     if (j != 0 && jm != j) {
       const float a = sc * (1.0f - csm.y), b = sc * (1.0f + csm.y), c = sc * csm.x;
       const float2 al = make_float2(fmaf(a, sm.x, b * sj.x), fmaf(a, sm.y, -b * sj.y));
       const float2 df = make_float2(sm.x - sj.x, sm.y + sj.y);
-      cf[cidx(jm)] = make_float4(al.x, al.y, -c * df.y, c * df.x);
+      cf[jm] = make_float4(al.x, al.y, -c * df.y, c * df.x);
     }
   }
 }
@@ -256,7 +276,7 @@ struct ConvShape {
   static constexpr int E = 1 << fft_elems_log(LOG2H2);
   static constexpr int TPH = H2 / E;
   static constexpr int TPR = 2 * TPH;                      // threads per row
-  static constexpr int NTHR = TPR > 256 ? TPR : 256;
+  static constexpr int NTHR = TPR > 64 ? TPR : 64;
   static constexpr int RPW = NTHR / TPR;                   // rows per workgroup
   static constexpr int HP = lds_padded_size(H2);
 };
@@ -292,12 +312,13 @@ __global__ __launch_bounds__(ConvShape<LOG2L>::NTHR) void conv_kernel(
   // 2. forward transforms of L/2 points
   lds_fft<S::LOG2H2, false>(mine, lt, true, twH);
   // 3. spectral step on bin pairs (j, L-j): Z'_j = alpha_j Z_j + beta_j conj(Z_{L-j})
-  const float4* __restrict__ cf = coef + (size_t)h * L + half * H2;
+  // weights of bin j = 2m + half are at coef[h][j]
+  const float4* __restrict__ cf = coef + (size_t)h * L + half;
   if (half == 0) {
     for (int m = lt; m <= H2 / 2; m += TPH) {
       const int mp = (H2 - m) & (H2 - 1);
       const float2 z1 = A[lds_pad(m)], z2 = A[lds_pad(mp)];
-      const float4 c1 = cf[m], c2 = cf[mp];
+      const float4 c1 = cf[2 * m], c2 = cf[2 * mp];
       const float2 o1 = cadd(cmul(make_float2(c1.x, c1.y), z1), cmul(make_float2(c1.z, c1.w), cconj(z2)));
       const float2 o2 = cadd(cmul(make_float2(c2.x, c2.y), z2), cmul(make_float2(c2.z, c2.w), cconj(z1)));
       A[lds_pad(m)] = o1;
@@ -307,7 +328,7 @@ __global__ __launch_bounds__(ConvShape<LOG2L>::NTHR) void conv_kernel(
     for (int m = lt; m < (H2 + 1) / 2; m += TPH) {
       const int mp = H2 - 1 - m;
       const float2 z1 = Bq[lds_pad(m)], z2 = Bq[lds_pad(mp)];
-      const float4 c1 = cf[m], c2 = cf[mp];
+      const float4 c1 = cf[2 * m], c2 = cf[2 * mp];
       const float2 o1 = cadd(cmul(make_float2(c1.x, c1.y), z1), cmul(make_float2(c1.z, c1.w), cconj(z2)));
       const float2 o2 = cadd(cmul(make_float2(c2.x, c2.y), z2), cmul(make_float2(c2.z, c2.w), cconj(z1)));
       Bq[lds_pad(m)] = o1;
@@ -326,6 +347,117 @@ __global__ __launch_bounds__(ConvShape<LOG2L>::NTHR) void conv_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Stage 2 for 32 <= L <= 1024: wave-resident rows
+// ---------------------------------------------------------------------------
+// The packed zero-padded row z (M = L complex points, upper half zero) is
+// transformed with M/16 lanes of one wavefront; the spectrum Z becomes that of
+// the output by Z'_j = alpha_j Z_j + beta_j conj(Z_{M-j}); the inverse
+// transform's first M/2 points are the L outputs (y_2k, y_2k+1) = z'_k.
+// Each wave loops over rows; the twiddles stay in registers across rows.
+constexpr int kWaveConvThreads = 256;
+
+template <int LOG2M>
+struct WaveConvShape {
+  static constexpr int M = 1 << LOG2M;
+  static constexpr int T = M / 16;                 // lanes per row
+  static constexpr int RPW = 64 / T;               // rows per wave
+  static constexpr int P = fft_num_passes(LOG2M);
+  static constexpr int MP = lds_padded_size(M);
+  static_assert(LOG2M >= 5 && LOG2M <= 10, "wave-resident range");
+};
+
+template <int LOG2M>
+__global__ __launch_bounds__(kWaveConvThreads) void conv_wave_kernel(
+    const float* __restrict__ u, float* __restrict__ y, const float4* __restrict__ coef,
+    const float2* __restrict__ tw, int H, int batch, int groups_per_wave) {
+  using S = WaveConvShape<LOG2M>;
+  constexpr int M = S::M, T = S::T, P = S::P;
+  __shared__ float2 lds[(kWaveConvThreads / 64) * S::RPW * S::MP];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rw = lane / T, lt = lane % T;
+  float2* buf = lds + (wave * S::RPW + rw) * S::MP;
+  float2 w1[16], w2[16];
+  if constexpr (P > 1) WPass<LOG2M, 1>::load_tw(w1, tw, lt);
+  if constexpr (P > 2) WPass<LOG2M, 2>::load_tw(w2, tw, lt);
+  const int rows = H * batch;
+  const int ngroups = (rows + S::RPW - 1) / S::RPW;
+  const int gw = xcd_remap(blockIdx.x, gridDim.x) * (kWaveConvThreads / 64) + wave;
+  for (int gi = 0; gi < groups_per_wave; ++gi) {
+    const int g = gw * groups_per_wave + gi;
+    if (g >= ngroups) break;
+    const int lrow = g * S::RPW + rw;            // logical row: channel-major
+    const bool active = lrow < rows;
+    const int h = active ? lrow / batch : 0;
+    const int b = active ? lrow - h * batch : 0;
+    const size_t roff = ((size_t)b * H + h) * M;
+    float2 v[16];
+    // forward pass 0 straight from memory: z_{lt + T r}, r < 8; the rest is padding
+    const float2* __restrict__ ur = reinterpret_cast<const float2*>(u + roff);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) v[r] = active ? ur[lt + T * r] : make_float2(0.f, 0.f);
+    dft16_fwd_half_input(v);
+    WPass<LOG2M, 0>::store(v, buf, lt);
+    wave_sync();
+    if constexpr (P > 1) {
+      WPass<LOG2M, 1>::load(v, buf, lt);
+      WPass<LOG2M, 1>::template compute<false>(v, w1);
+      WPass<LOG2M, 1>::store(v, buf, lt);
+      wave_sync();
+    }
+    if constexpr (P > 2) {
+      WPass<LOG2M, 2>::load(v, buf, lt);
+      WPass<LOG2M, 2>::template compute<false>(v, w2);
+      WPass<LOG2M, 2>::store(v, buf, lt);
+      wave_sync();
+    }
+    // spectral weights, read straight into the inverse pass-0 layout j = lt + T r
+    const float4* __restrict__ cf = coef + (size_t)h * M;
+    {
+      // Z_j at pad(lt) + pad_shift(T r); Z_{M-j} at pad(M - T r - lt), with
+      // pad(A - lt) = A + A/16 + pad(-lt) for A a multiple of 16 (j = 0 maps to 0)
+      const float2* __restrict__ bj = buf + lds_pad(lt);
+      const int nlt = -lt;
+      const float2* __restrict__ bm = buf + (nlt + (nlt >> 4));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = lt + T * r;
+        const float2 zj = bj[pad_shift(lt, T * r)];
+        float2 zm;
+        if (r == 0) zm = buf[lds_pad((M - lt) & (M - 1))];
+        else if (((M - T * r) & 15) == 0) zm = bm[(M - T * r) + ((M - T * r) >> 4)];
+        else zm = buf[lds_pad(M - j)];
+        const float4 c = cf[j];
+        v[r] = cadd(cmul(make_float2(c.x, c.y), zj), cmul(make_float2(c.z, c.w), cconj(zm)));
+      }
+    }
+    wave_sync();
+    WPass<LOG2M, 0>::template compute<true>(v, w1);
+    WPass<LOG2M, 0>::store(v, buf, lt);
+    wave_sync();
+    if constexpr (P > 2) {
+      WPass<LOG2M, 1>::load(v, buf, lt);
+      WPass<LOG2M, 1>::template compute<true>(v, w1);
+      WPass<LOG2M, 1>::store(v, buf, lt);
+      wave_sync();
+    }
+    // last inverse pass: only the outputs k < M/2 are kept
+    using LP = WPass<LOG2M, P - 1>;
+    LP::load(v, buf, lt);
+    if constexpr (P == 2) LP::template compute<true>(v, w1);
+    else LP::template compute<true>(v, w2);
+    float2* __restrict__ yr = reinterpret_cast<float2*>(y + roff);
+#pragma unroll
+    for (int q = 0; q < LP::NB; ++q) {
+      const int j = lt + q * T;                   // j < NS in the last pass
+#pragma unroll
+      for (int s2 = 0; s2 < LP::R / 2; ++s2)
+        if (active) yr[j + s2 * LP::NS] = v[q * LP::R + bitrev<LP::RL>(s2)];
+    }
+    wave_sync();
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 bool lds_path(const s4dplr_plan* p) { return p->log2L <= S4DPLR_LDS_MAX_LOG2L; }
@@ -336,14 +468,12 @@ static T* at(unsigned char* ws, size_t off) { return reinterpret_cast<T*>(ws + o
 hipError_t launch_pack(const s4dplr_plan* p, const float* lam, const float* P, const float* Q,
                        const float* B, const float* C, const float* dt, unsigned char* ws,
                        hipStream_t s) {
-  const int n = p->H * p->N;
-  const int blocks = (n + 255) / 256;
   const int diag = (p->flags & S4DPLR_DIAGONAL) ? 1 : 0;
-  pack_kernel<<<blocks, 256, 0, s>>>(
+  pack_kernel<<<p->H, 64, 0, s>>>(
       reinterpret_cast<const float2*>(lam), reinterpret_cast<const float2*>(P),
       reinterpret_cast<const float2*>(Q), reinterpret_cast<const float2*>(B),
       reinterpret_cast<const float2*>(C), dt, at<float4>(ws, p->off_poles),
-      at<float4>(ws, p->off_chan), p->H, p->N, diag);
+      at<float4>(ws, p->off_chan), p->N, p->NP, diag);
   return hipGetLastError();
 }
 
@@ -356,9 +486,9 @@ hipError_t launch_cauchy(const s4dplr_plan* p, unsigned char* ws, hipStream_t s)
   const float* tanT = at<const float>(ws, p->off_tan);
   float2* khat = at<float2>(ws, p->off_khat);
   if (p->flags & S4DPLR_DIAGONAL)
-    cauchy_kernel<F, true><<<grid, kCauchyThreads, 0, s>>>(poles, chan, tanT, khat, p->N, p->L);
+    cauchy_kernel<F, true><<<grid, kCauchyThreads, 0, s>>>(poles, chan, tanT, khat, p->NP, p->L);
   else
-    cauchy_kernel<F, false><<<grid, kCauchyThreads, 0, s>>>(poles, chan, tanT, khat, p->N, p->L);
+    cauchy_kernel<F, false><<<grid, kCauchyThreads, 0, s>>>(poles, chan, tanT, khat, p->NP, p->L);
   return hipGetLastError();
 }
 
@@ -380,6 +510,19 @@ static void kspec_launch(const s4dplr_plan* p, const float* Ktime, const float* 
 template <int LOG2L>
 static void conv_launch(const s4dplr_plan* p, const float* u, float* y, unsigned char* ws,
                         hipStream_t s) {
+  if constexpr (LOG2L >= 5 && LOG2L <= 10) {
+    using W = WaveConvShape<LOG2L>;
+    const int rows = p->batch * p->H;
+    const int ngroups = (rows + W::RPW - 1) / W::RPW;
+    constexpr int kTargetWaves = 256 * 8;        // two waves per SIMD
+    const int gpw = (ngroups + kTargetWaves - 1) / kTargetWaves;
+    const int waves = (ngroups + gpw - 1) / gpw;
+    const int blocks = (waves + 3) / 4;
+    conv_wave_kernel<LOG2L><<<blocks, kWaveConvThreads, 0, s>>>(
+        u, y, at<const float4>(ws, p->off_coef), at<const float2>(ws, p->off_twL), p->H,
+        p->batch, gpw);
+    return;
+  }
   using S = ConvShape<LOG2L>;
   const int rows = p->batch * p->H;
   const int blocks = (rows + S::RPW - 1) / S::RPW;

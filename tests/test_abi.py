@@ -30,6 +30,7 @@ def lib():
     L.s4dplr_kernel_gen.argtypes = [vp] * 10
     L.s4dplr_conv_fwd.argtypes = [vp] * 7
     L.s4dplr_forward.argtypes = [vp] * 13
+    L.s4dplr_conv_apply.argtypes = [vp] * 5
     L.s4dplr_plan_destroy.argtypes = [vp]
     L.s4dplr_status_string.restype = ctypes.c_char_p
     return L
@@ -46,7 +47,7 @@ def test_header_declares_the_boundary():
     for n in ["s4dplr_abi_version", "s4dplr_status_string", "s4dplr_plan_create",
               "s4dplr_plan_workspace_bytes", "s4dplr_plan_init", "s4dplr_kernel_gen",
               "s4dplr_conv_fwd", "s4dplr_forward", "s4dplr_plan_destroy",
-              "s4dplr_last_hip_error"]:
+              "s4dplr_last_hip_error", "s4dplr_conv_apply"]:
         assert n in names
 
 
@@ -123,6 +124,11 @@ def test_null_arguments(lib):
     assert lib.s4dplr_conv_fwd(h, None, fake, None, fake + 4096, ws, None) == ERR_NULL
     assert lib.s4dplr_conv_fwd(h, fake, None, None, fake + 4096, ws, None) == ERR_NULL
     assert lib.s4dplr_conv_fwd(h, fake, fake, None, None, ws, None) == ERR_NULL
+    # conv_apply: u, y required
+    assert lib.s4dplr_conv_apply(h, None, fake, ws, None) == ERR_NULL
+    assert lib.s4dplr_conv_apply(h, fake, None, ws, None) == ERR_NULL
+    assert lib.s4dplr_conv_apply(h, fake, fake + 8192, None, None) == ERR_NULL
+    assert lib.s4dplr_conv_apply(h, fake, fake + 8192, ws + 4, None) == ERR_WORKSPACE
     # forward: K and D optional
     assert lib.s4dplr_forward(h, None, fake, None, fake, fake, fake, None, fake, None, fake, ws, None) == ERR_NULL
     assert lib.s4dplr_forward(h, fake, fake, None, fake, fake, fake, None, None, None, fake, ws, None) == ERR_NULL
@@ -154,6 +160,8 @@ def test_aliasing_is_rejected_before_launch(lib):
     # y == u, y overlapping the tail of u, y overlapping K, y inside the workspace
     for y in (u, u + ub - 4, K, ws + 256):
         assert lib.s4dplr_conv_fwd(h, u, K, None, y, ws, None) == ERR_ALIAS
+    assert lib.s4dplr_conv_apply(h, u, u + 4, ws, None) == ERR_ALIAS
+    assert lib.s4dplr_conv_apply(h, u, ws, ws, None) == ERR_ALIAS
     # forward: y over u; K over y; K inside the workspace
     y = K + 4 * 4 * H * L
     assert lib.s4dplr_forward(h, 1, 1, None, 1, 1, 1, None, u, None, u, ws, None) == ERR_ALIAS
