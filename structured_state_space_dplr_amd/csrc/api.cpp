@@ -87,7 +87,6 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
   if (!is_pow2(L) || L < 2 || L > 65536) return S4DPLR_ERR_SHAPE;
   if ((long long)batch * H * L >= (1LL << 31)) return S4DPLR_ERR_SHAPE;
   const int log2L = ilog2(L);
-  if (log2L > S4DPLR_LDS_MAX_LOG2L) return S4DPLR_ERR_SHAPE;  // multi-pass path not built yet
 
   s4dplr_plan* p = new (std::nothrow) s4dplr_plan();
   if (!p) return S4DPLR_ERR_SHAPE;
@@ -105,11 +104,15 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
   off = align_up(off + sizeof(float) * L);
   p->off_cs = off;
   off = align_up(off + 2 * sizeof(float) * (L + 1));
+  const bool lds = log2L <= S4DPLR_LDS_MAX_LOG2L;
   p->off_twL = off;
-  off = align_up(off + 2 * sizeof(float) * (size_t)s4::fft_tw_size(log2L));
+  if (lds) off = align_up(off + 2 * sizeof(float) * (size_t)s4::fft_tw_size(log2L));
   p->off_twH = off;
-  off = align_up(off + 2 * sizeof(float) * (size_t)s4::fft_tw_size(log2L - 1));
-  p->off_tw4 = off;
+  if (lds) off = align_up(off + 2 * sizeof(float) * (size_t)s4::fft_tw_size(log2L - 1));
+  p->off_tw1 = off;
+  if (!lds) off = align_up(off + 2 * sizeof(float) * (size_t)s4::fft_tw_size(log2L - 8));
+  p->off_tw2 = off;
+  if (!lds) off = align_up(off + 2 * sizeof(float) * (size_t)s4::fft_tw_size(8));
   p->tables_bytes = off;
   // Scratch region.
   p->off_poles = off;
@@ -120,7 +123,10 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
   off = align_up(off + sizeof(float) * 2 * (size_t)H * L);
   p->off_coef = off;
   off = align_up(off + sizeof(float) * 4 * (size_t)H * L);
+  p->off_kbuf = off;
+  if (!lds) off = align_up(off + sizeof(float) * (size_t)H * L);
   p->off_big = off;
+  if (!lds) off = align_up(off + sizeof(float) * 2 * (size_t)batch * H * L);
   p->total = off;
 
   // fp64 tables, rounded once to fp32.
@@ -135,8 +141,13 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
   }
   cs[2 * L + 1] = 0.0f;      // sin(pi) exactly
   if (L % 2 == 0) cs[L + 0] = 0.0f;  // cos(pi/2) exactly, at j = L/2
-  fft_twiddles(log2L, reinterpret_cast<float*>(p->tables.data() + p->off_twL));
-  fft_twiddles(log2L - 1, reinterpret_cast<float*>(p->tables.data() + p->off_twH));
+  if (lds) {
+    fft_twiddles(log2L, reinterpret_cast<float*>(p->tables.data() + p->off_twL));
+    fft_twiddles(log2L - 1, reinterpret_cast<float*>(p->tables.data() + p->off_twH));
+  } else {
+    fft_twiddles(log2L - 8, reinterpret_cast<float*>(p->tables.data() + p->off_tw1));
+    fft_twiddles(8, reinterpret_cast<float*>(p->tables.data() + p->off_tw2));
+  }
   *out = p;
   return S4DPLR_OK;
 }

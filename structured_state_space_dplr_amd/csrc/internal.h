@@ -21,13 +21,15 @@ struct s4dplr_plan {
   size_t off_cs;     // [L+1] float2: (cos(pi j / L), sin(pi j / L))
   size_t off_twL;    // FFT twiddles for transforms of L points
   size_t off_twH;    // FFT twiddles for transforms of L/2 points
-  size_t off_tw4;    // multi-pass path: four-step twiddles (0 bytes otherwise)
+  size_t off_tw1;    // long path: FFT twiddles for the column transforms (L/256 points)
+  size_t off_tw2;    // long path: FFT twiddles for the row transforms (256 points)
   size_t tables_bytes;
   size_t off_poles;  // [H][NP][3] float4 packed pole records
   size_t off_chan;   // [H] float4: (2/dt, (dt/2) sum C B re, im, 0)
   size_t off_khat;   // [H][L] float2: generating function at the roots of unity
   size_t off_coef;   // [H][L] float4: spectral weights (alpha, beta) of bin j
-  size_t off_big;    // multi-pass path: [batch*H][L] float2 intermediate (0 bytes otherwise)
+  size_t off_kbuf;   // long path: [H][L] float time-domain kernel when not written out
+  size_t off_big;    // long path: [batch*H][L] float2 intermediate rows
   size_t total;
   std::vector<unsigned char> tables;  // exact bytes of the table region
 };
@@ -47,5 +49,10 @@ hipError_t launch_kspec(const s4dplr_plan* p, const float* Ktime, const float* D
                         unsigned char* ws, hipStream_t s);
 hipError_t launch_conv(const s4dplr_plan* p, const float* u, float* y, unsigned char* ws,
                        hipStream_t s);
+// Long sequences (log2 L = 15, 16): four-step transforms through the workspace.
+hipError_t launch_big_kspec(const s4dplr_plan* p, const float* Ktime, const float* D,
+                            float* Kout, unsigned char* ws, hipStream_t s);
+hipError_t launch_big_conv(const s4dplr_plan* p, const float* u, float* y, unsigned char* ws,
+                           hipStream_t s);
 
 }  // namespace s4

@@ -90,20 +90,23 @@ __global__ __launch_bounds__(64) void pack_kernel(
 //   k_ab += w_ab * rho.
 constexpr int kCauchyThreads = 256;
 
+// perm_m1 > 0: store in the permuted layout of the long path, position
+// p = k1*256 + k2 holding frequency l = k1 + perm_m1*k2.
 template <int F, bool DIAG>
 __global__ __launch_bounds__(kCauchyThreads) void cauchy_kernel(
     const float4* __restrict__ poles, const float4* __restrict__ chan,
-    const float* __restrict__ tanT, float2* __restrict__ khat, int NP, int L) {
+    const float* __restrict__ tanT, float2* __restrict__ khat, int NP, int L, int perm_m1) {
   const int h = blockIdx.y;
   const float4 ch = chan[h];
   const float4* __restrict__ pr = poles + (size_t)h * NP * 3;
-  int l[F];
+  int l[F], pos[F];
   float T[F], G[F];
   float acc[F][8];
 #pragma unroll
   for (int f = 0; f < F; ++f) {
-    l[f] = (blockIdx.x * F + f) * kCauchyThreads + threadIdx.x;
-    T[f] = l[f] < L ? tanT[l[f]] : 0.f;
+    pos[f] = (blockIdx.x * F + f) * kCauchyThreads + threadIdx.x;
+    l[f] = perm_m1 ? ((pos[f] >> 8) + perm_m1 * (pos[f] & 255)) : pos[f];
+    T[f] = pos[f] < L ? tanT[l[f]] : 0.f;
     G[f] = ch.x * T[f];
 #pragma unroll
     for (int a = 0; a < 8; ++a) acc[f][a] = 0.f;
@@ -145,7 +148,7 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_kernel(
   }
 #pragma unroll
   for (int f = 0; f < F; ++f) {
-    if (l[f] >= L) continue;
+    if (pos[f] >= L) continue;
     float2 kv = make_float2(acc[f][0], acc[f][1]);
     if constexpr (!DIAG) {
       // Woodbury: k00 - k01 k10 / (1 + k11)
@@ -159,7 +162,7 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_kernel(
     }
     float2 kh = cmul(make_float2(1.0f, T[f]), kv);       // times 2/(1+z)
     if (2 * l[f] == L) kh = make_float2(ch.y, ch.z);      // z = -1: the limit
-    khat[(size_t)h * L + l[f]] = kh;
+    khat[(size_t)h * L + pos[f]] = kh;
   }
 }
 
@@ -485,10 +488,13 @@ hipError_t launch_cauchy(const s4dplr_plan* p, unsigned char* ws, hipStream_t s)
   const float4* chan = at<const float4>(ws, p->off_chan);
   const float* tanT = at<const float>(ws, p->off_tan);
   float2* khat = at<float2>(ws, p->off_khat);
+  const int perm_m1 = lds_path(p) ? 0 : p->L / 256;
   if (p->flags & S4DPLR_DIAGONAL)
-    cauchy_kernel<F, true><<<grid, kCauchyThreads, 0, s>>>(poles, chan, tanT, khat, p->NP, p->L);
+    cauchy_kernel<F, true><<<grid, kCauchyThreads, 0, s>>>(poles, chan, tanT, khat, p->NP, p->L,
+                                                           perm_m1);
   else
-    cauchy_kernel<F, false><<<grid, kCauchyThreads, 0, s>>>(poles, chan, tanT, khat, p->NP, p->L);
+    cauchy_kernel<F, false><<<grid, kCauchyThreads, 0, s>>>(poles, chan, tanT, khat, p->NP, p->L,
+                                                            perm_m1);
   return hipGetLastError();
 }
 
@@ -552,12 +558,14 @@ static void conv_launch(const s4dplr_plan* p, const float* u, float* y, unsigned
 
 hipError_t launch_kspec(const s4dplr_plan* p, const float* Ktime, const float* D, float* Kout,
                         unsigned char* ws, hipStream_t s) {
+  if (!lds_path(p)) return launch_big_kspec(p, Ktime, D, Kout, ws, s);
   S4_DISPATCH_LOG2L(kspec_launch, p, Ktime, D, Kout, ws, s);
   return hipGetLastError();
 }
 
 hipError_t launch_conv(const s4dplr_plan* p, const float* u, float* y, unsigned char* ws,
                        hipStream_t s) {
+  if (!lds_path(p)) return launch_big_conv(p, u, y, ws, s);
   S4_DISPATCH_LOG2L(conv_launch, p, u, y, ws, s);
   return hipGetLastError();
 }

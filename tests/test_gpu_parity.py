@@ -57,7 +57,7 @@ def oracle_forward(x, diagonal=False, with_D=True):
 
 # ---- the five workloads at their full sizes --------------------------------
 
-@pytest.mark.parametrize("name", ["tiny", "mid", "long", "s4d_lin"])
+@pytest.mark.parametrize("name", ["tiny", "mid", "long", "s4d_lin", "waveform"])
 def test_workload_parity(s4, name):
     w = WORKLOADS[name]
     print(f"case: workload {w.describe()}", flush=True)
@@ -87,7 +87,7 @@ def test_workload_parity(s4, name):
 
 # ---- every sequence length, generic DPLR parameters ------------------------
 
-@pytest.mark.parametrize("L", [2 ** k for k in range(1, 15)])
+@pytest.mark.parametrize("L", [2 ** k for k in range(1, 17)])
 def test_all_lengths_generic(s4, L):
     print(f"case: generic H=3 N=8 L={L} batch=2", flush=True)
     x = make_generic_inputs(H=3, N=8, L=L, batch=2, seed=L)
@@ -129,7 +129,7 @@ def test_single_channel_single_row_many_poles(s4):
 
 # ---- the two halves separately ---------------------------------------------
 
-@pytest.mark.parametrize("L", [2, 8, 64, 1024, 16384])
+@pytest.mark.parametrize("L", [2, 8, 64, 1024, 16384, 32768, 65536])
 def test_conv_fwd_random_kernel(s4, L):
     import torch
     print(f"case: conv_fwd random K L={L}", flush=True)
