@@ -115,10 +115,6 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
   if (!lds) off = align_up(off + 2 * sizeof(float) * (size_t)s4::fft_tw_size(8));
   p->tables_bytes = off;
   // Scratch region.
-  p->off_poles = off;
-  off = align_up(off + sizeof(float) * 12 * (size_t)H * p->NP);
-  p->off_chan = off;
-  off = align_up(off + sizeof(float) * 4 * (size_t)H);
   p->off_khat = off;
   off = align_up(off + sizeof(float) * 2 * (size_t)H * L);
   p->off_coef = off;
@@ -193,9 +189,8 @@ s4dplr_status s4dplr_kernel_gen(const s4dplr_plan* p, const float* lambda, const
   if (overlaps(K, kb, ws, p->total)) return S4DPLR_ERR_ALIAS;
   unsigned char* w = static_cast<unsigned char*>(ws);
   hipError_t e;
-  if ((e = s4::launch_pack(p, lambda, P, Q, B, C, dt, w, stream)) != hipSuccess) return hip_fail(e);
-  if ((e = s4::launch_cauchy(p, w, stream)) != hipSuccess) return hip_fail(e);
-  if ((e = s4::launch_kspec(p, nullptr, nullptr, K, w, stream)) != hipSuccess) return hip_fail(e);
+  if ((e = s4::launch_kernel_gen(p, lambda, P, Q, B, C, dt, nullptr, K, w, stream)) != hipSuccess)
+    return hip_fail(e);
   return S4DPLR_OK;
 }
 
@@ -210,7 +205,7 @@ s4dplr_status s4dplr_conv_fwd(const s4dplr_plan* p, const float* u, const float*
     return S4DPLR_ERR_ALIAS;
   unsigned char* w = static_cast<unsigned char*>(ws);
   hipError_t e;
-  if ((e = s4::launch_kspec(p, K, D, nullptr, w, stream)) != hipSuccess) return hip_fail(e);
+  if ((e = s4::launch_spectrum_from_time(p, K, D, w, stream)) != hipSuccess) return hip_fail(e);
   if ((e = s4::launch_conv(p, u, y, w, stream)) != hipSuccess) return hip_fail(e);
   return S4DPLR_OK;
 }
@@ -230,9 +225,8 @@ s4dplr_status s4dplr_forward(const s4dplr_plan* p, const float* lambda, const fl
     return S4DPLR_ERR_ALIAS;
   unsigned char* w = static_cast<unsigned char*>(ws);
   hipError_t e;
-  if ((e = s4::launch_pack(p, lambda, P, Q, B, C, dt, w, stream)) != hipSuccess) return hip_fail(e);
-  if ((e = s4::launch_cauchy(p, w, stream)) != hipSuccess) return hip_fail(e);
-  if ((e = s4::launch_kspec(p, nullptr, D, K, w, stream)) != hipSuccess) return hip_fail(e);
+  if ((e = s4::launch_kernel_gen(p, lambda, P, Q, B, C, dt, D, K, w, stream)) != hipSuccess)
+    return hip_fail(e);
   if ((e = s4::launch_conv(p, u, y, w, stream)) != hipSuccess) return hip_fail(e);
   return S4DPLR_OK;
 }

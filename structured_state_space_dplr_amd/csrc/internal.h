@@ -24,8 +24,6 @@ struct s4dplr_plan {
   size_t off_tw1;    // long path: FFT twiddles for the column transforms (L/256 points)
   size_t off_tw2;    // long path: FFT twiddles for the row transforms (256 points)
   size_t tables_bytes;
-  size_t off_poles;  // [H][NP][3] float4 packed pole records
-  size_t off_chan;   // [H] float4: (2/dt, (dt/2) sum C B re, im, 0)
   size_t off_khat;   // [H][L] float2: generating function at the roots of unity
   size_t off_coef;   // [H][L] float4: spectral weights (alpha, beta) of bin j
   size_t off_kbuf;   // long path: [H][L] float time-domain kernel when not written out
@@ -38,15 +36,15 @@ namespace s4 {
 
 bool lds_path(const s4dplr_plan* p);
 
-hipError_t launch_pack(const s4dplr_plan* p, const float* lam, const float* P, const float* Q,
-                       const float* B, const float* C, const float* dt, unsigned char* ws,
-                       hipStream_t s);
-hipError_t launch_cauchy(const s4dplr_plan* p, unsigned char* ws, hipStream_t s);
-// Kernel spectrum: from the generating function in the workspace (Ktime ==
-// nullptr; writes the time-domain kernel to Kout if not null) or from a
-// time-domain kernel Ktime.  Folds D (may be null) into the weights.
-hipError_t launch_kspec(const s4dplr_plan* p, const float* Ktime, const float* D, float* Kout,
-                        unsigned char* ws, hipStream_t s);
+// Stage 1: the time-domain kernel K (written to Kout when not null) and the
+// convolution weights of the spectrum of (K + D delta) padded to 2L (D may be
+// null) in the workspace.
+hipError_t launch_kernel_gen(const s4dplr_plan* p, const float* lam, const float* P,
+                             const float* Q, const float* B, const float* C, const float* dt,
+                             const float* D, float* Kout, unsigned char* ws, hipStream_t s);
+// The convolution weights from a given time-domain kernel.
+hipError_t launch_spectrum_from_time(const s4dplr_plan* p, const float* Ktime, const float* D,
+                                     unsigned char* ws, hipStream_t s);
 hipError_t launch_conv(const s4dplr_plan* p, const float* u, float* y, unsigned char* ws,
                        hipStream_t s);
 // Long sequences (log2 L = 15, 16): four-step transforms through the workspace.

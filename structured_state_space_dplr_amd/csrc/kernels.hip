@@ -37,133 +37,311 @@
 namespace s4 {
 
 // ---------------------------------------------------------------------------
-// Stage 1a: pack pole records and channel constants
+// Stage 1a/1b: pole records and the Cauchy sums at the L roots of unity
 // ---------------------------------------------------------------------------
-// One wave per channel.  Pole records are padded to a multiple of
-// kPoleUnroll with inert poles (zero weights, Lambda = -1) so that the Cauchy
-// loop runs in whole unrolled blocks.
+// A block first writes its channel's pole records into LDS:
+//   rec[3n]   = (Im Lambda_n, (Re Lambda_n)^2, -Re Lambda_n, 0)
+//   rec[3n+1] = (w00, w01),  rec[3n+2] = (w10, w11)
+// with w00 = C B, w01 = C P, w10 = conj(Q) B, w11 = conj(Q) P.  Poles n in
+// [N, NP) (NP = N rounded up to kPoleUnroll) are inert: zero weights,
+// Lambda = -1.  Every Cauchy term is then pure VALU work on broadcast LDS
+// operands:  y = G - Im Lambda, d = (Re Lambda)^2 + y^2,
+//            rho = (-Re Lambda - i y)/d = 1/(i G - Lambda),  k_ab += w_ab rho.
 constexpr int kPoleUnroll = 4;
+constexpr int kMaxPoles = 256;
 
-__global__ __launch_bounds__(64) void pack_kernel(
-    const float2* __restrict__ lam, const float2* __restrict__ P, const float2* __restrict__ Q,
-    const float2* __restrict__ B, const float2* __restrict__ C, const float* __restrict__ dt,
-    float4* __restrict__ poles, float4* __restrict__ chan, int N, int NP, int diag) {
-  const int h = blockIdx.x, lane = threadIdx.x;
+struct ParamPtrs {
+  const float2* lam;
+  const float2* P;
+  const float2* Q;   // nullptr: Q = P
+  const float2* B;
+  const float2* C;
+  const float* dt;
+};
+
+// Builds the records of channel h with threads [0, nthr); returns this
+// thread's partial sum of w00 = C B over its poles.
+__device__ __forceinline__ float2 build_pole_records(const ParamPtrs& pp, int h, int N, int NP,
+                                                     bool diag, float4* __restrict__ rec, int tid,
+                                                     int nthr) {
   float2 s = make_float2(0.f, 0.f);
-  for (int n = lane; n < NP; n += 64) {
-    float4* rec = poles + 3 * ((size_t)h * NP + n);
+  for (int n = tid; n < NP; n += nthr) {
     if (n < N) {
       const size_t idx = (size_t)h * N + n;
-      const float2 l = lam[idx], b = B[idx], c = C[idx];
-      const float2 p = diag ? make_float2(0.f, 0.f) : P[idx];
-      const float2 q = diag ? make_float2(0.f, 0.f) : (Q ? Q[idx] : p);
-      const float2 w00 = cmul(c, b), w01 = cmul(c, p);
-      const float2 w10 = cmul(cconj(q), b), w11 = cmul(cconj(q), p);
-      rec[0] = make_float4(l.y, l.x * l.x, -l.x, 0.f);
-      rec[1] = make_float4(w00.x, w00.y, w01.x, w01.y);
-      rec[2] = make_float4(w10.x, w10.y, w11.x, w11.y);
+      const float2 l = pp.lam[idx], b = pp.B[idx], c = pp.C[idx];
+      const float2 pv = diag ? make_float2(0.f, 0.f) : pp.P[idx];
+      const float2 qv = diag ? make_float2(0.f, 0.f) : (pp.Q ? pp.Q[idx] : pv);
+      const float2 w00 = cmul(c, b), w01 = cmul(c, pv);
+      const float2 w10 = cmul(cconj(qv), b), w11 = cmul(cconj(qv), pv);
+      rec[3 * n + 0] = make_float4(l.y, l.x * l.x, -l.x, 0.f);
+      rec[3 * n + 1] = make_float4(w00.x, w00.y, w01.x, w01.y);
+      rec[3 * n + 2] = make_float4(w10.x, w10.y, w11.x, w11.y);
       s = cadd(s, w00);
     } else {
-      rec[0] = make_float4(0.f, 1.f, 1.f, 0.f);
-      rec[1] = make_float4(0.f, 0.f, 0.f, 0.f);
-      rec[2] = make_float4(0.f, 0.f, 0.f, 0.f);
+      rec[3 * n + 0] = make_float4(0.f, 1.f, 1.f, 0.f);
+      rec[3 * n + 1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      rec[3 * n + 2] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
+  return s;
+}
+
+// Sum of a float2 over the block (blockDim a multiple of 64); ends with a
+// barrier, so LDS written before the call is visible to all threads after it.
+template <int NTHR>
+__device__ __forceinline__ float2 block_sum2(float2 v, float2* __restrict__ red, int tid) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
-    s.x += __shfl_xor(s.x, off);
-    s.y += __shfl_xor(s.y, off);
+    v.x += __shfl_xor(v.x, off);
+    v.y += __shfl_xor(v.y, off);
   }
-  if (lane == 0) {
-    const float d = dt[h];
-    // limit of the generating function at z = -1: (dt/2) sum_n C_n B_n
-    chan[h] = make_float4(2.0f / d, 0.5f * d * s.x, 0.5f * d * s.y, 0.f);
+  if ((tid & 63) == 0) red[tid >> 6] = v;
+  __syncthreads();
+  float2 s = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int w = 0; w < NTHR / 64; ++w) s = cadd(s, red[w]);
+  return s;
+}
+
+// acc[f][0..7] += the four Cauchy sums (re, im) at G[f], over poles [0, NP).
+template <int F, bool DIAG>
+__device__ __forceinline__ void cauchy_sums(const float4* __restrict__ rec, int NP,
+                                            const float (&G)[F], float (&acc)[F][8]) {
+  for (int n0 = 0; n0 < NP; n0 += kPoleUnroll) {
+#pragma unroll
+    for (int n = n0; n < n0 + kPoleUnroll; ++n) {
+      const float4 p0 = rec[3 * n + 0];
+      const float4 p1 = rec[3 * n + 1];
+      float4 p2 = make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (!DIAG) p2 = rec[3 * n + 2];
+#pragma unroll
+      for (int f = 0; f < F; ++f) {
+        const float yv = G[f] - p0.x;
+        const float d = fmaf(yv, yv, p0.y);
+        const float r = __builtin_amdgcn_rcpf(d);
+        const float qr = p0.z * r;
+        const float qi = -yv * r;
+        acc[f][0] = fmaf(p1.x, qr, acc[f][0]);
+        acc[f][0] = fmaf(-p1.y, qi, acc[f][0]);
+        acc[f][1] = fmaf(p1.x, qi, acc[f][1]);
+        acc[f][1] = fmaf(p1.y, qr, acc[f][1]);
+        if constexpr (!DIAG) {
+          acc[f][2] = fmaf(p1.z, qr, acc[f][2]);
+          acc[f][2] = fmaf(-p1.w, qi, acc[f][2]);
+          acc[f][3] = fmaf(p1.z, qi, acc[f][3]);
+          acc[f][3] = fmaf(p1.w, qr, acc[f][3]);
+          acc[f][4] = fmaf(p2.x, qr, acc[f][4]);
+          acc[f][4] = fmaf(-p2.y, qi, acc[f][4]);
+          acc[f][5] = fmaf(p2.x, qi, acc[f][5]);
+          acc[f][5] = fmaf(p2.y, qr, acc[f][5]);
+          acc[f][6] = fmaf(p2.z, qr, acc[f][6]);
+          acc[f][6] = fmaf(-p2.w, qi, acc[f][6]);
+          acc[f][7] = fmaf(p2.z, qi, acc[f][7]);
+          acc[f][7] = fmaf(p2.w, qr, acc[f][7]);
+        }
+      }
+    }
   }
 }
 
-// ---------------------------------------------------------------------------
-// Stage 1b: Cauchy sums + Woodbury + 2/(1+z) at the L roots of unity
-// ---------------------------------------------------------------------------
-// Each thread evaluates F frequencies of one channel; the pole loop reads
-// wave-uniform records (scalar loads) so every term is pure VALU work:
-//   y = G - Im(Lambda), d = Re(Lambda)^2 + y^2, rho = (-Re(Lambda) - i y)/d,
-//   k_ab += w_ab * rho.
+// Woodbury correction and the 2/(1+z) = 1 + i tan(theta/2) factor; at z = -1
+// (the frequency l = L/2) the limit `nyq` = (dt/2) sum_n C_n B_n.
+template <bool DIAG>
+__device__ __forceinline__ float2 cauchy_epilogue(const float (&a)[8], float T, bool at_nyquist,
+                                                  float2 nyq) {
+  float2 kv = make_float2(a[0], a[1]);
+  if constexpr (!DIAG) {
+    // k00 - k01 k10 / (1 + k11)
+    const float2 k01 = make_float2(a[2], a[3]);
+    const float2 k10 = make_float2(a[4], a[5]);
+    const float2 den = make_float2(1.0f + a[6], a[7]);
+    const float2 num = cmul(k01, k10);
+    const float inv = 1.0f / fmaf(den.x, den.x, den.y * den.y);
+    const float2 t = cmulc(num, den);
+    kv = make_float2(fmaf(-t.x, inv, kv.x), fmaf(-t.y, inv, kv.y));
+  }
+  const float2 kh = cmul(make_float2(1.0f, T), kv);
+  return at_nyquist ? nyq : kh;
+}
+
+// General kernel generation step: F frequencies per thread, 256 threads, one
+// channel per blockIdx.y.  perm_m1 > 0 stores the long path's transposed
+// layout: position p = k1*256 + k2 holds frequency l = k1 + perm_m1*k2.
 constexpr int kCauchyThreads = 256;
 
-// perm_m1 > 0: store in the permuted layout of the long path, position
-// p = k1*256 + k2 holding frequency l = k1 + perm_m1*k2.
 template <int F, bool DIAG>
 __global__ __launch_bounds__(kCauchyThreads) void cauchy_kernel(
-    const float4* __restrict__ poles, const float4* __restrict__ chan,
-    const float* __restrict__ tanT, float2* __restrict__ khat, int NP, int L, int perm_m1) {
-  const int h = blockIdx.y;
-  const float4 ch = chan[h];
-  const float4* __restrict__ pr = poles + (size_t)h * NP * 3;
+    ParamPtrs pp, const float* __restrict__ tanT, float2* __restrict__ khat, int N, int NP, int L,
+    int perm_m1) {
+  __shared__ float4 rec[3 * kMaxPoles];
+  __shared__ float2 red[kCauchyThreads / 64];
+  const int h = blockIdx.y, tid = threadIdx.x;
+  const float2 part = build_pole_records(pp, h, N, NP, DIAG, rec, tid, kCauchyThreads);
+  const float2 sum = block_sum2<kCauchyThreads>(part, red, tid);
+  const float dt = pp.dt[h];
+  const float2 nyq = make_float2(0.5f * dt * sum.x, 0.5f * dt * sum.y);
+  const float two_dt = 2.0f / dt;
   int l[F], pos[F];
   float T[F], G[F];
   float acc[F][8];
 #pragma unroll
   for (int f = 0; f < F; ++f) {
-    pos[f] = (blockIdx.x * F + f) * kCauchyThreads + threadIdx.x;
+    pos[f] = (blockIdx.x * F + f) * kCauchyThreads + tid;
     l[f] = perm_m1 ? ((pos[f] >> 8) + perm_m1 * (pos[f] & 255)) : pos[f];
     T[f] = pos[f] < L ? tanT[l[f]] : 0.f;
-    G[f] = ch.x * T[f];
+    G[f] = two_dt * T[f];
 #pragma unroll
     for (int a = 0; a < 8; ++a) acc[f][a] = 0.f;
   }
-  for (int n0 = 0; n0 < NP; n0 += kPoleUnroll) {
+  cauchy_sums<F, DIAG>(rec, NP, G, acc);
 #pragma unroll
-  for (int n = n0; n < n0 + kPoleUnroll; ++n) {
-    const float4 p0 = pr[3 * n + 0];
-    const float4 p1 = pr[3 * n + 1];
-    float4 p2 = make_float4(0.f, 0.f, 0.f, 0.f);
-    if constexpr (!DIAG) p2 = pr[3 * n + 2];
-#pragma unroll
-    for (int f = 0; f < F; ++f) {
-      const float yv = G[f] - p0.x;
-      const float d = fmaf(yv, yv, p0.y);
-      const float r = __builtin_amdgcn_rcpf(d);
-      const float qr = p0.z * r;
-      const float qi = -yv * r;
-      acc[f][0] = fmaf(p1.x, qr, acc[f][0]);
-      acc[f][0] = fmaf(-p1.y, qi, acc[f][0]);
-      acc[f][1] = fmaf(p1.x, qi, acc[f][1]);
-      acc[f][1] = fmaf(p1.y, qr, acc[f][1]);
-      if constexpr (!DIAG) {
-        acc[f][2] = fmaf(p1.z, qr, acc[f][2]);
-        acc[f][2] = fmaf(-p1.w, qi, acc[f][2]);
-        acc[f][3] = fmaf(p1.z, qi, acc[f][3]);
-        acc[f][3] = fmaf(p1.w, qr, acc[f][3]);
-        acc[f][4] = fmaf(p2.x, qr, acc[f][4]);
-        acc[f][4] = fmaf(-p2.y, qi, acc[f][4]);
-        acc[f][5] = fmaf(p2.x, qi, acc[f][5]);
-        acc[f][5] = fmaf(p2.y, qr, acc[f][5]);
-        acc[f][6] = fmaf(p2.z, qr, acc[f][6]);
-        acc[f][6] = fmaf(-p2.w, qi, acc[f][6]);
-        acc[f][7] = fmaf(p2.z, qi, acc[f][7]);
-        acc[f][7] = fmaf(p2.w, qr, acc[f][7]);
+  for (int f = 0; f < F; ++f)
+    if (pos[f] < L) khat[(size_t)h * L + pos[f]] = cauchy_epilogue<DIAG>(acc[f], T[f], 2 * l[f] == L, nyq);
+}
+
+// ---------------------------------------------------------------------------
+// Stage 1 fused for 32 <= L <= 1024: one block per channel.  All threads form
+// the generating function (one frequency each) in LDS; one wave takes the
+// inverse transform to K and the transform of the zero-padded K; all threads
+// then form the convolution weights.  Also the kernel-spectrum step alone
+// (FROM_TIME: K given).
+// ---------------------------------------------------------------------------
+template <int LOG2L>
+struct KgenShape {
+  static constexpr int L = 1 << LOG2L;
+  static constexpr int NTHR = L < 256 ? 256 : L;
+  static constexpr int T = L / 16;
+  static constexpr int P = fft_num_passes(LOG2L);
+  static constexpr int MP = lds_padded_size(L);
+  static_assert(LOG2L >= 5 && LOG2L <= 10, "fused range");
+};
+
+// the real-FFT bin X_j from (Z_j, Z_{M-j}); csj = (cos, sin)(pi j / M)
+__device__ __forceinline__ float2 rfft_x(float2 zj, float2 zmj, float2 csj) {
+  const float2 p = make_float2(0.5f * (1.0f - csj.y), -0.5f * csj.x);
+  const float2 q = make_float2(0.5f * (1.0f + csj.y), 0.5f * csj.x);
+  return cadd(cmul(p, zj), cmul(q, cconj(zmj)));
+}
+
+// Convolution weights of the bin pair (j, L-j), j in [0, L/2], from the
+// spectrum Z (natural order, padded, in LDS) of the packed zero-padded kernel:
+//   S_j = X_j + D,  alpha_j = ((1 - s_j) S_j + (1 + s_j) conj(S_{L-j})) / (2L),
+//   beta_j = i c_j (S_j - conj(S_{L-j})) / (2L),   (c_j, s_j) = (cos, sin)(pi j / L).
+__device__ __forceinline__ void weights_pair(const float2* __restrict__ Zb, float4* __restrict__ cf,
+                                             const float2* __restrict__ cs, int L, int j, float Dh) {
+  const float sc = 0.5f / (float)L;
+  const int jm = L - j;
+  const float2 zj = Zb[lds_pad(j)], zm = Zb[lds_pad(jm & (L - 1))];
+  const float2 csj = cs[j], csm = cs[jm];
+  float2 sj = rfft_x(zj, zm, csj), sm = rfft_x(zm, zj, csm);
+  sj.x += Dh;
+  sm.x += Dh;
+  {
+    const float a = sc * (1.0f - csj.y), b = sc * (1.0f + csj.y), c = sc * csj.x;
+    const float2 al = make_float2(fmaf(a, sj.x, b * sm.x), fmaf(a, sj.y, -b * sm.y));
+    const float2 df = make_float2(sj.x - sm.x, sj.y + sm.y);   // S_j - conj(S_m)
+    cf[j] = make_float4(al.x, al.y, -c * df.y, c * df.x);
+  }
+  if (j != 0 && jm != j) {
+    const float a = sc * (1.0f - csm.y), b = sc * (1.0f + csm.y), c = sc * csm.x;
+    const float2 al = make_float2(fmaf(a, sm.x, b * sj.x), fmaf(a, sm.y, -b * sj.y));
+    const float2 df = make_float2(sm.x - sj.x, sm.y + sj.y);
+    cf[jm] = make_float4(al.x, al.y, -c * df.y, c * df.x);
+  }
+}
+
+template <int LOG2L, bool DIAG, bool FROM_TIME>
+__global__ __launch_bounds__(KgenShape<LOG2L>::NTHR) void kgen_wave_kernel(
+    ParamPtrs pp, const float* __restrict__ D, const float* __restrict__ Kin,
+    float* __restrict__ Kout, float4* __restrict__ coef, const float* __restrict__ tanT,
+    const float2* __restrict__ tw, const float2* __restrict__ cs, int N, int NP) {
+  using S = KgenShape<LOG2L>;
+  constexpr int L = S::L, T = S::T, NTHR = S::NTHR, P = S::P;
+  __shared__ float4 rec[FROM_TIME ? 3 : 3 * kMaxPoles];
+  __shared__ float2 red[NTHR / 64];
+  __shared__ float2 buf[S::MP];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63;
+  const bool fft_lane = tid < T;          // lanes of wave 0 that hold the transform
+  float2 v[16], w[16];
+  if constexpr (!FROM_TIME) {
+    const float2 part = build_pole_records(pp, h, N, NP, DIAG, rec, tid, NTHR);
+    const float2 sum = block_sum2<NTHR>(part, red, tid);
+    const float dt = pp.dt[h];
+    const float2 nyq = make_float2(0.5f * dt * sum.x, 0.5f * dt * sum.y);
+    if (tid < L) {
+      const float T0 = tanT[tid];
+      const float G[1] = {(2.0f / dt) * T0};
+      float acc[1][8] = {{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}};
+      cauchy_sums<1, DIAG>(rec, NP, G, acc);
+      buf[lds_pad(tid)] = cauchy_epilogue<DIAG>(acc[0], T0, 2 * tid == L, nyq);
+    }
+    __syncthreads();
+    // inverse transform of length L; K_k = Re / L
+    if (fft_lane) {
+      WPass<LOG2L, 0>::load(v, buf, lane);
+      WPass<LOG2L, 0>::template compute<true>(v, w);
+      WPass<LOG2L, 0>::store(v, buf, lane);
+      wave_sync();
+      if constexpr (P > 2) {
+        WPass<LOG2L, 1>::load_tw(w, tw, lane);
+        WPass<LOG2L, 1>::load(v, buf, lane);
+        WPass<LOG2L, 1>::template compute<true>(v, w);
+        WPass<LOG2L, 1>::store(v, buf, lane);
+        wave_sync();
       }
-    }
-  }
-  }
+      using LP = WPass<LOG2L, P - 1>;
+      LP::load_tw(w, tw, lane);
+      LP::load(v, buf, lane);
+      LP::template compute<true>(v, w);
+      const float invL = 1.0f / (float)L;
+      wave_sync();
 #pragma unroll
-  for (int f = 0; f < F; ++f) {
-    if (pos[f] >= L) continue;
-    float2 kv = make_float2(acc[f][0], acc[f][1]);
-    if constexpr (!DIAG) {
-      // Woodbury: k00 - k01 k10 / (1 + k11)
-      const float2 k01 = make_float2(acc[f][2], acc[f][3]);
-      const float2 k10 = make_float2(acc[f][4], acc[f][5]);
-      const float2 den = make_float2(1.0f + acc[f][6], acc[f][7]);
-      const float2 num = cmul(k01, k10);
-      const float inv = 1.0f / fmaf(den.x, den.x, den.y * den.y);
-      const float2 t = cmulc(num, den);
-      kv = make_float2(fmaf(-t.x, inv, kv.x), fmaf(-t.y, inv, kv.y));
+      for (int q = 0; q < LP::NB; ++q) {
+        const int j = lane + q * T;               // j < NS in the last pass
+#pragma unroll
+        for (int s = 0; s < LP::R; ++s) {
+          const int k = j + s * LP::NS;
+          const float kv = v[q * LP::R + bitrev<LP::RL>(s)].x * invL;
+          if (Kout) Kout[(size_t)h * L + k] = kv;
+          buf[lds_pad(k)] = make_float2(kv, 0.f);
+        }
+      }
+      wave_sync();
     }
-    float2 kh = cmul(make_float2(1.0f, T[f]), kv);       // times 2/(1+z)
-    if (2 * l[f] == L) kh = make_float2(ch.y, ch.z);      // z = -1: the limit
-    khat[(size_t)h * L + pos[f]] = kh;
+  } else {
+    for (int k = tid; k < L; k += NTHR) buf[lds_pad(k)] = make_float2(Kin[(size_t)h * L + k], 0.f);
+    __syncthreads();
   }
+  // transform of the packed zero-padded kernel z_k = K_2k + i K_2k+1 (k < L/2)
+  if (fft_lane) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int k = lane + T * r;
+      v[r] = make_float2(buf[lds_pad(2 * k)].x, buf[lds_pad(2 * k + 1)].x);
+    }
+    wave_sync();
+    dft16_fwd_half_input(v);
+    WPass<LOG2L, 0>::store(v, buf, lane);
+    wave_sync();
+    if constexpr (P > 1) {
+      WPass<LOG2L, 1>::load_tw(w, tw, lane);
+      WPass<LOG2L, 1>::load(v, buf, lane);
+      WPass<LOG2L, 1>::template compute<false>(v, w);
+      WPass<LOG2L, 1>::store(v, buf, lane);
+      wave_sync();
+    }
+    if constexpr (P > 2) {
+      WPass<LOG2L, 2>::load_tw(w, tw, lane);
+      WPass<LOG2L, 2>::load(v, buf, lane);
+      WPass<LOG2L, 2>::template compute<false>(v, w);
+      WPass<LOG2L, 2>::store(v, buf, lane);
+      wave_sync();
+    }
+  }
+  __syncthreads();
+  const float Dh = D ? D[h] : 0.f;
+  for (int j = tid; j <= L / 2; j += NTHR) weights_pair(buf, coef + (size_t)h * L, cs, L, j, Dh);
 }
 
 // ---------------------------------------------------------------------------
@@ -183,15 +361,6 @@ struct KspecShape {
   static constexpr int BUF = cmax(lds_padded_size(L), 2 * HP);
   static constexpr int ZPT = (H2 + NT - 1) / NT;
 };
-
-// (1 -+ i W_{2M}^j)/2 with W_{2M}^j = e^{-i pi j / M} given as (cos, sin) of pi j / M:
-//   p = ((1 - s) - i c)/2,  q = ((1 + s) + i c)/2.
-__device__ __forceinline__ float2 rfft_x(float2 zj, float2 zmj, float2 csj) {
-  // X_j = p_j Z_j + q_j conj(Z_{M-j})
-  const float2 p = make_float2(0.5f * (1.0f - csj.y), -0.5f * csj.x);
-  const float2 q = make_float2(0.5f * (1.0f + csj.y), 0.5f * csj.x);
-  return cadd(cmul(p, zj), cmul(q, cconj(zmj)));
-}
 
 template <int LOG2L, bool FROM_TIME>
 __global__ __launch_bounds__(KspecShape<LOG2L>::NT) void kspec_kernel(
@@ -468,32 +637,49 @@ bool lds_path(const s4dplr_plan* p) { return p->log2L <= S4DPLR_LDS_MAX_LOG2L; }
 template <typename T>
 static T* at(unsigned char* ws, size_t off) { return reinterpret_cast<T*>(ws + off); }
 
-hipError_t launch_pack(const s4dplr_plan* p, const float* lam, const float* P, const float* Q,
-                       const float* B, const float* C, const float* dt, unsigned char* ws,
-                       hipStream_t s) {
-  const int diag = (p->flags & S4DPLR_DIAGONAL) ? 1 : 0;
-  pack_kernel<<<p->H, 64, 0, s>>>(
-      reinterpret_cast<const float2*>(lam), reinterpret_cast<const float2*>(P),
-      reinterpret_cast<const float2*>(Q), reinterpret_cast<const float2*>(B),
-      reinterpret_cast<const float2*>(C), dt, at<float4>(ws, p->off_poles),
-      at<float4>(ws, p->off_chan), p->N, p->NP, diag);
-  return hipGetLastError();
+static ParamPtrs param_ptrs(const float* lam, const float* P, const float* Q, const float* B,
+                            const float* C, const float* dt) {
+  return ParamPtrs{reinterpret_cast<const float2*>(lam), reinterpret_cast<const float2*>(P),
+                   reinterpret_cast<const float2*>(Q), reinterpret_cast<const float2*>(B),
+                   reinterpret_cast<const float2*>(C), dt};
 }
 
-hipError_t launch_cauchy(const s4dplr_plan* p, unsigned char* ws, hipStream_t s) {
+static bool fused_path(const s4dplr_plan* p) { return p->log2L >= 5 && p->log2L <= 10; }
+
+template <int LOG2L>
+static void kgen_launch(const s4dplr_plan* p, const ParamPtrs& pp, const float* D,
+                        const float* Ktime, float* Kout, unsigned char* ws, hipStream_t s) {
+  if constexpr (LOG2L >= 5 && LOG2L <= 10) {
+    using S = KgenShape<LOG2L>;
+    float4* coef = at<float4>(ws, p->off_coef);
+    const float* tanT = at<const float>(ws, p->off_tan);
+    const float2* tw = at<const float2>(ws, p->off_twL);
+    const float2* cs = at<const float2>(ws, p->off_cs);
+    if (Ktime)
+      kgen_wave_kernel<LOG2L, false, true><<<p->H, S::NTHR, 0, s>>>(pp, D, Ktime, nullptr, coef,
+                                                                  tanT, tw, cs, p->N, p->NP);
+    else if (p->flags & S4DPLR_DIAGONAL)
+      kgen_wave_kernel<LOG2L, true, false><<<p->H, S::NTHR, 0, s>>>(pp, D, nullptr, Kout, coef,
+                                                                  tanT, tw, cs, p->N, p->NP);
+    else
+      kgen_wave_kernel<LOG2L, false, false><<<p->H, S::NTHR, 0, s>>>(pp, D, nullptr, Kout, coef,
+                                                                   tanT, tw, cs, p->N, p->NP);
+  }
+}
+
+hipError_t launch_cauchy(const s4dplr_plan* p, const ParamPtrs& pp, unsigned char* ws,
+                         hipStream_t s) {
   constexpr int F = 2;
   const int per_block = F * kCauchyThreads;
   dim3 grid((p->L + per_block - 1) / per_block, p->H);
-  const float4* poles = at<const float4>(ws, p->off_poles);
-  const float4* chan = at<const float4>(ws, p->off_chan);
   const float* tanT = at<const float>(ws, p->off_tan);
   float2* khat = at<float2>(ws, p->off_khat);
   const int perm_m1 = lds_path(p) ? 0 : p->L / 256;
   if (p->flags & S4DPLR_DIAGONAL)
-    cauchy_kernel<F, true><<<grid, kCauchyThreads, 0, s>>>(poles, chan, tanT, khat, p->NP, p->L,
+    cauchy_kernel<F, true><<<grid, kCauchyThreads, 0, s>>>(pp, tanT, khat, p->N, p->NP, p->L,
                                                            perm_m1);
   else
-    cauchy_kernel<F, false><<<grid, kCauchyThreads, 0, s>>>(poles, chan, tanT, khat, p->NP, p->L,
+    cauchy_kernel<F, false><<<grid, kCauchyThreads, 0, s>>>(pp, tanT, khat, p->N, p->NP, p->L,
                                                             perm_m1);
   return hipGetLastError();
 }
@@ -556,11 +742,34 @@ static void conv_launch(const s4dplr_plan* p, const float* u, float* y, unsigned
     default: return hipErrorInvalidValue;   \
   }
 
-hipError_t launch_kspec(const s4dplr_plan* p, const float* Ktime, const float* D, float* Kout,
-                        unsigned char* ws, hipStream_t s) {
+static hipError_t launch_kspec(const s4dplr_plan* p, const float* Ktime, const float* D,
+                               float* Kout, unsigned char* ws, hipStream_t s) {
   if (!lds_path(p)) return launch_big_kspec(p, Ktime, D, Kout, ws, s);
   S4_DISPATCH_LOG2L(kspec_launch, p, Ktime, D, Kout, ws, s);
   return hipGetLastError();
+}
+
+hipError_t launch_kernel_gen(const s4dplr_plan* p, const float* lam, const float* P,
+                             const float* Q, const float* B, const float* C, const float* dt,
+                             const float* D, float* Kout, unsigned char* ws, hipStream_t s) {
+  const ParamPtrs pp = param_ptrs(lam, P, Q, B, C, dt);
+  if (fused_path(p)) {
+    S4_DISPATCH_LOG2L(kgen_launch, p, pp, D, nullptr, Kout, ws, s);
+    return hipGetLastError();
+  }
+  hipError_t e = launch_cauchy(p, pp, ws, s);
+  if (e != hipSuccess) return e;
+  return launch_kspec(p, nullptr, D, Kout, ws, s);
+}
+
+hipError_t launch_spectrum_from_time(const s4dplr_plan* p, const float* Ktime, const float* D,
+                                     unsigned char* ws, hipStream_t s) {
+  if (fused_path(p)) {
+    const ParamPtrs pp{};
+    S4_DISPATCH_LOG2L(kgen_launch, p, pp, D, Ktime, nullptr, ws, s);
+    return hipGetLastError();
+  }
+  return launch_kspec(p, Ktime, D, nullptr, ws, s);
 }
 
 hipError_t launch_conv(const s4dplr_plan* p, const float* u, float* y, unsigned char* ws,
