@@ -209,7 +209,8 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_kernel(
 template <int LOG2L>
 struct KgenShape {
   static constexpr int L = 1 << LOG2L;
-  static constexpr int NTHR = L < 256 ? 256 : L;
+  static constexpr int F = L >= 512 ? 2 : 1;               // frequencies per thread
+  static constexpr int NTHR = L / F < 256 ? 256 : L / F;
   static constexpr int T = L / 16;
   static constexpr int P = fft_num_passes(LOG2L);
   static constexpr int MP = lds_padded_size(L);
@@ -269,12 +270,23 @@ __global__ __launch_bounds__(KgenShape<LOG2L>::NTHR) void kgen_wave_kernel(
     const float2 sum = block_sum2<NTHR>(part, red, tid);
     const float dt = pp.dt[h];
     const float2 nyq = make_float2(0.5f * dt * sum.x, 0.5f * dt * sum.y);
-    if (tid < L) {
-      const float T0 = tanT[tid];
-      const float G[1] = {(2.0f / dt) * T0};
-      float acc[1][8] = {{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}};
-      cauchy_sums<1, DIAG>(rec, NP, G, acc);
-      buf[lds_pad(tid)] = cauchy_epilogue<DIAG>(acc[0], T0, 2 * tid == L, nyq);
+    {
+      constexpr int F = S::F;
+      float T0[F], G[F], acc[F][8];
+#pragma unroll
+      for (int f = 0; f < F; ++f) {
+        const int l = tid + f * NTHR;
+        T0[f] = l < L ? tanT[l] : 0.f;
+        G[f] = (2.0f / dt) * T0[f];
+#pragma unroll
+        for (int a = 0; a < 8; ++a) acc[f][a] = 0.f;
+      }
+      cauchy_sums<F, DIAG>(rec, NP, G, acc);
+#pragma unroll
+      for (int f = 0; f < F; ++f) {
+        const int l = tid + f * NTHR;
+        if (l < L) buf[lds_pad(l)] = cauchy_epilogue<DIAG>(acc[f], T0[f], 2 * l == L, nyq);
+      }
     }
     __syncthreads();
     // inverse transform of length L; K_k = Re / L
@@ -554,52 +566,98 @@ __global__ __launch_bounds__(kWaveConvThreads) void conv_wave_kernel(
   const int rows = H * batch;
   const int ngroups = (rows + S::RPW - 1) / S::RPW;
   const int gw = xcd_remap(blockIdx.x, gridDim.x) * (kWaveConvThreads / 64) + wave;
+  // The next row's input and the current channel's weights are fetched ahead
+  // of their use so that their memory latency overlaps the transforms.
+  auto row_of = [&](int g, int& h, size_t& roff) -> bool {
+    const int lrow = g * S::RPW + rw;            // logical row: channel-major
+    const bool act = lrow < rows;
+    h = act ? lrow / batch : 0;
+    const int b = act ? lrow - h * batch : 0;
+    roff = ((size_t)b * H + h) * M;
+    return act;
+  };
+  float2 upre[8];
+  {
+    int h0;
+    size_t r0;
+    const bool a0 = row_of(gw * groups_per_wave, h0, r0);
+    const float2* __restrict__ ur = reinterpret_cast<const float2*>(u + (a0 ? r0 : 0));
+#pragma unroll
+    for (int r = 0; r < 8; ++r) upre[r] = ur[lt + T * r];
+    if (!a0) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) upre[r] = make_float2(0.f, 0.f);
+    }
+  }
+  float4 cw[16];
+  int hc = -1;
   for (int gi = 0; gi < groups_per_wave; ++gi) {
     const int g = gw * groups_per_wave + gi;
     if (g >= ngroups) break;
-    const int lrow = g * S::RPW + rw;            // logical row: channel-major
-    const bool active = lrow < rows;
-    const int h = active ? lrow / batch : 0;
-    const int b = active ? lrow - h * batch : 0;
-    const size_t roff = ((size_t)b * H + h) * M;
+    int h;
+    size_t roff;
+    const bool active = row_of(g, h, roff);
     float2 v[16];
     // forward pass 0 straight from memory: z_{lt + T r}, r < 8; the rest is padding
-    const float2* __restrict__ ur = reinterpret_cast<const float2*>(u + roff);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) v[r] = active ? ur[lt + T * r] : make_float2(0.f, 0.f);
+    for (int r = 0; r < 8; ++r) v[r] = upre[r];
+    if (h != hc) {
+      const float4* __restrict__ cf = coef + (size_t)h * M;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cw[r] = cf[lt + T * r];
+      hc = h;
+    }
     dft16_fwd_half_input(v);
     WPass<LOG2M, 0>::store(v, buf, lt);
     wave_sync();
-    if constexpr (P > 1) {
+    if constexpr (P > 2) {
       WPass<LOG2M, 1>::load(v, buf, lt);
       WPass<LOG2M, 1>::template compute<false>(v, w1);
       WPass<LOG2M, 1>::store(v, buf, lt);
       wave_sync();
     }
-    if constexpr (P > 2) {
-      WPass<LOG2M, 2>::load(v, buf, lt);
-      WPass<LOG2M, 2>::template compute<false>(v, w2);
-      WPass<LOG2M, 2>::store(v, buf, lt);
-      wave_sync();
-    }
-    // spectral weights, read straight into the inverse pass-0 layout j = lt + T r
-    const float4* __restrict__ cf = coef + (size_t)h * M;
+    // last forward pass; its outputs X_s of butterfly q are the bins
+    // lt + T (q + s NB), which is exactly the inverse pass-0 input set of this
+    // lane, so Z_j stays in registers and only Z_{M-j} comes from LDS
+    using FL = WPass<LOG2M, P - 1>;
+    FL::load(v, buf, lt);
+    if constexpr (P == 2) FL::template compute<false>(v, w1);
+    else FL::template compute<false>(v, w2);
+    FL::store(v, buf, lt);
+    float2 z[16];
+#pragma unroll
+    for (int q = 0; q < FL::NB; ++q)
+#pragma unroll
+      for (int s2 = 0; s2 < FL::R; ++s2) z[q + s2 * FL::NB] = v[q * FL::R + bitrev<FL::RL>(s2)];
+    wave_sync();
+    // spectral weights: Z'_j = alpha_j Z_j + beta_j conj(Z_{M-j}), j = lt + T r
     {
-      // Z_j at pad(lt) + pad_shift(T r); Z_{M-j} at pad(M - T r - lt), with
-      // pad(A - lt) = A + A/16 + pad(-lt) for A a multiple of 16 (j = 0 maps to 0)
-      const float2* __restrict__ bj = buf + lds_pad(lt);
+      // Z_{M-j} at pad(M - T r - lt) = (M - T r) + (M - T r)/16 + pad(-lt) for
+      // M - T r a multiple of 16 (j = 0 maps to 0)
       const int nlt = -lt;
       const float2* __restrict__ bm = buf + (nlt + (nlt >> 4));
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = lt + T * r;
-        const float2 zj = bj[pad_shift(lt, T * r)];
         float2 zm;
         if (r == 0) zm = buf[lds_pad((M - lt) & (M - 1))];
         else if (((M - T * r) & 15) == 0) zm = bm[(M - T * r) + ((M - T * r) >> 4)];
         else zm = buf[lds_pad(M - j)];
-        const float4 c = cf[j];
-        v[r] = cadd(cmul(make_float2(c.x, c.y), zj), cmul(make_float2(c.z, c.w), cconj(zm)));
+        const float4 c = cw[r];
+        v[r] = cadd(cmul(make_float2(c.x, c.y), z[r]), cmul(make_float2(c.z, c.w), cconj(zm)));
+      }
+    }
+    // next row's input, in flight during the inverse transform
+    if (gi + 1 < groups_per_wave && g + 1 < ngroups) {
+      int hn;
+      size_t rn;
+      const bool an = row_of(g + 1, hn, rn);
+      const float2* __restrict__ ur = reinterpret_cast<const float2*>(u + (an ? rn : 0));
+#pragma unroll
+      for (int r = 0; r < 8; ++r) upre[r] = ur[lt + T * r];
+      if (!an) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) upre[r] = make_float2(0.f, 0.f);
       }
     }
     wave_sync();
