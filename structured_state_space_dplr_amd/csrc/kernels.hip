@@ -39,14 +39,15 @@ namespace s4 {
 // ---------------------------------------------------------------------------
 // Stage 1a/1b: pole records and the Cauchy sums at the L roots of unity
 // ---------------------------------------------------------------------------
-// A block first writes its channel's pole records into LDS:
-//   rec[3n]   = (Im Lambda_n, (Re Lambda_n)^2, -Re Lambda_n, 0)
-//   rec[3n+1] = (w00, w01),  rec[3n+2] = (w10, w11)
-// with w00 = C B, w01 = C P, w10 = conj(Q) B, w11 = conj(Q) P.  Poles n in
-// [N, NP) (NP = N rounded up to kPoleUnroll) are inert: zero weights,
-// Lambda = -1.  Every Cauchy term is then pure VALU work on broadcast LDS
-// operands:  y = G - Im Lambda, d = (Re Lambda)^2 + y^2,
-//            rho = (-Re Lambda - i y)/d = 1/(i G - Lambda),  k_ab += w_ab rho.
+// A block first writes its channel's pole records into LDS (5 float4 each):
+//   rec[5n]   = (Im Lambda_n, (Re Lambda_n)^2, K00),  rec[5n+1] = (w00, K01),
+//   rec[5n+2] = (w01, K10),  rec[5n+3] = (w10, K11),  rec[5n+4] = (w11, 0)
+// with w00 = C B, w01 = C P, w10 = conj(Q) B, w11 = conj(Q) P and
+// K_ab = -Re(Lambda_n) w_ab (both parts).  Poles n in [N, NP) (NP = N rounded
+// up to kPoleUnroll) are inert: zero weights, Lambda = -1.  Per term, with
+// y = G - Im Lambda and r = 1 / ((Re Lambda)^2 + y^2),
+//   w_ab / (i G - Lambda) = r (K_ab.re + w_ab.im y) + i r (K_ab.im - w_ab.re y),
+// i.e. two FMAs for the numerator and two for the accumulation per sum.
 constexpr int kPoleUnroll = 4;
 constexpr int kMaxPoles = 256;
 
@@ -59,6 +60,8 @@ struct ParamPtrs {
   const float* dt;
 };
 
+constexpr int kRec = 5;   // float4 per pole record
+
 // Builds the records of channel h with threads [0, nthr); returns this
 // thread's partial sum of w00 = C B over its poles.
 __device__ __forceinline__ float2 build_pole_records(const ParamPtrs& pp, int h, int N, int NP,
@@ -66,6 +69,7 @@ __device__ __forceinline__ float2 build_pole_records(const ParamPtrs& pp, int h,
                                                      int nthr) {
   float2 s = make_float2(0.f, 0.f);
   for (int n = tid; n < NP; n += nthr) {
+    float4* rn = rec + kRec * n;
     if (n < N) {
       const size_t idx = (size_t)h * N + n;
       const float2 l = pp.lam[idx], b = pp.B[idx], c = pp.C[idx];
@@ -73,14 +77,19 @@ __device__ __forceinline__ float2 build_pole_records(const ParamPtrs& pp, int h,
       const float2 qv = diag ? make_float2(0.f, 0.f) : (pp.Q ? pp.Q[idx] : pv);
       const float2 w00 = cmul(c, b), w01 = cmul(c, pv);
       const float2 w10 = cmul(cconj(qv), b), w11 = cmul(cconj(qv), pv);
-      rec[3 * n + 0] = make_float4(l.y, l.x * l.x, -l.x, 0.f);
-      rec[3 * n + 1] = make_float4(w00.x, w00.y, w01.x, w01.y);
-      rec[3 * n + 2] = make_float4(w10.x, w10.y, w11.x, w11.y);
+      const float na = -l.x;
+      rn[0] = make_float4(l.y, l.x * l.x, na * w00.x, na * w00.y);
+      rn[1] = make_float4(w00.x, w00.y, na * w01.x, na * w01.y);
+      rn[2] = make_float4(w01.x, w01.y, na * w10.x, na * w10.y);
+      rn[3] = make_float4(w10.x, w10.y, na * w11.x, na * w11.y);
+      rn[4] = make_float4(w11.x, w11.y, 0.f, 0.f);
       s = cadd(s, w00);
     } else {
-      rec[3 * n + 0] = make_float4(0.f, 1.f, 1.f, 0.f);
-      rec[3 * n + 1] = make_float4(0.f, 0.f, 0.f, 0.f);
-      rec[3 * n + 2] = make_float4(0.f, 0.f, 0.f, 0.f);
+      rn[0] = make_float4(0.f, 1.f, 0.f, 0.f);
+      rn[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      rn[2] = make_float4(0.f, 0.f, 0.f, 0.f);
+      rn[3] = make_float4(0.f, 0.f, 0.f, 0.f);
+      rn[4] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
   return s;
@@ -110,34 +119,29 @@ __device__ __forceinline__ void cauchy_sums(const float4* __restrict__ rec, int 
   for (int n0 = 0; n0 < NP; n0 += kPoleUnroll) {
 #pragma unroll
     for (int n = n0; n < n0 + kPoleUnroll; ++n) {
-      const float4 p0 = rec[3 * n + 0];
-      const float4 p1 = rec[3 * n + 1];
-      float4 p2 = make_float4(0.f, 0.f, 0.f, 0.f);
-      if constexpr (!DIAG) p2 = rec[3 * n + 2];
+      const float4* rn = rec + kRec * n;
+      const float4 p0 = rn[0], p1 = rn[1];
+      float4 p2 = make_float4(0.f, 0.f, 0.f, 0.f), p3 = p2, p4 = p2;
+      if constexpr (!DIAG) {
+        p2 = rn[2];
+        p3 = rn[3];
+        p4 = rn[4];
+      }
 #pragma unroll
       for (int f = 0; f < F; ++f) {
         const float yv = G[f] - p0.x;
-        const float d = fmaf(yv, yv, p0.y);
-        const float r = __builtin_amdgcn_rcpf(d);
-        const float qr = p0.z * r;
-        const float qi = -yv * r;
-        acc[f][0] = fmaf(p1.x, qr, acc[f][0]);
-        acc[f][0] = fmaf(-p1.y, qi, acc[f][0]);
-        acc[f][1] = fmaf(p1.x, qi, acc[f][1]);
-        acc[f][1] = fmaf(p1.y, qr, acc[f][1]);
+        const float r = __builtin_amdgcn_rcpf(fmaf(yv, yv, p0.y));
+        // sum 00: w = p1.xy, K = p0.zw
+        acc[f][0] = fmaf(r, fmaf(p1.y, yv, p0.z), acc[f][0]);
+        acc[f][1] = fmaf(r, fmaf(-p1.x, yv, p0.w), acc[f][1]);
         if constexpr (!DIAG) {
-          acc[f][2] = fmaf(p1.z, qr, acc[f][2]);
-          acc[f][2] = fmaf(-p1.w, qi, acc[f][2]);
-          acc[f][3] = fmaf(p1.z, qi, acc[f][3]);
-          acc[f][3] = fmaf(p1.w, qr, acc[f][3]);
-          acc[f][4] = fmaf(p2.x, qr, acc[f][4]);
-          acc[f][4] = fmaf(-p2.y, qi, acc[f][4]);
-          acc[f][5] = fmaf(p2.x, qi, acc[f][5]);
-          acc[f][5] = fmaf(p2.y, qr, acc[f][5]);
-          acc[f][6] = fmaf(p2.z, qr, acc[f][6]);
-          acc[f][6] = fmaf(-p2.w, qi, acc[f][6]);
-          acc[f][7] = fmaf(p2.z, qi, acc[f][7]);
-          acc[f][7] = fmaf(p2.w, qr, acc[f][7]);
+          // sum 01: w = p2.xy, K = p1.zw; sum 10: w = p3.xy, K = p2.zw; sum 11: w = p4.xy, K = p3.zw
+          acc[f][2] = fmaf(r, fmaf(p2.y, yv, p1.z), acc[f][2]);
+          acc[f][3] = fmaf(r, fmaf(-p2.x, yv, p1.w), acc[f][3]);
+          acc[f][4] = fmaf(r, fmaf(p3.y, yv, p2.z), acc[f][4]);
+          acc[f][5] = fmaf(r, fmaf(-p3.x, yv, p2.w), acc[f][5]);
+          acc[f][6] = fmaf(r, fmaf(p4.y, yv, p3.z), acc[f][6]);
+          acc[f][7] = fmaf(r, fmaf(-p4.x, yv, p3.w), acc[f][7]);
         }
       }
     }
@@ -173,7 +177,7 @@ template <int F, bool DIAG>
 __global__ __launch_bounds__(kCauchyThreads) void cauchy_kernel(
     ParamPtrs pp, const float* __restrict__ tanT, float2* __restrict__ khat, int N, int NP, int L,
     int perm_m1) {
-  __shared__ float4 rec[3 * kMaxPoles];
+  __shared__ float4 rec[kRec * kMaxPoles];
   __shared__ float2 red[kCauchyThreads / 64];
   const int h = blockIdx.y, tid = threadIdx.x;
   const float2 part = build_pole_records(pp, h, N, NP, DIAG, rec, tid, kCauchyThreads);
@@ -229,11 +233,10 @@ __device__ __forceinline__ float2 rfft_x(float2 zj, float2 zmj, float2 csj) {
 //   S_j = X_j + D,  alpha_j = ((1 - s_j) S_j + (1 + s_j) conj(S_{L-j})) / (2L),
 //   beta_j = i c_j (S_j - conj(S_{L-j})) / (2L),   (c_j, s_j) = (cos, sin)(pi j / L).
 __device__ __forceinline__ void weights_pair(const float2* __restrict__ Zb, float4* __restrict__ cf,
-                                             const float2* __restrict__ cs, int L, int j, float Dh) {
+                                             float2 csj, float2 csm, int L, int j, float Dh) {
   const float sc = 0.5f / (float)L;
   const int jm = L - j;
   const float2 zj = Zb[lds_pad(j)], zm = Zb[lds_pad(jm & (L - 1))];
-  const float2 csj = cs[j], csm = cs[jm];
   float2 sj = rfft_x(zj, zm, csj), sm = rfft_x(zm, zj, csm);
   sj.x += Dh;
   sm.x += Dh;
@@ -258,13 +261,29 @@ __global__ __launch_bounds__(KgenShape<LOG2L>::NTHR) void kgen_wave_kernel(
     const float2* __restrict__ tw, const float2* __restrict__ cs, int N, int NP) {
   using S = KgenShape<LOG2L>;
   constexpr int L = S::L, T = S::T, NTHR = S::NTHR, P = S::P;
-  __shared__ float4 rec[FROM_TIME ? 3 : 3 * kMaxPoles];
+  __shared__ float4 rec[FROM_TIME ? 1 : kRec * kMaxPoles];
   __shared__ float2 red[NTHR / 64];
   __shared__ float2 buf[S::MP];
   const int h = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63;
   const bool fft_lane = tid < T;          // lanes of wave 0 that hold the transform
-  float2 v[16], w[16];
+  float2 v[16], wA[16], wB[16];
+  // everything the serial tail reads from memory is fetched up front
+  if (fft_lane) {
+    if constexpr (P > 2) WPass<LOG2L, 1>::load_tw(wA, tw, lane);
+    WPass<LOG2L, P - 1>::load_tw(wB, tw, lane);
+  }
+  constexpr int NW = (L / 2 + NTHR) / NTHR;     // bin pairs per thread in the weight step
+  float2 csj[NW], csm[NW];
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int j = tid + i * NTHR;
+    if (j <= L / 2) {
+      csj[i] = cs[j];
+      csm[i] = cs[L - j];
+    }
+  }
+  const float Dh = D ? D[h] : 0.f;
   if constexpr (!FROM_TIME) {
     const float2 part = build_pole_records(pp, h, N, NP, DIAG, rec, tid, NTHR);
     const float2 sum = block_sum2<NTHR>(part, red, tid);
@@ -292,20 +311,18 @@ __global__ __launch_bounds__(KgenShape<LOG2L>::NTHR) void kgen_wave_kernel(
     // inverse transform of length L; K_k = Re / L
     if (fft_lane) {
       WPass<LOG2L, 0>::load(v, buf, lane);
-      WPass<LOG2L, 0>::template compute<true>(v, w);
+      WPass<LOG2L, 0>::template compute<true>(v, wA);
       WPass<LOG2L, 0>::store(v, buf, lane);
       wave_sync();
       if constexpr (P > 2) {
-        WPass<LOG2L, 1>::load_tw(w, tw, lane);
         WPass<LOG2L, 1>::load(v, buf, lane);
-        WPass<LOG2L, 1>::template compute<true>(v, w);
+        WPass<LOG2L, 1>::template compute<true>(v, wA);
         WPass<LOG2L, 1>::store(v, buf, lane);
         wave_sync();
       }
       using LP = WPass<LOG2L, P - 1>;
-      LP::load_tw(w, tw, lane);
       LP::load(v, buf, lane);
-      LP::template compute<true>(v, w);
+      LP::template compute<true>(v, wB);
       const float invL = 1.0f / (float)L;
       wave_sync();
 #pragma unroll
@@ -336,24 +353,24 @@ __global__ __launch_bounds__(KgenShape<LOG2L>::NTHR) void kgen_wave_kernel(
     dft16_fwd_half_input(v);
     WPass<LOG2L, 0>::store(v, buf, lane);
     wave_sync();
-    if constexpr (P > 1) {
-      WPass<LOG2L, 1>::load_tw(w, tw, lane);
+    if constexpr (P > 2) {
       WPass<LOG2L, 1>::load(v, buf, lane);
-      WPass<LOG2L, 1>::template compute<false>(v, w);
+      WPass<LOG2L, 1>::template compute<false>(v, wA);
       WPass<LOG2L, 1>::store(v, buf, lane);
       wave_sync();
     }
-    if constexpr (P > 2) {
-      WPass<LOG2L, 2>::load_tw(w, tw, lane);
-      WPass<LOG2L, 2>::load(v, buf, lane);
-      WPass<LOG2L, 2>::template compute<false>(v, w);
-      WPass<LOG2L, 2>::store(v, buf, lane);
-      wave_sync();
-    }
+    using LP = WPass<LOG2L, P - 1>;
+    LP::load(v, buf, lane);
+    LP::template compute<false>(v, wB);
+    LP::store(v, buf, lane);
+    wave_sync();
   }
   __syncthreads();
-  const float Dh = D ? D[h] : 0.f;
-  for (int j = tid; j <= L / 2; j += NTHR) weights_pair(buf, coef + (size_t)h * L, cs, L, j, Dh);
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int j = tid + i * NTHR;
+    if (j <= L / 2) weights_pair(buf, coef + (size_t)h * L, csj[i], csm[i], L, j, Dh);
+  }
 }
 
 // ---------------------------------------------------------------------------
