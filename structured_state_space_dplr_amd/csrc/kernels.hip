@@ -705,6 +705,143 @@ __global__ __launch_bounds__(kWaveConvThreads) void conv_wave_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Stage 2 for 2048 <= L <= 16384: block-resident rows
+// ---------------------------------------------------------------------------
+// The same transform layout as the wave-resident kernel (M/16 threads per
+// row, 16 points each), with the row spread over several wavefronts, so the
+// passes are separated by workgroup barriers.  The padded row occupies M*17/16
+// complex of LDS (139 KB at L = 16384).
+template <int LOG2M>
+struct RowConvShape {
+  static constexpr int M = 1 << LOG2M;
+  static constexpr int T = M / 16;                 // threads per row
+  static constexpr int NTHR = T < 256 ? 256 : T;
+  static constexpr int RPB = NTHR / T;             // rows per block
+  static constexpr int P = fft_num_passes(LOG2M);
+  static constexpr int MP = lds_padded_size(M);
+  static_assert(LOG2M >= 11 && LOG2M <= 14, "block-resident range");
+};
+
+template <int LOG2M, int PASS, bool INV>
+__device__ __forceinline__ void row_pass(float2 (&v)[16], float2* __restrict__ buf, int lt,
+                                         const float2* __restrict__ tw) {
+  using W = WPass<LOG2M, PASS>;
+  float2 w[16];
+  W::load_tw(w, tw, lt);
+  W::load(v, buf, lt);
+  __syncthreads();
+  W::template compute<INV>(v, w);
+  W::store(v, buf, lt);
+  __syncthreads();
+}
+
+template <int LOG2M>
+__global__ __launch_bounds__(RowConvShape<LOG2M>::NTHR) void conv_rows_kernel(
+    const float* __restrict__ u, float* __restrict__ y, const float4* __restrict__ coef,
+    const float2* __restrict__ tw, int H, int batch, int groups_per_block) {
+  using S = RowConvShape<LOG2M>;
+  constexpr int M = S::M, T = S::T, P = S::P;
+  using FL = WPass<LOG2M, P - 1>;
+  __shared__ float2 lds[S::RPB * S::MP];
+  const int tid = threadIdx.x;
+  const int rw = tid / T, lt = tid % T;
+  float2* buf = lds + rw * S::MP;
+  const int rows = H * batch;
+  const int ngroups = (rows + S::RPB - 1) / S::RPB;
+  const int gb = xcd_remap(blockIdx.x, gridDim.x);
+  auto row_of = [&](int g, int& h, size_t& roff) -> bool {
+    const int lrow = g * S::RPB + rw;            // logical row: channel-major
+    const bool act = lrow < rows;
+    h = act ? lrow / batch : 0;
+    const int b = act ? lrow - h * batch : 0;
+    roff = ((size_t)b * H + h) * M;
+    return act;
+  };
+  float2 upre[8];
+  {
+    int h0;
+    size_t r0;
+    const bool a0 = row_of(gb * groups_per_block, h0, r0);
+    const float2* __restrict__ ur = reinterpret_cast<const float2*>(u + (a0 ? r0 : 0));
+#pragma unroll
+    for (int r = 0; r < 8; ++r) upre[r] = a0 ? ur[lt + T * r] : make_float2(0.f, 0.f);
+  }
+  for (int gi = 0; gi < groups_per_block; ++gi) {
+    const int g = gb * groups_per_block + gi;
+    if (g >= ngroups) break;                     // uniform over the block
+    int h;
+    size_t roff;
+    const bool active = row_of(g, h, roff);
+    float2 v[16];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) v[r] = upre[r];
+    dft16_fwd_half_input(v);
+    __syncthreads();                             // the previous row's last reads are done
+    WPass<LOG2M, 0>::store(v, buf, lt);
+    __syncthreads();
+    if constexpr (P > 2) row_pass<LOG2M, 1, false>(v, buf, lt, tw);
+    if constexpr (P > 3) row_pass<LOG2M, 2, false>(v, buf, lt, tw);
+    // last forward pass: the bins lt + T (q + s NB) stay in registers
+    float2 z[16];
+    {
+      float2 w[16];
+      FL::load_tw(w, tw, lt);
+      FL::load(v, buf, lt);
+      __syncthreads();
+      FL::template compute<false>(v, w);
+      FL::store(v, buf, lt);
+#pragma unroll
+      for (int q = 0; q < FL::NB; ++q)
+#pragma unroll
+        for (int s2 = 0; s2 < FL::R; ++s2) z[q + s2 * FL::NB] = v[q * FL::R + bitrev<FL::RL>(s2)];
+      __syncthreads();
+    }
+    {
+      const float4* __restrict__ cf = coef + (size_t)h * M;
+      const int nlt = -lt;
+      const float2* __restrict__ bm = buf + (nlt + (nlt >> 4));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float2 zm;
+        if (r == 0) zm = buf[lds_pad((M - lt) & (M - 1))];
+        else zm = bm[(M - T * r) + ((M - T * r) >> 4)];
+        const float4 c = cf[lt + T * r];
+        v[r] = cadd(cmul(make_float2(c.x, c.y), z[r]), cmul(make_float2(c.z, c.w), cconj(zm)));
+      }
+    }
+    // next row's input, in flight during the inverse transform
+    if (gi + 1 < groups_per_block && g + 1 < ngroups) {
+      int hn;
+      size_t rn;
+      const bool an = row_of(g + 1, hn, rn);
+      const float2* __restrict__ ur = reinterpret_cast<const float2*>(u + (an ? rn : 0));
+#pragma unroll
+      for (int r = 0; r < 8; ++r) upre[r] = an ? ur[lt + T * r] : make_float2(0.f, 0.f);
+    }
+    __syncthreads();                             // all partner reads done
+    WPass<LOG2M, 0>::template compute<true>(v, z);
+    WPass<LOG2M, 0>::store(v, buf, lt);
+    __syncthreads();
+    if constexpr (P > 2) row_pass<LOG2M, 1, true>(v, buf, lt, tw);
+    if constexpr (P > 3) row_pass<LOG2M, 2, true>(v, buf, lt, tw);
+    {
+      float2 w[16];
+      FL::load_tw(w, tw, lt);
+      FL::load(v, buf, lt);
+      FL::template compute<true>(v, w);
+    }
+    float2* __restrict__ yr = reinterpret_cast<float2*>(y + roff);
+#pragma unroll
+    for (int q = 0; q < FL::NB; ++q) {
+      const int j = lt + q * T;                   // j < NS in the last pass
+#pragma unroll
+      for (int s2 = 0; s2 < FL::R / 2; ++s2)
+        if (active) yr[j + s2 * FL::NS] = v[q * FL::R + bitrev<FL::RL>(s2)];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 bool lds_path(const s4dplr_plan* p) { return p->log2L <= S4DPLR_LDS_MAX_LOG2L; }
@@ -788,6 +925,22 @@ static void conv_launch(const s4dplr_plan* p, const float* u, float* y, unsigned
     conv_wave_kernel<LOG2L><<<blocks, kWaveConvThreads, 0, s>>>(
         u, y, at<const float4>(ws, p->off_coef), at<const float2>(ws, p->off_twL), p->H,
         p->batch, gpw);
+    return;
+  }
+  if constexpr (LOG2L >= 11 && LOG2L <= 14) {
+    using R = RowConvShape<LOG2L>;
+    const int rows = p->batch * p->H;
+    const int ngroups = (rows + R::RPB - 1) / R::RPB;
+    // blocks resident per CU, limited by LDS (160 KB) and 32 waves
+    constexpr int by_lds = (160 * 1024) / (R::RPB * R::MP * 8);
+    constexpr int by_waves = 32 / (R::NTHR / 64);
+    constexpr int per_cu = by_lds < by_waves ? by_lds : by_waves;
+    const int target = 256 * (per_cu > 0 ? per_cu : 1);
+    const int gpb = (ngroups + target - 1) / target;
+    const int blocks = (ngroups + gpb - 1) / gpb;
+    conv_rows_kernel<LOG2L><<<blocks, R::NTHR, 0, s>>>(
+        u, y, at<const float4>(ws, p->off_coef), at<const float2>(ws, p->off_twL), p->H,
+        p->batch, gpb);
     return;
   }
   using S = ConvShape<LOG2L>;
