@@ -113,6 +113,8 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
   if (!lds) off = align_up(off + 2 * sizeof(float) * (size_t)s4::fft_tw_size(log2L - 8));
   p->off_tw2 = off;
   if (!lds) off = align_up(off + 2 * sizeof(float) * (size_t)s4::fft_tw_size(8));
+  p->off_tw4 = off;
+  if (!lds) off = align_up(off + 2 * sizeof(float) * 512);
   p->tables_bytes = off;
   // Scratch region.
   p->off_khat = off;
@@ -143,6 +145,13 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
   } else {
     fft_twiddles(log2L - 8, reinterpret_cast<float*>(p->tables.data() + p->off_tw1));
     fft_twiddles(8, reinterpret_cast<float*>(p->tables.data() + p->off_tw2));
+    float* t4 = reinterpret_cast<float*>(p->tables.data() + p->off_tw4);
+    for (int i = 0; i < 512; ++i) {
+      const long m = i < 256 ? i : 256L * (i - 256);      // W_L^m
+      const double ang = -2.0 * M_PI * (double)(m % L) / (double)L;
+      t4[2 * i + 0] = (float)std::cos(ang);
+      t4[2 * i + 1] = (float)std::sin(ang);
+    }
   }
   *out = p;
   return S4DPLR_OK;

@@ -33,14 +33,19 @@ struct BigShape {
   static_assert(LOG2M >= 15 && LOG2M <= 16, "four-step range");
 };
 
-// e^{-2 pi i m / M} for 0 <= m < M from the table cs[j] = (cos, sin)(pi j / M).
-__device__ __forceinline__ float2 w_M(const float2* __restrict__ cs, int M, int m) {
-  if (2 * m <= M) {
-    const float2 c = cs[2 * m];
-    return make_float2(c.x, -c.y);
-  }
-  const float2 c = cs[2 * m - M];
-  return make_float2(-c.x, c.y);
+// The four-step twiddles W_M^m (m = n2 k1 < M) from two 256-entry tables
+// held in LDS: W_M^m = W_M^{256 (m >> 8)} * W_M^{m & 255}.  tw4 in the
+// workspace holds [lo: W_M^b, b < 256][hi: W_M^{256 a}, a < 256].
+struct TwM {
+  float2 lo[256];
+  float2 hi[256];
+};
+__device__ __forceinline__ void load_twM(TwM& t, const float2* __restrict__ tw4, int tid,
+                                         int nthr) {
+  for (int i = tid; i < 512; i += nthr) (i < 256 ? t.lo[i] : t.hi[i - 256]) = tw4[i];
+}
+__device__ __forceinline__ float2 w_M(const TwM& t, int m) {
+  return cmul(t.hi[m >> 8], t.lo[m & 255]);
 }
 
 // (1 -+ i W_{2M}^j)/2 applied to the pair (Z_j, Z_{M-j}): the bin X_j of the
@@ -58,11 +63,13 @@ __device__ __forceinline__ float2 big_rfft_x(float2 zj, float2 zmj, float2 csj) 
 template <int LOG2M>
 __global__ __launch_bounds__(kBigThreads) void big_cols_fwd_kernel(
     const float* __restrict__ x, float2* __restrict__ Y, const float2* __restrict__ tw1,
-    const float2* __restrict__ cs) {
+    const float2* __restrict__ tw4) {
   using S = BigShape<LOG2M>;
   constexpr int M = S::M, M1 = S::M1, M2 = S::M2, CT = S::CT, CP = S::CP;
   __shared__ float2 lds[CT * CP];
+  __shared__ TwM twm;
   const int tid = threadIdx.x, row = blockIdx.y, c0 = blockIdx.x * CT;
+  load_twM(twm, tw4, tid, kBigThreads);
   const float2* __restrict__ z = reinterpret_cast<const float2*>(x + (size_t)row * M);
   for (int idx = tid; idx < M1 * CT; idx += kBigThreads) {
     const int n1 = idx / CT, c = idx % CT;
@@ -73,7 +80,7 @@ __global__ __launch_bounds__(kBigThreads) void big_cols_fwd_kernel(
   float2* __restrict__ Yr = Y + (size_t)row * M;
   for (int idx = tid; idx < M1 * CT; idx += kBigThreads) {
     const int k1 = idx / CT, c = idx % CT, n2 = c0 + c;
-    Yr[k1 * M2 + n2] = cmul(lds[c * CP + lds_pad(k1)], w_M(cs, M, n2 * k1));
+    Yr[k1 * M2 + n2] = cmul(lds[c * CP + lds_pad(k1)], w_M(twm, n2 * k1));
   }
 }
 
@@ -120,11 +127,13 @@ __global__ __launch_bounds__(kBigThreads) void big_cols_inv_kernel(
 template <int LOG2M>
 __global__ __launch_bounds__(kBigThreads) void big_rows_inv_kernel(
     const float2* __restrict__ X, float2* __restrict__ Y, const float2* __restrict__ tw2,
-    const float2* __restrict__ cs) {
+    const float2* __restrict__ tw4) {
   using S = BigShape<LOG2M>;
   constexpr int M = S::M, M2 = S::M2, RT = S::RT, RP = S::RP;
   __shared__ float2 lds[RT * RP];
+  __shared__ TwM twm;
   const int tid = threadIdx.x, row = blockIdx.y, r0 = blockIdx.x * RT;
+  load_twM(twm, tw4, tid, kBigThreads);
   const float2* __restrict__ Xr = X + (size_t)row * M;
   for (int idx = tid; idx < RT * M2; idx += kBigThreads) {
     const int s = idx / M2, k2 = idx % M2;
@@ -135,7 +144,7 @@ __global__ __launch_bounds__(kBigThreads) void big_rows_inv_kernel(
   float2* __restrict__ Yr = Y + (size_t)row * M;
   for (int idx = tid; idx < RT * M2; idx += kBigThreads) {
     const int s = idx / M2, n2 = idx % M2, k1 = r0 + s;
-    Yr[k1 * M2 + n2] = cmulc(lds[s * RP + lds_pad(n2)], w_M(cs, M, n2 * k1));
+    Yr[k1 * M2 + n2] = cmulc(lds[s * RP + lds_pad(n2)], w_M(twm, n2 * k1));
   }
 }
 
@@ -150,12 +159,15 @@ __global__ __launch_bounds__(kBigThreads) void big_rows_inv_kernel(
 template <int LOG2M, bool CONV>
 __global__ __launch_bounds__(kBigThreads) void big_rows_pair_kernel(
     float2* __restrict__ Y, float4* __restrict__ coefp, const float* __restrict__ D,
-    const float2* __restrict__ tw2, const float2* __restrict__ cs, int batch) {
+    const float2* __restrict__ tw2, const float2* __restrict__ cs,
+    const float2* __restrict__ tw4, int batch) {
   using S = BigShape<LOG2M>;
   constexpr int M = S::M, M1 = S::M1, M2 = S::M2, RP = S::RP;
   constexpr int TASKS = 8;
   __shared__ float2 lds[2 * TASKS * RP];
+  __shared__ TwM twm;
   const int tid = threadIdx.x, row = blockIdx.y, t0 = blockIdx.x * TASKS;
+  if constexpr (CONV) load_twM(twm, tw4, tid, kBigThreads);
   const int h = CONV ? row / batch : row;     // logical rows: h*batch + b
   float2* __restrict__ Yr = Y + (size_t)row * M;
   auto slot_row = [&](int s) -> int {
@@ -218,7 +230,7 @@ __global__ __launch_bounds__(kBigThreads) void big_rows_pair_kernel(
       if (!task_valid(s)) continue;
       const int k1 = slot_row(s);
       if ((s & 1) && k1 == slot_row(s - 1)) continue;    // self-paired task: slot a only
-      Yr[k1 * M2 + n2] = cmulc(lds[s * RP + lds_pad(n2)], w_M(cs, M, n2 * k1));
+      Yr[k1 * M2 + n2] = cmulc(lds[s * RP + lds_pad(n2)], w_M(twm, n2 * k1));
     }
   }
 }
@@ -238,10 +250,11 @@ static void big_spectrum_from_time(const s4dplr_plan* p, const float* Ktime, con
   using S = BigShape<LOG2M>;
   float2* Y = wat<float2>(ws, p->off_big);
   const float2* cs = wat<const float2>(ws, p->off_cs);
+  const float2* tw4 = wat<const float2>(ws, p->off_tw4);
   big_cols_fwd_kernel<LOG2M><<<dim3(S::M2 / S::CT, p->H), kBigThreads, 0, s>>>(
-      Ktime, Y, wat<const float2>(ws, p->off_tw1), cs);
+      Ktime, Y, wat<const float2>(ws, p->off_tw1), tw4);
   big_rows_pair_kernel<LOG2M, false><<<dim3((S::M1 / 2 + 1 + 7) / 8, p->H), kBigThreads, 0, s>>>(
-      Y, wat<float4>(ws, p->off_coef), D, wat<const float2>(ws, p->off_tw2), cs, 1);
+      Y, wat<float4>(ws, p->off_coef), D, wat<const float2>(ws, p->off_tw2), cs, tw4, 1);
 }
 
 template <int LOG2M>
@@ -254,7 +267,7 @@ static void big_kspec(const s4dplr_plan* p, const float* Ktime, const float* D, 
     float* K = Kout ? Kout : wat<float>(ws, p->off_kbuf);
     big_rows_inv_kernel<LOG2M><<<dim3(S::M1 / S::RT, p->H), kBigThreads, 0, s>>>(
         wat<const float2>(ws, p->off_khat), Y, wat<const float2>(ws, p->off_tw2),
-        wat<const float2>(ws, p->off_cs));
+        wat<const float2>(ws, p->off_tw4));
     big_cols_inv_kernel<LOG2M, 1><<<dim3(S::M2 / S::CT, p->H), kBigThreads, 0, s>>>(
         Y, K, wat<const float2>(ws, p->off_tw1), 1.0f / (float)S::M);
     Ktime = K;
@@ -275,11 +288,13 @@ hipError_t launch_big_kspec(const s4dplr_plan* p, const float* Ktime, const floa
 template <int LOG2M>
 __global__ __launch_bounds__(kBigThreads) void big_conv_cols_fwd_kernel(
     const float* __restrict__ u, float2* __restrict__ Y, const float2* __restrict__ tw1,
-    const float2* __restrict__ cs, int H, int batch) {
+    const float2* __restrict__ tw4, int H, int batch) {
   using S = BigShape<LOG2M>;
   constexpr int M = S::M, M1 = S::M1, M2 = S::M2, CT = S::CT, CP = S::CP;
   __shared__ float2 lds[CT * CP];
+  __shared__ TwM twm;
   const int tid = threadIdx.x, lrow = blockIdx.y, c0 = blockIdx.x * CT;
+  load_twM(twm, tw4, tid, kBigThreads);
   const int h = lrow / batch, b = lrow - h * batch;
   const float2* __restrict__ z = reinterpret_cast<const float2*>(u + ((size_t)b * H + h) * M);
   for (int idx = tid; idx < M1 * CT; idx += kBigThreads) {
@@ -291,7 +306,7 @@ __global__ __launch_bounds__(kBigThreads) void big_conv_cols_fwd_kernel(
   float2* __restrict__ Yr = Y + (size_t)lrow * M;
   for (int idx = tid; idx < M1 * CT; idx += kBigThreads) {
     const int k1 = idx / CT, c = idx % CT, n2 = c0 + c;
-    Yr[k1 * M2 + n2] = cmul(lds[c * CP + lds_pad(k1)], w_M(cs, M, n2 * k1));
+    Yr[k1 * M2 + n2] = cmul(lds[c * CP + lds_pad(k1)], w_M(twm, n2 * k1));
   }
 }
 
@@ -325,10 +340,12 @@ static void big_conv(const s4dplr_plan* p, const float* u, float* y, unsigned ch
   const int rows = p->batch * p->H;
   float2* Y = wat<float2>(ws, p->off_big);
   const float2* cs = wat<const float2>(ws, p->off_cs);
+  const float2* tw4 = wat<const float2>(ws, p->off_tw4);
   big_conv_cols_fwd_kernel<LOG2M><<<dim3(S::M2 / S::CT, rows), kBigThreads, 0, s>>>(
-      u, Y, wat<const float2>(ws, p->off_tw1), cs, p->H, p->batch);
+      u, Y, wat<const float2>(ws, p->off_tw1), tw4, p->H, p->batch);
   big_rows_pair_kernel<LOG2M, true><<<dim3((S::M1 / 2 + 1 + 7) / 8, rows), kBigThreads, 0, s>>>(
-      Y, wat<float4>(ws, p->off_coef), nullptr, wat<const float2>(ws, p->off_tw2), cs, p->batch);
+      Y, wat<float4>(ws, p->off_coef), nullptr, wat<const float2>(ws, p->off_tw2), cs, tw4,
+      p->batch);
   big_conv_cols_inv_kernel<LOG2M><<<dim3(S::M2 / S::CT, rows), kBigThreads, 0, s>>>(
       Y, y, wat<const float2>(ws, p->off_tw1), p->H, p->batch);
 }

@@ -23,6 +23,7 @@ struct s4dplr_plan {
   size_t off_twH;    // FFT twiddles for transforms of L/2 points
   size_t off_tw1;    // long path: FFT twiddles for the column transforms (L/256 points)
   size_t off_tw2;    // long path: FFT twiddles for the row transforms (256 points)
+  size_t off_tw4;    // long path: [512] float2, W_L^b (b < 256) then W_L^(256 a) (a < 256)
   size_t tables_bytes;
   size_t off_khat;   // [H][L] float2: generating function at the roots of unity
   size_t off_coef;   // [H][L] float4: spectral weights (alpha, beta) of bin j
