@@ -192,3 +192,59 @@ def test_workspace_reuse_across_calls(s4):
     assert np.array_equal(outs[0], outs[2])
     assert _rel(outs[1], oracle_forward(x2)[1]) <= TOL
     plan.close()
+
+
+# ---- pole counts around the unroll padding, and the long paths' variants ----
+
+@pytest.mark.parametrize("N", [1, 3, 5, 7, 13, 255, 256])
+def test_pole_counts(s4, N):
+    print(f"case: generic H=2 N={N} L=512 batch=2", flush=True)
+    x = make_generic_inputs(H=2, N=N, L=512, batch=2, seed=100 + N)
+    K, y = run_forward(s4, x)
+    Kr, yr = oracle_forward(x)
+    assert _rel(K, Kr) <= TOL and _rel(y, yr) <= TOL
+
+
+@pytest.mark.parametrize("L", [2048, 16384, 65536])
+def test_diagonal_and_distinct_q_long(s4, L):
+    print(f"case: diagonal and distinct-Q L={L}", flush=True)
+    xd = make_generic_inputs(H=2, N=16, L=L, batch=2, seed=7 + L, diagonal=True)
+    K, y = run_forward(s4, xd, diagonal=True)
+    Kr, yr = oracle_forward(xd, diagonal=True)
+    assert _rel(K, Kr) <= TOL and _rel(y, yr) <= TOL
+    xq = make_generic_inputs(H=2, N=16, L=L, batch=2, seed=9 + L, distinct_q=True)
+    K, y = run_forward(s4, xq)
+    Kr, yr = oracle_forward(xq)
+    assert _rel(K, Kr) <= TOL and _rel(y, yr) <= TOL
+
+
+# ---- conv_apply: the spectrum left by the previous call, over other batches ----
+
+@pytest.mark.parametrize("L", [64, 1024, 4096, 32768])
+def test_conv_apply_reuses_the_spectrum(s4, L):
+    import torch
+    print(f"case: conv_apply L={L}", flush=True)
+    x = make_generic_inputs(H=3, N=8, L=L, batch=2, seed=31 + L)
+    plan = s4.Plan(3, 8, L, 2)
+    ws = plan.workspace()
+    t = {k: _dev(x[k]) for k in ("lam", "P", "B", "C", "dt", "D", "u")}
+    K = torch.empty((3, L), dtype=torch.float32, device="cuda")
+    y = torch.empty((2, 3, L), dtype=torch.float32, device="cuda")
+    s4.forward(plan, t["lam"], t["P"], None, t["B"], t["C"], t["dt"], t["D"], t["u"], K, y, ws)
+    u2 = np.random.default_rng(L).standard_normal((2, 3, L)).astype(np.float32)
+    y2 = torch.empty_like(y)
+    s4.conv_apply(plan, _dev(u2), y2, ws)
+    torch.cuda.synchronize()
+    Kr, _ = oracle_forward(x)
+    y2r = o.conv_fft(u2, Kr[None], x["D"].astype(np.float64)[None, :, None])
+    assert _rel(y2.cpu().numpy(), y2r) <= TOL
+    # after conv_fwd with a given kernel and D = NULL
+    Kg = (np.random.default_rng(L + 5).standard_normal((3, L)) * np.exp(-np.arange(L) / 50.0)).astype(np.float32)
+    y3 = torch.empty_like(y)
+    s4.conv_fwd(plan, _dev(u2), _dev(Kg), None, y3, ws)
+    y4 = torch.empty_like(y)
+    s4.conv_apply(plan, t["u"], y4, ws)
+    torch.cuda.synchronize()
+    assert _rel(y3.cpu().numpy(), o.conv_fft(u2, Kg[None], 0.0)) <= TOL
+    assert _rel(y4.cpu().numpy(), o.conv_fft(x["u"], Kg[None], 0.0)) <= TOL
+    plan.close()
