@@ -1,0 +1,38 @@
+// Host-only stand-ins for the HIP runtime calls and kernel launchers used by
+// api.cpp, so that the C-ABI host logic can be built with g++ and run under
+// AddressSanitizer / UndefinedBehaviorSanitizer without a GPU.
+#include <hip/hip_runtime_api.h>
+
+#include <cstring>
+
+#include "internal.h"
+
+static int g_launches = 0;
+int stub_launch_count() { return g_launches; }
+
+extern "C" hipError_t hipMemcpyAsync(void* dst, const void* src, size_t n, hipMemcpyKind,
+                                     hipStream_t) {
+  // the workspace pointer in the driver is real host memory
+  std::memcpy(dst, src, n);
+  return hipSuccess;
+}
+extern "C" hipError_t hipGetLastError(void) { return hipSuccess; }
+
+namespace s4 {
+bool lds_path(const s4dplr_plan* p) { return p->log2L <= S4DPLR_LDS_MAX_LOG2L; }
+hipError_t launch_kernel_gen(const s4dplr_plan*, const float*, const float*, const float*,
+                             const float*, const float*, const float*, const float*, float*,
+                             unsigned char*, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
+hipError_t launch_spectrum_from_time(const s4dplr_plan*, const float*, const float*,
+                                     unsigned char*, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
+hipError_t launch_conv(const s4dplr_plan*, const float*, float*, unsigned char*, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
+}  // namespace s4

@@ -248,3 +248,31 @@ def test_conv_apply_reuses_the_spectrum(s4, L):
     assert _rel(y3.cpu().numpy(), o.conv_fft(u2, Kg[None], 0.0)) <= TOL
     assert _rel(y4.cpu().numpy(), o.conv_fft(x["u"], Kg[None], 0.0)) <= TOL
     plan.close()
+
+
+# ---- every scratch read is of something written in the same call ------------
+
+@pytest.mark.parametrize("L", [256, 1024, 4096, 65536])
+def test_nan_poisoned_scratch(s4, L):
+    """The workspace's scratch arrays hold NaN before the call: a read of
+    scratch that the call did not write first would reach the outputs."""
+    import torch
+    print(f"case: NaN-poisoned workspace L={L}", flush=True)
+    x = make_generic_inputs(H=2, N=8, L=L, batch=2, seed=41 + L)
+    plan = s4.Plan(2, 8, L, 2)
+    ws = plan.workspace()
+    torch.cuda.synchronize()
+    # poison the whole workspace, then let plan_init rewrite its tables: the
+    # scratch arrays stay NaN until a kernel writes them
+    ws.fill_(0xFF)                            # NaN bit pattern in every float
+    s4.plan_init(plan.handle, ws)
+    t = {k: _dev(x[k]) for k in ("lam", "P", "B", "C", "dt", "D", "u")}
+    K = torch.full((2, L), float("nan"), device="cuda")
+    y = torch.full((2, 2, L), float("nan"), device="cuda")
+    s4.forward(plan, t["lam"], t["P"], None, t["B"], t["C"], t["dt"], t["D"], t["u"], K, y, ws)
+    torch.cuda.synchronize()
+    Kh, yh = K.cpu().numpy(), y.cpu().numpy()
+    assert np.isfinite(Kh).all() and np.isfinite(yh).all()
+    Kr, yr = oracle_forward(x)
+    assert _rel(Kh, Kr) <= TOL and _rel(yh, yr) <= TOL
+    plan.close()
