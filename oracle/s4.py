@@ -49,7 +49,7 @@ __all__ = [
     "dense_state_matrix", "discretize_bilinear", "discretize_zoh_scalar",
     "kernel_truncated", "kernel_aliased_dense", "generating_function",
     "kernel_cauchy", "conv_direct", "conv_direct_at", "conv_fft",
-    "recurrence", "forward",
+    "recurrence", "forward", "recurrent_forward",
 ]
 
 
@@ -259,18 +259,28 @@ def conv_fft(u, K, D):
     return y + np.asarray(D, np.float64) * u
 
 
-def recurrence(Abar, Bbar, C, D, u):
-    """Recurrent view x_t = A-bar x_{t-1} + B-bar u_t, y_t = Re(C x_t) + D u_t,
-    with x_{-1} = 0 ([scratch] section 5; [glossary] h_t = A-bar h_{t-1} + B-bar u_t)."""
+def recurrence(Abar, Bbar, C, D, u, x0=None, return_state=False):
+    """Recurrent view x_t = A-bar x_{t-1} + B-bar u_t, y_t = Re(C x_t) + D u_t
+    ([scratch] section 5; [glossary] h_t = A-bar h_{t-1} + B-bar u_t).
+
+    u is (..., T): every leading index is an independent sequence of the same
+    system.  The state before the first step is x0 (..., N), zero if None.
+    With return_state the state after the last step is returned as well.
+    """
     Abar = np.asarray(Abar, np.complex128)
     Bbar = np.asarray(Bbar, np.complex128)
     C = np.asarray(C, np.complex128)
-    x = np.zeros(Abar.shape[0], dtype=np.complex128)
-    y = np.empty(len(u), dtype=np.float64)
-    for t, ut in enumerate(np.asarray(u, np.float64)):
-        x = Abar @ x + Bbar * ut
-        y[t] = (C @ x).real + D * ut
-    return y
+    u = np.asarray(u, np.float64)
+    N = Abar.shape[0]
+    x = np.zeros(u.shape[:-1] + (N,), dtype=np.complex128)
+    if x0 is not None:
+        x = x + np.asarray(x0, np.complex128)
+    y = np.empty(u.shape, dtype=np.float64)
+    for t in range(u.shape[-1]):
+        ut = u[..., t]
+        x = x @ Abar.T + Bbar * ut[..., None]
+        y[..., t] = (x @ C).real + D * ut
+    return (y, x) if return_state else y
 
 
 # ---------------------------------------------------------------------------
@@ -319,3 +329,32 @@ def forward(lam, P, Q, B, C, dt, D, u, method="cauchy", diagonal=False):
             raise ValueError(method)
     y = conv_fft(u, K[None, :, :], D[None, :, None])
     return K, y
+
+
+def recurrent_forward(lam, P, Q, B, C, dt, D, u, x0=None, diagonal=False):
+    """The recurrent view over channels and batch: y [batch, H, T] and the
+    final state [batch, H, N] (complex), from the dense bilinear A-bar, B-bar
+    of A = Lambda - P Q^* ([scratch] sections 3 and 5; [wiki] "Structured
+    Transition Matrix").  Inputs as for ``forward``; x0 is [batch, H, N]
+    complex or None (zero).  ``diagonal`` drops the low-rank term."""
+    lam_c = _as_complex(lam)
+    H, N = lam_c.shape
+    u = np.asarray(u, np.float64)
+    if diagonal:
+        P_c = np.zeros((H, N), np.complex128)
+        Q_c = P_c
+    else:
+        P_c = _as_complex(P)
+        Q_c = P_c if Q is None else _as_complex(Q)
+    B_c = _as_complex(B)
+    C_c = _as_complex(C)
+    dt = np.asarray(dt, np.float64)
+    D = np.zeros(H) if D is None else np.asarray(D, np.float64)
+    y = np.empty(u.shape, dtype=np.float64)
+    xT = np.empty((u.shape[0], H, N), dtype=np.complex128)
+    for h in range(H):
+        A = dense_state_matrix(lam_c[h], P_c[h], Q_c[h])
+        Abar, Bbar = discretize_bilinear(A, B_c[h], dt[h])
+        y[:, h], xT[:, h] = recurrence(Abar, Bbar, C_c[h], D[h], u[:, h],
+                                       None if x0 is None else x0[:, h], return_state=True)
+    return y, xT

@@ -271,6 +271,71 @@ def test_s4d_lin_vandermonde_closed_form():
         assert np.abs(K[h] - ref).max() <= 1e-11 * np.abs(ref).max()
 
 
+# --- Recurrent view from a carried state -----------------------------------
+
+def test_recurrence_from_state_scalar_closed_form():
+    # zero input: x_t = a^(t+1) x0, so y_t = Re(c a^(t+1) x0) for every sequence
+    a, b, c = 0.9 * np.exp(0.3j), 0.7 - 0.2j, 1.3 + 0.4j
+    x0 = np.array([[1.0 - 2.0j], [0.5j], [-0.25 + 0.0j]])
+    T = 12
+    y, xT = o.recurrence(np.array([[a]]), np.array([b]), np.array([c]), 0.0,
+                         np.zeros((3, T)), x0=x0, return_state=True)
+    t = np.arange(T)
+    ref = (c * a ** (t[None, :] + 1) * x0).real
+    np.testing.assert_allclose(y, ref, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(xT, a ** T * x0, rtol=0, atol=1e-15)
+
+
+def test_recurrence_from_state_superposition_and_explicit_state():
+    # y(u, x0) = y(u, 0) + Re(C A-bar^(t+1) x0); x_T = A-bar^T x0 + sum_j A-bar^(T-1-j) B-bar u_j
+    rng = np.random.default_rng(21)
+    N, T = 4, 9
+    lam = -rng.uniform(0.1, 1, N) + 1j * rng.uniform(-2, 2, N)
+    P, B, C = 0.5 * _cn(rng, N), _cn(rng, N), _cn(rng, N)
+    Abar, Bbar = o.discretize_bilinear(o.dense_state_matrix(lam, P, P), B, 0.3)
+    u = rng.standard_normal((2, T))
+    x0 = _cn(rng, 2, N)
+    y, xT = o.recurrence(Abar, Bbar, C, 0.4, u, x0=x0, return_state=True)
+    y0 = o.recurrence(Abar, Bbar, C, 0.4, u)
+    for s in range(2):
+        free = np.array([(C @ np.linalg.matrix_power(Abar, t + 1) @ x0[s]).real for t in range(T)])
+        np.testing.assert_allclose(y[s], y0[s] + free, rtol=0, atol=1e-13 * np.abs(y[s]).max())
+        ref = np.linalg.matrix_power(Abar, T) @ x0[s]
+        for j in range(T):
+            ref = ref + np.linalg.matrix_power(Abar, T - 1 - j) @ Bbar * u[s, j]
+        np.testing.assert_allclose(xT[s], ref, rtol=0, atol=1e-13 * np.abs(ref).max())
+
+
+@pytest.mark.parametrize("diagonal,distinct_q", [(False, False), (False, True), (True, False)])
+def test_recurrent_forward_equals_truncated_convolution(diagonal, distinct_q):
+    # every (batch, channel) sequence: zero-state response = causal convolution
+    # with the truncated kernel C A-bar^k B-bar of that channel
+    x = make_generic_inputs(H=3, N=4, L=16, batch=2, seed=5, diagonal=diagonal,
+                            distinct_q=distinct_q)
+    y, _ = o.recurrent_forward(x["lam"], x["P"], x["Q"], x["B"], x["C"], x["dt"], x["D"], x["u"],
+                               diagonal=diagonal)
+    c = lambda a: a[..., 0].astype(np.float64) + 1j * a[..., 1]
+    for h in range(3):
+        P = np.zeros(4) if diagonal else c(x["P"][h])
+        Q = P if (diagonal or x["Q"] is None) else c(x["Q"][h])
+        Abar, Bbar = o.discretize_bilinear(o.dense_state_matrix(c(x["lam"][h]), P, Q),
+                                           c(x["B"][h]), float(x["dt"][h]))
+        Kt = o.kernel_truncated(Abar, Bbar, c(x["C"][h]), 16)
+        for b in range(2):
+            ref = o.conv_direct(x["u"][b, h], Kt, float(x["D"][h]))
+            np.testing.assert_allclose(y[b, h], ref, rtol=0, atol=1e-12 * np.abs(ref).max())
+
+
+def test_recurrent_forward_split_equals_whole():
+    x = make_generic_inputs(H=2, N=5, L=32, batch=3, seed=6)
+    args = (x["lam"], x["P"], x["Q"], x["B"], x["C"], x["dt"], x["D"])
+    y, xT = o.recurrent_forward(*args, x["u"])
+    y1, x1 = o.recurrent_forward(*args, x["u"][..., :11])
+    y2, x2 = o.recurrent_forward(*args, x["u"][..., 11:], x0=x1)
+    np.testing.assert_allclose(np.concatenate([y1, y2], -1), y, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(x2, xT, rtol=0, atol=1e-13)
+
+
 # --- P11 / P12: brute force on tiny inputs ----------------------------------
 
 @pytest.mark.parametrize("N,L", [(1, 4), (2, 8), (4, 16), (3, 16)])
