@@ -155,6 +155,48 @@ s4dplr_status s4dplr_forward(const s4dplr_plan* plan, const float* lambda, const
 s4dplr_status s4dplr_conv_apply(const s4dplr_plan* plan, const float* u, float* y, void* ws,
                                 hipStream_t stream);
 
+/*
+ * Recurrent view, stage 1 ("The S4 kernel, from scratch", section 5;
+ * "Structured state-space sequence model and S4", "One linear layer, two
+ * computational views"): form the per-pole step records of the bilinear
+ * system A-bar = (I - dt/2 A)^{-1} (I + dt/2 A), B-bar = (I - dt/2 A)^{-1} dt B
+ * (section 3) for A = Lambda - P Q^* ("S4" wiki, "Structured Transition
+ * Matrix"), in O(N) per channel through the Sherman-Morrison identity; kept in
+ * the workspace for s4dplr_recurrent_scan.  Arguments and layouts as for
+ * s4dplr_kernel_gen (Q == NULL means Q = P; with S4DPLR_DIAGONAL, P and Q are
+ * ignored).  Device pointers.  Does not touch the convolution state of the
+ * workspace.  The records are formed in fp64 and stored as fp32.
+ * Errors: ERR_NULL, ERR_WORKSPACE, ERR_HIP.
+ */
+s4dplr_status s4dplr_recurrent_prepare(const s4dplr_plan* plan, const float* lambda,
+                                       const float* P, const float* Q, const float* B,
+                                       const float* C, const float* dt, void* ws,
+                                       hipStream_t stream);
+
+/*
+ * Recurrent view, stage 2: T steps of
+ *     x_t = A-bar x_{t-1} + B-bar u_t,   y_t = Re(C x_t) + D u_t
+ * for every (batch, channel) sequence, starting from the state passed in and
+ * leaving the state after the last step in its place, so consecutive calls
+ * continue one stream (streaming inference).  A zero state at the first call
+ * gives y = K_T * u + D u with the untruncated-by-aliasing kernel
+ * K_k = Re(C A-bar^k B-bar) (section 4, "the kernel is the impulse response").
+ * Uses the records of the latest s4dplr_recurrent_prepare on this workspace
+ * in stream order (without one the results are unspecified; every access
+ * stays inside the workspace).
+ *   u, y  : [batch][H][T] float32 (T need not equal the plan's L).
+ *   state : [batch][H][N] complex, interleaved float32 (re, im); read and
+ *           written.
+ *   D     : [H] float32 or NULL (D = 0).
+ * T = 0 is a no-op (u and y may then be NULL).  y must not overlap u, state
+ * or the workspace; state must not overlap u or the workspace (ERR_ALIAS).
+ * Limits: 0 <= T and batch * H * T < 2^31 (ERR_SHAPE).
+ * Errors: ERR_NULL, ERR_SHAPE, ERR_ALIAS, ERR_WORKSPACE, ERR_HIP.
+ */
+s4dplr_status s4dplr_recurrent_scan(const s4dplr_plan* plan, const float* D, const float* u,
+                                    int T, float* state, float* y, void* ws,
+                                    hipStream_t stream);
+
 /* Release a plan (NULL is ignored).  Host-only. */
 void s4dplr_plan_destroy(s4dplr_plan* plan);
 

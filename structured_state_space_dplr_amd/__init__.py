@@ -19,7 +19,7 @@ import torch  # loads the HIP runtime that libs4dplr then shares
 __all__ = [
     "S4DPLRError", "DIAGONAL", "abi_version", "status_string", "plan_create",
     "plan_workspace_bytes", "plan_init", "kernel_gen", "conv_fwd", "forward",
-    "conv_apply", "plan_destroy", "Plan", "LIB_PATH",
+    "conv_apply", "recurrent_prepare", "recurrent_scan", "plan_destroy", "Plan", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libs4dplr.so")
@@ -54,6 +54,10 @@ _lib.s4dplr_forward.restype = ctypes.c_int
 _lib.s4dplr_forward.argtypes = [_p] * 13
 _lib.s4dplr_conv_apply.restype = ctypes.c_int
 _lib.s4dplr_conv_apply.argtypes = [_p] * 5
+_lib.s4dplr_recurrent_prepare.restype = ctypes.c_int
+_lib.s4dplr_recurrent_prepare.argtypes = [_p] * 9
+_lib.s4dplr_recurrent_scan.restype = ctypes.c_int
+_lib.s4dplr_recurrent_scan.argtypes = [_p, _p, _p, ctypes.c_int, _p, _p, _p, _p]
 _lib.s4dplr_plan_destroy.restype = None
 _lib.s4dplr_plan_destroy.argtypes = [_p]
 
@@ -160,6 +164,27 @@ def conv_apply(plan: "Plan | int", u, y, ws, stream=None) -> None:
     _check(_lib.s4dplr_conv_apply(
         p, _ptr(u, "u", (batch, H, L)), _ptr(y, "y", (batch, H, L)), _ws_ptr(ws),
         _stream(stream)), "conv_apply")
+
+
+def recurrent_prepare(plan: "Plan | int", lam, P, Q, B, C, dt, ws, stream=None) -> None:
+    p, (H, N, L, _) = _dims(plan)
+    cplx = (H, N, 2)
+    _check(_lib.s4dplr_recurrent_prepare(
+        p, _ptr(lam, "lam", cplx), _ptr(P, "P", cplx), _ptr(Q, "Q", cplx), _ptr(B, "B", cplx),
+        _ptr(C, "C", cplx), _ptr(dt, "dt", (H,)), _ws_ptr(ws), _stream(stream)),
+        "recurrent_prepare")
+
+
+def recurrent_scan(plan: "Plan | int", D, u, state, y, ws, stream=None) -> None:
+    """T = u.shape[-1] steps from ``state`` ([batch, H, N, 2], updated in place)."""
+    p, (H, N, L, batch) = _dims(plan)
+    if u is None or u.dim() != 3:
+        raise ValueError("u: expected a [batch, H, T] tensor")
+    T = int(u.shape[-1])
+    _check(_lib.s4dplr_recurrent_scan(
+        p, _ptr(D, "D", (H,)), _ptr(u, "u", (batch, H, T)), T,
+        _ptr(state, "state", (batch, H, N, 2)), _ptr(y, "y", (batch, H, T)), _ws_ptr(ws),
+        _stream(stream)), "recurrent_scan")
 
 
 def _dims(plan):

@@ -59,6 +59,35 @@ bool valid_plan(const s4dplr_plan* p) { return p != nullptr; }
 
 }  // namespace
 
+namespace s4 {
+
+void recurrent_shape(int N, long rows, int* ppl_out, int* log2g_out) {
+  auto groups_log2 = [N](int ppl) {
+    const int need = (N + ppl - 1) / ppl;
+    int lg = 0;
+    while ((1 << lg) < need) ++lg;
+    return lg;
+  };
+  int ppl = 1;
+  while (ppl < 8 && ppl < N) ppl <<= 1;
+  int lg = groups_log2(ppl);
+  // More lanes per sequence (fewer poles per lane) while the launch is short
+  // of about two waves per SIMD (256 CUs x 4 SIMDs).
+  constexpr long kTargetWaves = 2048;
+  while (ppl > 1) {
+    const int lg2 = groups_log2(ppl >> 1);
+    if (lg2 > 5) break;
+    const long waves = ((rows << lg) + 63) / 64;
+    if (waves >= kTargetWaves) break;
+    ppl >>= 1;
+    lg = lg2;
+  }
+  *ppl_out = ppl;
+  *log2g_out = lg;
+}
+
+}  // namespace s4
+
 extern "C" {
 
 int s4dplr_abi_version(void) { return S4DPLR_ABI_VERSION; }
@@ -125,6 +154,10 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
   if (!lds) off = align_up(off + sizeof(float) * (size_t)H * L);
   p->off_big = off;
   if (!lds) off = align_up(off + sizeof(float) * 2 * (size_t)batch * H * L);
+  p->off_rrec = off;
+  off = align_up(off + sizeof(float) * 16 * (size_t)H * N);
+  p->off_rchan = off;
+  off = align_up(off + sizeof(float) * 4 * (size_t)H);
   p->total = off;
 
   // fp64 tables, rounded once to fp32.
@@ -248,6 +281,40 @@ s4dplr_status s4dplr_conv_apply(const s4dplr_plan* p, const float* u, float* y, 
   const size_t ub = sizeof(float) * (size_t)p->batch * p->H * p->L;
   if (overlaps(y, ub, u, ub) || overlaps(y, ub, ws, p->total)) return S4DPLR_ERR_ALIAS;
   hipError_t e = s4::launch_conv(p, u, y, static_cast<unsigned char*>(ws), stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return S4DPLR_OK;
+}
+
+s4dplr_status s4dplr_recurrent_prepare(const s4dplr_plan* p, const float* lambda,
+                                       const float* P, const float* Q, const float* B,
+                                       const float* C, const float* dt, void* ws,
+                                       hipStream_t stream) {
+  if (!valid_plan(p)) return S4DPLR_ERR_NULL;
+  if (s4dplr_status st = check_params(p, lambda, P, B, C, dt)) return st;
+  if (s4dplr_status st = check_ws(ws)) return st;
+  hipError_t e = s4::launch_recurrent_prepare(p, lambda, P, Q, B, C, dt,
+                                              static_cast<unsigned char*>(ws), stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return S4DPLR_OK;
+}
+
+s4dplr_status s4dplr_recurrent_scan(const s4dplr_plan* p, const float* D, const float* u, int T,
+                                    float* state, float* y, void* ws, hipStream_t stream) {
+  if (!valid_plan(p)) return S4DPLR_ERR_NULL;
+  if (T < 0) return S4DPLR_ERR_SHAPE;
+  const long long rows = (long long)p->batch * p->H;
+  if (rows * T >= (1LL << 31)) return S4DPLR_ERR_SHAPE;
+  if (!state) return S4DPLR_ERR_NULL;
+  if (T > 0 && (!u || !y)) return S4DPLR_ERR_NULL;
+  if (s4dplr_status st = check_ws(ws)) return st;
+  const size_t ub = sizeof(float) * (size_t)rows * T;
+  const size_t sb = sizeof(float) * 2 * (size_t)rows * p->N;
+  if (overlaps(y, ub, u, ub) || overlaps(y, ub, state, sb) || overlaps(y, ub, ws, p->total) ||
+      overlaps(state, sb, u, ub) || overlaps(state, sb, ws, p->total))
+    return S4DPLR_ERR_ALIAS;
+  if (T == 0) return S4DPLR_OK;
+  hipError_t e = s4::launch_recurrent_scan(p, D, u, state, y, T,
+                                           static_cast<unsigned char*>(ws), stream);
   if (e != hipSuccess) return hip_fail(e);
   return S4DPLR_OK;
 }

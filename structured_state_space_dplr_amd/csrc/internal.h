@@ -29,6 +29,8 @@ struct s4dplr_plan {
   size_t off_coef;   // [H][L] float4: spectral weights (alpha, beta) of bin j
   size_t off_kbuf;   // long path: [H][L] float time-domain kernel when not written out
   size_t off_big;    // long path: [batch*H][L] float2 intermediate rows
+  size_t off_rrec;   // recurrent view: [H][N] x 4 float4 per-pole step records
+  size_t off_rchan;  // recurrent view: [H] float4 per-channel sums (S1, S2)
   size_t total;
   std::vector<unsigned char> tables;  // exact bytes of the table region
 };
@@ -53,5 +55,17 @@ hipError_t launch_big_kspec(const s4dplr_plan* p, const float* Ktime, const floa
                             float* Kout, unsigned char* ws, hipStream_t s);
 hipError_t launch_big_conv(const s4dplr_plan* p, const float* u, float* y, unsigned char* ws,
                            hipStream_t s);
+
+// Recurrent view: per-pole step records from the parameters, then T steps of
+// every (batch, channel) sequence from the carried state.
+hipError_t launch_recurrent_prepare(const s4dplr_plan* p, const float* lam, const float* P,
+                                    const float* Q, const float* B, const float* C,
+                                    const float* dt, unsigned char* ws, hipStream_t s);
+hipError_t launch_recurrent_scan(const s4dplr_plan* p, const float* D, const float* u,
+                                 float* state, float* y, int T, unsigned char* ws,
+                                 hipStream_t s);
+// Work split of the scan: poles per lane (1, 2, 4 or 8) and log2 of the lanes
+// per sequence (0..5), chosen from N and the number of sequences.
+void recurrent_shape(int N, long rows, int* ppl, int* log2g);
 
 }  // namespace s4

@@ -1,0 +1,318 @@
+// The recurrent view of the same layer ("The S4 kernel, from scratch",
+// section 5; "Structured state-space sequence model and S4", "One linear
+// layer, two computational views"):
+//   x_t = A-bar x_{t-1} + B-bar u_t,   y_t = Re(C x_t) + D u_t,
+// with the bilinear A-bar = (I - s A)^{-1} (I + s A), B-bar = (I - s A)^{-1} dt B,
+// s = dt/2 (section 3), and A = Lambda - P Q^* ("S4" wiki, "Structured
+// Transition Matrix").
+//
+// O(N) per step through the rank-1 structure.  With D0 = I - s Lambda
+// (diagonal), I - s A = D0 + s P Q^*, and the Sherman-Morrison identity gives
+//   (I - s A)^{-1} = D0^{-1} - s D0^{-1} P Q^* D0^{-1} / (1 + s Q^* D0^{-1} P).
+// Per pole n, once per parameter set:
+//   Abar0_n = (1 + s Lambda_n) / (1 - s Lambda_n),  e_n = s P_n / (1 - s Lambda_n),
+//   Bbar0_n = dt B_n / (1 - s Lambda_n),            g_n = e_n / den,
+//   den = 1 + s sum_n conj(Q_n) P_n / (1 - s Lambda_n),
+//   qa_n = conj(Q_n) Abar0_n,  S1 = sum_n conj(Q_n) e_n,  S2 = sum_n conj(Q_n) Bbar0_n.
+// One step, with qx = Q^* x and r2 = sum_n qa_n x_n carried over from the
+// previous step's sums:
+//   qw = r2 - S1 qx + S2 u   (= Q^* w),
+//   w_n = Abar0_n x_n - e_n qx + Bbar0_n u,   x'_n = w_n - g_n qw,
+// and one set of sums gives y = Re(sum_n C_n x'_n) + D u and the next qx, r2.
+// With the diagonal flag (P = Q = 0; "S4" wiki, "S4D") the step is
+// x'_n = Abar0_n x_n + Bbar0_n u.
+//
+// Work split: each (batch, channel) sequence is scanned by a group of G
+// lanes (G a power of two, 1..32), each lane holding PPL poles
+// (n = j + G k for lane j of the group) with their parameters in registers.
+// The per-step sums over the group are DPP butterflies (xor 1, 2, then the
+// half-row and row mirrors, then a cross-row swap for G = 32), so every lane
+// of a group ends with the same, bit-identical sum.
+#include <hip/hip_runtime.h>
+
+#include "device_fft.h"
+#include "internal.h"
+
+namespace s4 {
+
+// Per-pole record (4 float4): (Abar0, e), (Bbar0, g), (qa, conj Q), (C, 0).
+constexpr int kRecurRec = 4;
+
+namespace {
+
+struct cd {
+  double re, im;
+};
+__device__ __forceinline__ cd cd_mul(cd a, cd b) {
+  return {a.re * b.re - a.im * b.im, a.re * b.im + a.im * b.re};
+}
+__device__ __forceinline__ cd cd_div(cd a, cd b) {
+  const double inv = 1.0 / (b.re * b.re + b.im * b.im);
+  return {(a.re * b.re + a.im * b.im) * inv, (a.im * b.re - a.re * b.im) * inv};
+}
+__device__ __forceinline__ cd cd_load(const float2* p, size_t i) {
+  const float2 v = p[i];
+  return {(double)v.x, (double)v.y};
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the aligned group of 2^LOG2G lanes; every lane of the group gets
+// the same value.
+template <int LOG2G>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (LOG2G >= 1) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
+  if constexpr (LOG2G >= 2) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (LOG2G >= 3) v += dpp<0x141>(v);   // row_half_mirror: other quad of 8
+  if constexpr (LOG2G >= 4) v += dpp<0x140>(v);   // row_mirror: other half of 16
+  if constexpr (LOG2G >= 5) v += __shfl_xor(v, 16);
+  return v;
+}
+
+}  // namespace
+
+// One wave per channel; the records are formed in fp64 and rounded once.
+__global__ __launch_bounds__(64) void recurrent_prepare_kernel(
+    const float2* __restrict__ lam, const float2* __restrict__ P, const float2* __restrict__ Q,
+    const float2* __restrict__ B, const float2* __restrict__ C, const float* __restrict__ dt,
+    float4* __restrict__ rec, float4* __restrict__ chan, int N, int diag) {
+  const int h = blockIdx.x, lane = threadIdx.x;
+  const double d = (double)dt[h], s = 0.5 * d;
+  double den_re = 0.0, den_im = 0.0;
+  if (!diag) {
+    for (int n = lane; n < N; n += 64) {
+      const size_t i = (size_t)h * N + n;
+      const cd l = cd_load(lam, i), p = cd_load(P, i), q = cd_load(Q ? Q : P, i);
+      const cd t = cd_div(cd_mul({q.re, -q.im}, p), {1.0 - s * l.re, -s * l.im});
+      den_re += t.re;
+      den_im += t.im;
+    }
+    den_re = wave_sum_d(den_re);
+    den_im = wave_sum_d(den_im);
+  }
+  const cd den = {1.0 + s * den_re, s * den_im};
+  double s1r = 0.0, s1i = 0.0, s2r = 0.0, s2i = 0.0;
+  for (int n = lane; n < N; n += 64) {
+    const size_t i = (size_t)h * N + n;
+    const cd l = cd_load(lam, i), b = cd_load(B, i), c = cd_load(C, i);
+    const cd p = diag ? cd{0.0, 0.0} : cd_load(P, i);
+    const cd q = diag ? cd{0.0, 0.0} : cd_load(Q ? Q : P, i);
+    const cd d0 = {1.0 - s * l.re, -s * l.im};
+    const cd ab = cd_div({1.0 + s * l.re, s * l.im}, d0);
+    const cd e = cd_div({s * p.re, s * p.im}, d0);
+    const cd bb = cd_div({d * b.re, d * b.im}, d0);
+    const cd g = cd_div(e, den);
+    const cd qc = {q.re, -q.im};
+    const cd qa = cd_mul(qc, ab);
+    const cd t1 = cd_mul(qc, e), t2 = cd_mul(qc, bb);
+    s1r += t1.re;
+    s1i += t1.im;
+    s2r += t2.re;
+    s2i += t2.im;
+    float4* r = rec + kRecurRec * i;
+    r[0] = make_float4((float)ab.re, (float)ab.im, (float)e.re, (float)e.im);
+    r[1] = make_float4((float)bb.re, (float)bb.im, (float)g.re, (float)g.im);
+    r[2] = make_float4((float)qa.re, (float)qa.im, (float)qc.re, (float)qc.im);
+    r[3] = make_float4((float)c.re, (float)c.im, 0.f, 0.f);
+  }
+  s1r = wave_sum_d(s1r);
+  s1i = wave_sum_d(s1i);
+  s2r = wave_sum_d(s2r);
+  s2i = wave_sum_d(s2i);
+  if (lane == 0) chan[h] = make_float4((float)s1r, (float)s1i, (float)s2r, (float)s2i);
+}
+
+// Memory row = b * H + h; the group of 2^LOG2G lanes handles one row.
+// u and y are moved 16 steps at a time: lane j of a group holds the steps
+// t0 + j + G m, and each step's input is broadcast to the group.
+template <int PPL, int LOG2G, bool DIAG>
+__global__ __launch_bounds__(256) void recurrent_scan_kernel(
+    const float4* __restrict__ rec, const float4* __restrict__ chan, const float* __restrict__ D,
+    const float* __restrict__ u, float2* __restrict__ state, float* __restrict__ y, int H,
+    int rows, int N, int T) {
+  constexpr int G = 1 << LOG2G;
+  constexpr int CH = 16;
+  constexpr int NU = G >= CH ? 1 : CH / G;
+  const int lane = threadIdx.x & 63;
+  const int j = lane & (G - 1);
+  const int gbase = lane - j;
+  const long grow = ((long)blockIdx.x * 256 + threadIdx.x) >> LOG2G;
+  const bool valid = grow < rows;   // the whole group agrees
+  const int row = valid ? (int)grow : 0;
+  const int h = row % H;
+
+  float2 ab[PPL], e[PPL], bb[PPL], g[PPL], qa[PPL], qc[PPL], c[PPL], x[PPL];
+#pragma unroll
+  for (int k = 0; k < PPL; ++k) {
+    const int n = j + G * k;
+    ab[k] = e[k] = bb[k] = g[k] = qa[k] = qc[k] = c[k] = x[k] = make_float2(0.f, 0.f);
+    if (valid && n < N) {
+      const float4* r = rec + kRecurRec * ((size_t)h * N + n);
+      const float4 r0 = r[0], r1 = r[1], r2v = r[2], r3 = r[3];
+      ab[k] = make_float2(r0.x, r0.y);
+      e[k] = make_float2(r0.z, r0.w);
+      bb[k] = make_float2(r1.x, r1.y);
+      g[k] = make_float2(r1.z, r1.w);
+      qa[k] = make_float2(r2v.x, r2v.y);
+      qc[k] = make_float2(r2v.z, r2v.w);
+      c[k] = make_float2(r3.x, r3.y);
+      x[k] = state[(size_t)row * N + n];
+    }
+  }
+  float2 S1 = make_float2(0.f, 0.f), S2 = make_float2(0.f, 0.f);
+  float Dh = 0.f;
+  if (valid) {
+    const float4 ch = chan[h];
+    S1 = make_float2(ch.x, ch.y);
+    S2 = make_float2(ch.z, ch.w);
+    Dh = D ? D[h] : 0.f;
+  }
+
+  float2 qx = make_float2(0.f, 0.f), r2 = make_float2(0.f, 0.f);
+  if constexpr (!DIAG) {
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+      const float2 t1 = cmul(qc[k], x[k]), t2 = cmul(qa[k], x[k]);
+      a0 += t1.x;
+      a1 += t1.y;
+      a2 += t2.x;
+      a3 += t2.y;
+    }
+    qx = make_float2(group_sum<LOG2G>(a0), group_sum<LOG2G>(a1));
+    r2 = make_float2(group_sum<LOG2G>(a2), group_sum<LOG2G>(a3));
+  }
+
+  const float* __restrict__ ur = u + (size_t)row * T;
+  float* __restrict__ yr = y + (size_t)row * T;
+  for (int t0 = 0; t0 < T; t0 += CH) {
+    float uv[NU], yv[NU];
+#pragma unroll
+    for (int m = 0; m < NU; ++m) {
+      const int o = j + G * m, t = t0 + o;
+      uv[m] = (valid && o < CH && t < T) ? ur[t] : 0.f;
+      yv[m] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      if (t0 + i >= T) continue;   // the same for every lane
+      float ut;
+      if constexpr (G == 1) ut = uv[i];
+      else ut = __shfl(uv[i / G], gbase + (i % G));
+      float yre = 0.f;
+      if constexpr (DIAG) {
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) {
+          const float2 ax = cmul(ab[k], x[k]);
+          x[k] = make_float2(fmaf(bb[k].x, ut, ax.x), fmaf(bb[k].y, ut, ax.y));
+          yre = fmaf(c[k].x, x[k].x, fmaf(-c[k].y, x[k].y, yre));
+        }
+      } else {
+        const float2 qw = make_float2(fmaf(S2.x, ut, r2.x - fmaf(S1.x, qx.x, -S1.y * qx.y)),
+                                      fmaf(S2.y, ut, r2.y - fmaf(S1.x, qx.y, S1.y * qx.x)));
+        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+        for (int k = 0; k < PPL; ++k) {
+          const float2 ax = cmul(ab[k], x[k]), eq = cmul(e[k], qx), gq = cmul(g[k], qw);
+          x[k] = make_float2(fmaf(bb[k].x, ut, ax.x - eq.x) - gq.x,
+                             fmaf(bb[k].y, ut, ax.y - eq.y) - gq.y);
+          yre = fmaf(c[k].x, x[k].x, fmaf(-c[k].y, x[k].y, yre));
+          const float2 t1 = cmul(qc[k], x[k]), t2 = cmul(qa[k], x[k]);
+          a0 += t1.x;
+          a1 += t1.y;
+          a2 += t2.x;
+          a3 += t2.y;
+        }
+        qx = make_float2(group_sum<LOG2G>(a0), group_sum<LOG2G>(a1));
+        r2 = make_float2(group_sum<LOG2G>(a2), group_sum<LOG2G>(a3));
+      }
+      const float yt = fmaf(Dh, ut, group_sum<LOG2G>(yre));
+      if (j == (i % G)) yv[i / G] = yt;
+    }
+#pragma unroll
+    for (int m = 0; m < NU; ++m) {
+      const int o = j + G * m, t = t0 + o;
+      if (valid && o < CH && t < T) yr[t] = yv[m];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < PPL; ++k) {
+    const int n = j + G * k;
+    if (valid && n < N) state[(size_t)row * N + n] = x[k];
+  }
+}
+
+hipError_t launch_recurrent_prepare(const s4dplr_plan* p, const float* lam, const float* P,
+                                    const float* Q, const float* B, const float* C,
+                                    const float* dt, unsigned char* ws, hipStream_t s) {
+  const int diag = (p->flags & S4DPLR_DIAGONAL) ? 1 : 0;
+  recurrent_prepare_kernel<<<p->H, 64, 0, s>>>(
+      reinterpret_cast<const float2*>(lam), reinterpret_cast<const float2*>(P),
+      reinterpret_cast<const float2*>(Q), reinterpret_cast<const float2*>(B),
+      reinterpret_cast<const float2*>(C), dt, reinterpret_cast<float4*>(ws + p->off_rrec),
+      reinterpret_cast<float4*>(ws + p->off_rchan), p->N, diag);
+  return hipGetLastError();
+}
+
+namespace {
+
+template <int PPL, int LOG2G>
+void scan_launch(const s4dplr_plan* p, const float* D, const float* u, float* state, float* y,
+                 int T, unsigned char* ws, hipStream_t s) {
+  const int rows = p->batch * p->H;
+  const float4* rec = reinterpret_cast<const float4*>(ws + p->off_rrec);
+  const float4* chan = reinterpret_cast<const float4*>(ws + p->off_rchan);
+  float2* st = reinterpret_cast<float2*>(state);
+  const long threads = (long)rows << LOG2G;
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
+  if (p->flags & S4DPLR_DIAGONAL)
+    recurrent_scan_kernel<PPL, LOG2G, true>
+        <<<blocks, 256, 0, s>>>(rec, chan, D, u, st, y, p->H, rows, p->N, T);
+  else
+    recurrent_scan_kernel<PPL, LOG2G, false>
+        <<<blocks, 256, 0, s>>>(rec, chan, D, u, st, y, p->H, rows, p->N, T);
+}
+
+template <int PPL>
+bool scan_dispatch_g(int lg, const s4dplr_plan* p, const float* D, const float* u, float* state,
+                     float* y, int T, unsigned char* ws, hipStream_t s) {
+  switch (lg) {
+    case 0: scan_launch<PPL, 0>(p, D, u, state, y, T, ws, s); return true;
+    case 1: scan_launch<PPL, 1>(p, D, u, state, y, T, ws, s); return true;
+    case 2: scan_launch<PPL, 2>(p, D, u, state, y, T, ws, s); return true;
+    case 3: scan_launch<PPL, 3>(p, D, u, state, y, T, ws, s); return true;
+    case 4: scan_launch<PPL, 4>(p, D, u, state, y, T, ws, s); return true;
+    case 5: scan_launch<PPL, 5>(p, D, u, state, y, T, ws, s); return true;
+    default: return false;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_recurrent_scan(const s4dplr_plan* p, const float* D, const float* u,
+                                 float* state, float* y, int T, unsigned char* ws,
+                                 hipStream_t s) {
+  int ppl, lg;
+  recurrent_shape(p->N, (long)p->batch * p->H, &ppl, &lg);
+  bool ok = false;
+  switch (ppl) {
+    case 1: ok = scan_dispatch_g<1>(lg, p, D, u, state, y, T, ws, s); break;
+    case 2: ok = scan_dispatch_g<2>(lg, p, D, u, state, y, T, ws, s); break;
+    case 4: ok = scan_dispatch_g<4>(lg, p, D, u, state, y, T, ws, s); break;
+    case 8: ok = scan_dispatch_g<8>(lg, p, D, u, state, y, T, ws, s); break;
+    default: break;
+  }
+  if (!ok) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace s4

@@ -6,6 +6,7 @@
 #include <cstring>
 #include <vector>
 
+#include "internal.h"
 #include "s4dplr.h"
 
 int stub_launch_count();
@@ -44,11 +45,24 @@ int main() {
         CHECK(s4dplr_kernel_gen(p, f, f, nullptr, f, f, f, K, ws, nullptr) == S4DPLR_OK);
         CHECK(s4dplr_forward(p, f, f, nullptr, f, f, f, nullptr, u, nullptr, y, ws, nullptr) == S4DPLR_OK);
         CHECK(s4dplr_conv_apply(p, u, y, ws, nullptr) == S4DPLR_OK);
+        CHECK(s4dplr_recurrent_prepare(p, f, f, nullptr, f, f, f, ws, nullptr) == S4DPLR_OK);
+        CHECK(s4dplr_recurrent_scan(p, nullptr, u, 7, K, y, ws, nullptr) == S4DPLR_OK);
+        CHECK(s4dplr_recurrent_scan(p, nullptr, u, 7, K, u, ws, nullptr) == S4DPLR_ERR_ALIAS);
         CHECK(stub_launch_count() > before);
         CHECK(s4dplr_forward(p, f, f, nullptr, f, f, f, nullptr, u, nullptr, u, ws, nullptr) == S4DPLR_ERR_ALIAS);
         CHECK(s4dplr_conv_fwd(p, u, K, nullptr, y, nullptr, nullptr) == S4DPLR_ERR_NULL);
         s4dplr_plan_destroy(p);
       }
+  // the recurrent scan's work split covers every pole with at most 32 lanes
+  // per sequence and 8 poles per lane
+  for (int N = 1; N <= 256; ++N)
+    for (long rows : {1L, 7L, 64L, 1000L, 8192L, 16384L, 1L << 20}) {
+      int ppl = 0, lg = -1;
+      s4::recurrent_shape(N, rows, &ppl, &lg);
+      CHECK(ppl == 1 || ppl == 2 || ppl == 4 || ppl == 8);
+      CHECK(lg >= 0 && lg <= 5);
+      CHECK((ppl << lg) >= N);
+    }
   s4dplr_plan* p = nullptr;
   CHECK(s4dplr_plan_create(&p, 1, 1, 3, 1, 0) == S4DPLR_ERR_SHAPE && !p);
   CHECK(s4dplr_plan_create(&p, 1, 1, 4, 1, 8) == S4DPLR_ERR_UNSUPPORTED);

@@ -31,6 +31,8 @@ def lib():
     L.s4dplr_conv_fwd.argtypes = [vp] * 7
     L.s4dplr_forward.argtypes = [vp] * 13
     L.s4dplr_conv_apply.argtypes = [vp] * 5
+    L.s4dplr_recurrent_prepare.argtypes = [vp] * 9
+    L.s4dplr_recurrent_scan.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp]
     L.s4dplr_plan_destroy.argtypes = [vp]
     L.s4dplr_status_string.restype = ctypes.c_char_p
     return L
@@ -47,7 +49,8 @@ def test_header_declares_the_boundary():
     for n in ["s4dplr_abi_version", "s4dplr_status_string", "s4dplr_plan_create",
               "s4dplr_plan_workspace_bytes", "s4dplr_plan_init", "s4dplr_kernel_gen",
               "s4dplr_conv_fwd", "s4dplr_forward", "s4dplr_plan_destroy",
-              "s4dplr_last_hip_error", "s4dplr_conv_apply"]:
+              "s4dplr_last_hip_error", "s4dplr_conv_apply", "s4dplr_recurrent_prepare",
+              "s4dplr_recurrent_scan"]:
         assert n in names
 
 
@@ -178,4 +181,40 @@ def test_hip_error_is_reported_without_a_device(lib):
     st, h = _create(lib, 4, 16, 256, 2)
     assert lib.s4dplr_plan_init(h, 1 << 30, None) == ERR_HIP
     assert lib.s4dplr_last_hip_error() != 0
+    lib.s4dplr_plan_destroy(h)
+
+
+def test_recurrent_validation(lib):
+    H, N, L, B = 4, 16, 256, 2
+    st, h = _create(lib, H, N, L, B)
+    fake, ws = 1 << 20, 1 << 32
+    # prepare: lambda, P, B, C, dt required; Q optional
+    args = [fake] * 6
+    for i in [0, 1, 3, 4, 5]:
+        a = list(args)
+        a[i] = None
+        assert lib.s4dplr_recurrent_prepare(h, *a, ws, None) == ERR_NULL
+    assert lib.s4dplr_recurrent_prepare(h, *args, None, None) == ERR_NULL
+    assert lib.s4dplr_recurrent_prepare(h, *args, ws + 64, None) == ERR_WORKSPACE
+    assert lib.s4dplr_recurrent_prepare(None, *args, ws, None) == ERR_NULL
+    # scan: state always required; u and y unless T = 0; D optional
+    u, T = 1 << 24, 100
+    ub = 4 * B * H * T
+    state = u + 2 * ub
+    y = state + 8 * B * H * N
+    assert lib.s4dplr_recurrent_scan(h, None, u, T, None, y, ws, None) == ERR_NULL
+    assert lib.s4dplr_recurrent_scan(h, None, None, T, state, y, ws, None) == ERR_NULL
+    assert lib.s4dplr_recurrent_scan(h, None, u, T, state, None, ws, None) == ERR_NULL
+    assert lib.s4dplr_recurrent_scan(h, None, u, T, state, y, None, None) == ERR_NULL
+    assert lib.s4dplr_recurrent_scan(h, None, u, T, state, y, ws + 8, None) == ERR_WORKSPACE
+    assert lib.s4dplr_recurrent_scan(h, None, u, -1, state, y, ws, None) == ERR_SHAPE
+    assert lib.s4dplr_recurrent_scan(h, None, u, (1 << 31) // (B * H), state, y, ws, None) == ERR_SHAPE
+    # T = 0 enqueues nothing, so it succeeds even without a device
+    assert lib.s4dplr_recurrent_scan(h, None, None, 0, state, None, ws, None) == OK
+    # aliasing: y over u, y over the state, the state over u, the state inside the workspace
+    assert lib.s4dplr_recurrent_scan(h, None, u, T, state, u + 4, ws, None) == ERR_ALIAS
+    assert lib.s4dplr_recurrent_scan(h, None, u, T, state, state + 8, ws, None) == ERR_ALIAS
+    assert lib.s4dplr_recurrent_scan(h, None, u, T, u + ub - 8, y, ws, None) == ERR_ALIAS
+    assert lib.s4dplr_recurrent_scan(h, None, u, T, ws + 256, y, ws, None) == ERR_ALIAS
+    assert lib.s4dplr_recurrent_scan(h, None, u, T, state, ws + 256, ws, None) == ERR_ALIAS
     lib.s4dplr_plan_destroy(h)
