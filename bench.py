@@ -67,6 +67,22 @@ def algorithmic_counts(w):
     return F1, Q2
 
 
+def recurrent_counts(w):
+    """Algorithmic work of the recurrent view (O(N) bilinear DPLR step).
+
+    Flops per pole per step: the update w = Abar0 x - e qx + Bbar0 u (two
+    complex products, one real-by-complex product, two complex adds: 18),
+    x' = w - g qw (8), the output Re(C x') accumulated (4), and the two sums
+    conj(Q) x' and qa x' for the next step (16): 46.  Diagonal: Abar0 x +
+    Bbar0 u (10) and the output (4): 14.
+    Bytes of one decode step (T = 1): the state read and written (16 B per
+    pole), u read and y written (8 B per sequence).
+    """
+    per_pole = 14 if w.diagonal else 46
+    rows = w.batch * w.H
+    return per_pole * w.N * rows, 16 * w.N * rows + 8 * rows
+
+
 def read_traffic(workload_name: str):
     """HBM bytes per convolution launch from the committed rocprofv3 counter
     summary, if it was taken on the current kernel sources; else None."""
@@ -217,6 +233,23 @@ def main() -> int:
     log(f"[bench] kernel_gen {t_gen * 1e6:.1f} us ({F1 / t_gen / 1e9:.0f} GFLOP/s), "
         f"conv {t_conv * 1e6:.1f} us ({Q2 / t_conv / 1e9:.0f} GB/s)")
 
+    # ---- the recurrent view: a full scan (T = L) and one decode step (T = 1) ---
+    flops_step, decode_bytes = recurrent_counts(w)
+    s4.recurrent_prepare(plan, params["lam"], P, params["Q"], params["B"], params["C"],
+                         params["dt"], ws, stream)
+    state = torch.zeros((w.batch, w.H, w.N, 2), dtype=torch.float32, device=dev)
+    scan = lambda i: s4.recurrent_scan(plan, params["D"], us[i % nsets], state, ys[i % nsets],
+                                       ws, stream)
+    t_one = timed(scan, 1)
+    n_scan = max(3, min(args.steps, int(0.5 / max(t_one, 1e-6))))
+    t_scan = timed(scan, n_scan)
+    u1 = us[0][..., :1].contiguous()
+    y1 = torch.empty_like(u1)
+    t_dec = timed(lambda i: s4.recurrent_scan(plan, params["D"], u1, state, y1, ws, stream), 200)
+    rec_tflops = flops_step * w.L / t_scan / 1e12
+    log(f"[bench] recurrent scan {t_scan * 1e6:.1f} us ({samples / t_scan:.3g} samples/s, "
+        f"{rec_tflops:.1f} TFLOP/s); decode step {t_dec * 1e6:.2f} us")
+
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -259,6 +292,21 @@ def main() -> int:
             "frac_fp32_unpacked_peak": F1 / t_gen / 1e12 / FP32_UNPACKED_TFLOPS,
             "algorithmic_flops": F1,
             "note": "pack + Cauchy/Woodbury + kernel spectrum; flops counted for the Cauchy sums",
+        },
+        "recurrent": {
+            "kernel": "recurrent_scan_kernel (O(N) bilinear DPLR step, carried state)",
+            "scan_us": t_scan * 1e6,
+            "scan_samples_per_s": samples / t_scan,
+            "bound": "alu",
+            "achieved": rec_tflops,
+            "peak": FP32_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": rec_tflops / FP32_PEAK_TFLOPS,
+            "frac_unpacked_peak": rec_tflops / FP32_UNPACKED_TFLOPS,
+            "algorithmic_flops_per_step": flops_step,
+            "decode_step_us": t_dec * 1e6,
+            "decode_bytes_per_step": decode_bytes,
+            "decode_tokens_per_s": w.batch / t_dec,
         },
         "forward_us_events": fwd_ms_events * 1e3,
         "cpu_baseline": None,

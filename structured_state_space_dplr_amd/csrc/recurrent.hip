@@ -78,6 +78,21 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// The lane's share of the sums conj(Q)^T x (a0 + i a1) and qa^T x (a2 + i a3)
+// over its poles, as fused multiply-adds.
+template <int PPL>
+__device__ __forceinline__ void partial_sums(const float2 (&qc)[PPL], const float2 (&qa)[PPL],
+                                             const float2 (&x)[PPL], float& a0, float& a1,
+                                             float& a2, float& a3) {
+#pragma unroll
+  for (int k = 0; k < PPL; ++k) {
+    a0 = fmaf(-qc[k].y, x[k].y, fmaf(qc[k].x, x[k].x, a0));
+    a1 = fmaf(qc[k].y, x[k].x, fmaf(qc[k].x, x[k].y, a1));
+    a2 = fmaf(-qa[k].y, x[k].y, fmaf(qa[k].x, x[k].x, a2));
+    a3 = fmaf(qa[k].y, x[k].x, fmaf(qa[k].x, x[k].y, a3));
+  }
+}
+
 }  // namespace
 
 // One wave per channel; the records are formed in fp64 and rounded once.
@@ -180,14 +195,7 @@ __global__ __launch_bounds__(256) void recurrent_scan_kernel(
   float2 qx = make_float2(0.f, 0.f), r2 = make_float2(0.f, 0.f);
   if constexpr (!DIAG) {
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-    for (int k = 0; k < PPL; ++k) {
-      const float2 t1 = cmul(qc[k], x[k]), t2 = cmul(qa[k], x[k]);
-      a0 += t1.x;
-      a1 += t1.y;
-      a2 += t2.x;
-      a3 += t2.y;
-    }
+    partial_sums<PPL>(qc, qa, x, a0, a1, a2, a3);
     qx = make_float2(group_sum<LOG2G>(a0), group_sum<LOG2G>(a1));
     r2 = make_float2(group_sum<LOG2G>(a2), group_sum<LOG2G>(a3));
   }
@@ -222,16 +230,19 @@ __global__ __launch_bounds__(256) void recurrent_scan_kernel(
         float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
         for (int k = 0; k < PPL; ++k) {
-          const float2 ax = cmul(ab[k], x[k]), eq = cmul(e[k], qx), gq = cmul(g[k], qw);
-          x[k] = make_float2(fmaf(bb[k].x, ut, ax.x - eq.x) - gq.x,
-                             fmaf(bb[k].y, ut, ax.y - eq.y) - gq.y);
-          yre = fmaf(c[k].x, x[k].x, fmaf(-c[k].y, x[k].y, yre));
-          const float2 t1 = cmul(qc[k], x[k]), t2 = cmul(qa[k], x[k]);
-          a0 += t1.x;
-          a1 += t1.y;
-          a2 += t2.x;
-          a3 += t2.y;
+          // x' = Abar0 x - e qx + Bbar0 u - g qw, one chain of fmas per part
+          const float2 xo = x[k];
+          float re = bb[k].x * ut, im = bb[k].y * ut;
+          re = fmaf(-ab[k].y, xo.y, fmaf(ab[k].x, xo.x, re));
+          im = fmaf(ab[k].y, xo.x, fmaf(ab[k].x, xo.y, im));
+          re = fmaf(e[k].y, qx.y, fmaf(-e[k].x, qx.x, re));
+          im = fmaf(-e[k].y, qx.x, fmaf(-e[k].x, qx.y, im));
+          re = fmaf(g[k].y, qw.y, fmaf(-g[k].x, qw.x, re));
+          im = fmaf(-g[k].y, qw.x, fmaf(-g[k].x, qw.y, im));
+          x[k] = make_float2(re, im);
+          yre = fmaf(-c[k].y, im, fmaf(c[k].x, re, yre));
         }
+        partial_sums<PPL>(qc, qa, x, a0, a1, a2, a3);
         qx = make_float2(group_sum<LOG2G>(a0), group_sum<LOG2G>(a1));
         r2 = make_float2(group_sum<LOG2G>(a2), group_sum<LOG2G>(a3));
       }
