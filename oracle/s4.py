@@ -50,6 +50,7 @@ __all__ = [
     "kernel_truncated", "kernel_aliased_dense", "generating_function",
     "kernel_cauchy", "conv_direct", "conv_direct_at", "conv_fft",
     "recurrence", "forward", "recurrent_forward",
+    "conv_backward_direct", "conv_backward_fft", "kernel_backward_dense",
 ]
 
 
@@ -358,3 +359,100 @@ def recurrent_forward(lam, P, Q, B, C, dt, D, u, x0=None, diagonal=False):
         y[:, h], xT[:, h] = recurrence(Abar, Bbar, C_c[h], D[h], u[:, h],
                                        None if x0 is None else x0[:, h], return_state=True)
     return y, xT
+
+
+# ---------------------------------------------------------------------------
+# Backward pass of the convolution-mode forward   ([scratch] sections 5 and 6:
+# the layer is trained through the convolution; its parameters are
+# Lambda, P, B, C, dt, D)
+# ---------------------------------------------------------------------------
+
+def conv_backward_direct(u, K, D, dy):
+    """Gradients of a scalar loss through y = K * u + D u, given dy = dloss/dy,
+    by direct summation of their plain definitions:
+
+      du[b,h,t] = sum_{j=0}^{L-1-t} K[h,j] dy[b,h,t+j] + D[h] dy[b,h,t]
+      dK[h,j]   = sum_b sum_{t=j}^{L-1} dy[b,h,t] u[b,h,t-j]
+      dD[h]     = sum_b sum_t dy[b,h,t] u[b,h,t]
+
+    u, dy: (batch, H, L); K: (H, L); D: (H,).  Returns (du, dK, dD).
+    O(B H L^2): for small inputs."""
+    u = np.asarray(u, np.float64)
+    dy = np.asarray(dy, np.float64)
+    K = np.asarray(K, np.float64)
+    D = np.asarray(D, np.float64)
+    L = u.shape[-1]
+    du = D[None, :, None] * dy
+    dK = np.zeros(K.shape, np.float64)
+    for j in range(L):
+        du[..., : L - j] += K[None, :, j, None] * dy[..., j:]
+        dK[:, j] = np.sum(dy[..., j:] * u[..., : L - j], axis=(0, 2))
+    dD = np.sum(dy * u, axis=(0, 2))
+    return du, dK, dD
+
+
+def conv_backward_fft(u, K, D, dy):
+    """The same three gradients through fp64 FFTs of length 2L (library
+    routine): du is the correlation of dy with K, dK the correlation of dy
+    with u summed over the batch (zero padding to 2L leaves no wrap-around)."""
+    u = np.asarray(u, np.float64)
+    dy = np.asarray(dy, np.float64)
+    K = np.asarray(K, np.float64)
+    D = np.asarray(D, np.float64)
+    L = u.shape[-1]
+    n = 2 * L
+    Fy = np.fft.rfft(dy, n)
+    du = np.fft.irfft(Fy * np.conj(np.fft.rfft(K, n))[None], n)[..., :L] + D[None, :, None] * dy
+    dK = np.fft.irfft(np.sum(Fy * np.conj(np.fft.rfft(u, n)), axis=0), n)[..., :L]
+    dD = np.sum(dy * u, axis=(0, 2))
+    return du, dK, dD
+
+
+def kernel_backward_dense(lam, P, Q, B, C, dt, dK, diagonal=False):
+    """Gradients of loss = sum_{h,k} dK[h,k] K[h,k] with respect to the
+    kernel's parameters, where K is the plain aliased definition
+    K_k = Re(C A-bar^k (I - A-bar^L)^{-1} B-bar) of the dense bilinear system
+    for A = Lambda - P Q^* ([scratch] sections 3 and 4; [wiki] "Structured
+    Transition Matrix").  The derivative is taken by PyTorch's reverse-mode
+    differentiation (fp64, CPU) of that definition, with every complex
+    parameter held as its real and imaginary parts.
+
+    Inputs as for ``forward``; dK is (H, L).  Returns a dict of gradients in
+    the same (..., 2) layout: "lam", "B", "C", "dt" and, unless diagonal,
+    "P" and "Q" -- with Q None (Q = P) the P gradient includes the Q path
+    and "Q" is None."""
+    import torch
+    dK = np.asarray(dK, np.float64)
+    H, L = dK.shape
+    tied = Q is None
+    t = lambda a: torch.tensor(np.asarray(a, np.float64), requires_grad=True)
+    lam_t, B_t, C_t = t(lam), t(B), t(C)
+    dt_t = t(dt)
+    P_t = None if diagonal else t(P)
+    Q_t = None if (diagonal or tied) else t(Q)
+    cx = lambda a: torch.complex(a[..., 0], a[..., 1])
+    N = lam_t.shape[1]
+    eye = torch.eye(N, dtype=torch.complex128)
+    loss = torch.zeros((), dtype=torch.float64)
+    for h in range(H):
+        lam_c, B_c, C_c = cx(lam_t[h]), cx(B_t[h]), cx(C_t[h])
+        A = torch.diag(lam_c)
+        if not diagonal:
+            P_c = cx(P_t[h])
+            Q_c = P_c if tied else cx(Q_t[h])
+            A = A - torch.outer(P_c, Q_c.conj())
+        half = dt_t[h] / 2
+        M = eye - half * A
+        Abar = torch.linalg.solve(M, eye + half * A)
+        Bbar = torch.linalg.solve(M, (dt_t[h] * B_c)[:, None])[:, 0]
+        ApowL = torch.linalg.matrix_power(Abar, L)
+        x = torch.linalg.solve(eye - ApowL, Bbar[:, None])[:, 0]
+        Ks = []
+        for k in range(L):
+            Ks.append((C_c @ x).real)
+            x = Abar @ x
+        loss = loss + torch.sum(torch.stack(Ks) * torch.from_numpy(dK[h]))
+    loss.backward()
+    g = lambda a: None if a is None else a.grad.numpy().copy()
+    return {"lam": g(lam_t), "P": g(P_t), "Q": g(Q_t), "B": g(B_t), "C": g(C_t),
+            "dt": g(dt_t)}

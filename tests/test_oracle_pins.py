@@ -407,3 +407,109 @@ def test_forward_tiny_cauchy_vs_dense():
         for h in range(y1.shape[1]):
             yd = o.conv_direct(x["u"][b, h], K2[h], float(x["D"][h]))
             assert np.abs(yd - y1[b, h]).max() <= 1e-11 * np.abs(yd).max()
+
+
+# --- Backward pass ------------------------------------------------------------
+
+def test_conv_backward_adjoint_identities():
+    # y is linear in u, and jointly linear in (K, D): for every u, K, D,
+    # sum(dy * y) = sum(du * u) = sum(dK * K) + sum(dD * D)
+    rng = np.random.default_rng(30)
+    for (Bt, H, L) in [(2, 3, 1), (2, 3, 2), (3, 2, 17), (1, 4, 64)]:
+        u, dy = rng.standard_normal((Bt, H, L)), rng.standard_normal((Bt, H, L))
+        K, D = rng.standard_normal((H, L)), rng.standard_normal(H)
+        y = np.array([[o.conv_direct(u[b, h], K[h], D[h]) for h in range(H)] for b in range(Bt)])
+        du, dK, dD = o.conv_backward_direct(u, K, D, dy)
+        s = np.sum(dy * y)
+        assert abs(np.sum(du * u) - s) <= 1e-12 * (1 + abs(s))
+        assert abs(np.sum(dK * K) + np.sum(dD * D) - s) <= 1e-12 * (1 + abs(s))
+
+
+def test_conv_backward_impulses():
+    # dy a unit impulse at t0 picks out the row of the Jacobian: du[t] = K[t0-t] (t <= t0)
+    # plus D at t0; dK[j] = u[t0-j]; dD = u[t0]
+    rng = np.random.default_rng(31)
+    L = 9
+    u, K, D = rng.standard_normal((1, 1, L)), rng.standard_normal((1, L)), rng.standard_normal(1)
+    for t0 in range(L):
+        dy = np.zeros((1, 1, L))
+        dy[0, 0, t0] = 1.0
+        du, dK, dD = o.conv_backward_direct(u, K, D, dy)
+        ref = np.zeros(L)
+        ref[: t0 + 1] = K[0, t0::-1]
+        ref[t0] += D[0]
+        np.testing.assert_allclose(du[0, 0], ref, atol=1e-15)
+        refk = np.zeros(L)
+        refk[: t0 + 1] = u[0, 0, t0::-1]
+        np.testing.assert_allclose(dK[0], refk, atol=1e-15)
+        assert dD[0] == u[0, 0, t0]
+
+
+@pytest.mark.parametrize("L", [2, 8, 64, 256])
+def test_conv_backward_fft_equals_direct(L):
+    rng = np.random.default_rng(32)
+    u, dy = rng.standard_normal((3, 2, L)), rng.standard_normal((3, 2, L))
+    K, D = rng.standard_normal((2, L)), rng.standard_normal(2)
+    a = o.conv_backward_direct(u, K, D, dy)
+    b = o.conv_backward_fft(u, K, D, dy)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(y, x, rtol=0, atol=1e-12 * np.abs(x).max())
+
+
+def _kernel_loss(x, dK, diagonal=False):
+    K, _ = o.forward(x["lam"], x["P"], x["Q"], x["B"], x["C"], x["dt"], np.zeros(len(x["dt"])),
+                     np.zeros((1,) + dK.shape), method="dense", diagonal=diagonal)
+    return float(np.sum(K * dK))
+
+
+@pytest.mark.parametrize("diagonal,distinct_q", [(False, False), (False, True), (True, False)])
+def test_kernel_backward_finite_differences(diagonal, distinct_q):
+    # central differences of the dense aliased kernel, one real component at a time
+    x = make_generic_inputs(H=2, N=3, L=8, batch=1, seed=33, diagonal=diagonal,
+                            distinct_q=distinct_q)
+    x = {k: (None if v is None or k == "workload" else np.asarray(v, np.float64))
+         for k, v in x.items()}
+    dK = np.random.default_rng(34).standard_normal((2, 8))
+    g = o.kernel_backward_dense(x["lam"], x["P"], x["Q"], x["B"], x["C"], x["dt"], dK,
+                                diagonal=diagonal)
+    names = ["lam", "B", "C", "dt"] + ([] if diagonal else ["P"] + (["Q"] if distinct_q else []))
+    for name in names:
+        flat = x[name].reshape(-1)
+        for i in range(flat.size):
+            e = 1e-6 * max(1.0, abs(flat[i]))
+            xp = {k: (None if v is None else v.copy()) for k, v in x.items()}
+            xm = {k: (None if v is None else v.copy()) for k, v in x.items()}
+            xp[name].reshape(-1)[i] += e
+            xm[name].reshape(-1)[i] -= e
+            fd = (_kernel_loss(xp, dK, diagonal) - _kernel_loss(xm, dK, diagonal)) / (2 * e)
+            an = g[name].reshape(-1)[i]
+            assert abs(fd - an) <= 1e-5 * max(1.0, abs(an)), (name, i, fd, an)
+
+
+def test_kernel_backward_scalar_closed_form():
+    # N = 1, diagonal: K_k = Re(c m_k) with m_k = b-bar a-bar^k / (1 - a-bar^L), so
+    # dloss/dRe(c) + i dloss/dIm(c) = sum_k dK_k conj(m_k), and the same with c and b swapped
+    # through b-bar = dt b / (1 - dt lam / 2)
+    lam, b, c, dt, L = -0.3 + 2.0j, 0.8 - 0.4j, 1.1 + 0.6j, 0.25, 16
+    ab = (1 + dt * lam / 2) / (1 - dt * lam / 2)
+    bb = dt * b / (1 - dt * lam / 2)
+    k = np.arange(L)
+    dK = np.random.default_rng(35).standard_normal((1, L))
+    m = bb * ab ** k / (1 - ab ** L)
+    ri = lambda z: np.array([[[z.real, z.imag]]])
+    g = o.kernel_backward_dense(ri(lam), None, None, ri(b), ri(c), np.array([dt]), dK,
+                                diagonal=True)
+    gc = np.sum(dK[0] * np.conj(m))
+    np.testing.assert_allclose(g["C"][0, 0], [gc.real, gc.imag], rtol=1e-12)
+    gb = np.sum(dK[0] * np.conj(c * m / b))
+    np.testing.assert_allclose(g["B"][0, 0], [gb.real, gb.imag], rtol=1e-12)
+
+
+def test_kernel_backward_tied_q_is_sum_of_both_paths():
+    x = make_generic_inputs(H=1, N=4, L=8, batch=1, seed=36)
+    dK = np.random.default_rng(37).standard_normal((1, 8))
+    tied = o.kernel_backward_dense(x["lam"], x["P"], None, x["B"], x["C"], x["dt"], dK)
+    split = o.kernel_backward_dense(x["lam"], x["P"], x["P"], x["B"], x["C"], x["dt"], dK)
+    np.testing.assert_allclose(tied["P"], split["P"] + split["Q"], rtol=1e-12, atol=1e-14)
+    for k in ("lam", "B", "C", "dt"):
+        np.testing.assert_allclose(tied[k], split[k], rtol=1e-12, atol=1e-14)
