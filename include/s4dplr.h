@@ -197,6 +197,45 @@ s4dplr_status s4dplr_recurrent_scan(const s4dplr_plan* plan, const float* D, con
                                     int T, float* state, float* y, void* ws,
                                     hipStream_t stream);
 
+/*
+ * Backward pass of the causal convolution ("The S4 kernel, from scratch",
+ * sections 5 and 6: the layer is trained through the convolution).  Given
+ * dy = dloss/dy for y = K * u + D u:
+ *   du[b][h][t] = sum_{j=0}^{L-1-t} K[h][j] dy[b][h][t+j] + D[h] dy[b][h][t]
+ *   dK[h][j]    = sum_b sum_{t=j}^{L-1} dy[b][h][t] u[b][h][t-j]
+ *   dD[h]       = sum_b sum_t dy[b][h][t] u[b][h][t]
+ * each by FFTs zero-padded to 2L.  u, dy, du: [batch][H][L]; K, dK: [H][L];
+ * D, dD: [H].  Any of du, dK, dD may be NULL (not computed).  du needs K
+ * (D may be NULL: D = 0); dK and dD need u.  Outputs are overwritten, not
+ * accumulated, and must not overlap the inputs, each other or the workspace
+ * (ERR_ALIAS).  Computing du replaces the convolution weights held in the
+ * workspace (a later s4dplr_conv_apply then applies the correlation).
+ * Supported for L <= 16384 (ERR_UNSUPPORTED above).
+ * Errors: ERR_NULL, ERR_ALIAS, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP.
+ */
+s4dplr_status s4dplr_conv_bwd(const s4dplr_plan* plan, const float* u, const float* K,
+                              const float* D, const float* dy, float* du, float* dK, float* dD,
+                              void* ws, hipStream_t stream);
+
+/*
+ * Backward pass of kernel generation ("The S4 kernel, from scratch",
+ * sections 3-4): the gradients of loss = sum_{h,k} dK[h][k] K[h][k] with
+ * respect to lambda, P, Q, B, C (each [H][N] interleaved complex; the pair
+ * (re, im) of an output is (dloss/dRe, dloss/dIm)) and dt ([H]), for K the
+ * aliased kernel of s4dplr_kernel_gen.  Inputs as for s4dplr_kernel_gen plus
+ * dK [H][L].  Q == NULL means Q = P: dP then includes the path through Q and
+ * dQ is ignored.  With S4DPLR_DIAGONAL, dP and dQ are ignored.  Every output
+ * may be NULL (not written); outputs are overwritten, not accumulated, and
+ * must not overlap the inputs, each other or the workspace (ERR_ALIAS).
+ * Supported for L <= 16384 (ERR_UNSUPPORTED above).
+ * Errors: ERR_NULL, ERR_ALIAS, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP.
+ */
+s4dplr_status s4dplr_kernel_gen_bwd(const s4dplr_plan* plan, const float* lambda, const float* P,
+                                    const float* Q, const float* B, const float* C,
+                                    const float* dt, const float* dK, float* dlambda, float* dP,
+                                    float* dQ, float* dB, float* dC, float* ddt, void* ws,
+                                    hipStream_t stream);
+
 /* Release a plan (NULL is ignored).  Host-only. */
 void s4dplr_plan_destroy(s4dplr_plan* plan);
 

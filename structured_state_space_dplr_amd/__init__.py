@@ -19,7 +19,8 @@ import torch  # loads the HIP runtime that libs4dplr then shares
 __all__ = [
     "S4DPLRError", "DIAGONAL", "abi_version", "status_string", "plan_create",
     "plan_workspace_bytes", "plan_init", "kernel_gen", "conv_fwd", "forward",
-    "conv_apply", "recurrent_prepare", "recurrent_scan", "plan_destroy", "Plan", "LIB_PATH",
+    "conv_apply", "recurrent_prepare", "recurrent_scan", "conv_bwd", "kernel_gen_bwd",
+    "plan_destroy", "Plan", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libs4dplr.so")
@@ -58,6 +59,10 @@ _lib.s4dplr_recurrent_prepare.restype = ctypes.c_int
 _lib.s4dplr_recurrent_prepare.argtypes = [_p] * 9
 _lib.s4dplr_recurrent_scan.restype = ctypes.c_int
 _lib.s4dplr_recurrent_scan.argtypes = [_p, _p, _p, ctypes.c_int, _p, _p, _p, _p]
+_lib.s4dplr_conv_bwd.restype = ctypes.c_int
+_lib.s4dplr_conv_bwd.argtypes = [_p] * 10
+_lib.s4dplr_kernel_gen_bwd.restype = ctypes.c_int
+_lib.s4dplr_kernel_gen_bwd.argtypes = [_p] * 16
 _lib.s4dplr_plan_destroy.restype = None
 _lib.s4dplr_plan_destroy.argtypes = [_p]
 
@@ -185,6 +190,26 @@ def recurrent_scan(plan: "Plan | int", D, u, state, y, ws, stream=None) -> None:
         p, _ptr(D, "D", (H,)), _ptr(u, "u", (batch, H, T)), T,
         _ptr(state, "state", (batch, H, N, 2)), _ptr(y, "y", (batch, H, T)), _ws_ptr(ws),
         _stream(stream)), "recurrent_scan")
+
+
+def conv_bwd(plan: "Plan | int", u, K, D, dy, du, dK, dD, ws, stream=None) -> None:
+    p, (H, N, L, batch) = _dims(plan)
+    _check(_lib.s4dplr_conv_bwd(
+        p, _ptr(u, "u", (batch, H, L)), _ptr(K, "K", (H, L)), _ptr(D, "D", (H,)),
+        _ptr(dy, "dy", (batch, H, L)), _ptr(du, "du", (batch, H, L)), _ptr(dK, "dK", (H, L)),
+        _ptr(dD, "dD", (H,)), _ws_ptr(ws), _stream(stream)), "conv_bwd")
+
+
+def kernel_gen_bwd(plan: "Plan | int", lam, P, Q, B, C, dt, dK, dlam, dP, dQ, dB, dC, ddt, ws,
+                   stream=None) -> None:
+    p, (H, N, L, _) = _dims(plan)
+    cplx = (H, N, 2)
+    _check(_lib.s4dplr_kernel_gen_bwd(
+        p, _ptr(lam, "lam", cplx), _ptr(P, "P", cplx), _ptr(Q, "Q", cplx), _ptr(B, "B", cplx),
+        _ptr(C, "C", cplx), _ptr(dt, "dt", (H,)), _ptr(dK, "dK", (H, L)),
+        _ptr(dlam, "dlam", cplx), _ptr(dP, "dP", cplx), _ptr(dQ, "dQ", cplx),
+        _ptr(dB, "dB", cplx), _ptr(dC, "dC", cplx), _ptr(ddt, "ddt", (H,)), _ws_ptr(ws),
+        _stream(stream)), "kernel_gen_bwd")
 
 
 def _dims(plan):

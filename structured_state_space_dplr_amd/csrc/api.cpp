@@ -158,6 +158,18 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
   off = align_up(off + sizeof(float) * 16 * (size_t)H * N);
   p->off_rchan = off;
   off = align_up(off + sizeof(float) * 4 * (size_t)H);
+  p->off_bghat = off;
+  if (lds) off = align_up(off + sizeof(float) * 2 * (size_t)H * L);
+  p->off_bbeta = off;
+  if (lds) off = align_up(off + sizeof(float) * 8 * (size_t)H * L);
+  p->off_bpart = off;
+  if (lds) {
+    const size_t corr = sizeof(float) * 2 * (size_t)((batch + s4::kCorrRows - 1) / s4::kCorrRows) *
+                        H * (L + 1);
+    const size_t pole = sizeof(float) * 12 * (size_t)H * ((L + s4::kBwdChunk - 1) / s4::kBwdChunk) *
+                        N;
+    off = align_up(off + (corr > pole ? corr : pole));
+  }
   p->total = off;
 
   // fp64 tables, rounded once to fp32.
@@ -247,7 +259,7 @@ s4dplr_status s4dplr_conv_fwd(const s4dplr_plan* p, const float* u, const float*
     return S4DPLR_ERR_ALIAS;
   unsigned char* w = static_cast<unsigned char*>(ws);
   hipError_t e;
-  if ((e = s4::launch_spectrum_from_time(p, K, D, w, stream)) != hipSuccess) return hip_fail(e);
+  if ((e = s4::launch_spectrum_from_time(p, K, D, w, stream, 0)) != hipSuccess) return hip_fail(e);
   if ((e = s4::launch_conv(p, u, y, w, stream)) != hipSuccess) return hip_fail(e);
   return S4DPLR_OK;
 }
@@ -315,6 +327,74 @@ s4dplr_status s4dplr_recurrent_scan(const s4dplr_plan* p, const float* D, const 
   if (T == 0) return S4DPLR_OK;
   hipError_t e = s4::launch_recurrent_scan(p, D, u, state, y, T,
                                            static_cast<unsigned char*>(ws), stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return S4DPLR_OK;
+}
+
+s4dplr_status s4dplr_conv_bwd(const s4dplr_plan* p, const float* u, const float* K,
+                              const float* D, const float* dy, float* du, float* dK, float* dD,
+                              void* ws, hipStream_t stream) {
+  if (!valid_plan(p)) return S4DPLR_ERR_NULL;
+  if (!dy) return S4DPLR_ERR_NULL;
+  if (du && !K) return S4DPLR_ERR_NULL;
+  if ((dK || dD) && !u) return S4DPLR_ERR_NULL;
+  if (s4dplr_status st = check_ws(ws)) return st;
+  if (!s4::lds_path(p)) return S4DPLR_ERR_UNSUPPORTED;
+  const size_t ub = sizeof(float) * (size_t)p->batch * p->H * p->L;
+  const size_t kb = sizeof(float) * (size_t)p->H * p->L;
+  const size_t db = sizeof(float) * (size_t)p->H;
+  if (du && (overlaps(du, ub, dy, ub) || overlaps(du, ub, u, ub) || overlaps(du, ub, K, kb) ||
+             overlaps(du, ub, D, db) || overlaps(du, ub, ws, p->total)))
+    return S4DPLR_ERR_ALIAS;
+  if (dK && (overlaps(dK, kb, dy, ub) || overlaps(dK, kb, u, ub) || overlaps(dK, kb, du, ub) ||
+             overlaps(dK, kb, K, kb) || overlaps(dK, kb, ws, p->total)))
+    return S4DPLR_ERR_ALIAS;
+  if (dD && (overlaps(dD, db, dy, ub) || overlaps(dD, db, u, ub) || overlaps(dD, db, du, ub) ||
+             overlaps(dD, db, dK, kb) || overlaps(dD, db, ws, p->total)))
+    return S4DPLR_ERR_ALIAS;
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  hipError_t e;
+  if (du) {
+    if ((e = s4::launch_spectrum_from_time(p, K, D, w, stream, 1)) != hipSuccess) return hip_fail(e);
+    if ((e = s4::launch_conv(p, dy, du, w, stream)) != hipSuccess) return hip_fail(e);
+  }
+  if (dK || dD) {
+    if ((e = s4::launch_corr(p, u, dy, dK, dD, w, stream)) != hipSuccess) return hip_fail(e);
+  }
+  return S4DPLR_OK;
+}
+
+s4dplr_status s4dplr_kernel_gen_bwd(const s4dplr_plan* p, const float* lambda, const float* P,
+                                    const float* Q, const float* B, const float* C,
+                                    const float* dt, const float* dK, float* dlambda, float* dP,
+                                    float* dQ, float* dB, float* dC, float* ddt, void* ws,
+                                    hipStream_t stream) {
+  if (!valid_plan(p)) return S4DPLR_ERR_NULL;
+  if (s4dplr_status st = check_params(p, lambda, P, B, C, dt)) return st;
+  if (!dK) return S4DPLR_ERR_NULL;
+  if (s4dplr_status st = check_ws(ws)) return st;
+  if (!s4::lds_path(p)) return S4DPLR_ERR_UNSUPPORTED;
+  const bool diag = (p->flags & S4DPLR_DIAGONAL) != 0;
+  if (diag) dP = dQ = nullptr;
+  if (!Q) dQ = nullptr;
+  const size_t cb = sizeof(float) * 2 * (size_t)p->H * p->N;
+  const size_t hb = sizeof(float) * (size_t)p->H;
+  const size_t kb = sizeof(float) * (size_t)p->H * p->L;
+  // every output is disjoint from every input, from the workspace and from the other outputs
+  const void* ins[] = {lambda, P, Q, B, C, dK, dt};
+  const size_t inb[] = {cb, cb, cb, cb, cb, kb, hb};
+  void* outs[] = {dlambda, dP, dQ, dB, dC, ddt};
+  const size_t outb[] = {cb, cb, cb, cb, cb, hb};
+  for (int i = 0; i < 6; ++i) {
+    if (!outs[i]) continue;
+    if (overlaps(outs[i], outb[i], ws, p->total)) return S4DPLR_ERR_ALIAS;
+    for (int j = 0; j < 7; ++j)
+      if (overlaps(outs[i], outb[i], ins[j], inb[j])) return S4DPLR_ERR_ALIAS;
+    for (int j = 0; j < i; ++j)
+      if (overlaps(outs[i], outb[i], outs[j], outb[j])) return S4DPLR_ERR_ALIAS;
+  }
+  hipError_t e = s4::launch_kernel_gen_bwd(p, lambda, P, Q, B, C, dt, dK, dlambda, dP, dQ, dB,
+                                           dC, ddt, static_cast<unsigned char*>(ws), stream);
   if (e != hipSuccess) return hip_fail(e);
   return S4DPLR_OK;
 }

@@ -1,0 +1,513 @@
+// Backward pass of the convolution-mode forward ("The S4 kernel, from
+// scratch", sections 4-6: the layer is trained through the convolution).
+//
+// Convolution, y = K * u + D u (causal, per channel):
+//   du[t] = sum_j K_j dy[t+j] + D dy[t]    -- the correlation with (K + D delta);
+//            handled by the forward's convolution kernel with conjugated
+//            spectral weights (see launch_spectrum_from_time),
+//   dK[j] = sum_b sum_t dy[b,t] u[b,t-j]   -- this file: the batch sum of the
+//            correlation spectra conj(U) G, then one inverse transform,
+//   dD    = dK[0].
+//
+// Kernel generation, K = Re(ifft_L(Khat)), Khat_l = p_l (k00 - k01 k10 / (1 + k11)),
+// k_ab = sum_n w_ab,n r_n, r_n = 1/(g_l - Lambda_n), p_l = 2/(1+z_l) (section 4).
+// For a real loss and a complex quantity v, write grad(v) = dloss/dRe v +
+// i dloss/dIm v.  Then grad(Khat_l) = Ghat_l = FFT_L(dK)_l / L, and for a
+// parameter that Khat depends on holomorphically, grad = sum_l
+// conj(dKhat_l/dparam) Ghat_l (conj(Q) enters instead of Q: grad(Q) is the
+// conjugate of that sum for conj(Q)).  With alpha_ab = dKhat/dk_ab and
+// beta_ab,l = conj(alpha_ab,l) Ghat_l, per pole n:
+//   R_ab = sum_l beta_ab,l conj(r_n,l),
+//   T    = sum_l conj(r_n,l)^2 sum_ab conj(w_ab,n) beta_ab,l,
+//   E    = sum_l conj(g_l) conj(r_n,l)^2 sum_ab conj(w_ab,n) beta_ab,l,
+// and grad(C_n) = conj(B) R00 + conj(P) R01, grad(B_n) = conj(C) R00 + Q R10,
+// grad(P_n) = conj(C) R01 + Q R11, grad(Q_n) = B conj(R10) + P conj(R11),
+// grad(Lambda_n) = T, dloss/ddt = Re(sum_n E) / dt (g = (2/dt)(1-z)/(1+z)).
+// The frequency l = L/2 (z = -1) uses the limit Khat = (dt/2) sum_n C_n B_n
+// and is added separately.
+#include <hip/hip_runtime.h>
+
+#include "cauchy.h"
+#include "device_fft.h"
+#include "internal.h"
+
+namespace s4 {
+
+namespace {
+
+template <typename T>
+T* at(unsigned char* ws, size_t off) {
+  return reinterpret_cast<T*>(ws + off);
+}
+
+__host__ __device__ constexpr int imax(int a, int b) { return a > b ? a : b; }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// dK, dD: batch-summed correlation spectrum, then one inverse per channel
+// ---------------------------------------------------------------------------
+template <int LOG2L>
+struct CorrShape {
+  static constexpr int L = 1 << LOG2L;
+  static constexpr int E = 1 << fft_elems_log(LOG2L);
+  static constexpr int NTL = L / E;              // threads of one transform
+  static constexpr int NT = imax(64, NTL);
+  static constexpr int MP = lds_padded_size(L);
+  static constexpr int EPT = (L / 2 + 1 + NT - 1) / NT;   // even bins per thread
+  static constexpr int OPT = (L / 2 + NT - 1) / NT;       // odd bins per thread
+};
+
+// Block (h, c) sums conj(U_j) G_j, j in [0, L], over the batch rows
+// [c R, c R + R) of channel h, where U and G are the spectra of u and dy
+// zero-padded to 2L.  Both come from two L-point transforms of
+// a_n = u_n + i dy_n: the even bins 2k from A = DFT_L(a), the odd bins 2k+1
+// from B = DFT_L(a_n e^{-i pi n / L}), each split by the symmetry of real
+// sequences:
+//   U_2k = (A_k + conj A_{L-k}) / 2,     G_2k = (A_k - conj A_{L-k}) / 2i,
+//   U_2k+1 = (B_k + conj B_{L-1-k}) / 2, G_2k+1 = (B_k - conj B_{L-1-k}) / 2i.
+template <int LOG2L>
+__global__ __launch_bounds__(CorrShape<LOG2L>::NT) void corr_spec_kernel(
+    const float* __restrict__ u, const float* __restrict__ dy, float2* part, const float2* twL,
+    const float2* __restrict__ cs, int H, int batch) {
+  // (part and twL are not __restrict__: the row loop's stores to part then keep
+  // the compiler from hoisting every pass's twiddles out of the loop, which
+  // would hold them all in registers and spill at 1024 threads.)
+  using S = CorrShape<LOG2L>;
+  constexpr int L = S::L, NT = S::NT;
+  // Large transforms run 1024 threads with at most 128 VGPRs each: there the
+  // running sums live in the block's own output row (each bin always belongs
+  // to the same thread) instead of in registers.
+  constexpr bool kAccInRow = LOG2L >= 13;
+  constexpr int NE = kAccInRow ? 1 : S::EPT, NO = kAccInRow ? 1 : S::OPT;
+  __shared__ float2 buf[S::MP];
+  const int h = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+  float2* out = part + ((size_t)c * H + h) * (L + 1);
+  float2 acce[NE], acco[NO];
+#pragma unroll
+  for (int i = 0; i < NE; ++i) acce[i] = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int i = 0; i < NO; ++i) acco[i] = make_float2(0.f, 0.f);
+  // conj(U) G from the bin pair (X_k, conj X_partner) of the a-transform
+  auto corr = [](float2 xk, float2 xp) {
+    const float2 cx = cconj(xp);
+    const float2 U = make_float2(0.5f * (xk.x + cx.x), 0.5f * (xk.y + cx.y));
+    const float2 Gi = make_float2(0.5f * (xk.x - cx.x), 0.5f * (xk.y - cx.y));   // i G
+    return cmul(cconj(U), make_float2(Gi.y, -Gi.x));                               // G = -i (i G)
+  };
+  auto accum = [&](float2& acc, int j, bool first, float2 v) {
+    if constexpr (kAccInRow) {
+      out[j] = first ? v : cadd(out[j], v);
+    } else {
+      acc = cadd(acc, v);
+    }
+  };
+  const int b_first = c * kCorrRows;
+  const int b_end = min(batch, (c + 1) * kCorrRows);
+  for (int b = b_first; b < b_end; ++b) {
+    const size_t row = (size_t)b * H + h;
+    const float* ur = u + row * L;
+    const float* gr = dy + row * L;
+    const bool first = b == b_first;
+    // even bins
+#pragma unroll 4
+    for (int n = tid; n < L; n += NT) buf[lds_pad(n)] = make_float2(ur[n], gr[n]);
+    __syncthreads();
+    lds_fft<LOG2L, false>(buf, tid, tid < S::NTL, twL);
+    if constexpr (kAccInRow) {
+#pragma unroll 1
+      for (int k = tid; k <= L / 2; k += NT)
+        accum(acce[0], 2 * k, first, corr(buf[lds_pad(k & (L - 1))], buf[lds_pad((L - k) & (L - 1))]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < S::EPT; ++i) {
+        const int k = tid + i * NT;
+        if (k <= L / 2)
+          accum(acce[i], 2 * k, first,
+                corr(buf[lds_pad(k & (L - 1))], buf[lds_pad((L - k) & (L - 1))]));
+      }
+    }
+    __syncthreads();
+    // odd bins
+#pragma unroll 4
+    for (int n = tid; n < L; n += NT) {
+      const float2 w = cs[n];                             // e^{-i pi n/L} = conj(w)
+      buf[lds_pad(n)] = cmul(make_float2(ur[n], gr[n]), make_float2(w.x, -w.y));
+    }
+    __syncthreads();
+    lds_fft<LOG2L, false>(buf, tid, tid < S::NTL, twL);
+    if constexpr (kAccInRow) {
+#pragma unroll 1
+      for (int k = tid; k < L / 2; k += NT)
+        accum(acco[0], 2 * k + 1, first, corr(buf[lds_pad(k)], buf[lds_pad(L - 1 - k)]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < S::OPT; ++i) {
+        const int k = tid + i * NT;
+        if (k < L / 2)
+          accum(acco[i], 2 * k + 1, first, corr(buf[lds_pad(k)], buf[lds_pad(L - 1 - k)]));
+      }
+    }
+    __syncthreads();
+  }
+  if constexpr (!kAccInRow) {
+#pragma unroll
+    for (int i = 0; i < S::EPT; ++i) {
+      const int k = tid + i * NT;
+      if (k <= L / 2) out[2 * k] = acce[i];
+    }
+#pragma unroll
+    for (int i = 0; i < S::OPT; ++i) {
+      const int k = tid + i * NT;
+      if (k < L / 2) out[2 * k + 1] = acco[i];
+    }
+  }
+}
+
+// Sums the partial spectra S_j of channel h, j in [0, L], and inverts the
+// real 2L-point transform through the packing: with
+//   W_k = (S_k + conj S_{L-k}) / 2 + i e^{i pi k/L} (S_k - conj S_{L-k}) / 2,
+// (1/L) IDFT_L(W)_m = c_2m + i c_2m+1, and c_0 .. c_{L-1} is dK.
+template <int LOG2L>
+__global__ __launch_bounds__(CorrShape<LOG2L>::NT) void corr_inv_kernel(
+    const float2* __restrict__ part, float* __restrict__ dK, float* __restrict__ dD,
+    const float2* __restrict__ twL, const float2* __restrict__ cs, int H, int nparts) {
+  using S = CorrShape<LOG2L>;
+  constexpr int L = S::L, NT = S::NT;
+  __shared__ float2 buf[S::MP];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  for (int j = tid; j <= L; j += NT) {
+    float2 s = make_float2(0.f, 0.f);
+    for (int c = 0; c < nparts; ++c) s = cadd(s, part[((size_t)c * H + h) * (L + 1) + j]);
+    buf[lds_pad(j)] = s;
+  }
+  __syncthreads();
+  for (int k = tid; k <= L / 2; k += NT) {
+    const int km = L - k;
+    const float2 sk = buf[lds_pad(k)], sm = buf[lds_pad(km)];
+    const float2 ck = cs[k], cm = cs[km];
+    // W_k, and W_{L-k} from the same pair (for k = 0 the partner is the bin L)
+    const float2 ek = make_float2(0.5f * (sk.x + sm.x), 0.5f * (sk.y - sm.y));
+    const float2 dk = make_float2(0.5f * (sk.x - sm.x), 0.5f * (sk.y + sm.y));
+    const float2 ok = cmul(make_float2(-ck.y, ck.x), dk);       // i e^{i pi k/L} (S_k - conj S_m)/2
+    const float2 em = make_float2(0.5f * (sm.x + sk.x), 0.5f * (sm.y - sk.y));
+    const float2 dm = make_float2(0.5f * (sm.x - sk.x), 0.5f * (sm.y + sk.y));
+    const float2 om = cmul(make_float2(-cm.y, cm.x), dm);
+    buf[lds_pad(k)] = cadd(ek, ok);
+    if (k != 0 && km != k) buf[lds_pad(km)] = cadd(em, om);
+  }
+  __syncthreads();
+  lds_fft<LOG2L, true>(buf, tid, tid < S::NTL, twL);
+  const float invL = 1.0f / (float)L;
+  for (int m = tid; m < L / 2; m += NT) {
+    const float2 v = buf[lds_pad(m)];
+    const float2 o = make_float2(v.x * invL, v.y * invL);
+    if (dK) reinterpret_cast<float2*>(dK + (size_t)h * L)[m] = o;
+    if (m == 0 && dD) dD[h] = o.x;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel generation backward
+// ---------------------------------------------------------------------------
+// Ghat = FFT_L(dK) / L per channel.
+template <int LOG2L>
+__global__ __launch_bounds__(CorrShape<LOG2L>::NT) void ghat_kernel(
+    const float* __restrict__ dK, float2* __restrict__ ghat, const float2* __restrict__ twL) {
+  using S = CorrShape<LOG2L>;
+  constexpr int L = S::L, NT = S::NT;
+  __shared__ float2 buf[S::MP];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  for (int k = tid; k < L; k += NT) buf[lds_pad(k)] = make_float2(dK[(size_t)h * L + k], 0.f);
+  __syncthreads();
+  lds_fft<LOG2L, false>(buf, tid, tid < S::NTL, twL);
+  const float invL = 1.0f / (float)L;
+  for (int l = tid; l < L; l += NT) {
+    const float2 v = buf[lds_pad(l)];
+    ghat[(size_t)h * L + l] = make_float2(v.x * invL, v.y * invL);
+  }
+}
+
+// beta_ab,l = conj(alpha_ab,l) Ghat_l per (channel, frequency), stored as two
+// float4: (beta00, beta01), (beta10, beta11); zero at l = L/2.
+//   alpha00 = p, alpha01 = -p k10 / (1 + k11), alpha10 = -p k01 / (1 + k11),
+//   alpha11 = p k01 k10 / (1 + k11)^2, p = 2/(1+z) = 1 + i tan(pi l / L).
+template <int F, bool DIAG>
+__global__ __launch_bounds__(kCauchyThreads) void kgen_bwd_coef_kernel(
+    ParamPtrs pp, const float* __restrict__ tanT, const float2* __restrict__ ghat,
+    float4* __restrict__ beta, int N, int NP, int L) {
+  __shared__ float4 rec[kRec * kMaxPoles];
+  __shared__ float2 red[kCauchyThreads / 64];
+  const int h = blockIdx.y, tid = threadIdx.x;
+  const float2 part = build_pole_records(pp, h, N, NP, DIAG, rec, tid, kCauchyThreads);
+  block_sum2<kCauchyThreads>(part, red, tid);   // (barrier: the records are complete)
+  const float two_dt = 2.0f / pp.dt[h];
+  int l[F];
+  float T[F], G[F], acc[F][8];
+#pragma unroll
+  for (int f = 0; f < F; ++f) {
+    l[f] = (blockIdx.x * F + f) * kCauchyThreads + tid;
+    T[f] = l[f] < L ? tanT[l[f]] : 0.f;
+    G[f] = two_dt * T[f];
+#pragma unroll
+    for (int a = 0; a < 8; ++a) acc[f][a] = 0.f;
+  }
+  cauchy_sums<F, DIAG>(rec, NP, G, acc);
+#pragma unroll
+  for (int f = 0; f < F; ++f) {
+    if (l[f] >= L) continue;
+    float4* out = beta + 2 * ((size_t)h * L + l[f]);
+    if (2 * l[f] == L) {
+      out[0] = out[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      continue;
+    }
+    const float2 p = make_float2(1.0f, T[f]);
+    const float2 gh = ghat[(size_t)h * L + l[f]];
+    const float2 b00 = cmul(cconj(p), gh);
+    if constexpr (DIAG) {
+      out[0] = make_float4(b00.x, b00.y, 0.f, 0.f);
+      out[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+      const float2 k01 = make_float2(acc[f][2], acc[f][3]);
+      const float2 k10 = make_float2(acc[f][4], acc[f][5]);
+      const float2 d = make_float2(1.0f + acc[f][6], acc[f][7]);
+      const float inv = 1.0f / fmaf(d.x, d.x, d.y * d.y);
+      const float2 id = make_float2(d.x * inv, -d.y * inv);      // 1 / (1 + k11)
+      const float2 pid = cmul(p, id);
+      const float2 a01 = cmul(make_float2(-pid.x, -pid.y), k10);
+      const float2 a10 = cmul(make_float2(-pid.x, -pid.y), k01);
+      const float2 a11 = cmul(cmul(pid, id), cmul(k01, k10));
+      const float2 b01 = cmul(cconj(a01), gh), b10 = cmul(cconj(a10), gh);
+      const float2 b11 = cmul(cconj(a11), gh);
+      out[0] = make_float4(b00.x, b00.y, b01.x, b01.y);
+      out[1] = make_float4(b10.x, b10.y, b11.x, b11.y);
+    }
+  }
+}
+
+// Per-pole sums R_ab, T, E over a chunk of kBwdChunk frequencies: block
+// (chunk, h), thread = (pole n, frequency subset); partials to the workspace.
+template <bool DIAG>
+__global__ __launch_bounds__(256) void kgen_bwd_pole_kernel(
+    ParamPtrs pp, const float* __restrict__ tanT, const float4* __restrict__ beta,
+    float2* __restrict__ part, int N, int L, int log2npp) {
+  __shared__ float4 sb[2 * kBwdChunk];
+  __shared__ float sG[kBwdChunk];
+  __shared__ float red[256 * 12];
+  const int h = blockIdx.y, lc = blockIdx.x, tid = threadIdx.x;
+  const int l0 = lc * kBwdChunk;
+  const int nl = min(kBwdChunk, L - l0);
+  const float two_dt = 2.0f / pp.dt[h];
+  for (int i = tid; i < nl; i += 256) {
+    sb[2 * i] = beta[2 * ((size_t)h * L + l0 + i)];
+    sb[2 * i + 1] = beta[2 * ((size_t)h * L + l0 + i) + 1];
+    sG[i] = two_dt * tanT[l0 + i];
+  }
+  const int npp = 1 << log2npp, sub_n = 256 >> log2npp;
+  const int n = tid & (npp - 1), sub = tid >> log2npp;
+  float2 lam = make_float2(-1.f, 0.f), cw00 = make_float2(0.f, 0.f), cw01 = cw00, cw10 = cw00,
+         cw11 = cw00;
+  if (n < N) {
+    const size_t idx = (size_t)h * N + n;
+    lam = pp.lam[idx];
+    const float2 b = pp.B[idx], c = pp.C[idx];
+    cw00 = cconj(cmul(c, b));
+    if constexpr (!DIAG) {
+      const float2 pv = pp.P[idx], qv = pp.Q ? pp.Q[idx] : pv;
+      cw01 = cconj(cmul(c, pv));
+      cw10 = cconj(cmul(cconj(qv), b));
+      cw11 = cconj(cmul(cconj(qv), pv));
+    }
+  }
+  __syncthreads();
+  float2 R00 = make_float2(0.f, 0.f), R01 = R00, R10 = R00, R11 = R00, Tn = R00, En = R00;
+  const float nre = -lam.x;
+  for (int i = sub; i < nl; i += sub_n) {
+    const float G = sG[i];
+    const float y = G - lam.y;
+    const float inv = __builtin_amdgcn_rcpf(fmaf(y, y, lam.x * lam.x));
+    const float2 cr = make_float2(nre * inv, y * inv);            // conj(1 / (i G - Lambda))
+    const float4 b0 = sb[2 * i];
+    const float2 b00 = make_float2(b0.x, b0.y);
+    R00 = cadd(R00, cmul(b00, cr));
+    float2 m = cmul(cw00, b00);
+    if constexpr (!DIAG) {
+      const float4 b1 = sb[2 * i + 1];
+      const float2 b01 = make_float2(b0.z, b0.w), b10 = make_float2(b1.x, b1.y),
+                   b11 = make_float2(b1.z, b1.w);
+      R01 = cadd(R01, cmul(b01, cr));
+      R10 = cadd(R10, cmul(b10, cr));
+      R11 = cadd(R11, cmul(b11, cr));
+      m = cadd(m, cadd(cmul(cw01, b01), cadd(cmul(cw10, b10), cmul(cw11, b11))));
+    }
+    const float2 t = cmul(cmul(cr, cr), m);
+    Tn = cadd(Tn, t);
+    En = cadd(En, make_float2(G * t.y, -G * t.x));                // conj(i G) t
+  }
+  float* rv = red + 12 * tid;
+  rv[0] = R00.x; rv[1] = R00.y; rv[2] = R01.x; rv[3] = R01.y; rv[4] = R10.x; rv[5] = R10.y;
+  rv[6] = R11.x; rv[7] = R11.y; rv[8] = Tn.x; rv[9] = Tn.y; rv[10] = En.x; rv[11] = En.y;
+  __syncthreads();
+  if (sub == 0 && n < N) {
+    float s[12];
+#pragma unroll
+    for (int c = 0; c < 12; ++c) s[c] = 0.f;
+    for (int q = 0; q < sub_n; ++q) {
+      const float* o = red + 12 * (q * npp + n);
+#pragma unroll
+      for (int c = 0; c < 12; ++c) s[c] += o[c];
+    }
+    float2* out = part + 6 * (((size_t)h * gridDim.x + lc) * N + n);
+#pragma unroll
+    for (int c = 0; c < 6; ++c) out[c] = make_float2(s[2 * c], s[2 * c + 1]);
+  }
+}
+
+// Per channel: sums the chunk partials, adds the z = -1 terms, writes the
+// parameter gradients.  With Q tied to P, grad(P) includes the Q path.
+template <bool DIAG>
+__global__ __launch_bounds__(256) void kgen_bwd_final_kernel(
+    ParamPtrs pp, const float2* __restrict__ part, const float2* __restrict__ ghat,
+    float2* __restrict__ dlam, float2* __restrict__ dP, float2* __restrict__ dQ,
+    float2* __restrict__ dB, float2* __restrict__ dC, float* __restrict__ ddt, int N, int L,
+    int nchunks) {
+  __shared__ float red[4];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const float dt = pp.dt[h], half = 0.5f * dt;
+  const float2 gn = ghat[(size_t)h * L + L / 2];
+  float dsum = 0.f;
+  for (int n = tid; n < N; n += 256) {
+    const size_t idx = (size_t)h * N + n;
+    float2 s[6];
+#pragma unroll
+    for (int c = 0; c < 6; ++c) s[c] = make_float2(0.f, 0.f);
+    for (int lc = 0; lc < nchunks; ++lc) {
+      const float2* o = part + 6 * (((size_t)h * nchunks + lc) * N + n);
+#pragma unroll
+      for (int c = 0; c < 6; ++c) s[c] = cadd(s[c], o[c]);
+    }
+    const float2 b = pp.B[idx], c = pp.C[idx];
+    float2 gC = cadd(cmul(cconj(b), s[0]), cmul(cconj(make_float2(half * b.x, half * b.y)), gn));
+    float2 gB = cadd(cmul(cconj(c), s[0]), cmul(cconj(make_float2(half * c.x, half * c.y)), gn));
+    if constexpr (!DIAG) {
+      const float2 pv = pp.P[idx], qv = pp.Q ? pp.Q[idx] : pv;
+      gC = cadd(gC, cmul(cconj(pv), s[1]));
+      gB = cadd(gB, cmul(qv, s[2]));
+      float2 gP = cadd(cmul(cconj(c), s[1]), cmul(qv, s[3]));
+      const float2 gQ = cadd(cmul(b, cconj(s[2])), cmul(pv, cconj(s[3])));
+      if (pp.Q) {
+        if (dQ) dQ[idx] = gQ;
+      } else {
+        gP = cadd(gP, gQ);
+      }
+      if (dP) dP[idx] = gP;
+    }
+    if (dC) dC[idx] = gC;
+    if (dB) dB[idx] = gB;
+    if (dlam) dlam[idx] = s[4];
+    // dt: Re(E)/dt, and the z = -1 limit (dt/2) C B
+    dsum += s[5].x / dt + (0.5f * cmul(c, b).x * gn.x + 0.5f * cmul(c, b).y * gn.y);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) dsum += __shfl_xor(dsum, off);
+  if ((tid & 63) == 0) red[tid >> 6] = dsum;
+  __syncthreads();
+  if (tid == 0 && ddt) ddt[h] = red[0] + red[1] + red[2] + red[3];
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (L <= 2^14: every transform fits one workgroup's LDS)
+// ---------------------------------------------------------------------------
+namespace {
+
+template <int LOG2L>
+void corr_launch(const s4dplr_plan* p, const float* u, const float* dy, float* dK, float* dD,
+                 unsigned char* ws, hipStream_t s) {
+  using S = CorrShape<LOG2L>;
+  const int nparts = (p->batch + kCorrRows - 1) / kCorrRows;
+  float2* part = at<float2>(ws, p->off_bpart);
+  const float2* twL = at<const float2>(ws, p->off_twL);
+  const float2* cs = at<const float2>(ws, p->off_cs);
+  corr_spec_kernel<LOG2L><<<dim3(p->H, nparts), S::NT, 0, s>>>(u, dy, part, twL, cs, p->H,
+                                                                p->batch);
+  corr_inv_kernel<LOG2L><<<p->H, S::NT, 0, s>>>(part, dK, dD, twL, cs, p->H, nparts);
+}
+
+template <int LOG2L>
+void ghat_launch(const s4dplr_plan* p, const float* dK, unsigned char* ws, hipStream_t s) {
+  using S = CorrShape<LOG2L>;
+  ghat_kernel<LOG2L><<<p->H, S::NT, 0, s>>>(dK, at<float2>(ws, p->off_bghat),
+                                            at<const float2>(ws, p->off_twL));
+}
+
+#define S4_BWD_DISPATCH(fn, ...)            \
+  switch (p->log2L) {                       \
+    case 1: fn<1>(__VA_ARGS__); break;      \
+    case 2: fn<2>(__VA_ARGS__); break;      \
+    case 3: fn<3>(__VA_ARGS__); break;      \
+    case 4: fn<4>(__VA_ARGS__); break;      \
+    case 5: fn<5>(__VA_ARGS__); break;      \
+    case 6: fn<6>(__VA_ARGS__); break;      \
+    case 7: fn<7>(__VA_ARGS__); break;      \
+    case 8: fn<8>(__VA_ARGS__); break;      \
+    case 9: fn<9>(__VA_ARGS__); break;      \
+    case 10: fn<10>(__VA_ARGS__); break;    \
+    case 11: fn<11>(__VA_ARGS__); break;    \
+    case 12: fn<12>(__VA_ARGS__); break;    \
+    case 13: fn<13>(__VA_ARGS__); break;    \
+    case 14: fn<14>(__VA_ARGS__); break;    \
+    default: return hipErrorInvalidValue;   \
+  }
+
+}  // namespace
+
+hipError_t launch_corr(const s4dplr_plan* p, const float* u, const float* dy, float* dK,
+                       float* dD, unsigned char* ws, hipStream_t s) {
+  S4_BWD_DISPATCH(corr_launch, p, u, dy, dK, dD, ws, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_kernel_gen_bwd(const s4dplr_plan* p, const float* lam, const float* P,
+                                 const float* Q, const float* B, const float* C, const float* dt,
+                                 const float* dK, float* dlam, float* dP, float* dQ, float* dB,
+                                 float* dC, float* ddt, unsigned char* ws, hipStream_t s) {
+  const bool diag = (p->flags & S4DPLR_DIAGONAL) != 0;
+  ParamPtrs pp;
+  pp.lam = reinterpret_cast<const float2*>(lam);
+  pp.P = diag ? nullptr : reinterpret_cast<const float2*>(P);
+  pp.Q = diag ? nullptr : reinterpret_cast<const float2*>(Q);
+  pp.B = reinterpret_cast<const float2*>(B);
+  pp.C = reinterpret_cast<const float2*>(C);
+  pp.dt = dt;
+  S4_BWD_DISPATCH(ghat_launch, p, dK, ws, s);
+  const float* tanT = at<const float>(ws, p->off_tan);
+  const float2* ghat = at<const float2>(ws, p->off_bghat);
+  float4* beta = at<float4>(ws, p->off_bbeta);
+  constexpr int F = 2;
+  const dim3 cgrid((p->L + F * kCauchyThreads - 1) / (F * kCauchyThreads), p->H);
+  if (diag)
+    kgen_bwd_coef_kernel<F, true><<<cgrid, kCauchyThreads, 0, s>>>(pp, tanT, ghat, beta, p->N,
+                                                                   p->NP, p->L);
+  else
+    kgen_bwd_coef_kernel<F, false><<<cgrid, kCauchyThreads, 0, s>>>(pp, tanT, ghat, beta, p->N,
+                                                                    p->NP, p->L);
+  int log2npp = 0;
+  while ((1 << log2npp) < p->N) ++log2npp;
+  const int nchunks = (p->L + kBwdChunk - 1) / kBwdChunk;
+  float2* part = at<float2>(ws, p->off_bpart);
+  const dim3 pgrid(nchunks, p->H);
+  if (diag)
+    kgen_bwd_pole_kernel<true><<<pgrid, 256, 0, s>>>(pp, tanT, beta, part, p->N, p->L, log2npp);
+  else
+    kgen_bwd_pole_kernel<false><<<pgrid, 256, 0, s>>>(pp, tanT, beta, part, p->N, p->L, log2npp);
+  auto c2 = [](float* q) { return reinterpret_cast<float2*>(q); };
+  if (diag)
+    kgen_bwd_final_kernel<true><<<p->H, 256, 0, s>>>(pp, part, ghat, c2(dlam), nullptr, nullptr,
+                                                     c2(dB), c2(dC), ddt, p->N, p->L, nchunks);
+  else
+    kgen_bwd_final_kernel<false><<<p->H, 256, 0, s>>>(pp, part, ghat, c2(dlam), c2(dP), c2(dQ),
+                                                      c2(dB), c2(dC), ddt, p->N, p->L, nchunks);
+  return hipGetLastError();
+}
+
+}  // namespace s4

@@ -160,7 +160,7 @@ template <int LOG2M, bool CONV>
 __global__ __launch_bounds__(kBigThreads) void big_rows_pair_kernel(
     float2* __restrict__ Y, float4* __restrict__ coefp, const float* __restrict__ D,
     const float2* __restrict__ tw2, const float2* __restrict__ cs,
-    const float2* __restrict__ tw4, int batch) {
+    const float2* __restrict__ tw4, int batch, int conj) {
   using S = BigShape<LOG2M>;
   constexpr int M = S::M, M1 = S::M1, M2 = S::M2, RP = S::RP;
   constexpr int TASKS = 8;
@@ -208,6 +208,10 @@ __global__ __launch_bounds__(kBigThreads) void big_rows_pair_kernel(
       float2 sa = big_rfft_x(za, zb, csa), sb = big_rfft_x(zb, za, csb);
       sa.x += Dh;
       sb.x += Dh;
+      if (conj) {   // weights of the correlation with (K + D delta)
+        sa.y = -sa.y;
+        sb.y = -sb.y;
+      }
       {
         const float a = sc * (1.0f - csa.y), b = sc * (1.0f + csa.y), c = sc * csa.x;
         const float2 al = make_float2(fmaf(a, sa.x, b * sb.x), fmaf(a, sa.y, -b * sb.y));
@@ -246,7 +250,7 @@ static T* wat(unsigned char* ws, size_t off) { return reinterpret_cast<T*>(ws + 
 
 template <int LOG2M>
 static void big_spectrum_from_time(const s4dplr_plan* p, const float* Ktime, const float* D,
-                                   unsigned char* ws, hipStream_t s) {
+                                   unsigned char* ws, hipStream_t s, int conj) {
   using S = BigShape<LOG2M>;
   float2* Y = wat<float2>(ws, p->off_big);
   const float2* cs = wat<const float2>(ws, p->off_cs);
@@ -254,12 +258,12 @@ static void big_spectrum_from_time(const s4dplr_plan* p, const float* Ktime, con
   big_cols_fwd_kernel<LOG2M><<<dim3(S::M2 / S::CT, p->H), kBigThreads, 0, s>>>(
       Ktime, Y, wat<const float2>(ws, p->off_tw1), tw4);
   big_rows_pair_kernel<LOG2M, false><<<dim3((S::M1 / 2 + 1 + 7) / 8, p->H), kBigThreads, 0, s>>>(
-      Y, wat<float4>(ws, p->off_coef), D, wat<const float2>(ws, p->off_tw2), cs, tw4, 1);
+      Y, wat<float4>(ws, p->off_coef), D, wat<const float2>(ws, p->off_tw2), cs, tw4, 1, conj);
 }
 
 template <int LOG2M>
 static void big_kspec(const s4dplr_plan* p, const float* Ktime, const float* D, float* Kout,
-                      unsigned char* ws, hipStream_t s) {
+                      unsigned char* ws, hipStream_t s, int conj) {
   using S = BigShape<LOG2M>;
   if (!Ktime) {
     // inverse transform of the generating function (permuted layout) -> K
@@ -272,13 +276,13 @@ static void big_kspec(const s4dplr_plan* p, const float* Ktime, const float* D, 
         Y, K, wat<const float2>(ws, p->off_tw1), 1.0f / (float)S::M);
     Ktime = K;
   }
-  big_spectrum_from_time<LOG2M>(p, Ktime, D, ws, s);
+  big_spectrum_from_time<LOG2M>(p, Ktime, D, ws, s, conj);
 }
 
 hipError_t launch_big_kspec(const s4dplr_plan* p, const float* Ktime, const float* D,
-                            float* Kout, unsigned char* ws, hipStream_t s) {
-  if (p->log2L == 15) big_kspec<15>(p, Ktime, D, Kout, ws, s);
-  else if (p->log2L == 16) big_kspec<16>(p, Ktime, D, Kout, ws, s);
+                            float* Kout, unsigned char* ws, hipStream_t s, int conj) {
+  if (p->log2L == 15) big_kspec<15>(p, Ktime, D, Kout, ws, s, conj);
+  else if (p->log2L == 16) big_kspec<16>(p, Ktime, D, Kout, ws, s, conj);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -345,7 +349,7 @@ static void big_conv(const s4dplr_plan* p, const float* u, float* y, unsigned ch
       u, Y, wat<const float2>(ws, p->off_tw1), tw4, p->H, p->batch);
   big_rows_pair_kernel<LOG2M, true><<<dim3((S::M1 / 2 + 1 + 7) / 8, rows), kBigThreads, 0, s>>>(
       Y, wat<float4>(ws, p->off_coef), nullptr, wat<const float2>(ws, p->off_tw2), cs, tw4,
-      p->batch);
+      p->batch, 0);
   big_conv_cols_inv_kernel<LOG2M><<<dim3(S::M2 / S::CT, rows), kBigThreads, 0, s>>>(
       Y, y, wat<const float2>(ws, p->off_tw1), p->H, p->batch);
 }

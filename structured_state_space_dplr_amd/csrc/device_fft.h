@@ -19,6 +19,15 @@ __device__ __forceinline__ float2 cmul(float2 a, float2 b) {
 __device__ __forceinline__ float2 cmulc(float2 a, float2 b) {
   return make_float2(fmaf(a.x, b.x, a.y * b.y), fmaf(a.y, b.x, -a.x * b.y));
 }
+// The bin X_j of the 2M-point DFT of a real sequence x from the M-point DFT Z
+// of its packing z_k = x_2k + i x_2k+1, given Z_j and Z_{M-j};
+// csj = (cos, sin)(pi j / M).
+__device__ __forceinline__ float2 rfft_x(float2 zj, float2 zmj, float2 csj) {
+  const float2 p = make_float2(0.5f * (1.0f - csj.y), -0.5f * csj.x);
+  const float2 q = make_float2(0.5f * (1.0f + csj.y), 0.5f * csj.x);
+  return cadd(cmul(p, zj), cmul(q, cconj(zmj)));
+}
+
 // Multiply by a stored forward twiddle w (forward) or by conj(w) (inverse).
 template <bool INV>
 __device__ __forceinline__ float2 cmulw(float2 a, float2 w) {

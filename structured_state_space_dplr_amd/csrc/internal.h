@@ -31,11 +31,19 @@ struct s4dplr_plan {
   size_t off_big;    // long path: [batch*H][L] float2 intermediate rows
   size_t off_rrec;   // recurrent view: [H][N] x 4 float4 per-pole step records
   size_t off_rchan;  // recurrent view: [H] float4 per-channel sums (S1, S2)
+  // Backward pass (L <= 2^S4DPLR_LDS_MAX_LOG2L only):
+  size_t off_bghat;  // [H][L] float2: FFT_L(dK) / L
+  size_t off_bbeta;  // [H][L] x 2 float4: conj(dKhat/dk_ab) * Ghat per frequency
+  size_t off_bpart;  // partial sums: correlation spectra [ceil(B/kCorrRows)][H][L+1] float2,
+                     // or per-pole sums [H][ceil(L/kBwdChunk)][N] x 6 float2
   size_t total;
   std::vector<unsigned char> tables;  // exact bytes of the table region
 };
 
 namespace s4 {
+
+constexpr int kCorrRows = 4;     // batch rows per block of the dK correlation
+constexpr int kBwdChunk = 256;   // frequencies per block of the per-pole backward sums
 
 bool lds_path(const s4dplr_plan* p);
 
@@ -45,14 +53,15 @@ bool lds_path(const s4dplr_plan* p);
 hipError_t launch_kernel_gen(const s4dplr_plan* p, const float* lam, const float* P,
                              const float* Q, const float* B, const float* C, const float* dt,
                              const float* D, float* Kout, unsigned char* ws, hipStream_t s);
-// The convolution weights from a given time-domain kernel.
+// The convolution weights from a given time-domain kernel; with conj set, the
+// weights of the correlation with (K + D delta) instead (the input gradient).
 hipError_t launch_spectrum_from_time(const s4dplr_plan* p, const float* Ktime, const float* D,
-                                     unsigned char* ws, hipStream_t s);
+                                     unsigned char* ws, hipStream_t s, int conj);
 hipError_t launch_conv(const s4dplr_plan* p, const float* u, float* y, unsigned char* ws,
                        hipStream_t s);
 // Long sequences (log2 L = 15, 16): four-step transforms through the workspace.
 hipError_t launch_big_kspec(const s4dplr_plan* p, const float* Ktime, const float* D,
-                            float* Kout, unsigned char* ws, hipStream_t s);
+                            float* Kout, unsigned char* ws, hipStream_t s, int conj);
 hipError_t launch_big_conv(const s4dplr_plan* p, const float* u, float* y, unsigned char* ws,
                            hipStream_t s);
 
@@ -64,6 +73,15 @@ hipError_t launch_recurrent_prepare(const s4dplr_plan* p, const float* lam, cons
 hipError_t launch_recurrent_scan(const s4dplr_plan* p, const float* D, const float* u,
                                  float* state, float* y, int T, unsigned char* ws,
                                  hipStream_t s);
+// Backward pass.  dK (may be null) and dD (may be null) of the convolution:
+// the batch sum of the correlation of dy with u.
+hipError_t launch_corr(const s4dplr_plan* p, const float* u, const float* dy, float* dK,
+                       float* dD, unsigned char* ws, hipStream_t s);
+// Parameter gradients of kernel generation from dK (each output may be null).
+hipError_t launch_kernel_gen_bwd(const s4dplr_plan* p, const float* lam, const float* P,
+                                 const float* Q, const float* B, const float* C, const float* dt,
+                                 const float* dK, float* dlam, float* dP, float* dQ, float* dB,
+                                 float* dC, float* ddt, unsigned char* ws, hipStream_t s);
 // Work split of the scan: poles per lane (1, 2, 4 or 8) and log2 of the lanes
 // per sequence (0..5), chosen from N and the number of sequences.
 void recurrent_shape(int N, long rows, int* ppl, int* log2g);

@@ -31,147 +31,15 @@
 // L/2 points forward and two back, joined only at the ends.
 #include <hip/hip_runtime.h>
 
+#include "cauchy.h"
 #include "device_fft.h"
 #include "internal.h"
 
 namespace s4 {
 
-// ---------------------------------------------------------------------------
-// Stage 1a/1b: pole records and the Cauchy sums at the L roots of unity
-// ---------------------------------------------------------------------------
-// A block first writes its channel's pole records into LDS (5 float4 each):
-//   rec[5n]   = (Im Lambda_n, (Re Lambda_n)^2, K00),  rec[5n+1] = (w00, K01),
-//   rec[5n+2] = (w01, K10),  rec[5n+3] = (w10, K11),  rec[5n+4] = (w11, 0)
-// with w00 = C B, w01 = C P, w10 = conj(Q) B, w11 = conj(Q) P and
-// K_ab = -Re(Lambda_n) w_ab (both parts).  Poles n in [N, NP) (NP = N rounded
-// up to kPoleUnroll) are inert: zero weights, Lambda = -1.  Per term, with
-// y = G - Im Lambda and r = 1 / ((Re Lambda)^2 + y^2),
-//   w_ab / (i G - Lambda) = r (K_ab.re + w_ab.im y) + i r (K_ab.im - w_ab.re y),
-// i.e. two FMAs for the numerator and two for the accumulation per sum.
-constexpr int kPoleUnroll = 4;
-constexpr int kMaxPoles = 256;
-
-struct ParamPtrs {
-  const float2* lam;
-  const float2* P;
-  const float2* Q;   // nullptr: Q = P
-  const float2* B;
-  const float2* C;
-  const float* dt;
-};
-
-constexpr int kRec = 5;   // float4 per pole record
-
-// Builds the records of channel h with threads [0, nthr); returns this
-// thread's partial sum of w00 = C B over its poles.
-__device__ __forceinline__ float2 build_pole_records(const ParamPtrs& pp, int h, int N, int NP,
-                                                     bool diag, float4* __restrict__ rec, int tid,
-                                                     int nthr) {
-  float2 s = make_float2(0.f, 0.f);
-  for (int n = tid; n < NP; n += nthr) {
-    float4* rn = rec + kRec * n;
-    if (n < N) {
-      const size_t idx = (size_t)h * N + n;
-      const float2 l = pp.lam[idx], b = pp.B[idx], c = pp.C[idx];
-      const float2 pv = diag ? make_float2(0.f, 0.f) : pp.P[idx];
-      const float2 qv = diag ? make_float2(0.f, 0.f) : (pp.Q ? pp.Q[idx] : pv);
-      const float2 w00 = cmul(c, b), w01 = cmul(c, pv);
-      const float2 w10 = cmul(cconj(qv), b), w11 = cmul(cconj(qv), pv);
-      const float na = -l.x;
-      rn[0] = make_float4(l.y, l.x * l.x, na * w00.x, na * w00.y);
-      rn[1] = make_float4(w00.x, w00.y, na * w01.x, na * w01.y);
-      rn[2] = make_float4(w01.x, w01.y, na * w10.x, na * w10.y);
-      rn[3] = make_float4(w10.x, w10.y, na * w11.x, na * w11.y);
-      rn[4] = make_float4(w11.x, w11.y, 0.f, 0.f);
-      s = cadd(s, w00);
-    } else {
-      rn[0] = make_float4(0.f, 1.f, 0.f, 0.f);
-      rn[1] = make_float4(0.f, 0.f, 0.f, 0.f);
-      rn[2] = make_float4(0.f, 0.f, 0.f, 0.f);
-      rn[3] = make_float4(0.f, 0.f, 0.f, 0.f);
-      rn[4] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  }
-  return s;
-}
-
-// Sum of a float2 over the block (blockDim a multiple of 64); ends with a
-// barrier, so LDS written before the call is visible to all threads after it.
-template <int NTHR>
-__device__ __forceinline__ float2 block_sum2(float2 v, float2* __restrict__ red, int tid) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    v.x += __shfl_xor(v.x, off);
-    v.y += __shfl_xor(v.y, off);
-  }
-  if ((tid & 63) == 0) red[tid >> 6] = v;
-  __syncthreads();
-  float2 s = make_float2(0.f, 0.f);
-#pragma unroll
-  for (int w = 0; w < NTHR / 64; ++w) s = cadd(s, red[w]);
-  return s;
-}
-
-// acc[f][0..7] += the four Cauchy sums (re, im) at G[f], over poles [0, NP).
-template <int F, bool DIAG>
-__device__ __forceinline__ void cauchy_sums(const float4* __restrict__ rec, int NP,
-                                            const float (&G)[F], float (&acc)[F][8]) {
-  for (int n0 = 0; n0 < NP; n0 += kPoleUnroll) {
-#pragma unroll
-    for (int n = n0; n < n0 + kPoleUnroll; ++n) {
-      const float4* rn = rec + kRec * n;
-      const float4 p0 = rn[0], p1 = rn[1];
-      float4 p2 = make_float4(0.f, 0.f, 0.f, 0.f), p3 = p2, p4 = p2;
-      if constexpr (!DIAG) {
-        p2 = rn[2];
-        p3 = rn[3];
-        p4 = rn[4];
-      }
-#pragma unroll
-      for (int f = 0; f < F; ++f) {
-        const float yv = G[f] - p0.x;
-        const float r = __builtin_amdgcn_rcpf(fmaf(yv, yv, p0.y));
-        // sum 00: w = p1.xy, K = p0.zw
-        acc[f][0] = fmaf(r, fmaf(p1.y, yv, p0.z), acc[f][0]);
-        acc[f][1] = fmaf(r, fmaf(-p1.x, yv, p0.w), acc[f][1]);
-        if constexpr (!DIAG) {
-          // sum 01: w = p2.xy, K = p1.zw; sum 10: w = p3.xy, K = p2.zw; sum 11: w = p4.xy, K = p3.zw
-          acc[f][2] = fmaf(r, fmaf(p2.y, yv, p1.z), acc[f][2]);
-          acc[f][3] = fmaf(r, fmaf(-p2.x, yv, p1.w), acc[f][3]);
-          acc[f][4] = fmaf(r, fmaf(p3.y, yv, p2.z), acc[f][4]);
-          acc[f][5] = fmaf(r, fmaf(-p3.x, yv, p2.w), acc[f][5]);
-          acc[f][6] = fmaf(r, fmaf(p4.y, yv, p3.z), acc[f][6]);
-          acc[f][7] = fmaf(r, fmaf(-p4.x, yv, p3.w), acc[f][7]);
-        }
-      }
-    }
-  }
-}
-
-// Woodbury correction and the 2/(1+z) = 1 + i tan(theta/2) factor; at z = -1
-// (the frequency l = L/2) the limit `nyq` = (dt/2) sum_n C_n B_n.
-template <bool DIAG>
-__device__ __forceinline__ float2 cauchy_epilogue(const float (&a)[8], float T, bool at_nyquist,
-                                                  float2 nyq) {
-  float2 kv = make_float2(a[0], a[1]);
-  if constexpr (!DIAG) {
-    // k00 - k01 k10 / (1 + k11)
-    const float2 k01 = make_float2(a[2], a[3]);
-    const float2 k10 = make_float2(a[4], a[5]);
-    const float2 den = make_float2(1.0f + a[6], a[7]);
-    const float2 num = cmul(k01, k10);
-    const float inv = 1.0f / fmaf(den.x, den.x, den.y * den.y);
-    const float2 t = cmulc(num, den);
-    kv = make_float2(fmaf(-t.x, inv, kv.x), fmaf(-t.y, inv, kv.y));
-  }
-  const float2 kh = cmul(make_float2(1.0f, T), kv);
-  return at_nyquist ? nyq : kh;
-}
-
 // General kernel generation step: F frequencies per thread, 256 threads, one
 // channel per blockIdx.y.  perm_m1 > 0 stores the long path's transposed
 // layout: position p = k1*256 + k2 holds frequency l = k1 + perm_m1*k2.
-constexpr int kCauchyThreads = 256;
 
 template <int F, bool DIAG>
 __global__ __launch_bounds__(kCauchyThreads) void cauchy_kernel(
@@ -221,25 +89,26 @@ struct KgenShape {
   static_assert(LOG2L >= 5 && LOG2L <= 10, "fused range");
 };
 
-// the real-FFT bin X_j from (Z_j, Z_{M-j}); csj = (cos, sin)(pi j / M)
-__device__ __forceinline__ float2 rfft_x(float2 zj, float2 zmj, float2 csj) {
-  const float2 p = make_float2(0.5f * (1.0f - csj.y), -0.5f * csj.x);
-  const float2 q = make_float2(0.5f * (1.0f + csj.y), 0.5f * csj.x);
-  return cadd(cmul(p, zj), cmul(q, cconj(zmj)));
-}
 
 // Convolution weights of the bin pair (j, L-j), j in [0, L/2], from the
 // spectrum Z (natural order, padded, in LDS) of the packed zero-padded kernel:
 //   S_j = X_j + D,  alpha_j = ((1 - s_j) S_j + (1 + s_j) conj(S_{L-j})) / (2L),
 //   beta_j = i c_j (S_j - conj(S_{L-j})) / (2L),   (c_j, s_j) = (cos, sin)(pi j / L).
+// With conj set, S_j is replaced by conj(S_j): the weights of the correlation
+// with (K + D delta), sum_j K_j x_{t+j} + D x_t, instead of the convolution.
 __device__ __forceinline__ void weights_pair(const float2* __restrict__ Zb, float4* __restrict__ cf,
-                                             float2 csj, float2 csm, int L, int j, float Dh) {
+                                             float2 csj, float2 csm, int L, int j, float Dh,
+                                             int conj) {
   const float sc = 0.5f / (float)L;
   const int jm = L - j;
   const float2 zj = Zb[lds_pad(j)], zm = Zb[lds_pad(jm & (L - 1))];
   float2 sj = rfft_x(zj, zm, csj), sm = rfft_x(zm, zj, csm);
   sj.x += Dh;
   sm.x += Dh;
+  if (conj) {
+    sj.y = -sj.y;
+    sm.y = -sm.y;
+  }
   {
     const float a = sc * (1.0f - csj.y), b = sc * (1.0f + csj.y), c = sc * csj.x;
     const float2 al = make_float2(fmaf(a, sj.x, b * sm.x), fmaf(a, sj.y, -b * sm.y));
@@ -258,7 +127,7 @@ template <int LOG2L, bool DIAG, bool FROM_TIME>
 __global__ __launch_bounds__(KgenShape<LOG2L>::NTHR) void kgen_wave_kernel(
     ParamPtrs pp, const float* __restrict__ D, const float* __restrict__ Kin,
     float* __restrict__ Kout, float4* __restrict__ coef, const float* __restrict__ tanT,
-    const float2* __restrict__ tw, const float2* __restrict__ cs, int N, int NP) {
+    const float2* __restrict__ tw, const float2* __restrict__ cs, int N, int NP, int conj) {
   using S = KgenShape<LOG2L>;
   constexpr int L = S::L, T = S::T, NTHR = S::NTHR, P = S::P;
   __shared__ float4 rec[FROM_TIME ? 1 : kRec * kMaxPoles];
@@ -369,7 +238,7 @@ __global__ __launch_bounds__(KgenShape<LOG2L>::NTHR) void kgen_wave_kernel(
 #pragma unroll
   for (int i = 0; i < NW; ++i) {
     const int j = tid + i * NTHR;
-    if (j <= L / 2) weights_pair(buf, coef + (size_t)h * L, csj[i], csm[i], L, j, Dh);
+    if (j <= L / 2) weights_pair(buf, coef + (size_t)h * L, csj[i], csm[i], L, j, Dh, conj);
   }
 }
 
@@ -395,7 +264,7 @@ template <int LOG2L, bool FROM_TIME>
 __global__ __launch_bounds__(KspecShape<LOG2L>::NT) void kspec_kernel(
     const float2* __restrict__ khat, const float* __restrict__ Kin, const float* __restrict__ D,
     float* __restrict__ Kout, float4* __restrict__ coef, const float2* __restrict__ twL,
-    const float2* __restrict__ twH, const float2* __restrict__ cs) {
+    const float2* __restrict__ twH, const float2* __restrict__ cs, int conj) {
   using S = KspecShape<LOG2L>;
   constexpr int L = S::L, H2 = S::H2, NT = S::NT;
   __shared__ float2 buf[S::BUF];
@@ -453,6 +322,10 @@ __global__ __launch_bounds__(KspecShape<LOG2L>::NT) void kspec_kernel(
     float2 sj = rfft_x(zj, zm, csj), sm = rfft_x(zm, zj, csm);
     sj.x += Dh;
     sm.x += Dh;
+    if (conj) {   // correlation instead of convolution (see weights_pair)
+      sj.y = -sj.y;
+      sm.y = -sm.y;
+    }
     {
       const float a = sc * (1.0f - csj.y), b = sc * (1.0f + csj.y), c = sc * csj.x;
       const float2 al = make_float2(fmaf(a, sj.x, b * sm.x), fmaf(a, sj.y, -b * sm.y));
@@ -860,7 +733,8 @@ static bool fused_path(const s4dplr_plan* p) { return p->log2L >= 5 && p->log2L 
 
 template <int LOG2L>
 static void kgen_launch(const s4dplr_plan* p, const ParamPtrs& pp, const float* D,
-                        const float* Ktime, float* Kout, unsigned char* ws, hipStream_t s) {
+                        const float* Ktime, float* Kout, unsigned char* ws, hipStream_t s,
+                        int conj) {
   if constexpr (LOG2L >= 5 && LOG2L <= 10) {
     using S = KgenShape<LOG2L>;
     float4* coef = at<float4>(ws, p->off_coef);
@@ -869,13 +743,13 @@ static void kgen_launch(const s4dplr_plan* p, const ParamPtrs& pp, const float* 
     const float2* cs = at<const float2>(ws, p->off_cs);
     if (Ktime)
       kgen_wave_kernel<LOG2L, false, true><<<p->H, S::NTHR, 0, s>>>(pp, D, Ktime, nullptr, coef,
-                                                                  tanT, tw, cs, p->N, p->NP);
+                                                                  tanT, tw, cs, p->N, p->NP, conj);
     else if (p->flags & S4DPLR_DIAGONAL)
       kgen_wave_kernel<LOG2L, true, false><<<p->H, S::NTHR, 0, s>>>(pp, D, nullptr, Kout, coef,
-                                                                  tanT, tw, cs, p->N, p->NP);
+                                                                  tanT, tw, cs, p->N, p->NP, 0);
     else
       kgen_wave_kernel<LOG2L, false, false><<<p->H, S::NTHR, 0, s>>>(pp, D, nullptr, Kout, coef,
-                                                                   tanT, tw, cs, p->N, p->NP);
+                                                                   tanT, tw, cs, p->N, p->NP, 0);
   }
 }
 
@@ -898,7 +772,7 @@ hipError_t launch_cauchy(const s4dplr_plan* p, const ParamPtrs& pp, unsigned cha
 
 template <int LOG2L>
 static void kspec_launch(const s4dplr_plan* p, const float* Ktime, const float* D, float* Kout,
-                         unsigned char* ws, hipStream_t s) {
+                         unsigned char* ws, hipStream_t s, int conj) {
   using S = KspecShape<LOG2L>;
   const float2* khat = at<const float2>(ws, p->off_khat);
   float4* coef = at<float4>(ws, p->off_coef);
@@ -906,9 +780,11 @@ static void kspec_launch(const s4dplr_plan* p, const float* Ktime, const float* 
   const float2* twH = at<const float2>(ws, p->off_twH);
   const float2* cs = at<const float2>(ws, p->off_cs);
   if (Ktime)
-    kspec_kernel<LOG2L, true><<<p->H, S::NT, 0, s>>>(khat, Ktime, D, Kout, coef, twL, twH, cs);
+    kspec_kernel<LOG2L, true><<<p->H, S::NT, 0, s>>>(khat, Ktime, D, Kout, coef, twL, twH, cs,
+                                                     conj);
   else
-    kspec_kernel<LOG2L, false><<<p->H, S::NT, 0, s>>>(khat, Ktime, D, Kout, coef, twL, twH, cs);
+    kspec_kernel<LOG2L, false><<<p->H, S::NT, 0, s>>>(khat, Ktime, D, Kout, coef, twL, twH, cs,
+                                                      conj);
 }
 
 template <int LOG2L>
@@ -971,9 +847,9 @@ static void conv_launch(const s4dplr_plan* p, const float* u, float* y, unsigned
   }
 
 static hipError_t launch_kspec(const s4dplr_plan* p, const float* Ktime, const float* D,
-                               float* Kout, unsigned char* ws, hipStream_t s) {
-  if (!lds_path(p)) return launch_big_kspec(p, Ktime, D, Kout, ws, s);
-  S4_DISPATCH_LOG2L(kspec_launch, p, Ktime, D, Kout, ws, s);
+                               float* Kout, unsigned char* ws, hipStream_t s, int conj) {
+  if (!lds_path(p)) return launch_big_kspec(p, Ktime, D, Kout, ws, s, conj);
+  S4_DISPATCH_LOG2L(kspec_launch, p, Ktime, D, Kout, ws, s, conj);
   return hipGetLastError();
 }
 
@@ -982,22 +858,22 @@ hipError_t launch_kernel_gen(const s4dplr_plan* p, const float* lam, const float
                              const float* D, float* Kout, unsigned char* ws, hipStream_t s) {
   const ParamPtrs pp = param_ptrs(lam, P, Q, B, C, dt);
   if (fused_path(p)) {
-    S4_DISPATCH_LOG2L(kgen_launch, p, pp, D, nullptr, Kout, ws, s);
+    S4_DISPATCH_LOG2L(kgen_launch, p, pp, D, nullptr, Kout, ws, s, 0);
     return hipGetLastError();
   }
   hipError_t e = launch_cauchy(p, pp, ws, s);
   if (e != hipSuccess) return e;
-  return launch_kspec(p, nullptr, D, Kout, ws, s);
+  return launch_kspec(p, nullptr, D, Kout, ws, s, 0);
 }
 
 hipError_t launch_spectrum_from_time(const s4dplr_plan* p, const float* Ktime, const float* D,
-                                     unsigned char* ws, hipStream_t s) {
+                                     unsigned char* ws, hipStream_t s, int conj) {
   if (fused_path(p)) {
     const ParamPtrs pp{};
-    S4_DISPATCH_LOG2L(kgen_launch, p, pp, D, Ktime, nullptr, ws, s);
+    S4_DISPATCH_LOG2L(kgen_launch, p, pp, D, Ktime, nullptr, ws, s, conj);
     return hipGetLastError();
   }
-  return launch_kspec(p, Ktime, D, nullptr, ws, s);
+  return launch_kspec(p, Ktime, D, nullptr, ws, s, conj);
 }
 
 hipError_t launch_conv(const s4dplr_plan* p, const float* u, float* y, unsigned char* ws,

@@ -46,6 +46,17 @@ int main() {
         CHECK(s4dplr_forward(p, f, f, nullptr, f, f, f, nullptr, u, nullptr, y, ws, nullptr) == S4DPLR_OK);
         CHECK(s4dplr_conv_apply(p, u, y, ws, nullptr) == S4DPLR_OK);
         CHECK(s4dplr_recurrent_prepare(p, f, f, nullptr, f, f, f, ws, nullptr) == S4DPLR_OK);
+        {
+          float* g = reinterpret_cast<float*>(base + 4 * gap);
+          float* o = reinterpret_cast<float*>(base + 5 * gap);
+          const s4dplr_status want = L <= 16384 ? S4DPLR_OK : S4DPLR_ERR_UNSUPPORTED;
+          CHECK(s4dplr_conv_bwd(p, u, K, nullptr, g, y, o, nullptr, ws, nullptr) == want);
+          float* outs = reinterpret_cast<float*>(base + 6 * gap);
+          const size_t cb = 2 * 3 * (size_t)N;   // floats of one [H][N] complex output
+          CHECK(s4dplr_kernel_gen_bwd(p, f, f, nullptr, f, f, f, K, outs, outs + cb, nullptr,
+                                      outs + 2 * cb, outs + 3 * cb, outs + 4 * cb, ws,
+                                      nullptr) == want);
+        }
         CHECK(s4dplr_recurrent_scan(p, nullptr, u, 7, K, y, ws, nullptr) == S4DPLR_OK);
         CHECK(s4dplr_recurrent_scan(p, nullptr, u, 7, K, u, ws, nullptr) == S4DPLR_ERR_ALIAS);
         CHECK(stub_launch_count() > before);

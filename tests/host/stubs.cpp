@@ -27,11 +27,23 @@ hipError_t launch_kernel_gen(const s4dplr_plan*, const float*, const float*, con
   return hipSuccess;
 }
 hipError_t launch_spectrum_from_time(const s4dplr_plan*, const float*, const float*,
-                                     unsigned char*, hipStream_t) {
+                                     unsigned char*, hipStream_t, int) {
   ++g_launches;
   return hipSuccess;
 }
 hipError_t launch_conv(const s4dplr_plan*, const float*, float*, unsigned char*, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
+hipError_t launch_corr(const s4dplr_plan*, const float*, const float*, float*, float*,
+                       unsigned char*, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
+hipError_t launch_kernel_gen_bwd(const s4dplr_plan*, const float*, const float*, const float*,
+                                 const float*, const float*, const float*, const float*, float*,
+                                 float*, float*, float*, float*, float*, unsigned char*,
+                                 hipStream_t) {
   ++g_launches;
   return hipSuccess;
 }

@@ -33,6 +33,8 @@ def lib():
     L.s4dplr_conv_apply.argtypes = [vp] * 5
     L.s4dplr_recurrent_prepare.argtypes = [vp] * 9
     L.s4dplr_recurrent_scan.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp]
+    L.s4dplr_conv_bwd.argtypes = [vp] * 10
+    L.s4dplr_kernel_gen_bwd.argtypes = [vp] * 16
     L.s4dplr_plan_destroy.argtypes = [vp]
     L.s4dplr_status_string.restype = ctypes.c_char_p
     return L
@@ -50,7 +52,7 @@ def test_header_declares_the_boundary():
               "s4dplr_plan_workspace_bytes", "s4dplr_plan_init", "s4dplr_kernel_gen",
               "s4dplr_conv_fwd", "s4dplr_forward", "s4dplr_plan_destroy",
               "s4dplr_last_hip_error", "s4dplr_conv_apply", "s4dplr_recurrent_prepare",
-              "s4dplr_recurrent_scan"]:
+              "s4dplr_recurrent_scan", "s4dplr_conv_bwd", "s4dplr_kernel_gen_bwd"]:
         assert n in names
 
 
@@ -218,3 +220,45 @@ def test_recurrent_validation(lib):
     assert lib.s4dplr_recurrent_scan(h, None, u, T, ws + 256, y, ws, None) == ERR_ALIAS
     assert lib.s4dplr_recurrent_scan(h, None, u, T, state, ws + 256, ws, None) == ERR_ALIAS
     lib.s4dplr_plan_destroy(h)
+
+
+def test_backward_validation(lib):
+    H, N, L, B = 4, 16, 256, 2
+    st, h = _create(lib, H, N, L, B)
+    ws = 1 << 32
+    u = 1 << 24
+    ub, kb = 4 * B * H * L, 4 * H * L
+    dy, K, du, dK, dD = u + ub, u + 2 * ub, u + 3 * ub, u + 4 * ub, u + 4 * ub + kb
+    # conv_bwd: dy always; K for du; u for dK / dD
+    assert lib.s4dplr_conv_bwd(h, u, K, None, None, du, dK, dD, ws, None) == ERR_NULL
+    assert lib.s4dplr_conv_bwd(h, u, None, None, dy, du, None, None, ws, None) == ERR_NULL
+    assert lib.s4dplr_conv_bwd(h, None, K, None, dy, None, dK, None, ws, None) == ERR_NULL
+    assert lib.s4dplr_conv_bwd(h, None, K, None, dy, None, None, dD, ws, None) == ERR_NULL
+    assert lib.s4dplr_conv_bwd(h, u, K, None, dy, du, dK, dD, ws + 4, None) == ERR_WORKSPACE
+    # outputs over inputs, over each other, inside the workspace
+    assert lib.s4dplr_conv_bwd(h, u, K, None, dy, dy + 4, None, None, ws, None) == ERR_ALIAS
+    assert lib.s4dplr_conv_bwd(h, u, K, None, dy, du, u, None, ws, None) == ERR_ALIAS
+    assert lib.s4dplr_conv_bwd(h, u, K, None, dy, du, du + 8, None, ws, None) == ERR_ALIAS
+    assert lib.s4dplr_conv_bwd(h, u, K, None, dy, None, dK, dK + 4, ws, None) == ERR_ALIAS
+    assert lib.s4dplr_conv_bwd(h, u, K, None, dy, ws + 512, None, None, ws, None) == ERR_ALIAS
+    # kernel_gen_bwd: parameters and dK required; outputs disjoint from inputs and each other
+    f = 1 << 20
+    cb = 8 * H * N
+    prm = [f, f + cb, None, f + 2 * cb, f + 3 * cb, f + 4 * cb]      # lambda P Q B C dt
+    dKi = f + 5 * cb
+    o0 = 1 << 28
+    outs = [o0, o0 + cb, None, o0 + 2 * cb, o0 + 3 * cb, o0 + 4 * cb]  # dlam dP dQ dB dC ddt
+    assert lib.s4dplr_kernel_gen_bwd(h, *prm, None, *outs, ws, None) == ERR_NULL
+    bad = list(prm)
+    bad[0] = None
+    assert lib.s4dplr_kernel_gen_bwd(h, *bad, dKi, *outs, ws, None) == ERR_NULL
+    for i, target in [(0, f), (3, dKi), (1, o0 + 8), (5, ws + 1024)]:
+        o = list(outs)
+        o[i] = target
+        assert lib.s4dplr_kernel_gen_bwd(h, *prm, dKi, *o, ws, None) == ERR_ALIAS, i
+    lib.s4dplr_plan_destroy(h)
+    # the backward pass is limited to L <= 16384
+    st, h2 = _create(lib, 1, 4, 32768, 1)
+    assert lib.s4dplr_conv_bwd(h2, u, K, None, dy, du, None, None, ws, None) == ERR_UNSUPPORTED
+    assert lib.s4dplr_kernel_gen_bwd(h2, *prm, dKi, *outs, ws, None) == ERR_UNSUPPORTED
+    lib.s4dplr_plan_destroy(h2)
