@@ -51,6 +51,7 @@ __all__ = [
     "kernel_cauchy", "conv_direct", "conv_direct_at", "conv_fft",
     "recurrence", "forward", "recurrent_forward",
     "conv_backward_direct", "conv_backward_fft", "kernel_backward_dense",
+    "kernel_vandermonde_zoh",
 ]
 
 
@@ -176,6 +177,21 @@ def kernel_aliased_dense(Abar, Bbar, C, L):
     return kernel_truncated(Abar, x0, C, L)
 
 
+def kernel_vandermonde_zoh(lam, B, C, dt, L):
+    """Kernel of a diagonal system ([wiki] "S4D": A = diag(a_n)) discretized by
+    zero-order hold ([scratch] section 3: A-bar_n = exp(dt a_n); B-bar_n from
+    ``discretize_zoh_scalar``), as the Vandermonde product of its definition
+    K_k = Re(sum_n C_n B-bar_n A-bar_n^k), k = 0 .. L-1 ([scratch] section 4,
+    the powers written out).  This is the kernel itself, not an aliased one."""
+    lam = np.asarray(lam, np.complex128)
+    disc = [discretize_zoh_scalar(a, b, dt) for a, b in zip(lam, np.asarray(B, np.complex128))]
+    Abar = np.array([d[0] for d in disc], dtype=np.complex128)
+    Bbar = np.array([d[1] for d in disc], dtype=np.complex128)
+    k = np.arange(L)
+    V = Abar[None, :] ** k[:, None]                     # Vandermonde matrix [L][N]
+    return (V @ (np.asarray(C, np.complex128) * Bbar)).real
+
+
 # ---------------------------------------------------------------------------
 # Convolution kernel: the pages' method   ([scratch] section 4)
 # ---------------------------------------------------------------------------
@@ -295,7 +311,7 @@ def _as_complex(a):
     return a[..., 0] + 1j * a[..., 1]
 
 
-def forward(lam, P, Q, B, C, dt, D, u, method="cauchy", diagonal=False):
+def forward(lam, P, Q, B, C, dt, D, u, method="cauchy", diagonal=False, disc="bilinear"):
     """K [H, L] and y [batch, H, L] for H independent channels
     ([scratch] section 1: one SSM per feature channel).
 
@@ -303,7 +319,20 @@ def forward(lam, P, Q, B, C, dt, D, u, method="cauchy", diagonal=False):
     (batch, H, L).  ``method`` selects the kernel: "cauchy" (the pages'
     generating-function method) or "dense" (the aliased plain definition).
     ``diagonal`` drops the low-rank term (S4D, [wiki] "S4D": P = Q = 0).
+    ``disc="zoh"`` (diagonal only) uses the zero-order-hold Vandermonde kernel
+    of ``kernel_vandermonde_zoh`` instead.
     """
+    if disc == "zoh":
+        if not diagonal:
+            raise ValueError("zero-order hold is defined here for diagonal systems only")
+        lam_c, B_c, C_c = _as_complex(lam), _as_complex(B), _as_complex(C)
+        dts = np.asarray(dt, np.float64)
+        u = np.asarray(u, np.float64)
+        L = u.shape[-1]
+        K = np.stack([kernel_vandermonde_zoh(lam_c[h], B_c[h], C_c[h], dts[h], L)
+                      for h in range(lam_c.shape[0])])
+        Dv = np.zeros(lam_c.shape[0]) if D is None else np.asarray(D, np.float64)
+        return K, conv_fft(u, K[None, :, :], Dv[None, :, None])
     lam_c = _as_complex(lam)
     H, N = lam_c.shape
     u = np.asarray(u, np.float64)
@@ -332,7 +361,7 @@ def forward(lam, P, Q, B, C, dt, D, u, method="cauchy", diagonal=False):
     return K, y
 
 
-def recurrent_forward(lam, P, Q, B, C, dt, D, u, x0=None, diagonal=False):
+def recurrent_forward(lam, P, Q, B, C, dt, D, u, x0=None, diagonal=False, disc="bilinear"):
     """The recurrent view over channels and batch: y [batch, H, T] and the
     final state [batch, H, N] (complex), from the dense bilinear A-bar, B-bar
     of A = Lambda - P Q^* ([scratch] sections 3 and 5; [wiki] "Structured
@@ -354,8 +383,15 @@ def recurrent_forward(lam, P, Q, B, C, dt, D, u, x0=None, diagonal=False):
     y = np.empty(u.shape, dtype=np.float64)
     xT = np.empty((u.shape[0], H, N), dtype=np.complex128)
     for h in range(H):
-        A = dense_state_matrix(lam_c[h], P_c[h], Q_c[h])
-        Abar, Bbar = discretize_bilinear(A, B_c[h], dt[h])
+        if disc == "zoh":
+            if not diagonal:
+                raise ValueError("zero-order hold is defined here for diagonal systems only")
+            d = [discretize_zoh_scalar(a, b, dt[h]) for a, b in zip(lam_c[h], B_c[h])]
+            Abar = np.diag([e[0] for e in d]).astype(np.complex128)
+            Bbar = np.array([e[1] for e in d], dtype=np.complex128)
+        else:
+            A = dense_state_matrix(lam_c[h], P_c[h], Q_c[h])
+            Abar, Bbar = discretize_bilinear(A, B_c[h], dt[h])
         y[:, h], xT[:, h] = recurrence(Abar, Bbar, C_c[h], D[h], u[:, h],
                                        None if x0 is None else x0[:, h], return_state=True)
     return y, xT
@@ -408,7 +444,7 @@ def conv_backward_fft(u, K, D, dy):
     return du, dK, dD
 
 
-def kernel_backward_dense(lam, P, Q, B, C, dt, dK, diagonal=False):
+def kernel_backward_dense(lam, P, Q, B, C, dt, dK, diagonal=False, disc="bilinear"):
     """Gradients of loss = sum_{h,k} dK[h,k] K[h,k] with respect to the
     kernel's parameters, where K is the plain aliased definition
     K_k = Re(C A-bar^k (I - A-bar^L)^{-1} B-bar) of the dense bilinear system
@@ -436,6 +472,15 @@ def kernel_backward_dense(lam, P, Q, B, C, dt, dK, diagonal=False):
     loss = torch.zeros((), dtype=torch.float64)
     for h in range(H):
         lam_c, B_c, C_c = cx(lam_t[h]), cx(B_t[h]), cx(C_t[h])
+        if disc == "zoh":
+            # the Vandermonde definition of kernel_vandermonde_zoh (diagonal only)
+            z = dt_t[h] * lam_c
+            Bbar = torch.expm1(z) / lam_c * B_c
+            k = torch.arange(L, dtype=torch.float64)
+            V = torch.exp(k[:, None] * z[None, :])
+            Kh = (V @ (C_c * Bbar)).real
+            loss = loss + torch.sum(Kh * torch.from_numpy(dK[h]))
+            continue
         A = torch.diag(lam_c)
         if not diagonal:
             P_c = cx(P_t[h])

@@ -513,3 +513,66 @@ def test_kernel_backward_tied_q_is_sum_of_both_paths():
     np.testing.assert_allclose(tied["P"], split["P"] + split["Q"], rtol=1e-12, atol=1e-14)
     for k in ("lam", "B", "C", "dt"):
         np.testing.assert_allclose(tied[k], split[k], rtol=1e-12, atol=1e-14)
+
+
+# --- Zero-order hold, diagonal: the Vandermonde kernel ---------------------------
+
+def test_zoh_vandermonde_worked_example():
+    g = _golden("worked_example_zoh.txt")
+    K = o.kernel_vandermonde_zoh(np.array([g["a"]]), np.array([g["b"]]), np.array([g["c"]]),
+                                 g["dt"], 2)
+    assert abs(K[0] - g["k0"]) < 1e-10 and abs(K[1] - g["k1"]) < 1e-10
+
+
+@pytest.mark.parametrize("N,L", [(1, 8), (4, 32), (16, 64)])
+def test_zoh_vandermonde_equals_matrix_powers(N, L):
+    rng = np.random.default_rng(80 + N)
+    lam = -rng.uniform(0.05, 1, N) + 1j * rng.uniform(-20, 20, N)
+    B, C = _cn(rng, N), _cn(rng, N)
+    dt = 0.07
+    d = [o.discretize_zoh_scalar(a, b, dt) for a, b in zip(lam, B)]
+    Abar = np.diag([e[0] for e in d])
+    Bbar = np.array([e[1] for e in d])
+    ref = o.kernel_truncated(Abar, Bbar, C, L)
+    K = o.kernel_vandermonde_zoh(lam, B, C, dt, L)
+    np.testing.assert_allclose(K, ref, rtol=0, atol=1e-13 * np.abs(ref).max())
+    # and it is the impulse response of the ZOH recurrence
+    u = np.zeros(L)
+    u[0] = 1.0
+    np.testing.assert_allclose(o.recurrence(Abar, Bbar, C, 0.0, u), K, atol=1e-13 * np.abs(K).max())
+
+
+def test_zoh_forward_and_recurrent_forward_agree():
+    # with zero-order hold the kernel is not aliased, so the convolution and
+    # the recurrence give the same outputs exactly (up to rounding)
+    x = make_generic_inputs(H=2, N=6, L=40, batch=2, seed=82, diagonal=True)
+    K, y = o.forward(x["lam"], None, None, x["B"], x["C"], x["dt"], x["D"], x["u"],
+                     diagonal=True, disc="zoh")
+    yr, _ = o.recurrent_forward(x["lam"], None, None, x["B"], x["C"], x["dt"], x["D"], x["u"],
+                                diagonal=True, disc="zoh")
+    np.testing.assert_allclose(y, yr, rtol=0, atol=1e-12 * np.abs(y).max())
+
+
+def test_zoh_kernel_backward_finite_differences():
+    x = make_generic_inputs(H=2, N=3, L=12, batch=1, seed=83, diagonal=True)
+    x = {k: (None if v is None or k == "workload" else np.asarray(v, np.float64))
+         for k, v in x.items()}
+    dK = np.random.default_rng(84).standard_normal((2, 12))
+    g = o.kernel_backward_dense(x["lam"], None, None, x["B"], x["C"], x["dt"], dK, diagonal=True,
+                                disc="zoh")
+
+    def loss(xx):
+        K, _ = o.forward(xx["lam"], None, None, xx["B"], xx["C"], xx["dt"], np.zeros(2),
+                         np.zeros((1, 2, 12)), diagonal=True, disc="zoh")
+        return float(np.sum(K * dK))
+    for name in ["lam", "B", "C", "dt"]:
+        flat = x[name].reshape(-1)
+        for i in range(flat.size):
+            e = 1e-6 * max(1.0, abs(flat[i]))
+            xp = {k: (None if v is None else v.copy()) for k, v in x.items()}
+            xm = {k: (None if v is None else v.copy()) for k, v in x.items()}
+            xp[name].reshape(-1)[i] += e
+            xm[name].reshape(-1)[i] -= e
+            fd = (loss(xp) - loss(xm)) / (2 * e)
+            an = g[name].reshape(-1)[i]
+            assert abs(fd - an) <= 1e-5 * max(1.0, abs(an)), (name, i, fd, an)
