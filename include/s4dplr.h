@@ -70,6 +70,13 @@ typedef enum s4dplr_status {
 
 /* Plan flag: diagonal state matrix (S4D).  P and Q are ignored (may be NULL). */
 #define S4DPLR_DIAGONAL 1u
+/* Plan flag (with S4DPLR_DIAGONAL only): zero-order-hold discretization
+ * ("The S4 kernel, from scratch", section 3: A-bar = exp(dt a)); kernel
+ * generation then evaluates the Vandermonde product
+ * K[h][k] = Re(sum_n C_n B-bar_n A-bar_n^k), B-bar_n = B_n (exp(dt a_n) - 1) / a_n,
+ * which is the kernel itself (not aliased), and the recurrent view and the
+ * backward pass use the same discretization. */
+#define S4DPLR_ZOH 2u
 
 typedef struct s4dplr_plan s4dplr_plan;
 

@@ -17,7 +17,7 @@ import os
 import torch  # loads the HIP runtime that libs4dplr then shares
 
 __all__ = [
-    "S4DPLRError", "DIAGONAL", "abi_version", "status_string", "plan_create",
+    "S4DPLRError", "DIAGONAL", "ZOH", "abi_version", "status_string", "plan_create",
     "plan_workspace_bytes", "plan_init", "kernel_gen", "conv_fwd", "forward",
     "conv_apply", "recurrent_prepare", "recurrent_scan", "conv_bwd", "kernel_gen_bwd",
     "plan_destroy", "Plan", "LIB_PATH",
@@ -25,6 +25,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libs4dplr.so")
 DIAGONAL = 1
+ZOH = 2
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -222,10 +223,11 @@ class Plan:
     """Owns a plan handle and (optionally) a workspace tensor on one device."""
 
     def __init__(self, H: int, N: int, L: int, batch: int, diagonal: bool = False,
-                 device=None):
+                 device=None, zoh: bool = False):
         self.H, self.N, self.L, self.batch = H, N, L, batch
-        self.diagonal = diagonal
-        self.handle = plan_create(H, N, L, batch, DIAGONAL if diagonal else 0)
+        self.diagonal, self.zoh = diagonal, zoh
+        self.handle = plan_create(H, N, L, batch,
+                                  (DIAGONAL if diagonal else 0) | (ZOH if zoh else 0))
         self.workspace_bytes = plan_workspace_bytes(self.handle)
         self.device = torch.device("cuda" if device is None else device)
         self._ws_store = None

@@ -111,7 +111,9 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
                                  unsigned flags) {
   if (!out) return S4DPLR_ERR_NULL;
   *out = nullptr;
-  if (flags & ~S4DPLR_DIAGONAL) return S4DPLR_ERR_UNSUPPORTED;
+  if (flags & ~(S4DPLR_DIAGONAL | S4DPLR_ZOH)) return S4DPLR_ERR_UNSUPPORTED;
+  if ((flags & S4DPLR_ZOH) && !(flags & S4DPLR_DIAGONAL)) return S4DPLR_ERR_UNSUPPORTED;
+  const bool zoh = (flags & S4DPLR_ZOH) != 0;
   if (H < 1 || batch < 1 || N < 1 || N > 256) return S4DPLR_ERR_SHAPE;
   if (!is_pow2(L) || L < 2 || L > 65536) return S4DPLR_ERR_SHAPE;
   if ((long long)batch * H * L >= (1LL << 31)) return S4DPLR_ERR_SHAPE;
@@ -151,7 +153,7 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
   p->off_coef = off;
   off = align_up(off + sizeof(float) * 4 * (size_t)H * L);
   p->off_kbuf = off;
-  if (!lds) off = align_up(off + sizeof(float) * (size_t)H * L);
+  if (!lds || zoh) off = align_up(off + sizeof(float) * (size_t)H * L);
   p->off_big = off;
   if (!lds) off = align_up(off + sizeof(float) * 2 * (size_t)batch * H * L);
   p->off_rrec = off;
@@ -163,12 +165,20 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
   p->off_bbeta = off;
   if (lds) off = align_up(off + sizeof(float) * 8 * (size_t)H * L);
   p->off_bpart = off;
-  if (lds) {
-    const size_t corr = sizeof(float) * 2 * (size_t)((batch + s4::kCorrRows - 1) / s4::kCorrRows) *
-                        H * (L + 1);
-    const size_t pole = sizeof(float) * 12 * (size_t)H * ((L + s4::kBwdChunk - 1) / s4::kBwdChunk) *
-                        N;
-    off = align_up(off + (corr > pole ? corr : pole));
+  {
+    const size_t nchunks = (L + s4::kBwdChunk - 1) / s4::kBwdChunk;
+    size_t need = 0;
+    if (lds) {
+      const size_t corr = sizeof(float) * 2 *
+                          (size_t)((batch + s4::kCorrRows - 1) / s4::kCorrRows) * H * (L + 1);
+      const size_t pole = sizeof(float) * 12 * (size_t)H * nchunks * N;
+      need = corr > pole ? corr : pole;
+    }
+    if (zoh) {
+      const size_t vpart = sizeof(float) * 4 * (size_t)H * nchunks * N;
+      if (vpart > need) need = vpart;
+    }
+    off = align_up(off + need);
   }
   p->total = off;
 
@@ -373,7 +383,8 @@ s4dplr_status s4dplr_kernel_gen_bwd(const s4dplr_plan* p, const float* lambda, c
   if (s4dplr_status st = check_params(p, lambda, P, B, C, dt)) return st;
   if (!dK) return S4DPLR_ERR_NULL;
   if (s4dplr_status st = check_ws(ws)) return st;
-  if (!s4::lds_path(p)) return S4DPLR_ERR_UNSUPPORTED;
+  const bool zoh = (p->flags & S4DPLR_ZOH) != 0;
+  if (!zoh && !s4::lds_path(p)) return S4DPLR_ERR_UNSUPPORTED;
   const bool diag = (p->flags & S4DPLR_DIAGONAL) != 0;
   if (diag) dP = dQ = nullptr;
   if (!Q) dQ = nullptr;
@@ -393,8 +404,11 @@ s4dplr_status s4dplr_kernel_gen_bwd(const s4dplr_plan* p, const float* lambda, c
     for (int j = 0; j < i; ++j)
       if (overlaps(outs[i], outb[i], outs[j], outb[j])) return S4DPLR_ERR_ALIAS;
   }
-  hipError_t e = s4::launch_kernel_gen_bwd(p, lambda, P, Q, B, C, dt, dK, dlambda, dP, dQ, dB,
-                                           dC, ddt, static_cast<unsigned char*>(ws), stream);
+  hipError_t e = zoh ? s4::launch_vandermonde_bwd(p, lambda, B, C, dt, dK, dlambda, dB, dC, ddt,
+                                                  static_cast<unsigned char*>(ws), stream)
+                     : s4::launch_kernel_gen_bwd(p, lambda, P, Q, B, C, dt, dK, dlambda, dP, dQ,
+                                                 dB, dC, ddt, static_cast<unsigned char*>(ws),
+                                                 stream);
   if (e != hipSuccess) return hip_fail(e);
   return S4DPLR_OK;
 }

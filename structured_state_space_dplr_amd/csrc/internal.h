@@ -27,11 +27,11 @@ struct s4dplr_plan {
   size_t tables_bytes;
   size_t off_khat;   // [H][L] float2: generating function at the roots of unity
   size_t off_coef;   // [H][L] float4: spectral weights (alpha, beta) of bin j
-  size_t off_kbuf;   // long path: [H][L] float time-domain kernel when not written out
+  size_t off_kbuf;   // [H][L] float time-domain kernel when not written out (long path, ZOH)
   size_t off_big;    // long path: [batch*H][L] float2 intermediate rows
   size_t off_rrec;   // recurrent view: [H][N] x 4 float4 per-pole step records
   size_t off_rchan;  // recurrent view: [H] float4 per-channel sums (S1, S2)
-  // Backward pass (L <= 2^S4DPLR_LDS_MAX_LOG2L only):
+  // Backward pass (L <= 2^S4DPLR_LDS_MAX_LOG2L; with ZOH the partial sums for every L):
   size_t off_bghat;  // [H][L] float2: FFT_L(dK) / L
   size_t off_bbeta;  // [H][L] x 2 float4: conj(dKhat/dk_ab) * Ghat per frequency
   size_t off_bpart;  // partial sums: correlation spectra [ceil(B/kCorrRows)][H][L+1] float2,
@@ -82,6 +82,14 @@ hipError_t launch_kernel_gen_bwd(const s4dplr_plan* p, const float* lam, const f
                                  const float* Q, const float* B, const float* C, const float* dt,
                                  const float* dK, float* dlam, float* dP, float* dQ, float* dB,
                                  float* dC, float* ddt, unsigned char* ws, hipStream_t s);
+// Zero-order hold, diagonal: the Vandermonde kernel K [H][L] (all L), and its
+// parameter gradients from dK (outputs may be null).
+hipError_t launch_vandermonde(const s4dplr_plan* p, const float* lam, const float* B,
+                              const float* C, const float* dt, float* K, hipStream_t s);
+hipError_t launch_vandermonde_bwd(const s4dplr_plan* p, const float* lam, const float* B,
+                                  const float* C, const float* dt, const float* dK, float* dlam,
+                                  float* dB, float* dC, float* ddt, unsigned char* ws,
+                                  hipStream_t s);
 // Work split of the scan: poles per lane (1, 2, 4 or 8) and log2 of the lanes
 // per sequence (0..5), chosen from N and the number of sequences.
 void recurrent_shape(int N, long rows, int* ppl, int* log2g);

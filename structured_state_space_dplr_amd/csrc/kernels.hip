@@ -856,6 +856,13 @@ static hipError_t launch_kspec(const s4dplr_plan* p, const float* Ktime, const f
 hipError_t launch_kernel_gen(const s4dplr_plan* p, const float* lam, const float* P,
                              const float* Q, const float* B, const float* C, const float* dt,
                              const float* D, float* Kout, unsigned char* ws, hipStream_t s) {
+  if (p->flags & S4DPLR_ZOH) {
+    // zero-order hold: the Vandermonde kernel, then the spectrum of (K + D delta)
+    float* K = Kout ? Kout : at<float>(ws, p->off_kbuf);
+    hipError_t e = launch_vandermonde(p, lam, B, C, dt, K, s);
+    if (e != hipSuccess) return e;
+    return launch_spectrum_from_time(p, K, D, ws, s, 0);
+  }
   const ParamPtrs pp = param_ptrs(lam, P, Q, B, C, dt);
   if (fused_path(p)) {
     S4_DISPATCH_LOG2L(kgen_launch, p, pp, D, nullptr, Kout, ws, s, 0);

@@ -99,7 +99,7 @@ __device__ __forceinline__ void partial_sums(const float2 (&qc)[PPL], const floa
 __global__ __launch_bounds__(64) void recurrent_prepare_kernel(
     const float2* __restrict__ lam, const float2* __restrict__ P, const float2* __restrict__ Q,
     const float2* __restrict__ B, const float2* __restrict__ C, const float* __restrict__ dt,
-    float4* __restrict__ rec, float4* __restrict__ chan, int N, int diag) {
+    float4* __restrict__ rec, float4* __restrict__ chan, int N, int diag, int zoh) {
   const int h = blockIdx.x, lane = threadIdx.x;
   const double d = (double)dt[h], s = 0.5 * d;
   double den_re = 0.0, den_im = 0.0;
@@ -122,9 +122,22 @@ __global__ __launch_bounds__(64) void recurrent_prepare_kernel(
     const cd p = diag ? cd{0.0, 0.0} : cd_load(P, i);
     const cd q = diag ? cd{0.0, 0.0} : cd_load(Q ? Q : P, i);
     const cd d0 = {1.0 - s * l.re, -s * l.im};
-    const cd ab = cd_div({1.0 + s * l.re, s * l.im}, d0);
+    cd ab = cd_div({1.0 + s * l.re, s * l.im}, d0);
     const cd e = cd_div({s * p.re, s * p.im}, d0);
-    const cd bb = cd_div({d * b.re, d * b.im}, d0);
+    cd bb = cd_div({d * b.re, d * b.im}, d0);
+    if (zoh) {
+      // zero-order hold (diagonal): A-bar = exp(dt lambda), B-bar = b expm1(dt lambda) / lambda
+      const double ex = exp(d * l.re);
+      double sn, cs;
+      sincos(d * l.im, &sn, &cs);
+      ab = {ex * cs, ex * sn};
+      if (l.re == 0.0 && l.im == 0.0) {
+        bb = {d * b.re, d * b.im};
+      } else {
+        const double sh = sin(0.5 * d * l.im);
+        bb = cd_mul(b, cd_div({expm1(d * l.re) * cs - 2.0 * sh * sh, ex * sn}, l));
+      }
+    }
     const cd g = cd_div(e, den);
     const cd qc = {q.re, -q.im};
     const cd qa = cd_mul(qc, ab);
@@ -266,11 +279,12 @@ hipError_t launch_recurrent_prepare(const s4dplr_plan* p, const float* lam, cons
                                     const float* Q, const float* B, const float* C,
                                     const float* dt, unsigned char* ws, hipStream_t s) {
   const int diag = (p->flags & S4DPLR_DIAGONAL) ? 1 : 0;
+  const int zoh = (p->flags & S4DPLR_ZOH) ? 1 : 0;
   recurrent_prepare_kernel<<<p->H, 64, 0, s>>>(
       reinterpret_cast<const float2*>(lam), reinterpret_cast<const float2*>(P),
       reinterpret_cast<const float2*>(Q), reinterpret_cast<const float2*>(B),
       reinterpret_cast<const float2*>(C), dt, reinterpret_cast<float4*>(ws + p->off_rrec),
-      reinterpret_cast<float4*>(ws + p->off_rchan), p->N, diag);
+      reinterpret_cast<float4*>(ws + p->off_rchan), p->N, diag, zoh);
   return hipGetLastError();
 }
 

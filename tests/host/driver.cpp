@@ -24,7 +24,7 @@ int main() {
   const int Ns[] = {1, 3, 64, 256};
   for (int L : Ls)
     for (int N : Ns)
-      for (unsigned flags : {0u, 1u}) {
+      for (unsigned flags : {0u, 1u, 3u}) {
         s4dplr_plan* p = nullptr;
         CHECK(s4dplr_plan_create(&p, 3, N, L, 2, flags) == S4DPLR_OK && p);
         size_t bytes = 0;
@@ -51,11 +51,13 @@ int main() {
           float* o = reinterpret_cast<float*>(base + 5 * gap);
           const s4dplr_status want = L <= 16384 ? S4DPLR_OK : S4DPLR_ERR_UNSUPPORTED;
           CHECK(s4dplr_conv_bwd(p, u, K, nullptr, g, y, o, nullptr, ws, nullptr) == want);
+          const s4dplr_status want_kg = (L <= 16384 || (flags & S4DPLR_ZOH)) ? S4DPLR_OK
+                                                                              : S4DPLR_ERR_UNSUPPORTED;
           float* outs = reinterpret_cast<float*>(base + 6 * gap);
           const size_t cb = 2 * 3 * (size_t)N;   // floats of one [H][N] complex output
           CHECK(s4dplr_kernel_gen_bwd(p, f, f, nullptr, f, f, f, K, outs, outs + cb, nullptr,
                                       outs + 2 * cb, outs + 3 * cb, outs + 4 * cb, ws,
-                                      nullptr) == want);
+                                      nullptr) == want_kg);
         }
         CHECK(s4dplr_recurrent_scan(p, nullptr, u, 7, K, y, ws, nullptr) == S4DPLR_OK);
         CHECK(s4dplr_recurrent_scan(p, nullptr, u, 7, K, u, ws, nullptr) == S4DPLR_ERR_ALIAS);
@@ -77,6 +79,7 @@ int main() {
   s4dplr_plan* p = nullptr;
   CHECK(s4dplr_plan_create(&p, 1, 1, 3, 1, 0) == S4DPLR_ERR_SHAPE && !p);
   CHECK(s4dplr_plan_create(&p, 1, 1, 4, 1, 8) == S4DPLR_ERR_UNSUPPORTED);
+  CHECK(s4dplr_plan_create(&p, 1, 1, 4, 1, S4DPLR_ZOH) == S4DPLR_ERR_UNSUPPORTED);
   CHECK(s4dplr_plan_create(nullptr, 1, 1, 4, 1, 0) == S4DPLR_ERR_NULL);
   for (int s = -1; s < 9; ++s) CHECK(std::strlen(s4dplr_status_string(static_cast<s4dplr_status>(s))) > 0);
   s4dplr_plan_destroy(nullptr);

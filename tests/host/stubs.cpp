@@ -47,6 +47,17 @@ hipError_t launch_kernel_gen_bwd(const s4dplr_plan*, const float*, const float*,
   ++g_launches;
   return hipSuccess;
 }
+hipError_t launch_vandermonde(const s4dplr_plan*, const float*, const float*, const float*,
+                              const float*, float*, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
+hipError_t launch_vandermonde_bwd(const s4dplr_plan*, const float*, const float*, const float*,
+                                  const float*, const float*, float*, float*, float*, float*,
+                                  unsigned char*, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
 hipError_t launch_recurrent_prepare(const s4dplr_plan*, const float*, const float*,
                                     const float*, const float*, const float*, const float*,
                                     unsigned char*, hipStream_t) {

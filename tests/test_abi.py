@@ -90,7 +90,9 @@ def _create(lib, H, N, L, B, flags=0):
     (4, 16, 131072, 2, 0, ERR_SHAPE),
     (4, 16, 256, 0, 0, ERR_SHAPE),
     (4096, 16, 65536, 16, 0, ERR_SHAPE),     # batch*H*L >= 2^31
-    (4, 16, 256, 2, 2, ERR_UNSUPPORTED),
+    (4, 16, 256, 2, 3, OK),                  # diagonal + zero-order hold
+    (4, 16, 256, 2, 2, ERR_UNSUPPORTED),     # zero-order hold needs the diagonal flag
+    (4, 16, 256, 2, 4, ERR_UNSUPPORTED),
 ])
 def test_plan_create_validation(lib, H, N, L, B, flags, expect):
     st, h = _create(lib, H, N, L, B, flags)
