@@ -83,6 +83,23 @@ def recurrent_counts(w):
     return per_pole * w.N * rows, 16 * w.N * rows + 8 * rows
 
 
+def backward_counts(w):
+    """Algorithmic work of the backward pass.
+
+    conv_bwd bytes: u, dy read and du written once each (4 B per sample),
+    K read and dK written (4 B per (h, k)), D and dD.
+    kernel_gen_bwd flops per (h, l, n): the forward Cauchy sums recomputed
+    for the Woodbury partials (40 DPLR / 16 diagonal, as in the forward) and
+    the transposed per-pole sums: the reciprocal (8), the sums R_ab (8 per
+    complex multiply-add: 32 DPLR / 8 diagonal), sum_ab conj(w_ab) beta_ab
+    (32 / 8), conj(r)^2 (6), t = conj(r)^2 m (6), T += t (2), E += conj(g) t (4).
+    """
+    bhl, hl = w.batch * w.H * w.L, w.H * w.L
+    q_conv = 12 * bhl + 8 * hl + 8 * w.H
+    per_term = (16 + 8 + 8 + 8 + 18) if w.diagonal else (40 + 8 + 32 + 32 + 18)
+    return q_conv, w.H * w.L * w.N * per_term
+
+
 def read_traffic(workload_name: str):
     """HBM bytes per convolution launch from the committed rocprofv3 counter
     summary, if it was taken on the current kernel sources; else None."""
@@ -250,6 +267,49 @@ def main() -> int:
     log(f"[bench] recurrent scan {t_scan * 1e6:.1f} us ({samples / t_scan:.3g} samples/s, "
         f"{rec_tflops:.1f} TFLOP/s); decode step {t_dec * 1e6:.2f} us")
 
+    # ---- zero-order hold (diagonal): the Vandermonde kernel on the same poles ---
+    zplan = s4.Plan(w.H, w.N, w.L, w.batch, diagonal=True, zoh=True, device=dev)
+    zws = zplan.workspace()
+    t_vd = timed(lambda i: s4.kernel_gen(zplan, params["lam"], None, None, params["B"],
+                                         params["C"], params["dt"], K, zws, stream), args.steps)
+    f_vd = 7 * w.H * w.L * w.N      # per (h, k, n): one complex product and one add
+    log(f"[bench] zoh kernel_gen {t_vd * 1e6:.1f} us ({f_vd / t_vd / 1e9:.0f} GFLOP/s)")
+    zoh = {"kernel_gen_us": t_vd * 1e6, "gflops": f_vd / t_vd / 1e9,
+           "frac_fp32_peak": f_vd / t_vd / 1e12 / FP32_PEAK_TFLOPS, "algorithmic_flops": f_vd,
+           "note": "Vandermonde kernel plus the spectrum of K padded to 2L"}
+    zplan.close()
+
+    # ---- the backward pass (L <= 16384): conv_bwd and kernel_gen_bwd ----------
+    bwd = None
+    if w.L <= 16384:
+        q_bwd, f_bwd = backward_counts(w)
+        dy = ys[1 % nsets]
+        du = ys[2 % nsets]
+        dK = torch.empty((w.H, w.L), dtype=torch.float32, device=dev)
+        dD = torch.empty((w.H,), dtype=torch.float32, device=dev)
+        grads = {k: torch.empty((w.H, w.N, 2), dtype=torch.float32, device=dev)
+                 for k in ("lam", "P", "B", "C")}
+        ddt = torch.empty((w.H,), dtype=torch.float32, device=dev)
+        t_cb = timed(lambda i: s4.conv_bwd(plan, us[i % nsets], K, params["D"], dy, du, dK, dD,
+                                           ws, stream), args.steps)
+        t_kb = timed(lambda i: s4.kernel_gen_bwd(
+            plan, params["lam"], P, params["Q"], params["B"], params["C"], params["dt"], dK,
+            grads["lam"], None if w.diagonal else grads["P"], None, grads["B"], grads["C"], ddt,
+            ws, stream), args.steps)
+        log(f"[bench] conv_bwd {t_cb * 1e6:.1f} us ({q_bwd / t_cb / 1e9:.0f} GB/s), "
+            f"kernel_gen_bwd {t_kb * 1e6:.1f} us ({f_bwd / t_kb / 1e9:.0f} GFLOP/s)")
+        bwd = {
+            "conv_bwd_us": t_cb * 1e6,
+            "conv_bwd_gbs": q_bwd / t_cb / 1e9,
+            "conv_bwd_frac_hbm": q_bwd / t_cb / 1e9 / HBM_PEAK_GBS,
+            "conv_bwd_algorithmic_bytes": q_bwd,
+            "kernel_gen_bwd_us": t_kb * 1e6,
+            "kernel_gen_bwd_gflops": f_bwd / t_kb / 1e9,
+            "kernel_gen_bwd_frac_fp32_peak": f_bwd / t_kb / 1e12 / FP32_PEAK_TFLOPS,
+            "kernel_gen_bwd_algorithmic_flops": f_bwd,
+            "samples_per_s": samples / (t_cb + t_kb),
+        }
+
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -308,6 +368,8 @@ def main() -> int:
             "decode_bytes_per_step": decode_bytes,
             "decode_tokens_per_s": w.batch / t_dec,
         },
+        "backward": bwd,
+        "zoh": zoh,
         "forward_us_events": fwd_ms_events * 1e3,
         "cpu_baseline": None,
     }

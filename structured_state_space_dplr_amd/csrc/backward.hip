@@ -66,6 +66,8 @@ struct CorrShape {
 // sequences:
 //   U_2k = (A_k + conj A_{L-k}) / 2,     G_2k = (A_k - conj A_{L-k}) / 2i,
 //   U_2k+1 = (B_k + conj B_{L-1-k}) / 2, G_2k+1 = (B_k - conj B_{L-1-k}) / 2i.
+// Up to L = 4096 each thread keeps its share of a row in registers for both
+// transforms and loads the next row while the current one is transformed.
 template <int LOG2L>
 __global__ __launch_bounds__(CorrShape<LOG2L>::NT) void corr_spec_kernel(
     const float* __restrict__ u, const float* __restrict__ dy, float2* part, const float2* twL,
@@ -75,11 +77,13 @@ __global__ __launch_bounds__(CorrShape<LOG2L>::NT) void corr_spec_kernel(
   // would hold them all in registers and spill at 1024 threads.)
   using S = CorrShape<LOG2L>;
   constexpr int L = S::L, NT = S::NT;
+  constexpr int PE = (L + NT - 1) / NT;   // samples of a row per thread
   // Large transforms run 1024 threads with at most 128 VGPRs each: there the
   // running sums live in the block's own output row (each bin always belongs
-  // to the same thread) instead of in registers.
+  // to the same thread) and rows are read when needed.
   constexpr bool kAccInRow = LOG2L >= 13;
   constexpr int NE = kAccInRow ? 1 : S::EPT, NO = kAccInRow ? 1 : S::OPT;
+  constexpr int PR = kAccInRow ? 1 : PE;   // register copies of a row
   __shared__ float2 buf[S::MP];
   const int h = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
   float2* out = part + ((size_t)c * H + h) * (L + 1);
@@ -104,14 +108,41 @@ __global__ __launch_bounds__(CorrShape<LOG2L>::NT) void corr_spec_kernel(
   };
   const int b_first = c * kCorrRows;
   const int b_end = min(batch, (c + 1) * kCorrRows);
+  float2 cur[PR], nxt[PR], wn[PR];
+  auto load_row = [&](float2 (&dst)[PR], int b) {
+    const size_t row = (size_t)b * H + h;
+#pragma unroll
+    for (int i = 0; i < PR; ++i) {
+      const int n = tid + i * NT;
+      dst[i] = n < L ? make_float2(u[row * L + n], dy[row * L + n]) : make_float2(0.f, 0.f);
+    }
+  };
+  if constexpr (!kAccInRow) {
+#pragma unroll
+    for (int i = 0; i < PR; ++i) {
+      const int n = tid + i * NT;
+      const float2 w = n < L ? cs[n] : make_float2(1.f, 0.f);
+      wn[i] = make_float2(w.x, -w.y);                        // e^{-i pi n/L}
+    }
+    if (b_first < b_end) load_row(cur, b_first);
+  }
   for (int b = b_first; b < b_end; ++b) {
     const size_t row = (size_t)b * H + h;
     const float* ur = u + row * L;
     const float* gr = dy + row * L;
     const bool first = b == b_first;
+    if constexpr (!kAccInRow) {
+      if (b + 1 < b_end) load_row(nxt, b + 1);
+    }
     // even bins
+    if constexpr (kAccInRow) {
 #pragma unroll 4
-    for (int n = tid; n < L; n += NT) buf[lds_pad(n)] = make_float2(ur[n], gr[n]);
+      for (int n = tid; n < L; n += NT) buf[lds_pad(n)] = make_float2(ur[n], gr[n]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < PR; ++i)
+        if (tid + i * NT < L) buf[lds_pad(tid + i * NT)] = cur[i];
+    }
     __syncthreads();
     lds_fft<LOG2L, false>(buf, tid, tid < S::NTL, twL);
     if constexpr (kAccInRow) {
@@ -129,10 +160,16 @@ __global__ __launch_bounds__(CorrShape<LOG2L>::NT) void corr_spec_kernel(
     }
     __syncthreads();
     // odd bins
+    if constexpr (kAccInRow) {
 #pragma unroll 4
-    for (int n = tid; n < L; n += NT) {
-      const float2 w = cs[n];                             // e^{-i pi n/L} = conj(w)
-      buf[lds_pad(n)] = cmul(make_float2(ur[n], gr[n]), make_float2(w.x, -w.y));
+      for (int n = tid; n < L; n += NT) {
+        const float2 w = cs[n];                             // e^{-i pi n/L} = conj(w)
+        buf[lds_pad(n)] = cmul(make_float2(ur[n], gr[n]), make_float2(w.x, -w.y));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PR; ++i)
+        if (tid + i * NT < L) buf[lds_pad(tid + i * NT)] = cmul(cur[i], wn[i]);
     }
     __syncthreads();
     lds_fft<LOG2L, false>(buf, tid, tid < S::NTL, twL);
@@ -149,6 +186,10 @@ __global__ __launch_bounds__(CorrShape<LOG2L>::NT) void corr_spec_kernel(
       }
     }
     __syncthreads();
+    if constexpr (!kAccInRow) {
+#pragma unroll
+      for (int i = 0; i < PR; ++i) cur[i] = nxt[i];
+    }
   }
   if constexpr (!kAccInRow) {
 #pragma unroll
@@ -169,11 +210,11 @@ __global__ __launch_bounds__(CorrShape<LOG2L>::NT) void corr_spec_kernel(
 //   W_k = (S_k + conj S_{L-k}) / 2 + i e^{i pi k/L} (S_k - conj S_{L-k}) / 2,
 // (1/L) IDFT_L(W)_m = c_2m + i c_2m+1, and c_0 .. c_{L-1} is dK.
 template <int LOG2L>
-__global__ __launch_bounds__(CorrShape<LOG2L>::NT) void corr_inv_kernel(
+__global__ __launch_bounds__(imax(256, CorrShape<LOG2L>::NT)) void corr_inv_kernel(
     const float2* __restrict__ part, float* __restrict__ dK, float* __restrict__ dD,
     const float2* __restrict__ twL, const float2* __restrict__ cs, int H, int nparts) {
   using S = CorrShape<LOG2L>;
-  constexpr int L = S::L, NT = S::NT;
+  constexpr int L = S::L, NT = imax(256, S::NT);   // more threads for the partial sums
   __shared__ float2 buf[S::MP];
   const int h = blockIdx.x, tid = threadIdx.x;
   for (int j = tid; j <= L; j += NT) {
@@ -430,7 +471,7 @@ void corr_launch(const s4dplr_plan* p, const float* u, const float* dy, float* d
   const float2* cs = at<const float2>(ws, p->off_cs);
   corr_spec_kernel<LOG2L><<<dim3(p->H, nparts), S::NT, 0, s>>>(u, dy, part, twL, cs, p->H,
                                                                 p->batch);
-  corr_inv_kernel<LOG2L><<<p->H, S::NT, 0, s>>>(part, dK, dD, twL, cs, p->H, nparts);
+  corr_inv_kernel<LOG2L><<<p->H, imax(256, S::NT), 0, s>>>(part, dK, dD, twL, cs, p->H, nparts);
 }
 
 template <int LOG2L>

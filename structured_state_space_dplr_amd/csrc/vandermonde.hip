@@ -28,10 +28,13 @@ namespace s4 {
 
 namespace {
 
-constexpr int kVanderThreads = 256;
-constexpr int kVanderTaps = 16;
+constexpr int kVanderTaps = 16;                    // consecutive taps per thread
+constexpr int kVanderKT = 64;                      // tap threads per block (one wave)
+constexpr int kVanderPG = 4;                       // pole groups per block (waves)
+constexpr int kVanderThreads = kVanderKT * kVanderPG;
 constexpr int kMaxPolesZoh = 256;
 constexpr double kTwoPi = 6.283185307179586476925286766559;
+constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
 
 struct cd {
   double re, im;
@@ -74,7 +77,7 @@ __device__ __forceinline__ ZohPole zoh_pole(cd lam, double dt) {
 // exp(k z) for an integer k >= 0 with the phase reduced in fp64.
 __device__ __forceinline__ float2 power_of(double zre, double zim, double k) {
   double ph = k * zim;
-  ph = fma(-kTwoPi, rint(ph / kTwoPi), ph);
+  ph = fma(-kTwoPi, rint(ph * kInvTwoPi), ph);
   const float mag = expf((float)(k * zre));
   float s, c;
   sincosf((float)ph, &s, &c);
@@ -84,11 +87,14 @@ __device__ __forceinline__ float2 power_of(double zre, double zim, double k) {
 }  // namespace
 
 // Pole records in LDS: (W re, W im, A-bar re, A-bar im) and (z re, z im) in fp64.
+// Block (tap range, h): wave g sums the poles n = g, g + kVanderPG, ... for
+// kVanderTaps taps per lane; the waves' partial sums meet in LDS.
 __global__ __launch_bounds__(kVanderThreads) void vander_kernel(
     const float2* __restrict__ lam, const float2* __restrict__ B, const float2* __restrict__ C,
     const float* __restrict__ dt, float* __restrict__ K, int N, int L) {
   __shared__ float4 wa[kMaxPolesZoh];
   __shared__ double2 zz[kMaxPolesZoh];
+  __shared__ float red[kVanderPG][kVanderKT][kVanderTaps + 1];
   const int h = blockIdx.y, tid = threadIdx.x;
   const double d = (double)dt[h];
   for (int n = tid; n < N; n += kVanderThreads) {
@@ -101,31 +107,39 @@ __global__ __launch_bounds__(kVanderThreads) void vander_kernel(
     zz[n] = make_double2(d * l.re, d * l.im);
   }
   __syncthreads();
-  const int k0 = (blockIdx.x * kVanderThreads + tid) * kVanderTaps;
-  if (k0 >= L) return;
+  const int kt = tid % kVanderKT, pg = tid / kVanderKT;
+  const int k0 = (blockIdx.x * kVanderKT + kt) * kVanderTaps;
   float acc[kVanderTaps];
 #pragma unroll
   for (int j = 0; j < kVanderTaps; ++j) acc[j] = 0.f;
-  for (int n = 0; n < N; ++n) {
-    const float4 r = wa[n];
-    const double2 z = zz[n];
-    const float2 a = make_float2(r.z, r.w);
-    float2 q = cmul(make_float2(r.x, r.y), power_of(z.x, z.y, (double)k0));
+  if (k0 < L) {
+    for (int n = pg; n < N; n += kVanderPG) {
+      const float4 r = wa[n];
+      const double2 z = zz[n];
+      const float2 a = make_float2(r.z, r.w);
+      float2 q = cmul(make_float2(r.x, r.y), power_of(z.x, z.y, (double)k0));
 #pragma unroll
-    for (int j = 0; j < kVanderTaps; ++j) {
-      acc[j] += q.x;
-      q = cmul(q, a);
+      for (int j = 0; j < kVanderTaps; ++j) {
+        acc[j] += q.x;
+        q = cmul(q, a);
+      }
     }
   }
-  float* out = K + (size_t)h * L + k0;
-  if (k0 + kVanderTaps <= L) {
 #pragma unroll
-    for (int j = 0; j < kVanderTaps; j += 4)
-      *reinterpret_cast<float4*>(out + j) = make_float4(acc[j], acc[j + 1], acc[j + 2], acc[j + 3]);
-  } else {
+  for (int j = 0; j < kVanderTaps; ++j) red[pg][kt][j] = acc[j];
+  __syncthreads();
+  // thread (kt, pg) finishes taps [pg T/G, (pg + 1) T/G) of its tap range
+  constexpr int TPG = kVanderTaps / kVanderPG;
+  if (k0 < L) {
+    float* out = K + (size_t)h * L + k0;
 #pragma unroll
-    for (int j = 0; j < kVanderTaps; ++j)
-      if (k0 + j < L) out[j] = acc[j];
+    for (int m = 0; m < TPG; ++m) {
+      const int j = pg * TPG + m;
+      float v = 0.f;
+#pragma unroll
+      for (int g = 0; g < kVanderPG; ++g) v += red[g][kt][j];
+      if (k0 + j < L) out[j] = v;
+    }
   }
 }
 
@@ -238,7 +252,7 @@ __global__ __launch_bounds__(256) void vander_bwd_final_kernel(
 
 hipError_t launch_vandermonde(const s4dplr_plan* p, const float* lam, const float* B,
                               const float* C, const float* dt, float* K, hipStream_t s) {
-  const int per_block = kVanderThreads * kVanderTaps;
+  const int per_block = kVanderKT * kVanderTaps;
   const dim3 grid((p->L + per_block - 1) / per_block, p->H);
   vander_kernel<<<grid, kVanderThreads, 0, s>>>(
       reinterpret_cast<const float2*>(lam), reinterpret_cast<const float2*>(B),
