@@ -51,7 +51,7 @@ __all__ = [
     "kernel_cauchy", "conv_direct", "conv_direct_at", "conv_fft",
     "recurrence", "forward", "recurrent_forward",
     "conv_backward_direct", "conv_backward_fft", "kernel_backward_dense",
-    "kernel_vandermonde_zoh",
+    "kernel_vandermonde_zoh", "layer_norm", "glu_projection", "block_forward",
 ]
 
 
@@ -501,3 +501,42 @@ def kernel_backward_dense(lam, P, Q, B, C, dt, dK, diagonal=False, disc="bilinea
     g = lambda a: None if a is None else a.grad.numpy().copy()
     return {"lam": g(lam_t), "P": g(P_t), "Q": g(Q_t), "B": g(B_t), "C": g(C_t),
             "dt": g(dt_t)}
+
+
+# ---------------------------------------------------------------------------
+# The block around the layer   ([scratch] section 6: the block adds a
+# pre-norm, a GLU-gated projection and a residual connection)
+# ---------------------------------------------------------------------------
+
+def layer_norm(x, gamma, beta, eps=1e-5):
+    """Normalization over the H channels at every (batch, time) position
+    (reading: layer normalization with the biased variance, eps = 1e-5, and a
+    per-channel gain and shift).  x: (batch, H, L)."""
+    x = np.asarray(x, np.float64)
+    mu = x.mean(axis=1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=1, keepdims=True)
+    g = np.asarray(gamma, np.float64)[None, :, None]
+    b = np.asarray(beta, np.float64)[None, :, None]
+    return (x - mu) / np.sqrt(var + eps) * g + b
+
+
+def glu_projection(s, W, bias):
+    """[a; g] = W s + bias over the channels (W: (2H, H)), then the gated
+    linear unit a * sigmoid(g) (reading: the first H outputs are the values,
+    the last H the gates).  s: (batch, H, L) -> (batch, H, L)."""
+    s = np.asarray(s, np.float64)
+    W = np.asarray(W, np.float64)
+    H = s.shape[1]
+    z = np.einsum("oh,bhl->bol", W, s) + np.asarray(bias, np.float64)[None, :, None]
+    a, g = z[:, :H], z[:, H:]
+    return a / (1.0 + np.exp(-g))
+
+
+def block_forward(x, gamma, beta, lam, P, Q, B, C, dt, D, W, bias, diagonal=False,
+                  disc="bilinear"):
+    """out = x + GLU(W s + bias), s = the layer applied to layer_norm(x)
+    ([scratch] section 6; readings: no activation between the layer and the
+    projection, no dropout)."""
+    z = layer_norm(x, gamma, beta)
+    _, s = forward(lam, P, Q, B, C, dt, D, z, diagonal=diagonal, disc=disc)
+    return np.asarray(x, np.float64) + glu_projection(s, W, bias)

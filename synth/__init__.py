@@ -169,3 +169,18 @@ def make_generic_inputs(H: int, N: int, L: int, batch: int, seed: int = 0,
         "B": f32(_ri(B)), "C": f32(_ri(C)), "dt": f32(np.exp(log_dt)), "D": f32(D),
         "u": f32(u), "workload": None,
     }
+
+
+def make_block_params(H: int, seed: int = 1):
+    """Random-initialized parameters of the block around the layer (pre-norm,
+    GLU-gated projection): LayerNorm gain gamma = 1 + 0.1 N(0,1) and shift
+    beta = 0.1 N(0,1) per channel, projection W (2H x H) with N(0, 1/H)
+    entries (rows [0, H): the value half, rows [H, 2H): the gate half) and bias
+    0.1 N(0,1) (2H).  Draw order: gamma, beta, W, bias.  fp32."""
+    rng = np.random.default_rng(seed)
+    gamma = 1.0 + 0.1 * rng.standard_normal(H)
+    beta = 0.1 * rng.standard_normal(H)
+    W = rng.standard_normal((2 * H, H)) / np.sqrt(H)
+    bias = 0.1 * rng.standard_normal(2 * H)
+    f32 = lambda a: np.ascontiguousarray(a, dtype=np.float32)
+    return {"gamma": f32(gamma), "beta": f32(beta), "W": f32(W), "bias": f32(bias)}

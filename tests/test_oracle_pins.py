@@ -576,3 +576,53 @@ def test_zoh_kernel_backward_finite_differences():
             fd = (loss(xp) - loss(xm)) / (2 * e)
             an = g[name].reshape(-1)[i]
             assert abs(fd - an) <= 1e-5 * max(1.0, abs(an)), (name, i, fd, an)
+
+
+# --- The block: pre-norm, GLU-gated projection, residual ------------------------
+
+def test_layer_norm_properties():
+    rng = np.random.default_rng(90)
+    x = 3.0 + 2.0 * rng.standard_normal((2, 7, 5))
+    z = o.layer_norm(x, np.ones(7), np.zeros(7), eps=0.0)
+    np.testing.assert_allclose(z.mean(axis=1), 0.0, atol=1e-13)
+    np.testing.assert_allclose((z ** 2).mean(axis=1), 1.0, atol=1e-12)
+    g, b = rng.standard_normal(7), rng.standard_normal(7)
+    np.testing.assert_allclose(o.layer_norm(x, g, b, eps=0.0), z * g[None, :, None] + b[None, :, None],
+                               atol=1e-12)
+    # a constant column normalizes to the shift alone
+    xc = np.ones((1, 7, 1)) * 4.2
+    np.testing.assert_allclose(o.layer_norm(xc, g, b)[0, :, 0], b, atol=1e-12)
+
+
+def test_glu_projection_closed_forms():
+    rng = np.random.default_rng(91)
+    H = 5
+    s = rng.standard_normal((2, H, 4))
+    # W = [I; 0], no bias: a = s, g = 0 -> s / 2
+    W = np.vstack([np.eye(H), np.zeros((H, H))])
+    np.testing.assert_allclose(o.glu_projection(s, W, np.zeros(2 * H)), s / 2, atol=1e-15)
+    # a permutation in the value half moves channels: output channel c is s[perm[c]] / 2
+    perm = np.array([3, 0, 4, 1, 2])
+    Wp = np.vstack([np.eye(H)[perm], np.zeros((H, H))])
+    np.testing.assert_allclose(o.glu_projection(s, Wp, np.zeros(2 * H)), s[:, perm] / 2, atol=1e-15)
+    # W = 0: the output is the bias gate a sigmoid(g), the same at every position
+    bias = rng.standard_normal(2 * H)
+    out = o.glu_projection(s, np.zeros((2 * H, H)), bias)
+    ref = bias[:H] / (1 + np.exp(-bias[H:]))
+    np.testing.assert_allclose(out, np.broadcast_to(ref[None, :, None], out.shape), atol=1e-15)
+    # the gate half: W = [0; I], bias = [1; 0] -> sigmoid(s)
+    Wg = np.vstack([np.zeros((H, H)), np.eye(H)])
+    bg = np.concatenate([np.ones(H), np.zeros(H)])
+    np.testing.assert_allclose(o.glu_projection(s, Wg, bg), 1 / (1 + np.exp(-s)), atol=1e-15)
+
+
+def test_block_forward_composition():
+    # with W = [I; 0] and no bias the block is x + layer(layer_norm(x)) / 2
+    x = make_generic_inputs(H=3, N=4, L=16, batch=2, seed=92)
+    p = {"gamma": np.array([1.0, 0.5, 2.0]), "beta": np.array([0.0, 0.1, -0.2])}
+    W = np.vstack([np.eye(3), np.zeros((3, 3))])
+    out = o.block_forward(x["u"], p["gamma"], p["beta"], x["lam"], x["P"], x["Q"], x["B"],
+                          x["C"], x["dt"], x["D"], W, np.zeros(6))
+    z = o.layer_norm(x["u"], p["gamma"], p["beta"])
+    _, s = o.forward(x["lam"], x["P"], x["Q"], x["B"], x["C"], x["dt"], x["D"], z)
+    np.testing.assert_allclose(out, x["u"] + s / 2, atol=1e-12)
