@@ -77,6 +77,8 @@ typedef enum s4dplr_status {
  * which is the kernel itself (not aliased), and the recurrent view and the
  * backward pass use the same discretization. */
 #define S4DPLR_ZOH 2u
+/* Plan flag: reserve the workspace buffers of s4dplr_block_forward. */
+#define S4DPLR_BLOCK 4u
 
 typedef struct s4dplr_plan s4dplr_plan;
 
@@ -242,6 +244,28 @@ s4dplr_status s4dplr_kernel_gen_bwd(const s4dplr_plan* plan, const float* lambda
                                     const float* dt, const float* dK, float* dlambda, float* dP,
                                     float* dQ, float* dB, float* dC, float* ddt, void* ws,
                                     hipStream_t stream);
+
+/*
+ * The block around the layer ("The S4 kernel, from scratch", section 6: a
+ * pre-norm, a GLU-gated projection and a residual connection):
+ *   z = LayerNorm_h(x) * gamma + beta   (over the H channels at each (b, t);
+ *                                       biased variance, eps = 1e-5),
+ *   s = the layer applied to z          (s4dplr_forward with these parameters),
+ *   out = x + a * sigmoid(g),  [a; g] = W s + bias  (W: [2H][H] row-major fp32,
+ *                                       rows [0, H) values, [H, 2H) gates).
+ * x, out: [batch][H][L]; gamma, beta: [H]; bias: [2H]; the layer's parameters
+ * as for s4dplr_forward (Q and D may be NULL).  The plan must have been
+ * created with S4DPLR_BLOCK.  out may be x itself (in place); otherwise it
+ * must not overlap x, and it must never overlap the other inputs or the
+ * workspace (ERR_ALIAS).  The projection runs on the matrix cores in fp32.
+ * Limit: batch <= 65535 (ERR_SHAPE).
+ * Errors: ERR_NULL, ERR_SHAPE, ERR_ALIAS, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP.
+ */
+s4dplr_status s4dplr_block_forward(const s4dplr_plan* plan, const float* x, const float* gamma,
+                                   const float* beta, const float* lambda, const float* P,
+                                   const float* Q, const float* B, const float* C,
+                                   const float* dt, const float* D, const float* W,
+                                   const float* bias, float* out, void* ws, hipStream_t stream);
 
 /* Release a plan (NULL is ignored).  Host-only. */
 void s4dplr_plan_destroy(s4dplr_plan* plan);

@@ -527,7 +527,7 @@ def glu_projection(s, W, bias):
     s = np.asarray(s, np.float64)
     W = np.asarray(W, np.float64)
     H = s.shape[1]
-    z = np.einsum("oh,bhl->bol", W, s) + np.asarray(bias, np.float64)[None, :, None]
+    z = np.matmul(W[None], s) + np.asarray(bias, np.float64)[None, :, None]
     a, g = z[:, :H], z[:, H:]
     return a / (1.0 + np.exp(-g))
 

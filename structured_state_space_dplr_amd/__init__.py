@@ -17,15 +17,17 @@ import os
 import torch  # loads the HIP runtime that libs4dplr then shares
 
 __all__ = [
-    "S4DPLRError", "DIAGONAL", "ZOH", "abi_version", "status_string", "plan_create",
+    "S4DPLRError", "DIAGONAL", "ZOH", "BLOCK", "abi_version", "status_string", "plan_create",
     "plan_workspace_bytes", "plan_init", "kernel_gen", "conv_fwd", "forward",
     "conv_apply", "recurrent_prepare", "recurrent_scan", "conv_bwd", "kernel_gen_bwd",
+    "block_forward",
     "plan_destroy", "Plan", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libs4dplr.so")
 DIAGONAL = 1
 ZOH = 2
+BLOCK = 4
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -64,6 +66,8 @@ _lib.s4dplr_conv_bwd.restype = ctypes.c_int
 _lib.s4dplr_conv_bwd.argtypes = [_p] * 10
 _lib.s4dplr_kernel_gen_bwd.restype = ctypes.c_int
 _lib.s4dplr_kernel_gen_bwd.argtypes = [_p] * 16
+_lib.s4dplr_block_forward.restype = ctypes.c_int
+_lib.s4dplr_block_forward.argtypes = [_p] * 16
 _lib.s4dplr_plan_destroy.restype = None
 _lib.s4dplr_plan_destroy.argtypes = [_p]
 
@@ -213,6 +217,18 @@ def kernel_gen_bwd(plan: "Plan | int", lam, P, Q, B, C, dt, dK, dlam, dP, dQ, dB
         _stream(stream)), "kernel_gen_bwd")
 
 
+def block_forward(plan: "Plan | int", x, gamma, beta, lam, P, Q, B, C, dt, D, W, bias, out, ws,
+                  stream=None) -> None:
+    p, (H, N, L, batch) = _dims(plan)
+    cplx = (H, N, 2)
+    _check(_lib.s4dplr_block_forward(
+        p, _ptr(x, "x", (batch, H, L)), _ptr(gamma, "gamma", (H,)), _ptr(beta, "beta", (H,)),
+        _ptr(lam, "lam", cplx), _ptr(P, "P", cplx), _ptr(Q, "Q", cplx), _ptr(B, "B", cplx),
+        _ptr(C, "C", cplx), _ptr(dt, "dt", (H,)), _ptr(D, "D", (H,)), _ptr(W, "W", (2 * H, H)),
+        _ptr(bias, "bias", (2 * H,)), _ptr(out, "out", (batch, H, L)), _ws_ptr(ws),
+        _stream(stream)), "block_forward")
+
+
 def _dims(plan):
     if isinstance(plan, Plan):
         return plan.handle, (plan.H, plan.N, plan.L, plan.batch)
@@ -223,11 +239,11 @@ class Plan:
     """Owns a plan handle and (optionally) a workspace tensor on one device."""
 
     def __init__(self, H: int, N: int, L: int, batch: int, diagonal: bool = False,
-                 device=None, zoh: bool = False):
+                 device=None, zoh: bool = False, block: bool = False):
         self.H, self.N, self.L, self.batch = H, N, L, batch
-        self.diagonal, self.zoh = diagonal, zoh
-        self.handle = plan_create(H, N, L, batch,
-                                  (DIAGONAL if diagonal else 0) | (ZOH if zoh else 0))
+        self.diagonal, self.zoh, self.block = diagonal, zoh, block
+        self.handle = plan_create(H, N, L, batch, (DIAGONAL if diagonal else 0)
+                                  | (ZOH if zoh else 0) | (BLOCK if block else 0))
         self.workspace_bytes = plan_workspace_bytes(self.handle)
         self.device = torch.device("cuda" if device is None else device)
         self._ws_store = None

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libs4dplr.so")
-SOURCES = ["kernels.hip", "big.hip", "recurrent.hip", "backward.hip", "vandermonde.hip", "api.cpp"]
+SOURCES = ["kernels.hip", "big.hip", "recurrent.hip", "backward.hip", "vandermonde.hip", "block.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

@@ -111,7 +111,7 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
                                  unsigned flags) {
   if (!out) return S4DPLR_ERR_NULL;
   *out = nullptr;
-  if (flags & ~(S4DPLR_DIAGONAL | S4DPLR_ZOH)) return S4DPLR_ERR_UNSUPPORTED;
+  if (flags & ~(S4DPLR_DIAGONAL | S4DPLR_ZOH | S4DPLR_BLOCK)) return S4DPLR_ERR_UNSUPPORTED;
   if ((flags & S4DPLR_ZOH) && !(flags & S4DPLR_DIAGONAL)) return S4DPLR_ERR_UNSUPPORTED;
   const bool zoh = (flags & S4DPLR_ZOH) != 0;
   if (H < 1 || batch < 1 || N < 1 || N > 256) return S4DPLR_ERR_SHAPE;
@@ -180,6 +180,10 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
     }
     off = align_up(off + need);
   }
+  p->off_bz = off;
+  if (flags & S4DPLR_BLOCK) off = align_up(off + sizeof(float) * (size_t)batch * H * L);
+  p->off_bs = off;
+  if (flags & S4DPLR_BLOCK) off = align_up(off + sizeof(float) * (size_t)batch * H * L);
   p->total = off;
 
   // fp64 tables, rounded once to fp32.
@@ -410,6 +414,40 @@ s4dplr_status s4dplr_kernel_gen_bwd(const s4dplr_plan* p, const float* lambda, c
                                                  dB, dC, ddt, static_cast<unsigned char*>(ws),
                                                  stream);
   if (e != hipSuccess) return hip_fail(e);
+  return S4DPLR_OK;
+}
+
+s4dplr_status s4dplr_block_forward(const s4dplr_plan* p, const float* x, const float* gamma,
+                                   const float* beta, const float* lambda, const float* P,
+                                   const float* Q, const float* B, const float* C,
+                                   const float* dt, const float* D, const float* W,
+                                   const float* bias, float* out, void* ws, hipStream_t stream) {
+  if (!valid_plan(p)) return S4DPLR_ERR_NULL;
+  if (s4dplr_status st = check_params(p, lambda, P, B, C, dt)) return st;
+  if (!x || !gamma || !beta || !W || !bias || !out) return S4DPLR_ERR_NULL;
+  if (s4dplr_status st = check_ws(ws)) return st;
+  if (!(p->flags & S4DPLR_BLOCK)) return S4DPLR_ERR_UNSUPPORTED;
+  if (p->batch > 65535) return S4DPLR_ERR_SHAPE;   // one grid row per batch row
+  const size_t ub = sizeof(float) * (size_t)p->batch * p->H * p->L;
+  const size_t hb = sizeof(float) * (size_t)p->H;
+  const size_t cb = 2 * sizeof(float) * (size_t)p->H * p->N;
+  const size_t wb = 2 * sizeof(float) * (size_t)p->H * p->H;
+  if (out != x && overlaps(out, ub, x, ub)) return S4DPLR_ERR_ALIAS;
+  const void* ins[] = {gamma, beta, lambda, P, Q, B, C, dt, D, W, bias};
+  const size_t inb[] = {hb, hb, cb, cb, cb, cb, cb, hb, hb, wb, 2 * hb};
+  for (int i = 0; i < 11; ++i)
+    if (overlaps(out, ub, ins[i], inb[i])) return S4DPLR_ERR_ALIAS;
+  if (overlaps(out, ub, ws, p->total) || overlaps(x, ub, ws, p->total)) return S4DPLR_ERR_ALIAS;
+  unsigned char* w = static_cast<unsigned char*>(ws);
+  float* z = reinterpret_cast<float*>(w + p->off_bz);
+  float* sv = reinterpret_cast<float*>(w + p->off_bs);
+  hipError_t e;
+  if ((e = s4::launch_layer_norm(p, x, gamma, beta, z, stream)) != hipSuccess) return hip_fail(e);
+  if ((e = s4::launch_kernel_gen(p, lambda, P, Q, B, C, dt, D, nullptr, w, stream)) != hipSuccess)
+    return hip_fail(e);
+  if ((e = s4::launch_conv(p, z, sv, w, stream)) != hipSuccess) return hip_fail(e);
+  if ((e = s4::launch_block_epilogue(p, x, sv, W, bias, out, stream)) != hipSuccess)
+    return hip_fail(e);
   return S4DPLR_OK;
 }
 

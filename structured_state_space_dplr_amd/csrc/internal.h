@@ -36,6 +36,8 @@ struct s4dplr_plan {
   size_t off_bbeta;  // [H][L] x 2 float4: conj(dKhat/dk_ab) * Ghat per frequency
   size_t off_bpart;  // partial sums: correlation spectra [ceil(B/kCorrRows)][H][L+1] float2,
                      // or per-pole sums [H][ceil(L/kBwdChunk)][N] x 6 float2
+  size_t off_bz;     // block (S4DPLR_BLOCK): [batch][H][L] float normalized input
+  size_t off_bs;     // block (S4DPLR_BLOCK): [batch][H][L] float layer output
   size_t total;
   std::vector<unsigned char> tables;  // exact bytes of the table region
 };
@@ -90,6 +92,12 @@ hipError_t launch_vandermonde_bwd(const s4dplr_plan* p, const float* lam, const 
                                   const float* C, const float* dt, const float* dK, float* dlam,
                                   float* dB, float* dC, float* ddt, unsigned char* ws,
                                   hipStream_t s);
+// The block: layer norm over channels into z, and the fused GLU projection
+// with bias and residual.
+hipError_t launch_layer_norm(const s4dplr_plan* p, const float* x, const float* gamma,
+                             const float* beta, float* z, hipStream_t s);
+hipError_t launch_block_epilogue(const s4dplr_plan* p, const float* x, const float* s,
+                                 const float* W, const float* bias, float* out, hipStream_t st);
 // Work split of the scan: poles per lane (1, 2, 4 or 8) and log2 of the lanes
 // per sequence (0..5), chosen from N and the number of sequences.
 void recurrent_shape(int N, long rows, int* ppl, int* log2g);

@@ -24,7 +24,7 @@ int main() {
   const int Ns[] = {1, 3, 64, 256};
   for (int L : Ls)
     for (int N : Ns)
-      for (unsigned flags : {0u, 1u, 3u}) {
+      for (unsigned flags : {0u, 1u, 3u, 4u}) {
         s4dplr_plan* p = nullptr;
         CHECK(s4dplr_plan_create(&p, 3, N, L, 2, flags) == S4DPLR_OK && p);
         size_t bytes = 0;
@@ -61,6 +61,11 @@ int main() {
         }
         CHECK(s4dplr_recurrent_scan(p, nullptr, u, 7, K, y, ws, nullptr) == S4DPLR_OK);
         CHECK(s4dplr_recurrent_scan(p, nullptr, u, 7, K, u, ws, nullptr) == S4DPLR_ERR_ALIAS);
+        if (flags & S4DPLR_BLOCK) {
+          float* xo = reinterpret_cast<float*>(base + 7 * gap);
+          CHECK(s4dplr_block_forward(p, xo, f, f, f, f, nullptr, f, f, f, nullptr, f, f, xo, ws,
+                                     nullptr) == S4DPLR_OK);
+        }
         CHECK(stub_launch_count() > before);
         CHECK(s4dplr_forward(p, f, f, nullptr, f, f, f, nullptr, u, nullptr, u, ws, nullptr) == S4DPLR_ERR_ALIAS);
         CHECK(s4dplr_conv_fwd(p, u, K, nullptr, y, nullptr, nullptr) == S4DPLR_ERR_NULL);

@@ -35,6 +35,7 @@ def lib():
     L.s4dplr_recurrent_scan.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp]
     L.s4dplr_conv_bwd.argtypes = [vp] * 10
     L.s4dplr_kernel_gen_bwd.argtypes = [vp] * 16
+    L.s4dplr_block_forward.argtypes = [vp] * 16
     L.s4dplr_plan_destroy.argtypes = [vp]
     L.s4dplr_status_string.restype = ctypes.c_char_p
     return L
@@ -52,7 +53,8 @@ def test_header_declares_the_boundary():
               "s4dplr_plan_workspace_bytes", "s4dplr_plan_init", "s4dplr_kernel_gen",
               "s4dplr_conv_fwd", "s4dplr_forward", "s4dplr_plan_destroy",
               "s4dplr_last_hip_error", "s4dplr_conv_apply", "s4dplr_recurrent_prepare",
-              "s4dplr_recurrent_scan", "s4dplr_conv_bwd", "s4dplr_kernel_gen_bwd"]:
+              "s4dplr_recurrent_scan", "s4dplr_conv_bwd", "s4dplr_kernel_gen_bwd",
+              "s4dplr_block_forward"]:
         assert n in names
 
 
@@ -92,7 +94,8 @@ def _create(lib, H, N, L, B, flags=0):
     (4096, 16, 65536, 16, 0, ERR_SHAPE),     # batch*H*L >= 2^31
     (4, 16, 256, 2, 3, OK),                  # diagonal + zero-order hold
     (4, 16, 256, 2, 2, ERR_UNSUPPORTED),     # zero-order hold needs the diagonal flag
-    (4, 16, 256, 2, 4, ERR_UNSUPPORTED),
+    (4, 16, 256, 2, 4, OK),                  # block buffers
+    (4, 16, 256, 2, 8, ERR_UNSUPPORTED),
 ])
 def test_plan_create_validation(lib, H, N, L, B, flags, expect):
     st, h = _create(lib, H, N, L, B, flags)
@@ -264,3 +267,25 @@ def test_backward_validation(lib):
     assert lib.s4dplr_conv_bwd(h2, u, K, None, dy, du, None, None, ws, None) == ERR_UNSUPPORTED
     assert lib.s4dplr_kernel_gen_bwd(h2, *prm, dKi, *outs, ws, None) == ERR_UNSUPPORTED
     lib.s4dplr_plan_destroy(h2)
+
+
+def test_block_validation(lib):
+    H, N, L, B = 4, 16, 256, 2
+    st, h = _create(lib, H, N, L, B)                 # no block flag
+    st, hb = _create(lib, H, N, L, B, flags=4)
+    ws = 1 << 32
+    f = 1 << 20
+    x = 1 << 24
+    ub = 4 * B * H * L
+    args = lambda out: [x, f, f, f, f, None, f, f, f, None, f, f, out, ws, None]
+    assert lib.s4dplr_block_forward(h, *args(x + ub)) == ERR_UNSUPPORTED
+    assert lib.s4dplr_block_forward(hb, *args(None)) == ERR_NULL
+    a = args(x + ub)
+    a[1] = None                                      # gamma
+    assert lib.s4dplr_block_forward(hb, *a) == ERR_NULL
+    # out may be x itself, but not a shifted view of it, an input or the workspace
+    assert lib.s4dplr_block_forward(hb, *args(x + 4)) == ERR_ALIAS
+    assert lib.s4dplr_block_forward(hb, *args(f)) == ERR_ALIAS
+    assert lib.s4dplr_block_forward(hb, *args(ws + 256)) == ERR_ALIAS
+    lib.s4dplr_plan_destroy(h)
+    lib.s4dplr_plan_destroy(hb)
