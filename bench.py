@@ -279,6 +279,23 @@ def main() -> int:
            "note": "Vandermonde kernel plus the spectrum of K padded to 2L"}
     zplan.close()
 
+    # ---- the block around the layer: layer norm, the layer, GLU projection ------
+    from synth import make_block_params
+    bp = {k: g(v) for k, v in make_block_params(w.H, seed=1).items()}
+    bplan = s4.Plan(w.H, w.N, w.L, w.batch, diagonal=w.diagonal, device=dev, block=True)
+    bws = bplan.workspace()
+    t_blk = timed(lambda i: s4.block_forward(
+        bplan, us[i % nsets], bp["gamma"], bp["beta"], params["lam"], P, params["Q"],
+        params["B"], params["C"], params["dt"], params["D"], bp["W"], bp["bias"],
+        ys[i % nsets], bws, stream), args.steps)
+    f_proj = 2 * (2 * w.H) * w.H * w.batch * w.L        # the projection GEMM
+    log(f"[bench] block forward {t_blk * 1e6:.1f} us ({samples / t_blk:.3g} samples/s; "
+        f"projection {f_proj / 1e9:.2f} GFLOP)")
+    block = {"us": t_blk * 1e6, "samples_per_s": samples / t_blk,
+             "projection_flops": f_proj,
+             "note": "layer norm + layer + fp32-MFMA GLU projection with residual"}
+    bplan.close()
+
     # ---- the backward pass (L <= 16384): conv_bwd and kernel_gen_bwd ----------
     bwd = None
     if w.L <= 16384:
@@ -370,6 +387,7 @@ def main() -> int:
         },
         "backward": bwd,
         "zoh": zoh,
+        "block": block,
         "forward_us_events": fwd_ms_events * 1e3,
         "cpu_baseline": None,
     }
