@@ -219,8 +219,7 @@ s4dplr_status s4dplr_recurrent_scan(const s4dplr_plan* plan, const float* D, con
  * accumulated, and must not overlap the inputs, each other or the workspace
  * (ERR_ALIAS).  Computing du replaces the convolution weights held in the
  * workspace (a later s4dplr_conv_apply then applies the correlation).
- * Supported for L <= 16384 (ERR_UNSUPPORTED above).
- * Errors: ERR_NULL, ERR_ALIAS, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP.
+ * Errors: ERR_NULL, ERR_ALIAS, ERR_WORKSPACE, ERR_HIP.
  */
 s4dplr_status s4dplr_conv_bwd(const s4dplr_plan* plan, const float* u, const float* K,
                               const float* D, const float* dy, float* du, float* dK, float* dD,
@@ -236,8 +235,7 @@ s4dplr_status s4dplr_conv_bwd(const s4dplr_plan* plan, const float* u, const flo
  * dQ is ignored.  With S4DPLR_DIAGONAL, dP and dQ are ignored.  Every output
  * may be NULL (not written); outputs are overwritten, not accumulated, and
  * must not overlap the inputs, each other or the workspace (ERR_ALIAS).
- * Supported for L <= 16384 (ERR_UNSUPPORTED above).
- * Errors: ERR_NULL, ERR_ALIAS, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP.
+ * Errors: ERR_NULL, ERR_ALIAS, ERR_WORKSPACE, ERR_HIP.
  */
 s4dplr_status s4dplr_kernel_gen_bwd(const s4dplr_plan* plan, const float* lambda, const float* P,
                                     const float* Q, const float* B, const float* C,

@@ -156,23 +156,24 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
   if (!lds || zoh) off = align_up(off + sizeof(float) * (size_t)H * L);
   p->off_big = off;
   if (!lds) off = align_up(off + sizeof(float) * 2 * (size_t)batch * H * L);
+  p->off_big2 = off;
+  if (!lds) off = align_up(off + sizeof(float) * 2 * (size_t)batch * H * L);
   p->off_rrec = off;
   off = align_up(off + sizeof(float) * 16 * (size_t)H * N);
   p->off_rchan = off;
   off = align_up(off + sizeof(float) * 4 * (size_t)H);
   p->off_bghat = off;
-  if (lds) off = align_up(off + sizeof(float) * 2 * (size_t)H * L);
+  off = align_up(off + sizeof(float) * 2 * (size_t)H * L);
   p->off_bbeta = off;
-  if (lds) off = align_up(off + sizeof(float) * 8 * (size_t)H * L);
+  off = align_up(off + sizeof(float) * 8 * (size_t)H * L);
   p->off_bpart = off;
   {
     const size_t nchunks = (L + s4::kBwdChunk - 1) / s4::kBwdChunk;
-    size_t need = 0;
+    size_t need = sizeof(float) * 12 * (size_t)H * nchunks * N;   // per-pole sums
     if (lds) {
       const size_t corr = sizeof(float) * 2 *
                           (size_t)((batch + s4::kCorrRows - 1) / s4::kCorrRows) * H * (L + 1);
-      const size_t pole = sizeof(float) * 12 * (size_t)H * nchunks * N;
-      need = corr > pole ? corr : pole;
+      if (corr > need) need = corr;
     }
     if (zoh) {
       const size_t vpart = sizeof(float) * 4 * (size_t)H * nchunks * N;
@@ -353,7 +354,6 @@ s4dplr_status s4dplr_conv_bwd(const s4dplr_plan* p, const float* u, const float*
   if (du && !K) return S4DPLR_ERR_NULL;
   if ((dK || dD) && !u) return S4DPLR_ERR_NULL;
   if (s4dplr_status st = check_ws(ws)) return st;
-  if (!s4::lds_path(p)) return S4DPLR_ERR_UNSUPPORTED;
   const size_t ub = sizeof(float) * (size_t)p->batch * p->H * p->L;
   const size_t kb = sizeof(float) * (size_t)p->H * p->L;
   const size_t db = sizeof(float) * (size_t)p->H;
@@ -388,7 +388,6 @@ s4dplr_status s4dplr_kernel_gen_bwd(const s4dplr_plan* p, const float* lambda, c
   if (!dK) return S4DPLR_ERR_NULL;
   if (s4dplr_status st = check_ws(ws)) return st;
   const bool zoh = (p->flags & S4DPLR_ZOH) != 0;
-  if (!zoh && !s4::lds_path(p)) return S4DPLR_ERR_UNSUPPORTED;
   const bool diag = (p->flags & S4DPLR_DIAGONAL) != 0;
   if (diag) dP = dQ = nullptr;
   if (!Q) dQ = nullptr;

@@ -504,6 +504,7 @@ void ghat_launch(const s4dplr_plan* p, const float* dK, unsigned char* ws, hipSt
 
 hipError_t launch_corr(const s4dplr_plan* p, const float* u, const float* dy, float* dK,
                        float* dD, unsigned char* ws, hipStream_t s) {
+  if (!lds_path(p)) return launch_big_corr(p, u, dy, dK, dD, ws, s);
   S4_BWD_DISPATCH(corr_launch, p, u, dy, dK, dD, ws, s);
   return hipGetLastError();
 }
@@ -520,7 +521,12 @@ hipError_t launch_kernel_gen_bwd(const s4dplr_plan* p, const float* lam, const f
   pp.B = reinterpret_cast<const float2*>(B);
   pp.C = reinterpret_cast<const float2*>(C);
   pp.dt = dt;
-  S4_BWD_DISPATCH(ghat_launch, p, dK, ws, s);
+  if (!lds_path(p)) {
+    const hipError_t e = launch_big_ghat(p, dK, ws, s);
+    if (e != hipSuccess) return e;
+  } else {
+    S4_BWD_DISPATCH(ghat_launch, p, dK, ws, s);
+  }
   const float* tanT = at<const float>(ws, p->off_tan);
   const float2* ghat = at<const float2>(ws, p->off_bghat);
   float4* beta = at<float4>(ws, p->off_bbeta);

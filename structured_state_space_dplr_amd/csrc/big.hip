@@ -354,6 +354,164 @@ static void big_conv(const s4dplr_plan* p, const float* u, float* y, unsigned ch
       Y, y, wat<const float2>(ws, p->off_tw1), p->H, p->batch);
 }
 
+// ---------------------------------------------------------------------------
+// Backward pass for the long path.  Row step of the forward transform alone:
+// Z[k1][k2] = sum_{n2} Y[k1][n2] W_M2^{n2 k2}, in place (the column step has
+// already applied the twiddle), leaving bin k1 + M1 k2 at k1 M2 + k2.
+// ---------------------------------------------------------------------------
+template <int LOG2M>
+__global__ __launch_bounds__(kBigThreads) void big_rows_fwd_kernel(
+    float2* __restrict__ Y, const float2* __restrict__ tw2) {
+  using S = BigShape<LOG2M>;
+  constexpr int M = S::M, M2 = S::M2, RT = S::RT, RP = S::RP;
+  __shared__ float2 lds[RT * RP];
+  const int tid = threadIdx.x, row = blockIdx.y, r0 = blockIdx.x * RT;
+  float2* __restrict__ Yr = Y + (size_t)row * M;
+  for (int idx = tid; idx < RT * M2; idx += kBigThreads) {
+    const int s = idx / M2, n2 = idx % M2;
+    lds[s * RP + lds_pad(n2)] = Yr[(r0 + s) * M2 + n2];
+  }
+  __syncthreads();
+  lds_fft<S::LOG2M2, false>(lds + (tid / 16) * RP, tid % 16, true, tw2);
+  for (int idx = tid; idx < RT * M2; idx += kBigThreads) {
+    const int s = idx / M2, k2 = idx % M2;
+    Yr[(r0 + s) * M2 + k2] = lds[s * RP + lds_pad(k2)];
+  }
+}
+
+// position of bin k in the permuted layout
+template <int LOG2M>
+__device__ __forceinline__ int big_pos(int k) {
+  using S = BigShape<LOG2M>;
+  return (k & (S::M1 - 1)) * S::M2 + (k >> S::LOG2M1);
+}
+
+// dK: per channel h and bin pair (k, M - k), k in [0, M/2], the batch sum
+// S_j = sum_b conj(U_j) G_j of the spectra of the zero-padded u and dy rows
+// (X_j = big_rfft_x(Z_j, Z_{M-j}), Z_M = Z_0), then the packed inverse input
+//   W_k = (S_k + conj S_{M-k}) / 2 + i e^{i pi k/M} (S_k - conj S_{M-k}) / 2
+// for k and M - k, scaled by 1/M, in the permuted layout (k = 0 pairs with the
+// bin M of the real transform).
+template <int LOG2M>
+__global__ __launch_bounds__(kBigThreads) void big_corr_kernel(
+    const float2* __restrict__ Zu, const float2* __restrict__ Zg, float2* __restrict__ W,
+    const float2* __restrict__ cs, int batch) {
+  using S = BigShape<LOG2M>;
+  constexpr int M = S::M;
+  const int h = blockIdx.y;
+  const int k = blockIdx.x * kBigThreads + threadIdx.x;
+  if (k > M / 2) return;
+  const int km = M - k;                       // in [M/2, M]
+  const int pk = big_pos<LOG2M>(k), pm = big_pos<LOG2M>(km & (M - 1));
+  const float2 ck = cs[k], cm = cs[km];
+  float2 sk = make_float2(0.f, 0.f), sm = sk;
+  for (int b = 0; b < batch; ++b) {
+    const size_t r = ((size_t)h * batch + b) * M;
+    const float2 uk = Zu[r + pk], um = Zu[r + pm], gk = Zg[r + pk], gm = Zg[r + pm];
+    const float2 Uk = big_rfft_x(uk, um, ck), Gk = big_rfft_x(gk, gm, ck);
+    const float2 Um = big_rfft_x(um, uk, cm), Gm = big_rfft_x(gm, gk, cm);
+    sk = cadd(sk, cmul(cconj(Uk), Gk));
+    sm = cadd(sm, cmul(cconj(Um), Gm));
+  }
+  const float sc = 0.5f / (float)M;
+  // W_k = (S_k + conj S_m)/2 + i e^{i pi k/M} (S_k - conj S_m)/2, scaled by 1/M
+  const float2 ek = make_float2(sk.x + sm.x, sk.y - sm.y);
+  const float2 dk = make_float2(sk.x - sm.x, sk.y + sm.y);
+  const float2 wk = cadd(ek, cmul(make_float2(-ck.y, ck.x), dk));
+  float2* __restrict__ Wh = W + (size_t)h * M;
+  Wh[pk] = make_float2(sc * wk.x, sc * wk.y);
+  if (k != 0 && km != k) {
+    const float2 em = make_float2(sm.x + sk.x, sm.y - sk.y);
+    const float2 dm = make_float2(sm.x - sk.x, sm.y + sk.y);
+    const float2 wm = cadd(em, cmul(make_float2(-cm.y, cm.x), dm));
+    Wh[pm] = make_float2(sc * wm.x, sc * wm.y);
+  }
+}
+
+// Ghat_l = FFT_L(dK)_l / L = X_{2l} / L, X the spectrum of dK zero-padded to
+// 2L (from Z in the permuted layout); X_{2M - j} = conj(X_j).
+template <int LOG2M>
+__global__ __launch_bounds__(kBigThreads) void big_ghat_kernel(
+    const float2* __restrict__ Z, float2* __restrict__ ghat, const float2* __restrict__ cs) {
+  using S = BigShape<LOG2M>;
+  constexpr int M = S::M;
+  const int h = blockIdx.y;
+  const int l = blockIdx.x * kBigThreads + threadIdx.x;
+  if (l >= M) return;
+  int j = 2 * l;
+  const bool mirror = j > M;
+  if (mirror) j = 2 * M - j;
+  const float2* __restrict__ Zh = Z + (size_t)h * M;
+  const float2 zj = Zh[big_pos<LOG2M>(j & (M - 1))], zm = Zh[big_pos<LOG2M>((M - j) & (M - 1))];
+  float2 x = big_rfft_x(zj, zm, cs[j]);
+  if (mirror) x = cconj(x);
+  const float inv = 1.0f / (float)M;
+  ghat[(size_t)h * M + l] = make_float2(x.x * inv, x.y * inv);
+}
+
+__global__ void big_first_col_kernel(const float* __restrict__ K, float* __restrict__ d, int H,
+                                     int L) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h < H) d[h] = K[(size_t)h * L];
+}
+
+template <int LOG2M>
+static void big_corr(const s4dplr_plan* p, const float* u, const float* dy, float* dK, float* dD,
+                     unsigned char* ws, hipStream_t s) {
+  using S = BigShape<LOG2M>;
+  const int rows = p->batch * p->H;
+  float2* Yu = wat<float2>(ws, p->off_big);
+  float2* Yg = wat<float2>(ws, p->off_big2);
+  const float2* tw1 = wat<const float2>(ws, p->off_tw1);
+  const float2* tw2 = wat<const float2>(ws, p->off_tw2);
+  const float2* tw4 = wat<const float2>(ws, p->off_tw4);
+  const float2* cs = wat<const float2>(ws, p->off_cs);
+  const dim3 cgrid(S::M2 / S::CT, rows), rgrid(S::M1 / S::RT, rows);
+  big_conv_cols_fwd_kernel<LOG2M><<<cgrid, kBigThreads, 0, s>>>(u, Yu, tw1, tw4, p->H, p->batch);
+  big_conv_cols_fwd_kernel<LOG2M><<<cgrid, kBigThreads, 0, s>>>(dy, Yg, tw1, tw4, p->H, p->batch);
+  big_rows_fwd_kernel<LOG2M><<<rgrid, kBigThreads, 0, s>>>(Yu, tw2);
+  big_rows_fwd_kernel<LOG2M><<<rgrid, kBigThreads, 0, s>>>(Yg, tw2);
+  float2* Wb = wat<float2>(ws, p->off_khat);
+  big_corr_kernel<LOG2M><<<dim3((S::M / 2 + kBigThreads) / kBigThreads, p->H), kBigThreads, 0,
+                           s>>>(Yu, Yg, Wb, cs, p->batch);
+  // inverse: rows then columns, the first M/2 outputs as (c_2n, c_2n+1)
+  float* out = dK ? dK : wat<float>(ws, p->off_kbuf);
+  big_rows_inv_kernel<LOG2M><<<dim3(S::M1 / S::RT, p->H), kBigThreads, 0, s>>>(Wb, Yu, tw2, tw4);
+  big_cols_inv_kernel<LOG2M, 0><<<dim3(S::M2 / S::CT, p->H), kBigThreads, 0, s>>>(Yu, out, tw1,
+                                                                                 1.0f);
+  if (dD) big_first_col_kernel<<<(p->H + 255) / 256, 256, 0, s>>>(out, dD, p->H, p->L);
+}
+
+template <int LOG2M>
+static void big_ghat(const s4dplr_plan* p, const float* dK, float2* ghat, unsigned char* ws,
+                     hipStream_t s) {
+  using S = BigShape<LOG2M>;
+  float2* Y = wat<float2>(ws, p->off_big);
+  big_cols_fwd_kernel<LOG2M><<<dim3(S::M2 / S::CT, p->H), kBigThreads, 0, s>>>(
+      dK, Y, wat<const float2>(ws, p->off_tw1), wat<const float2>(ws, p->off_tw4));
+  big_rows_fwd_kernel<LOG2M><<<dim3(S::M1 / S::RT, p->H), kBigThreads, 0, s>>>(
+      Y, wat<const float2>(ws, p->off_tw2));
+  big_ghat_kernel<LOG2M><<<dim3(S::M / kBigThreads, p->H), kBigThreads, 0, s>>>(
+      Y, ghat, wat<const float2>(ws, p->off_cs));
+}
+
+hipError_t launch_big_corr(const s4dplr_plan* p, const float* u, const float* dy, float* dK,
+                           float* dD, unsigned char* ws, hipStream_t s) {
+  if (p->log2L == 15) big_corr<15>(p, u, dy, dK, dD, ws, s);
+  else if (p->log2L == 16) big_corr<16>(p, u, dy, dK, dD, ws, s);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_big_ghat(const s4dplr_plan* p, const float* dK, unsigned char* ws,
+                           hipStream_t s) {
+  float2* ghat = wat<float2>(ws, p->off_bghat);
+  if (p->log2L == 15) big_ghat<15>(p, dK, ghat, ws, s);
+  else if (p->log2L == 16) big_ghat<16>(p, dK, ghat, ws, s);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 hipError_t launch_big_conv(const s4dplr_plan* p, const float* u, float* y, unsigned char* ws,
                            hipStream_t s) {
   if (p->log2L == 15) big_conv<15>(p, u, y, ws, s);

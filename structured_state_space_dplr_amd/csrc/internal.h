@@ -29,9 +29,10 @@ struct s4dplr_plan {
   size_t off_coef;   // [H][L] float4: spectral weights (alpha, beta) of bin j
   size_t off_kbuf;   // [H][L] float time-domain kernel when not written out (long path, ZOH)
   size_t off_big;    // long path: [batch*H][L] float2 intermediate rows
+  size_t off_big2;   // long path, backward: a second [batch*H][L] float2 buffer
   size_t off_rrec;   // recurrent view: [H][N] x 4 float4 per-pole step records
   size_t off_rchan;  // recurrent view: [H] float4 per-channel sums (S1, S2)
-  // Backward pass (L <= 2^S4DPLR_LDS_MAX_LOG2L; with ZOH the partial sums for every L):
+  // Backward pass:
   size_t off_bghat;  // [H][L] float2: FFT_L(dK) / L
   size_t off_bbeta;  // [H][L] x 2 float4: conj(dKhat/dk_ab) * Ghat per frequency
   size_t off_bpart;  // partial sums: correlation spectra [ceil(B/kCorrRows)][H][L+1] float2,
@@ -65,6 +66,12 @@ hipError_t launch_conv(const s4dplr_plan* p, const float* u, float* y, unsigned 
 hipError_t launch_big_kspec(const s4dplr_plan* p, const float* Ktime, const float* D,
                             float* Kout, unsigned char* ws, hipStream_t s, int conj);
 hipError_t launch_big_conv(const s4dplr_plan* p, const float* u, float* y, unsigned char* ws,
+                           hipStream_t s);
+// Long path backward: dK, dD of the convolution, and Ghat = FFT_L(dK) / L into
+// the workspace.
+hipError_t launch_big_corr(const s4dplr_plan* p, const float* u, const float* dy, float* dK,
+                           float* dD, unsigned char* ws, hipStream_t s);
+hipError_t launch_big_ghat(const s4dplr_plan* p, const float* dK, unsigned char* ws,
                            hipStream_t s);
 
 // Recurrent view: per-pole step records from the parameters, then T steps of

@@ -68,6 +68,15 @@ hipError_t launch_block_epilogue(const s4dplr_plan*, const float*, const float*,
   ++g_launches;
   return hipSuccess;
 }
+hipError_t launch_big_corr(const s4dplr_plan*, const float*, const float*, float*, float*,
+                           unsigned char*, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
+hipError_t launch_big_ghat(const s4dplr_plan*, const float*, unsigned char*, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
 hipError_t launch_recurrent_prepare(const s4dplr_plan*, const float*, const float*,
                                     const float*, const float*, const float*, const float*,
                                     unsigned char*, hipStream_t) {

@@ -262,11 +262,6 @@ def test_backward_validation(lib):
         o[i] = target
         assert lib.s4dplr_kernel_gen_bwd(h, *prm, dKi, *o, ws, None) == ERR_ALIAS, i
     lib.s4dplr_plan_destroy(h)
-    # the backward pass is limited to L <= 16384
-    st, h2 = _create(lib, 1, 4, 32768, 1)
-    assert lib.s4dplr_conv_bwd(h2, u, K, None, dy, du, None, None, ws, None) == ERR_UNSUPPORTED
-    assert lib.s4dplr_kernel_gen_bwd(h2, *prm, dKi, *outs, ws, None) == ERR_UNSUPPORTED
-    lib.s4dplr_plan_destroy(h2)
 
 
 def test_block_validation(lib):

@@ -81,7 +81,7 @@ def check_param_grads(g, ref, label):
 
 # ---- convolution backward ---------------------------------------------------
 
-@pytest.mark.parametrize("L", [2 ** k for k in range(1, 15)])
+@pytest.mark.parametrize("L", [2 ** k for k in range(1, 17)])
 def test_conv_bwd_all_lengths(s4, L):
     print(f"case: conv_bwd L={L}", flush=True)
     rng = np.random.default_rng(L)
@@ -129,11 +129,12 @@ def test_conv_bwd_large_batch(s4):
 
 # ---- kernel generation backward -----------------------------------------------
 
-@pytest.mark.parametrize("L", [2, 4, 16, 64, 256, 1024, 2048])
+@pytest.mark.parametrize("L", [2, 4, 16, 64, 256, 1024, 2048, 32768, 65536])
 def test_kernel_gen_bwd_lengths(s4, L):
-    print(f"case: kernel_gen_bwd generic H=2 N=8 L={L}", flush=True)
-    x = make_generic_inputs(H=2, N=8, L=L, batch=1, seed=40 + L)
-    dK = np.random.default_rng(L).standard_normal((2, L)).astype(np.float32)
+    H = 2 if L <= 2048 else 1
+    print(f"case: kernel_gen_bwd generic H={H} N=8 L={L}", flush=True)
+    x = make_generic_inputs(H=H, N=8, L=L, batch=1, seed=40 + L)
+    dK = np.random.default_rng(L).standard_normal((H, L)).astype(np.float32)
     g = gpu_kernel_gen_bwd(s4, x, dK)
     ref = o.kernel_backward_dense(x["lam"], x["P"], x["Q"], x["B"], x["C"], x["dt"], dK)
     check_param_grads(g, ref, f"L={L}")
@@ -165,7 +166,7 @@ def _slice(x, hs):
     return {k: (v[hs] if isinstance(v, np.ndarray) and k != "u" else v) for k, v in x.items()}
 
 
-@pytest.mark.parametrize("name,n_ch", [("tiny", 4), ("mid", 2), ("s4d_lin", 1)])
+@pytest.mark.parametrize("name,n_ch", [("tiny", 4), ("mid", 2), ("s4d_lin", 1), ("waveform", 1)])
 def test_layer_gradients_workload(s4, name, n_ch):
     # the whole chain on the GPU: forward, then conv_bwd -> dK -> kernel_gen_bwd,
     # against the oracle's chain on sampled channels
