@@ -296,9 +296,9 @@ def main() -> int:
              "note": "layer norm + layer + fp32-MFMA GLU projection with residual"}
     bplan.close()
 
-    # ---- the backward pass (L <= 16384): conv_bwd and kernel_gen_bwd ----------
+    # ---- the backward pass: conv_bwd and kernel_gen_bwd -----------------------
     bwd = None
-    if w.L <= 16384:
+    if True:
         q_bwd, f_bwd = backward_counts(w)
         dy = ys[1 % nsets]
         du = ys[2 % nsets]

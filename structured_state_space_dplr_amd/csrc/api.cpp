@@ -171,8 +171,9 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
     const size_t nchunks = (L + s4::kBwdChunk - 1) / s4::kBwdChunk;
     size_t need = sizeof(float) * 12 * (size_t)H * nchunks * N;   // per-pole sums
     if (lds) {
+      // the partial spectra of the batch-row groups, plus one row for their sum
       const size_t corr = sizeof(float) * 2 *
-                          (size_t)((batch + s4::kCorrRows - 1) / s4::kCorrRows) * H * (L + 1);
+                          (size_t)((batch + s4::kCorrRows - 1) / s4::kCorrRows + 1) * H * (L + 1);
       if (corr > need) need = corr;
     }
     if (zoh) {

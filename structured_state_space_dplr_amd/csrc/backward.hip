@@ -205,6 +205,163 @@ __global__ __launch_bounds__(CorrShape<LOG2L>::NT) void corr_spec_kernel(
   }
 }
 
+// Wave-resident form of corr_spec_kernel for 256 <= L <= 1024: a wave takes
+// one (channel, group of kCorrRows batch rows) task, RPW = 64 / (L/16) rows
+// at a time, L/16 lanes per row with 16 points each.  Each row's a_n is loaded
+// straight into the first pass (and the next row's while the current one is
+// transformed); the pass twiddles and e^{-i pi n/L} stay in registers; LDS is
+// private to the wave, so the passes need no workgroup barrier.
+template <int LOG2M>
+struct CorrWaveShape {
+  static constexpr int M = 1 << LOG2M;
+  static constexpr int T = M / 16;
+  static constexpr int RPW = 64 / T;
+  static constexpr int P = fft_num_passes(LOG2M);
+  static constexpr int MP = lds_padded_size(M);
+  static constexpr int EPT = (M / 2 + 1 + T - 1) / T;   // even bins per lane
+  static constexpr int OPT = (M / 2 + T - 1) / T;       // odd bins per lane
+  static constexpr int ITER = (kCorrRows + RPW - 1) / RPW;
+  static_assert(LOG2M >= 8 && LOG2M <= 10, "wave-resident correlation range");
+};
+
+template <int LOG2M>
+__device__ __forceinline__ void wave_fwd_transform(float2 (&v)[16], float2* __restrict__ buf,
+                                                   int lt, const float2 (&w1)[16],
+                                                   const float2 (&w2)[16]) {
+  constexpr int P = fft_num_passes(LOG2M);
+  WPass<LOG2M, 0>::template compute<false>(v, w1);     // span 1: no twiddles
+  WPass<LOG2M, 0>::store(v, buf, lt);
+  wave_sync();
+  WPass<LOG2M, 1>::load(v, buf, lt);
+  WPass<LOG2M, 1>::template compute<false>(v, w1);
+  WPass<LOG2M, 1>::store(v, buf, lt);
+  wave_sync();
+  if constexpr (P > 2) {
+    WPass<LOG2M, 2>::load(v, buf, lt);
+    WPass<LOG2M, 2>::template compute<false>(v, w2);
+    WPass<LOG2M, 2>::store(v, buf, lt);
+    wave_sync();
+  }
+}
+
+template <int LOG2M>
+__global__ __launch_bounds__(256) void corr_wave_kernel(
+    const float* __restrict__ u, const float* __restrict__ dy, float2* __restrict__ part,
+    const float2* __restrict__ tw, const float2* __restrict__ cs, int H, int batch, int nparts) {
+  using S = CorrWaveShape<LOG2M>;
+  constexpr int M = S::M, T = S::T, RPW = S::RPW;
+  __shared__ float2 lds[4 * RPW * S::MP];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rw = lane / T, lt = lane % T;
+  float2* buf = lds + (wave * RPW + rw) * S::MP;
+  const int task = blockIdx.x * 4 + wave;
+  if (task >= H * nparts) return;                  // the whole wave leaves together
+  const int h = task / nparts, c = task - h * nparts;
+  const int b_first = c * kCorrRows, b_end = min(batch, b_first + kCorrRows);
+  float2 w1[16], w2[16], wo[16];
+  WPass<LOG2M, 1>::load_tw(w1, tw, lt);
+  if constexpr (S::P > 2) WPass<LOG2M, 2>::load_tw(w2, tw, lt);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float2 cw = cs[lt + T * r];                // e^{-i pi n/M} = conj(cs[n])
+    wo[r] = make_float2(cw.x, -cw.y);
+  }
+  float2 acce[S::EPT], acco[S::OPT];
+#pragma unroll
+  for (int i = 0; i < S::EPT; ++i) acce[i] = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int i = 0; i < S::OPT; ++i) acco[i] = make_float2(0.f, 0.f);
+  auto corr = [](float2 xk, float2 xp) {
+    const float2 cx = cconj(xp);
+    const float2 U = make_float2(0.5f * (xk.x + cx.x), 0.5f * (xk.y + cx.y));
+    const float2 Gi = make_float2(0.5f * (xk.x - cx.x), 0.5f * (xk.y - cx.y));   // i G
+    return cmul(cconj(U), make_float2(Gi.y, -Gi.x));
+  };
+  float2 nxt[16];
+  auto load_row = [&](int it) {
+    const int b = b_first + it * RPW + rw;
+    const bool ok = b < b_end;
+    const size_t row = ((size_t)(ok ? b : b_first) * H + h) * M;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int n = lt + T * r;
+      nxt[r] = ok ? make_float2(u[row + n], dy[row + n]) : make_float2(0.f, 0.f);
+    }
+  };
+  load_row(0);
+#pragma unroll 1
+  for (int it = 0; it < S::ITER; ++it) {
+    float2 a[16], v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) a[r] = v[r] = nxt[r];
+    if (it + 1 < S::ITER) load_row(it + 1);
+    // even bins: A = DFT_M(a)
+    wave_fwd_transform<LOG2M>(v, buf, lt, w1, w2);
+#pragma unroll
+    for (int i = 0; i < S::EPT; ++i) {
+      const int k = lt + T * i;
+      if (k <= M / 2)
+        acce[i] = cadd(acce[i], corr(buf[lds_pad(k & (M - 1))], buf[lds_pad((M - k) & (M - 1))]));
+    }
+    wave_sync();
+    // odd bins: B = DFT_M(a_n e^{-i pi n/M})
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = cmul(a[r], wo[r]);
+    wave_fwd_transform<LOG2M>(v, buf, lt, w1, w2);
+#pragma unroll
+    for (int i = 0; i < S::OPT; ++i) {
+      const int k = lt + T * i;
+      if (k < M / 2) acco[i] = cadd(acco[i], corr(buf[lds_pad(k)], buf[lds_pad(M - 1 - k)]));
+    }
+    wave_sync();
+  }
+  // the RPW row slots hold sums for the same bins: add them through LDS
+  float2* out = part + ((size_t)c * H + h) * (M + 1);
+  if constexpr (RPW == 1) {
+#pragma unroll
+    for (int i = 0; i < S::EPT; ++i) {
+      const int k = lt + T * i;
+      if (k <= M / 2) out[2 * k] = acce[i];
+    }
+#pragma unroll
+    for (int i = 0; i < S::OPT; ++i) {
+      const int k = lt + T * i;
+      if (k < M / 2) out[2 * k + 1] = acco[i];
+    }
+  } else {
+    float2* red = lds + wave * RPW * S::MP;          // the wave's region, slot-major
+#pragma unroll
+    for (int i = 0; i < S::EPT; ++i) {
+      const int k = lt + T * i;
+      if (k <= M / 2) red[rw * (M + 1) + 2 * k] = acce[i];
+    }
+#pragma unroll
+    for (int i = 0; i < S::OPT; ++i) {
+      const int k = lt + T * i;
+      if (k < M / 2) red[rw * (M + 1) + 2 * k + 1] = acco[i];
+    }
+    wave_sync();
+    for (int j = lane; j <= M; j += 64) {
+      float2 sum = make_float2(0.f, 0.f);
+#pragma unroll
+      for (int q = 0; q < RPW; ++q) sum = cadd(sum, red[q * (M + 1) + j]);
+      out[j] = sum;
+    }
+  }
+}
+
+// The partial spectra of channel h summed, S_j = sum_c part[c][h][j], into
+// the extra row part[nparts][h].
+__global__ __launch_bounds__(256) void corr_sum_kernel(float2* __restrict__ part, int H, int L,
+                                                       int nparts) {
+  const int h = blockIdx.y;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j > L) return;
+  float2 s = make_float2(0.f, 0.f);
+  for (int c = 0; c < nparts; ++c) s = cadd(s, part[((size_t)c * H + h) * (L + 1) + j]);
+  part[((size_t)nparts * H + h) * (L + 1) + j] = s;
+}
+
 // Sums the partial spectra S_j of channel h, j in [0, L], and inverts the
 // real 2L-point transform through the packing: with
 //   W_k = (S_k + conj S_{L-k}) / 2 + i e^{i pi k/L} (S_k - conj S_{L-k}) / 2,
@@ -469,9 +626,18 @@ void corr_launch(const s4dplr_plan* p, const float* u, const float* dy, float* d
   float2* part = at<float2>(ws, p->off_bpart);
   const float2* twL = at<const float2>(ws, p->off_twL);
   const float2* cs = at<const float2>(ws, p->off_cs);
-  corr_spec_kernel<LOG2L><<<dim3(p->H, nparts), S::NT, 0, s>>>(u, dy, part, twL, cs, p->H,
-                                                                p->batch);
-  corr_inv_kernel<LOG2L><<<p->H, imax(256, S::NT), 0, s>>>(part, dK, dD, twL, cs, p->H, nparts);
+  if constexpr (LOG2L >= 8 && LOG2L <= 10) {
+    const int tasks = p->H * nparts;
+    corr_wave_kernel<LOG2L><<<(tasks + 3) / 4, 256, 0, s>>>(u, dy, part, twL, cs, p->H, p->batch,
+                                                            nparts);
+  } else {
+    corr_spec_kernel<LOG2L><<<dim3(p->H, nparts), S::NT, 0, s>>>(u, dy, part, twL, cs, p->H,
+                                                                  p->batch);
+  }
+  // the partials summed into the row after them, then the inverse per channel
+  corr_sum_kernel<<<dim3((p->L + 1 + 255) / 256, p->H), 256, 0, s>>>(part, p->H, p->L, nparts);
+  corr_inv_kernel<LOG2L><<<p->H, imax(256, S::NT), 0, s>>>(
+      part + (size_t)nparts * p->H * (p->L + 1), dK, dD, twL, cs, p->H, 1);
 }
 
 template <int LOG2L>

@@ -35,7 +35,7 @@ struct s4dplr_plan {
   // Backward pass:
   size_t off_bghat;  // [H][L] float2: FFT_L(dK) / L
   size_t off_bbeta;  // [H][L] x 2 float4: conj(dKhat/dk_ab) * Ghat per frequency
-  size_t off_bpart;  // partial sums: correlation spectra [ceil(B/kCorrRows)][H][L+1] float2,
+  size_t off_bpart;  // partial sums: correlation spectra [ceil(B/kCorrRows) + 1][H][L+1] float2,
                      // or per-pole sums [H][ceil(L/kBwdChunk)][N] x 6 float2
   size_t off_bz;     // block (S4DPLR_BLOCK): [batch][H][L] float normalized input
   size_t off_bs;     // block (S4DPLR_BLOCK): [batch][H][L] float layer output
