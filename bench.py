@@ -188,7 +188,7 @@ def main() -> int:
     params = {k: g(x[k]) for k in ("lam", "P", "Q", "B", "C", "dt", "D")}
     u0 = g(x["u"])
     row_bytes = 4 * w.batch * w.H * w.L
-    nsets = max(2, -(-(512 << 20) // (2 * row_bytes)) + 1)
+    nsets = min(1024, max(2, -(-(512 << 20) // (2 * row_bytes)) + 1))
     us = [u0] + [u0.clone() for _ in range(nsets - 1)]
     ys = [torch.empty_like(u0) for _ in range(nsets)]
     K = torch.empty((w.H, w.L), dtype=torch.float32, device=dev)

@@ -386,23 +386,25 @@ __device__ __forceinline__ int big_pos(int k) {
   return (k & (S::M1 - 1)) * S::M2 + (k >> S::LOG2M1);
 }
 
-// dK: per channel h and bin pair (k, M - k), k in [0, M/2], the batch sum
-// S_j = sum_b conj(U_j) G_j of the spectra of the zero-padded u and dy rows
-// (X_j = big_rfft_x(Z_j, Z_{M-j}), Z_M = Z_0), then the packed inverse input
-//   W_k = (S_k + conj S_{M-k}) / 2 + i e^{i pi k/M} (S_k - conj S_{M-k}) / 2
-// for k and M - k, scaled by 1/M, in the permuted layout (k = 0 pairs with the
-// bin M of the real transform).
+// dK: per channel h and bin k, the batch sums S_k and S_{M-k} of
+// conj(U_j) G_j over the spectra of the zero-padded u and dy rows
+// (X_j = big_rfft_x(Z_j, Z_{M-j}), Z_M = Z_0), and the packed inverse input
+//   W_k = (S_k + conj S_{M-k}) / 2 + i e^{i pi k/M} (S_k - conj S_{M-k}) / 2,
+// scaled by 1/M, at the bin's position in the permuted layout.  Thread i takes
+// position i, so the reads of bin k and of its partner M - k (rows k1 and
+// M1 - k1 read backwards, or row 0 with k2 -> -k2) are both contiguous.
 template <int LOG2M>
 __global__ __launch_bounds__(kBigThreads) void big_corr_kernel(
     const float2* __restrict__ Zu, const float2* __restrict__ Zg, float2* __restrict__ W,
     const float2* __restrict__ cs, int batch) {
   using S = BigShape<LOG2M>;
-  constexpr int M = S::M;
+  constexpr int M = S::M, M1 = S::M1, M2 = S::M2;
   const int h = blockIdx.y;
-  const int k = blockIdx.x * kBigThreads + threadIdx.x;
-  if (k > M / 2) return;
-  const int km = M - k;                       // in [M/2, M]
-  const int pk = big_pos<LOG2M>(k), pm = big_pos<LOG2M>(km & (M - 1));
+  const int pk = blockIdx.x * kBigThreads + threadIdx.x;     // < M (grid is exact)
+  const int k1 = pk / M2, k2 = pk % M2;
+  const int k = k1 + M1 * k2;
+  const int km = M - k;                                       // in [1, M]
+  const int pm = big_pos<LOG2M>(km & (M - 1));
   const float2 ck = cs[k], cm = cs[km];
   float2 sk = make_float2(0.f, 0.f), sm = sk;
   for (int b = 0; b < batch; ++b) {
@@ -414,18 +416,10 @@ __global__ __launch_bounds__(kBigThreads) void big_corr_kernel(
     sm = cadd(sm, cmul(cconj(Um), Gm));
   }
   const float sc = 0.5f / (float)M;
-  // W_k = (S_k + conj S_m)/2 + i e^{i pi k/M} (S_k - conj S_m)/2, scaled by 1/M
   const float2 ek = make_float2(sk.x + sm.x, sk.y - sm.y);
   const float2 dk = make_float2(sk.x - sm.x, sk.y + sm.y);
   const float2 wk = cadd(ek, cmul(make_float2(-ck.y, ck.x), dk));
-  float2* __restrict__ Wh = W + (size_t)h * M;
-  Wh[pk] = make_float2(sc * wk.x, sc * wk.y);
-  if (k != 0 && km != k) {
-    const float2 em = make_float2(sm.x + sk.x, sm.y - sk.y);
-    const float2 dm = make_float2(sm.x - sk.x, sm.y + sk.y);
-    const float2 wm = cadd(em, cmul(make_float2(-cm.y, cm.x), dm));
-    Wh[pm] = make_float2(sc * wm.x, sc * wm.y);
-  }
+  W[(size_t)h * M + pk] = make_float2(sc * wk.x, sc * wk.y);
 }
 
 // Ghat_l = FFT_L(dK)_l / L = X_{2l} / L, X the spectrum of dK zero-padded to
@@ -472,8 +466,8 @@ static void big_corr(const s4dplr_plan* p, const float* u, const float* dy, floa
   big_rows_fwd_kernel<LOG2M><<<rgrid, kBigThreads, 0, s>>>(Yu, tw2);
   big_rows_fwd_kernel<LOG2M><<<rgrid, kBigThreads, 0, s>>>(Yg, tw2);
   float2* Wb = wat<float2>(ws, p->off_khat);
-  big_corr_kernel<LOG2M><<<dim3((S::M / 2 + kBigThreads) / kBigThreads, p->H), kBigThreads, 0,
-                           s>>>(Yu, Yg, Wb, cs, p->batch);
+  big_corr_kernel<LOG2M><<<dim3(S::M / kBigThreads, p->H), kBigThreads, 0, s>>>(Yu, Yg, Wb, cs,
+                                                                               p->batch);
   // inverse: rows then columns, the first M/2 outputs as (c_2n, c_2n+1)
   float* out = dK ? dK : wat<float>(ws, p->off_kbuf);
   big_rows_inv_kernel<LOG2M><<<dim3(S::M1 / S::RT, p->H), kBigThreads, 0, s>>>(Wb, Yu, tw2, tw4);
