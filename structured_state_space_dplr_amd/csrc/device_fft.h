@@ -94,65 +94,6 @@ __device__ __forceinline__ void dft_dif(float2* v) {
   dif_all<R, R / 2, INV>(v);
 }
 
-// Stockham pass P of an in-place LDS transform of 2^LOG2N points.  `lt` is
-// the thread's index within the transform (0 .. n/E-1); `on` = false lets a
-// thread take part in the barriers without touching data.
-template <int LOG2N, int P, bool INV>
-struct FftPass {
-  static __device__ __forceinline__ void run(float2* __restrict__ buf, int lt, bool on,
-                                             const float2* __restrict__ tw) {
-    constexpr int N = 1 << LOG2N;
-    constexpr int E = 1 << fft_elems_log(LOG2N);
-    constexpr int NT = N / E;
-    constexpr int RL = fft_radix_log(LOG2N, P);
-    constexpr int R = 1 << RL;
-    constexpr int NB = E / R;
-    constexpr int NSL = fft_ns_log(LOG2N, P);
-    constexpr int NS = 1 << NSL;
-    constexpr int STRIDE = N / R;
-    constexpr int TWOFF = fft_tw_offset(LOG2N, P);
-    float2 v[NB][R];
-    if (on) {
-#pragma unroll
-      for (int q = 0; q < NB; ++q)
-#pragma unroll
-        for (int r = 0; r < R; ++r) v[q][r] = buf[lds_pad(lt + q * NT + r * STRIDE)];
-    }
-    __syncthreads();
-    if (on) {
-#pragma unroll
-      for (int q = 0; q < NB; ++q) {
-        const int j = lt + q * NT;
-        const int k = j & (NS - 1);
-        if constexpr (NS > 1) {
-          const float4* t4 = reinterpret_cast<const float4*>(tw + TWOFF + k * R);
-#pragma unroll
-          for (int r2 = 0; r2 < R / 2; ++r2) {
-            const float4 w = t4[r2];
-            if (r2 > 0) v[q][2 * r2] = cmulw<INV>(v[q][2 * r2], make_float2(w.x, w.y));
-            v[q][2 * r2 + 1] = cmulw<INV>(v[q][2 * r2 + 1], make_float2(w.z, w.w));
-          }
-        }
-        dft_dif<R, INV>(v[q]);
-        const int base = ((j >> NSL) << (NSL + RL)) + k;
-#pragma unroll
-        for (int s = 0; s < R; ++s) buf[lds_pad(base + s * NS)] = v[q][bitrev<RL>(s)];
-      }
-    }
-    __syncthreads();
-    if constexpr (P + 1 < fft_num_passes(LOG2N)) FftPass<LOG2N, P + 1, INV>::run(buf, lt, on, tw);
-  }
-};
-
-// In-place, unnormalized transform of 2^LOG2N points held in LDS (padded
-// indexing).  Forward: sum_r x_r e^{-2 pi i r s / n}; inverse: e^{+...}.
-// Ends with a barrier; all threads of the workgroup must call it.
-template <int LOG2N, bool INV>
-__device__ __forceinline__ void lds_fft(float2* __restrict__ buf, int lt, bool on,
-                                        const float2* __restrict__ tw) {
-  if constexpr (LOG2N > 0) FftPass<LOG2N, 0, INV>::run(buf, lt, on, tw);
-}
-
 // ---------------------------------------------------------------------------
 // Wave-resident transforms: a transform of M = 2^LOG2M points (32 <= M <=
 // 1024) is held by T = M/16 lanes of one wavefront, 16 points per lane, and
@@ -234,6 +175,151 @@ struct WPass {
     }
   }
 };
+
+// Twiddles of pass PASS for the butterflies of thread lt, rebuilt at each use
+// from the table entries W^k (and W^{4k} for radix 16), W = W_{Ns R}: the
+// other powers W^{rk} follow by at most three complex products, so only two
+// (radix 16) or NB (shorter radix) values per pass stay in registers across
+// the rows of a block instead of fifteen.
+template <int LOG2M, int PASS>
+struct PassTwiddles {
+  using W = WPass<LOG2M, PASS>;
+  static constexpr int NBASE = W::R == 16 ? 2 : W::NB;
+  float2 b[NBASE];
+  __device__ __forceinline__ void load(const float2* __restrict__ tw, int lt) {
+    if constexpr (W::R == 16) {
+      const int k = lt & (W::NS - 1);
+      b[0] = tw[W::TWOFF + k * 16 + 1];
+      b[1] = tw[W::TWOFF + k * 16 + 4];
+    } else {
+#pragma unroll
+      for (int q = 0; q < W::NB; ++q) {
+        const int k = (lt + q * W::T) & (W::NS - 1);
+        b[q] = tw[W::TWOFF + k * W::R + 1];
+      }
+    }
+  }
+  // w[q R + r] = W^{r k_q}, r = 1 .. R-1
+  __device__ __forceinline__ void expand(float2 (&w)[16]) const {
+    float2 e[NBASE];
+#pragma unroll
+    for (int i = 0; i < NBASE; ++i) {
+      e[i] = b[i];
+      // an opaque copy: keeps the products inside the row loop rather than
+      // hoisted out of it, where all of them would hold registers
+      asm volatile("" : "+v"(e[i].x), "+v"(e[i].y));
+    }
+    if constexpr (W::R == 16) {
+      const float2 w1 = e[0], w4 = e[1];
+      const float2 w2 = cmul(w1, w1), w3 = cmul(w2, w1), w8 = cmul(w4, w4);
+      const float2 w12 = cmul(w8, w4);
+      w[1] = w1;
+      w[2] = w2;
+      w[3] = w3;
+      w[4] = w4;
+      w[5] = cmul(w4, w1);
+      w[6] = cmul(w4, w2);
+      w[7] = cmul(w4, w3);
+      w[8] = w8;
+      w[9] = cmul(w8, w1);
+      w[10] = cmul(w8, w2);
+      w[11] = cmul(w8, w3);
+      w[12] = w12;
+      w[13] = cmul(w12, w1);
+      w[14] = cmul(w12, w2);
+      w[15] = cmul(w12, w3);
+    } else {
+#pragma unroll
+      for (int q = 0; q < W::NB; ++q) {
+        const float2 w1 = e[q];
+        w[q * W::R + 1] = w1;
+        if constexpr (W::R >= 4) {
+          const float2 w2 = cmul(w1, w1), w3 = cmul(w2, w1);
+          w[q * W::R + 2] = w2;
+          w[q * W::R + 3] = w3;
+          if constexpr (W::R == 8) {
+            const float2 w4 = cmul(w2, w2);
+            w[q * W::R + 4] = w4;
+            w[q * W::R + 5] = cmul(w4, w1);
+            w[q * W::R + 6] = cmul(w4, w2);
+            w[q * W::R + 7] = cmul(w4, w3);
+          }
+        }
+      }
+    }
+  }
+};
+
+// Stockham pass P of an in-place LDS transform of 2^LOG2N points.  `lt` is
+// the thread's index within the transform (0 .. n/E-1); `on` = false lets a
+// thread take part in the barriers without touching data.
+template <int LOG2N, int P, bool INV>
+struct FftPass {
+  static __device__ __forceinline__ void run(float2* __restrict__ buf, int lt, bool on,
+                                             const float2* __restrict__ tw) {
+    constexpr int N = 1 << LOG2N;
+    constexpr int E = 1 << fft_elems_log(LOG2N);
+    constexpr int NT = N / E;
+    constexpr int RL = fft_radix_log(LOG2N, P);
+    constexpr int R = 1 << RL;
+    constexpr int NB = E / R;
+    constexpr int NSL = fft_ns_log(LOG2N, P);
+    constexpr int NS = 1 << NSL;
+    constexpr int STRIDE = N / R;
+    constexpr int TWOFF = fft_tw_offset(LOG2N, P);
+    // with 16 points per thread the twiddles come from two (radix 16) or NB
+    // table entries fetched before the barrier, so their latency overlaps it
+    constexpr bool BASES = E == 16 && NS > 1;
+    PassTwiddles<(BASES ? LOG2N : 4), (BASES ? P : 1)> pt;
+    if constexpr (BASES) {
+      if (on) pt.load(tw, lt);
+    }
+    float2 v[NB][R];
+    if (on) {
+#pragma unroll
+      for (int q = 0; q < NB; ++q)
+#pragma unroll
+        for (int r = 0; r < R; ++r) v[q][r] = buf[lds_pad(lt + q * NT + r * STRIDE)];
+    }
+    __syncthreads();
+    if (on) {
+      float2 wb[16];
+      if constexpr (BASES) pt.expand(wb);
+#pragma unroll
+      for (int q = 0; q < NB; ++q) {
+        const int j = lt + q * NT;
+        const int k = j & (NS - 1);
+        if constexpr (BASES) {
+#pragma unroll
+          for (int r = 1; r < R; ++r) v[q][r] = cmulw<INV>(v[q][r], wb[q * R + r]);
+        } else if constexpr (NS > 1) {
+          const float4* t4 = reinterpret_cast<const float4*>(tw + TWOFF + k * R);
+#pragma unroll
+          for (int r2 = 0; r2 < R / 2; ++r2) {
+            const float4 w = t4[r2];
+            if (r2 > 0) v[q][2 * r2] = cmulw<INV>(v[q][2 * r2], make_float2(w.x, w.y));
+            v[q][2 * r2 + 1] = cmulw<INV>(v[q][2 * r2 + 1], make_float2(w.z, w.w));
+          }
+        }
+        dft_dif<R, INV>(v[q]);
+        const int base = ((j >> NSL) << (NSL + RL)) + k;
+#pragma unroll
+        for (int s = 0; s < R; ++s) buf[lds_pad(base + s * NS)] = v[q][bitrev<RL>(s)];
+      }
+    }
+    __syncthreads();
+    if constexpr (P + 1 < fft_num_passes(LOG2N)) FftPass<LOG2N, P + 1, INV>::run(buf, lt, on, tw);
+  }
+};
+
+// In-place, unnormalized transform of 2^LOG2N points held in LDS (padded
+// indexing).  Forward: sum_r x_r e^{-2 pi i r s / n}; inverse: e^{+...}.
+// Ends with a barrier; all threads of the workgroup must call it.
+template <int LOG2N, bool INV>
+__device__ __forceinline__ void lds_fft(float2* __restrict__ buf, int lt, bool on,
+                                        const float2* __restrict__ tw) {
+  if constexpr (LOG2N > 0) FftPass<LOG2N, 0, INV>::run(buf, lt, on, tw);
+}
 
 // First forward pass (radix 16, span 1) when the upper half of the input is
 // zero: the first DIF stage reduces to v[i+8] = v[i] W_16^i.

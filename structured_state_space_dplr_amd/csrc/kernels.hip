@@ -595,80 +595,6 @@ struct RowConvShape {
   static_assert(LOG2M >= 11 && LOG2M <= 14, "block-resident range");
 };
 
-// Twiddles of pass PASS for the butterflies of thread lt, rebuilt at each use
-// from the table entries W^k (and W^{4k} for radix 16), W = W_{Ns R}: the
-// other powers W^{rk} follow by at most three complex products, so only two
-// (radix 16) or NB (shorter radix) values per pass stay in registers across
-// the rows of a block instead of fifteen.
-template <int LOG2M, int PASS>
-struct PassTwiddles {
-  using W = WPass<LOG2M, PASS>;
-  static constexpr int NBASE = W::R == 16 ? 2 : W::NB;
-  float2 b[NBASE];
-  __device__ __forceinline__ void load(const float2* __restrict__ tw, int lt) {
-    if constexpr (W::R == 16) {
-      const int k = lt & (W::NS - 1);
-      b[0] = tw[W::TWOFF + k * 16 + 1];
-      b[1] = tw[W::TWOFF + k * 16 + 4];
-    } else {
-#pragma unroll
-      for (int q = 0; q < W::NB; ++q) {
-        const int k = (lt + q * W::T) & (W::NS - 1);
-        b[q] = tw[W::TWOFF + k * W::R + 1];
-      }
-    }
-  }
-  // w[q R + r] = W^{r k_q}, r = 1 .. R-1
-  __device__ __forceinline__ void expand(float2 (&w)[16]) const {
-    float2 e[NBASE];
-#pragma unroll
-    for (int i = 0; i < NBASE; ++i) {
-      e[i] = b[i];
-      // an opaque copy: keeps the products inside the row loop rather than
-      // hoisted out of it, where all of them would hold registers
-      asm volatile("" : "+v"(e[i].x), "+v"(e[i].y));
-    }
-    if constexpr (W::R == 16) {
-      const float2 w1 = e[0], w4 = e[1];
-      const float2 w2 = cmul(w1, w1), w3 = cmul(w2, w1), w8 = cmul(w4, w4);
-      const float2 w12 = cmul(w8, w4);
-      w[1] = w1;
-      w[2] = w2;
-      w[3] = w3;
-      w[4] = w4;
-      w[5] = cmul(w4, w1);
-      w[6] = cmul(w4, w2);
-      w[7] = cmul(w4, w3);
-      w[8] = w8;
-      w[9] = cmul(w8, w1);
-      w[10] = cmul(w8, w2);
-      w[11] = cmul(w8, w3);
-      w[12] = w12;
-      w[13] = cmul(w12, w1);
-      w[14] = cmul(w12, w2);
-      w[15] = cmul(w12, w3);
-    } else {
-#pragma unroll
-      for (int q = 0; q < W::NB; ++q) {
-        const float2 w1 = e[q];
-        w[q * W::R + 1] = w1;
-        if constexpr (W::R >= 4) {
-          const float2 w2 = cmul(w1, w1), w3 = cmul(w2, w1);
-          w[q * W::R + 2] = w2;
-          w[q * W::R + 3] = w3;
-          if constexpr (W::R == 8) {
-            const float2 w4 = cmul(w2, w2);
-            w[q * W::R + 4] = w4;
-            w[q * W::R + 5] = cmul(w4, w1);
-            w[q * W::R + 6] = cmul(w4, w2);
-            w[q * W::R + 7] = cmul(w4, w3);
-          }
-        }
-      }
-    }
-  }
-};
-
 template <int LOG2M, int PASS, bool INV>
 __device__ __forceinline__ void row_pass(float2 (&v)[16], float2* __restrict__ buf, int lt,
                                          const PassTwiddles<LOG2M, PASS>& pt) {
