@@ -578,6 +578,181 @@ __global__ __launch_bounds__(kWaveConvThreads) void conv_wave_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Stage 2 at L = 1024 (M = 1024): the wave-resident row with paired lanes
+// ---------------------------------------------------------------------------
+// As conv_wave_kernel, one wave per row and 16 points per lane, with two
+// changes that remove one of the row's five LDS exchanges.  The last forward
+// pass (radix 4, span 256) gives lane lt the butterflies a in
+// {lt, 64 + lt, 192 - lt, 256 - lt} (lane 0: {0, 64, 192, 128}), so the bins
+// a + 256 s and their real-FFT partners M - a - 256 s = (256 - a) + 256 (3 - s)
+// sit in the same lane and the spectral weights are applied in registers.
+// The inverse is then taken over that layout:
+//   Y[a][n1] = W_M^{-n1 a} sum_s Z'[a + 256 s] W_4^{-n1 s}          (registers)
+//   S[n1][a1][m] = W_256^{-m a1} sum_{a2} Y[a1 + 16 a2][n1] W_16^{-m a2}
+//   x[n1 + 4 m + 64 m'] = sum_{a1} S[n1][a1][m] W_16^{-m' a1},  m' < 8,
+// the last line giving exactly the kept outputs n < M/2 (y_2n, y_2n+1).
+// The twiddles of the forward passes serve the inverse too (conjugated).
+__device__ __forceinline__ int pair_butterfly(int lt, int q) {
+  if (lt == 0) return q == 0 ? 0 : q == 1 ? 64 : q == 2 ? 192 : 128;
+  return q == 0 ? lt : q == 1 ? 64 + lt : q == 2 ? 192 - lt : 256 - lt;
+}
+
+__global__ __launch_bounds__(kWaveConvThreads) void conv_pair1024_kernel(
+    const float* __restrict__ u, float* __restrict__ y, const float4* __restrict__ coef,
+    const float2* __restrict__ tw, int H, int batch, int groups_per_wave) {
+  constexpr int LOG2M = 10, M = 1024, T = 64;
+  using S = WaveConvShape<LOG2M>;
+  using P1 = WPass<LOG2M, 1>;
+  static_assert(S::RPW == 1 && S::P == 3, "one row per wave, passes 16 x 16 x 4");
+  __shared__ float2 lds[(kWaveConvThreads / 64) * S::MP];
+  const int wave = threadIdx.x >> 6, lt = threadIdx.x & 63;
+  float2* buf = lds + wave * S::MP;
+  // w1: pass-1 twiddles W_256^{k r}, k = lt & 15 (inverse pass 1: conj, index m)
+  // w2: the last pass's W_M^{a r} for this lane's butterflies a (inverse step 1: conj)
+  float2 w1[16], w2[16];
+  P1::load_tw(w1, tw, lt);
+  int bq[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    bq[q] = pair_butterfly(lt, q);
+    const float4 t0 = reinterpret_cast<const float4*>(tw + WPass<LOG2M, 2>::TWOFF + bq[q] * 4)[0];
+    const float4 t1 = reinterpret_cast<const float4*>(tw + WPass<LOG2M, 2>::TWOFF + bq[q] * 4)[1];
+    w2[q * 4 + 1] = make_float2(t0.z, t0.w);
+    w2[q * 4 + 2] = make_float2(t1.x, t1.y);
+    w2[q * 4 + 3] = make_float2(t1.z, t1.w);
+  }
+  const int rows = H * batch;
+  const int gw = xcd_remap(blockIdx.x, gridDim.x) * (kWaveConvThreads / 64) + wave;
+  auto row_of = [&](int g, int& h, size_t& roff) -> bool {
+    const bool act = g < rows;                   // logical row g: channel-major
+    h = act ? g / batch : 0;
+    const int b = act ? g - h * batch : 0;
+    roff = ((size_t)b * H + h) * M;
+    return act;
+  };
+  float2 upre[8];
+  {
+    int h0;
+    size_t r0;
+    const bool a0 = row_of(gw * groups_per_wave, h0, r0);
+    const float2* __restrict__ ur = reinterpret_cast<const float2*>(u + (a0 ? r0 : 0));
+#pragma unroll
+    for (int r = 0; r < 8; ++r) upre[r] = a0 ? ur[lt + T * r] : make_float2(0.f, 0.f);
+  }
+  float4 cw[16];
+  int hc = -1;
+  for (int gi = 0; gi < groups_per_wave; ++gi) {
+    const int g = gw * groups_per_wave + gi;
+    if (g >= rows) break;
+    int h;
+    size_t roff;
+    const bool active = row_of(g, h, roff);
+    float2 v[16];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) v[r] = upre[r];
+    if (h != hc) {
+      // weights of the lane's bins a_q + 256 s, held across the channel's rows
+      const float4* __restrict__ cf = coef + (size_t)h * M;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) cw[q * 4 + s] = cf[bq[q] + 256 * s];
+      hc = h;
+    }
+    // forward passes 0 and 1 (Stockham, as the generic kernel)
+    dft16_fwd_half_input(v);
+    WPass<LOG2M, 0>::store(v, buf, lt);
+    wave_sync();
+    P1::load(v, buf, lt);
+    P1::template compute<false>(v, w1);
+    P1::store(v, buf, lt);
+    wave_sync();
+    // last forward pass on the paired butterflies: X[a + 256 s] -> v[q*4 + bitrev(s)]
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // pad(a + 256 r) = pad(a) + 272 r
+      const float2* __restrict__ bb = buf + lds_pad(bq[q]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[q * 4 + r] = bb[272 * r];
+#pragma unroll
+      for (int r = 1; r < 4; ++r) v[q * 4 + r] = cmul(v[q * 4 + r], w2[q * 4 + r]);
+      dft_dif<4, false>(&v[q * 4]);
+    }
+    // next row's input, in flight during the spectral step and the inverse
+    if (gi + 1 < groups_per_wave && g + 1 < rows) {
+      int hn;
+      size_t rn;
+      const bool an = row_of(g + 1, hn, rn);
+      const float2* __restrict__ ur = reinterpret_cast<const float2*>(u + (an ? rn : 0));
+#pragma unroll
+      for (int r = 0; r < 8; ++r) upre[r] = an ? ur[lt + T * r] : make_float2(0.f, 0.f);
+    }
+    // spectral weights in registers: Z'_j = alpha_j Z_j + beta_j conj(Z_{M-j})
+    float2 zs[16];
+    const bool l0 = lt == 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        // partner slot: butterfly 256 - a, output 3 - s; lane 0's butterflies
+        // 0 and 128 pair with themselves (outputs -s mod 4 and 3 - s)
+        const float2 zp_gen = v[(3 - q) * 4 + bitrev<2>(3 - s)];
+        float2 zp = zp_gen;
+        if (q == 0) zp = l0 ? v[bitrev<2>((4 - s) & 3)] : zp_gen;
+        if (q == 3) zp = l0 ? v[12 + bitrev<2>(3 - s)] : zp_gen;
+        const float4 c = cw[q * 4 + s];
+        zs[q * 4 + s] = cadd(cmul(make_float2(c.x, c.y), v[q * 4 + bitrev<2>(s)]),
+                             cmul(make_float2(c.z, c.w), cconj(zp)));
+      }
+    // inverse step 1 (registers): Y[a][n1], stored at [n1][a]
+    wave_sync();                                 // pass-2 reads of this row are done
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      dft_dif<4, true>(&zs[q * 4]);              // n1 at position bitrev(n1)
+      float2* __restrict__ bb = buf + lds_pad(bq[q]);
+#pragma unroll
+      for (int n1 = 0; n1 < 4; ++n1) {
+        float2 yv = zs[q * 4 + bitrev<2>(n1)];
+        if (n1 > 0) yv = cmulc(yv, w2[q * 4 + n1]);
+        bb[272 * n1] = yv;                       // [n1][a] at pad(256 n1 + a)
+      }
+    }
+    wave_sync();
+    // inverse pass 1: lane (n1, a1) = (lt >> 4, lt & 15), radix 16 over a2
+    {
+      const int n1 = lt >> 4, a1 = lt & 15;
+      // pad(256 n1 + a1 + 16 c) = 272 n1 + a1 + 17 c for a1 < 16
+      float2* __restrict__ bb = buf + 272 * n1 + a1;
+#pragma unroll
+      for (int a2 = 0; a2 < 16; ++a2) v[a2] = bb[17 * a2];
+      dft_dif<16, true>(v);                      // m at position bitrev(m)
+      wave_sync();
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        float2 sv = v[bitrev<4>(m)];
+        if (m > 0) sv = cmulc(sv, w1[m]);
+        bb[17 * m] = sv;                         // [n1][m][a1] at pad(256 n1 + 16 m + a1)
+      }
+    }
+    wave_sync();
+    // inverse pass 2: lane (n1, m) = (lt >> 4, lt & 15), radix 16 over a1,
+    // outputs m' < 8 only: x[n1 + 4 m + 64 m']
+    {
+      const int n1 = lt >> 4, m = lt & 15;
+      const float2* __restrict__ bb = buf + 272 * n1 + 17 * m;
+#pragma unroll
+      for (int a1 = 0; a1 < 16; ++a1) v[a1] = bb[a1];
+      dft_dif<16, true>(v);
+      float2* __restrict__ yr = reinterpret_cast<float2*>(y + roff);
+#pragma unroll
+      for (int mp = 0; mp < 8; ++mp)
+        if (active) yr[n1 + 4 * m + 64 * mp] = v[bitrev<4>(mp)];
+    }
+    wave_sync();
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Stage 2 for 2048 <= L <= 16384: block-resident rows
 // ---------------------------------------------------------------------------
 // The same transform layout as the wave-resident kernel (M/16 threads per
@@ -805,6 +980,12 @@ static void conv_launch(const s4dplr_plan* p, const float* u, float* y, unsigned
     const int gpw = (ngroups + kTargetWaves - 1) / kTargetWaves;
     const int waves = (ngroups + gpw - 1) / gpw;
     const int blocks = (waves + 3) / 4;
+    if constexpr (LOG2L == 10) {
+      conv_pair1024_kernel<<<blocks, kWaveConvThreads, 0, s>>>(
+          u, y, at<const float4>(ws, p->off_coef), at<const float2>(ws, p->off_twL), p->H,
+          p->batch, gpw);
+      return;
+    }
     conv_wave_kernel<LOG2L><<<blocks, kWaveConvThreads, 0, s>>>(
         u, y, at<const float4>(ws, p->off_coef), at<const float2>(ws, p->off_twL), p->H,
         p->batch, gpw);
