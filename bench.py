@@ -101,7 +101,9 @@ def backward_counts(w):
 
 def conv_kernel_name(L: int) -> str:
     """The kernel(s) that apply the convolution at sequence length L."""
-    if 32 <= L <= 1024:
+    if L == 1024:
+        return "conv_pair1024_kernel (one row per wave, paired lanes, one launch per step)"
+    if 32 <= L <= 512:
         return "conv_wave_kernel (one row per wave, one launch per step)"
     if 2048 <= L <= 16384:
         return "conv_rows_kernel (one row per workgroup, one launch per step)"
