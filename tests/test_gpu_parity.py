@@ -218,6 +218,30 @@ def test_diagonal_and_distinct_q_long(s4, L):
     assert _rel(K, Kr) <= TOL and _rel(y, yr) <= TOL
 
 
+@pytest.mark.parametrize("L,H,batch", [(1024, 700, 3), (4096, 700, 5)])
+def test_conv_fwd_rows_straddle_channels(s4, L, H, batch):
+    # more rows than one pass of the grid, with channel boundaries inside the
+    # runs of rows that one wave (L = 1024) or one workgroup (L = 4096) takes:
+    # the per-channel weights cached across rows must be refetched at each
+    # boundary
+    import torch
+    print(f"case: conv_fwd straddling rows L={L} H={H} batch={batch}", flush=True)
+    rng = np.random.default_rng(L + H + batch)
+    u = rng.standard_normal((batch, H, L)).astype(np.float32)
+    K = (rng.standard_normal((H, L)) * np.exp(-np.arange(L) / (L / 8))).astype(np.float32)
+    D = rng.standard_normal(H).astype(np.float32)
+    plan = s4.Plan(H, 4, L, batch)
+    ws = plan.workspace()
+    y = torch.empty((batch, H, L), dtype=torch.float32, device="cuda")
+    s4.conv_fwd(plan, _dev(u), _dev(K), _dev(D), y, ws)
+    torch.cuda.synchronize()
+    yr = o.conv_fft(u, K[None], D[None, :, None])
+    e = _rel(y.cpu().numpy(), yr)
+    print(f"  rel err y {e:.2e}", flush=True)
+    assert e <= TOL
+    plan.close()
+
+
 # ---- conv_apply: the spectrum left by the previous call, over other batches ----
 
 @pytest.mark.parametrize("L", [64, 1024, 4096, 32768])
