@@ -186,6 +186,8 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
   if (flags & S4DPLR_BLOCK) off = align_up(off + sizeof(float) * (size_t)batch * H * L);
   p->off_bs = off;
   if (flags & S4DPLR_BLOCK) off = align_up(off + sizeof(float) * (size_t)batch * H * L);
+  p->off_bw = off;
+  if (flags & S4DPLR_BLOCK) off = align_up(off + sizeof(unsigned short) * 4 * (size_t)H * H);
   p->total = off;
 
   // fp64 tables, rounded once to fp32.
@@ -446,7 +448,7 @@ s4dplr_status s4dplr_block_forward(const s4dplr_plan* p, const float* x, const f
   if ((e = s4::launch_kernel_gen(p, lambda, P, Q, B, C, dt, D, nullptr, w, stream)) != hipSuccess)
     return hip_fail(e);
   if ((e = s4::launch_conv(p, z, sv, w, stream)) != hipSuccess) return hip_fail(e);
-  if ((e = s4::launch_block_epilogue(p, x, sv, W, bias, out, stream)) != hipSuccess)
+  if ((e = s4::launch_block_epilogue(p, x, sv, W, bias, out, w, stream)) != hipSuccess)
     return hip_fail(e);
   return S4DPLR_OK;
 }

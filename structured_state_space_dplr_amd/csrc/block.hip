@@ -6,9 +6,10 @@
 //
 // The projection is the block's only dense contraction: per batch row it is a
 // GEMM with M = H output channels (for each of the two halves), N = L time
-// steps and K = H input channels, done on the matrix cores with fp32 MFMA
-// (v_mfma_f32_32x32x2f32), so that the block keeps fp32 accuracy.  The bias,
-// the gate and the residual are applied to the accumulators in registers.
+// steps and K = H input channels, done on the bf16 matrix cores with split
+// operands (three products per k) so that the block keeps fp32 accuracy.  The
+// bias, the gate and the residual are applied to the accumulators in
+// registers.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -20,11 +21,9 @@ namespace {
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kLnThreads = 256;
-// Projection tile: a block computes 64 channels x 128 time steps of both
-// halves; wave w owns channels [32 (w / 2), +32) and time steps [64 (w % 2), +64)
-// as two 32 x 32 MFMA tiles per half.
-constexpr int kPM = 64, kPN = 128, kPK = 32;
-constexpr int kPThreads = 256;
+// Projection tile: 128 time steps by K stages of 32 channels (the channel
+// extent of a tile is the kernel's template argument).
+constexpr int kPN = 128, kPK = 32;
 
 }  // namespace
 
@@ -86,12 +85,16 @@ __global__ __launch_bounds__(kLnThreads) void layer_norm_kernel(
 // significant bits together), and summing the three products
 // w_hi s_hi + w_hi s_lo + w_lo s_hi in the fp32 accumulators; the dropped
 // w_lo s_lo and the split's own rounding are below 2^-16 relative per term.
-// Each K stage of 32 channels stages 64 rows x 32 of each W half as [row][k]
-// and 32 x 128 of s transposed as [t][k] through LDS, both split, so that a
-// lane's eight consecutive k of an operand are one 16-byte read; the next
-// stage's global loads are issued before the current stage's MFMAs.  Fully
-// in-range tiles (H % 32 == 0 and L % 128 == 0 here) take the vector path;
-// edge tiles load element by element with zero fill.
+// W is split once per call by split_w_kernel (every tile reads it); s is
+// split while staged.  A block owns CM channels x 128 time steps of both
+// halves, CM = 128 when H allows it (s is then split by half as many blocks),
+// else 64; wave w owns channels [32 (w / 2), +32) and time steps
+// [64 (w % 2), +64) as two 32 x 32 tiles per half.  Each K stage of 32
+// channels stages CM rows x 32 of each W part as [row][k] and 32 x 128 of s
+// transposed as [t][k] through LDS, so that a lane's eight consecutive k of
+// an operand are one 16-byte read; the next stage's global loads are issued
+// before the current stage's MFMAs.  Fully in-range tiles take the vector
+// path; edge tiles load element by element with zero fill.
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ unsigned short bf16_bits(float x) {
@@ -102,57 +105,73 @@ __device__ __forceinline__ unsigned short bf16_bits(float x) {
 __device__ __forceinline__ float bf16_value(unsigned short b) {
   return __uint_as_float((unsigned int)b << 16);
 }
-// hi and lo parts of x
 __device__ __forceinline__ void split_bf16(float x, unsigned short& hi, unsigned short& lo) {
   hi = bf16_bits(x);
   lo = bf16_bits(x - bf16_value(hi));
 }
 
+// Wp[part][r][h] (part 0 = hi, 1 = lo) for the 2H x H matrix W
+__global__ __launch_bounds__(256) void split_w_kernel(const float* __restrict__ W,
+                                                      unsigned short* __restrict__ Wp,
+                                                      size_t n) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  unsigned short hi, lo;
+  split_bf16(W[i], hi, lo);
+  Wp[i] = hi;
+  Wp[n + i] = lo;
+}
+
 constexpr int kPKP = kPK + 8;   // padded k extent of a staged row (bf16 elements)
 
-__global__ __launch_bounds__(kPThreads) void glu_proj_kernel(
-    const float* x, const float* __restrict__ s, const float* __restrict__ W,
+template <int CM>
+__global__ __launch_bounds__(CM * 4) void glu_proj_kernel(
+    const float* x, const float* __restrict__ s, const unsigned short* __restrict__ Wp,
     const float* __restrict__ bias, float* out, int H, int L) {
-  // [part][row][k]: part 0 = hi, 1 = lo
-  __shared__ __attribute__((aligned(16))) unsigned short sWa[2][kPM][kPKP];
-  __shared__ __attribute__((aligned(16))) unsigned short sWg[2][kPM][kPKP];
+  constexpr int NT = CM * 4;                       // threads: 2 (CM / 32) waves
+  // W slots: 2 parts x 2 halves x CM rows x 32 k = 16 CM uint4 (8 bf16 each);
+  // s slots: 32 x 128 floats = 1024 float4, taken as channel pairs
+  constexpr int NWQ = 16 * CM / NT;                // uint4 of W per thread (4)
+  constexpr int NSQ = 512 / NT;                    // channel pairs of s per thread (2 or 1)
+  static_assert(NWQ == 4 && (NSQ == 1 || NSQ == 2), "tile shape");
+  __shared__ __attribute__((aligned(16))) unsigned short sWa[2][CM][kPKP];
+  __shared__ __attribute__((aligned(16))) unsigned short sWg[2][CM][kPKP];
   __shared__ __attribute__((aligned(16))) unsigned short sS[2][kPN][kPKP];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int b = blockIdx.z, c0 = blockIdx.y * kPM, t0 = blockIdx.x * kPN;
+  const int b = blockIdx.z, c0 = blockIdx.y * CM, t0 = blockIdx.x * kPN;
   const int cw = 32 * (w >> 1), tw = 64 * (w & 1);
   const float* sb = s + (size_t)b * H * L;
-  const bool vec = (H % kPK == 0) && (c0 + kPM <= H) && (t0 + kPN <= L) && (L % 4 == 0);
-  // float4 slots of a stage, in named registers (an indexed array here ends
-  // up in scratch memory): W slot Q of thread tid is i = tid + 256 Q (half
-  // Q / 2, row (i >> 3) & 63, k 4 (i & 7)); s slots Q = 0, 1 hold channels
-  // 2p and 2p + 1, p = (tid >> 5) + 8 Q, of time steps 4 (tid & 31) .. + 3
-  float4 rw0, rw1, rw2, rw3, rs0, rs1, rs2, rs3;
+  const size_t nW = (size_t)2 * H * H;
+  const bool vec = (H % kPK == 0) && (c0 + CM <= H) && (t0 + kPN <= L) && (L % 4 == 0);
+  // slot Q of W: i = tid + NT Q; part (i / (4 CM)) & 1 ... as below; held in
+  // named registers (an indexed array here ends up in scratch memory)
+  uint4 rw0, rw1, rw2, rw3;
+  float4 rs0, rs0b, rs1, rs1b;
+  // W slot i in [0, 16 CM): part = i / (8 CM), half = (i / (4 CM)) & 1,
+  // row = (i >> 2) % CM, k = 8 (i & 3)
 #define PROJ_FETCH_W(Q, H0)                                                                      \
   do {                                                                                           \
-    const int i_ = tid + (Q) * kPThreads;                                                        \
-    rw##Q = *reinterpret_cast<const float4*>(                                                    \
-        W + (size_t)(((Q) >> 1) * H + c0 + ((i_ >> 3) & 63)) * H + (H0) + (i_ & 7) * 4);          \
+    const int i_ = tid + (Q) * NT;                                                               \
+    const int part_ = i_ / (8 * CM), half_ = (i_ / (4 * CM)) & 1, r_ = (i_ >> 2) % CM;           \
+    rw##Q = *reinterpret_cast<const uint4*>(Wp + part_ * nW +                                    \
+                                            (size_t)(half_ * H + c0 + r_) * H + (H0) +           \
+                                            8 * (i_ & 3));                                       \
   } while (0)
+#define PROJ_STAGE_W(Q)                                                                          \
+  do {                                                                                           \
+    const int i_ = tid + (Q) * NT;                                                               \
+    const int part_ = i_ / (8 * CM), half_ = (i_ / (4 * CM)) & 1, r_ = (i_ >> 2) % CM;           \
+    unsigned short* d_ = half_ ? &sWg[part_][r_][8 * (i_ & 3)] : &sWa[part_][r_][8 * (i_ & 3)];  \
+    *reinterpret_cast<uint4*>(d_) = rw##Q;                                                       \
+  } while (0)
+  // s pair slot Q: channels 2p, 2p + 1 with p = (tid >> 5) + (NT / 32) Q, time
+  // steps 4 (tid & 31) .. + 3
 #define PROJ_FETCH_S(Q, H0)                                                                      \
   do {                                                                                           \
-    const int p_ = (tid >> 5) + 8 * (Q);                                                         \
+    const int p_ = (tid >> 5) + (NT / 32) * (Q);                                                 \
     const float* r_ = sb + (size_t)((H0) + 2 * p_) * L + t0 + (tid & 31) * 4;                    \
     rs##Q = *reinterpret_cast<const float4*>(r_);                                                \
     rs##Q##b = *reinterpret_cast<const float4*>(r_ + L);                                         \
-  } while (0)
-#define PROJ_STAGE_W(Q, DST)                                                                     \
-  do {                                                                                           \
-    const int i_ = tid + (Q) * kPThreads;                                                        \
-    const int r_ = (i_ >> 3) & 63, k_ = (i_ & 7) * 4;                                            \
-    unsigned short h_[4], l_[4];                                                                 \
-    split_bf16(rw##Q.x, h_[0], l_[0]);                                                           \
-    split_bf16(rw##Q.y, h_[1], l_[1]);                                                           \
-    split_bf16(rw##Q.z, h_[2], l_[2]);                                                           \
-    split_bf16(rw##Q.w, h_[3], l_[3]);                                                           \
-    *reinterpret_cast<uint2*>(&DST[0][r_][k_]) =                                                 \
-        make_uint2(h_[0] | ((unsigned)h_[1] << 16), h_[2] | ((unsigned)h_[3] << 16));            \
-    *reinterpret_cast<uint2*>(&DST[1][r_][k_]) =                                                 \
-        make_uint2(l_[0] | ((unsigned)l_[1] << 16), l_[2] | ((unsigned)l_[3] << 16));            \
   } while (0)
 #define PROJ_STAGE_S1(T_, A_, B_)                                                                \
   do {                                                                                           \
@@ -164,15 +183,12 @@ __global__ __launch_bounds__(kPThreads) void glu_proj_kernel(
   } while (0)
 #define PROJ_STAGE_S(Q)                                                                          \
   do {                                                                                           \
-    const int p_ = (tid >> 5) + 8 * (Q), tt_ = (tid & 31) * 4;                                   \
+    const int p_ = (tid >> 5) + (NT / 32) * (Q), tt_ = (tid & 31) * 4;                           \
     PROJ_STAGE_S1(tt_ + 0, rs##Q.x, rs##Q##b.x);                                                 \
     PROJ_STAGE_S1(tt_ + 1, rs##Q.y, rs##Q##b.y);                                                 \
     PROJ_STAGE_S1(tt_ + 2, rs##Q.z, rs##Q##b.z);                                                 \
     PROJ_STAGE_S1(tt_ + 3, rs##Q.w, rs##Q##b.w);                                                 \
   } while (0)
-  float4 rs0b, rs1b;
-  (void)rs2;
-  (void)rs3;
   v16f acc_a0 = {}, acc_a1 = {}, acc_g0 = {}, acc_g1 = {};
   if (vec) {
     PROJ_FETCH_W(0, 0);
@@ -180,30 +196,28 @@ __global__ __launch_bounds__(kPThreads) void glu_proj_kernel(
     PROJ_FETCH_W(2, 0);
     PROJ_FETCH_W(3, 0);
     PROJ_FETCH_S(0, 0);
-    PROJ_FETCH_S(1, 0);
+    if constexpr (NSQ == 2) PROJ_FETCH_S(1, 0);
   }
   for (int h0 = 0; h0 < H; h0 += kPK) {
     if (vec) {
-      PROJ_STAGE_W(0, sWa);
-      PROJ_STAGE_W(1, sWa);
-      PROJ_STAGE_W(2, sWg);
-      PROJ_STAGE_W(3, sWg);
+      PROJ_STAGE_W(0);
+      PROJ_STAGE_W(1);
+      PROJ_STAGE_W(2);
+      PROJ_STAGE_W(3);
       PROJ_STAGE_S(0);
-      PROJ_STAGE_S(1);
+      if constexpr (NSQ == 2) PROJ_STAGE_S(1);
     } else {
-      for (int i = tid; i < kPM * kPK; i += kPThreads) {
+      for (int i = tid; i < CM * kPK; i += NT) {
         const int r = i / kPK, k = i % kPK;
         const int c = c0 + r, h = h0 + k;
         const bool ok = c < H && h < H;
-        unsigned short hi, lo;
-        split_bf16(ok ? W[(size_t)c * H + h] : 0.f, hi, lo);
-        sWa[0][r][k] = hi;
-        sWa[1][r][k] = lo;
-        split_bf16(ok ? W[(size_t)(H + c) * H + h] : 0.f, hi, lo);
-        sWg[0][r][k] = hi;
-        sWg[1][r][k] = lo;
+        const size_t ia = (size_t)c * H + h, ig = (size_t)(H + c) * H + h;
+        sWa[0][r][k] = ok ? Wp[ia] : 0;
+        sWa[1][r][k] = ok ? Wp[nW + ia] : 0;
+        sWg[0][r][k] = ok ? Wp[ig] : 0;
+        sWg[1][r][k] = ok ? Wp[nW + ig] : 0;
       }
-      for (int i = tid; i < kPK * kPN; i += kPThreads) {
+      for (int i = tid; i < kPK * kPN; i += NT) {
         const int k = i / kPN, n = i % kPN;
         const int h = h0 + k, t = t0 + n;
         unsigned short hi, lo;
@@ -219,7 +233,7 @@ __global__ __launch_bounds__(kPThreads) void glu_proj_kernel(
       PROJ_FETCH_W(2, h0 + kPK);
       PROJ_FETCH_W(3, h0 + kPK);
       PROJ_FETCH_S(0, h0 + kPK);
-      PROJ_FETCH_S(1, h0 + kPK);
+      if constexpr (NSQ == 2) PROJ_FETCH_S(1, h0 + kPK);
     }
     // lane l: operand rows/columns l % 32, k = kk + 8 (l / 32) .. + 7
     const int i = lane & 31, kq = 8 * (lane >> 5);
@@ -274,9 +288,18 @@ __global__ __launch_bounds__(kPThreads) void glu_proj_kernel(
 }
 
 hipError_t launch_block_epilogue(const s4dplr_plan* p, const float* x, const float* s,
-                                 const float* W, const float* bias, float* out, hipStream_t st) {
-  const dim3 grid((p->L + kPN - 1) / kPN, (p->H + kPM - 1) / kPM, p->batch);
-  glu_proj_kernel<<<grid, kPThreads, 0, st>>>(x, s, W, bias, out, p->H, p->L);
+                                 const float* W, const float* bias, float* out,
+                                 unsigned char* ws, hipStream_t st) {
+  unsigned short* Wp = reinterpret_cast<unsigned short*>(ws + p->off_bw);
+  const size_t nW = (size_t)2 * p->H * p->H;
+  split_w_kernel<<<(unsigned)((nW + 255) / 256), 256, 0, st>>>(W, Wp, nW);
+  if (p->H % 128 == 0) {
+    const dim3 grid((p->L + kPN - 1) / kPN, p->H / 128, p->batch);
+    glu_proj_kernel<128><<<grid, 512, 0, st>>>(x, s, Wp, bias, out, p->H, p->L);
+  } else {
+    const dim3 grid((p->L + kPN - 1) / kPN, (p->H + 63) / 64, p->batch);
+    glu_proj_kernel<64><<<grid, 256, 0, st>>>(x, s, Wp, bias, out, p->H, p->L);
+  }
   return hipGetLastError();
 }
 

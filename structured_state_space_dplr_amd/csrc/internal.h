@@ -39,6 +39,7 @@ struct s4dplr_plan {
                      // or per-pole sums [H][ceil(L/kBwdChunk)][N] x 6 float2
   size_t off_bz;     // block (S4DPLR_BLOCK): [batch][H][L] float normalized input
   size_t off_bs;     // block (S4DPLR_BLOCK): [batch][H][L] float layer output
+  size_t off_bw;     // block (S4DPLR_BLOCK): [2][2H][H] bf16: W split into hi and lo parts
   size_t total;
   std::vector<unsigned char> tables;  // exact bytes of the table region
 };
@@ -104,7 +105,8 @@ hipError_t launch_vandermonde_bwd(const s4dplr_plan* p, const float* lam, const 
 hipError_t launch_layer_norm(const s4dplr_plan* p, const float* x, const float* gamma,
                              const float* beta, float* z, hipStream_t s);
 hipError_t launch_block_epilogue(const s4dplr_plan* p, const float* x, const float* s,
-                                 const float* W, const float* bias, float* out, hipStream_t st);
+                                 const float* W, const float* bias, float* out,
+                                 unsigned char* ws, hipStream_t st);
 // Work split of the scan: poles per lane (1, 2, 4 or 8) and log2 of the lanes
 // per sequence (0..5), chosen from N and the number of sequences.
 void recurrent_shape(int N, long rows, int* ppl, int* log2g);

@@ -64,7 +64,7 @@ hipError_t launch_layer_norm(const s4dplr_plan*, const float*, const float*, con
   return hipSuccess;
 }
 hipError_t launch_block_epilogue(const s4dplr_plan*, const float*, const float*, const float*,
-                                 const float*, float*, hipStream_t) {
+                                 const float*, float*, unsigned char*, hipStream_t) {
   ++g_launches;
   return hipSuccess;
 }
