@@ -132,8 +132,8 @@ __global__ __launch_bounds__(CM * 4) void glu_proj_kernel(
   // W slots: 2 parts x 2 halves x CM rows x 32 k = 16 CM uint4 (8 bf16 each);
   // s slots: 32 x 128 floats = 1024 float4, taken as channel pairs
   constexpr int NWQ = 16 * CM / NT;                // uint4 of W per thread (4)
-  constexpr int NSQ = 512 / NT;                    // channel pairs of s per thread (2 or 1)
-  static_assert(NWQ == 4 && (NSQ == 1 || NSQ == 2), "tile shape");
+  constexpr int NSG = 512 / NT;                    // groups of 8 channels of s per thread
+  static_assert(NWQ == 4 && (NSG == 1 || NSG == 2), "tile shape");
   __shared__ __attribute__((aligned(16))) unsigned short sWa[2][CM][kPKP];
   __shared__ __attribute__((aligned(16))) unsigned short sWg[2][CM][kPKP];
   __shared__ __attribute__((aligned(16))) unsigned short sS[2][kPN][kPKP];
@@ -143,10 +143,10 @@ __global__ __launch_bounds__(CM * 4) void glu_proj_kernel(
   const float* sb = s + (size_t)b * H * L;
   const size_t nW = (size_t)2 * H * H;
   const bool vec = (H % kPK == 0) && (c0 + CM <= H) && (t0 + kPN <= L) && (L % 4 == 0);
-  // slot Q of W: i = tid + NT Q; part (i / (4 CM)) & 1 ... as below; held in
-  // named registers (an indexed array here ends up in scratch memory)
+  // W slots in named registers (indexed through a macro argument); s slots in
+  // an array indexed by unrolled loops only
   uint4 rw0, rw1, rw2, rw3;
-  float4 rs0, rs0b, rs1, rs1b;
+  float rs[NSG * 8];
   // W slot i in [0, 16 CM): part = i / (8 CM), half = (i / (4 CM)) & 1,
   // row = (i >> 2) % CM, k = 8 (i & 3)
 #define PROJ_FETCH_W(Q, H0)                                                                      \
@@ -164,30 +164,31 @@ __global__ __launch_bounds__(CM * 4) void glu_proj_kernel(
     unsigned short* d_ = half_ ? &sWg[part_][r_][8 * (i_ & 3)] : &sWa[part_][r_][8 * (i_ & 3)];  \
     *reinterpret_cast<uint4*>(d_) = rw##Q;                                                       \
   } while (0)
-  // s pair slot Q: channels 2p, 2p + 1 with p = (tid >> 5) + (NT / 32) Q, time
-  // steps 4 (tid & 31) .. + 3
-#define PROJ_FETCH_S(Q, H0)                                                                      \
+  // s slots: thread tid takes time step t0 + (tid & 127) and channels
+  // h0 + 8 g + j, j < 8, of its groups g = (tid >> 7) + (NT / 128) G; the
+  // loads are coalesced over the lanes' consecutive time steps, and each group
+  // is one 16-byte LDS store per part (rows 80 bytes apart: no bank conflicts)
+#define PROJ_FETCH_S(H0)                                                                         \
   do {                                                                                           \
-    const int p_ = (tid >> 5) + (NT / 32) * (Q);                                                 \
-    const float* r_ = sb + (size_t)((H0) + 2 * p_) * L + t0 + (tid & 31) * 4;                    \
-    rs##Q = *reinterpret_cast<const float4*>(r_);                                                \
-    rs##Q##b = *reinterpret_cast<const float4*>(r_ + L);                                         \
+    _Pragma("unroll") for (int G_ = 0; G_ < NSG; ++G_) {                                         \
+      const int g_ = (tid >> 7) + (NT / 128) * G_;                                               \
+      const float* r_ = sb + (size_t)((H0) + 8 * g_) * L + t0 + (tid & 127);                     \
+      _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_) rs[G_ * 8 + j_] = r_[(size_t)j_ * L];     \
+    }                                                                                            \
   } while (0)
-#define PROJ_STAGE_S1(T_, A_, B_)                                                                \
+#define PROJ_STAGE_S()                                                                           \
   do {                                                                                           \
-    unsigned short ha_, la_, hb_, lb_;                                                           \
-    split_bf16(A_, ha_, la_);                                                                    \
-    split_bf16(B_, hb_, lb_);                                                                    \
-    *reinterpret_cast<unsigned int*>(&sS[0][T_][2 * p_]) = ha_ | ((unsigned)hb_ << 16);          \
-    *reinterpret_cast<unsigned int*>(&sS[1][T_][2 * p_]) = la_ | ((unsigned)lb_ << 16);          \
-  } while (0)
-#define PROJ_STAGE_S(Q)                                                                          \
-  do {                                                                                           \
-    const int p_ = (tid >> 5) + (NT / 32) * (Q), tt_ = (tid & 31) * 4;                           \
-    PROJ_STAGE_S1(tt_ + 0, rs##Q.x, rs##Q##b.x);                                                 \
-    PROJ_STAGE_S1(tt_ + 1, rs##Q.y, rs##Q##b.y);                                                 \
-    PROJ_STAGE_S1(tt_ + 2, rs##Q.z, rs##Q##b.z);                                                 \
-    PROJ_STAGE_S1(tt_ + 3, rs##Q.w, rs##Q##b.w);                                                 \
+    _Pragma("unroll") for (int G_ = 0; G_ < NSG; ++G_) {                                         \
+      const int g_ = (tid >> 7) + (NT / 128) * G_;                                               \
+      unsigned short h_[8], l_[8];                                                               \
+      _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_) split_bf16(rs[G_ * 8 + j_], h_[j_], l_[j_]); \
+      *reinterpret_cast<uint4*>(&sS[0][tid & 127][8 * g_]) =                                     \
+          make_uint4(h_[0] | ((unsigned)h_[1] << 16), h_[2] | ((unsigned)h_[3] << 16),           \
+                     h_[4] | ((unsigned)h_[5] << 16), h_[6] | ((unsigned)h_[7] << 16));          \
+      *reinterpret_cast<uint4*>(&sS[1][tid & 127][8 * g_]) =                                     \
+          make_uint4(l_[0] | ((unsigned)l_[1] << 16), l_[2] | ((unsigned)l_[3] << 16),           \
+                     l_[4] | ((unsigned)l_[5] << 16), l_[6] | ((unsigned)l_[7] << 16));          \
+    }                                                                                            \
   } while (0)
   v16f acc_a0 = {}, acc_a1 = {}, acc_g0 = {}, acc_g1 = {};
   if (vec) {
@@ -195,8 +196,7 @@ __global__ __launch_bounds__(CM * 4) void glu_proj_kernel(
     PROJ_FETCH_W(1, 0);
     PROJ_FETCH_W(2, 0);
     PROJ_FETCH_W(3, 0);
-    PROJ_FETCH_S(0, 0);
-    if constexpr (NSQ == 2) PROJ_FETCH_S(1, 0);
+    PROJ_FETCH_S(0);
   }
   for (int h0 = 0; h0 < H; h0 += kPK) {
     if (vec) {
@@ -204,8 +204,7 @@ __global__ __launch_bounds__(CM * 4) void glu_proj_kernel(
       PROJ_STAGE_W(1);
       PROJ_STAGE_W(2);
       PROJ_STAGE_W(3);
-      PROJ_STAGE_S(0);
-      if constexpr (NSQ == 2) PROJ_STAGE_S(1);
+      PROJ_STAGE_S();
     } else {
       for (int i = tid; i < CM * kPK; i += NT) {
         const int r = i / kPK, k = i % kPK;
@@ -232,8 +231,7 @@ __global__ __launch_bounds__(CM * 4) void glu_proj_kernel(
       PROJ_FETCH_W(1, h0 + kPK);
       PROJ_FETCH_W(2, h0 + kPK);
       PROJ_FETCH_W(3, h0 + kPK);
-      PROJ_FETCH_S(0, h0 + kPK);
-      if constexpr (NSQ == 2) PROJ_FETCH_S(1, h0 + kPK);
+      PROJ_FETCH_S(h0 + kPK);
     }
     // lane l: operand rows/columns l % 32, k = kk + 8 (l / 32) .. + 7
     const int i = lane & 31, kq = 8 * (lane >> 5);
@@ -284,7 +282,6 @@ __global__ __launch_bounds__(CM * 4) void glu_proj_kernel(
 #undef PROJ_FETCH_S
 #undef PROJ_STAGE_W
 #undef PROJ_STAGE_S
-#undef PROJ_STAGE_S1
 }
 
 hipError_t launch_block_epilogue(const s4dplr_plan* p, const float* x, const float* s,
