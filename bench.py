@@ -306,7 +306,7 @@ def main() -> int:
         f"projection {f_proj / 1e9:.2f} GFLOP)")
     block = {"us": t_blk * 1e6, "samples_per_s": samples / t_blk,
              "projection_flops": f_proj,
-             "note": "layer norm + layer + fp32-MFMA GLU projection with residual"}
+             "note": "layer norm + layer + GLU projection with residual (bf16 MFMA on hi/lo split operands, fp32 accumulation)"}
     bplan.close()
 
     # ---- the backward pass: conv_bwd and kernel_gen_bwd -----------------------
