@@ -821,6 +821,11 @@ __global__ __launch_bounds__(RowConvShape<LOG2M>::NTHR) void conv_rows_kernel(
 #pragma unroll
     for (int r = 0; r < 8; ++r) upre[r] = a0 ? ur[lt + T * r] : make_float2(0.f, 0.f);
   }
+  // weights of the thread's bins, held across the rows of a channel where the
+  // registers allow it (M <= 4096)
+  constexpr bool kCache = LOG2M <= 12;
+  float4 cw[kCache ? 16 : 1];
+  int hc = -1;
   for (int gi = 0; gi < groups_per_block; ++gi) {
     const int g = gb * groups_per_block + gi;
     if (g >= ngroups) break;                     // uniform over the block
@@ -830,6 +835,14 @@ __global__ __launch_bounds__(RowConvShape<LOG2M>::NTHR) void conv_rows_kernel(
     float2 v[16];
 #pragma unroll
     for (int r = 0; r < 8; ++r) v[r] = upre[r];
+    if constexpr (kCache) {
+      if (h != hc) {
+        const float4* __restrict__ cf = coef + (size_t)h * M;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cw[r] = cf[lt + T * r];
+        hc = h;
+      }
+    }
     dft16_fwd_half_input(v);
     __syncthreads();                             // the previous row's last reads are done
     WPass<LOG2M, 0>::store(v, buf, lt);
@@ -860,7 +873,9 @@ __global__ __launch_bounds__(RowConvShape<LOG2M>::NTHR) void conv_rows_kernel(
         float2 zm;
         if (r == 0) zm = buf[lds_pad((M - lt) & (M - 1))];
         else zm = bm[(M - T * r) + ((M - T * r) >> 4)];
-        const float4 c = cf[lt + T * r];
+        float4 c;
+        if constexpr (kCache) c = cw[r];
+        else c = cf[lt + T * r];
         v[r] = cadd(cmul(make_float2(c.x, c.y), z[r]), cmul(make_float2(c.z, c.w), cconj(zm)));
       }
     }
