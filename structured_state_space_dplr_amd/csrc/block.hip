@@ -122,33 +122,45 @@ __global__ __launch_bounds__(256) void split_w_kernel(const float* __restrict__ 
   Wp[n + i] = lo;
 }
 
-constexpr int kPKP = kPK + 8;   // padded k extent of a staged row (bf16 elements)
 
-template <int CM>
+// Offset (bf16 elements) of the 16-byte chunk c (k = 8 c .. 8 c + 7) of row r
+// in a staged [row][32] operand: 64-byte rows with the chunk index XORed by
+// (r / 4) mod 4, so that 16-byte reads of 32 consecutive rows at one chunk and
+// 16-byte writes of consecutive rows or chunks meet no bank conflicts.
+__device__ __forceinline__ int swz(int r, int c) { return 32 * r + 8 * (c ^ ((r >> 2) & 3)); }
+
+template <int CM, int TN>
 __global__ __launch_bounds__(CM * 4) void glu_proj_kernel(
     const float* x, const float* __restrict__ s, const unsigned short* __restrict__ Wp,
     const float* __restrict__ bias, float* out, int H, int L) {
   constexpr int NT = CM * 4;                       // threads: 2 (CM / 32) waves
+  constexpr int JT = TN / 64;                      // 32 x 32 tiles per half and wave
   // W slots: 2 parts x 2 halves x CM rows x 32 k = 16 CM uint4 (8 bf16 each);
-  // s slots: 32 x 128 floats = 1024 float4, taken as channel pairs
+  // s slots: TN time steps x 4 groups of 8 channels
   constexpr int NWQ = 16 * CM / NT;                // uint4 of W per thread (4)
-  constexpr int NSG = 512 / NT;                    // groups of 8 channels of s per thread
-  static_assert(NWQ == 4 && (NSG == 1 || NSG == 2), "tile shape");
-  __shared__ __attribute__((aligned(16))) unsigned short sWa[2][CM][kPKP];
-  __shared__ __attribute__((aligned(16))) unsigned short sWg[2][CM][kPKP];
-  __shared__ __attribute__((aligned(16))) unsigned short sS[2][kPN][kPKP];
+  constexpr int NSG = 4 * TN / NT;                 // groups of 8 channels of s per thread
+  static_assert(NWQ == 4 && NSG >= 1 && NSG <= 4 && (NT % TN == 0 || TN % NT == 0), "tile shape");
+  static_assert(kPK == 32, "swizzle assumes 32-channel stages");
+  // two buffers of each staged operand: stage k is read from buffer k % 2
+  // while stage k + 1 is written to the other
+  constexpr int WB = 2 * 2 * CM * kPK;             // [half][part][row][32] per buffer
+  constexpr int SB = 2 * TN * kPK;                 // [part][t][32] per buffer
+  __shared__ __attribute__((aligned(16))) unsigned short sW[2 * WB];
+  __shared__ __attribute__((aligned(16))) unsigned short sS[2 * SB];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int b = blockIdx.z, c0 = blockIdx.y * CM, t0 = blockIdx.x * kPN;
-  const int cw = 32 * (w >> 1), tw = 64 * (w & 1);
+  const int b = blockIdx.z, c0 = blockIdx.y * CM, t0 = blockIdx.x * TN;
+  const int cw = 32 * (w >> 1), tw = (TN / 2) * (w & 1);
   const float* sb = s + (size_t)b * H * L;
   const size_t nW = (size_t)2 * H * H;
-  const bool vec = (H % kPK == 0) && (c0 + CM <= H) && (t0 + kPN <= L) && (L % 4 == 0);
+  const bool vec = (H % kPK == 0) && (c0 + CM <= H) && (t0 + TN <= L);
+  auto wofs = [](int half, int part, int r, int c) { return ((half * 2 + part) * CM) * kPK + swz(r, c); };
+  auto sofs = [](int part, int t, int c) { return part * TN * kPK + swz(t, c); };
   // W slots in named registers (indexed through a macro argument); s slots in
   // an array indexed by unrolled loops only
   uint4 rw0, rw1, rw2, rw3;
   float rs[NSG * 8];
   // W slot i in [0, 16 CM): part = i / (8 CM), half = (i / (4 CM)) & 1,
-  // row = (i >> 2) % CM, k = 8 (i & 3)
+  // row = (i >> 2) % CM, chunk = i & 3
 #define PROJ_FETCH_W(Q, H0)                                                                      \
   do {                                                                                           \
     const int i_ = tid + (Q) * NT;                                                               \
@@ -157,125 +169,179 @@ __global__ __launch_bounds__(CM * 4) void glu_proj_kernel(
                                             (size_t)(half_ * H + c0 + r_) * H + (H0) +           \
                                             8 * (i_ & 3));                                       \
   } while (0)
-#define PROJ_STAGE_W(Q)                                                                          \
+#define PROJ_STAGE_W(Q, BUF)                                                                     \
   do {                                                                                           \
     const int i_ = tid + (Q) * NT;                                                               \
     const int part_ = i_ / (8 * CM), half_ = (i_ / (4 * CM)) & 1, r_ = (i_ >> 2) % CM;           \
-    unsigned short* d_ = half_ ? &sWg[part_][r_][8 * (i_ & 3)] : &sWa[part_][r_][8 * (i_ & 3)];  \
-    *reinterpret_cast<uint4*>(d_) = rw##Q;                                                       \
+    *reinterpret_cast<uint4*>(&sW[(BUF) * WB + wofs(half_, part_, r_, i_ & 3)]) = rw##Q;         \
   } while (0)
-  // s slots: thread tid takes time step t0 + (tid & 127) and channels
-  // h0 + 8 g + j, j < 8, of its groups g = (tid >> 7) + (NT / 128) G; the
-  // loads are coalesced over the lanes' consecutive time steps, and each group
-  // is one 16-byte LDS store per part (rows 80 bytes apart: no bank conflicts)
+  // s slots: thread tid takes time step t0 + tid % TN and channels h0 + 8 g + j,
+  // j < 8, of its groups g = tid / TN + (NT / TN) G; the loads are coalesced
+  // over the lanes' consecutive time steps, and each group is one 16-byte LDS
+  // store per part
 #define PROJ_FETCH_S(H0)                                                                         \
   do {                                                                                           \
     _Pragma("unroll") for (int G_ = 0; G_ < NSG; ++G_) {                                         \
-      const int g_ = (tid >> 7) + (NT / 128) * G_;                                               \
-      const float* r_ = sb + (size_t)((H0) + 8 * g_) * L + t0 + (tid & 127);                     \
+      const int g_ = tid / TN + (NT / TN) * G_;                                                  \
+      const float* r_ = sb + (size_t)((H0) + 8 * g_) * L + t0 + tid % TN;                        \
       _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_) rs[G_ * 8 + j_] = r_[(size_t)j_ * L];     \
     }                                                                                            \
   } while (0)
-#define PROJ_STAGE_S()                                                                           \
+#define PROJ_STAGE_S(BUF)                                                                        \
   do {                                                                                           \
     _Pragma("unroll") for (int G_ = 0; G_ < NSG; ++G_) {                                         \
-      const int g_ = (tid >> 7) + (NT / 128) * G_;                                               \
+      const int g_ = tid / TN + (NT / TN) * G_;                                                  \
       unsigned short h_[8], l_[8];                                                               \
       _Pragma("unroll") for (int j_ = 0; j_ < 8; ++j_) split_bf16(rs[G_ * 8 + j_], h_[j_], l_[j_]); \
-      *reinterpret_cast<uint4*>(&sS[0][tid & 127][8 * g_]) =                                     \
+      *reinterpret_cast<uint4*>(&sS[(BUF) * SB + sofs(0, tid % TN, g_)]) =                       \
           make_uint4(h_[0] | ((unsigned)h_[1] << 16), h_[2] | ((unsigned)h_[3] << 16),           \
                      h_[4] | ((unsigned)h_[5] << 16), h_[6] | ((unsigned)h_[7] << 16));          \
-      *reinterpret_cast<uint4*>(&sS[1][tid & 127][8 * g_]) =                                     \
+      *reinterpret_cast<uint4*>(&sS[(BUF) * SB + sofs(1, tid % TN, g_)]) =                       \
           make_uint4(l_[0] | ((unsigned)l_[1] << 16), l_[2] | ((unsigned)l_[3] << 16),           \
                      l_[4] | ((unsigned)l_[5] << 16), l_[6] | ((unsigned)l_[7] << 16));          \
     }                                                                                            \
   } while (0)
-  v16f acc_a0 = {}, acc_a1 = {}, acc_g0 = {}, acc_g1 = {};
+  // edge tiles: element by element with zero fill
+  auto stage_elements = [&](int h0, int buf) {
+    for (int i = tid; i < CM * kPK; i += NT) {
+      const int r = i / kPK, k = i % kPK;
+      const int c = c0 + r, h = h0 + k;
+      const bool ok = c < H && h < H;
+      const size_t ia = (size_t)c * H + h, ig = (size_t)(H + c) * H + h;
+      const int o = buf * WB + (k & 7);
+      sW[o + wofs(0, 0, r, k >> 3)] = ok ? Wp[ia] : 0;
+      sW[o + wofs(0, 1, r, k >> 3)] = ok ? Wp[nW + ia] : 0;
+      sW[o + wofs(1, 0, r, k >> 3)] = ok ? Wp[ig] : 0;
+      sW[o + wofs(1, 1, r, k >> 3)] = ok ? Wp[nW + ig] : 0;
+    }
+    for (int i = tid; i < kPK * TN; i += NT) {
+      const int k = i / TN, n = i % TN;
+      const int h = h0 + k, t = t0 + n;
+      unsigned short hi, lo;
+      split_bf16((h < H && t < L) ? sb[(size_t)h * L + t] : 0.f, hi, lo);
+      sS[buf * SB + sofs(0, n, k >> 3) + (k & 7)] = hi;
+      sS[buf * SB + sofs(1, n, k >> 3) + (k & 7)] = lo;
+    }
+  };
+  v16f acc_a[JT], acc_g[JT];
+#pragma unroll
+  for (int j = 0; j < JT; ++j) {
+    acc_a[j] = v16f{};
+    acc_g[j] = v16f{};
+  }
+  const int nst = (H + kPK - 1) / kPK;
   if (vec) {
     PROJ_FETCH_W(0, 0);
     PROJ_FETCH_W(1, 0);
     PROJ_FETCH_W(2, 0);
     PROJ_FETCH_W(3, 0);
     PROJ_FETCH_S(0);
+    PROJ_STAGE_W(0, 0);
+    PROJ_STAGE_W(1, 0);
+    PROJ_STAGE_W(2, 0);
+    PROJ_STAGE_W(3, 0);
+    PROJ_STAGE_S(0);
+    if (nst > 1) {
+      PROJ_FETCH_W(0, kPK);
+      PROJ_FETCH_W(1, kPK);
+      PROJ_FETCH_W(2, kPK);
+      PROJ_FETCH_W(3, kPK);
+      PROJ_FETCH_S(kPK);
+    }
+  } else {
+    stage_elements(0, 0);
   }
-  for (int h0 = 0; h0 < H; h0 += kPK) {
-    if (vec) {
-      PROJ_STAGE_W(0);
-      PROJ_STAGE_W(1);
-      PROJ_STAGE_W(2);
-      PROJ_STAGE_W(3);
-      PROJ_STAGE_S();
-    } else {
-      for (int i = tid; i < CM * kPK; i += NT) {
-        const int r = i / kPK, k = i % kPK;
-        const int c = c0 + r, h = h0 + k;
-        const bool ok = c < H && h < H;
-        const size_t ia = (size_t)c * H + h, ig = (size_t)(H + c) * H + h;
-        sWa[0][r][k] = ok ? Wp[ia] : 0;
-        sWa[1][r][k] = ok ? Wp[nW + ia] : 0;
-        sWg[0][r][k] = ok ? Wp[ig] : 0;
-        sWg[1][r][k] = ok ? Wp[nW + ig] : 0;
-      }
-      for (int i = tid; i < kPK * kPN; i += NT) {
-        const int k = i / kPN, n = i % kPN;
-        const int h = h0 + k, t = t0 + n;
-        unsigned short hi, lo;
-        split_bf16((h < H && t < L) ? sb[(size_t)h * L + t] : 0.f, hi, lo);
-        sS[0][n][k] = hi;
-        sS[1][n][k] = lo;
-      }
-    }
-    __syncthreads();
-    if (vec && h0 + kPK < H) {   // the next stage's loads, in flight during the MFMAs
-      PROJ_FETCH_W(0, h0 + kPK);
-      PROJ_FETCH_W(1, h0 + kPK);
-      PROJ_FETCH_W(2, h0 + kPK);
-      PROJ_FETCH_W(3, h0 + kPK);
-      PROJ_FETCH_S(h0 + kPK);
-    }
-    // lane l: operand rows/columns l % 32, k = kk + 8 (l / 32) .. + 7
-    const int i = lane & 31, kq = 8 * (lane >> 5);
+  __syncthreads();
+  // lane l: operand rows/columns l % 32, k = kk + 8 (l / 32) .. + 7
+  const int i = lane & 31, kq = lane >> 5;
+  for (int st = 0; st < nst; ++st) {
+    const int cur = st & 1;
+    const unsigned short* bW = sW + cur * WB;
+    const unsigned short* bS = sS + cur * SB;
 #pragma unroll
-    for (int kk = 0; kk < kPK; kk += 16) {
-      const v8bf ah = *reinterpret_cast<const v8bf*>(&sWa[0][cw + i][kk + kq]);
-      const v8bf al = *reinterpret_cast<const v8bf*>(&sWa[1][cw + i][kk + kq]);
-      const v8bf gh = *reinterpret_cast<const v8bf*>(&sWg[0][cw + i][kk + kq]);
-      const v8bf gl = *reinterpret_cast<const v8bf*>(&sWg[1][cw + i][kk + kq]);
-      const v8bf b0h = *reinterpret_cast<const v8bf*>(&sS[0][tw + i][kk + kq]);
-      const v8bf b0l = *reinterpret_cast<const v8bf*>(&sS[1][tw + i][kk + kq]);
-      const v8bf b1h = *reinterpret_cast<const v8bf*>(&sS[0][tw + 32 + i][kk + kq]);
-      const v8bf b1l = *reinterpret_cast<const v8bf*>(&sS[1][tw + 32 + i][kk + kq]);
-      acc_a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b0h, acc_a0, 0, 0, 0);
-      acc_a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b1h, acc_a1, 0, 0, 0);
-      acc_g0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gh, b0h, acc_g0, 0, 0, 0);
-      acc_g1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gh, b1h, acc_g1, 0, 0, 0);
-      acc_a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b0l, acc_a0, 0, 0, 0);
-      acc_a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b1l, acc_a1, 0, 0, 0);
-      acc_g0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gh, b0l, acc_g0, 0, 0, 0);
-      acc_g1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gh, b1l, acc_g1, 0, 0, 0);
-      acc_a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b0h, acc_a0, 0, 0, 0);
-      acc_a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b1h, acc_a1, 0, 0, 0);
-      acc_g0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gl, b0h, acc_g0, 0, 0, 0);
-      acc_g1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gl, b1h, acc_g1, 0, 0, 0);
+    for (int kc = 0; kc < 4; kc += 2) {           // 16-channel halves of the stage
+      const v8bf ah = *reinterpret_cast<const v8bf*>(&bW[wofs(0, 0, cw + i, kc + kq)]);
+      const v8bf al = *reinterpret_cast<const v8bf*>(&bW[wofs(0, 1, cw + i, kc + kq)]);
+      const v8bf gh = *reinterpret_cast<const v8bf*>(&bW[wofs(1, 0, cw + i, kc + kq)]);
+      const v8bf gl = *reinterpret_cast<const v8bf*>(&bW[wofs(1, 1, cw + i, kc + kq)]);
+#pragma unroll
+      for (int j = 0; j < JT; ++j) {
+        const v8bf bh = *reinterpret_cast<const v8bf*>(&bS[sofs(0, tw + 32 * j + i, kc + kq)]);
+        const v8bf bl = *reinterpret_cast<const v8bf*>(&bS[sofs(1, tw + 32 * j + i, kc + kq)]);
+        acc_a[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc_a[j], 0, 0, 0);
+        acc_g[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gh, bh, acc_g[j], 0, 0, 0);
+        acc_a[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc_a[j], 0, 0, 0);
+        acc_g[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gh, bl, acc_g[j], 0, 0, 0);
+        acc_a[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc_a[j], 0, 0, 0);
+        acc_g[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gl, bh, acc_g[j], 0, 0, 0);
+      }
+    }
+    // the next stage into the other buffer (last read before the previous
+    // barrier), then the loads of the stage after it
+    if (st + 1 < nst) {
+      if (vec) {
+        PROJ_STAGE_W(0, cur ^ 1);
+        PROJ_STAGE_W(1, cur ^ 1);
+        PROJ_STAGE_W(2, cur ^ 1);
+        PROJ_STAGE_W(3, cur ^ 1);
+        PROJ_STAGE_S(cur ^ 1);
+        if (st + 2 < nst) {
+          const int h2 = (st + 2) * kPK;
+          PROJ_FETCH_W(0, h2);
+          PROJ_FETCH_W(1, h2);
+          PROJ_FETCH_W(2, h2);
+          PROJ_FETCH_W(3, h2);
+          PROJ_FETCH_S(h2);
+        }
+      } else {
+        stage_elements((st + 1) * kPK, cur ^ 1);
+      }
     }
     __syncthreads();
   }
   // accumulator register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4,
   // column l % 32 of the 32 x 32 tile
   const size_t base = (size_t)b * H * L;
+  if (vec) {
+    // every residual and bias value first, then the outputs: the loads are in
+    // flight together (out may alias x, so a load placed after a store would
+    // wait for it; each element is still read and then written by one lane)
+    const float* xr = x + base + (size_t)(c0 + cw + 4 * (lane >> 5)) * L + t0 + tw + (lane & 31);
+    float* orow = out + base + (size_t)(c0 + cw + 4 * (lane >> 5)) * L + t0 + tw + (lane & 31);
+    float xv[16][JT], ba[16], bg[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int c = c0 + cw + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    if (c >= H) continue;
-    const float ba = bias[c], bg = bias[H + c];
+    for (int r = 0; r < 16; ++r) {
+      const int dc = 8 * (r >> 2) + (r & 3);
+      ba[r] = bias[c0 + cw + 4 * (lane >> 5) + dc];
+      bg[r] = bias[H + c0 + cw + 4 * (lane >> 5) + dc];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int t = t0 + tw + 32 * j + (lane & 31);
-      if (t >= L) continue;
-      const float a = (j ? acc_a1[r] : acc_a0[r]) + ba;
-      const float g = (j ? acc_g1[r] : acc_g0[r]) + bg;
-      const size_t o = base + (size_t)c * L + t;
-      out[o] = x[o] + a * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+      for (int j = 0; j < JT; ++j) xv[r][j] = xr[(size_t)dc * L + 32 * j];
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int dc = 8 * (r >> 2) + (r & 3);
+#pragma unroll
+      for (int j = 0; j < JT; ++j) {
+        const float a = acc_a[j][r] + ba[r];
+        const float g = acc_g[j][r] + bg[r];
+        orow[(size_t)dc * L + 32 * j] = xv[r][j] + a * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int c = c0 + cw + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (c >= H) continue;
+      const float ba = bias[c], bg = bias[H + c];
+#pragma unroll
+      for (int j = 0; j < JT; ++j) {
+        const int t = t0 + tw + 32 * j + (lane & 31);
+        if (t >= L) continue;
+        const float a = acc_a[j][r] + ba;
+        const float g = acc_g[j][r] + bg;
+        const size_t o = base + (size_t)c * L + t;
+        out[o] = x[o] + a * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+      }
     }
   }
 #undef PROJ_FETCH_W
@@ -291,11 +357,12 @@ hipError_t launch_block_epilogue(const s4dplr_plan* p, const float* x, const flo
   const size_t nW = (size_t)2 * p->H * p->H;
   split_w_kernel<<<(unsigned)((nW + 255) / 256), 256, 0, st>>>(W, Wp, nW);
   if (p->H % 128 == 0) {
-    const dim3 grid((p->L + kPN - 1) / kPN, p->H / 128, p->batch);
-    glu_proj_kernel<128><<<grid, 512, 0, st>>>(x, s, Wp, bias, out, p->H, p->L);
+    constexpr int TN = 2 * kPN;
+    const dim3 grid((p->L + TN - 1) / TN, p->H / 128, p->batch);
+    glu_proj_kernel<128, TN><<<grid, 512, 0, st>>>(x, s, Wp, bias, out, p->H, p->L);
   } else {
     const dim3 grid((p->L + kPN - 1) / kPN, (p->H + 63) / 64, p->batch);
-    glu_proj_kernel<64><<<grid, 256, 0, st>>>(x, s, Wp, bias, out, p->H, p->L);
+    glu_proj_kernel<64, kPN><<<grid, 256, 0, st>>>(x, s, Wp, bias, out, p->H, p->L);
   }
   return hipGetLastError();
 }
