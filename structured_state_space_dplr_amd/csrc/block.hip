@@ -31,23 +31,40 @@ constexpr int kPN = 128, kPK = 32;
 // z[b][h][t] = (x - mean) rstd gamma_h + beta_h.  Block (64 time steps, b):
 // wave g sums the channels h = g, g + 4, ... of its lane's time step; the four
 // partial sums meet in LDS, and the normalization is split the same way.
+// HPT > 0 (H = 4 HPT): the thread keeps its HPT values of x in registers
+// between the two steps, so x is read from memory once; HPT = 0: any H, x is
+// read again for the normalization.
+template <int HPT>
 __global__ __launch_bounds__(kLnThreads) void layer_norm_kernel(
     const float* __restrict__ x, const float* __restrict__ gamma, const float* __restrict__ beta,
     float* __restrict__ z, int H, int L, float eps) {
   constexpr int G = kLnThreads / 64;
   __shared__ double red[2][G][64];
   __shared__ float stat[2][64];
-  const int b = blockIdx.y, lane = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int b = blockIdx.y, lane = threadIdx.x & 63;
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t = blockIdx.x * 64 + lane;
   const bool on = t < L;
   const float* xb = x + (size_t)b * H * L + t;
+  float xv[HPT > 0 ? HPT : 1];
   double s1 = 0.0, s2 = 0.0;
   if (on) {
+    if constexpr (HPT > 0) {
+#pragma unroll
+      for (int i = 0; i < HPT; ++i) xv[i] = xb[(size_t)(g + G * i) * L];
+#pragma unroll
+      for (int i = 0; i < HPT; ++i) {
+        const double v = (double)xv[i];
+        s1 += v;
+        s2 += v * v;
+      }
+    } else {
 #pragma unroll 8
-    for (int h = g; h < H; h += G) {
-      const double v = (double)xb[(size_t)h * L];
-      s1 += v;
-      s2 += v * v;
+      for (int h = g; h < H; h += G) {
+        const double v = (double)xb[(size_t)h * L];
+        s1 += v;
+        s2 += v * v;
+      }
     }
   }
   red[0][g][lane] = s1;
@@ -69,10 +86,18 @@ __global__ __launch_bounds__(kLnThreads) void layer_norm_kernel(
   if (!on) return;
   const float m = stat[0][lane], r = stat[1][lane];
   float* zb = z + (size_t)b * H * L + t;
+  if constexpr (HPT > 0) {
+#pragma unroll
+    for (int i = 0; i < HPT; ++i) {
+      const int h = g + G * i;
+      zb[(size_t)h * L] = fmaf((xv[i] - m) * r, gamma[h], beta[h]);
+    }
+  } else {
 #pragma unroll 8
-  for (int h = g; h < H; h += G) {
-    const size_t o = (size_t)h * L;
-    zb[o] = fmaf((xb[o] - m) * r, gamma[h], beta[h]);
+    for (int h = g; h < H; h += G) {
+      const size_t o = (size_t)h * L;
+      zb[o] = fmaf((xb[o] - m) * r, gamma[h], beta[h]);
+    }
   }
 }
 
@@ -370,7 +395,16 @@ hipError_t launch_block_epilogue(const s4dplr_plan* p, const float* x, const flo
 hipError_t launch_layer_norm(const s4dplr_plan* p, const float* x, const float* gamma,
                              const float* beta, float* z, hipStream_t st) {
   const dim3 grid((p->L + 63) / 64, p->batch);
-  layer_norm_kernel<<<grid, kLnThreads, 0, st>>>(x, gamma, beta, z, p->H, p->L, 1e-5f);
+  auto run = [&](auto kernel) {
+    kernel<<<grid, kLnThreads, 0, st>>>(x, gamma, beta, z, p->H, p->L, 1e-5f);
+  };
+  switch (p->H) {   // x held in registers between the two steps where H allows
+    case 64: run(layer_norm_kernel<16>); break;
+    case 128: run(layer_norm_kernel<32>); break;
+    case 256: run(layer_norm_kernel<64>); break;
+    case 512: run(layer_norm_kernel<128>); break;
+    default: run(layer_norm_kernel<0>); break;
+  }
   return hipGetLastError();
 }
 

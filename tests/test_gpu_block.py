@@ -57,7 +57,7 @@ def oracle_block(x, bp, diagonal=False, zoh=False):
                                          (33, 8, 64, 1), (256, 8, 32, 2),
                                          # full 128-channel x 256-step tiles (L is a
                                          # power of two, so only L < 256 leaves a tail)
-                                         (128, 8, 512, 2), (384, 8, 256, 1)])
+                                         (128, 8, 512, 2), (384, 8, 256, 1), (512, 8, 256, 1)])
 def test_block_shapes(s4, H, N, L, batch):
     print(f"case: block H={H} N={N} L={L} batch={batch}", flush=True)
     x = make_generic_inputs(H=H, N=N, L=L, batch=batch, seed=H + L)
