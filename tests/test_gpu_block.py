@@ -1,6 +1,6 @@
 """GPU parity of the block around the layer (s4dplr_block_forward through the C
-ABI: layer norm over channels, the layer, the fp32-MFMA GLU projection with
-bias and residual) against the fp64 oracle's block_forward on the same
+ABI: layer norm over channels, the layer, the GLU projection on the bf16
+matrix cores with split operands, bias and residual) against the fp64 oracle's block_forward on the same
 seeded inputs.  Gate: max|gpu - oracle| / max|oracle| <= 1e-4."""
 import numpy as np
 import pytest
@@ -76,6 +76,19 @@ def test_block_in_place_and_diagonal_zoh(s4):
     out = run_block(s4, x, bp, diagonal=True, zoh=True, in_place=True)
     ref = oracle_block(x, bp, diagonal=True, zoh=True)
     assert _rel(out, ref) <= TOL
+
+
+def test_block_in_place_full_tiles(s4):
+    # H a multiple of 128 and L >= 256: every projection tile takes the
+    # full-tile path, whose epilogue reads all residuals before any store
+    print("case: block in place, H=128 N=8 L=512 batch=2", flush=True)
+    x = make_generic_inputs(H=128, N=8, L=512, batch=2, seed=11)
+    bp = make_block_params(128, seed=12)
+    out = run_block(s4, x, bp, in_place=True)
+    ref = oracle_block(x, bp)
+    e = _rel(out, ref)
+    print(f"  rel err {e:.2e}", flush=True)
+    assert e <= TOL
 
 
 def test_block_mid_workload(s4):
