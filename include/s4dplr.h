@@ -174,7 +174,10 @@ s4dplr_status s4dplr_conv_apply(const s4dplr_plan* plan, const float* u, float* 
  * the workspace for s4dplr_recurrent_scan.  Arguments and layouts as for
  * s4dplr_kernel_gen (Q == NULL means Q = P; with S4DPLR_DIAGONAL, P and Q are
  * ignored).  Device pointers.  Does not touch the convolution state of the
- * workspace.  The records are formed in fp64 and stored as fp32.
+ * workspace.  The records are formed in fp64 and stored as fp32.  For plans
+ * with N <= 64, L >= 128 and batch * H < 4096 it also forms, per channel,
+ * A-bar^C (fp64 squarings, stored as fp32) for the chunk length C the plan
+ * chose, which the chunked form of s4dplr_recurrent_scan uses.
  * Errors: ERR_NULL, ERR_WORKSPACE, ERR_HIP.
  */
 s4dplr_status s4dplr_recurrent_prepare(const s4dplr_plan* plan, const float* lambda,
@@ -199,6 +202,10 @@ s4dplr_status s4dplr_recurrent_prepare(const s4dplr_plan* plan, const float* lam
  *   D     : [H] float32 or NULL (D = 0).
  * T = 0 is a no-op (u and y may then be NULL).  y must not overlap u, state
  * or the workspace; state must not overlap u or the workspace (ERR_ALIAS).
+ * When the plan has a chunk length C (see s4dplr_recurrent_prepare) and the
+ * call spans 2 .. L/C chunks, the sequences are scanned chunk by chunk in
+ * parallel and joined through A-bar^C (three launches); otherwise each
+ * sequence is scanned step by step.  Both compute the same recurrence.
  * Limits: 0 <= T and batch * H * T < 2^31 (ERR_SHAPE).
  * Errors: ERR_NULL, ERR_SHAPE, ERR_ALIAS, ERR_WORKSPACE, ERR_HIP.
  */

@@ -162,6 +162,24 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
   off = align_up(off + sizeof(float) * 16 * (size_t)H * N);
   p->off_rchan = off;
   off = align_up(off + sizeof(float) * 4 * (size_t)H);
+  // Chunked scan: when the batch * H sequences alone would give under about
+  // two waves per SIMD, each sequence of L steps is cut into rnc chunks of C
+  // steps (C >= 64, a power of two) so that sequences x chunks reach 16384.
+  p->rchunk = 0;
+  p->rnc = 0;
+  {
+    const long rows = (long)batch * H;
+    if (N <= 64 && rows < 4096 && L >= 128) {
+      int nc = 2;
+      while ((long)nc * rows < 16384 && L / (2 * nc) >= 64) nc *= 2;
+      p->rchunk = L / nc;
+      p->rnc = nc;
+    }
+  }
+  p->off_rpow = off;
+  if (p->rchunk) off = align_up(off + sizeof(float) * 2 * (size_t)H * 64 * 64);
+  p->off_rcs = off;
+  if (p->rchunk) off = align_up(off + sizeof(float) * 2 * (size_t)batch * H * p->rnc * N);
   p->off_bghat = off;
   off = align_up(off + sizeof(float) * 2 * (size_t)H * L);
   p->off_bbeta = off;

@@ -32,6 +32,10 @@ struct s4dplr_plan {
   size_t off_big2;   // long path, backward: a second [batch*H][L] float2 buffer
   size_t off_rrec;   // recurrent view: [H][N] x 4 float4 per-pole step records
   size_t off_rchan;  // recurrent view: [H] float4 per-channel sums (S1, S2)
+  int rchunk;        // recurrent view: chunk length C of the chunked scan (0: whole sequences)
+  int rnc;           // recurrent view: chunks per sequence the chunk-state buffer holds
+  size_t off_rpow;   // recurrent view, chunked: [H][64][64] float2 A-bar^C
+  size_t off_rcs;    // recurrent view, chunked: [batch*H][rnc][N] float2 chunk states
   // Backward pass:
   size_t off_bghat;  // [H][L] float2: FFT_L(dK) / L
   size_t off_bbeta;  // [H][L] x 2 float4: conj(dKhat/dk_ab) * Ghat per frequency

@@ -162,11 +162,20 @@ __global__ __launch_bounds__(64) void recurrent_prepare_kernel(
 // Memory row = b * H + h; the group of 2^LOG2G lanes handles one row.
 // u and y are moved 16 steps at a time: lane j of a group holds the steps
 // t0 + j + G m, and each step's input is broadcast to the group.
+//
+// Chunked form (mode != kScanWhole): the sequence of memory row r is cut into
+// nc chunks of C steps (the last may be shorter) and the group takes the
+// chunk v = r nc + c.  kScanLocal starts the chunk from a zero state, writes
+// no output and leaves the chunk's final state in cst[v]; kScanCarried starts
+// from cst[v] (the true state before the chunk), writes y, and the last chunk
+// leaves the final state in `state`.
+constexpr int kScanWhole = 0, kScanLocal = 1, kScanCarried = 2;
+
 template <int PPL, int LOG2G, bool DIAG>
 __global__ __launch_bounds__(256) void recurrent_scan_kernel(
     const float4* __restrict__ rec, const float4* __restrict__ chan, const float* __restrict__ D,
     const float* __restrict__ u, float2* __restrict__ state, float* __restrict__ y, int H,
-    int rows, int N, int T) {
+    int vrows, int N, int T, int C, int nc, int mode, float2* __restrict__ cst) {
   constexpr int G = 1 << LOG2G;
   constexpr int CH = 16;
   constexpr int NU = G >= CH ? 1 : CH / G;
@@ -174,9 +183,12 @@ __global__ __launch_bounds__(256) void recurrent_scan_kernel(
   const int j = lane & (G - 1);
   const int gbase = lane - j;
   const long grow = ((long)blockIdx.x * 256 + threadIdx.x) >> LOG2G;
-  const bool valid = grow < rows;   // the whole group agrees
-  const int row = valid ? (int)grow : 0;
+  const bool valid = grow < vrows;  // the whole group agrees
+  const int v = valid ? (int)grow : 0;
+  const int row = v / nc, ck = v - row * nc;   // memory row, chunk
   const int h = row % H;
+  const int tb = ck * C;                       // first step of the chunk
+  const int len = min(C, T - tb);              // steps of the chunk
 
   float2 ab[PPL], e[PPL], bb[PPL], g[PPL], qa[PPL], qc[PPL], c[PPL], x[PPL];
 #pragma unroll
@@ -193,7 +205,8 @@ __global__ __launch_bounds__(256) void recurrent_scan_kernel(
       qa[k] = make_float2(r2v.x, r2v.y);
       qc[k] = make_float2(r2v.z, r2v.w);
       c[k] = make_float2(r3.x, r3.y);
-      x[k] = state[(size_t)row * N + n];
+      if (mode == kScanWhole) x[k] = state[(size_t)row * N + n];
+      else if (mode == kScanCarried) x[k] = cst[(size_t)v * N + n];
     }
   }
   float2 S1 = make_float2(0.f, 0.f), S2 = make_float2(0.f, 0.f);
@@ -213,19 +226,20 @@ __global__ __launch_bounds__(256) void recurrent_scan_kernel(
     r2 = make_float2(group_sum<LOG2G>(a2), group_sum<LOG2G>(a3));
   }
 
-  const float* __restrict__ ur = u + (size_t)row * T;
-  float* __restrict__ yr = y + (size_t)row * T;
-  for (int t0 = 0; t0 < T; t0 += CH) {
+  const float* __restrict__ ur = u + (size_t)row * T + tb;
+  float* __restrict__ yr = y + (size_t)row * T + tb;
+  const bool out_y = mode != kScanLocal;
+  for (int t0 = 0; t0 < len; t0 += CH) {
     float uv[NU], yv[NU];
 #pragma unroll
     for (int m = 0; m < NU; ++m) {
       const int o = j + G * m, t = t0 + o;
-      uv[m] = (valid && o < CH && t < T) ? ur[t] : 0.f;
+      uv[m] = (valid && o < CH && t < len) ? ur[t] : 0.f;
       yv[m] = 0.f;
     }
 #pragma unroll
     for (int i = 0; i < CH; ++i) {
-      if (t0 + i >= T) continue;   // the same for every lane
+      if (t0 + i >= len) continue;   // the same for every lane
       float ut;
       if constexpr (G == 1) ut = uv[i];
       else ut = __shfl(uv[i / G], gbase + (i % G));
@@ -262,16 +276,158 @@ __global__ __launch_bounds__(256) void recurrent_scan_kernel(
       const float yt = fmaf(Dh, ut, group_sum<LOG2G>(yre));
       if (j == (i % G)) yv[i / G] = yt;
     }
+    if (out_y) {
 #pragma unroll
-    for (int m = 0; m < NU; ++m) {
-      const int o = j + G * m, t = t0 + o;
-      if (valid && o < CH && t < T) yr[t] = yv[m];
+      for (int m = 0; m < NU; ++m) {
+        const int o = j + G * m, t = t0 + o;
+        if (valid && o < CH && t < len) yr[t] = yv[m];
+      }
     }
   }
 #pragma unroll
   for (int k = 0; k < PPL; ++k) {
     const int n = j + G * k;
-    if (valid && n < N) state[(size_t)row * N + n] = x[k];
+    if (!valid || n >= N) continue;
+    if (mode == kScanLocal) cst[(size_t)v * N + n] = x[k];
+    else if (mode == kScanWhole || ck == nc - 1) state[(size_t)row * N + n] = x[k];
+  }
+}
+
+// A-bar^C of channel h (C = 2^log2C), zero-padded to 64 x 64: A-bar from the
+// per-pole quantities of the step above, column j being the step applied to
+// the unit vector e_j,
+//   A-bar[i][j] = Abar0_j delta_ij - e_i conj(Q_j) - g_i conj(Q_j) (Abar0_j - S1),
+// then log2C squarings, all in fp64 in LDS, rounded once.  N <= 64.
+constexpr int kPowDim = 64;
+
+__global__ __launch_bounds__(256) void recurrent_power_kernel(
+    const float2* __restrict__ lam, const float2* __restrict__ P, const float2* __restrict__ Q,
+    const float* __restrict__ dt, float2* __restrict__ pw, int N, int diag, int zoh,
+    int log2C) {
+  constexpr int D = kPowDim;
+  __shared__ cd m0[D * D], m1[D * D];
+  __shared__ cd pab[D], pe[D], pg[D], pqc[D];
+  __shared__ cd s1s;
+  const int h = blockIdx.x, tid = threadIdx.x;
+  if (tid < 64) {
+    const int n = tid;
+    const double d = (double)dt[h], s = 0.5 * d;
+    cd l = {0.0, 0.0}, p = {0.0, 0.0}, q = {0.0, 0.0};
+    if (n < N) {
+      const size_t i = (size_t)h * N + n;
+      l = cd_load(lam, i);
+      if (!diag) {
+        p = cd_load(P, i);
+        q = cd_load(Q ? Q : P, i);
+      }
+    }
+    const cd d0 = {1.0 - s * l.re, -s * l.im};
+    cd t = {0.0, 0.0};
+    if (n < N && !diag) t = cd_div(cd_mul({q.re, -q.im}, p), d0);
+    const cd den = {1.0 + s * wave_sum_d(t.re), s * wave_sum_d(t.im)};
+    cd ab = {0.0, 0.0}, e = {0.0, 0.0}, g = {0.0, 0.0};
+    const cd qc = {q.re, -q.im};
+    if (n < N) {
+      ab = cd_div({1.0 + s * l.re, s * l.im}, d0);
+      if (zoh) {
+        const double ex = exp(d * l.re);
+        double sn, cs;
+        sincos(d * l.im, &sn, &cs);
+        ab = {ex * cs, ex * sn};
+      }
+      e = cd_div({s * p.re, s * p.im}, d0);
+      g = cd_div(e, den);
+    }
+    const cd qe = cd_mul(qc, e);
+    const cd s1 = {wave_sum_d(qe.re), wave_sum_d(qe.im)};
+    pab[n] = ab;
+    pe[n] = e;
+    pg[n] = g;
+    pqc[n] = qc;
+    if (n == 0) s1s = s1;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < D * D; idx += 256) {
+    const int i = idx / D, jj = idx % D;
+    cd v = {0.0, 0.0};
+    if (i < N && jj < N) {
+      const cd a = pab[jj], qj = pqc[jj];
+      const cd w = cd_mul(qj, {a.re - s1s.re, a.im - s1s.im});
+      const cd t1 = cd_mul(pe[i], qj), t2 = cd_mul(pg[i], w);
+      v = {(i == jj ? a.re : 0.0) - t1.re - t2.re, (i == jj ? a.im : 0.0) - t1.im - t2.im};
+    }
+    m0[idx] = v;
+  }
+  __syncthreads();
+  // squarings: thread tid forms the 4 x 4 block at rows 4 (tid / 16), columns 4 (tid % 16)
+  cd* src = m0;
+  cd* dst = m1;
+  const int i0 = 4 * (tid >> 4), j0 = 4 * (tid & 15);
+  for (int sq = 0; sq < log2C; ++sq) {
+    cd acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[a][b] = {0.0, 0.0};
+    for (int k = 0; k < D; ++k) {
+      cd ra[4], rb[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) ra[a] = src[(i0 + a) * D + k];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) rb[b] = src[k * D + j0 + b];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          acc[a][b].re = fma(ra[a].re, rb[b].re, fma(-ra[a].im, rb[b].im, acc[a][b].re));
+          acc[a][b].im = fma(ra[a].re, rb[b].im, fma(ra[a].im, rb[b].re, acc[a][b].im));
+        }
+    }
+    __syncthreads();                             // every read of src is done
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) dst[(i0 + a) * D + j0 + b] = acc[a][b];
+    __syncthreads();
+    cd* t = src;
+    src = dst;
+    dst = t;
+  }
+  float2* out = pw + (size_t)h * D * D;
+  for (int idx = tid; idx < D * D; idx += 256)
+    out[idx] = make_float2((float)src[idx].re, (float)src[idx].im);
+}
+
+// The chunk carries of memory row `row` (one wave): starting from the state
+// passed in, s_0 = state, s_{c+1} = A-bar^C s_c + f_c, where f_c (in cst,
+// from the zero-state scan of chunk c) is replaced by s_c.  Lane i holds row
+// i of A-bar^C; s_j reaches every lane as a scalar.
+__global__ __launch_bounds__(64) void recurrent_carry_kernel(const float2* __restrict__ pw,
+                                                             const float2* __restrict__ state,
+                                                             float2* __restrict__ cst, int H,
+                                                             int N, int nc) {
+  constexpr int D = kPowDim;
+  const int row = blockIdx.x, lane = threadIdx.x, h = row % H;
+  const bool on = lane < N;
+  float2 m[D];
+  const float2* mr = pw + ((size_t)h * D + lane) * D;
+#pragma unroll
+  for (int jj = 0; jj < D; ++jj) m[jj] = mr[jj];
+  float2 sv = on ? state[(size_t)row * N + lane] : make_float2(0.f, 0.f);
+  float2* cr = cst + (size_t)row * nc * N;
+  for (int c = 0; c < nc; ++c) {
+    const float2 f = on ? cr[(size_t)c * N + lane] : make_float2(0.f, 0.f);
+    if (on) cr[(size_t)c * N + lane] = sv;
+    if (c == nc - 1) break;
+    float re = f.x, im = f.y;
+#pragma unroll
+    for (int jj = 0; jj < D; ++jj) {
+      const float sr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv.x), jj));
+      const float si = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sv.y), jj));
+      re = fmaf(m[jj].x, sr, fmaf(-m[jj].y, si, re));
+      im = fmaf(m[jj].x, si, fmaf(m[jj].y, sr, im));
+    }
+    sv = make_float2(re, im);
   }
 }
 
@@ -285,58 +441,97 @@ hipError_t launch_recurrent_prepare(const s4dplr_plan* p, const float* lam, cons
       reinterpret_cast<const float2*>(Q), reinterpret_cast<const float2*>(B),
       reinterpret_cast<const float2*>(C), dt, reinterpret_cast<float4*>(ws + p->off_rrec),
       reinterpret_cast<float4*>(ws + p->off_rchan), p->N, diag, zoh);
+  if (p->rchunk > 0) {
+    int log2C = 0;
+    while ((1 << log2C) < p->rchunk) ++log2C;
+    recurrent_power_kernel<<<p->H, 256, 0, s>>>(
+        reinterpret_cast<const float2*>(lam), reinterpret_cast<const float2*>(P),
+        reinterpret_cast<const float2*>(Q), dt, reinterpret_cast<float2*>(ws + p->off_rpow), p->N,
+        diag, zoh, log2C);
+  }
   return hipGetLastError();
 }
 
 namespace {
 
+// One launch of the scan kernel over vrows = rows * nc groups.
+struct ScanArgs {
+  const float* D;
+  const float* u;
+  float* state;
+  float* y;
+  int T, C, nc, mode;
+  float2* cst;
+};
+
 template <int PPL, int LOG2G>
-void scan_launch(const s4dplr_plan* p, const float* D, const float* u, float* state, float* y,
-                 int T, unsigned char* ws, hipStream_t s) {
-  const int rows = p->batch * p->H;
+void scan_launch(const s4dplr_plan* p, const ScanArgs& a, unsigned char* ws, hipStream_t s) {
+  const int vrows = p->batch * p->H * a.nc;
   const float4* rec = reinterpret_cast<const float4*>(ws + p->off_rrec);
   const float4* chan = reinterpret_cast<const float4*>(ws + p->off_rchan);
-  float2* st = reinterpret_cast<float2*>(state);
-  const long threads = (long)rows << LOG2G;
+  float2* st = reinterpret_cast<float2*>(a.state);
+  const long threads = (long)vrows << LOG2G;
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   if (p->flags & S4DPLR_DIAGONAL)
-    recurrent_scan_kernel<PPL, LOG2G, true>
-        <<<blocks, 256, 0, s>>>(rec, chan, D, u, st, y, p->H, rows, p->N, T);
+    recurrent_scan_kernel<PPL, LOG2G, true><<<blocks, 256, 0, s>>>(
+        rec, chan, a.D, a.u, st, a.y, p->H, vrows, p->N, a.T, a.C, a.nc, a.mode, a.cst);
   else
-    recurrent_scan_kernel<PPL, LOG2G, false>
-        <<<blocks, 256, 0, s>>>(rec, chan, D, u, st, y, p->H, rows, p->N, T);
+    recurrent_scan_kernel<PPL, LOG2G, false><<<blocks, 256, 0, s>>>(
+        rec, chan, a.D, a.u, st, a.y, p->H, vrows, p->N, a.T, a.C, a.nc, a.mode, a.cst);
 }
 
 template <int PPL>
-bool scan_dispatch_g(int lg, const s4dplr_plan* p, const float* D, const float* u, float* state,
-                     float* y, int T, unsigned char* ws, hipStream_t s) {
+bool scan_dispatch_g(int lg, const s4dplr_plan* p, const ScanArgs& a, unsigned char* ws,
+                     hipStream_t s) {
   switch (lg) {
-    case 0: scan_launch<PPL, 0>(p, D, u, state, y, T, ws, s); return true;
-    case 1: scan_launch<PPL, 1>(p, D, u, state, y, T, ws, s); return true;
-    case 2: scan_launch<PPL, 2>(p, D, u, state, y, T, ws, s); return true;
-    case 3: scan_launch<PPL, 3>(p, D, u, state, y, T, ws, s); return true;
-    case 4: scan_launch<PPL, 4>(p, D, u, state, y, T, ws, s); return true;
-    case 5: scan_launch<PPL, 5>(p, D, u, state, y, T, ws, s); return true;
+    case 0: scan_launch<PPL, 0>(p, a, ws, s); return true;
+    case 1: scan_launch<PPL, 1>(p, a, ws, s); return true;
+    case 2: scan_launch<PPL, 2>(p, a, ws, s); return true;
+    case 3: scan_launch<PPL, 3>(p, a, ws, s); return true;
+    case 4: scan_launch<PPL, 4>(p, a, ws, s); return true;
+    case 5: scan_launch<PPL, 5>(p, a, ws, s); return true;
+    default: return false;
+  }
+}
+
+bool scan_dispatch(const s4dplr_plan* p, const ScanArgs& a, unsigned char* ws, hipStream_t s) {
+  int ppl, lg;
+  recurrent_shape(p->N, (long)p->batch * p->H * a.nc, &ppl, &lg);
+  switch (ppl) {
+    case 1: return scan_dispatch_g<1>(lg, p, a, ws, s);
+    case 2: return scan_dispatch_g<2>(lg, p, a, ws, s);
+    case 4: return scan_dispatch_g<4>(lg, p, a, ws, s);
+    case 8: return scan_dispatch_g<8>(lg, p, a, ws, s);
     default: return false;
   }
 }
 
 }  // namespace
 
+// Sequences alone give few lanes when batch * H is small, and each lane then
+// walks all T steps in order.  With the plan's chunk length C (N <= 64, few
+// sequences) a scan of at least two chunks runs as three launches: every
+// chunk from a zero state (its final state f_c), the carries
+// s_{c+1} = A-bar^C s_c + f_c per sequence, and every chunk again from s_c,
+// writing y.  The result is the same linear recurrence.
 hipError_t launch_recurrent_scan(const s4dplr_plan* p, const float* D, const float* u,
                                  float* state, float* y, int T, unsigned char* ws,
                                  hipStream_t s) {
-  int ppl, lg;
-  recurrent_shape(p->N, (long)p->batch * p->H, &ppl, &lg);
-  bool ok = false;
-  switch (ppl) {
-    case 1: ok = scan_dispatch_g<1>(lg, p, D, u, state, y, T, ws, s); break;
-    case 2: ok = scan_dispatch_g<2>(lg, p, D, u, state, y, T, ws, s); break;
-    case 4: ok = scan_dispatch_g<4>(lg, p, D, u, state, y, T, ws, s); break;
-    case 8: ok = scan_dispatch_g<8>(lg, p, D, u, state, y, T, ws, s); break;
-    default: break;
+  const int C = p->rchunk;
+  const int nc = C > 0 ? (T + C - 1) / C : 1;
+  if (C > 0 && nc >= 2 && nc <= p->rnc) {
+    float2* cst = reinterpret_cast<float2*>(ws + p->off_rcs);
+    const ScanArgs local{D, u, state, y, T, C, nc, kScanLocal, cst};
+    if (!scan_dispatch(p, local, ws, s)) return hipErrorInvalidValue;
+    recurrent_carry_kernel<<<p->batch * p->H, 64, 0, s>>>(
+        reinterpret_cast<const float2*>(ws + p->off_rpow), reinterpret_cast<const float2*>(state),
+        cst, p->H, p->N, nc);
+    const ScanArgs carried{D, u, state, y, T, C, nc, kScanCarried, cst};
+    if (!scan_dispatch(p, carried, ws, s)) return hipErrorInvalidValue;
+    return hipGetLastError();
   }
-  if (!ok) return hipErrorInvalidValue;
+  const ScanArgs whole{D, u, state, y, T, T, 1, kScanWhole, nullptr};
+  if (!scan_dispatch(p, whole, ws, s)) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

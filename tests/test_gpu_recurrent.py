@@ -140,6 +140,40 @@ def test_from_nonzero_state(s4):
     check(s4, x, x0=x0, label="x0")
 
 
+def test_chunked_from_nonzero_state(s4):
+    # L = 512 with 12 sequences: chunks of 64 steps; T = 300 is five chunks,
+    # the last one 44 steps, carried from a nonzero starting state
+    print("case: recurrent chunked, nonzero state, T=300 (chunks of 64)", flush=True)
+    x = make_generic_inputs(H=3, N=32, L=300, batch=4, seed=21)
+    rng = np.random.default_rng(22)
+    x0 = rng.standard_normal((4, 3, 32)) + 1j * rng.standard_normal((4, 3, 32))
+    x0 = _c(_pack(x0))
+    check(s4, x, x0=x0, label="chunked x0")
+
+
+def test_call_longer_than_the_chunk_buffer(s4):
+    # a plan with L = 128 holds two chunks of 64; a call of T = 300 steps
+    # takes the step-by-step form
+    import torch
+    print("case: recurrent T=300 on a plan with L=128", flush=True)
+    x = make_generic_inputs(H=3, N=16, L=300, batch=2, seed=23)
+    plan = s4.Plan(3, 16, 128, 2)
+    ws = plan.workspace()
+    t = {k: _dev(x[k]) for k in ("lam", "P", "Q", "B", "C", "dt", "D", "u")}
+    s4.recurrent_prepare(plan, t["lam"], t["P"], t["Q"], t["B"], t["C"], t["dt"], ws)
+    state = torch.zeros((2, 3, 16, 2), dtype=torch.float32, device="cuda")
+    y = torch.empty_like(t["u"])
+    s4.recurrent_scan(plan, t["D"], t["u"], state, y, ws)
+    torch.cuda.synchronize()
+    yg = y.cpu().numpy()
+    sg = state.cpu().numpy()
+    plan.close()
+    yr, sr = oracle_rec(x)
+    ey, es = _rel(yg, yr), _rel(sg[..., 0] + 1j * sg[..., 1], sr)
+    print(f"  rel err y {ey:.3e}  state {es:.3e}", flush=True)
+    assert ey <= TOL and es <= TOL
+
+
 # ---- streaming: consecutive calls continue one sequence ---------------------
 
 def test_split_scan_continues_the_stream(s4):
