@@ -179,7 +179,9 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
   p->off_rpow = off;
   if (p->rchunk) off = align_up(off + sizeof(float) * 2 * (size_t)H * 64 * 64);
   p->off_rcs = off;
-  if (p->rchunk) off = align_up(off + sizeof(float) * 2 * (size_t)batch * H * p->rnc * N);
+  if (p->rchunk) off = align_up(off + sizeof(float) * 2 * (size_t)batch * H * p->rnc * 64);
+  p->off_rct = off;
+  if (p->rchunk) off = align_up(off + sizeof(float) * 2 * (size_t)H * p->rchunk * N);
   p->off_bghat = off;
   off = align_up(off + sizeof(float) * 2 * (size_t)H * L);
   p->off_bbeta = off;

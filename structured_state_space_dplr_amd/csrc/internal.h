@@ -35,7 +35,8 @@ struct s4dplr_plan {
   int rchunk;        // recurrent view: chunk length C of the chunked scan (0: whole sequences)
   int rnc;           // recurrent view: chunks per sequence the chunk-state buffer holds
   size_t off_rpow;   // recurrent view, chunked: [H][64][64] float2 A-bar^C
-  size_t off_rcs;    // recurrent view, chunked: [batch*H][rnc][N] float2 chunk states
+  size_t off_rcs;    // recurrent view, chunked: [batch*H][rnc][64] float2 chunk states
+  size_t off_rct;    // recurrent view, chunked: [H][C][N] float2 rows C A-bar^tau, tau < C
   // Backward pass:
   size_t off_bghat;  // [H][L] float2: FFT_L(dK) / L
   size_t off_bbeta;  // [H][L] x 2 float4: conj(dKhat/dk_ab) * Ghat per frequency

@@ -164,18 +164,20 @@ __global__ __launch_bounds__(64) void recurrent_prepare_kernel(
 // t0 + j + G m, and each step's input is broadcast to the group.
 //
 // Chunked form (mode != kScanWhole): the sequence of memory row r is cut into
-// nc chunks of C steps (the last may be shorter) and the group takes the
-// chunk v = r nc + c.  kScanLocal starts the chunk from a zero state, writes
-// no output and leaves the chunk's final state in cst[v]; kScanCarried starts
-// from cst[v] (the true state before the chunk), writes y, and the last chunk
-// leaves the final state in `state`.
+// nc chunks of C steps (the last may be shorter); a launch takes the chunks
+// [c0, c0 + ncl) of every row, group v = r ncl + (c - c0).  kScanLocal starts
+// each chunk from a zero state, writes its zero-state output and leaves the
+// chunk's final state in cst[r nc + c]; kScanCarried starts from that entry
+// (the true state before the chunk), writes y, and the last chunk leaves the
+// final state in `state`.
 constexpr int kScanWhole = 0, kScanLocal = 1, kScanCarried = 2;
 
 template <int PPL, int LOG2G, bool DIAG>
 __global__ __launch_bounds__(256) void recurrent_scan_kernel(
     const float4* __restrict__ rec, const float4* __restrict__ chan, const float* __restrict__ D,
     const float* __restrict__ u, float2* __restrict__ state, float* __restrict__ y, int H,
-    int vrows, int N, int T, int C, int nc, int mode, float2* __restrict__ cst) {
+    int vrows, int N, int T, int C, int nc, int c0, int ncl, int mode,
+    float2* __restrict__ cst) {
   constexpr int G = 1 << LOG2G;
   constexpr int CH = 16;
   constexpr int NU = G >= CH ? 1 : CH / G;
@@ -185,7 +187,8 @@ __global__ __launch_bounds__(256) void recurrent_scan_kernel(
   const long grow = ((long)blockIdx.x * 256 + threadIdx.x) >> LOG2G;
   const bool valid = grow < vrows;  // the whole group agrees
   const int v = valid ? (int)grow : 0;
-  const int row = v / nc, ck = v - row * nc;   // memory row, chunk
+  const int row = v / ncl, ck = c0 + (v - row * ncl);   // memory row, chunk
+  const size_t cv = (size_t)row * nc + ck;               // its chunk-state entry (64 wide)
   const int h = row % H;
   const int tb = ck * C;                       // first step of the chunk
   const int len = min(C, T - tb);              // steps of the chunk
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(256) void recurrent_scan_kernel(
       qc[k] = make_float2(r2v.z, r2v.w);
       c[k] = make_float2(r3.x, r3.y);
       if (mode == kScanWhole) x[k] = state[(size_t)row * N + n];
-      else if (mode == kScanCarried) x[k] = cst[(size_t)v * N + n];
+      else if (mode == kScanCarried) x[k] = cst[cv * 64 + n];
     }
   }
   float2 S1 = make_float2(0.f, 0.f), S2 = make_float2(0.f, 0.f);
@@ -228,7 +231,6 @@ __global__ __launch_bounds__(256) void recurrent_scan_kernel(
 
   const float* __restrict__ ur = u + (size_t)row * T + tb;
   float* __restrict__ yr = y + (size_t)row * T + tb;
-  const bool out_y = mode != kScanLocal;
   for (int t0 = 0; t0 < len; t0 += CH) {
     float uv[NU], yv[NU];
 #pragma unroll
@@ -276,19 +278,17 @@ __global__ __launch_bounds__(256) void recurrent_scan_kernel(
       const float yt = fmaf(Dh, ut, group_sum<LOG2G>(yre));
       if (j == (i % G)) yv[i / G] = yt;
     }
-    if (out_y) {
 #pragma unroll
-      for (int m = 0; m < NU; ++m) {
-        const int o = j + G * m, t = t0 + o;
-        if (valid && o < CH && t < len) yr[t] = yv[m];
-      }
+    for (int m = 0; m < NU; ++m) {
+      const int o = j + G * m, t = t0 + o;
+      if (valid && o < CH && t < len) yr[t] = yv[m];
     }
   }
 #pragma unroll
   for (int k = 0; k < PPL; ++k) {
     const int n = j + G * k;
     if (!valid || n >= N) continue;
-    if (mode == kScanLocal) cst[(size_t)v * N + n] = x[k];
+    if (mode == kScanLocal) cst[cv * 64 + n] = x[k];
     else if (mode == kScanWhole || ck == nc - 1) state[(size_t)row * N + n] = x[k];
   }
 }
@@ -400,12 +400,14 @@ __global__ __launch_bounds__(256) void recurrent_power_kernel(
 
 // The chunk carries of memory row `row` (one wave): starting from the state
 // passed in, s_0 = state, s_{c+1} = A-bar^C s_c + f_c, where f_c (in cst,
-// from the zero-state scan of chunk c) is replaced by s_c.  Lane i holds row
-// i of A-bar^C; s_j reaches every lane as a scalar.
+// from the zero-state scan of chunk c) is replaced by s_c.  With `full` (the
+// last chunk has C steps too) the final state s_nc is written to `state`.
+// Lane i holds row i of A-bar^C; s_j reaches every lane as a scalar.  Chunk
+// states are 64 entries wide, zero beyond N after this kernel.
 __global__ __launch_bounds__(64) void recurrent_carry_kernel(const float2* __restrict__ pw,
-                                                             const float2* __restrict__ state,
+                                                             float2* __restrict__ state,
                                                              float2* __restrict__ cst, int H,
-                                                             int N, int nc) {
+                                                             int N, int nc, int full) {
   constexpr int D = kPowDim;
   const int row = blockIdx.x, lane = threadIdx.x, h = row % H;
   const bool on = lane < N;
@@ -414,11 +416,11 @@ __global__ __launch_bounds__(64) void recurrent_carry_kernel(const float2* __res
 #pragma unroll
   for (int jj = 0; jj < D; ++jj) m[jj] = mr[jj];
   float2 sv = on ? state[(size_t)row * N + lane] : make_float2(0.f, 0.f);
-  float2* cr = cst + (size_t)row * nc * N;
+  float2* cr = cst + (size_t)row * nc * D;
   for (int c = 0; c < nc; ++c) {
-    const float2 f = on ? cr[(size_t)c * N + lane] : make_float2(0.f, 0.f);
-    if (on) cr[(size_t)c * N + lane] = sv;
-    if (c == nc - 1) break;
+    const float2 f = on ? cr[(size_t)c * D + lane] : make_float2(0.f, 0.f);
+    cr[(size_t)c * D + lane] = sv;
+    if (c == nc - 1 && !full) break;
     float re = f.x, im = f.y;
 #pragma unroll
     for (int jj = 0; jj < D; ++jj) {
@@ -428,6 +430,89 @@ __global__ __launch_bounds__(64) void recurrent_carry_kernel(const float2* __res
       im = fmaf(m[jj].x, si, fmaf(m[jj].y, sr, im));
     }
     sv = make_float2(re, im);
+  }
+  if (full && on) state[(size_t)row * N + lane] = sv;
+}
+
+// c_tau = C A-bar^(tau + 1), tau < C, of channel h (one wave, lane n holds
+// entry n), for the outputs' dependence on the state s before a chunk (the
+// chunk's first step already multiplies s by A-bar):
+// y_{t0 + tau} = (zero-state output) + Re(c_tau . s).  The transposed step,
+// with A-bar = (I - g conj(Q)^T)(diag(Abar0) - e conj(Q)^T), is
+//   c1 = c - (c . g) conj(Q)^T,   c' = c1 o Abar0 - (c1 . e) conj(Q)^T,
+// in fp64, each row rounded once.  ct: [H][C][N] float2.
+__global__ __launch_bounds__(64) void recurrent_ctab_kernel(
+    const float2* __restrict__ lam, const float2* __restrict__ P, const float2* __restrict__ Q,
+    const float2* __restrict__ Cp, const float* __restrict__ dt, float2* __restrict__ ct, int N,
+    int diag, int zoh, int C) {
+  const int h = blockIdx.x, n = threadIdx.x;
+  const bool on = n < N;
+  const double d = (double)dt[h], s = 0.5 * d;
+  cd l = {0.0, 0.0}, p = {0.0, 0.0}, q = {0.0, 0.0}, c = {0.0, 0.0};
+  if (on) {
+    const size_t i = (size_t)h * N + n;
+    l = cd_load(lam, i);
+    c = cd_load(Cp, i);
+    if (!diag) {
+      p = cd_load(P, i);
+      q = cd_load(Q ? Q : P, i);
+    }
+  }
+  const cd d0 = {1.0 - s * l.re, -s * l.im};
+  cd t = {0.0, 0.0};
+  if (on && !diag) t = cd_div(cd_mul({q.re, -q.im}, p), d0);
+  const cd den = {1.0 + s * wave_sum_d(t.re), s * wave_sum_d(t.im)};
+  cd ab = {0.0, 0.0}, e = {0.0, 0.0}, g = {0.0, 0.0};
+  const cd qc = {q.re, -q.im};
+  if (on) {
+    ab = cd_div({1.0 + s * l.re, s * l.im}, d0);
+    if (zoh) {
+      const double ex = exp(d * l.re);
+      double sn, cs;
+      sincos(d * l.im, &sn, &cs);
+      ab = {ex * cs, ex * sn};
+    }
+    e = cd_div({s * p.re, s * p.im}, d0);
+    g = cd_div(e, den);
+  }
+  float2* out = ct + (size_t)h * C * N;
+  for (int tau = 0; tau < C; ++tau) {
+    const cd cg = cd_mul(c, g);
+    const cd sg = {wave_sum_d(cg.re), wave_sum_d(cg.im)};
+    const cd t1 = cd_mul(sg, qc);
+    const cd c1 = {c.re - t1.re, c.im - t1.im};
+    const cd ce = cd_mul(c1, e);
+    const cd se = {wave_sum_d(ce.re), wave_sum_d(ce.im)};
+    const cd a1 = cd_mul(c1, ab), t2 = cd_mul(se, qc);
+    c = {a1.re - t2.re, a1.im - t2.im};
+    if (on) out[(size_t)tau * N + n] = make_float2((float)c.re, (float)c.im);
+  }
+}
+
+// y[b][h][c C + tau] += Re(c_tau . s_{b,c}) for the chunks c < nfull of every
+// batch row b: thread tau of block (tau tile, h) keeps c_tau in registers
+// and takes each chunk state, uniform over the block, as scalars.
+constexpr int kCorrTau = 256;
+
+__global__ __launch_bounds__(kCorrTau) void recurrent_correct_kernel(
+    const float2* __restrict__ ct, const float2* __restrict__ cst, float* __restrict__ y, int H,
+    int batch, int N, int T, int C, int nc, int nfull) {
+  constexpr int D = kPowDim;
+  const int h = blockIdx.y, tau = blockIdx.x * kCorrTau + threadIdx.x;
+  const bool on = tau < C;
+  float2 cv[D];
+  const float2* cr = ct + ((size_t)h * C + (on ? tau : 0)) * N;
+#pragma unroll
+  for (int n = 0; n < D; ++n) cv[n] = (n < N) ? cr[n] : make_float2(0.f, 0.f);
+  for (int b = 0; b < batch; ++b) {
+    const size_t row = (size_t)b * H + h;
+    for (int c = 0; c < nfull; ++c) {
+      const float2* __restrict__ sv = cst + (row * nc + c) * D;   // zero beyond N
+      float acc = 0.f;
+#pragma unroll
+      for (int n = 0; n < D; ++n) acc = fmaf(cv[n].x, sv[n].x, fmaf(-cv[n].y, sv[n].y, acc));
+      if (on) y[row * T + (size_t)c * C + tau] += acc;
+    }
   }
 }
 
@@ -448,25 +533,30 @@ hipError_t launch_recurrent_prepare(const s4dplr_plan* p, const float* lam, cons
         reinterpret_cast<const float2*>(lam), reinterpret_cast<const float2*>(P),
         reinterpret_cast<const float2*>(Q), dt, reinterpret_cast<float2*>(ws + p->off_rpow), p->N,
         diag, zoh, log2C);
+    recurrent_ctab_kernel<<<p->H, 64, 0, s>>>(
+        reinterpret_cast<const float2*>(lam), reinterpret_cast<const float2*>(P),
+        reinterpret_cast<const float2*>(Q), reinterpret_cast<const float2*>(C), dt,
+        reinterpret_cast<float2*>(ws + p->off_rct), p->N, diag, zoh, p->rchunk);
   }
   return hipGetLastError();
 }
 
 namespace {
 
-// One launch of the scan kernel over vrows = rows * nc groups.
+// One launch of the scan kernel over vrows = rows * ncl groups (chunks
+// [c0, c0 + ncl) of the nc chunks of every row).
 struct ScanArgs {
   const float* D;
   const float* u;
   float* state;
   float* y;
-  int T, C, nc, mode;
+  int T, C, nc, c0, ncl, mode;
   float2* cst;
 };
 
 template <int PPL, int LOG2G>
 void scan_launch(const s4dplr_plan* p, const ScanArgs& a, unsigned char* ws, hipStream_t s) {
-  const int vrows = p->batch * p->H * a.nc;
+  const int vrows = p->batch * p->H * a.ncl;
   const float4* rec = reinterpret_cast<const float4*>(ws + p->off_rrec);
   const float4* chan = reinterpret_cast<const float4*>(ws + p->off_rchan);
   float2* st = reinterpret_cast<float2*>(a.state);
@@ -474,10 +564,12 @@ void scan_launch(const s4dplr_plan* p, const ScanArgs& a, unsigned char* ws, hip
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   if (p->flags & S4DPLR_DIAGONAL)
     recurrent_scan_kernel<PPL, LOG2G, true><<<blocks, 256, 0, s>>>(
-        rec, chan, a.D, a.u, st, a.y, p->H, vrows, p->N, a.T, a.C, a.nc, a.mode, a.cst);
+        rec, chan, a.D, a.u, st, a.y, p->H, vrows, p->N, a.T, a.C, a.nc, a.c0, a.ncl, a.mode,
+        a.cst);
   else
     recurrent_scan_kernel<PPL, LOG2G, false><<<blocks, 256, 0, s>>>(
-        rec, chan, a.D, a.u, st, a.y, p->H, vrows, p->N, a.T, a.C, a.nc, a.mode, a.cst);
+        rec, chan, a.D, a.u, st, a.y, p->H, vrows, p->N, a.T, a.C, a.nc, a.c0, a.ncl, a.mode,
+        a.cst);
 }
 
 template <int PPL>
@@ -496,7 +588,7 @@ bool scan_dispatch_g(int lg, const s4dplr_plan* p, const ScanArgs& a, unsigned c
 
 bool scan_dispatch(const s4dplr_plan* p, const ScanArgs& a, unsigned char* ws, hipStream_t s) {
   int ppl, lg;
-  recurrent_shape(p->N, (long)p->batch * p->H * a.nc, &ppl, &lg);
+  recurrent_shape(p->N, (long)p->batch * p->H * a.ncl, &ppl, &lg);
   switch (ppl) {
     case 1: return scan_dispatch_g<1>(lg, p, a, ws, s);
     case 2: return scan_dispatch_g<2>(lg, p, a, ws, s);
@@ -510,10 +602,13 @@ bool scan_dispatch(const s4dplr_plan* p, const ScanArgs& a, unsigned char* ws, h
 
 // Sequences alone give few lanes when batch * H is small, and each lane then
 // walks all T steps in order.  With the plan's chunk length C (N <= 64, few
-// sequences) a scan of at least two chunks runs as three launches: every
-// chunk from a zero state (its final state f_c), the carries
-// s_{c+1} = A-bar^C s_c + f_c per sequence, and every chunk again from s_c,
-// writing y.  The result is the same linear recurrence.
+// sequences) a scan of at least two chunks runs as three or four launches,
+// the same linear recurrence:
+//   1. every chunk from a zero state: its zero-state output and final state f_c;
+//   2. the carries s_{c+1} = A-bar^C s_c + f_c of every row (s_0 = state);
+//   3. y += Re(c_tau . s_c) on every full chunk (c_tau = C A-bar^(tau+1));
+//   4. a shorter last chunk again from its carry, writing y and the final
+//      state (with a full last chunk the carries give the final state).
 hipError_t launch_recurrent_scan(const s4dplr_plan* p, const float* D, const float* u,
                                  float* state, float* y, int T, unsigned char* ws,
                                  hipStream_t s) {
@@ -521,16 +616,22 @@ hipError_t launch_recurrent_scan(const s4dplr_plan* p, const float* D, const flo
   const int nc = C > 0 ? (T + C - 1) / C : 1;
   if (C > 0 && nc >= 2 && nc <= p->rnc) {
     float2* cst = reinterpret_cast<float2*>(ws + p->off_rcs);
-    const ScanArgs local{D, u, state, y, T, C, nc, kScanLocal, cst};
+    const ScanArgs local{D, u, state, y, T, C, nc, 0, nc, kScanLocal, cst};
     if (!scan_dispatch(p, local, ws, s)) return hipErrorInvalidValue;
+    const int full = T % C == 0;
     recurrent_carry_kernel<<<p->batch * p->H, 64, 0, s>>>(
-        reinterpret_cast<const float2*>(ws + p->off_rpow), reinterpret_cast<const float2*>(state),
-        cst, p->H, p->N, nc);
-    const ScanArgs carried{D, u, state, y, T, C, nc, kScanCarried, cst};
-    if (!scan_dispatch(p, carried, ws, s)) return hipErrorInvalidValue;
+        reinterpret_cast<const float2*>(ws + p->off_rpow), reinterpret_cast<float2*>(state), cst,
+        p->H, p->N, nc, full);
+    recurrent_correct_kernel<<<dim3((C + kCorrTau - 1) / kCorrTau, p->H), kCorrTau, 0, s>>>(
+        reinterpret_cast<const float2*>(ws + p->off_rct), cst, y, p->H, p->batch, p->N, T, C, nc,
+        full ? nc : nc - 1);
+    if (!full) {   // a shorter last chunk: scanned again from its carry
+      const ScanArgs last{D, u, state, y, T, C, nc, nc - 1, 1, kScanCarried, cst};
+      if (!scan_dispatch(p, last, ws, s)) return hipErrorInvalidValue;
+    }
     return hipGetLastError();
   }
-  const ScanArgs whole{D, u, state, y, T, T, 1, kScanWhole, nullptr};
+  const ScanArgs whole{D, u, state, y, T, T, 1, 0, 1, kScanWhole, nullptr};
   if (!scan_dispatch(p, whole, ws, s)) return hipErrorInvalidValue;
   return hipGetLastError();
 }
