@@ -489,8 +489,8 @@ __global__ __launch_bounds__(64) void recurrent_ctab_kernel(
   }
 }
 
-// y[b][h][c C + tau] += Re(c_tau . s_{b,c}) for the chunks c < nfull of every
-// batch row b: thread tau of block (tau tile, h) keeps c_tau in registers
+// y[b][h][c C + tau] += Re(c_tau . s_{b,c}) for the chunks c < nfull of
+// batch row b: thread tau of block (tau tile, h, b) keeps c_tau in registers
 // and takes each chunk state, uniform over the block, as scalars.
 constexpr int kCorrTau = 256;
 
@@ -504,8 +504,8 @@ __global__ __launch_bounds__(kCorrTau) void recurrent_correct_kernel(
   const float2* cr = ct + ((size_t)h * C + (on ? tau : 0)) * N;
 #pragma unroll
   for (int n = 0; n < D; ++n) cv[n] = (n < N) ? cr[n] : make_float2(0.f, 0.f);
-  for (int b = 0; b < batch; ++b) {
-    const size_t row = (size_t)b * H + h;
+  {
+    const size_t row = (size_t)blockIdx.z * H + h;
     for (int c = 0; c < nfull; ++c) {
       const float2* __restrict__ sv = cst + (row * nc + c) * D;   // zero beyond N
       float acc = 0.f;
@@ -622,7 +622,8 @@ hipError_t launch_recurrent_scan(const s4dplr_plan* p, const float* D, const flo
     recurrent_carry_kernel<<<p->batch * p->H, 64, 0, s>>>(
         reinterpret_cast<const float2*>(ws + p->off_rpow), reinterpret_cast<float2*>(state), cst,
         p->H, p->N, nc, full);
-    recurrent_correct_kernel<<<dim3((C + kCorrTau - 1) / kCorrTau, p->H), kCorrTau, 0, s>>>(
+    recurrent_correct_kernel<<<dim3((C + kCorrTau - 1) / kCorrTau, p->H, p->batch), kCorrTau, 0,
+                               s>>>(
         reinterpret_cast<const float2*>(ws + p->off_rct), cst, y, p->H, p->batch, p->N, T, C, nc,
         full ? nc : nc - 1);
     if (!full) {   // a shorter last chunk: scanned again from its carry
