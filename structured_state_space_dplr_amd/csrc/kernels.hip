@@ -82,7 +82,12 @@ template <int LOG2L>
 struct KgenShape {
   static constexpr int L = 1 << LOG2L;
   static constexpr int F = L >= 512 ? 2 : 1;               // frequencies per thread
-  static constexpr int NTHR = L / F < 256 ? 256 : L / F;
+  static constexpr int NF = L / F < 256 ? 256 : L / F;     // threads over the frequencies
+  // L >= 512: the poles are split in two halves over two sets of NF threads
+  // (four waves per SIMD for the Cauchy sums, each wave reading half the
+  // pole records), the halves' sums meeting in LDS
+  static constexpr int PS = LOG2L >= 9 ? 2 : 1;
+  static constexpr int NTHR = NF * PS;
   static constexpr int T = L / 16;
   static constexpr int P = fft_num_passes(LOG2L);
   static constexpr int MP = lds_padded_size(L);
@@ -133,15 +138,20 @@ __global__ __launch_bounds__(KgenShape<LOG2L>::NTHR) void kgen_wave_kernel(
   __shared__ float4 rec[FROM_TIME ? 1 : kRec * kMaxPoles];
   __shared__ float2 red[NTHR / 64];
   __shared__ float2 buf[S::MP];
+  __shared__ float xs[(FROM_TIME || S::PS == 1) ? 1 : S::NF * S::F * 8];
   const int h = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63;
   const bool fft_lane = tid < T;          // lanes of wave 0 that hold the transform
   float2 v[16], wA[16], wB[16];
-  // everything the serial tail reads from memory is fetched up front
-  if (fft_lane) {
-    if constexpr (P > 2) WPass<LOG2L, 1>::load_tw(wA, tw, lane);
-    WPass<LOG2L, P - 1>::load_tw(wB, tw, lane);
-  }
+  // the serial tail's twiddles: fetched up front when the Cauchy sums do not
+  // need the registers (one set of poles per thread), else after the sums
+  auto load_tail_tw = [&]() {
+    if (fft_lane) {
+      if constexpr (P > 2) WPass<LOG2L, 1>::load_tw(wA, tw, lane);
+      WPass<LOG2L, P - 1>::load_tw(wB, tw, lane);
+    }
+  };
+  if constexpr (S::PS == 1 || FROM_TIME) load_tail_tw();
   constexpr int NW = (L / 2 + NTHR) / NTHR;     // bin pairs per thread in the weight step
   float2 csj[NW], csm[NW];
 #pragma unroll
@@ -159,21 +169,44 @@ __global__ __launch_bounds__(KgenShape<LOG2L>::NTHR) void kgen_wave_kernel(
     const float dt = pp.dt[h];
     const float2 nyq = make_float2(0.5f * dt * sum.x, 0.5f * dt * sum.y);
     {
-      constexpr int F = S::F;
+      constexpr int F = S::F, NF = S::NF;
+      const int ft = tid % NF, ph = tid / NF;     // frequency thread, pole half
       float T0[F], G[F], acc[F][8];
 #pragma unroll
       for (int f = 0; f < F; ++f) {
-        const int l = tid + f * NTHR;
+        const int l = ft + f * NF;
         T0[f] = l < L ? tanT[l] : 0.f;
         G[f] = (2.0f / dt) * T0[f];
 #pragma unroll
         for (int a = 0; a < 8; ++a) acc[f][a] = 0.f;
       }
-      cauchy_sums<F, DIAG>(rec, NP, G, acc);
+      if constexpr (S::PS == 2) {
+        const int nmid = (NP / 2) / kPoleUnroll * kPoleUnroll;
+        if (ph == 0) cauchy_sums<F, DIAG>(rec, nmid, G, acc);
+        else cauchy_sums<F, DIAG>(rec + kRec * nmid, NP - nmid, G, acc);
+        load_tail_tw();
+        if (ph == 1) {
 #pragma unroll
-      for (int f = 0; f < F; ++f) {
-        const int l = tid + f * NTHR;
-        if (l < L) buf[lds_pad(l)] = cauchy_epilogue<DIAG>(acc[f], T0[f], 2 * l == L, nyq);
+          for (int f = 0; f < F; ++f)
+#pragma unroll
+            for (int a = 0; a < 8; ++a) xs[(f * 8 + a) * NF + ft] = acc[f][a];
+        }
+        __syncthreads();
+        if (ph == 0) {
+#pragma unroll
+          for (int f = 0; f < F; ++f)
+#pragma unroll
+            for (int a = 0; a < 8; ++a) acc[f][a] += xs[(f * 8 + a) * NF + ft];
+        }
+      } else {
+        cauchy_sums<F, DIAG>(rec, NP, G, acc);
+      }
+      if (ph == 0) {
+#pragma unroll
+        for (int f = 0; f < F; ++f) {
+          const int l = ft + f * NF;
+          if (l < L) buf[lds_pad(l)] = cauchy_epilogue<DIAG>(acc[f], T0[f], 2 * l == L, nyq);
+        }
       }
     }
     __syncthreads();
