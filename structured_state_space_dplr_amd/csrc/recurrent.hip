@@ -489,32 +489,65 @@ __global__ __launch_bounds__(64) void recurrent_ctab_kernel(
   }
 }
 
-// y[b][h][c C + tau] += Re(c_tau . s_{b,c}) for the chunks c < nfull of
-// batch row b: thread tau of block (tau tile, h, b) keeps c_tau in registers
-// and takes each chunk state, uniform over the block, as scalars.
-constexpr int kCorrTau = 256;
+// y[b][h][c C + tau] += Re(c_tau . s_{b,c}) for the chunks c < nfull, as a
+// matrix product on the fp32 matrix cores per channel:
+// y[m][tau] += sum_k A[m][k] Bt[k][tau] over the rows m = (b, c),
+// c < nfull, with k = 2n + p interleaving the parts,
+//   A[m][2n] = Re s_{b,c}[n],  A[m][2n+1] = -Im s_{b,c}[n],
+//   Bt[2n][tau] = Re c_tau[n], Bt[2n+1][tau] = Im c_tau[n].
+// Block (32 steps tau, 128 rows m, channel h): the 128 x 32 tile of Bt in
+// LDS, wave w the rows [32 w, 32 w + 32) of the group, one 32 x 32 tile of
+// v_mfma_f32_32x32x2_f32 products (lane l feeds A[l % 32][k0 + l / 32] and
+// Bt[k0 + l / 32][l % 32]; accumulator register r holds row
+// 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32).
+typedef float v16f_r __attribute__((ext_vector_type(16)));
 
-__global__ __launch_bounds__(kCorrTau) void recurrent_correct_kernel(
+__global__ __launch_bounds__(256) void recurrent_correct_mfma_kernel(
     const float2* __restrict__ ct, const float2* __restrict__ cst, float* __restrict__ y, int H,
     int batch, int N, int T, int C, int nc, int nfull) {
   constexpr int D = kPowDim;
-  const int h = blockIdx.y, tau = blockIdx.x * kCorrTau + threadIdx.x;
-  const bool on = tau < C;
-  float2 cv[D];
-  const float2* cr = ct + ((size_t)h * C + (on ? tau : 0)) * N;
-#pragma unroll
-  for (int n = 0; n < D; ++n) cv[n] = (n < N) ? cr[n] : make_float2(0.f, 0.f);
-  {
-    const size_t row = (size_t)blockIdx.z * H + h;
-    for (int c = 0; c < nfull; ++c) {
-      const float2* __restrict__ sv = cst + (row * nc + c) * D;   // zero beyond N
-      float acc = 0.f;
-#pragma unroll
-      for (int n = 0; n < D; ++n) acc = fmaf(cv[n].x, sv[n].x, fmaf(-cv[n].y, sv[n].y, acc));
-      if (on) y[row * T + (size_t)c * C + tau] += acc;
+  __shared__ float sb[2 * D][32];
+  const int h = blockIdx.z, tau0 = blockIdx.x * 32, tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int M = batch * nfull;
+  // Bt tile: k in [0, 128), tau in [tau0, tau0 + 32)
+  for (int idx = tid; idx < 2 * D * 32; idx += 256) {
+    const int kk = idx >> 5, tt = idx & 31, n = kk >> 1, tau = tau0 + tt;
+    float v = 0.f;
+    if (n < N && tau < C) {
+      const float2 c = ct[((size_t)h * C + tau) * N + n];
+      v = (kk & 1) ? c.y : c.x;
     }
+    sb[kk][tt] = v;
+  }
+  // A rows of this wave: m = m0 + lane % 32
+  const int m0 = (blockIdx.y * 4 + w) * 32;
+  const int m = m0 + (lane & 31), part = lane >> 5;
+  const bool mon = m < M;
+  const int bm = mon ? m / nfull : 0, cm = mon ? m - bm * nfull : 0;
+  const float* sr = reinterpret_cast<const float*>(cst + (((size_t)bm * H + h) * nc + cm) * D);
+  float av[D];
+#pragma unroll
+  for (int n = 0; n < D; ++n) {
+    const float v = mon ? sr[2 * n + part] : 0.f;
+    av[n] = part ? -v : v;
+  }
+  __syncthreads();
+  v16f_r acc = {};
+#pragma unroll
+  for (int n = 0; n < D; ++n)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[n], sb[2 * n + part][lane & 31], acc, 0, 0, 0);
+  const int tau = tau0 + (lane & 31);
+  if (tau >= C) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int mr = m0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    if (mr >= M) continue;
+    const int b = mr / nfull, c = mr - b * nfull;
+    y[((size_t)b * H + h) * T + (size_t)c * C + tau] += acc[r];
   }
 }
+
 
 hipError_t launch_recurrent_prepare(const s4dplr_plan* p, const float* lam, const float* P,
                                     const float* Q, const float* B, const float* C,
@@ -622,10 +655,11 @@ hipError_t launch_recurrent_scan(const s4dplr_plan* p, const float* D, const flo
     recurrent_carry_kernel<<<p->batch * p->H, 64, 0, s>>>(
         reinterpret_cast<const float2*>(ws + p->off_rpow), reinterpret_cast<float2*>(state), cst,
         p->H, p->N, nc, full);
-    recurrent_correct_kernel<<<dim3((C + kCorrTau - 1) / kCorrTau, p->H, p->batch), kCorrTau, 0,
-                               s>>>(
+    const int nfull = full ? nc : nc - 1;
+    const int mrows = p->batch * nfull;
+    recurrent_correct_mfma_kernel<<<dim3((C + 31) / 32, (mrows + 127) / 128, p->H), 256, 0, s>>>(
         reinterpret_cast<const float2*>(ws + p->off_rct), cst, y, p->H, p->batch, p->N, T, C, nc,
-        full ? nc : nc - 1);
+        nfull);
     if (!full) {   // a shorter last chunk: scanned again from its carry
       const ScanArgs last{D, u, state, y, T, C, nc, nc - 1, 1, kScanCarried, cst};
       if (!scan_dispatch(p, last, ws, s)) return hipErrorInvalidValue;
