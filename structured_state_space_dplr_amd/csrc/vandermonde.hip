@@ -6,9 +6,11 @@
 // (B-bar_n = dt B_n at Lambda_n = 0), for k = 0 .. L-1: the kernel itself, not
 // an aliased one.
 //
-// Each thread owns kVanderTaps consecutive taps: it forms W A-bar^k0 once per
-// pole (exp of k0 z with the phase reduced modulo 2 pi in fp64, so the
-// rounding does not grow with k0) and steps the rest by complex products.
+// Each thread owns TAPS consecutive taps (16, or 32 for L >= 4096, where
+// the per-pole start below is then spread over twice the taps): it forms
+// W A-bar^k0 once per pole (exp of k0 z with the phase reduced modulo 2 pi in
+// fp64, so the rounding does not grow with k0) and steps the rest by complex
+// products.
 //
 // Backward: with S0_n = sum_k dK_k conj(A-bar_n)^k and
 // S1_n = sum_k k dK_k conj(A-bar_n)^k, and grad(v) = dloss/dRe v + i dloss/dIm v,
@@ -28,7 +30,6 @@ namespace s4 {
 
 namespace {
 
-constexpr int kVanderTaps = 16;                    // consecutive taps per thread
 constexpr int kVanderKT = 64;                      // tap threads per block (one wave)
 constexpr int kVanderPG = 4;                       // pole groups per block (waves)
 constexpr int kVanderThreads = kVanderKT * kVanderPG;
@@ -88,13 +89,14 @@ __device__ __forceinline__ float2 power_of(double zre, double zim, double k) {
 
 // Pole records in LDS: (W re, W im, A-bar re, A-bar im) and (z re, z im) in fp64.
 // Block (tap range, h): wave g sums the poles n = g, g + kVanderPG, ... for
-// kVanderTaps taps per lane; the waves' partial sums meet in LDS.
+// TAPS taps per lane; the waves' partial sums meet in LDS.
+template <int TAPS>
 __global__ __launch_bounds__(kVanderThreads) void vander_kernel(
     const float2* __restrict__ lam, const float2* __restrict__ B, const float2* __restrict__ C,
     const float* __restrict__ dt, float* __restrict__ K, int N, int L) {
   __shared__ float4 wa[kMaxPolesZoh];
   __shared__ double2 zz[kMaxPolesZoh];
-  __shared__ float red[kVanderPG][kVanderKT][kVanderTaps + 1];
+  __shared__ float red[kVanderPG][kVanderKT][TAPS + 1];
   const int h = blockIdx.y, tid = threadIdx.x;
   const double d = (double)dt[h];
   for (int n = tid; n < N; n += kVanderThreads) {
@@ -108,10 +110,10 @@ __global__ __launch_bounds__(kVanderThreads) void vander_kernel(
   }
   __syncthreads();
   const int kt = tid % kVanderKT, pg = tid / kVanderKT;
-  const int k0 = (blockIdx.x * kVanderKT + kt) * kVanderTaps;
-  float acc[kVanderTaps];
+  const int k0 = (blockIdx.x * kVanderKT + kt) * TAPS;
+  float acc[TAPS];
 #pragma unroll
-  for (int j = 0; j < kVanderTaps; ++j) acc[j] = 0.f;
+  for (int j = 0; j < TAPS; ++j) acc[j] = 0.f;
   if (k0 < L) {
     for (int n = pg; n < N; n += kVanderPG) {
       const float4 r = wa[n];
@@ -119,17 +121,17 @@ __global__ __launch_bounds__(kVanderThreads) void vander_kernel(
       const float2 a = make_float2(r.z, r.w);
       float2 q = cmul(make_float2(r.x, r.y), power_of(z.x, z.y, (double)k0));
 #pragma unroll
-      for (int j = 0; j < kVanderTaps; ++j) {
+      for (int j = 0; j < TAPS; ++j) {
         acc[j] += q.x;
         q = cmul(q, a);
       }
     }
   }
 #pragma unroll
-  for (int j = 0; j < kVanderTaps; ++j) red[pg][kt][j] = acc[j];
+  for (int j = 0; j < TAPS; ++j) red[pg][kt][j] = acc[j];
   __syncthreads();
   // thread (kt, pg) finishes taps [pg T/G, (pg + 1) T/G) of its tap range
-  constexpr int TPG = kVanderTaps / kVanderPG;
+  constexpr int TPG = TAPS / kVanderPG;
   if (k0 < L) {
     float* out = K + (size_t)h * L + k0;
 #pragma unroll
@@ -252,11 +254,15 @@ __global__ __launch_bounds__(256) void vander_bwd_final_kernel(
 
 hipError_t launch_vandermonde(const s4dplr_plan* p, const float* lam, const float* B,
                               const float* C, const float* dt, float* K, hipStream_t s) {
-  const int per_block = kVanderKT * kVanderTaps;
-  const dim3 grid((p->L + per_block - 1) / per_block, p->H);
-  vander_kernel<<<grid, kVanderThreads, 0, s>>>(
-      reinterpret_cast<const float2*>(lam), reinterpret_cast<const float2*>(B),
-      reinterpret_cast<const float2*>(C), dt, K, p->N, p->L);
+  auto run = [&](auto kern, int taps) {
+    const int per_block = kVanderKT * taps;
+    const dim3 grid((p->L + per_block - 1) / per_block, p->H);
+    kern<<<grid, kVanderThreads, 0, s>>>(
+        reinterpret_cast<const float2*>(lam), reinterpret_cast<const float2*>(B),
+        reinterpret_cast<const float2*>(C), dt, K, p->N, p->L);
+  };
+  if (p->L >= 4096) run(vander_kernel<32>, 32);
+  else run(vander_kernel<16>, 16);
   return hipGetLastError();
 }
 
