@@ -26,8 +26,6 @@ struct BigShape {
   static constexpr int M = 1 << LOG2M;
   static constexpr int LOG2M2 = 8, M2 = 256;
   static constexpr int LOG2M1 = LOG2M - 8, M1 = M / 256;
-  static constexpr int CT = kBigThreads / (M1 / 16);   // columns per block (16 threads each)
-  static constexpr int CP = lds_padded_size(M1);        // padded column length
   static constexpr int RP = lds_padded_size(M2);        // padded row length
   static constexpr int RT = kBigThreads / (M2 / 16);   // rows per block (16)
   static_assert(LOG2M >= 15 && LOG2M <= 16, "four-step range");
@@ -57,65 +55,162 @@ __device__ __forceinline__ float2 big_rfft_x(float2 zj, float2 zmj, float2 csj) 
 }
 
 // ---------------------------------------------------------------------------
-// Forward column step on real rows x (L floats, packed z_k = x_2k + i x_2k+1,
-// z zero for k >= M/2): Y[row][k1][n2] = W_M^{n2 k1} sum_{n1} z[M2 n1 + n2] W_M1^{n1 k1}
+// Column steps.  A task is CT = 256/T adjacent columns n2 of one logical row,
+// T = M1/16 lanes per column, 16 points per lane:
+//   * global reads with the column index fastest (whole cache lines), straight
+//     into the first radix-16 pass (input n1 = la + T r in lane la);
+//   * LDS, then the remaining pass with the T lanes of a column inside one
+//     wave; its outputs go back to LDS in natural order;
+//   * global writes with the column index fastest.
+// Blocks are persistent (a few per CU) and the next task's input is in flight
+// while the current one is transformed.  Logical row h*batch + b reads or
+// writes memory row b*H + h of the [batch][H][L] arrays (batch = 1: row h).
 // ---------------------------------------------------------------------------
 template <int LOG2M>
-__global__ __launch_bounds__(kBigThreads) void big_cols_fwd_kernel(
-    const float* __restrict__ x, float2* __restrict__ Y, const float2* __restrict__ tw1,
-    const float2* __restrict__ tw4) {
+struct ColShape {
   using S = BigShape<LOG2M>;
-  constexpr int M = S::M, M1 = S::M1, M2 = S::M2, CT = S::CT, CP = S::CP;
+  static constexpr int LOG2M1 = S::LOG2M1, M1 = S::M1, M2 = S::M2;
+  static constexpr int T = M1 / 16;                  // lanes per column
+  static constexpr int CT = kBigThreads / T;         // columns per task
+  static constexpr int NG = M2 / CT;                 // tasks per logical row
+  static constexpr int CP = lds_padded_size(M1);
+  static_assert(fft_num_passes(LOG2M1) == 2 && fft_radix_log(LOG2M1, 0) == 4, "two passes");
+};
+constexpr int kColBlocks = 256 * 4;   // four resident blocks per CU (LDS-bound)
+
+template <int LOG2M>
+static int col_blocks(int rows) {
+  const int ntask = rows * ColShape<LOG2M>::NG;
+  return ntask < kColBlocks ? ntask : kColBlocks;
+}
+
+__device__ __forceinline__ size_t mem_row(int lrow, int H, int batch) {
+  const int h = lrow / batch, b = lrow - h * batch;
+  return (size_t)b * H + h;
+}
+
+// Forward column step on real rows x (L floats, packed z_k = x_2k + i x_2k+1,
+// z zero for k >= M/2): Y[row][k1][n2] = W_M^{n2 k1} sum_{n1} z[M2 n1 + n2] W_M1^{n1 k1}
+template <int LOG2M>
+__global__ __launch_bounds__(kBigThreads, 4) void big_cols_fwd_kernel(
+    const float* __restrict__ x, float2* __restrict__ Y, const float2* __restrict__ tw1,
+    const float2* __restrict__ tw4, int rows, int H, int batch) {
+  using C = ColShape<LOG2M>;
+  using P0 = WPass<C::LOG2M1, 0>;
+  using P1 = WPass<C::LOG2M1, 1>;
+  constexpr int M = BigShape<LOG2M>::M, M2 = C::M2, T = C::T, CT = C::CT, NG = C::NG,
+                CP = C::CP;
   __shared__ float2 lds[CT * CP];
   __shared__ TwM twm;
-  const int tid = threadIdx.x, row = blockIdx.y, c0 = blockIdx.x * CT;
+  const int tid = threadIdx.x;
+  const int ca = tid % CT, la = tid / CT;    // global side: column fastest
+  const int cb = tid / T, lb = tid % T;      // transform side: a column's lanes in one wave
   load_twM(twm, tw4, tid, kBigThreads);
-  const float2* __restrict__ z = reinterpret_cast<const float2*>(x + (size_t)row * M);
-  for (int idx = tid; idx < M1 * CT; idx += kBigThreads) {
-    const int n1 = idx / CT, c = idx % CT;
-    lds[c * CP + lds_pad(n1)] = (n1 < M1 / 2) ? z[M2 * n1 + c0 + c] : make_float2(0.f, 0.f);
-  }
+  PassTwiddles<C::LOG2M1, 1> pt;
+  pt.load(tw1, lb);
+  const int ntask = rows * NG;
+  float2 pre[8];
+  auto fetch = [&](int task) {
+    const int lrow = task / NG, g = task - lrow * NG;
+    const float2* __restrict__ z =
+        reinterpret_cast<const float2*>(x + mem_row(lrow, H, batch) * M) + g * CT + ca;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) pre[r] = z[M2 * (la + T * r)];   // n1 < M1/2
+  };
+  int task = blockIdx.x;
+  if (task < ntask) fetch(task);
   __syncthreads();
-  lds_fft<S::LOG2M1, false>(lds + (tid / (M1 / 16)) * CP, tid % (M1 / 16), true, tw1);
-  float2* __restrict__ Yr = Y + (size_t)row * M;
-  for (int idx = tid; idx < M1 * CT; idx += kBigThreads) {
-    const int k1 = idx / CT, c = idx % CT, n2 = c0 + c;
-    Yr[k1 * M2 + n2] = cmul(lds[c * CP + lds_pad(k1)], w_M(twm, n2 * k1));
+  for (; task < ntask; task += gridDim.x) {
+    float2 v[16];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) v[r] = pre[r];
+    if (task + (int)gridDim.x < ntask) fetch(task + gridDim.x);
+    dft16_fwd_half_input(v);
+    P0::store(v, lds + ca * CP, la);
+    __syncthreads();
+    P1::load(v, lds + cb * CP, lb);
+    {
+      float2 w1[16];
+      pt.expand(w1);
+      P1::template compute<false>(v, w1);
+    }
+    wave_sync();
+    P1::store(v, lds + cb * CP, lb);
+    __syncthreads();
+    const int lrow = task / NG, n2 = (task - lrow * NG) * CT + ca;
+    float2* __restrict__ Yr = Y + (size_t)lrow * M + n2;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int k1 = la + T * r;
+      Yr[k1 * M2] = cmul(lds[ca * CP + lds_pad(k1)], w_M(twm, n2 * k1));
+    }
+    __syncthreads();
   }
 }
 
-// ---------------------------------------------------------------------------
 // Inverse column step: x[M2 n1 + n2] = sum_{k1} Y[k1][n2] W_M1^{-n1 k1}.
 // MODE 0: outputs n < M/2 as (y_2n, y_2n+1) (the kept half of the causal
 // convolution).  MODE 1: all n, real part times `scale` (time-domain kernel).
-// ---------------------------------------------------------------------------
 template <int LOG2M, int MODE>
-__global__ __launch_bounds__(kBigThreads) void big_cols_inv_kernel(
+__global__ __launch_bounds__(kBigThreads, 4) void big_cols_inv_kernel(
     const float2* __restrict__ Y, float* __restrict__ out, const float2* __restrict__ tw1,
-    float scale) {
-  using S = BigShape<LOG2M>;
-  constexpr int M = S::M, M1 = S::M1, M2 = S::M2, CT = S::CT, CP = S::CP;
+    int rows, int H, int batch, float scale) {
+  using C = ColShape<LOG2M>;
+  using P0 = WPass<C::LOG2M1, 0>;
+  using P1 = WPass<C::LOG2M1, 1>;
+  constexpr int M = BigShape<LOG2M>::M, M2 = C::M2, T = C::T, CT = C::CT, NG = C::NG,
+                CP = C::CP;
   __shared__ float2 lds[CT * CP];
-  const int tid = threadIdx.x, row = blockIdx.y, c0 = blockIdx.x * CT;
-  const float2* __restrict__ Yr = Y + (size_t)row * M;
-  for (int idx = tid; idx < M1 * CT; idx += kBigThreads) {
-    const int k1 = idx / CT, c = idx % CT;
-    lds[c * CP + lds_pad(k1)] = Yr[k1 * M2 + c0 + c];
-  }
-  __syncthreads();
-  lds_fft<S::LOG2M1, true>(lds + (tid / (M1 / 16)) * CP, tid % (M1 / 16), true, tw1);
-  if constexpr (MODE == 0) {
-    float2* __restrict__ yr = reinterpret_cast<float2*>(out + (size_t)row * M);
-    for (int idx = tid; idx < (M1 / 2) * CT; idx += kBigThreads) {
-      const int n1 = idx / CT, c = idx % CT;
-      yr[M2 * n1 + c0 + c] = lds[c * CP + lds_pad(n1)];
+  const int tid = threadIdx.x;
+  const int ca = tid % CT, la = tid / CT;
+  const int cb = tid / T, lb = tid % T;
+  PassTwiddles<C::LOG2M1, 1> pt;
+  pt.load(tw1, lb);
+  const int ntask = rows * NG;
+  float2 pre[16];
+  auto fetch = [&](int task) {
+    const int lrow = task / NG, g = task - lrow * NG;
+    const float2* __restrict__ Yr = Y + (size_t)lrow * M + g * CT + ca;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pre[r] = Yr[M2 * (la + T * r)];
+  };
+  int task = blockIdx.x;
+  if (task < ntask) fetch(task);
+  for (; task < ntask; task += gridDim.x) {
+    float2 v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = pre[r];
+    if (task + (int)gridDim.x < ntask) fetch(task + gridDim.x);
+    dft_dif<16, true>(v);
+    P0::store(v, lds + ca * CP, la);
+    __syncthreads();
+    P1::load(v, lds + cb * CP, lb);
+    {
+      float2 w1[16];
+      pt.expand(w1);
+      P1::template compute<true>(v, w1);
     }
-  } else {
-    float* __restrict__ kr = out + (size_t)row * M;
-    for (int idx = tid; idx < M1 * CT; idx += kBigThreads) {
-      const int n1 = idx / CT, c = idx % CT;
-      kr[M2 * n1 + c0 + c] = lds[c * CP + lds_pad(n1)].x * scale;
+    wave_sync();
+    P1::store(v, lds + cb * CP, lb);
+    __syncthreads();
+    const int lrow = task / NG, n2 = (task - lrow * NG) * CT + ca;
+    if constexpr (MODE == 0) {
+      float2* __restrict__ yr =
+          reinterpret_cast<float2*>(out + mem_row(lrow, H, batch) * M) + n2;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int n1 = la + T * r;     // < M1/2
+        yr[M2 * n1] = lds[ca * CP + lds_pad(n1)];
+      }
+    } else {
+      float* __restrict__ kr = out + mem_row(lrow, H, batch) * M + n2;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int n1 = la + T * r;
+        kr[M2 * n1] = lds[ca * CP + lds_pad(n1)].x * scale;
+      }
     }
+    __syncthreads();
   }
 }
 
@@ -149,10 +244,22 @@ __global__ __launch_bounds__(kBigThreads) void big_rows_inv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Paired row steps.  A block takes 8 pair tasks t (rows k1 = t and M1 - t,
-// t = 0 .. M1/2) into 16 LDS slots and runs the forward row DFTs.
+// Paired row steps, one pair task per 16-lane group and no workgroup barrier
+// after the twiddle table is in LDS.  Task (h, t, b), t = 0 .. M1/2, takes
+// rows ka = t and kb = M1 - t (mod M1) of logical row h*batch + b; the
+// tasks are numbered with b fastest, so the groups of one wave that share a
+// channel read the same weights in the same instructions.
+// Lane lt runs the 256-point transforms of row ka as transform lane lt and of
+// row kb as transform lane lb = 15 - lt (t = 0: lb = -lt mod 16).  After the
+// forward passes the lane holds bins k2 = lt + 16 s of row ka, and the
+// real-FFT partner of each, bin M2-1-k2 (row 0: -k2) of row kb, is bin
+// lb + 16 (15 - s) of row kb in the same lane (t = 0, lt = 0: bin
+// 16 ((16 - s) mod 16) of row 0 itself).  Tasks t = 0 and t = M1/2 pair a row
+// with itself: the lane's row-ka bins are then the whole row and only they
+// are kept.
 //   CONV:  spectral weights Z'_k = alpha_k Z_k + beta_k conj(Z_{M-k}), the
-//          inverse row DFTs and the inverse twiddle, back into Y.
+//          inverse row DFTs (the lane's bins are exactly its first inverse
+//          pass input) and the inverse twiddle, back into Y.
 //   !CONV: the spectrum of (K + D delta) padded to 2L and the weights
 //          alpha, beta of every bin, written in the permuted layout.
 // ---------------------------------------------------------------------------
@@ -160,52 +267,125 @@ template <int LOG2M, bool CONV>
 __global__ __launch_bounds__(kBigThreads) void big_rows_pair_kernel(
     float2* __restrict__ Y, float4* __restrict__ coefp, const float* __restrict__ D,
     const float2* __restrict__ tw2, const float2* __restrict__ cs,
-    const float2* __restrict__ tw4, int batch, int conj) {
+    const float2* __restrict__ tw4, int nh, int batch, int conj) {
   using S = BigShape<LOG2M>;
-  constexpr int M = S::M, M1 = S::M1, M2 = S::M2, RP = S::RP;
-  constexpr int TASKS = 8;
-  __shared__ float2 lds[2 * TASKS * RP];
+  using P0 = WPass<8, 0>;
+  using P1 = WPass<8, 1>;
+  static_assert(S::M2 == 256 && P0::T == 16 && P1::NS == 16, "256-point rows, 16 lanes");
+  constexpr int M = S::M, M1 = S::M1, M2 = S::M2;
+  constexpr int MP = lds_padded_size(M2);
+  constexpr int G = kBigThreads / 16;      // pair tasks per block
+  constexpr int TP = M1 / 2 + 1;           // pair tasks per logical row
+  __shared__ float2 lds[G * 2 * MP];
   __shared__ TwM twm;
-  const int tid = threadIdx.x, row = blockIdx.y, t0 = blockIdx.x * TASKS;
-  if constexpr (CONV) load_twM(twm, tw4, tid, kBigThreads);
-  const int h = CONV ? row / batch : row;     // logical rows: h*batch + b
-  float2* __restrict__ Yr = Y + (size_t)row * M;
-  auto slot_row = [&](int s) -> int {
-    const int t = t0 + s / 2;
-    return (s & 1) ? ((M1 - t) & (M1 - 1)) : t;
-  };
-  auto task_valid = [&](int s) -> bool { return t0 + s / 2 <= M1 / 2; };
-  for (int idx = tid; idx < 2 * TASKS * M2; idx += kBigThreads) {
-    const int s = idx / M2, k = idx % M2;
-    lds[s * RP + lds_pad(k)] = task_valid(s) ? Yr[slot_row(s) * M2 + k] : make_float2(0.f, 0.f);
+  const int tid = threadIdx.x, grp = tid >> 4, lt = tid & 15;
+  if constexpr (CONV) {
+    load_twM(twm, tw4, tid, kBigThreads);
+    __syncthreads();
   }
-  __syncthreads();
-  lds_fft<S::LOG2M2, false>(lds + (tid / 16) * RP, tid % 16, true, tw2);
-  // pairs: every item (task i, k2) of slot a = 2i meets (slot b = 2i+1, k2p)
-  const float4* __restrict__ cfh = coefp + (size_t)h * M;
-  const float sc = 0.5f / (float)M;
-  const float Dh = (!CONV && D) ? D[h] : 0.f;
-  for (int idx = tid; idx < TASKS * M2; idx += kBigThreads) {
-    const int i = idx / M2, k2 = idx % M2, t = t0 + i;
-    if (t > M1 / 2) continue;
-    const int ka = t, kb = (M1 - t) & (M1 - 1);
-    const bool self = (ka == kb);
-    const int k2p = (ka == 0) ? ((M2 - k2) & (M2 - 1)) : (M2 - 1 - k2);
-    if (self && k2p < k2) continue;
-    float2* A = lds + (2 * i) * RP;
-    float2* B = self ? A : lds + (2 * i + 1) * RP;
-    const float2 za = A[lds_pad(k2)], zb = B[lds_pad(k2p)];
-    if constexpr (CONV) {
-      const float4 ca = cfh[ka * M2 + k2], cb = cfh[kb * M2 + k2p];
-      const float2 oa = cadd(cmul(make_float2(ca.x, ca.y), za), cmul(make_float2(ca.z, ca.w), cconj(zb)));
-      const float2 ob = cadd(cmul(make_float2(cb.x, cb.y), zb), cmul(make_float2(cb.z, cb.w), cconj(za)));
-      A[lds_pad(k2)] = oa;
-      if (!(self && k2p == k2)) B[lds_pad(k2p)] = ob;
-    } else {
-      const int kk = ka + M1 * k2;          // bin of slot a
+  const int task = blockIdx.x * G + grp;
+  if (task >= nh * TP * batch) return;
+  const int b = task % batch, ht = task / batch, t = ht % TP, h = ht / TP;
+  const int ka = t, kb = (M1 - t) & (M1 - 1);
+  const bool self = ka == kb;
+  const int lb = (t == 0) ? ((16 - lt) & 15) : 15 - lt;
+  const bool sp = (t == 0) && (lt == 0);
+  float2* __restrict__ Yr = Y + (size_t)(h * batch + b) * M;
+  float2* __restrict__ bufA = lds + grp * 2 * MP;
+  float2* __restrict__ bufB = bufA + MP;
+  float2 za[16], zb[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    za[r] = Yr[ka * M2 + lt + 16 * r];
+    zb[r] = Yr[kb * M2 + lb + 16 * r];
+  }
+  PassTwiddles<8, 1> pta, ptb;
+  pta.load(tw2, lt);
+  ptb.load(tw2, lb);
+  // forward pass 0 (span 1, no twiddles), then pass 1 through LDS
+  dft_dif<16, false>(za);
+  dft_dif<16, false>(zb);
+  P0::store(za, bufA, lt);
+  P0::store(zb, bufB, lb);
+  float4 ca[16], cb[16];
+  if constexpr (CONV) {
+    const float4* __restrict__ cfh = coefp + (size_t)h * M;
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2) {
+      ca[s2] = cfh[ka * M2 + lt + 16 * s2];
+      cb[s2] = cfh[kb * M2 + lb + 16 * s2];
+    }
+  }
+  wave_sync();
+  P1::load(za, bufA, lt);
+  P1::load(zb, bufB, lb);
+  {
+    float2 w[16];
+    pta.expand(w);
+    P1::template compute<false>(za, w);
+    ptb.expand(w);
+    P1::template compute<false>(zb, w);
+  }
+  // bin lt + 16 s of row ka is za[bitrev(s)]; its partner is pz[s]
+  float2 pz[16];
+#pragma unroll
+  for (int s2 = 0; s2 < 16; ++s2)
+    pz[s2] = sp ? zb[bitrev<4>((16 - s2) & 15)] : zb[bitrev<4>(15 - s2)];
+  if constexpr (CONV) {
+    // weighted bins in natural order: oa[s] = Z'(lt + 16 s) of row ka,
+    // ob[s] = Z'(lb + 16 s) of row kb (whose partners, for the tasks that
+    // keep row kb, are the row-ka bins lt + 16 (15 - s))
+    float2 oa[16], ob[16];
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2) {
+      const float4 c = ca[s2], d = cb[s2];
+      oa[s2] = cadd(cmul(make_float2(c.x, c.y), za[bitrev<4>(s2)]),
+                    cmul(make_float2(c.z, c.w), cconj(pz[s2])));
+      ob[s2] = cadd(cmul(make_float2(d.x, d.y), zb[bitrev<4>(s2)]),
+                    cmul(make_float2(d.z, d.w), cconj(za[bitrev<4>(15 - s2)])));
+    }
+    // inverse pass 0: input x[lt + 16 r] = bin lt + 16 r, already in this lane
+    dft_dif<16, true>(oa);
+    dft_dif<16, true>(ob);
+    wave_sync();
+    P0::store(oa, bufA, lt);
+    P0::store(ob, bufB, lb);
+    wave_sync();
+    P1::load(oa, bufA, lt);
+    P1::load(ob, bufB, lb);
+    {
+      float2 w[16];
+      pta.expand(w);
+      P1::template compute<true>(oa, w);
+      ptb.expand(w);
+      P1::template compute<true>(ob, w);
+    }
+    // output n2 = lt + 16 s (row kb: lb + 16 s) in [bitrev(s)]
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2) {
+      const int n2 = lt + 16 * s2;
+      Yr[ka * M2 + n2] = cmulc(oa[bitrev<4>(s2)], w_M(twm, n2 * ka));
+    }
+    if (!self) {
+#pragma unroll
+      for (int s2 = 0; s2 < 16; ++s2) {
+        const int n2 = lb + 16 * s2;
+        Yr[kb * M2 + n2] = cmulc(ob[bitrev<4>(s2)], w_M(twm, n2 * kb));
+      }
+    }
+  } else {
+    const float sc = 0.5f / (float)M;
+    const float Dh = D ? D[h] : 0.f;
+    float4* __restrict__ cfh = coefp + (size_t)h * M;
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2) {
+      const int k2 = lt + 16 * s2;
+      const int k2p = sp ? ((16 - s2) & 15) * 16 : lb + 16 * (15 - s2);   // partner's k2
+      const float2 za_ = za[bitrev<4>(s2)], zb_ = pz[s2];
+      const int kk = ka + M1 * k2;          // bin of row ka
       const int km = M - kk;                // its partner, in [1, M]
       const float2 csa = cs[kk], csb = cs[km];
-      float2 sa = big_rfft_x(za, zb, csa), sb = big_rfft_x(zb, za, csb);
+      float2 sa = big_rfft_x(za_, zb_, csa), sb = big_rfft_x(zb_, za_, csb);
       sa.x += Dh;
       sb.x += Dh;
       if (conj) {   // weights of the correlation with (K + D delta)
@@ -213,28 +393,17 @@ __global__ __launch_bounds__(kBigThreads) void big_rows_pair_kernel(
         sb.y = -sb.y;
       }
       {
-        const float a = sc * (1.0f - csa.y), b = sc * (1.0f + csa.y), c = sc * csa.x;
-        const float2 al = make_float2(fmaf(a, sa.x, b * sb.x), fmaf(a, sa.y, -b * sb.y));
+        const float a = sc * (1.0f - csa.y), bb = sc * (1.0f + csa.y), c = sc * csa.x;
+        const float2 al = make_float2(fmaf(a, sa.x, bb * sb.x), fmaf(a, sa.y, -bb * sb.y));
         const float2 df = make_float2(sa.x - sb.x, sa.y + sb.y);
-        coefp[(size_t)h * M + ka * M2 + k2] = make_float4(al.x, al.y, -c * df.y, c * df.x);
+        cfh[ka * M2 + k2] = make_float4(al.x, al.y, -c * df.y, c * df.x);
       }
-      if (km < M && km != kk) {
-        const float a = sc * (1.0f - csb.y), b = sc * (1.0f + csb.y), c = sc * csb.x;
-        const float2 al = make_float2(fmaf(a, sb.x, b * sa.x), fmaf(a, sb.y, -b * sa.y));
+      if (!self) {
+        const float a = sc * (1.0f - csb.y), bb = sc * (1.0f + csb.y), c = sc * csb.x;
+        const float2 al = make_float2(fmaf(a, sb.x, bb * sa.x), fmaf(a, sb.y, -bb * sa.y));
         const float2 df = make_float2(sb.x - sa.x, sb.y + sa.y);
-        coefp[(size_t)h * M + kb * M2 + k2p] = make_float4(al.x, al.y, -c * df.y, c * df.x);
+        cfh[kb * M2 + k2p] = make_float4(al.x, al.y, -c * df.y, c * df.x);
       }
-    }
-  }
-  if constexpr (CONV) {
-    __syncthreads();
-    lds_fft<S::LOG2M2, true>(lds + (tid / 16) * RP, tid % 16, true, tw2);
-    for (int idx = tid; idx < 2 * TASKS * M2; idx += kBigThreads) {
-      const int s = idx / M2, n2 = idx % M2;
-      if (!task_valid(s)) continue;
-      const int k1 = slot_row(s);
-      if ((s & 1) && k1 == slot_row(s - 1)) continue;    // self-paired task: slot a only
-      Yr[k1 * M2 + n2] = cmulc(lds[s * RP + lds_pad(n2)], w_M(twm, n2 * k1));
     }
   }
 }
@@ -248,17 +417,25 @@ __global__ __launch_bounds__(kBigThreads) void big_rows_pair_kernel(
 template <typename T>
 static T* wat(unsigned char* ws, size_t off) { return reinterpret_cast<T*>(ws + off); }
 
+// blocks of the paired row step: M1/2 + 1 pair tasks per logical row, one per
+// 16-lane group
+template <int LOG2M>
+static int pair_blocks(int rows) {
+  constexpr int TP = BigShape<LOG2M>::M1 / 2 + 1, G = kBigThreads / 16;
+  return (rows * TP + G - 1) / G;
+}
+
 template <int LOG2M>
 static void big_spectrum_from_time(const s4dplr_plan* p, const float* Ktime, const float* D,
                                    unsigned char* ws, hipStream_t s, int conj) {
-  using S = BigShape<LOG2M>;
   float2* Y = wat<float2>(ws, p->off_big);
   const float2* cs = wat<const float2>(ws, p->off_cs);
   const float2* tw4 = wat<const float2>(ws, p->off_tw4);
-  big_cols_fwd_kernel<LOG2M><<<dim3(S::M2 / S::CT, p->H), kBigThreads, 0, s>>>(
-      Ktime, Y, wat<const float2>(ws, p->off_tw1), tw4);
-  big_rows_pair_kernel<LOG2M, false><<<dim3((S::M1 / 2 + 1 + 7) / 8, p->H), kBigThreads, 0, s>>>(
-      Y, wat<float4>(ws, p->off_coef), D, wat<const float2>(ws, p->off_tw2), cs, tw4, 1, conj);
+  big_cols_fwd_kernel<LOG2M><<<col_blocks<LOG2M>(p->H), kBigThreads, 0, s>>>(
+      Ktime, Y, wat<const float2>(ws, p->off_tw1), tw4, p->H, p->H, 1);
+  big_rows_pair_kernel<LOG2M, false><<<pair_blocks<LOG2M>(p->H), kBigThreads, 0, s>>>(
+      Y, wat<float4>(ws, p->off_coef), D, wat<const float2>(ws, p->off_tw2), cs, tw4, p->H, 1,
+      conj);
 }
 
 template <int LOG2M>
@@ -272,8 +449,8 @@ static void big_kspec(const s4dplr_plan* p, const float* Ktime, const float* D, 
     big_rows_inv_kernel<LOG2M><<<dim3(S::M1 / S::RT, p->H), kBigThreads, 0, s>>>(
         wat<const float2>(ws, p->off_khat), Y, wat<const float2>(ws, p->off_tw2),
         wat<const float2>(ws, p->off_tw4));
-    big_cols_inv_kernel<LOG2M, 1><<<dim3(S::M2 / S::CT, p->H), kBigThreads, 0, s>>>(
-        Y, K, wat<const float2>(ws, p->off_tw1), 1.0f / (float)S::M);
+    big_cols_inv_kernel<LOG2M, 1><<<col_blocks<LOG2M>(p->H), kBigThreads, 0, s>>>(
+        Y, K, wat<const float2>(ws, p->off_tw1), p->H, p->H, 1, 1.0f / (float)S::M);
     Ktime = K;
   }
   big_spectrum_from_time<LOG2M>(p, Ktime, D, ws, s, conj);
@@ -287,71 +464,20 @@ hipError_t launch_big_kspec(const s4dplr_plan* p, const float* Ktime, const floa
   return hipGetLastError();
 }
 
-// Column kernels for the convolution need the memory row of a logical row;
-// they are instantiated over a row-remapping wrapper below.
-template <int LOG2M>
-__global__ __launch_bounds__(kBigThreads) void big_conv_cols_fwd_kernel(
-    const float* __restrict__ u, float2* __restrict__ Y, const float2* __restrict__ tw1,
-    const float2* __restrict__ tw4, int H, int batch) {
-  using S = BigShape<LOG2M>;
-  constexpr int M = S::M, M1 = S::M1, M2 = S::M2, CT = S::CT, CP = S::CP;
-  __shared__ float2 lds[CT * CP];
-  __shared__ TwM twm;
-  const int tid = threadIdx.x, lrow = blockIdx.y, c0 = blockIdx.x * CT;
-  load_twM(twm, tw4, tid, kBigThreads);
-  const int h = lrow / batch, b = lrow - h * batch;
-  const float2* __restrict__ z = reinterpret_cast<const float2*>(u + ((size_t)b * H + h) * M);
-  for (int idx = tid; idx < M1 * CT; idx += kBigThreads) {
-    const int n1 = idx / CT, c = idx % CT;
-    lds[c * CP + lds_pad(n1)] = (n1 < M1 / 2) ? z[M2 * n1 + c0 + c] : make_float2(0.f, 0.f);
-  }
-  __syncthreads();
-  lds_fft<S::LOG2M1, false>(lds + (tid / (M1 / 16)) * CP, tid % (M1 / 16), true, tw1);
-  float2* __restrict__ Yr = Y + (size_t)lrow * M;
-  for (int idx = tid; idx < M1 * CT; idx += kBigThreads) {
-    const int k1 = idx / CT, c = idx % CT, n2 = c0 + c;
-    Yr[k1 * M2 + n2] = cmul(lds[c * CP + lds_pad(k1)], w_M(twm, n2 * k1));
-  }
-}
-
-template <int LOG2M>
-__global__ __launch_bounds__(kBigThreads) void big_conv_cols_inv_kernel(
-    const float2* __restrict__ Y, float* __restrict__ y, const float2* __restrict__ tw1, int H,
-    int batch) {
-  using S = BigShape<LOG2M>;
-  constexpr int M = S::M, M1 = S::M1, M2 = S::M2, CT = S::CT, CP = S::CP;
-  __shared__ float2 lds[CT * CP];
-  const int tid = threadIdx.x, lrow = blockIdx.y, c0 = blockIdx.x * CT;
-  const int h = lrow / batch, b = lrow - h * batch;
-  const float2* __restrict__ Yr = Y + (size_t)lrow * M;
-  for (int idx = tid; idx < M1 * CT; idx += kBigThreads) {
-    const int k1 = idx / CT, c = idx % CT;
-    lds[c * CP + lds_pad(k1)] = Yr[k1 * M2 + c0 + c];
-  }
-  __syncthreads();
-  lds_fft<S::LOG2M1, true>(lds + (tid / (M1 / 16)) * CP, tid % (M1 / 16), true, tw1);
-  float2* __restrict__ yr = reinterpret_cast<float2*>(y + ((size_t)b * H + h) * M);
-  for (int idx = tid; idx < (M1 / 2) * CT; idx += kBigThreads) {
-    const int n1 = idx / CT, c = idx % CT;
-    yr[M2 * n1 + c0 + c] = lds[c * CP + lds_pad(n1)];
-  }
-}
-
 template <int LOG2M>
 static void big_conv(const s4dplr_plan* p, const float* u, float* y, unsigned char* ws,
                      hipStream_t s) {
-  using S = BigShape<LOG2M>;
   const int rows = p->batch * p->H;
   float2* Y = wat<float2>(ws, p->off_big);
   const float2* cs = wat<const float2>(ws, p->off_cs);
   const float2* tw4 = wat<const float2>(ws, p->off_tw4);
-  big_conv_cols_fwd_kernel<LOG2M><<<dim3(S::M2 / S::CT, rows), kBigThreads, 0, s>>>(
-      u, Y, wat<const float2>(ws, p->off_tw1), tw4, p->H, p->batch);
-  big_rows_pair_kernel<LOG2M, true><<<dim3((S::M1 / 2 + 1 + 7) / 8, rows), kBigThreads, 0, s>>>(
+  big_cols_fwd_kernel<LOG2M><<<col_blocks<LOG2M>(rows), kBigThreads, 0, s>>>(
+      u, Y, wat<const float2>(ws, p->off_tw1), tw4, rows, p->H, p->batch);
+  big_rows_pair_kernel<LOG2M, true><<<pair_blocks<LOG2M>(rows), kBigThreads, 0, s>>>(
       Y, wat<float4>(ws, p->off_coef), nullptr, wat<const float2>(ws, p->off_tw2), cs, tw4,
-      p->batch, 0);
-  big_conv_cols_inv_kernel<LOG2M><<<dim3(S::M2 / S::CT, rows), kBigThreads, 0, s>>>(
-      Y, y, wat<const float2>(ws, p->off_tw1), p->H, p->batch);
+      p->H, p->batch, 0);
+  big_cols_inv_kernel<LOG2M, 0><<<col_blocks<LOG2M>(rows), kBigThreads, 0, s>>>(
+      Y, y, wat<const float2>(ws, p->off_tw1), rows, p->H, p->batch, 1.0f);
 }
 
 // ---------------------------------------------------------------------------
@@ -460,9 +586,11 @@ static void big_corr(const s4dplr_plan* p, const float* u, const float* dy, floa
   const float2* tw2 = wat<const float2>(ws, p->off_tw2);
   const float2* tw4 = wat<const float2>(ws, p->off_tw4);
   const float2* cs = wat<const float2>(ws, p->off_cs);
-  const dim3 cgrid(S::M2 / S::CT, rows), rgrid(S::M1 / S::RT, rows);
-  big_conv_cols_fwd_kernel<LOG2M><<<cgrid, kBigThreads, 0, s>>>(u, Yu, tw1, tw4, p->H, p->batch);
-  big_conv_cols_fwd_kernel<LOG2M><<<cgrid, kBigThreads, 0, s>>>(dy, Yg, tw1, tw4, p->H, p->batch);
+  const dim3 rgrid(S::M1 / S::RT, rows);
+  big_cols_fwd_kernel<LOG2M><<<col_blocks<LOG2M>(rows), kBigThreads, 0, s>>>(u, Yu, tw1, tw4,
+                                                                             rows, p->H, p->batch);
+  big_cols_fwd_kernel<LOG2M><<<col_blocks<LOG2M>(rows), kBigThreads, 0, s>>>(dy, Yg, tw1, tw4,
+                                                                             rows, p->H, p->batch);
   big_rows_fwd_kernel<LOG2M><<<rgrid, kBigThreads, 0, s>>>(Yu, tw2);
   big_rows_fwd_kernel<LOG2M><<<rgrid, kBigThreads, 0, s>>>(Yg, tw2);
   float2* Wb = wat<float2>(ws, p->off_khat);
@@ -471,8 +599,8 @@ static void big_corr(const s4dplr_plan* p, const float* u, const float* dy, floa
   // inverse: rows then columns, the first M/2 outputs as (c_2n, c_2n+1)
   float* out = dK ? dK : wat<float>(ws, p->off_kbuf);
   big_rows_inv_kernel<LOG2M><<<dim3(S::M1 / S::RT, p->H), kBigThreads, 0, s>>>(Wb, Yu, tw2, tw4);
-  big_cols_inv_kernel<LOG2M, 0><<<dim3(S::M2 / S::CT, p->H), kBigThreads, 0, s>>>(Yu, out, tw1,
-                                                                                 1.0f);
+  big_cols_inv_kernel<LOG2M, 0><<<col_blocks<LOG2M>(p->H), kBigThreads, 0, s>>>(
+      Yu, out, tw1, p->H, p->H, 1, 1.0f);
   if (dD) big_first_col_kernel<<<(p->H + 255) / 256, 256, 0, s>>>(out, dD, p->H, p->L);
 }
 
@@ -481,8 +609,8 @@ static void big_ghat(const s4dplr_plan* p, const float* dK, float2* ghat, unsign
                      hipStream_t s) {
   using S = BigShape<LOG2M>;
   float2* Y = wat<float2>(ws, p->off_big);
-  big_cols_fwd_kernel<LOG2M><<<dim3(S::M2 / S::CT, p->H), kBigThreads, 0, s>>>(
-      dK, Y, wat<const float2>(ws, p->off_tw1), wat<const float2>(ws, p->off_tw4));
+  big_cols_fwd_kernel<LOG2M><<<col_blocks<LOG2M>(p->H), kBigThreads, 0, s>>>(
+      dK, Y, wat<const float2>(ws, p->off_tw1), wat<const float2>(ws, p->off_tw4), p->H, p->H, 1);
   big_rows_fwd_kernel<LOG2M><<<dim3(S::M1 / S::RT, p->H), kBigThreads, 0, s>>>(
       Y, wat<const float2>(ws, p->off_tw2));
   big_ghat_kernel<LOG2M><<<dim3(S::M / kBigThreads, p->H), kBigThreads, 0, s>>>(
