@@ -26,8 +26,6 @@ struct BigShape {
   static constexpr int M = 1 << LOG2M;
   static constexpr int LOG2M2 = 8, M2 = 256;
   static constexpr int LOG2M1 = LOG2M - 8, M1 = M / 256;
-  static constexpr int RP = lds_padded_size(M2);        // padded row length
-  static constexpr int RT = kBigThreads / (M2 / 16);   // rows per block (16)
   static_assert(LOG2M >= 15 && LOG2M <= 16, "four-step range");
 };
 
@@ -45,6 +43,10 @@ __device__ __forceinline__ void load_twM(TwM& t, const float2* __restrict__ tw4,
 __device__ __forceinline__ float2 w_M(const TwM& t, int m) {
   return cmul(t.hi[m >> 8], t.lo[m & 255]);
 }
+
+// (cos, sin)(pi s / 16), s < 16
+__device__ constexpr float kCos32[16] = {1.000000000e+00f, 9.807852804e-01f, 9.238795325e-01f, 8.314696123e-01f, 7.071067812e-01f, 5.555702330e-01f, 3.826834324e-01f, 1.950903220e-01f, 0.0f, -1.950903220e-01f, -3.826834324e-01f, -5.555702330e-01f, -7.071067812e-01f, -8.314696123e-01f, -9.238795325e-01f, -9.807852804e-01f};
+__device__ constexpr float kSin32[16] = {0.000000000e+00f, 1.950903220e-01f, 3.826834324e-01f, 5.555702330e-01f, 7.071067812e-01f, 8.314696123e-01f, 9.238795325e-01f, 9.807852804e-01f, 1.000000000e+00f, 9.807852804e-01f, 9.238795325e-01f, 8.314696123e-01f, 7.071067812e-01f, 5.555702330e-01f, 3.826834324e-01f, 1.950903220e-01f};
 
 // (1 -+ i W_{2M}^j)/2 applied to the pair (Z_j, Z_{M-j}): the bin X_j of the
 // real transform of length 2M; csj = (cos, sin)(pi j / M).
@@ -215,32 +217,63 @@ __global__ __launch_bounds__(kBigThreads, 4) void big_cols_inv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Row step of the inverse transform alone (time-domain kernel from the
-// generating function, stored in the permuted layout by the Cauchy kernel):
-// Y[k1][n2] = W_M^{-n2 k1} sum_{k2} X[k1][k2] W_M2^{-n2 k2}
+// Row step alone, one 256-point row per 16-lane group (no workgroup barrier
+// after the twiddle table is in LDS):
+//   forward (!INV): Z[k1][k2] = sum_{n2} Y[k1][n2] W_M2^{n2 k2}, in place (the
+//                   column step has applied the twiddle); bin k1 + M1 k2 is
+//                   left at k1 M2 + k2;
+//   inverse (INV):  Y[k1][n2] = W_M^{-n2 k1} sum_{k2} X[k1][k2] W_M2^{-n2 k2}
+//                   (X in the permuted layout, e.g. the generating function).
+// Every lane reads and writes the same 16 points of its row, so X may be Y.
 // ---------------------------------------------------------------------------
-template <int LOG2M>
-__global__ __launch_bounds__(kBigThreads) void big_rows_inv_kernel(
-    const float2* __restrict__ X, float2* __restrict__ Y, const float2* __restrict__ tw2,
-    const float2* __restrict__ tw4) {
+template <int LOG2M, bool INV>
+__global__ __launch_bounds__(kBigThreads) void big_rows_kernel(
+    const float2* X, float2* Y, const float2* __restrict__ tw2, const float2* __restrict__ tw4,
+    int rows) {
   using S = BigShape<LOG2M>;
-  constexpr int M = S::M, M2 = S::M2, RT = S::RT, RP = S::RP;
-  __shared__ float2 lds[RT * RP];
+  using P0 = WPass<8, 0>;
+  using P1 = WPass<8, 1>;
+  constexpr int M = S::M, M1 = S::M1, M2 = S::M2, MP = lds_padded_size(M2);
+  constexpr int G = kBigThreads / 16;
+  __shared__ float2 lds[G * MP];
   __shared__ TwM twm;
-  const int tid = threadIdx.x, row = blockIdx.y, r0 = blockIdx.x * RT;
-  load_twM(twm, tw4, tid, kBigThreads);
-  const float2* __restrict__ Xr = X + (size_t)row * M;
-  for (int idx = tid; idx < RT * M2; idx += kBigThreads) {
-    const int s = idx / M2, k2 = idx % M2;
-    lds[s * RP + lds_pad(k2)] = Xr[(r0 + s) * M2 + k2];
+  const int tid = threadIdx.x, grp = tid >> 4, lt = tid & 15;
+  if constexpr (INV) {
+    load_twM(twm, tw4, tid, kBigThreads);
+    __syncthreads();
   }
-  __syncthreads();
-  lds_fft<S::LOG2M2, true>(lds + (tid / 16) * RP, tid % 16, true, tw2);
-  float2* __restrict__ Yr = Y + (size_t)row * M;
-  for (int idx = tid; idx < RT * M2; idx += kBigThreads) {
-    const int s = idx / M2, n2 = idx % M2, k1 = r0 + s;
-    Yr[k1 * M2 + n2] = cmulc(lds[s * RP + lds_pad(n2)], w_M(twm, n2 * k1));
+  const int task = blockIdx.x * G + grp;
+  if (task >= rows * M1) return;
+  const int lrow = task / M1, k1 = task - lrow * M1;
+  const float2* Xr = X + (size_t)lrow * M + k1 * M2;
+  float2 v[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) v[r] = Xr[lt + 16 * r];
+  PassTwiddles<8, 1> pt;
+  pt.load(tw2, lt);
+  float2* buf = lds + grp * MP;
+  dft_dif<16, INV>(v);
+  P0::store(v, buf, lt);
+  wave_sync();
+  P1::load(v, buf, lt);
+  {
+    float2 w[16];
+    pt.expand(w);
+    P1::template compute<INV>(v, w);
   }
+  float2* Yr = Y + (size_t)lrow * M + k1 * M2;
+#pragma unroll
+  for (int s2 = 0; s2 < 16; ++s2) {
+    const int n = lt + 16 * s2;
+    float2 o = v[bitrev<4>(s2)];
+    if constexpr (INV) o = cmulc(o, w_M(twm, n * k1));
+    Yr[n] = o;
+  }
+}
+
+template <int LOG2M>
+static int rows_blocks(int rows) {
+  return (rows * BigShape<LOG2M>::M1 + kBigThreads / 16 - 1) / (kBigThreads / 16);
 }
 
 // ---------------------------------------------------------------------------
@@ -377,14 +410,16 @@ __global__ __launch_bounds__(kBigThreads) void big_rows_pair_kernel(
     const float sc = 0.5f / (float)M;
     const float Dh = D ? D[h] : 0.f;
     float4* __restrict__ cfh = coefp + (size_t)h * M;
+    const float2 cs0 = cs[ka + M1 * lt];
 #pragma unroll
     for (int s2 = 0; s2 < 16; ++s2) {
       const int k2 = lt + 16 * s2;
       const int k2p = sp ? ((16 - s2) & 15) * 16 : lb + 16 * (15 - s2);   // partner's k2
       const float2 za_ = za[bitrev<4>(s2)], zb_ = pz[s2];
-      const int kk = ka + M1 * k2;          // bin of row ka
-      const int km = M - kk;                // its partner, in [1, M]
-      const float2 csa = cs[kk], csb = cs[km];
+      // cs_k = (cos, sin)(pi k / M) for k = ka + M1 (lt + 16 s) is cs of the
+      // lane's first bin turned by pi s / 16; cs_{M-k} = (-cos, sin)(pi k / M)
+      const float2 csa = cmul(cs0, make_float2(kCos32[s2], kSin32[s2]));
+      const float2 csb = make_float2(-csa.x, csa.y);
       float2 sa = big_rfft_x(za_, zb_, csa), sb = big_rfft_x(zb_, za_, csb);
       sa.x += Dh;
       sb.x += Dh;
@@ -446,9 +481,9 @@ static void big_kspec(const s4dplr_plan* p, const float* Ktime, const float* D, 
     // inverse transform of the generating function (permuted layout) -> K
     float2* Y = wat<float2>(ws, p->off_big);
     float* K = Kout ? Kout : wat<float>(ws, p->off_kbuf);
-    big_rows_inv_kernel<LOG2M><<<dim3(S::M1 / S::RT, p->H), kBigThreads, 0, s>>>(
+    big_rows_kernel<LOG2M, true><<<rows_blocks<LOG2M>(p->H), kBigThreads, 0, s>>>(
         wat<const float2>(ws, p->off_khat), Y, wat<const float2>(ws, p->off_tw2),
-        wat<const float2>(ws, p->off_tw4));
+        wat<const float2>(ws, p->off_tw4), p->H);
     big_cols_inv_kernel<LOG2M, 1><<<col_blocks<LOG2M>(p->H), kBigThreads, 0, s>>>(
         Y, K, wat<const float2>(ws, p->off_tw1), p->H, p->H, 1, 1.0f / (float)S::M);
     Ktime = K;
@@ -481,29 +516,8 @@ static void big_conv(const s4dplr_plan* p, const float* u, float* y, unsigned ch
 }
 
 // ---------------------------------------------------------------------------
-// Backward pass for the long path.  Row step of the forward transform alone:
-// Z[k1][k2] = sum_{n2} Y[k1][n2] W_M2^{n2 k2}, in place (the column step has
-// already applied the twiddle), leaving bin k1 + M1 k2 at k1 M2 + k2.
+// Backward pass for the long path.
 // ---------------------------------------------------------------------------
-template <int LOG2M>
-__global__ __launch_bounds__(kBigThreads) void big_rows_fwd_kernel(
-    float2* __restrict__ Y, const float2* __restrict__ tw2) {
-  using S = BigShape<LOG2M>;
-  constexpr int M = S::M, M2 = S::M2, RT = S::RT, RP = S::RP;
-  __shared__ float2 lds[RT * RP];
-  const int tid = threadIdx.x, row = blockIdx.y, r0 = blockIdx.x * RT;
-  float2* __restrict__ Yr = Y + (size_t)row * M;
-  for (int idx = tid; idx < RT * M2; idx += kBigThreads) {
-    const int s = idx / M2, n2 = idx % M2;
-    lds[s * RP + lds_pad(n2)] = Yr[(r0 + s) * M2 + n2];
-  }
-  __syncthreads();
-  lds_fft<S::LOG2M2, false>(lds + (tid / 16) * RP, tid % 16, true, tw2);
-  for (int idx = tid; idx < RT * M2; idx += kBigThreads) {
-    const int s = idx / M2, k2 = idx % M2;
-    Yr[(r0 + s) * M2 + k2] = lds[s * RP + lds_pad(k2)];
-  }
-}
 
 // position of bin k in the permuted layout
 template <int LOG2M>
@@ -516,36 +530,63 @@ __device__ __forceinline__ int big_pos(int k) {
 // conj(U_j) G_j over the spectra of the zero-padded u and dy rows
 // (X_j = big_rfft_x(Z_j, Z_{M-j}), Z_M = Z_0), and the packed inverse input
 //   W_k = (S_k + conj S_{M-k}) / 2 + i e^{i pi k/M} (S_k - conj S_{M-k}) / 2,
-// scaled by 1/M, at the bin's position in the permuted layout.  Thread i takes
-// position i, so the reads of bin k and of its partner M - k (rows k1 and
-// M1 - k1 read backwards, or row 0 with k2 -> -k2) are both contiguous.
+// scaled by 1/M, at the bin's position in the permuted layout.  Block t takes
+// rows k1 = t and M1 - t (t = 0 .. M1/2), thread i the bin at position i of
+// row t and its partner M - k (row M1 - t read backwards, or row 0 with
+// k2 -> -k2), so every spectrum value is read once and both reads are
+// contiguous; the thread writes W at both bins (rows 0 and M1/2 pair with
+// themselves and write only their own bin).
 template <int LOG2M>
 __global__ __launch_bounds__(kBigThreads) void big_corr_kernel(
     const float2* __restrict__ Zu, const float2* __restrict__ Zg, float2* __restrict__ W,
     const float2* __restrict__ cs, int batch) {
   using S = BigShape<LOG2M>;
   constexpr int M = S::M, M1 = S::M1, M2 = S::M2;
-  const int h = blockIdx.y;
-  const int pk = blockIdx.x * kBigThreads + threadIdx.x;     // < M (grid is exact)
-  const int k1 = pk / M2, k2 = pk % M2;
-  const int k = k1 + M1 * k2;
+  static_assert(M2 == kBigThreads, "one thread per bin of a row");
+  const int h = blockIdx.y, t = blockIdx.x, k2 = threadIdx.x;
+  const bool self = t == 0 || t == M1 / 2;
+  const int pk = t * M2 + k2;
+  const int k = t + M1 * k2;
   const int km = M - k;                                       // in [1, M]
   const int pm = big_pos<LOG2M>(km & (M - 1));
-  const float2 ck = cs[k], cm = cs[km];
+  // cs_{M-k} = (cos, sin)(pi - pi k/M) = (-cos, sin)(pi k/M)
+  const float2 ck = cs[k], cm = make_float2(-ck.x, ck.y);
   float2 sk = make_float2(0.f, 0.f), sm = sk;
-  for (int b = 0; b < batch; ++b) {
-    const size_t r = ((size_t)h * batch + b) * M;
-    const float2 uk = Zu[r + pk], um = Zu[r + pm], gk = Zg[r + pk], gm = Zg[r + pm];
-    const float2 Uk = big_rfft_x(uk, um, ck), Gk = big_rfft_x(gk, gm, ck);
-    const float2 Um = big_rfft_x(um, uk, cm), Gm = big_rfft_x(gm, gk, cm);
-    sk = cadd(sk, cmul(cconj(Uk), Gk));
-    sm = cadd(sm, cmul(cconj(Um), Gm));
+  // four batch rows per round, all their loads issued before the products
+  for (int b0 = 0; b0 < batch; b0 += 4) {
+    float2 uk[4], um[4], gk[4], gm[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = b0 + i < batch ? b0 + i : batch - 1;
+      const size_t r = ((size_t)h * batch + b) * M;
+      uk[i] = Zu[r + pk];
+      um[i] = Zu[r + pm];
+      gk[i] = Zg[r + pk];
+      gm[i] = Zg[r + pm];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (b0 + i >= batch) break;
+      const float2 Uk = big_rfft_x(uk[i], um[i], ck), Gk = big_rfft_x(gk[i], gm[i], ck);
+      const float2 Um = big_rfft_x(um[i], uk[i], cm), Gm = big_rfft_x(gm[i], gk[i], cm);
+      sk = cadd(sk, cmul(cconj(Uk), Gk));
+      sm = cadd(sm, cmul(cconj(Um), Gm));
+    }
   }
   const float sc = 0.5f / (float)M;
-  const float2 ek = make_float2(sk.x + sm.x, sk.y - sm.y);
-  const float2 dk = make_float2(sk.x - sm.x, sk.y + sm.y);
-  const float2 wk = cadd(ek, cmul(make_float2(-ck.y, ck.x), dk));
-  W[(size_t)h * M + pk] = make_float2(sc * wk.x, sc * wk.y);
+  float2* __restrict__ Wh = W + (size_t)h * M;
+  {
+    const float2 e = make_float2(sk.x + sm.x, sk.y - sm.y);
+    const float2 d = make_float2(sk.x - sm.x, sk.y + sm.y);
+    const float2 w = cadd(e, cmul(make_float2(-ck.y, ck.x), d));
+    Wh[pk] = make_float2(sc * w.x, sc * w.y);
+  }
+  if (!self) {
+    const float2 e = make_float2(sm.x + sk.x, sm.y - sk.y);
+    const float2 d = make_float2(sm.x - sk.x, sm.y + sk.y);
+    const float2 w = cadd(e, cmul(make_float2(-cm.y, cm.x), d));
+    Wh[pm] = make_float2(sc * w.x, sc * w.y);
+  }
 }
 
 // Ghat_l = FFT_L(dK)_l / L = X_{2l} / L, X the spectrum of dK zero-padded to
@@ -586,19 +627,21 @@ static void big_corr(const s4dplr_plan* p, const float* u, const float* dy, floa
   const float2* tw2 = wat<const float2>(ws, p->off_tw2);
   const float2* tw4 = wat<const float2>(ws, p->off_tw4);
   const float2* cs = wat<const float2>(ws, p->off_cs);
-  const dim3 rgrid(S::M1 / S::RT, rows);
   big_cols_fwd_kernel<LOG2M><<<col_blocks<LOG2M>(rows), kBigThreads, 0, s>>>(u, Yu, tw1, tw4,
                                                                              rows, p->H, p->batch);
   big_cols_fwd_kernel<LOG2M><<<col_blocks<LOG2M>(rows), kBigThreads, 0, s>>>(dy, Yg, tw1, tw4,
                                                                              rows, p->H, p->batch);
-  big_rows_fwd_kernel<LOG2M><<<rgrid, kBigThreads, 0, s>>>(Yu, tw2);
-  big_rows_fwd_kernel<LOG2M><<<rgrid, kBigThreads, 0, s>>>(Yg, tw2);
+  big_rows_kernel<LOG2M, false><<<rows_blocks<LOG2M>(rows), kBigThreads, 0, s>>>(Yu, Yu, tw2,
+                                                                                tw4, rows);
+  big_rows_kernel<LOG2M, false><<<rows_blocks<LOG2M>(rows), kBigThreads, 0, s>>>(Yg, Yg, tw2,
+                                                                                tw4, rows);
   float2* Wb = wat<float2>(ws, p->off_khat);
-  big_corr_kernel<LOG2M><<<dim3(S::M / kBigThreads, p->H), kBigThreads, 0, s>>>(Yu, Yg, Wb, cs,
-                                                                               p->batch);
+  big_corr_kernel<LOG2M><<<dim3(S::M1 / 2 + 1, p->H), kBigThreads, 0, s>>>(Yu, Yg, Wb, cs,
+                                                                           p->batch);
   // inverse: rows then columns, the first M/2 outputs as (c_2n, c_2n+1)
   float* out = dK ? dK : wat<float>(ws, p->off_kbuf);
-  big_rows_inv_kernel<LOG2M><<<dim3(S::M1 / S::RT, p->H), kBigThreads, 0, s>>>(Wb, Yu, tw2, tw4);
+  big_rows_kernel<LOG2M, true><<<rows_blocks<LOG2M>(p->H), kBigThreads, 0, s>>>(Wb, Yu, tw2, tw4,
+                                                                               p->H);
   big_cols_inv_kernel<LOG2M, 0><<<col_blocks<LOG2M>(p->H), kBigThreads, 0, s>>>(
       Yu, out, tw1, p->H, p->H, 1, 1.0f);
   if (dD) big_first_col_kernel<<<(p->H + 255) / 256, 256, 0, s>>>(out, dD, p->H, p->L);
@@ -611,8 +654,8 @@ static void big_ghat(const s4dplr_plan* p, const float* dK, float2* ghat, unsign
   float2* Y = wat<float2>(ws, p->off_big);
   big_cols_fwd_kernel<LOG2M><<<col_blocks<LOG2M>(p->H), kBigThreads, 0, s>>>(
       dK, Y, wat<const float2>(ws, p->off_tw1), wat<const float2>(ws, p->off_tw4), p->H, p->H, 1);
-  big_rows_fwd_kernel<LOG2M><<<dim3(S::M1 / S::RT, p->H), kBigThreads, 0, s>>>(
-      Y, wat<const float2>(ws, p->off_tw2));
+  big_rows_kernel<LOG2M, false><<<rows_blocks<LOG2M>(p->H), kBigThreads, 0, s>>>(
+      Y, Y, wat<const float2>(ws, p->off_tw2), wat<const float2>(ws, p->off_tw4), p->H);
   big_ghat_kernel<LOG2M><<<dim3(S::M / kBigThreads, p->H), kBigThreads, 0, s>>>(
       Y, ghat, wat<const float2>(ws, p->off_cs));
 }
