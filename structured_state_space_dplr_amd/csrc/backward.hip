@@ -205,6 +205,128 @@ __global__ __launch_bounds__(CorrShape<LOG2L>::NT) void corr_spec_kernel(
   }
 }
 
+// Row form of corr_spec_kernel for 2048 <= L <= 8192, with the transform
+// layout of the convolution's block-resident rows: L/16 threads, 16 points
+// each (a_n for n = lt + T r), the data in registers between the LDS
+// exchanges, the sums of the thread's bins in registers, and the next row's
+// samples in flight during the current row.  (At L = 16384 the 1024 threads
+// get 128 VGPRs each, too few for this form.)  After the last
+// pass the thread holds the bins k = lt + T m, m = q + s NB; the sums need
+// k <= L/2 (even bins: m < 8, or m = 8 at lt = 0) and k < L/2 (odd bins:
+// m < 8), the partners L - k and L - 1 - k come from LDS.
+template <int LOG2L>
+__global__ __launch_bounds__(1 << (LOG2L - 4)) void corr_rows_kernel(
+    const float* __restrict__ u, const float* __restrict__ dy, float2* __restrict__ part,
+    const float2* __restrict__ twL, const float2* __restrict__ cs, int H, int batch) {
+  constexpr int L = 1 << LOG2L, T = L / 16, P = fft_num_passes(LOG2L);
+  using FL = WPass<LOG2L, P - 1>;
+  static_assert(LOG2L >= 11 && LOG2L <= 13 && P >= 3, "row form range");
+  __shared__ float2 buf[lds_padded_size(L)];
+  const int h = blockIdx.x, c = blockIdx.y, lt = threadIdx.x;
+  PassTwiddles<LOG2L, 1> pt1;
+  PassTwiddles<LOG2L, (P > 3 ? 2 : 1)> pt2;
+  PassTwiddles<LOG2L, P - 1> ptl;
+  pt1.load(twL, lt);
+  if constexpr (P > 3) pt2.load(twL, lt);
+  ptl.load(twL, lt);
+  const float2 w0 = cs[lt];                       // e^{+i pi lt / L}
+  const int b_first = c * kCorrRows, b_end = min(batch, (c + 1) * kCorrRows);
+  auto pass = [&](float2 (&v)[16], auto pt, auto W) {
+    using Wp = decltype(W);
+    float2 w[16];
+    pt.expand(w);
+    Wp::load(v, buf, lt);
+    __syncthreads();
+    Wp::template compute<false>(v, w);
+    Wp::store(v, buf, lt);
+    __syncthreads();
+  };
+  // forward transform of v (16 points per thread, pass-0 layout); the outputs
+  // stay in v and are also left in LDS in natural order
+  auto transform = [&](float2 (&v)[16]) {
+    dft_dif<16, false>(v);
+    WPass<LOG2L, 0>::store(v, buf, lt);
+    __syncthreads();
+    pass(v, pt1, WPass<LOG2L, 1>{});
+    if constexpr (P > 3) pass(v, pt2, WPass<LOG2L, 2>{});
+    float2 w[16];
+    ptl.expand(w);
+    FL::load(v, buf, lt);
+    __syncthreads();
+    FL::template compute<false>(v, w);
+    FL::store(v, buf, lt);
+    __syncthreads();
+  };
+  auto corr = [](float2 xk, float2 xp) {
+    const float2 cx = cconj(xp);
+    const float2 U = make_float2(0.5f * (xk.x + cx.x), 0.5f * (xk.y + cx.y));
+    const float2 Gi = make_float2(0.5f * (xk.x - cx.x), 0.5f * (xk.y - cx.y));   // i G
+    return cmul(cconj(U), make_float2(Gi.y, -Gi.x));                               // G = -i (i G)
+  };
+  float2 acce[9], acco[8];
+#pragma unroll
+  for (int i = 0; i < 9; ++i) acce[i] = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acco[i] = make_float2(0.f, 0.f);
+  float2 a[16], an[16];
+  auto load_row = [&](float2* dst, int b) {
+    const size_t row = ((size_t)b * H + h) * L;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dst[r] = make_float2(u[row + lt + T * r], dy[row + lt + T * r]);
+  };
+  if (b_first < b_end) load_row(a, b_first);
+  for (int b = b_first; b < b_end; ++b) {
+    if (b + 1 < b_end) load_row(an, b + 1);
+    float2 v[16];
+    // even bins 2k from A = DFT_L(a)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = a[r];
+    transform(v);
+#pragma unroll
+    for (int q = 0; q < FL::NB; ++q)
+#pragma unroll
+      for (int s2 = 0; s2 < FL::R; ++s2) {
+        const int m = q + s2 * FL::NB;
+        if (m < 8 || (m == 8 && lt == 0)) {
+          const int k = lt + T * m;
+          const float2 xk = v[q * FL::R + bitrev<FL::RL>(s2)];
+          const float2 c2 = corr(xk, buf[lds_pad((L - k) & (L - 1))]);
+          acce[m < 8 ? m : 8] = cadd(acce[m < 8 ? m : 8], c2);
+        }
+      }
+    __syncthreads();
+    // odd bins 2k+1 from B = DFT_L(a_n e^{-i pi n/L}), n = lt + T r:
+    // e^{-i pi n/L} = conj(w0 (cos, sin)(pi r/16))
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float2 w = cmul(w0, make_float2(kCos32[r], kSin32[r]));
+      v[r] = cmul(a[r], make_float2(w.x, -w.y));
+    }
+    transform(v);
+#pragma unroll
+    for (int q = 0; q < FL::NB; ++q)
+#pragma unroll
+      for (int s2 = 0; s2 < FL::R; ++s2) {
+        const int m = q + s2 * FL::NB;
+        if (m < 8) {
+          const int k = lt + T * m;
+          const float2 xk = v[q * FL::R + bitrev<FL::RL>(s2)];
+          acco[m] = cadd(acco[m], corr(xk, buf[lds_pad(L - 1 - k)]));
+        }
+      }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) a[r] = an[r];
+  }
+  float2* out = part + ((size_t)c * H + h) * (L + 1);
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    out[2 * (lt + T * m)] = acce[m];
+    out[2 * (lt + T * m) + 1] = acco[m];
+  }
+  if (lt == 0) out[L] = acce[8];
+}
+
 // Wave-resident form of corr_spec_kernel for 256 <= L <= 1024: a wave takes
 // one (channel, group of kCorrRows batch rows) task, RPW = 64 / (L/16) rows
 // at a time, L/16 lanes per row with 16 points each.  Each row's a_n is loaded
@@ -630,6 +752,9 @@ void corr_launch(const s4dplr_plan* p, const float* u, const float* dy, float* d
     const int tasks = p->H * nparts;
     corr_wave_kernel<LOG2L><<<(tasks + 3) / 4, 256, 0, s>>>(u, dy, part, twL, cs, p->H, p->batch,
                                                             nparts);
+  } else if constexpr (LOG2L >= 11 && LOG2L <= 13) {
+    corr_rows_kernel<LOG2L><<<dim3(p->H, nparts), 1 << (LOG2L - 4), 0, s>>>(u, dy, part, twL, cs,
+                                                                          p->H, p->batch);
   } else {
     corr_spec_kernel<LOG2L><<<dim3(p->H, nparts), S::NT, 0, s>>>(u, dy, part, twL, cs, p->H,
                                                                   p->batch);

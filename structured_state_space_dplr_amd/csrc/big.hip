@@ -44,10 +44,6 @@ __device__ __forceinline__ float2 w_M(const TwM& t, int m) {
   return cmul(t.hi[m >> 8], t.lo[m & 255]);
 }
 
-// (cos, sin)(pi s / 16), s < 16
-__device__ constexpr float kCos32[16] = {1.000000000e+00f, 9.807852804e-01f, 9.238795325e-01f, 8.314696123e-01f, 7.071067812e-01f, 5.555702330e-01f, 3.826834324e-01f, 1.950903220e-01f, 0.0f, -1.950903220e-01f, -3.826834324e-01f, -5.555702330e-01f, -7.071067812e-01f, -8.314696123e-01f, -9.238795325e-01f, -9.807852804e-01f};
-__device__ constexpr float kSin32[16] = {0.000000000e+00f, 1.950903220e-01f, 3.826834324e-01f, 5.555702330e-01f, 7.071067812e-01f, 8.314696123e-01f, 9.238795325e-01f, 9.807852804e-01f, 1.000000000e+00f, 9.807852804e-01f, 9.238795325e-01f, 8.314696123e-01f, 7.071067812e-01f, 5.555702330e-01f, 3.826834324e-01f, 1.950903220e-01f};
-
 // (1 -+ i W_{2M}^j)/2 applied to the pair (Z_j, Z_{M-j}): the bin X_j of the
 // real transform of length 2M; csj = (cos, sin)(pi j / M).
 __device__ __forceinline__ float2 big_rfft_x(float2 zj, float2 zmj, float2 csj) {

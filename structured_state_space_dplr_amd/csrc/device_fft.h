@@ -36,6 +36,10 @@ __device__ __forceinline__ float2 cmulw(float2 a, float2 w) {
 }
 
 // cos and sin of 2*pi*k/16, k = 0..7 (exact values of the 16th roots of unity).
+// (cos, sin)(pi s / 16), s < 16
+__device__ constexpr float kCos32[16] = {1.000000000e+00f, 9.807852804e-01f, 9.238795325e-01f, 8.314696123e-01f, 7.071067812e-01f, 5.555702330e-01f, 3.826834324e-01f, 1.950903220e-01f, 0.0f, -1.950903220e-01f, -3.826834324e-01f, -5.555702330e-01f, -7.071067812e-01f, -8.314696123e-01f, -9.238795325e-01f, -9.807852804e-01f};
+__device__ constexpr float kSin32[16] = {0.000000000e+00f, 1.950903220e-01f, 3.826834324e-01f, 5.555702330e-01f, 7.071067812e-01f, 8.314696123e-01f, 9.238795325e-01f, 9.807852804e-01f, 1.000000000e+00f, 9.807852804e-01f, 9.238795325e-01f, 8.314696123e-01f, 7.071067812e-01f, 5.555702330e-01f, 3.826834324e-01f, 1.950903220e-01f};
+
 __device__ constexpr float kCos16[8] = {1.0f, 0.923879532511286756f, 0.707106781186547524f,
                                         0.382683432365089772f, 0.0f, -0.382683432365089772f,
                                         -0.707106781186547524f, -0.923879532511286756f};
