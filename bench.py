@@ -17,7 +17,8 @@ After the K timed steps the two stages are timed separately with HIP events
 on the launch stream: kernel generation alone, and the convolution kernel
 alone (``conv_apply``: one launch of the convolution kernel per step) -- the
 latter gives the roofline figure.  The CPU baseline runs the fp64 oracle on
-the host (one thread) on the same workload.
+the host on the same workload, on one thread and split over channels across
+a pool of worker processes.
 """
 from __future__ import annotations
 
@@ -64,6 +65,16 @@ def algorithmic_counts(w):
     F1 = w.H * w.L * w.N * (8 + 8 * S)
     Q2 = 8 * w.batch * w.H * w.L + 4 * w.H * w.L + 4 * w.H
     return F1, Q2
+
+
+def stage2_flops(w):
+    """Convolution flops, for the VALU cross-check only: B*H*(5*2L*log2(2L) +
+    6(L+1)) for the transforms of u and y and the bin products, plus
+    H*2.5*2L*log2(2L) for the kernel spectrum."""
+    import math
+    n2 = 2 * w.L
+    lg = math.log2(n2)
+    return w.batch * w.H * (5 * n2 * lg + 6 * (w.L + 1)) + w.H * 2.5 * n2 * lg
 
 
 def recurrent_counts(w):
@@ -160,6 +171,61 @@ def cpu_baseline(x, K_gpu, y_gpu, min_seconds: float):
         "reference": "fp64 oracle, same seeded inputs"}
 
 
+_POOL_X = None
+
+
+def _pool_part(hs):
+    """One worker's share of the pool baseline: the oracle forward on channels
+    hs[0]:hs[1] of the inputs inherited from the parent, one BLAS thread."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    x = _POOL_X
+    sl = slice(hs[0], hs[1])
+    cut = lambda a: None if a is None else a[sl]
+    with threadpool_limits(1):
+        oracle.forward(x["lam"][sl], cut(x["P"]), cut(x["Q"]), x["B"][sl], x["C"][sl],
+                       x["dt"][sl], x["D"][sl], x["u"][:, sl], method="cauchy",
+                       diagonal=x["workload"].diagonal)
+    return hs
+
+
+def cpu_baseline_pool(x, max_workers: int = 16):
+    """The same oracle forward split over channels across a pool of worker
+    processes (fork, one BLAS thread each): the median of 3 timed runs after
+    one warm-up.  Workers never touch the GPU."""
+    import multiprocessing as mp
+
+    global _POOL_X
+    w = x["workload"]
+    P = max(1, min(max_workers, len(os.sched_getaffinity(0)), w.H))
+    bounds = [(w.H * i // P, w.H * (i + 1) // P) for i in range(P)]
+    _POOL_X = x
+    times = []
+    with mp.get_context("fork").Pool(P) as pool:
+        pool.map(_pool_part, bounds)
+        for _ in range(3):
+            t0 = time.perf_counter()
+            pool.map(_pool_part, bounds)
+            times.append(time.perf_counter() - t0)
+    _POOL_X = None
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    t = statistics.median(times)
+    return {"value": w.batch * w.H * w.L / t, "unit": "samples/s", "cores": P, "kind": "oracle",
+            "sample": (f"whole {w.name} workload split over channels across {P} worker "
+                       f"processes (fp64 NumPy oracle, one thread each); median of 3 runs"),
+            "cpu_model": model, "seconds_per_forward": t}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,6 +299,17 @@ def main() -> int:
     samples = w.batch * w.H * w.L
     value = samples / (wall / args.steps)
     log(f"[bench] forward: {ms_per_step * 1e3:.1f} us/step (events {fwd_ms_events * 1e3:.1f} us)")
+    # the same steps once more, each between its own events: median and minimum
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i, (a, b) in enumerate(evs):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_step_us = [a.elapsed_time(b) * 1e3 for a, b in evs]
+    fwd_med_us, fwd_min_us = statistics.median(per_step_us), min(per_step_us)
+    log(f"[bench] forward per step: median {fwd_med_us:.1f} us, minimum {fwd_min_us:.1f} us")
 
     # keep the first set's outputs for the parity check against the oracle
     step(0)
@@ -374,6 +451,7 @@ def main() -> int:
             "traffic": traffic,
             "algorithmic_bytes_per_launch": Q2,
             "launch_us": t_conv * 1e6,
+            "valu_frac_fp32_peak": stage2_flops(w) / t_conv / 1e12 / FP32_PEAK_TFLOPS,
         },
         "kernel_gen": {
             "us": t_gen * 1e6,
@@ -400,6 +478,8 @@ def main() -> int:
         "zoh": zoh,
         "block": block,
         "forward_us_events": fwd_ms_events * 1e3,
+        "forward_us_median": fwd_med_us,
+        "forward_us_min": fwd_min_us,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -409,6 +489,10 @@ def main() -> int:
         result["parity"] = parity
         log(f"[bench] oracle {cb['value']:.3g} samples/s; parity K {parity['K_max_rel_err']:.2e} "
             f"y {parity['y_max_rel_err']:.2e}")
+        cp = cpu_baseline_pool(x)
+        result["cpu_baseline_pool"] = cp
+        log(f"[bench] oracle on {cp['cores']} worker processes: {cp['value']:.3g} samples/s "
+            f"({cp['cpu_model']})")
     plan.close()
     print(json.dumps(result), flush=True)
     return 0
