@@ -119,7 +119,7 @@ def conv_kernel_name(L: int) -> str:
     if 2048 <= L <= 16384:
         return "conv_rows_kernel (one row per workgroup, one launch per step)"
     if L >= 32768:
-        return ("big_conv_cols_fwd_kernel + big_rows_pair_kernel + big_conv_cols_inv_kernel "
+        return ("big_cols_fwd_kernel + big_rows_pair_kernel + big_cols_inv_kernel "
                 "(four-step transform, three launches per step)")
     return "conv_kernel (halves formulation, one launch per step)"
 
