@@ -148,6 +148,29 @@ def test_conv_fwd_random_kernel(s4, L):
     plan.close()
 
 
+@pytest.mark.parametrize("L,H,batch", [(65536, 2, 1), (65536, 3, 3), (32768, 5, 3)])
+def test_conv_fwd_four_step_batches(s4, L, H, batch):
+    # the four-step path numbers its row-pair tasks batch-fastest within a
+    # channel and runs persistent column blocks over rows*tasks: batch sizes
+    # that are not multiples of a wave's four groups, and a single row
+    import torch
+    print(f"case: conv_fwd four-step L={L} H={H} batch={batch}", flush=True)
+    rng = np.random.default_rng(L + 10 * H + batch)
+    u = rng.standard_normal((batch, H, L)).astype(np.float32)
+    K = (rng.standard_normal((H, L)) * np.exp(-np.arange(L) / (L / 8))).astype(np.float32)
+    D = rng.standard_normal(H).astype(np.float32)
+    plan = s4.Plan(H, 4, L, batch)
+    ws = plan.workspace()
+    y = torch.empty((batch, H, L), dtype=torch.float32, device="cuda")
+    s4.conv_fwd(plan, _dev(u), _dev(K), _dev(D), y, ws)
+    torch.cuda.synchronize()
+    yr = o.conv_fft(u, K[None], D[None, :, None])
+    e = _rel(y.cpu().numpy(), yr)
+    print(f"  rel err y {e:.2e}", flush=True)
+    assert e <= TOL
+    plan.close()
+
+
 def test_kernel_gen_matches_forward_kernel(s4):
     import torch
     x = make_inputs("tiny")
