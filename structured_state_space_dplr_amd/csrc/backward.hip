@@ -683,56 +683,79 @@ __global__ __launch_bounds__(256) void kgen_bwd_pole_kernel(
   }
 }
 
+constexpr int kFinalWaves = 16;   // waves per block of the final combine
+
 // Per channel: sums the chunk partials, adds the z = -1 terms, writes the
 // parameter gradients.  With Q tied to P, grad(P) includes the Q path.
+// Each of the block's nw <= 16 waves (one per chunk up to 16) sums every nw-th
+// frequency chunk for 64 poles at a time (lane = pole); the partial sums meet
+// in LDS in a fixed order, so the result does not depend on timing.
 template <bool DIAG>
-__global__ __launch_bounds__(256) void kgen_bwd_final_kernel(
+__global__ __launch_bounds__(64 * kFinalWaves) void kgen_bwd_final_kernel(
     ParamPtrs pp, const float2* __restrict__ part, const float2* __restrict__ ghat,
     float2* __restrict__ dlam, float2* __restrict__ dP, float2* __restrict__ dQ,
     float2* __restrict__ dB, float2* __restrict__ dC, float* __restrict__ ddt, int N, int L,
     int nchunks) {
-  __shared__ float red[4];
-  const int h = blockIdx.x, tid = threadIdx.x;
+  __shared__ float2 acc[kFinalWaves][6][64];
+  const int h = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nw = blockDim.x >> 6;
   const float dt = pp.dt[h], half = 0.5f * dt;
   const float2 gn = ghat[(size_t)h * L + L / 2];
   float dsum = 0.f;
-  for (int n = tid; n < N; n += 256) {
-    const size_t idx = (size_t)h * N + n;
+  for (int n0 = 0; n0 < N; n0 += 64) {              // uniform over the block
+    const int n = n0 + lane;
     float2 s[6];
 #pragma unroll
     for (int c = 0; c < 6; ++c) s[c] = make_float2(0.f, 0.f);
-    for (int lc = 0; lc < nchunks; ++lc) {
-      const float2* o = part + 6 * (((size_t)h * nchunks + lc) * N + n);
+    if (n < N) {
+#pragma unroll 4
+      for (int lc = wave; lc < nchunks; lc += nw) {
+        const float2* o = part + 6 * (((size_t)h * nchunks + lc) * N + n);
 #pragma unroll
-      for (int c = 0; c < 6; ++c) s[c] = cadd(s[c], o[c]);
-    }
-    const float2 b = pp.B[idx], c = pp.C[idx];
-    float2 gC = cadd(cmul(cconj(b), s[0]), cmul(cconj(make_float2(half * b.x, half * b.y)), gn));
-    float2 gB = cadd(cmul(cconj(c), s[0]), cmul(cconj(make_float2(half * c.x, half * c.y)), gn));
-    if constexpr (!DIAG) {
-      const float2 pv = pp.P[idx], qv = pp.Q ? pp.Q[idx] : pv;
-      gC = cadd(gC, cmul(cconj(pv), s[1]));
-      gB = cadd(gB, cmul(qv, s[2]));
-      float2 gP = cadd(cmul(cconj(c), s[1]), cmul(qv, s[3]));
-      const float2 gQ = cadd(cmul(b, cconj(s[2])), cmul(pv, cconj(s[3])));
-      if (pp.Q) {
-        if (dQ) dQ[idx] = gQ;
-      } else {
-        gP = cadd(gP, gQ);
+        for (int c = 0; c < 6; ++c) s[c] = cadd(s[c], o[c]);
       }
-      if (dP) dP[idx] = gP;
     }
-    if (dC) dC[idx] = gC;
-    if (dB) dB[idx] = gB;
-    if (dlam) dlam[idx] = s[4];
-    // dt: Re(E)/dt, and the z = -1 limit (dt/2) C B
-    dsum += s[5].x / dt + (0.5f * cmul(c, b).x * gn.x + 0.5f * cmul(c, b).y * gn.y);
-  }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) dsum += __shfl_xor(dsum, off);
-  if ((tid & 63) == 0) red[tid >> 6] = dsum;
-  __syncthreads();
-  if (tid == 0 && ddt) ddt[h] = red[0] + red[1] + red[2] + red[3];
+    for (int c = 0; c < 6; ++c) acc[wave][c][lane] = s[c];
+    __syncthreads();
+    if (wave == 0 && n < N) {
+#pragma unroll
+      for (int c = 0; c < 6; ++c) {
+        s[c] = acc[0][c][lane];
+#pragma unroll
+        for (int w = 1; w < kFinalWaves; ++w)
+          if (w < nw) s[c] = cadd(s[c], acc[w][c][lane]);
+      }
+      const size_t idx = (size_t)h * N + n;
+      const float2 b = pp.B[idx], c = pp.C[idx];
+      float2 gC = cadd(cmul(cconj(b), s[0]), cmul(cconj(make_float2(half * b.x, half * b.y)), gn));
+      float2 gB = cadd(cmul(cconj(c), s[0]), cmul(cconj(make_float2(half * c.x, half * c.y)), gn));
+      if constexpr (!DIAG) {
+        const float2 pv = pp.P[idx], qv = pp.Q ? pp.Q[idx] : pv;
+        gC = cadd(gC, cmul(cconj(pv), s[1]));
+        gB = cadd(gB, cmul(qv, s[2]));
+        float2 gP = cadd(cmul(cconj(c), s[1]), cmul(qv, s[3]));
+        const float2 gQ = cadd(cmul(b, cconj(s[2])), cmul(pv, cconj(s[3])));
+        if (pp.Q) {
+          if (dQ) dQ[idx] = gQ;
+        } else {
+          gP = cadd(gP, gQ);
+        }
+        if (dP) dP[idx] = gP;
+      }
+      if (dC) dC[idx] = gC;
+      if (dB) dB[idx] = gB;
+      if (dlam) dlam[idx] = s[4];
+      // dt: Re(E)/dt, and the z = -1 limit (dt/2) C B
+      dsum += s[5].x / dt + (0.5f * cmul(c, b).x * gn.x + 0.5f * cmul(c, b).y * gn.y);
+    }
+    __syncthreads();
+  }
+  if (wave == 0) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) dsum += __shfl_xor(dsum, off);
+    if (lane == 0 && ddt) ddt[h] = dsum;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -839,12 +862,13 @@ hipError_t launch_kernel_gen_bwd(const s4dplr_plan* p, const float* lam, const f
   else
     kgen_bwd_pole_kernel<false><<<pgrid, 256, 0, s>>>(pp, tanT, beta, part, p->N, p->L, log2npp);
   auto c2 = [](float* q) { return reinterpret_cast<float2*>(q); };
+  const int fthreads = 64 * (nchunks < kFinalWaves ? nchunks : kFinalWaves);
   if (diag)
-    kgen_bwd_final_kernel<true><<<p->H, 256, 0, s>>>(pp, part, ghat, c2(dlam), nullptr, nullptr,
-                                                     c2(dB), c2(dC), ddt, p->N, p->L, nchunks);
+    kgen_bwd_final_kernel<true><<<p->H, fthreads, 0, s>>>(
+        pp, part, ghat, c2(dlam), nullptr, nullptr, c2(dB), c2(dC), ddt, p->N, p->L, nchunks);
   else
-    kgen_bwd_final_kernel<false><<<p->H, 256, 0, s>>>(pp, part, ghat, c2(dlam), c2(dP), c2(dQ),
-                                                      c2(dB), c2(dC), ddt, p->N, p->L, nchunks);
+    kgen_bwd_final_kernel<false><<<p->H, fthreads, 0, s>>>(
+        pp, part, ghat, c2(dlam), c2(dP), c2(dQ), c2(dB), c2(dC), ddt, p->N, p->L, nchunks);
   return hipGetLastError();
 }
 
