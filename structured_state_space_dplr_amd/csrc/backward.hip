@@ -346,21 +346,29 @@ struct CorrWaveShape {
   static_assert(LOG2M >= 8 && LOG2M <= 10, "wave-resident correlation range");
 };
 
+// The pass twiddles are rebuilt from their table bases at each use, which
+// keeps two full sets out of the registers held across the row loop.
 template <int LOG2M>
-__device__ __forceinline__ void wave_fwd_transform(float2 (&v)[16], float2* __restrict__ buf,
-                                                   int lt, const float2 (&w1)[16],
-                                                   const float2 (&w2)[16]) {
+__device__ __forceinline__ void wave_fwd_transform(
+    float2 (&v)[16], float2* __restrict__ buf, int lt, const PassTwiddles<LOG2M, 1>& pt1,
+    const PassTwiddles<LOG2M, (fft_num_passes(LOG2M) > 2 ? 2 : 1)>& pt2) {
   constexpr int P = fft_num_passes(LOG2M);
-  WPass<LOG2M, 0>::template compute<false>(v, w1);     // span 1: no twiddles
+  dft_dif<16, false>(v);                                // pass 0, span 1: no twiddles
   WPass<LOG2M, 0>::store(v, buf, lt);
   wave_sync();
-  WPass<LOG2M, 1>::load(v, buf, lt);
-  WPass<LOG2M, 1>::template compute<false>(v, w1);
+  {
+    float2 w[16];
+    pt1.expand(w);
+    WPass<LOG2M, 1>::load(v, buf, lt);
+    WPass<LOG2M, 1>::template compute<false>(v, w);
+  }
   WPass<LOG2M, 1>::store(v, buf, lt);
   wave_sync();
   if constexpr (P > 2) {
+    float2 w[16];
+    pt2.expand(w);
     WPass<LOG2M, 2>::load(v, buf, lt);
-    WPass<LOG2M, 2>::template compute<false>(v, w2);
+    WPass<LOG2M, 2>::template compute<false>(v, w);
     WPass<LOG2M, 2>::store(v, buf, lt);
     wave_sync();
   }
@@ -380,14 +388,13 @@ __global__ __launch_bounds__(256) void corr_wave_kernel(
   if (task >= H * nparts) return;                  // the whole wave leaves together
   const int h = task / nparts, c = task - h * nparts;
   const int b_first = c * kCorrRows, b_end = min(batch, b_first + kCorrRows);
-  float2 w1[16], w2[16], wo[16];
-  WPass<LOG2M, 1>::load_tw(w1, tw, lt);
-  if constexpr (S::P > 2) WPass<LOG2M, 2>::load_tw(w2, tw, lt);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const float2 cw = cs[lt + T * r];                // e^{-i pi n/M} = conj(cs[n])
-    wo[r] = make_float2(cw.x, -cw.y);
-  }
+  PassTwiddles<LOG2M, 1> pt1;
+  PassTwiddles<LOG2M, (S::P > 2 ? 2 : 1)> pt2;
+  pt1.load(tw, lt);
+  if constexpr (S::P > 2) pt2.load(tw, lt);
+  // e^{-i pi n/M} for n = lt + T r (T = M/16): the lane's first value,
+  // conj(cs[lt]), turned by -pi r/16
+  const float2 cw0 = cs[lt];
   float2 acce[S::EPT], acco[S::OPT];
 #pragma unroll
   for (int i = 0; i < S::EPT; ++i) acce[i] = make_float2(0.f, 0.f);
@@ -418,7 +425,7 @@ __global__ __launch_bounds__(256) void corr_wave_kernel(
     for (int r = 0; r < 16; ++r) a[r] = v[r] = nxt[r];
     if (it + 1 < S::ITER) load_row(it + 1);
     // even bins: A = DFT_M(a)
-    wave_fwd_transform<LOG2M>(v, buf, lt, w1, w2);
+    wave_fwd_transform<LOG2M>(v, buf, lt, pt1, pt2);
 #pragma unroll
     for (int i = 0; i < S::EPT; ++i) {
       const int k = lt + T * i;
@@ -428,8 +435,11 @@ __global__ __launch_bounds__(256) void corr_wave_kernel(
     wave_sync();
     // odd bins: B = DFT_M(a_n e^{-i pi n/M})
 #pragma unroll
-    for (int r = 0; r < 16; ++r) v[r] = cmul(a[r], wo[r]);
-    wave_fwd_transform<LOG2M>(v, buf, lt, w1, w2);
+    for (int r = 0; r < 16; ++r) {
+      const float2 w = cmul(cw0, make_float2(kCos32[r], kSin32[r]));
+      v[r] = cmul(a[r], make_float2(w.x, -w.y));
+    }
+    wave_fwd_transform<LOG2M>(v, buf, lt, pt1, pt2);
 #pragma unroll
     for (int i = 0; i < S::OPT; ++i) {
       const int k = lt + T * i;
