@@ -32,7 +32,6 @@ namespace {
 
 constexpr int kVanderKT = 64;                      // tap threads per block (one wave)
 constexpr int kVanderPG = 4;                       // pole groups per block (waves)
-constexpr int kVanderThreads = kVanderKT * kVanderPG;
 constexpr int kMaxPolesZoh = 256;
 constexpr double kTwoPi = 6.283185307179586476925286766559;
 constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
@@ -88,18 +87,21 @@ __device__ __forceinline__ float2 power_of(double zre, double zim, double k) {
 }  // namespace
 
 // Pole records in LDS: (W re, W im, A-bar re, A-bar im) and (z re, z im) in fp64.
-// Block (tap range, h): wave g sums the poles n = g, g + kVanderPG, ... for
-// TAPS taps per lane; the waves' partial sums meet in LDS.
-template <int TAPS>
-__global__ __launch_bounds__(kVanderThreads) void vander_kernel(
+// Block (tap range, h): wave g of the PG waves sums the poles n = g, g + PG,
+// ... for TAPS taps per lane; the waves' partial sums meet in LDS.  Short
+// kernels (few tap ranges per channel) take PG = 16 so that the grid still
+// gives every SIMD several waves.
+template <int TAPS, int PG>
+__global__ __launch_bounds__(kVanderKT * PG) void vander_kernel(
     const float2* __restrict__ lam, const float2* __restrict__ B, const float2* __restrict__ C,
     const float* __restrict__ dt, float* __restrict__ K, int N, int L) {
+  static_assert(TAPS % PG == 0, "each thread finishes TAPS / PG taps");
   __shared__ float4 wa[kMaxPolesZoh];
   __shared__ double2 zz[kMaxPolesZoh];
-  __shared__ float red[kVanderPG][kVanderKT][TAPS + 1];
+  __shared__ float red[PG][kVanderKT][TAPS + 1];
   const int h = blockIdx.y, tid = threadIdx.x;
   const double d = (double)dt[h];
-  for (int n = tid; n < N; n += kVanderThreads) {
+  for (int n = tid; n < N; n += kVanderKT * PG) {
     const size_t i = (size_t)h * N + n;
     const cd l = cd_load(lam, i);
     const ZohPole zp = zoh_pole(l, d);
@@ -115,7 +117,7 @@ __global__ __launch_bounds__(kVanderThreads) void vander_kernel(
 #pragma unroll
   for (int j = 0; j < TAPS; ++j) acc[j] = 0.f;
   if (k0 < L) {
-    for (int n = pg; n < N; n += kVanderPG) {
+    for (int n = pg; n < N; n += PG) {
       const float4 r = wa[n];
       const double2 z = zz[n];
       const float2 a = make_float2(r.z, r.w);
@@ -131,7 +133,7 @@ __global__ __launch_bounds__(kVanderThreads) void vander_kernel(
   for (int j = 0; j < TAPS; ++j) red[pg][kt][j] = acc[j];
   __syncthreads();
   // thread (kt, pg) finishes taps [pg T/G, (pg + 1) T/G) of its tap range
-  constexpr int TPG = TAPS / kVanderPG;
+  constexpr int TPG = TAPS / PG;
   if (k0 < L) {
     float* out = K + (size_t)h * L + k0;
 #pragma unroll
@@ -139,7 +141,7 @@ __global__ __launch_bounds__(kVanderThreads) void vander_kernel(
       const int j = pg * TPG + m;
       float v = 0.f;
 #pragma unroll
-      for (int g = 0; g < kVanderPG; ++g) v += red[g][kt][j];
+      for (int g = 0; g < PG; ++g) v += red[g][kt][j];
       if (k0 + j < L) out[j] = v;
     }
   }
@@ -254,15 +256,17 @@ __global__ __launch_bounds__(256) void vander_bwd_final_kernel(
 
 hipError_t launch_vandermonde(const s4dplr_plan* p, const float* lam, const float* B,
                               const float* C, const float* dt, float* K, hipStream_t s) {
-  auto run = [&](auto kern, int taps) {
+  auto run = [&](auto kern, int taps, int pg) {
     const int per_block = kVanderKT * taps;
     const dim3 grid((p->L + per_block - 1) / per_block, p->H);
-    kern<<<grid, kVanderThreads, 0, s>>>(
+    kern<<<grid, kVanderKT * pg, 0, s>>>(
         reinterpret_cast<const float2*>(lam), reinterpret_cast<const float2*>(B),
         reinterpret_cast<const float2*>(C), dt, K, p->N, p->L);
   };
-  if (p->L >= 4096) run(vander_kernel<32>, 32);
-  else run(vander_kernel<16>, 16);
+  const int blocks16 = (p->L + kVanderKT * 16 - 1) / (kVanderKT * 16) * p->H;
+  if (p->L >= 4096) run(vander_kernel<32, kVanderPG>, 32, kVanderPG);
+  else if (blocks16 < 1024) run(vander_kernel<16, 16>, 16, 16);
+  else run(vander_kernel<16, kVanderPG>, 16, kVanderPG);
   return hipGetLastError();
 }
 
