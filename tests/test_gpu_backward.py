@@ -100,6 +100,23 @@ def test_conv_bwd_all_lengths(s4, L):
         assert _rel(g["du"], d2[0]) <= TOL and _rel(g["dK"], d2[1]) <= TOL
 
 
+@pytest.mark.parametrize("L", [1024, 4096, 16384, 65536])
+def test_conv_bwd_single_row(s4, L):
+    # one channel, one batch row: a single row group in the correlation
+    # kernels, the smallest grids of the four-step and row forms
+    print(f"case: conv_bwd single row L={L}", flush=True)
+    rng = np.random.default_rng(3 * L + 1)
+    u = rng.standard_normal((1, 1, L)).astype(np.float32)
+    dy = rng.standard_normal((1, 1, L)).astype(np.float32)
+    K = (rng.standard_normal((1, L)) * np.exp(-np.arange(L) / (L / 4))).astype(np.float32)
+    D = rng.standard_normal(1).astype(np.float32)
+    g = gpu_conv_bwd(s4, u, K, D, dy)
+    du, dK, dD = o.conv_backward_fft(u, K, D, dy)
+    e = (_rel(g["du"], du), _rel(g["dK"], dK), _rel(g["dD"], dD))
+    print(f"  rel err du {e[0]:.2e} dK {e[1]:.2e} dD {e[2]:.2e}", flush=True)
+    assert max(e) <= TOL
+
+
 def test_conv_bwd_optional_outputs_and_no_D(s4):
     rng = np.random.default_rng(7)
     u, dy = rng.standard_normal((2, 4, 256)), rng.standard_normal((2, 4, 256))
