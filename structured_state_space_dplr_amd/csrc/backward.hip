@@ -66,8 +66,10 @@ struct CorrShape {
 // sequences:
 //   U_2k = (A_k + conj A_{L-k}) / 2,     G_2k = (A_k - conj A_{L-k}) / 2i,
 //   U_2k+1 = (B_k + conj B_{L-1-k}) / 2, G_2k+1 = (B_k - conj B_{L-1-k}) / 2i.
-// Up to L = 4096 each thread keeps its share of a row in registers for both
-// transforms and loads the next row while the current one is transformed.
+// This generic form serves L <= 128 and L = 16384 (the wave and row forms
+// below take the lengths between).  Up to L = 4096 each thread keeps its
+// share of a row in registers for both transforms and loads the next row
+// while the current one is transformed.
 template <int LOG2L>
 __global__ __launch_bounds__(CorrShape<LOG2L>::NT) void corr_spec_kernel(
     const float* __restrict__ u, const float* __restrict__ dy, float2* part, const float2* twL,
