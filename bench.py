@@ -8,23 +8,39 @@ kernel spectrum (inverse FFT to K, which is written out, and the zero-padded
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mid]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload waveform]
+                  [--configs all|none|name,name,...]
+
+The headline workload is the largest single-GPU one (waveform: H = 64, N = 64,
+L = 65536, batch = 4, the most work per step).  ``value`` is its whole-step
+throughput, B*H*L samples per second.  The same line carries a ``configs``
+map with the forward, stage-1 and convolution figures of every workload.
 
 Inputs are resident in HBM before the timed region.  The timed steps rotate
-over several input/output buffer sets whose total exceeds 512 MB so that the
-256 MB last-level cache does not hold a step's data from the previous step.
-After the K timed steps the two stages are timed separately with HIP events
-on the launch stream: kernel generation alone, and the convolution kernel
-alone (``conv_apply``: one launch of the convolution kernel per step) -- the
-latter gives the roofline figure.  The CPU baseline runs the fp64 oracle on
-the host on the same workload, on one thread and split over channels across
-a pool of worker processes.
+over several input/output buffer sets totalling more than 512 MB, so that the
+256 MB last-level cache does not hold a step's data from the previous step
+(the tiny workload's sets are capped at 1024 and stay cache-resident; that
+workload is launch-bound).  After the K timed steps each stage is timed alone
+with HIP events on the launch stream: kernel generation (stage 1), the
+generating function alone (the Cauchy kernel), and the convolution
+(``conv_apply``).  The CPU baseline runs the fp64 oracle on the host on a
+bounded sample of the headline workload (a subset of its channels, every
+batch row), on one thread and over a pool of worker processes.
+
+Two more modes turn rocprofv3 output into the summaries under ``profiles/``:
+  python bench.py --summarize-trace DIR --label NAME
+  python bench.py --summarize-counters FETCH_DIR WRITE_DIR --workload NAME
+and ``--counters`` runs the short, fixed launch sequence those counter runs
+profile (see the design doc for the commands).
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
+import math
 import os
 import statistics
 import sys
@@ -35,9 +51,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "S4 conv fwd samples/s (B·H·L/s) + Cauchy kernel-gen GFLOP/s vs fp32 peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
-FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector, published
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv_traffic.json")
-KERNEL_SOURCES = ["kernels.hip", "device_fft.h", "fft_sched.h"]
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector, published: 256 CU x 4 SIMD x 2.4 GHz x 64 flop/clk
+HEADLINE = "waveform"
+ALL_CONFIGS = ["tiny", "mid", "long", "s4d_lin", "waveform"]
+PROFILES = os.path.join(ROOT, "profiles")
+# sources whose change makes a recorded counter figure stale
+KERNEL_SOURCES = ["kernels.hip", "big.hip", "cauchy.h", "device_fft.h", "fft_sched.h"]
 
 
 def log(*a):
@@ -71,7 +90,6 @@ def stage2_flops(w):
     """Convolution flops, for the VALU cross-check only: B*H*(5*2L*log2(2L) +
     6(L+1)) for the transforms of u and y and the bin products, plus
     H*2.5*2L*log2(2L) for the kernel spectrum."""
-    import math
     n2 = 2 * w.L
     lg = math.log2(n2)
     return w.batch * w.H * (5 * n2 * lg + 6 * (w.L + 1)) + w.H * 2.5 * n2 * lg
@@ -110,64 +128,100 @@ def backward_counts(w):
     return q_conv, w.H * w.L * w.N * per_term
 
 
-def conv_kernel_name(L: int) -> str:
+def fused_stage1(L: int) -> bool:
+    return 32 <= L <= 1024
+
+
+def stage1_kernel_name(L: int) -> str:
+    if fused_stage1(L):
+        return "kgen_wave_kernel"
+    return "cauchy_kernel"
+
+
+def conv_kernel_names(L: int) -> list[str]:
     """The kernel(s) that apply the convolution at sequence length L."""
     if L == 1024:
-        return "conv_pair1024_kernel (one row per wave, paired lanes, one launch per step)"
+        return ["conv_pair1024_kernel"]
     if 32 <= L <= 512:
-        return "conv_wave_kernel (one row per wave, one launch per step)"
+        return ["conv_wave_kernel"]
     if 2048 <= L <= 16384:
-        return "conv_rows_kernel (one row per workgroup, one launch per step)"
+        return ["conv_rows_kernel"]
     if L >= 32768:
-        return ("big_cols_fwd_kernel + big_rows_pair_kernel + big_cols_inv_kernel "
-                "(four-step transform, three launches per step)")
-    return "conv_kernel (halves formulation, one launch per step)"
+        return ["big_cols_fwd_kernel", "big_rows_pair_kernel", "big_cols_inv_kernel"]
+    return ["conv_kernel"]
 
 
-def read_traffic(workload_name: str):
-    """HBM bytes per convolution launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel sources; else None."""
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"traffic_{workload}.json")
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch by kernel from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources; else {}."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None
-    if t.get("workload") != workload_name or t.get("kernel_source_sha") != kernel_source_hash():
-        return None
-    return t.get("bytes_per_launch")
+        return {}
+    if t.get("kernel_source_sha") != kernel_source_hash():
+        return {}
+    return {k: v["bytes_per_launch"] for k, v in t.get("kernels", {}).items()}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline (the oracle): the only leg that touches oracle/
+# ---------------------------------------------------------------------------
+
+def _oracle_forward(x, hs):
+    import oracle
+    sl = slice(hs[0], hs[1])
+    cut = lambda a: None if a is None else a[sl]
+    return oracle.forward(x["lam"][sl], cut(x["P"]), cut(x["Q"]), x["B"][sl], x["C"][sl],
+                          x["dt"][sl], x["D"][sl], x["u"][:, sl], method="cauchy",
+                          diagonal=x["workload"].diagonal)
 
 
 def cpu_baseline(x, K_gpu, y_gpu, min_seconds: float):
     """The fp64 oracle (the pages' Cauchy/Woodbury method and an fp64 FFT
-    convolution) on the whole workload, one BLAS thread, repeated until
-    `min_seconds` of CPU work; also the GPU result's error against it."""
+    convolution) on a bounded sample of the workload: the first `hs` channels
+    with every batch row, `hs` chosen so that one run takes about 2 s; one
+    BLAS thread, repeated until `min_seconds` of CPU work.  Also the GPU
+    result's error against it on those channels (whole sample and worst
+    channel)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
-    import oracle
-
     w = x["workload"]
-    times = []
     with threadpool_limits(1):
+        t0 = time.perf_counter()
+        _oracle_forward(x, (0, 1))
+        t1 = time.perf_counter() - t0
+        hs = max(1, min(w.H, int(2.0 / max(t1, 1e-3))))
+        times = []
         t_start = time.perf_counter()
         while True:
             t0 = time.perf_counter()
-            K, y = oracle.forward(x["lam"], x["P"], x["Q"], x["B"], x["C"], x["dt"], x["D"],
-                                  x["u"], method="cauchy", diagonal=w.diagonal)
+            K, y = _oracle_forward(x, (0, hs))
             times.append(time.perf_counter() - t0)
             if time.perf_counter() - t_start >= min_seconds and len(times) >= 3:
                 break
     t = statistics.median(times)
-    samples = w.batch * w.H * w.L
-    eK = float(np.abs(K_gpu - K).max() / np.abs(K).max())
-    ey = float(np.abs(y_gpu - y).max() / np.abs(y).max())
+    samples = w.batch * hs * w.L
+    Kg, yg = K_gpu[:hs], y_gpu[:, :hs]
+    eK = float(np.abs(Kg - K).max() / np.abs(K).max())
+    ey = float(np.abs(yg - y).max() / np.abs(y).max())
+    cK = np.abs(Kg - K).max(axis=1) / np.abs(K).max(axis=1)
+    cy = np.abs(yg - y).max(axis=(0, 2)) / np.abs(y).max(axis=(0, 2))
     return {
         "value": samples / t, "unit": "samples/s", "cores": 1, "kind": "oracle",
-        "sample": (f"whole {w.name} workload (H={w.H}, N={w.N}, L={w.L}, batch={w.batch}), "
-                   f"fp64 NumPy oracle: Cauchy/Woodbury kernel + rfft convolution; "
-                   f"median of {len(times)} runs, 1 thread"),
-        "seconds_per_forward": t,
-    }, {"K_max_rel_err": eK, "y_max_rel_err": ey, "tolerance": 1e-4,
+        "sample": (f"{w.name} workload, channels 0..{hs - 1} of {w.H} with all {w.batch} batch "
+                   f"rows (B*{hs}*L = {samples} samples per run), fp64 NumPy oracle: "
+                   f"Cauchy/Woodbury kernel + rfft convolution; median of {len(times)} runs, "
+                   f"1 thread"),
+        "seconds_per_run": t,
+    }, {"K_max_rel_err": eK, "y_max_rel_err": ey,
+        "K_worst_channel_rel_err": float(cK.max()), "y_worst_channel_rel_err": float(cy.max()),
+        "channels_checked": hs, "tolerance": 1e-4,
         "reference": "fp64 oracle, same seeded inputs"}
 
 
@@ -178,28 +232,22 @@ def _pool_part(hs):
     """One worker's share of the pool baseline: the oracle forward on channels
     hs[0]:hs[1] of the inputs inherited from the parent, one BLAS thread."""
     from threadpoolctl import threadpool_limits
-
-    import oracle
-
-    x = _POOL_X
-    sl = slice(hs[0], hs[1])
-    cut = lambda a: None if a is None else a[sl]
     with threadpool_limits(1):
-        oracle.forward(x["lam"][sl], cut(x["P"]), cut(x["Q"]), x["B"][sl], x["C"][sl],
-                       x["dt"][sl], x["D"][sl], x["u"][:, sl], method="cauchy",
-                       diagonal=x["workload"].diagonal)
+        _oracle_forward(_POOL_X, hs)
     return hs
 
 
 def cpu_baseline_pool(x, max_workers: int = 16):
-    """The same oracle forward split over channels across a pool of worker
-    processes (fork, one BLAS thread each): the median of 3 timed runs after
-    one warm-up.  Workers never touch the GPU."""
+    """The same oracle forward on the whole workload, split over channels
+    across a pool of worker processes (fork, one BLAS thread each): the median
+    of 3 timed runs after one warm-up.  The pool has min(16, affinity, H)
+    workers: 16 is the host's CPU share per GPU.  Workers never touch the GPU."""
     import multiprocessing as mp
 
     global _POOL_X
     w = x["workload"]
-    P = max(1, min(max_workers, len(os.sched_getaffinity(0)), w.H))
+    affinity = len(os.sched_getaffinity(0))
+    P = max(1, min(max_workers, affinity, w.H))
     bounds = [(w.H * i // P, w.H * (i + 1) // P) for i in range(P)]
     _POOL_X = x
     times = []
@@ -222,22 +270,420 @@ def cpu_baseline_pool(x, max_workers: int = 16):
     t = statistics.median(times)
     return {"value": w.batch * w.H * w.L / t, "unit": "samples/s", "cores": P, "kind": "oracle",
             "sample": (f"whole {w.name} workload split over channels across {P} worker "
-                       f"processes (fp64 NumPy oracle, one thread each); median of 3 runs"),
+                       f"processes (fp64 NumPy oracle, one thread each; {affinity} cores in "
+                       f"the affinity mask, capped at 16); median of 3 runs"),
             "cpu_model": model, "seconds_per_forward": t}
 
+
+# ---------------------------------------------------------------------------
+# GPU measurement of one workload
+# ---------------------------------------------------------------------------
+
+class Workbench:
+    """Inputs, rotating buffer sets, plan and workspace of one workload."""
+
+    def __init__(self, s4, torch, w, dev):
+        import numpy as np
+
+        from synth import make_inputs
+        self.s4, self.torch, self.w, self.dev = s4, torch, w, dev
+        self.x = make_inputs(w.name)
+        g = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        self.params = {k: g(self.x[k]) for k in ("lam", "P", "Q", "B", "C", "dt", "D")}
+        self.P = None if w.diagonal else self.params["P"]
+        u0 = g(self.x["u"])
+        row_bytes = 4 * w.batch * w.H * w.L
+        self.nsets = min(1024, max(2, -(-(512 << 20) // (2 * row_bytes)) + 1))
+        self.set_mib = 2 * row_bytes / 2 ** 20
+        self.us = [u0] + [u0.clone() for _ in range(self.nsets - 1)]
+        self.ys = [torch.empty_like(u0) for _ in range(self.nsets)]
+        self.K = torch.empty((w.H, w.L), dtype=torch.float32, device=dev)
+        self.khat = torch.empty((w.H, w.L, 2), dtype=torch.float32, device=dev)
+        self.plan = s4.Plan(w.H, w.N, w.L, w.batch, diagonal=w.diagonal, device=dev)
+        self.ws = self.plan.workspace()
+        self.stream = torch.cuda.current_stream()
+
+    def step(self, i):
+        p = self.params
+        self.s4.forward(self.plan, p["lam"], self.P, p["Q"], p["B"], p["C"], p["dt"], p["D"],
+                        self.us[i % self.nsets], self.K, self.ys[i % self.nsets], self.ws,
+                        self.stream)
+
+    def kernel_gen(self, i):
+        p = self.params
+        self.s4.kernel_gen(self.plan, p["lam"], self.P, p["Q"], p["B"], p["C"], p["dt"], self.K,
+                           self.ws, self.stream)
+
+    def cauchy(self, i):
+        p = self.params
+        self.s4.generating_function(self.plan, p["lam"], self.P, p["Q"], p["B"], p["C"], p["dt"],
+                                    self.khat, self.ws, self.stream)
+
+    def conv(self, i):
+        self.s4.conv_apply(self.plan, self.us[i % self.nsets], self.ys[i % self.nsets], self.ws,
+                           self.stream)
+
+    def timed(self, fn, n, warm=3):
+        """Seconds per call: n calls between two HIP events on the launch
+        stream, after `warm` untimed calls."""
+        torch = self.torch
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(warm):
+            fn(i)
+        torch.cuda.synchronize()
+        a.record(self.stream)
+        for i in range(n):
+            fn(i)
+        b.record(self.stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e-3
+
+    def per_call(self, fn, n):
+        """Per-call durations (seconds), each call between its own events."""
+        torch = self.torch
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for i, (a, b) in enumerate(evs):
+            a.record(self.stream)
+            fn(i)
+            b.record(self.stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) * 1e-3 for a, b in evs]
+
+    def stages(self, n):
+        """Stage timings: kernel generation, the generating function (Cauchy
+        kernel alone) and one convolution launch."""
+        t_gen = self.timed(self.kernel_gen, n)
+        t_cauchy = self.timed(self.cauchy, n)
+        self.step(0)    # leaves this layer's spectrum (with D) in the workspace
+        t_conv = self.timed(self.conv, n)
+        return t_gen, t_cauchy, t_conv
+
+    def close(self):
+        self.plan.close()
+
+
+def config_figures(wb, steps, warmup):
+    """The per-workload entry of the ``configs`` map."""
+    w = wb.w
+    F1, Q2 = algorithmic_counts(w)
+    for i in range(warmup):
+        wb.step(i)
+    wb.torch.cuda.synchronize()
+    t_fwd = wb.timed(wb.step, steps, warm=0)
+    per = wb.per_call(wb.step, steps)
+    t_gen, t_cauchy, t_conv = wb.stages(steps)
+    samples = w.batch * w.H * w.L
+    s1_kernel_t = t_gen if fused_stage1(w.L) else t_cauchy
+    return {
+        "H": w.H, "N": w.N, "L": w.L, "batch": w.batch, "init": w.init,
+        "forward_us": t_fwd * 1e6,
+        "forward_us_median": statistics.median(per) * 1e6,
+        "forward_us_min": min(per) * 1e6,
+        "samples_per_s": samples / t_fwd,
+        "stage1_us": t_gen * 1e6,
+        "stage1_frac_fp32_peak": F1 / t_gen / 1e12 / FP32_PEAK_TFLOPS,
+        "stage1_kernel": stage1_kernel_name(w.L),
+        "stage1_kernel_us": s1_kernel_t * 1e6,
+        "stage1_kernel_frac_fp32_peak": F1 / s1_kernel_t / 1e12 / FP32_PEAK_TFLOPS,
+        "cauchy_algorithmic_flops": F1,
+        "conv_kernels": conv_kernel_names(w.L),
+        "conv_us": t_conv * 1e6,
+        "conv_gbs": Q2 / t_conv / 1e9,
+        "conv_frac_hbm": Q2 / t_conv / 1e9 / HBM_PEAK_GBS,
+        "conv_algorithmic_bytes": Q2,
+        "stage2_samples_per_s": samples / t_conv,
+    }, (t_fwd, per, t_gen, t_cauchy, t_conv)
+
+
+def secondary_legs(wb, steps, dev):
+    """The (f) rows on the headline workload: recurrent view, zero-order hold,
+    block and backward pass, each timed with HIP events on the launch stream."""
+    s4, torch, w = wb.s4, wb.torch, wb.w
+    p, P = wb.params, wb.P
+    samples = w.batch * w.H * w.L
+    out = {}
+    flops_step, decode_bytes = recurrent_counts(w)
+    s4.recurrent_prepare(wb.plan, p["lam"], P, p["Q"], p["B"], p["C"], p["dt"], wb.ws, wb.stream)
+    state = torch.zeros((w.batch, w.H, w.N, 2), dtype=torch.float32, device=dev)
+    scan = lambda i: s4.recurrent_scan(wb.plan, p["D"], wb.us[i % wb.nsets], state,
+                                       wb.ys[i % wb.nsets], wb.ws, wb.stream)
+    t_one = wb.timed(scan, 1)
+    n_scan = max(3, min(steps, int(0.5 / max(t_one, 1e-6))))
+    t_scan = wb.timed(scan, n_scan)
+    u1 = wb.us[0][..., :1].contiguous()
+    y1 = torch.empty_like(u1)
+    t_dec = wb.timed(lambda i: s4.recurrent_scan(wb.plan, p["D"], u1, state, y1, wb.ws,
+                                                 wb.stream), 200)
+    rec_tflops = flops_step * w.L / t_scan / 1e12
+    log(f"[bench] recurrent scan {t_scan * 1e6:.1f} us ({samples / t_scan:.3g} samples/s, "
+        f"{rec_tflops:.1f} TFLOP/s); decode step {t_dec * 1e6:.2f} us")
+    out["recurrent"] = {
+        "kernel": "recurrent_scan_kernel (O(N) bilinear DPLR step, carried state)",
+        "scan_us": t_scan * 1e6, "scan_samples_per_s": samples / t_scan, "bound": "alu",
+        "achieved": rec_tflops, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "frac": rec_tflops / FP32_PEAK_TFLOPS, "algorithmic_flops_per_step": flops_step,
+        "decode_step_us": t_dec * 1e6, "decode_bytes_per_step": decode_bytes,
+        "decode_tokens_per_s": w.batch / t_dec,
+    }
+    # zero-order hold (diagonal): the Vandermonde kernel on the same poles
+    zplan = s4.Plan(w.H, w.N, w.L, w.batch, diagonal=True, zoh=True, device=dev)
+    zws = zplan.workspace()
+    t_vd = wb.timed(lambda i: s4.kernel_gen(zplan, p["lam"], None, None, p["B"], p["C"], p["dt"],
+                                            wb.K, zws, wb.stream), steps)
+    f_vd = 7 * w.H * w.L * w.N      # per (h, k, n): one complex product and one add
+    log(f"[bench] zoh kernel_gen {t_vd * 1e6:.1f} us ({f_vd / t_vd / 1e9:.0f} GFLOP/s)")
+    out["zoh"] = {"kernel_gen_us": t_vd * 1e6, "gflops": f_vd / t_vd / 1e9,
+                  "frac_fp32_peak": f_vd / t_vd / 1e12 / FP32_PEAK_TFLOPS,
+                  "algorithmic_flops": f_vd,
+                  "note": "Vandermonde kernel plus the spectrum of K padded to 2L"}
+    zplan.close()
+    del zws
+    # the block around the layer: layer norm, the layer, GLU projection
+    from synth import make_block_params
+    import numpy as np
+    bp = {k: torch.from_numpy(np.ascontiguousarray(v)).to(dev)
+          for k, v in make_block_params(w.H, seed=1).items()}
+    bplan = s4.Plan(w.H, w.N, w.L, w.batch, diagonal=w.diagonal, device=dev, block=True)
+    bws = bplan.workspace()
+    t_blk = wb.timed(lambda i: s4.block_forward(
+        bplan, wb.us[i % wb.nsets], bp["gamma"], bp["beta"], p["lam"], P, p["Q"], p["B"], p["C"],
+        p["dt"], p["D"], bp["W"], bp["bias"], wb.ys[i % wb.nsets], bws, wb.stream), steps)
+    f_proj = 2 * (2 * w.H) * w.H * w.batch * w.L        # the projection GEMM
+    log(f"[bench] block forward {t_blk * 1e6:.1f} us ({samples / t_blk:.3g} samples/s)")
+    out["block"] = {"us": t_blk * 1e6, "samples_per_s": samples / t_blk,
+                    "projection_flops": f_proj,
+                    "note": "layer norm + layer + GLU projection with residual (bf16 MFMA on "
+                            "hi/lo split operands, fp32 accumulation)"}
+    bplan.close()
+    del bws
+    # the backward pass: conv_bwd and kernel_gen_bwd
+    q_bwd, f_bwd = backward_counts(w)
+    dy, du = wb.ys[1 % wb.nsets], wb.ys[2 % wb.nsets]
+    dK = torch.empty((w.H, w.L), dtype=torch.float32, device=dev)
+    dD = torch.empty((w.H,), dtype=torch.float32, device=dev)
+    grads = {k: torch.empty((w.H, w.N, 2), dtype=torch.float32, device=dev)
+             for k in ("lam", "P", "B", "C")}
+    ddt = torch.empty((w.H,), dtype=torch.float32, device=dev)
+    t_cb = wb.timed(lambda i: s4.conv_bwd(wb.plan, wb.us[i % wb.nsets], wb.K, p["D"], dy, du, dK,
+                                          dD, wb.ws, wb.stream), steps)
+    t_kb = wb.timed(lambda i: s4.kernel_gen_bwd(
+        wb.plan, p["lam"], P, p["Q"], p["B"], p["C"], p["dt"], dK, grads["lam"],
+        None if w.diagonal else grads["P"], None, grads["B"], grads["C"], ddt, wb.ws,
+        wb.stream), steps)
+    log(f"[bench] conv_bwd {t_cb * 1e6:.1f} us ({q_bwd / t_cb / 1e9:.0f} GB/s), "
+        f"kernel_gen_bwd {t_kb * 1e6:.1f} us ({f_bwd / t_kb / 1e9:.0f} GFLOP/s)")
+    out["backward"] = {
+        "conv_bwd_us": t_cb * 1e6, "conv_bwd_gbs": q_bwd / t_cb / 1e9,
+        "conv_bwd_frac_hbm": q_bwd / t_cb / 1e9 / HBM_PEAK_GBS,
+        "conv_bwd_algorithmic_bytes": q_bwd,
+        "kernel_gen_bwd_us": t_kb * 1e6, "kernel_gen_bwd_gflops": f_bwd / t_kb / 1e9,
+        "kernel_gen_bwd_frac_fp32_peak": f_bwd / t_kb / 1e12 / FP32_PEAK_TFLOPS,
+        "kernel_gen_bwd_algorithmic_flops": f_bwd,
+        "samples_per_s": samples / (t_cb + t_kb),
+    }
+    return out
+
+
+def roofline(w, t_gen, t_cauchy, t_conv):
+    """Roofline of the dominant kernel of the forward step, with the other
+    stage beside it.  Stage 1 (the Cauchy sums) is bound by fp32 VALU
+    arithmetic; the convolution nominally by HBM bandwidth.  The dominant
+    kernel is the single kernel with the largest share of the step: the
+    Cauchy kernel where the convolution is split over three four-step
+    kernels (L >= 32768), else the slower of the two stages."""
+    F1, Q2 = algorithmic_counts(w)
+    traffic = read_traffic(w.name)
+    s1_name = stage1_kernel_name(w.L)
+    s1_t = t_gen if fused_stage1(w.L) else t_cauchy
+    conv_names = conv_kernel_names(w.L)
+    conv_traffic = None
+    if all(k in traffic for k in conv_names):
+        conv_traffic = sum(traffic[k] for k in conv_names)
+    s1 = {"kernel": s1_name, "bound": "alu", "achieved": F1 / s1_t / 1e12,
+          "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": F1 / s1_t / 1e12 / FP32_PEAK_TFLOPS,
+          "traffic": traffic.get(s1_name), "algorithmic_flops_per_launch": F1,
+          "launch_us": s1_t * 1e6,
+          "stage1_us": t_gen * 1e6, "stage1_frac": F1 / t_gen / 1e12 / FP32_PEAK_TFLOPS}
+    cv = {"kernel": " + ".join(conv_names), "bound": "hbm", "achieved": Q2 / t_conv / 1e9,
+          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": Q2 / t_conv / 1e9 / HBM_PEAK_GBS,
+          "traffic": conv_traffic, "algorithmic_bytes_per_launch": Q2,
+          "launch_us": t_conv * 1e6,
+          "valu_frac_fp32_peak": stage2_flops(w) / t_conv / 1e12 / FP32_PEAK_TFLOPS}
+    if w.L >= 32768 or s1_t >= t_conv:
+        main, other, other_key = s1, cv, "conv"
+    else:
+        main, other, other_key = cv, s1, "stage1_kernel"
+    out = dict(main)
+    out[other_key] = other
+    return out
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries
+# ---------------------------------------------------------------------------
+
+def _find_csv(d, suffix):
+    hits = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return hits[-1]
+
+
+def _short_name(name: str) -> str:
+    """Kernel name without template arguments, parameters or launch suffix."""
+    n = name.split("(")[0]
+    n = n.split("<")[0]
+    n = n.replace("void ", "").strip()
+    return n.split("::")[-1]
+
+
+def summarize_trace(d, label, command):
+    """Markdown table of per-kernel launch durations from a rocprofv3
+    --kernel-trace run (kernel_trace.csv: end minus start per dispatch)."""
+    path = _find_csv(d, "kernel_trace.csv")
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            per.setdefault(_short_name(r["Kernel_Name"]), []).append(dur)
+    total = sum(sum(v) for v in per.values())
+    rows = sorted(per.items(), key=lambda kv: -sum(kv[1]))
+    out = [f"# Kernel time per launch: {label}", "", "Command (run from the repository root):",
+           "", "```", command, "```", "",
+           "Source: `kernel_trace.csv` of rocprofv3 `--kernel-trace --stats`, durations are end "
+           "minus start per dispatch, summarized by `python bench.py --summarize-trace`.", "",
+           "| kernel | calls | average (us) | median (us) | min (us) | max (us) | share of GPU time |",
+           "|---|---|---|---|---|---|---|"]
+    for k, v in rows:
+        out.append(f"| {k} | {len(v)} | {statistics.mean(v):.2f} | {statistics.median(v):.2f} | "
+                   f"{min(v):.2f} | {max(v):.2f} | {100 * sum(v) / total:.1f}% |")
+    return "\n".join(out) + "\n"
+
+
+def _counter_rows(d):
+    path = _find_csv(d, "counter_collection.csv")
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_counters(fetch_dir, write_dir, workload, commands):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the --counters launch
+    sequence, scaled by what the same counters read for a plain 1 GiB copy:
+    bytes per launch of each kernel, the median over its last five dispatches
+    (the profiled calls; earlier dispatches of the same kernel belong to the
+    set-up forward pass)."""
+    out = {"workload": workload, "kernel_source_sha": kernel_source_hash(), "kernels": {},
+           "commands": commands}
+    vals = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        for r in _counter_rows(d):
+            if r.get("Counter_Name") != counter:
+                continue
+            name = _short_name(r["Kernel_Name"])
+            key = (name, int(r.get("Dispatch_Id", r.get("Correlation_Id", 0))))
+            vals.setdefault(counter, {}).setdefault(key, 0.0)
+            vals[counter][key] += float(r["Counter_Value"])
+    def per_kernel(counter):
+        by = {}
+        for (name, disp), v in sorted(vals[counter].items(), key=lambda kv: kv[0][1]):
+            by.setdefault(name, []).append(v)
+        return by
+    fetch, write = per_kernel("FETCH_SIZE"), per_kernel("WRITE_SIZE")
+    copy_bytes = 1 << 30
+    copy_names = [k for k in fetch if "copy" in k.lower() or "elementwise" in k.lower()]
+    # the calibration copy is the largest dispatch among the copy kernels
+    cf = max((v for k in copy_names for v in fetch[k]), default=None)
+    cw = max((v for k in copy_names for v in write.get(k, [])), default=None)
+    if not cf or not cw:
+        raise SystemExit("no calibration copy found in the counter runs")
+    fscale, wscale = copy_bytes / (1024 * cf), copy_bytes / (1024 * cw)
+    out["calibration"] = {"copy_bytes": copy_bytes, "copy_fetch_size_kib": cf,
+                          "copy_write_size_kib": cw, "fetch_scale": fscale, "write_scale": wscale}
+    names = ["cauchy_kernel", "kgen_wave_kernel", "conv_pair1024_kernel", "conv_wave_kernel",
+             "conv_rows_kernel", "conv_kernel", "big_cols_fwd_kernel", "big_rows_pair_kernel",
+             "big_cols_inv_kernel"]
+    for k in names:
+        if k in fetch and k in write:
+            fk = statistics.median(fetch[k][-5:])
+            wk = statistics.median(write[k][-5:])
+            out["kernels"][k] = {"fetch_size_kib": fk, "write_size_kib": wk,
+                                 "bytes_per_launch": fscale * 1024 * fk + wscale * 1024 * wk}
+    out["formula"] = ("bytes = fetch_scale * 1024 * FETCH_SIZE + write_scale * 1024 * WRITE_SIZE "
+                      "(KiB per dispatch, median over the kernel's profiled dispatches); scales "
+                      "from a plain 1 GiB device copy in the same run")
+    return out
+
+
+def counters_sequence(args):
+    """The fixed launch sequence of a counter run: one forward pass (set-up),
+    five generating-function calls, five convolution launches, then a plain
+    1 GiB device copy for the counters' calibration."""
+    import torch
+
+    import structured_state_space_dplr_amd as s4
+    from synth import WORKLOADS
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wb = Workbench(s4, torch, WORKLOADS[args.workload], dev)
+    wb.step(0)
+    for i in range(5):
+        wb.cauchy(i)
+    for i in range(5):
+        wb.conv(i)
+    torch.cuda.synchronize()
+    wb.close()
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] counter sequence done: {args.workload}")
+    return 0
+
+
+# ---------------------------------------------------------------------------
 
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mid",
-                    help="tiny | mid | long | s4d_lin | waveform (default: mid)")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE,
+                    help="headline workload: tiny | mid | long | s4d_lin | waveform "
+                         f"(default: {HEADLINE}, the largest)")
+    ap.add_argument("--configs", default="all",
+                    help="workloads of the configs map: all | none | comma-separated names")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 1 GiB device copy (counter calibration runs)")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the recurrent, ZOH, block and backward legs")
+    ap.add_argument("--counters", action="store_true",
+                    help="run only the counter-collection launch sequence")
+    ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--label", default="")
+    ap.add_argument("--command", default="")
+    ap.add_argument("--out", default="")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        text = summarize_trace(args.summarize_trace, args.label or args.workload, args.command)
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(text)
+        else:
+            sys.stdout.write(text)
+        return 0
+    if args.summarize_counters:
+        cmds = [c for c in args.command.split(" ;; ") if c]
+        res = summarize_counters(*args.summarize_counters, args.workload, cmds)
+        text = json.dumps(res, indent=1)
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(text + "\n")
+        else:
+            print(text)
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -250,48 +696,30 @@ def main() -> int:
     import torch
 
     import structured_state_space_dplr_amd as s4
-    from synth import WORKLOADS, make_inputs
+    from synth import WORKLOADS
 
     if not torch.cuda.is_available():
         log("no GPU visible")
         return 1
-    w = WORKLOADS[args.workload]
-    log(f"[bench] workload {w.describe()}; generating inputs")
-    x = make_inputs(w.name)
+    if args.counters:
+        return counters_sequence(args)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-
-    def g(a):
-        return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
-    params = {k: g(x[k]) for k in ("lam", "P", "Q", "B", "C", "dt", "D")}
-    u0 = g(x["u"])
-    row_bytes = 4 * w.batch * w.H * w.L
-    nsets = min(1024, max(2, -(-(512 << 20) // (2 * row_bytes)) + 1))
-    us = [u0] + [u0.clone() for _ in range(nsets - 1)]
-    ys = [torch.empty_like(u0) for _ in range(nsets)]
-    K = torch.empty((w.H, w.L), dtype=torch.float32, device=dev)
-    plan = s4.Plan(w.H, w.N, w.L, w.batch, diagonal=w.diagonal, device=dev)
-    ws = plan.workspace()
-    stream = torch.cuda.current_stream()
-    P = None if w.diagonal else params["P"]
-
-    def step(i):
-        s4.forward(plan, params["lam"], P, params["Q"], params["B"], params["C"], params["dt"],
-                   params["D"], us[i % nsets], K, ys[i % nsets], ws, stream)
-
-    log(f"[bench] {nsets} buffer sets of {2 * row_bytes / 2**20:.1f} MiB; warmup {args.warmup}")
+    w = WORKLOADS[args.workload]
+    log(f"[bench] workload {w.describe()}; generating inputs")
+    wb = Workbench(s4, torch, w, dev)
+    log(f"[bench] {wb.nsets} buffer sets of {wb.set_mib:.1f} MiB; warmup {args.warmup}")
     for i in range(args.warmup):
-        step(i)
+        wb.step(i)
     torch.cuda.synchronize()
     # ---- timed region: exactly K forward steps ---------------------------------
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
+    ev0.record(wb.stream)
     for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
+        wb.step(i)
+    ev1.record(wb.stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     fwd_ms_events = ev0.elapsed_time(ev1) / args.steps
@@ -299,133 +727,59 @@ def main() -> int:
     samples = w.batch * w.H * w.L
     value = samples / (wall / args.steps)
     log(f"[bench] forward: {ms_per_step * 1e3:.1f} us/step (events {fwd_ms_events * 1e3:.1f} us)")
-    # the same steps once more, each between its own events: median and minimum
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for i, (a, b) in enumerate(evs):
-        a.record(stream)
-        step(i)
-        b.record(stream)
+    per = wb.per_call(wb.step, args.steps)
+    log(f"[bench] forward per step: median {statistics.median(per) * 1e6:.1f} us, "
+        f"minimum {min(per) * 1e6:.1f} us")
+    # the first set's outputs, for the parity check against the oracle
+    wb.step(0)
     torch.cuda.synchronize()
-    per_step_us = [a.elapsed_time(b) * 1e3 for a, b in evs]
-    fwd_med_us, fwd_min_us = statistics.median(per_step_us), min(per_step_us)
-    log(f"[bench] forward per step: median {fwd_med_us:.1f} us, minimum {fwd_min_us:.1f} us")
-
-    # keep the first set's outputs for the parity check against the oracle
-    step(0)
-    torch.cuda.synchronize()
-    K_gpu = K.cpu().numpy().astype(np.float64)
-    y_gpu = ys[0].cpu().numpy().astype(np.float64)
-
-    # ---- stage 1 alone: kernel generation (pack, Cauchy, kernel spectrum) ------
-    def timed(fn, n):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for i in range(3):
-            fn(i)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for i in range(n):
-            fn(i)
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / n * 1e-3       # seconds per call
-
-    t_gen = timed(lambda i: s4.kernel_gen(plan, params["lam"], P, params["Q"], params["B"],
-                                          params["C"], params["dt"], K, ws, stream), args.steps)
-    # ---- stage 2 alone: one convolution-kernel launch per call ------------------
-    step(0)    # leaves the spectrum of this layer (with D) in the workspace
-    t_conv = timed(lambda i: s4.conv_apply(plan, us[i % nsets], ys[i % nsets], ws, stream),
-                   args.steps)
+    K_gpu = wb.K.cpu().numpy().astype(np.float64)
+    y_gpu = wb.ys[0].cpu().numpy().astype(np.float64)
+    t_gen, t_cauchy, t_conv = wb.stages(args.steps)
     F1, Q2 = algorithmic_counts(w)
     log(f"[bench] kernel_gen {t_gen * 1e6:.1f} us ({F1 / t_gen / 1e9:.0f} GFLOP/s), "
+        f"generating function {t_cauchy * 1e6:.1f} us ({F1 / t_cauchy / 1e9:.0f} GFLOP/s), "
         f"conv {t_conv * 1e6:.1f} us ({Q2 / t_conv / 1e9:.0f} GB/s)")
+    secondary = {} if args.no_secondary else secondary_legs(wb, args.steps, dev)
+    x_head = wb.x
+    wb.close()
+    del wb
+    torch.cuda.empty_cache()
 
-    # ---- the recurrent view: a full scan (T = L) and one decode step (T = 1) ---
-    flops_step, decode_bytes = recurrent_counts(w)
-    s4.recurrent_prepare(plan, params["lam"], P, params["Q"], params["B"], params["C"],
-                         params["dt"], ws, stream)
-    state = torch.zeros((w.batch, w.H, w.N, 2), dtype=torch.float32, device=dev)
-    scan = lambda i: s4.recurrent_scan(plan, params["D"], us[i % nsets], state, ys[i % nsets],
-                                       ws, stream)
-    t_one = timed(scan, 1)
-    n_scan = max(3, min(args.steps, int(0.5 / max(t_one, 1e-6))))
-    t_scan = timed(scan, n_scan)
-    u1 = us[0][..., :1].contiguous()
-    y1 = torch.empty_like(u1)
-    t_dec = timed(lambda i: s4.recurrent_scan(plan, params["D"], u1, state, y1, ws, stream), 200)
-    rec_tflops = flops_step * w.L / t_scan / 1e12
-    log(f"[bench] recurrent scan {t_scan * 1e6:.1f} us ({samples / t_scan:.3g} samples/s, "
-        f"{rec_tflops:.1f} TFLOP/s); decode step {t_dec * 1e6:.2f} us")
+    # ---- every workload: the configs map -----------------------------------------
+    names = (ALL_CONFIGS if args.configs == "all" else
+             [] if args.configs == "none" else args.configs.split(","))
+    configs = {}
+    for name in names:
+        cw = WORKLOADS[name]
+        if name == w.name:
+            configs[name] = {
+                "H": w.H, "N": w.N, "L": w.L, "batch": w.batch, "init": w.init,
+                "forward_us": fwd_ms_events * 1e3,
+                "forward_us_median": statistics.median(per) * 1e6,
+                "forward_us_min": min(per) * 1e6, "samples_per_s": samples / (fwd_ms_events * 1e-3),
+                "stage1_us": t_gen * 1e6,
+                "stage1_frac_fp32_peak": F1 / t_gen / 1e12 / FP32_PEAK_TFLOPS,
+                "stage1_kernel": stage1_kernel_name(w.L),
+                "stage1_kernel_us": (t_gen if fused_stage1(w.L) else t_cauchy) * 1e6,
+                "stage1_kernel_frac_fp32_peak":
+                    F1 / (t_gen if fused_stage1(w.L) else t_cauchy) / 1e12 / FP32_PEAK_TFLOPS,
+                "cauchy_algorithmic_flops": F1, "conv_kernels": conv_kernel_names(w.L),
+                "conv_us": t_conv * 1e6, "conv_gbs": Q2 / t_conv / 1e9,
+                "conv_frac_hbm": Q2 / t_conv / 1e9 / HBM_PEAK_GBS, "conv_algorithmic_bytes": Q2,
+                "stage2_samples_per_s": samples / t_conv}
+            continue
+        log(f"[bench] config {cw.describe()}")
+        cb = Workbench(s4, torch, cw, dev)
+        configs[name], _ = config_figures(cb, min(args.steps, 20), min(args.warmup, 5))
+        c = configs[name]
+        log(f"[bench]   forward {c['forward_us']:.1f} us ({c['samples_per_s']:.3g} samples/s); "
+            f"stage 1 {c['stage1_us']:.1f} us (frac {c['stage1_frac_fp32_peak']:.3f}); "
+            f"conv {c['conv_us']:.1f} us (frac {c['conv_frac_hbm']:.3f})")
+        cb.close()
+        del cb
+        torch.cuda.empty_cache()
 
-    # ---- zero-order hold (diagonal): the Vandermonde kernel on the same poles ---
-    zplan = s4.Plan(w.H, w.N, w.L, w.batch, diagonal=True, zoh=True, device=dev)
-    zws = zplan.workspace()
-    t_vd = timed(lambda i: s4.kernel_gen(zplan, params["lam"], None, None, params["B"],
-                                         params["C"], params["dt"], K, zws, stream), args.steps)
-    f_vd = 7 * w.H * w.L * w.N      # per (h, k, n): one complex product and one add
-    log(f"[bench] zoh kernel_gen {t_vd * 1e6:.1f} us ({f_vd / t_vd / 1e9:.0f} GFLOP/s)")
-    zoh = {"kernel_gen_us": t_vd * 1e6, "gflops": f_vd / t_vd / 1e9,
-           "frac_fp32_peak": f_vd / t_vd / 1e12 / FP32_PEAK_TFLOPS, "algorithmic_flops": f_vd,
-           "note": "Vandermonde kernel plus the spectrum of K padded to 2L"}
-    zplan.close()
-
-    # ---- the block around the layer: layer norm, the layer, GLU projection ------
-    from synth import make_block_params
-    bp = {k: g(v) for k, v in make_block_params(w.H, seed=1).items()}
-    bplan = s4.Plan(w.H, w.N, w.L, w.batch, diagonal=w.diagonal, device=dev, block=True)
-    bws = bplan.workspace()
-    t_blk = timed(lambda i: s4.block_forward(
-        bplan, us[i % nsets], bp["gamma"], bp["beta"], params["lam"], P, params["Q"],
-        params["B"], params["C"], params["dt"], params["D"], bp["W"], bp["bias"],
-        ys[i % nsets], bws, stream), args.steps)
-    f_proj = 2 * (2 * w.H) * w.H * w.batch * w.L        # the projection GEMM
-    log(f"[bench] block forward {t_blk * 1e6:.1f} us ({samples / t_blk:.3g} samples/s; "
-        f"projection {f_proj / 1e9:.2f} GFLOP)")
-    block = {"us": t_blk * 1e6, "samples_per_s": samples / t_blk,
-             "projection_flops": f_proj,
-             "note": "layer norm + layer + GLU projection with residual (bf16 MFMA on hi/lo split operands, fp32 accumulation)"}
-    bplan.close()
-
-    # ---- the backward pass: conv_bwd and kernel_gen_bwd -----------------------
-    bwd = None
-    if True:
-        q_bwd, f_bwd = backward_counts(w)
-        dy = ys[1 % nsets]
-        du = ys[2 % nsets]
-        dK = torch.empty((w.H, w.L), dtype=torch.float32, device=dev)
-        dD = torch.empty((w.H,), dtype=torch.float32, device=dev)
-        grads = {k: torch.empty((w.H, w.N, 2), dtype=torch.float32, device=dev)
-                 for k in ("lam", "P", "B", "C")}
-        ddt = torch.empty((w.H,), dtype=torch.float32, device=dev)
-        t_cb = timed(lambda i: s4.conv_bwd(plan, us[i % nsets], K, params["D"], dy, du, dK, dD,
-                                           ws, stream), args.steps)
-        t_kb = timed(lambda i: s4.kernel_gen_bwd(
-            plan, params["lam"], P, params["Q"], params["B"], params["C"], params["dt"], dK,
-            grads["lam"], None if w.diagonal else grads["P"], None, grads["B"], grads["C"], ddt,
-            ws, stream), args.steps)
-        log(f"[bench] conv_bwd {t_cb * 1e6:.1f} us ({q_bwd / t_cb / 1e9:.0f} GB/s), "
-            f"kernel_gen_bwd {t_kb * 1e6:.1f} us ({f_bwd / t_kb / 1e9:.0f} GFLOP/s)")
-        bwd = {
-            "conv_bwd_us": t_cb * 1e6,
-            "conv_bwd_gbs": q_bwd / t_cb / 1e9,
-            "conv_bwd_frac_hbm": q_bwd / t_cb / 1e9 / HBM_PEAK_GBS,
-            "conv_bwd_algorithmic_bytes": q_bwd,
-            "kernel_gen_bwd_us": t_kb * 1e6,
-            "kernel_gen_bwd_gflops": f_bwd / t_kb / 1e9,
-            "kernel_gen_bwd_frac_fp32_peak": f_bwd / t_kb / 1e12 / FP32_PEAK_TFLOPS,
-            "kernel_gen_bwd_algorithmic_flops": f_bwd,
-            "samples_per_s": samples / (t_cb + t_kb),
-        }
-
-    if args.copy_calibration:
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log("[bench] copy calibration: 5 copies of 1 GiB done")
-
-    traffic = read_traffic(w.name)
     result = {
         "metric": METRIC,
         "value": value,
@@ -441,59 +795,34 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "H": w.H, "N": w.N, "L": w.L, "batch": w.batch,
                    "init": w.init, "u": w.u_kind, "seed": 0},
-        "roofline": {
-            "kernel": conv_kernel_name(w.L),
-            "bound": "hbm",
-            "achieved": Q2 / t_conv / 1e9,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": Q2 / t_conv / 1e9 / HBM_PEAK_GBS,
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": Q2,
-            "launch_us": t_conv * 1e6,
-            "valu_frac_fp32_peak": stage2_flops(w) / t_conv / 1e12 / FP32_PEAK_TFLOPS,
-        },
+        "roofline": roofline(w, t_gen, t_cauchy, t_conv),
         "kernel_gen": {
-            "us": t_gen * 1e6,
-            "gflops": F1 / t_gen / 1e9,
-            "frac_fp32_peak": F1 / t_gen / 1e12 / FP32_PEAK_TFLOPS,
-            "algorithmic_flops": F1,
-            "note": "pack + Cauchy/Woodbury + kernel spectrum; flops counted for the Cauchy sums",
+            "us": t_gen * 1e6, "gflops": F1 / t_gen / 1e9,
+            "frac_fp32_peak": F1 / t_gen / 1e12 / FP32_PEAK_TFLOPS, "algorithmic_flops": F1,
+            "generating_function_us": t_cauchy * 1e6,
+            "note": "stage 1 = pack + Cauchy/Woodbury + kernel spectrum; the generating "
+                    "function is the Cauchy kernel alone; flops counted for the Cauchy sums",
         },
-        "recurrent": {
-            "kernel": "recurrent_scan_kernel (O(N) bilinear DPLR step, carried state)",
-            "scan_us": t_scan * 1e6,
-            "scan_samples_per_s": samples / t_scan,
-            "bound": "alu",
-            "achieved": rec_tflops,
-            "peak": FP32_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": rec_tflops / FP32_PEAK_TFLOPS,
-            "algorithmic_flops_per_step": flops_step,
-            "decode_step_us": t_dec * 1e6,
-            "decode_bytes_per_step": decode_bytes,
-            "decode_tokens_per_s": w.batch / t_dec,
-        },
-        "backward": bwd,
-        "zoh": zoh,
-        "block": block,
+        "stage2_samples_per_s": samples / t_conv,
         "forward_us_events": fwd_ms_events * 1e3,
-        "forward_us_median": fwd_med_us,
-        "forward_us_min": fwd_min_us,
+        "forward_us_median": statistics.median(per) * 1e6,
+        "forward_us_min": min(per) * 1e6,
+        "configs": configs,
+        **secondary,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         log(f"[bench] CPU baseline: fp64 oracle, >= {args.cpu_seconds:.0f} s")
-        cb, parity = cpu_baseline(x, K_gpu, y_gpu, args.cpu_seconds)
-        result["cpu_baseline"] = cb
+        cbl, parity = cpu_baseline(x_head, K_gpu, y_gpu, args.cpu_seconds)
+        result["cpu_baseline"] = cbl
         result["parity"] = parity
-        log(f"[bench] oracle {cb['value']:.3g} samples/s; parity K {parity['K_max_rel_err']:.2e} "
-            f"y {parity['y_max_rel_err']:.2e}")
-        cp = cpu_baseline_pool(x)
+        log(f"[bench] oracle {cbl['value']:.3g} samples/s; parity K {parity['K_max_rel_err']:.2e} "
+            f"y {parity['y_max_rel_err']:.2e} (worst channel K "
+            f"{parity['K_worst_channel_rel_err']:.2e}, y {parity['y_worst_channel_rel_err']:.2e})")
+        cp = cpu_baseline_pool(x_head)
         result["cpu_baseline_pool"] = cp
         log(f"[bench] oracle on {cp['cores']} worker processes: {cp['value']:.3g} samples/s "
             f"({cp['cpu_model']})")
-    plan.close()
     print(json.dumps(result), flush=True)
     return 0
 

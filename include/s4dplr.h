@@ -39,7 +39,12 @@
  * s4dplr_plan_workspace_bytes() bytes and 256-byte aligned.
  *
  * Preconditions not checked on the device: Re(Lambda_n) < 0 (a stable
- * system), dt > 0, all values finite.
+ * system: "The S4 kernel, from scratch", section 6 keeps the real parts
+ * negative; "ML//SSM//S4": the discrete eigenvalues then lie inside the unit
+ * circle), dt > 0, all values finite.  The library does not test them; a
+ * violation gives unspecified (possibly non-finite) outputs but no access
+ * outside the buffers.  The Python binding checks them on the host before
+ * each call when the environment variable S4DPLR_VALIDATE is 1.
  *
  * Errors: every entry point returns a status code and never aborts or prints.
  * Host-side validation runs before any launch; on a validation error nothing
@@ -127,6 +132,25 @@ s4dplr_status s4dplr_plan_init(const s4dplr_plan* plan, void* ws, hipStream_t st
 s4dplr_status s4dplr_kernel_gen(const s4dplr_plan* plan, const float* lambda, const float* P,
                                 const float* Q, const float* B, const float* C,
                                 const float* dt, float* K, void* ws, hipStream_t stream);
+
+/*
+ * The generating function alone ("The S4 kernel, from scratch", section 4):
+ * khat[h][l] = Khat(z_l) at the L roots of unity z_l = exp(-2 pi i l / L),
+ *     Khat(z) = 2/(1+z) * (k00 - k01 k10 / (1 + k11)),
+ * the four Cauchy sums over the N poles and the rank-1 Woodbury correction,
+ * with the limit (dt/2) sum_n C_n B_n at z = -1.  With S4DPLR_DIAGONAL only
+ * k00 is formed ("S4" wiki, "S4D").  khat is [H][L] interleaved complex
+ * float32 in natural frequency order; its inverse FFT's real part is the
+ * kernel of s4dplr_kernel_gen.  Parameters as for s4dplr_kernel_gen; device
+ * pointers.  Needs the plan's tables in ws (s4dplr_plan_init); writes nothing
+ * else.  khat must not overlap the inputs or the workspace (ERR_ALIAS).
+ * Errors: ERR_NULL, ERR_ALIAS, ERR_WORKSPACE, ERR_UNSUPPORTED (a plan with
+ * S4DPLR_ZOH, whose kernel is not built from this function), ERR_HIP.
+ */
+s4dplr_status s4dplr_generating_function(const s4dplr_plan* plan, const float* lambda,
+                                         const float* P, const float* Q, const float* B,
+                                         const float* C, const float* dt, float* khat, void* ws,
+                                         hipStream_t stream);
 
 /*
  * Causal convolution ("The S4 kernel, from scratch", sections 1 and 5):
@@ -262,7 +286,11 @@ s4dplr_status s4dplr_kernel_gen_bwd(const s4dplr_plan* plan, const float* lambda
  * as for s4dplr_forward (Q and D may be NULL).  The plan must have been
  * created with S4DPLR_BLOCK.  out may be x itself (in place); otherwise it
  * must not overlap x, and it must never overlap the other inputs or the
- * workspace (ERR_ALIAS).  The projection runs on the matrix cores in fp32.
+ * workspace (ERR_ALIAS).  The projection runs on the bf16 matrix cores with
+ * every operand split into two bf16 parts (hi = bf16(v), lo = bf16(v - hi))
+ * and the three products hi*hi + hi*lo + lo*hi summed in fp32 accumulators:
+ * 16 significant bits per operand, within 6e-6 of the fp64 result on the
+ * tested shapes.
  * Limit: batch <= 65535 (ERR_SHAPE).
  * Errors: ERR_NULL, ERR_SHAPE, ERR_ALIAS, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP.
  */

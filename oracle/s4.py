@@ -230,8 +230,9 @@ def generating_function(lam, P, Q, B, C, dt, L):
 
 
 def kernel_cauchy(lam, P, Q, B, C, dt, L):
-    """Time-domain kernel K = Re(ifft(K-hat)) ([scratch] section 4: "an
-    inverse FFT returns the time-domain kernel"; readings R5, R8)."""
+    """Time-domain kernel K = Re(ifft(K-hat)) ([scratch] section 4: the
+    length-L inverse FFT of the generating function gives the kernel in time;
+    readings R5, R8)."""
     return np.fft.ifft(generating_function(lam, P, Q, B, C, dt, L)).real
 
 
@@ -262,8 +263,9 @@ def conv_direct_at(u, K, D, t):
 
 
 def conv_fft(u, K, D):
-    """Causal convolution by an FFT zero-padded to 2L ([scratch] section 5,
-    "zero-padded to avoid circular wrap-around"; reading R12), plus D u.
+    """Causal convolution by an FFT zero-padded to 2L ([scratch] section 5:
+    the padding keeps the circular product from wrapping the tail of the
+    output onto its start; reading R12), plus D u.
 
     ``u`` may be [..., L]; ``K`` broadcasts against it; ``D`` likewise
     (shape [..., 1] or scalar).

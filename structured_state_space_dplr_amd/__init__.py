@@ -8,6 +8,13 @@ float32, contiguous and on the GPU; complex parameters are [H, N, 2]
 
 There is no fallback: if the library is missing or fails to load, importing
 this package raises.
+
+Preconditions that the kernels do not test on the device -- Re(Lambda) < 0
+(stable poles), dt > 0 and every value finite -- are checked on the host
+before the call when the environment variable ``S4DPLR_VALIDATE`` is ``1``;
+a violation raises ``S4DPLRPreconditionError``.  The check copies the
+inputs to host memory and synchronizes, so it is for debugging, not for the
+timed path.
 """
 from __future__ import annotations
 
@@ -17,8 +24,10 @@ import os
 import torch  # loads the HIP runtime that libs4dplr then shares
 
 __all__ = [
-    "S4DPLRError", "DIAGONAL", "ZOH", "BLOCK", "abi_version", "status_string", "plan_create",
-    "plan_workspace_bytes", "plan_init", "kernel_gen", "conv_fwd", "forward",
+    "S4DPLRError", "S4DPLRPreconditionError", "check_preconditions", "validation_enabled",
+    "DIAGONAL", "ZOH", "BLOCK", "abi_version", "status_string", "plan_create",
+    "plan_workspace_bytes", "plan_init", "kernel_gen", "generating_function", "conv_fwd",
+    "forward",
     "conv_apply", "recurrent_prepare", "recurrent_scan", "conv_bwd", "kernel_gen_bwd",
     "block_forward",
     "plan_destroy", "Plan", "LIB_PATH",
@@ -52,6 +61,8 @@ _lib.s4dplr_plan_init.restype = ctypes.c_int
 _lib.s4dplr_plan_init.argtypes = [_p, _p, _p]
 _lib.s4dplr_kernel_gen.restype = ctypes.c_int
 _lib.s4dplr_kernel_gen.argtypes = [_p] * 10
+_lib.s4dplr_generating_function.restype = ctypes.c_int
+_lib.s4dplr_generating_function.argtypes = [_p] * 10
 _lib.s4dplr_conv_fwd.restype = ctypes.c_int
 _lib.s4dplr_conv_fwd.argtypes = [_p] * 7
 _lib.s4dplr_forward.restype = ctypes.c_int
@@ -84,6 +95,65 @@ class S4DPLRError(RuntimeError):
 def _check(status: int, where: str) -> None:
     if status != 0:
         raise S4DPLRError(status, where)
+
+
+VALIDATE_ENV = "S4DPLR_VALIDATE"
+
+
+class S4DPLRPreconditionError(ValueError):
+    """An input violates a precondition the kernels do not check: Re(Lambda)
+    < 0 ("The S4 kernel, from scratch", section 6 keeps the real parts of the
+    poles negative; "ML//SSM//S4": a stable discrete system needs its
+    eigenvalues inside the unit circle, which the bilinear map gives exactly
+    for Re(Lambda) < 0), dt > 0, or finite values.  Raised only with
+    S4DPLR_VALIDATE=1."""
+
+    def __init__(self, where: str, what: str):
+        super().__init__(f"{where}: {what}")
+        self.where, self.what = where, what
+
+
+def validation_enabled() -> bool:
+    return os.environ.get(VALIDATE_ENV, "") == "1"
+
+
+def _host(t):
+    return torch.as_tensor(t).detach().to(device="cpu", dtype=torch.float64)
+
+
+def check_preconditions(where: str = "check_preconditions", lam=None, dt=None, **tensors) -> None:
+    """Raise S4DPLRPreconditionError for the first violated precondition:
+    every given tensor finite, Re(lam[..., 0]) < 0 strictly, dt > 0 strictly.
+    Tensors may live on any device (they are copied to host memory); None is
+    skipped."""
+    named = dict(tensors)
+    named["lam"], named["dt"] = lam, dt
+    for name, t in named.items():
+        if t is None:
+            continue
+        h = _host(t)
+        bad = ~torch.isfinite(h)
+        if bool(bad.any()):
+            idx = tuple(int(i) for i in bad.nonzero()[0])
+            raise S4DPLRPreconditionError(where, f"{name} is not finite at index {idx}")
+    if lam is not None:
+        re = _host(lam)[..., 0]
+        bad = re >= 0
+        if bool(bad.any()):
+            idx = tuple(int(i) for i in bad.nonzero()[0])
+            raise S4DPLRPreconditionError(
+                where, f"Re(lam) must be < 0 (stable pole); lam{list(idx)} has Re = {float(re[idx]):g}")
+    if dt is not None:
+        d = _host(dt)
+        bad = d <= 0
+        if bool(bad.any()):
+            idx = int(bad.nonzero()[0][0])
+            raise S4DPLRPreconditionError(where, f"dt must be > 0; dt[{idx}] = {float(d[idx]):g}")
+
+
+def _validate(where: str, **kw) -> None:
+    if validation_enabled():
+        check_preconditions(where, **kw)
 
 
 def abi_version() -> int:
@@ -144,6 +214,7 @@ def plan_init(plan: int, ws, stream=None) -> None:
 
 
 def kernel_gen(plan: "Plan | int", lam, P, Q, B, C, dt, K, ws, stream=None) -> None:
+    _validate("kernel_gen", lam=lam, dt=dt, P=P, Q=Q, B=B, C=C)
     p, (H, N, L, _) = _dims(plan)
     cplx = (H, N, 2)
     _check(_lib.s4dplr_kernel_gen(
@@ -152,7 +223,19 @@ def kernel_gen(plan: "Plan | int", lam, P, Q, B, C, dt, K, ws, stream=None) -> N
         _stream(stream)), "kernel_gen")
 
 
+def generating_function(plan: "Plan | int", lam, P, Q, B, C, dt, khat, ws, stream=None) -> None:
+    """K-hat at the L roots of unity into ``khat`` ([H, L, 2] float32)."""
+    _validate("generating_function", lam=lam, dt=dt, P=P, Q=Q, B=B, C=C)
+    p, (H, N, L, _) = _dims(plan)
+    cplx = (H, N, 2)
+    _check(_lib.s4dplr_generating_function(
+        p, _ptr(lam, "lam", cplx), _ptr(P, "P", cplx), _ptr(Q, "Q", cplx), _ptr(B, "B", cplx),
+        _ptr(C, "C", cplx), _ptr(dt, "dt", (H,)), _ptr(khat, "khat", (H, L, 2)), _ws_ptr(ws),
+        _stream(stream)), "generating_function")
+
+
 def conv_fwd(plan: "Plan | int", u, K, D, y, ws, stream=None) -> None:
+    _validate("conv_fwd", u=u, K=K, D=D)
     p, (H, N, L, batch) = _dims(plan)
     _check(_lib.s4dplr_conv_fwd(
         p, _ptr(u, "u", (batch, H, L)), _ptr(K, "K", (H, L)), _ptr(D, "D", (H,)),
@@ -160,6 +243,7 @@ def conv_fwd(plan: "Plan | int", u, K, D, y, ws, stream=None) -> None:
 
 
 def forward(plan: "Plan | int", lam, P, Q, B, C, dt, D, u, K, y, ws, stream=None) -> None:
+    _validate("forward", lam=lam, dt=dt, P=P, Q=Q, B=B, C=C, D=D, u=u)
     p, (H, N, L, batch) = _dims(plan)
     cplx = (H, N, 2)
     _check(_lib.s4dplr_forward(
@@ -170,6 +254,7 @@ def forward(plan: "Plan | int", lam, P, Q, B, C, dt, D, u, K, y, ws, stream=None
 
 
 def conv_apply(plan: "Plan | int", u, y, ws, stream=None) -> None:
+    _validate("conv_apply", u=u)
     p, (H, N, L, batch) = _dims(plan)
     _check(_lib.s4dplr_conv_apply(
         p, _ptr(u, "u", (batch, H, L)), _ptr(y, "y", (batch, H, L)), _ws_ptr(ws),
@@ -177,6 +262,7 @@ def conv_apply(plan: "Plan | int", u, y, ws, stream=None) -> None:
 
 
 def recurrent_prepare(plan: "Plan | int", lam, P, Q, B, C, dt, ws, stream=None) -> None:
+    _validate("recurrent_prepare", lam=lam, dt=dt, P=P, Q=Q, B=B, C=C)
     p, (H, N, L, _) = _dims(plan)
     cplx = (H, N, 2)
     _check(_lib.s4dplr_recurrent_prepare(
@@ -188,6 +274,7 @@ def recurrent_prepare(plan: "Plan | int", lam, P, Q, B, C, dt, ws, stream=None) 
 def recurrent_scan(plan: "Plan | int", D, u, state, y, ws, stream=None) -> None:
     """T = u.shape[-1] steps from ``state`` ([batch, H, N, 2], updated in place)."""
     p, (H, N, L, batch) = _dims(plan)
+    _validate("recurrent_scan", D=D, u=u, state=state)
     if u is None or u.dim() != 3:
         raise ValueError("u: expected a [batch, H, T] tensor")
     T = int(u.shape[-1])
@@ -198,6 +285,7 @@ def recurrent_scan(plan: "Plan | int", D, u, state, y, ws, stream=None) -> None:
 
 
 def conv_bwd(plan: "Plan | int", u, K, D, dy, du, dK, dD, ws, stream=None) -> None:
+    _validate("conv_bwd", u=u, K=K, D=D, dy=dy)
     p, (H, N, L, batch) = _dims(plan)
     _check(_lib.s4dplr_conv_bwd(
         p, _ptr(u, "u", (batch, H, L)), _ptr(K, "K", (H, L)), _ptr(D, "D", (H,)),
@@ -207,6 +295,7 @@ def conv_bwd(plan: "Plan | int", u, K, D, dy, du, dK, dD, ws, stream=None) -> No
 
 def kernel_gen_bwd(plan: "Plan | int", lam, P, Q, B, C, dt, dK, dlam, dP, dQ, dB, dC, ddt, ws,
                    stream=None) -> None:
+    _validate("kernel_gen_bwd", lam=lam, dt=dt, P=P, Q=Q, B=B, C=C, dK=dK)
     p, (H, N, L, _) = _dims(plan)
     cplx = (H, N, 2)
     _check(_lib.s4dplr_kernel_gen_bwd(
@@ -219,6 +308,8 @@ def kernel_gen_bwd(plan: "Plan | int", lam, P, Q, B, C, dt, dK, dlam, dP, dQ, dB
 
 def block_forward(plan: "Plan | int", x, gamma, beta, lam, P, Q, B, C, dt, D, W, bias, out, ws,
                   stream=None) -> None:
+    _validate("block_forward", lam=lam, dt=dt, x=x, gamma=gamma, beta=beta, P=P, Q=Q, B=B, C=C,
+              D=D, W=W, bias=bias)
     p, (H, N, L, batch) = _dims(plan)
     cplx = (H, N, 2)
     _check(_lib.s4dplr_block_forward(

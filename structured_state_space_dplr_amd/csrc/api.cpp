@@ -286,6 +286,28 @@ s4dplr_status s4dplr_kernel_gen(const s4dplr_plan* p, const float* lambda, const
   return S4DPLR_OK;
 }
 
+s4dplr_status s4dplr_generating_function(const s4dplr_plan* p, const float* lambda,
+                                         const float* P, const float* Q, const float* B,
+                                         const float* C, const float* dt, float* khat, void* ws,
+                                         hipStream_t stream) {
+  if (!valid_plan(p)) return S4DPLR_ERR_NULL;
+  if (s4dplr_status st = check_params(p, lambda, P, B, C, dt)) return st;
+  if (!khat) return S4DPLR_ERR_NULL;
+  if (s4dplr_status st = check_ws(ws)) return st;
+  if (p->flags & S4DPLR_ZOH) return S4DPLR_ERR_UNSUPPORTED;
+  const size_t kb = 2 * sizeof(float) * (size_t)p->H * p->L;
+  const size_t cb = 2 * sizeof(float) * (size_t)p->H * p->N;
+  const size_t hb = sizeof(float) * (size_t)p->H;
+  if (overlaps(khat, kb, ws, p->total) || overlaps(khat, kb, lambda, cb) ||
+      overlaps(khat, kb, P, cb) || overlaps(khat, kb, Q, cb) || overlaps(khat, kb, B, cb) ||
+      overlaps(khat, kb, C, cb) || overlaps(khat, kb, dt, hb))
+    return S4DPLR_ERR_ALIAS;
+  hipError_t e = s4::launch_generating_function(p, lambda, P, Q, B, C, dt, khat,
+                                                static_cast<unsigned char*>(ws), stream);
+  if (e != hipSuccess) return hip_fail(e);
+  return S4DPLR_OK;
+}
+
 s4dplr_status s4dplr_conv_fwd(const s4dplr_plan* p, const float* u, const float* K,
                               const float* D, float* y, void* ws, hipStream_t stream) {
   if (!valid_plan(p)) return S4DPLR_ERR_NULL;

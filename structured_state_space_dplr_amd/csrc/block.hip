@@ -21,8 +21,9 @@ namespace {
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kLnThreads = 256;
-// Projection tile: 128 time steps by K stages of 32 channels (the channel
-// extent of a tile is the kernel's template argument).
+// Projection tiles: K stages of 32 channels; 128 time steps per tile for
+// 64-channel tiles, 2 * 128 = 256 for 128-channel tiles (the channel and time
+// extents of a tile are the kernel's template arguments).
 constexpr int kPN = 128, kPK = 32;
 
 }  // namespace
@@ -111,14 +112,15 @@ __global__ __launch_bounds__(kLnThreads) void layer_norm_kernel(
 // w_hi s_hi + w_hi s_lo + w_lo s_hi in the fp32 accumulators; the dropped
 // w_lo s_lo and the split's own rounding are below 2^-16 relative per term.
 // W is split once per call by split_w_kernel (every tile reads it); s is
-// split while staged.  A block owns CM channels x 128 time steps of both
-// halves, CM = 128 when H allows it (s is then split by half as many blocks),
-// else 64; wave w owns channels [32 (w / 2), +32) and time steps
-// [64 (w % 2), +64) as two 32 x 32 tiles per half.  Each K stage of 32
-// channels stages CM rows x 32 of each W part as [row][k] and 32 x 128 of s
-// transposed as [t][k] through LDS, so that a lane's eight consecutive k of
-// an operand are one 16-byte read; the next stage's global loads are issued
-// before the current stage's MFMAs.  Fully in-range tiles take the vector
+// split while staged.  A block owns CM channels x TN time steps of both
+// halves: CM = 128 and TN = 256 (512 threads) when H is a multiple of 128,
+// else CM = 64 and TN = 128 (256 threads); wave w owns channels
+// [32 (w / 2), +32) and time steps [(TN / 2) (w % 2), +TN / 2) as TN / 64
+// 32 x 32 tiles per half.  Each K stage of 32 channels stages CM rows x 32 of
+// each W part as [row][k] and 32 x TN of s as [t][k] through double-buffered
+// LDS, so that a lane's eight consecutive k of an operand are one 16-byte
+// read; the next stage's global loads are issued before the current stage's
+// MFMAs.  Fully in-range tiles take the vector
 // path; edge tiles load element by element with zero fill.
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 

@@ -62,6 +62,12 @@ bool lds_path(const s4dplr_plan* p);
 hipError_t launch_kernel_gen(const s4dplr_plan* p, const float* lam, const float* P,
                              const float* Q, const float* B, const float* C, const float* dt,
                              const float* D, float* Kout, unsigned char* ws, hipStream_t s);
+// The generating function at the L roots of unity into khat [H][L] (natural
+// order when natural is set, else the order the plan's kernel spectrum reads).
+hipError_t launch_generating_function(const s4dplr_plan* p, const float* lam, const float* P,
+                                      const float* Q, const float* B, const float* C,
+                                      const float* dt, float* khat, unsigned char* ws,
+                                      hipStream_t s);
 // The convolution weights from a given time-domain kernel; with conj set, the
 // weights of the correlation with (K + D delta) instead (the input gradient).
 hipError_t launch_spectrum_from_time(const s4dplr_plan* p, const float* Ktime, const float* D,

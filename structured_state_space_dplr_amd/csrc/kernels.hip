@@ -983,14 +983,12 @@ static void kgen_launch(const s4dplr_plan* p, const ParamPtrs& pp, const float* 
   }
 }
 
-hipError_t launch_cauchy(const s4dplr_plan* p, const ParamPtrs& pp, unsigned char* ws,
-                         hipStream_t s) {
+static hipError_t launch_cauchy_to(const s4dplr_plan* p, const ParamPtrs& pp, float2* khat,
+                                   int perm_m1, unsigned char* ws, hipStream_t s) {
   constexpr int F = 2;
   const int per_block = F * kCauchyThreads;
   dim3 grid((p->L + per_block - 1) / per_block, p->H);
   const float* tanT = at<const float>(ws, p->off_tan);
-  float2* khat = at<float2>(ws, p->off_khat);
-  const int perm_m1 = lds_path(p) ? 0 : p->L / 256;
   if (p->flags & S4DPLR_DIAGONAL)
     cauchy_kernel<F, true><<<grid, kCauchyThreads, 0, s>>>(pp, tanT, khat, p->N, p->NP, p->L,
                                                            perm_m1);
@@ -998,6 +996,20 @@ hipError_t launch_cauchy(const s4dplr_plan* p, const ParamPtrs& pp, unsigned cha
     cauchy_kernel<F, false><<<grid, kCauchyThreads, 0, s>>>(pp, tanT, khat, p->N, p->NP, p->L,
                                                             perm_m1);
   return hipGetLastError();
+}
+
+hipError_t launch_cauchy(const s4dplr_plan* p, const ParamPtrs& pp, unsigned char* ws,
+                         hipStream_t s) {
+  return launch_cauchy_to(p, pp, at<float2>(ws, p->off_khat), lds_path(p) ? 0 : p->L / 256, ws,
+                          s);
+}
+
+hipError_t launch_generating_function(const s4dplr_plan* p, const float* lam, const float* P,
+                                      const float* Q, const float* B, const float* C,
+                                      const float* dt, float* khat, unsigned char* ws,
+                                      hipStream_t s) {
+  return launch_cauchy_to(p, param_ptrs(lam, P, Q, B, C, dt), reinterpret_cast<float2*>(khat), 0,
+                          ws, s);
 }
 
 template <int LOG2L>

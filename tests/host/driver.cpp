@@ -45,6 +45,19 @@ int main() {
         CHECK(s4dplr_kernel_gen(p, f, f, nullptr, f, f, f, K, ws, nullptr) == S4DPLR_OK);
         CHECK(s4dplr_forward(p, f, f, nullptr, f, f, f, nullptr, u, nullptr, y, ws, nullptr) == S4DPLR_OK);
         CHECK(s4dplr_conv_apply(p, u, y, ws, nullptr) == S4DPLR_OK);
+        {
+          float* kh = reinterpret_cast<float*>(base + 8 * gap);
+          const s4dplr_status want = (flags & S4DPLR_ZOH) ? S4DPLR_ERR_UNSUPPORTED : S4DPLR_OK;
+          CHECK(s4dplr_generating_function(p, f, f, nullptr, f, f, f, kh, ws, nullptr) == want);
+          CHECK(s4dplr_generating_function(p, f, f, nullptr, f, f, f, nullptr, ws, nullptr) ==
+                S4DPLR_ERR_NULL);
+          // khat overlapping the workspace or a parameter
+          const s4dplr_status alias = (flags & S4DPLR_ZOH) ? S4DPLR_ERR_UNSUPPORTED : S4DPLR_ERR_ALIAS;
+          CHECK(s4dplr_generating_function(p, f, f, nullptr, f, f, f, static_cast<float*>(ws), ws,
+                                           nullptr) == alias);
+          CHECK(s4dplr_generating_function(p, f, f, nullptr, f, f, f, const_cast<float*>(f), ws,
+                                           nullptr) == alias);
+        }
         CHECK(s4dplr_recurrent_prepare(p, f, f, nullptr, f, f, f, ws, nullptr) == S4DPLR_OK);
         {
           float* g = reinterpret_cast<float*>(base + 4 * gap);

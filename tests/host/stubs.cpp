@@ -26,6 +26,12 @@ hipError_t launch_kernel_gen(const s4dplr_plan*, const float*, const float*, con
   ++g_launches;
   return hipSuccess;
 }
+hipError_t launch_generating_function(const s4dplr_plan*, const float*, const float*,
+                                      const float*, const float*, const float*, const float*,
+                                      float*, unsigned char*, hipStream_t) {
+  ++g_launches;
+  return hipSuccess;
+}
 hipError_t launch_spectrum_from_time(const s4dplr_plan*, const float*, const float*,
                                      unsigned char*, hipStream_t, int) {
   ++g_launches;

@@ -54,7 +54,7 @@ def test_header_declares_the_boundary():
               "s4dplr_conv_fwd", "s4dplr_forward", "s4dplr_plan_destroy",
               "s4dplr_last_hip_error", "s4dplr_conv_apply", "s4dplr_recurrent_prepare",
               "s4dplr_recurrent_scan", "s4dplr_conv_bwd", "s4dplr_kernel_gen_bwd",
-              "s4dplr_block_forward"]:
+              "s4dplr_block_forward", "s4dplr_generating_function"]:
         assert n in names
 
 

@@ -26,3 +26,54 @@ def test_pool_baseline_splits_every_channel():
     assert r["kind"] == "oracle" and r["unit"] == "samples/s"
     assert 1 <= r["cores"] <= min(3, w.H)
     assert r["value"] > 0 and r["seconds_per_forward"] > 0
+
+
+def test_cpu_baseline_sample_and_parity_fields():
+    # the GPU outputs replaced by the oracle's own: zero error, every field
+    import numpy as np
+    import oracle
+    x = make_inputs("tiny")
+    K, y = oracle.forward(x["lam"], x["P"], x["Q"], x["B"], x["C"], x["dt"], x["D"], x["u"])
+    cb, par = bench.cpu_baseline(x, K, y, min_seconds=0.0)
+    assert cb["kind"] == "oracle" and cb["cores"] == 1 and cb["value"] > 0
+    assert 1 <= par["channels_checked"] <= x["workload"].H
+    assert par["K_max_rel_err"] == 0.0 and par["y_worst_channel_rel_err"] == 0.0
+
+
+def test_roofline_picks_the_dominant_kernel():
+    w = WORKLOADS["waveform"]
+    r = bench.roofline(w, t_gen=190e-6, t_cauchy=130e-6, t_conv=136e-6)
+    assert r["kernel"] == "cauchy_kernel" and r["bound"] == "alu" and r["unit"] == "TFLOP/s"
+    assert math.isclose(r["frac"], bench.algorithmic_counts(w)[0] / 130e-6 / 1e12 / 157.3)
+    assert r["conv"]["bound"] == "hbm" and "big_rows_pair_kernel" in r["conv"]["kernel"]
+    m = WORKLOADS["mid"]
+    r = bench.roofline(m, t_gen=16e-6, t_cauchy=20e-6, t_conv=26e-6)
+    assert r["kernel"] == "conv_pair1024_kernel" and r["bound"] == "hbm"
+    assert r["stage1_kernel"]["kernel"] == "kgen_wave_kernel"
+
+
+def test_trace_and_counter_summaries(tmp_path):
+    tr = tmp_path / "trace" / "host"
+    tr.mkdir(parents=True)
+    rows = [("void s4::cauchy_kernel<2, false>(s4::ParamPtrs, ...)", 0, 1000),
+            ("void s4::cauchy_kernel<2, false>(s4::ParamPtrs, ...)", 5000, 7000),
+            ("big_rows_pair_kernel(float2 const*, ...)", 8000, 8500)]
+    with open(tr / "x_kernel_trace.csv", "w") as f:
+        f.write("Kernel_Name,Start_Timestamp,End_Timestamp\n")
+        for n, a, b in rows:
+            f.write(f'"{n}",{a},{b}\n')
+    md = bench.summarize_trace(str(tmp_path / "trace"), "label", "cmd")
+    assert "| cauchy_kernel | 2 | 1.50 |" in md and "| big_rows_pair_kernel | 1 | 0.50 |" in md
+    for counter, val, copy in (("FETCH_SIZE", 100.0, 524288.0), ("WRITE_SIZE", 300.0, 1048576.0)):
+        d = tmp_path / counter
+        d.mkdir()
+        with open(d / "r_counter_collection.csv", "w") as f:
+            f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+            for i in range(6):
+                f.write(f'{i},"s4::cauchy_kernel<2, false>(x)",{counter},{val}\n')
+            f.write(f'9,"__amd_rocclr_copyBuffer",{counter},{copy}\n')
+    res = bench.summarize_counters(str(tmp_path / "FETCH_SIZE"), str(tmp_path / "WRITE_SIZE"),
+                                   "waveform", ["c1", "c2"])
+    k = res["kernels"]["cauchy_kernel"]
+    assert math.isclose(res["calibration"]["fetch_scale"], 2.0)
+    assert math.isclose(k["bytes_per_launch"], 2.0 * 1024 * 100 + 1.0 * 1024 * 300)

@@ -146,8 +146,10 @@ def test_conv_bwd_large_batch(s4):
 
 # ---- kernel generation backward -----------------------------------------------
 
-@pytest.mark.parametrize("L", [2, 4, 16, 64, 256, 1024, 2048, 32768, 65536])
+@pytest.mark.parametrize("L", [2, 4, 16, 64, 256, 1024, 2048, 4096, 8192, 16384, 32768, 65536])
 def test_kernel_gen_bwd_lengths(s4, L):
+    # every length class of the Ghat transform (wave-resident, LDS Stockham
+    # for 2048 <= L <= 16384, four-step above)
     H = 2 if L <= 2048 else 1
     print(f"case: kernel_gen_bwd generic H={H} N=8 L={L}", flush=True)
     x = make_generic_inputs(H=H, N=8, L=L, batch=1, seed=40 + L)
@@ -155,6 +157,23 @@ def test_kernel_gen_bwd_lengths(s4, L):
     g = gpu_kernel_gen_bwd(s4, x, dK)
     ref = o.kernel_backward_dense(x["lam"], x["P"], x["Q"], x["B"], x["C"], x["dt"], dK)
     check_param_grads(g, ref, f"L={L}")
+
+
+@pytest.mark.parametrize("L,init", [(4096, "generic"), (8192, "hippo"), (16384, "generic"),
+                                    (16384, "hippo")])
+def test_kernel_gen_bwd_64_poles_long(s4, L, init):
+    # 64 poles (the workloads' pole count) at the lengths whose Ghat comes
+    # from the block-level Stockham transform; HiPPO-LegS poles with the
+    # long workload's step range, or generic per-channel DPLR parameters
+    print(f"case: kernel_gen_bwd {init} H=2 N=64 L={L}", flush=True)
+    if init == "hippo":
+        x = make_inputs("long", H=2, batch=1, L=L)
+    else:
+        x = make_generic_inputs(H=2, N=64, L=L, batch=1, seed=80 + L)
+    dK = np.random.default_rng(L + 3).standard_normal((2, L)).astype(np.float32)
+    g = gpu_kernel_gen_bwd(s4, x, dK)
+    ref = o.kernel_backward_dense(x["lam"], x["P"], x["Q"], x["B"], x["C"], x["dt"], dK)
+    check_param_grads(g, ref, f"{init} N=64 L={L}")
 
 
 @pytest.mark.parametrize("diagonal,distinct_q", [(True, False), (False, True)])
@@ -183,7 +202,8 @@ def _slice(x, hs):
     return {k: (v[hs] if isinstance(v, np.ndarray) and k != "u" else v) for k, v in x.items()}
 
 
-@pytest.mark.parametrize("name,n_ch", [("tiny", 4), ("mid", 2), ("s4d_lin", 1), ("waveform", 1)])
+@pytest.mark.parametrize("name,n_ch", [("tiny", 4), ("mid", 2), ("long", 1), ("s4d_lin", 1),
+                                         ("waveform", 1)])
 def test_layer_gradients_workload(s4, name, n_ch):
     # the whole chain on the GPU: forward, then conv_bwd -> dK -> kernel_gen_bwd,
     # against the oracle's chain on sampled channels

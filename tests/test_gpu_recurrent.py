@@ -223,7 +223,8 @@ def test_deterministic_and_non_default_stream(s4):
 
 # ---- the workloads at full size, sampled channels ---------------------------
 
-@pytest.mark.parametrize("name,n_ch", [("tiny", 16), ("mid", 4), ("s4d_lin", 2), ("long", 1)])
+@pytest.mark.parametrize("name,n_ch", [("tiny", 16), ("mid", 4), ("s4d_lin", 2), ("long", 1),
+                                         ("waveform", 1)])
 def test_workload_parity_sampled(s4, name, n_ch):
     w = WORKLOADS[name]
     print(f"case: recurrent workload {w.describe()}, {n_ch} channels checked", flush=True)
