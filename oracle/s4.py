@@ -48,6 +48,7 @@ __all__ = [
     "hippo_legs", "nplr_legs", "dplr_legs",
     "dense_state_matrix", "discretize_bilinear", "discretize_zoh_scalar",
     "kernel_truncated", "kernel_aliased_dense", "generating_function",
+    "generating_function_lowrank",
     "kernel_cauchy", "conv_direct", "conv_direct_at", "conv_fft",
     "recurrence", "forward", "recurrent_forward",
     "conv_backward_direct", "conv_backward_fft", "kernel_backward_dense",
@@ -117,10 +118,16 @@ def dplr_legs(N: int):
 # ---------------------------------------------------------------------------
 
 def dense_state_matrix(lam, P, Q):
-    """A = diag(Lambda) - P Q^*  ([scratch] section 2; [wiki] eq. A = Lambda - PQ^*)."""
+    """A = diag(Lambda) - P Q^*  ([scratch] section 2; [wiki] "Structured
+    Transition Matrix": A = Lambda - P Q^* with low-rank P, Q).
+
+    P, Q are vectors (rank 1) or N x r matrices (rank r)."""
     lam = np.asarray(lam, dtype=np.complex128)
-    return np.diag(lam) - np.outer(np.asarray(P, np.complex128),
-                                   np.conj(np.asarray(Q, np.complex128)))
+    P = np.asarray(P, np.complex128)
+    Q = np.asarray(Q, np.complex128)
+    if P.ndim == 1:
+        return np.diag(lam) - np.outer(P, np.conj(Q))
+    return np.diag(lam) - P @ np.conj(Q).T
 
 
 def discretize_bilinear(A, B, dt):
@@ -229,10 +236,51 @@ def generating_function(lam, P, Q, B, C, dt, L):
     return Khat
 
 
+def generating_function_lowrank(lam, P, Q, B, C, dt, L):
+    """K-hat at the L roots of unity for a rank-r low-rank term, A = Lambda -
+    P Q^* with P, Q of shape (N, r) ([wiki] "Structured Transition Matrix":
+    low-rank P, Q, the correction handled by the Woodbury identity;
+    [scratch] section 4 for g, the roots of unity and the 2/(1+z) factor).
+
+    With R = (g I - Lambda)^{-1} diagonal, the Woodbury identity gives
+      C (g I - A)^{-1} B = k00 - k01 (I_r + k11)^{-1} k10,
+    k00 = C R B (scalar), k01 = C R P (1 x r), k10 = Q^* R B (r x 1),
+    k11 = Q^* R P (r x r): (r + 1)^2 Cauchy sums over the poles.  The r x r
+    system is solved per frequency by a library solve.  At z = -1 the limit
+    (dt/2) sum_n C_n B_n (reading R9: the correction vanishes like 1/g^2).
+    For r = 1 this is ``generating_function``."""
+    lam = np.asarray(lam, np.complex128)
+    P = np.asarray(P, np.complex128)
+    Q = np.asarray(Q, np.complex128)
+    B = np.asarray(B, np.complex128)
+    C = np.asarray(C, np.complex128)
+    r_rank = P.shape[1]
+    ell = np.arange(L)
+    Khat = np.empty(L, dtype=np.complex128)
+    regular = np.ones(L, dtype=bool)
+    if L % 2 == 0:
+        regular[L // 2] = False
+    z = np.exp(-2j * np.pi * ell[regular] / L)
+    g = (2.0 / dt) * (1.0 - z) / (1.0 + z)
+    R = 1.0 / (g[:, None] - lam[None, :])               # Cauchy matrix [l, n]
+    k00 = R @ (C * B)                                   # [l]
+    k01 = R @ (C[:, None] * P)                          # [l, r]
+    k10 = R @ (np.conj(Q) * B[:, None])                 # [l, r]
+    k11 = np.einsum("ln,ni,nj->lij", R, np.conj(Q), P)  # [l, r, r]
+    I = np.eye(r_rank, dtype=np.complex128)
+    x = np.linalg.solve(I[None] + k11, k10[..., None])[..., 0]   # (I + k11)^{-1} k10
+    Khat[regular] = (2.0 / (1.0 + z)) * (k00 - np.sum(k01 * x, axis=1))
+    if L % 2 == 0:
+        Khat[L // 2] = (dt / 2.0) * np.sum(C * B)
+    return Khat
+
+
 def kernel_cauchy(lam, P, Q, B, C, dt, L):
     """Time-domain kernel K = Re(ifft(K-hat)) ([scratch] section 4: the
     length-L inverse FFT of the generating function gives the kernel in time;
     readings R5, R8)."""
+    if np.ndim(P) == 2:
+        return np.fft.ifft(generating_function_lowrank(lam, P, Q, B, C, dt, L)).real
     return np.fft.ifft(generating_function(lam, P, Q, B, C, dt, L)).real
 
 
@@ -313,12 +361,21 @@ def _as_complex(a):
     return a[..., 0] + 1j * a[..., 1]
 
 
+def _low_rank(a):
+    """P or Q as stored, (H, N, 2) for rank 1 or (H, r, N, 2) for rank r
+    (the r vectors of length N one after another), -> complex (H, N) or
+    (H, N, r): per channel the N x r matrix of [wiki] "Structured Transition
+    Matrix"."""
+    c = _as_complex(a)
+    return c if c.ndim == 2 else np.swapaxes(c, 1, 2)
+
+
 def forward(lam, P, Q, B, C, dt, D, u, method="cauchy", diagonal=False, disc="bilinear"):
     """K [H, L] and y [batch, H, L] for H independent channels
     ([scratch] section 1: one SSM per feature channel).
 
-    Complex inputs are (H, N, 2) float arrays; dt, D are (H,); u is
-    (batch, H, L).  ``method`` selects the kernel: "cauchy" (the pages'
+    Complex inputs are (H, N, 2) float arrays (P and Q may be (H, r, N, 2)
+    for a rank-r low-rank term); dt, D are (H,); u is (batch, H, L).  ``method`` selects the kernel: "cauchy" (the pages'
     generating-function method) or "dense" (the aliased plain definition).
     ``diagonal`` drops the low-rank term (S4D, [wiki] "S4D": P = Q = 0).
     ``disc="zoh"`` (diagonal only) uses the zero-order-hold Vandermonde kernel
@@ -343,8 +400,8 @@ def forward(lam, P, Q, B, C, dt, D, u, method="cauchy", diagonal=False, disc="bi
         P_c = np.zeros((H, N), np.complex128)
         Q_c = P_c
     else:
-        P_c = _as_complex(P)
-        Q_c = P_c if Q is None else _as_complex(Q)
+        P_c = _low_rank(P)
+        Q_c = P_c if Q is None else _low_rank(Q)
     B_c = _as_complex(B)
     C_c = _as_complex(C)
     dt = np.asarray(dt, np.float64)
@@ -376,8 +433,8 @@ def recurrent_forward(lam, P, Q, B, C, dt, D, u, x0=None, diagonal=False, disc="
         P_c = np.zeros((H, N), np.complex128)
         Q_c = P_c
     else:
-        P_c = _as_complex(P)
-        Q_c = P_c if Q is None else _as_complex(Q)
+        P_c = _low_rank(P)
+        Q_c = P_c if Q is None else _low_rank(Q)
     B_c = _as_complex(B)
     C_c = _as_complex(C)
     dt = np.asarray(dt, np.float64)

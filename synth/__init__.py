@@ -144,21 +144,23 @@ def make_inputs(workload, seed: int = 0, batch: int | None = None, H: int | None
 
 def make_generic_inputs(H: int, N: int, L: int, batch: int, seed: int = 0,
                         diagonal: bool = False, distinct_q: bool = False,
-                        dt_lo: float = 1e-3, dt_hi: float = 1e-1):
+                        dt_lo: float = 1e-3, dt_hi: float = 1e-1, rank: int = 1):
     """Per-channel random DPLR parameters (not an initialization from the
     pages) for robustness cases: Re(Lambda) in -[0.05, 1], Im(Lambda) in
     [-40, 40], P, B, C complex Gaussian drawn independently, so B is not a
     multiple of P; with ``distinct_q`` an independent Q of modest size.
+    With ``rank`` r > 1, P (and Q) hold r vectors of N: shape [H, r, N, 2].
 
     Draw order: Lambda re, Lambda im, P, B, C, Q (if distinct), log dt, D, u.
     """
     rng = np.random.default_rng(seed)
     cn = lambda *s: rng.normal(0.0, np.sqrt(0.5), size=s) + 1j * rng.normal(0.0, np.sqrt(0.5), size=s)
     lam = -rng.uniform(0.05, 1.0, size=(H, N)) + 1j * rng.uniform(-40.0, 40.0, size=(H, N))
-    P = cn(H, N)
+    lr = (H, N) if rank == 1 else (H, rank, N)
+    P = cn(*lr)
     B = cn(H, N)
     C = cn(H, N)
-    Q = 0.3 * cn(H, N) if distinct_q else None
+    Q = 0.3 * cn(*lr) if distinct_q else None
     log_dt = rng.uniform(np.log(dt_lo), np.log(dt_hi), size=H)
     D = rng.standard_normal(H)
     u = rng.standard_normal((batch, H, L))

@@ -626,3 +626,110 @@ def test_block_forward_composition():
     z = o.layer_norm(x["u"], p["gamma"], p["beta"])
     _, s = o.forward(x["lam"], x["P"], x["Q"], x["B"], x["C"], x["dt"], x["D"], z)
     np.testing.assert_allclose(out, x["u"] + s / 2, atol=1e-12)
+
+
+# ---- rank-r low-rank term ([wiki] "Structured Transition Matrix": A = Lambda
+# - P Q^* with low-rank P, Q; the correction by the Woodbury identity) --------
+
+def _rank_case(N, r, seed, distinct_q):
+    rng = np.random.default_rng(seed)
+    cn = lambda *s: rng.normal(0, np.sqrt(0.5), s) + 1j * rng.normal(0, np.sqrt(0.5), s)
+    lam = -rng.uniform(0.05, 1.0, N) + 1j * rng.uniform(-20, 20, N)
+    P = cn(N, r)
+    Q = 0.4 * cn(N, r) if distinct_q else P
+    return lam, P, Q, cn(N), cn(N), float(np.exp(rng.uniform(np.log(1e-2), np.log(0.3))))
+
+
+@pytest.mark.parametrize("r,distinct_q", [(2, False), (3, True), (4, False), (4, True)])
+def test_lowrank_cauchy_equals_dense_aliased(r, distinct_q):
+    # the plain definition (matrix powers of the dense bilinear system)
+    # against the Cauchy sums + r x r Woodbury solve, on the same A
+    N, L = 12, 64
+    lam, P, Q, B, C, dt = _rank_case(N, r, 100 + r, distinct_q)
+    K = np.fft.ifft(o.generating_function_lowrank(lam, P, Q, B, C, dt, L)).real
+    Abar, Bbar = o.discretize_bilinear(o.dense_state_matrix(lam, P, Q), B, dt)
+    Kd = o.kernel_aliased_dense(Abar, Bbar, C, L)
+    assert np.abs(K - Kd).max() <= 1e-10 * np.abs(Kd).max()
+
+
+@pytest.mark.parametrize("r", [2, 3])
+def test_lowrank_generating_function_equals_resolvent_solve(r):
+    # K-hat_l = 2/(1+z) C (g I - A)^{-1} B by a dense linear solve at every
+    # regular root of unity, and the closed-form limit at z = -1
+    N, L = 9, 32
+    lam, P, Q, B, C, dt = _rank_case(N, r, 200 + r, True)
+    # A written out as the diagonal minus r rank-one terms
+    A = np.diag(lam) - sum(np.outer(P[:, j], Q[:, j].conj()) for j in range(r))
+    kh = o.generating_function_lowrank(lam, P, Q, B, C, dt, L)
+    for l in range(L):
+        if 2 * l == L:
+            assert abs(kh[l] - dt / 2 * np.sum(C * B)) <= 1e-13 * np.abs(kh).max()
+            continue
+        z = np.exp(-2j * np.pi * l / L)
+        g = 2 / dt * (1 - z) / (1 + z)
+        ref = 2 / (1 + z) * (C @ np.linalg.solve(g * np.eye(N) - A, B))
+        assert abs(kh[l] - ref) <= 1e-11 * abs(ref) + 1e-13
+
+
+def test_lowrank_zero_column_reduces_the_rank():
+    # a zero column of P (with any Q) or of Q removes that rank-one term
+    N, L = 10, 48
+    lam, P, Q, B, C, dt = _rank_case(N, 3, 300, True)
+    for j in range(3):
+        keep = [i for i in range(3) if i != j]
+        Pz = P.copy()
+        Pz[:, j] = 0
+        ref = o.generating_function_lowrank(lam, P[:, keep], Q[:, keep], B, C, dt, L)
+        got = o.generating_function_lowrank(lam, Pz, Q, B, C, dt, L)
+        assert np.abs(got - ref).max() <= 1e-12 * np.abs(ref).max()
+        Qz = Q.copy()
+        Qz[:, j] = 0
+        got = o.generating_function_lowrank(lam, P, Qz, B, C, dt, L)
+        assert np.abs(got - ref).max() <= 1e-12 * np.abs(ref).max()
+    # all columns zero: the diagonal system
+    Z = np.zeros((N, 3), np.complex128)
+    diag = o.generating_function(lam, np.zeros(N), np.zeros(N), B, C, dt, L)
+    assert np.abs(o.generating_function_lowrank(lam, Z, Q, B, C, dt, L) - diag).max() \
+        <= 1e-13 * np.abs(diag).max()
+
+
+def test_lowrank_rank_one_and_column_order():
+    # r = 1 is the rank-1 generating function; permuting the columns of P and
+    # Q together leaves P Q^* (and so K-hat) unchanged
+    N, L = 16, 64
+    lam, P, Q, B, C, dt = _rank_case(N, 1, 400, True)
+    ref = o.generating_function(lam, P[:, 0], Q[:, 0], B, C, dt, L)
+    got = o.generating_function_lowrank(lam, P, Q, B, C, dt, L)
+    assert np.abs(got - ref).max() <= 1e-13 * np.abs(ref).max()
+    lam, P, Q, B, C, dt = _rank_case(N, 4, 401, True)
+    perm = [2, 0, 3, 1]
+    a = o.generating_function_lowrank(lam, P, Q, B, C, dt, L)
+    b = o.generating_function_lowrank(lam, P[:, perm], Q[:, perm], B, C, dt, L)
+    assert np.abs(a - b).max() <= 1e-12 * np.abs(a).max()
+
+
+@pytest.mark.parametrize("L", [16, 256])
+def test_lowrank_dc_and_nyquist_sums(L):
+    # sum_k K_k = Re K-hat(1) = Re(-C A^{-1} B); sum_k (-1)^k K_k = Re((dt/2) C.B)
+    N = 8
+    lam, P, Q, B, C, dt = _rank_case(N, 2, 500 + L, True)
+    K = np.fft.ifft(o.generating_function_lowrank(lam, P, Q, B, C, dt, L)).real
+    A = o.dense_state_matrix(lam, P, Q)
+    dc = (-C @ np.linalg.solve(A, B)).real
+    assert abs(K.sum() - dc) <= 1e-11 * max(1.0, abs(dc))
+    ny = (dt / 2 * np.sum(C * B)).real
+    assert abs(np.sum(K * (-1.0) ** np.arange(L)) - ny) <= 1e-11 * max(1.0, abs(ny))
+
+
+def test_lowrank_forward_layout():
+    # the (H, r, N, 2) storage: forward() per channel equals the per-channel
+    # generating function of the N x r matrices
+    x = make_generic_inputs(H=2, N=8, L=32, batch=2, seed=600, rank=3, distinct_q=True)
+    K, y = o.forward(x["lam"], x["P"], x["Q"], x["B"], x["C"], x["dt"], x["D"], x["u"])
+    c = lambda a: a[..., 0].astype(np.float64) + 1j * a[..., 1]
+    for h in range(2):
+        Pm, Qm = c(x["P"][h]).T, c(x["Q"][h]).T         # (N, r)
+        Abar, Bbar = o.discretize_bilinear(o.dense_state_matrix(c(x["lam"][h]), Pm, Qm),
+                                           c(x["B"][h]), float(x["dt"][h]))
+        Kd = o.kernel_aliased_dense(Abar, Bbar, c(x["C"][h]), 32)
+        assert np.abs(K[h] - Kd).max() <= 1e-10 * np.abs(Kd).max()
