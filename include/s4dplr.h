@@ -70,7 +70,8 @@ typedef enum s4dplr_status {
   S4DPLR_ERR_WORKSPACE = 3,   /* workspace NULL-sized or not 256-byte aligned    */
   S4DPLR_ERR_UNSUPPORTED = 4, /* unknown flag bits                               */
   S4DPLR_ERR_HIP = 5,         /* HIP runtime error while enqueueing              */
-  S4DPLR_ERR_ALIAS = 6        /* output buffer overlaps an input it must not     */
+  S4DPLR_ERR_ALIAS = 6,       /* output buffer overlaps an input it must not     */
+  S4DPLR_ERR_TOO_LARGE = 7    /* plan exceeds the static scratch of *_noalloc    */
 } s4dplr_status;
 
 /* Plan flag: diagonal state matrix (S4D).  P and Q are ignored (may be NULL). */
@@ -173,6 +174,28 @@ s4dplr_status s4dplr_forward(const s4dplr_plan* plan, const float* lambda, const
                              const float* Q, const float* B, const float* C, const float* dt,
                              const float* D, const float* u, float* K, float* y, void* ws,
                              hipStream_t stream);
+
+/*
+ * s4dplr_forward without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops that forbid
+ * allocation): the scratch is a static device array of the library, 64 MiB
+ * per GPU, held from its first use on that GPU until the process ends.  Plans
+ * whose forward pass needs more (the four-step path at large batch * H, e.g.
+ * H = 64, L = 65536, batch = 4) are rejected with ERR_TOO_LARGE; the
+ * tiny, mid, long and S4D-Lin workload shapes fit.  Computes exactly what
+ * s4dplr_forward computes, with the same kernels, on the current device;
+ * stream must belong to it.  Every call re-writes the plan's tables into the
+ * array (a copy from the plan's host memory, so the plan must outlive the
+ * call's completion on the stream), then generates the kernel and applies the
+ * convolution.  All calls on one GPU share its array: calls that can overlap
+ * in time on one GPU (other streams, other threads) race and must be
+ * serialized by the caller.  No device memory is allocated or freed.
+ * Errors: ERR_NULL, ERR_ALIAS, ERR_TOO_LARGE, ERR_HIP.
+ */
+s4dplr_status s4dplr_forward_noalloc(const s4dplr_plan* plan, const float* lambda,
+                                     const float* P, const float* Q, const float* B,
+                                     const float* C, const float* dt, const float* D,
+                                     const float* u, float* K, float* y, hipStream_t stream);
 
 /*
  * Apply the convolution with the kernel spectrum already in the workspace:

@@ -27,7 +27,7 @@ __all__ = [
     "S4DPLRError", "S4DPLRPreconditionError", "check_preconditions", "validation_enabled",
     "DIAGONAL", "ZOH", "BLOCK", "abi_version", "status_string", "plan_create",
     "plan_workspace_bytes", "plan_init", "kernel_gen", "generating_function", "conv_fwd",
-    "forward",
+    "forward", "forward_noalloc",
     "conv_apply", "recurrent_prepare", "recurrent_scan", "conv_bwd", "kernel_gen_bwd",
     "block_forward",
     "plan_destroy", "Plan", "LIB_PATH",
@@ -67,6 +67,8 @@ _lib.s4dplr_conv_fwd.restype = ctypes.c_int
 _lib.s4dplr_conv_fwd.argtypes = [_p] * 7
 _lib.s4dplr_forward.restype = ctypes.c_int
 _lib.s4dplr_forward.argtypes = [_p] * 13
+_lib.s4dplr_forward_noalloc.restype = ctypes.c_int
+_lib.s4dplr_forward_noalloc.argtypes = [_p] * 12
 _lib.s4dplr_conv_apply.restype = ctypes.c_int
 _lib.s4dplr_conv_apply.argtypes = [_p] * 5
 _lib.s4dplr_recurrent_prepare.restype = ctypes.c_int
@@ -251,6 +253,18 @@ def forward(plan: "Plan | int", lam, P, Q, B, C, dt, D, u, K, y, ws, stream=None
         _ptr(C, "C", cplx), _ptr(dt, "dt", (H,)), _ptr(D, "D", (H,)),
         _ptr(u, "u", (batch, H, L)), _ptr(K, "K", (H, L)), _ptr(y, "y", (batch, H, L)),
         _ws_ptr(ws), _stream(stream)), "forward")
+
+
+def forward_noalloc(plan: "Plan | int", lam, P, Q, B, C, dt, D, u, K, y, stream=None) -> None:
+    """``forward`` on the library's static device scratch (no workspace)."""
+    _validate("forward_noalloc", lam=lam, dt=dt, P=P, Q=Q, B=B, C=C, D=D, u=u)
+    p, (H, N, L, batch) = _dims(plan)
+    cplx = (H, N, 2)
+    _check(_lib.s4dplr_forward_noalloc(
+        p, _ptr(lam, "lam", cplx), _ptr(P, "P", cplx), _ptr(Q, "Q", cplx), _ptr(B, "B", cplx),
+        _ptr(C, "C", cplx), _ptr(dt, "dt", (H,)), _ptr(D, "D", (H,)),
+        _ptr(u, "u", (batch, H, L)), _ptr(K, "K", (H, L)), _ptr(y, "y", (batch, H, L)),
+        _stream(stream)), "forward_noalloc")
 
 
 def conv_apply(plan: "Plan | int", u, y, ws, stream=None) -> None:

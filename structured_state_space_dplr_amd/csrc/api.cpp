@@ -103,6 +103,8 @@ const char* s4dplr_status_string(s4dplr_status s) {
     case S4DPLR_ERR_UNSUPPORTED: return "unsupported flags";
     case S4DPLR_ERR_HIP: return "HIP runtime error while enqueueing";
     case S4DPLR_ERR_ALIAS: return "an output buffer overlaps an input or the workspace";
+    case S4DPLR_ERR_TOO_LARGE:
+      return "the plan needs more scratch than the library's static device array holds";
   }
   return "unknown status";
 }
@@ -157,6 +159,7 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
   p->off_big = off;
   if (!lds) off = align_up(off + sizeof(float) * 2 * (size_t)batch * H * L);
   p->off_big2 = off;
+  p->fwd_bytes = off;   // the forward pass uses nothing past this point
   if (!lds) off = align_up(off + sizeof(float) * 2 * (size_t)batch * H * L);
   p->off_rrec = off;
   off = align_up(off + sizeof(float) * 16 * (size_t)H * N);
@@ -339,6 +342,32 @@ s4dplr_status s4dplr_forward(const s4dplr_plan* p, const float* lambda, const fl
     return S4DPLR_ERR_ALIAS;
   unsigned char* w = static_cast<unsigned char*>(ws);
   hipError_t e;
+  if ((e = s4::launch_kernel_gen(p, lambda, P, Q, B, C, dt, D, K, w, stream)) != hipSuccess)
+    return hip_fail(e);
+  if ((e = s4::launch_conv(p, u, y, w, stream)) != hipSuccess) return hip_fail(e);
+  return S4DPLR_OK;
+}
+
+s4dplr_status s4dplr_forward_noalloc(const s4dplr_plan* p, const float* lambda, const float* P,
+                                     const float* Q, const float* B, const float* C,
+                                     const float* dt, const float* D, const float* u, float* K,
+                                     float* y, hipStream_t stream) {
+  if (!valid_plan(p)) return S4DPLR_ERR_NULL;
+  if (s4dplr_status st = check_params(p, lambda, P, B, C, dt)) return st;
+  if (!u || !y) return S4DPLR_ERR_NULL;
+  const size_t ub = sizeof(float) * (size_t)p->batch * p->H * p->L;
+  const size_t kb = sizeof(float) * (size_t)p->H * p->L;
+  if (overlaps(y, ub, u, ub)) return S4DPLR_ERR_ALIAS;
+  if (K && (overlaps(K, kb, u, ub) || overlaps(K, kb, y, ub))) return S4DPLR_ERR_ALIAS;
+  if (p->fwd_bytes > s4::noalloc_scratch_bytes()) return S4DPLR_ERR_TOO_LARGE;
+  unsigned char* w = nullptr;
+  hipError_t e = s4::noalloc_scratch(&w);
+  if (e != hipSuccess) return hip_fail(e);
+  // the array keeps whatever the last call on this device left in it: the
+  // tables of this plan are written again by every call
+  if ((e = hipMemcpyAsync(w, p->tables.data(), p->tables_bytes, hipMemcpyHostToDevice,
+                          stream)) != hipSuccess)
+    return hip_fail(e);
   if ((e = s4::launch_kernel_gen(p, lambda, P, Q, B, C, dt, D, K, w, stream)) != hipSuccess)
     return hip_fail(e);
   if ((e = s4::launch_conv(p, u, y, w, stream)) != hipSuccess) return hip_fail(e);

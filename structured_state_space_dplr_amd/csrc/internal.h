@@ -45,6 +45,7 @@ struct s4dplr_plan {
   size_t off_bz;     // block (S4DPLR_BLOCK): [batch][H][L] float normalized input
   size_t off_bs;     // block (S4DPLR_BLOCK): [batch][H][L] float layer output
   size_t off_bw;     // block (S4DPLR_BLOCK): [2][2H][H] bf16: W split into hi and lo parts
+  size_t fwd_bytes;  // prefix of the workspace the forward pass touches (tables .. off_big2)
   size_t total;
   std::vector<unsigned char> tables;  // exact bytes of the table region
 };
@@ -85,6 +86,11 @@ hipError_t launch_big_corr(const s4dplr_plan* p, const float* u, const float* dy
                            float* dD, unsigned char* ws, hipStream_t s);
 hipError_t launch_big_ghat(const s4dplr_plan* p, const float* dK, unsigned char* ws,
                            hipStream_t s);
+
+// The library's own device scratch for s4dplr_forward_noalloc: its size, and
+// its address on the current device (looked up once per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(unsigned char** out);
 
 // Recurrent view: per-pole step records from the parameters, then T steps of
 // every (batch, channel) sequence from the carried state.

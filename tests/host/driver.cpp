@@ -45,6 +45,9 @@ int main() {
         CHECK(s4dplr_kernel_gen(p, f, f, nullptr, f, f, f, K, ws, nullptr) == S4DPLR_OK);
         CHECK(s4dplr_forward(p, f, f, nullptr, f, f, f, nullptr, u, nullptr, y, ws, nullptr) == S4DPLR_OK);
         CHECK(s4dplr_conv_apply(p, u, y, ws, nullptr) == S4DPLR_OK);
+        CHECK(s4dplr_forward_noalloc(p, f, f, nullptr, f, f, f, nullptr, u, K, y, nullptr) == S4DPLR_OK);
+        CHECK(s4dplr_forward_noalloc(p, f, f, nullptr, f, f, f, nullptr, u, K, u, nullptr) == S4DPLR_ERR_ALIAS);
+        CHECK(s4dplr_forward_noalloc(p, f, f, nullptr, f, f, f, nullptr, nullptr, K, y, nullptr) == S4DPLR_ERR_NULL);
         {
           float* kh = reinterpret_cast<float*>(base + 8 * gap);
           const s4dplr_status want = (flags & S4DPLR_ZOH) ? S4DPLR_ERR_UNSUPPORTED : S4DPLR_OK;
@@ -92,6 +95,23 @@ int main() {
       CHECK(lg >= 0 && lg <= 5);
       CHECK((ppl << lg) >= N);
     }
+  {
+    // the no-allocation forward rejects plans whose forward scratch exceeds
+    // the static array (H = 64, L = 65536, batch = 4: about 241 MiB)
+    s4dplr_plan* big = nullptr;
+    CHECK(s4dplr_plan_create(&big, 64, 64, 65536, 4, 0) == S4DPLR_OK);
+    const uintptr_t base = uintptr_t(1) << 40, gap = uintptr_t(1) << 34;
+    const float* f = reinterpret_cast<const float*>(base);
+    float* u = reinterpret_cast<float*>(base + gap);
+    float* y = reinterpret_cast<float*>(base + 2 * gap);
+    CHECK(s4dplr_forward_noalloc(big, f, f, nullptr, f, f, f, nullptr, u, nullptr, y, nullptr) ==
+          S4DPLR_ERR_TOO_LARGE);
+    s4dplr_plan_destroy(big);
+    CHECK(s4dplr_plan_create(&big, 128, 64, 16384, 8, 0) == S4DPLR_OK);
+    CHECK(s4dplr_forward_noalloc(big, f, f, nullptr, f, f, f, nullptr, u, nullptr, y, nullptr) ==
+          S4DPLR_OK);
+    s4dplr_plan_destroy(big);
+  }
   s4dplr_plan* p = nullptr;
   CHECK(s4dplr_plan_create(&p, 1, 1, 3, 1, 0) == S4DPLR_ERR_SHAPE && !p);
   CHECK(s4dplr_plan_create(&p, 1, 1, 4, 1, 8) == S4DPLR_ERR_UNSUPPORTED);

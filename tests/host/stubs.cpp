@@ -4,6 +4,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <cstring>
+#include <vector>
 
 #include "internal.h"
 
@@ -19,6 +20,14 @@ extern "C" hipError_t hipMemcpyAsync(void* dst, const void* src, size_t n, hipMe
 extern "C" hipError_t hipGetLastError(void) { return hipSuccess; }
 
 namespace s4 {
+// the library's static scratch, played by host memory of the same size
+static std::vector<unsigned char>* g_scratch = nullptr;
+size_t noalloc_scratch_bytes() { return size_t(64) << 20; }
+hipError_t noalloc_scratch(unsigned char** out) {
+  if (!g_scratch) g_scratch = new std::vector<unsigned char>(noalloc_scratch_bytes());
+  *out = g_scratch->data();
+  return hipSuccess;
+}
 bool lds_path(const s4dplr_plan* p) { return p->log2L <= S4DPLR_LDS_MAX_LOG2L; }
 hipError_t launch_kernel_gen(const s4dplr_plan*, const float*, const float*, const float*,
                              const float*, const float*, const float*, const float*, float*,

@@ -54,7 +54,7 @@ def test_header_declares_the_boundary():
               "s4dplr_conv_fwd", "s4dplr_forward", "s4dplr_plan_destroy",
               "s4dplr_last_hip_error", "s4dplr_conv_apply", "s4dplr_recurrent_prepare",
               "s4dplr_recurrent_scan", "s4dplr_conv_bwd", "s4dplr_kernel_gen_bwd",
-              "s4dplr_block_forward", "s4dplr_generating_function"]:
+              "s4dplr_block_forward", "s4dplr_generating_function", "s4dplr_forward_noalloc"]:
         assert n in names
 
 
@@ -68,7 +68,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.s4dplr_abi_version() == 1
-    for s in range(7):
+    for s in range(8):
         assert len(lib.s4dplr_status_string(s)) > 0
     assert lib.s4dplr_status_string(99) == b"unknown status"
 
