@@ -187,12 +187,10 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
   if (p->rchunk) off = align_up(off + sizeof(float) * 2 * (size_t)H * p->rchunk * N);
   p->off_bghat = off;
   off = align_up(off + sizeof(float) * 2 * (size_t)H * L);
-  p->off_bbeta = off;
-  off = align_up(off + sizeof(float) * 8 * (size_t)H * L);
   p->off_bpart = off;
   {
     const size_t nchunks = (L + s4::kBwdChunk - 1) / s4::kBwdChunk;
-    size_t need = sizeof(float) * 12 * (size_t)H * nchunks * N;   // per-pole sums
+    size_t need = sizeof(double) * 10 * (size_t)H * nchunks * N;   // 5 fp64 complex per-pole sums
     if (lds) {
       // the partial spectra of the batch-row groups, plus one row for their sum
       const size_t corr = sizeof(float) * 2 *

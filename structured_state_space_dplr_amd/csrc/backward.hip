@@ -19,12 +19,13 @@
 // beta_ab,l = conj(alpha_ab,l) Ghat_l, per pole n:
 //   R_ab = sum_l beta_ab,l conj(r_n,l),
 //   T    = sum_l conj(r_n,l)^2 sum_ab conj(w_ab,n) beta_ab,l,
-//   E    = sum_l conj(g_l) conj(r_n,l)^2 sum_ab conj(w_ab,n) beta_ab,l,
 // and grad(C_n) = conj(B) R00 + conj(P) R01, grad(B_n) = conj(C) R00 + Q R10,
 // grad(P_n) = conj(C) R01 + Q R11, grad(Q_n) = B conj(R10) + P conj(R11),
-// grad(Lambda_n) = T, dloss/ddt = Re(sum_n E) / dt (g = (2/dt)(1-z)/(1+z)).
-// The frequency l = L/2 (z = -1) uses the limit Khat = (dt/2) sum_n C_n B_n
-// and is added separately.
+// grad(Lambda_n) = T.  The frequency l = L/2 (z = -1) uses the limit
+// Khat = (dt/2) sum_n C_n B_n and is added separately.  dt enters the
+// bilinear kernel only through dt Lambda, dt P Q^* and dt B, so
+// dt dloss/ddt = Re sum_n [conj(grad Lambda_n) Lambda_n + conj(grad B_n) B_n
+// + conj(grad_P-path P_n) P_n].
 #include <hip/hip_runtime.h>
 
 #include "cauchy.h"
@@ -560,213 +561,226 @@ __global__ __launch_bounds__(CorrShape<LOG2L>::NT) void ghat_kernel(
   }
 }
 
-// beta_ab,l = conj(alpha_ab,l) Ghat_l per (channel, frequency), stored as two
-// float4: (beta00, beta01), (beta10, beta11); zero at l = L/2.
-//   alpha00 = p, alpha01 = -p k10 / (1 + k11), alpha10 = -p k01 / (1 + k11),
-//   alpha11 = p k01 k10 / (1 + k11)^2, p = 2/(1+z) = 1 + i tan(pi l / L).
-template <int F, bool DIAG>
-__global__ __launch_bounds__(kCauchyThreads) void kgen_bwd_coef_kernel(
-    ParamPtrs pp, const float* __restrict__ tanT, const float2* __restrict__ ghat,
-    float4* __restrict__ beta, int N, int NP, int L) {
-  __shared__ float4 rec[kRec * kMaxPoles];
-  __shared__ float2 red[kCauchyThreads / 64];
-  const int h = blockIdx.y, tid = threadIdx.x;
-  const float2 part = build_pole_records(pp, h, N, NP, DIAG, rec, tid, kCauchyThreads);
-  block_sum2<kCauchyThreads>(part, red, tid);   // (barrier: the records are complete)
-  const float two_dt = 2.0f / pp.dt[h];
-  int l[F];
-  float T[F], G[F], acc[F][8];
-#pragma unroll
-  for (int f = 0; f < F; ++f) {
-    l[f] = (blockIdx.x * F + f) * kCauchyThreads + tid;
-    T[f] = l[f] < L ? tanT[l[f]] : 0.f;
-    G[f] = two_dt * T[f];
-#pragma unroll
-    for (int a = 0; a < 8; ++a) acc[f][a] = 0.f;
-  }
-  cauchy_sums<F, DIAG>(rec, NP, G, acc);
-#pragma unroll
-  for (int f = 0; f < F; ++f) {
-    if (l[f] >= L) continue;
-    float4* out = beta + 2 * ((size_t)h * L + l[f]);
-    if (2 * l[f] == L) {
-      out[0] = out[1] = make_float4(0.f, 0.f, 0.f, 0.f);
-      continue;
-    }
-    const float2 p = make_float2(1.0f, T[f]);
-    const float2 gh = ghat[(size_t)h * L + l[f]];
-    const float2 b00 = cmul(cconj(p), gh);
-    if constexpr (DIAG) {
-      out[0] = make_float4(b00.x, b00.y, 0.f, 0.f);
-      out[1] = make_float4(0.f, 0.f, 0.f, 0.f);
-    } else {
-      const float2 k01 = make_float2(acc[f][2], acc[f][3]);
-      const float2 k10 = make_float2(acc[f][4], acc[f][5]);
-      const float2 d = make_float2(1.0f + acc[f][6], acc[f][7]);
-      const float inv = 1.0f / fmaf(d.x, d.x, d.y * d.y);
-      const float2 id = make_float2(d.x * inv, -d.y * inv);      // 1 / (1 + k11)
-      const float2 pid = cmul(p, id);
-      const float2 a01 = cmul(make_float2(-pid.x, -pid.y), k10);
-      const float2 a10 = cmul(make_float2(-pid.x, -pid.y), k01);
-      const float2 a11 = cmul(cmul(pid, id), cmul(k01, k10));
-      const float2 b01 = cmul(cconj(a01), gh), b10 = cmul(cconj(a10), gh);
-      const float2 b11 = cmul(cconj(a11), gh);
-      out[0] = make_float4(b00.x, b00.y, b01.x, b01.y);
-      out[1] = make_float4(b10.x, b10.y, b11.x, b11.y);
-    }
-  }
+// fp64 complex helpers of the per-pole sums
+struct dcx {
+  double x, y;
+};
+__device__ __forceinline__ dcx dc(float2 a) { return dcx{(double)a.x, (double)a.y}; }
+__device__ __forceinline__ dcx dadd(dcx a, dcx b) { return dcx{a.x + b.x, a.y + b.y}; }
+__device__ __forceinline__ dcx dmul(dcx a, dcx b) {
+  return dcx{fma(a.x, b.x, -a.y * b.y), fma(a.x, b.y, a.y * b.x)};
+}
+__device__ __forceinline__ dcx dconj(dcx a) { return dcx{a.x, -a.y}; }
+__device__ __forceinline__ dcx dmac(dcx acc, dcx a, dcx b) {   // acc + a b
+  return dcx{fma(a.x, b.x, fma(-a.y, b.y, acc.x)), fma(a.x, b.y, fma(a.y, b.x, acc.y))};
 }
 
-// Per-pole sums R_ab, T, E over a chunk of kBwdChunk frequencies: block
-// (chunk, h), thread = (pole n, frequency subset); partials to the workspace.
+// Per-pole sums over one chunk of kBwdChunk frequencies of channel h, in two
+// phases that meet in LDS:
+//  1. thread t takes frequency l = l0 + t: the forward Cauchy sums k_ab
+//     (fp32, the forward's own helper) and the Woodbury partials
+//       beta_ab = conj(alpha_ab) Ghat_l,  alpha00 = p,
+//       alpha01 = -p k10 / (1 + k11),  alpha10 = -p k01 / (1 + k11),
+//       alpha11 = p k01 k10 / (1 + k11)^2,  p = 2/(1+z) = 1 + i tan(pi l / L),
+//     formed in fp64 (zero at l = L/2);
+//  2. thread (pole n, frequency subset) accumulates in fp64
+//       R_ab = sum_l beta_ab conj(r),  T = sum_l conj(r)^2 sum_ab conj(w_ab) beta_ab,
+//     r = 1 / (i G_l - Lambda_n), then the subsets meet in LDS.
+// The partials [R00, R01, R10, R11, T] per pole go to the workspace as fp64.
+// The gradient of dt is formed later from these sums (see the final kernel);
+// it cancels across poles, and fp32 partials would cost it several digits.
+constexpr int kPoleSums = 5;
+
 template <bool DIAG>
-__global__ __launch_bounds__(256) void kgen_bwd_pole_kernel(
-    ParamPtrs pp, const float* __restrict__ tanT, const float4* __restrict__ beta,
-    float2* __restrict__ part, int N, int L, int log2npp) {
-  __shared__ float4 sb[2 * kBwdChunk];
+__global__ __launch_bounds__(256) void kgen_bwd_chunk_kernel(
+    ParamPtrs pp, const float* __restrict__ tanT, const float2* __restrict__ ghat,
+    dcx* __restrict__ part, int N, int NP, int L, int log2npp) {
+  constexpr int NB = DIAG ? 1 : 4;
+  __shared__ float4 rec[kRec * kMaxPoles];
+  __shared__ float2 red2[256 / 64];
+  __shared__ dcx sb[NB * kBwdChunk];
   __shared__ float sG[kBwdChunk];
-  __shared__ float red[256 * 12];
+  __shared__ double red[256 * 2 * kPoleSums];
   const int h = blockIdx.y, lc = blockIdx.x, tid = threadIdx.x;
   const int l0 = lc * kBwdChunk;
   const int nl = min(kBwdChunk, L - l0);
+  const float2 wsum = build_pole_records(pp, h, N, NP, DIAG, rec, tid, 256);
+  block_sum2<256>(wsum, red2, tid);   // (barrier: the records are complete)
   const float two_dt = 2.0f / pp.dt[h];
-  for (int i = tid; i < nl; i += 256) {
-    sb[2 * i] = beta[2 * ((size_t)h * L + l0 + i)];
-    sb[2 * i + 1] = beta[2 * ((size_t)h * L + l0 + i) + 1];
-    sG[i] = two_dt * tanT[l0 + i];
+  {
+    const int l = l0 + tid;
+    float Tl[1], G[1], acc[1][8];
+    Tl[0] = tid < nl ? tanT[l] : 0.f;
+    G[0] = two_dt * Tl[0];
+#pragma unroll
+    for (int a = 0; a < 8; ++a) acc[0][a] = 0.f;
+    cauchy_sums<1, DIAG>(rec, NP, G, acc);
+    if (tid < nl) {
+      sG[tid] = G[0];
+      dcx b[4] = {{0.0, 0.0}, {0.0, 0.0}, {0.0, 0.0}, {0.0, 0.0}};
+      if (2 * l != L) {
+        const dcx p = dcx{1.0, (double)Tl[0]};
+        const dcx gh = dc(ghat[(size_t)h * L + l]);
+        b[0] = dmul(dconj(p), gh);
+        if constexpr (!DIAG) {
+          const dcx k01 = dcx{acc[0][2], acc[0][3]}, k10 = dcx{acc[0][4], acc[0][5]};
+          const dcx d = dcx{1.0 + acc[0][6], acc[0][7]};
+          const double inv = 1.0 / fma(d.x, d.x, d.y * d.y);
+          const dcx id = dcx{d.x * inv, -d.y * inv};          // 1 / (1 + k11)
+          const dcx pid = dmul(p, id);
+          const dcx mpid = dcx{-pid.x, -pid.y};
+          b[1] = dmul(dconj(dmul(mpid, k10)), gh);
+          b[2] = dmul(dconj(dmul(mpid, k01)), gh);
+          b[3] = dmul(dconj(dmul(dmul(pid, id), dmul(k01, k10))), gh);
+        }
+      }
+#pragma unroll
+      for (int a = 0; a < NB; ++a) sb[NB * tid + a] = b[a];
+    }
   }
+  __syncthreads();
   const int npp = 1 << log2npp, sub_n = 256 >> log2npp;
   const int n = tid & (npp - 1), sub = tid >> log2npp;
-  float2 lam = make_float2(-1.f, 0.f), cw00 = make_float2(0.f, 0.f), cw01 = cw00, cw10 = cw00,
-         cw11 = cw00;
+  float2 lam = make_float2(-1.f, 0.f);
+  dcx cw[4] = {{0.0, 0.0}, {0.0, 0.0}, {0.0, 0.0}, {0.0, 0.0}};
   if (n < N) {
     const size_t idx = (size_t)h * N + n;
     lam = pp.lam[idx];
-    const float2 b = pp.B[idx], c = pp.C[idx];
-    cw00 = cconj(cmul(c, b));
+    const float2 bv = pp.B[idx], cv = pp.C[idx];
+    cw[0] = dconj(dmul(dc(cv), dc(bv)));
     if constexpr (!DIAG) {
       const float2 pv = pp.P[idx], qv = pp.Q ? pp.Q[idx] : pv;
-      cw01 = cconj(cmul(c, pv));
-      cw10 = cconj(cmul(cconj(qv), b));
-      cw11 = cconj(cmul(cconj(qv), pv));
+      cw[1] = dconj(dmul(dc(cv), dc(pv)));
+      cw[2] = dconj(dmul(dconj(dc(qv)), dc(bv)));
+      cw[3] = dconj(dmul(dconj(dc(qv)), dc(pv)));
     }
   }
-  __syncthreads();
-  float2 R00 = make_float2(0.f, 0.f), R01 = R00, R10 = R00, R11 = R00, Tn = R00, En = R00;
+  dcx R[4] = {{0.0, 0.0}, {0.0, 0.0}, {0.0, 0.0}, {0.0, 0.0}};
+  dcx Tn = {0.0, 0.0};
   const float nre = -lam.x;
   for (int i = sub; i < nl; i += sub_n) {
-    const float G = sG[i];
-    const float y = G - lam.y;
+    const float y = sG[i] - lam.y;
     const float inv = __builtin_amdgcn_rcpf(fmaf(y, y, lam.x * lam.x));
-    const float2 cr = make_float2(nre * inv, y * inv);            // conj(1 / (i G - Lambda))
-    const float4 b0 = sb[2 * i];
-    const float2 b00 = make_float2(b0.x, b0.y);
-    R00 = cadd(R00, cmul(b00, cr));
-    float2 m = cmul(cw00, b00);
-    if constexpr (!DIAG) {
-      const float4 b1 = sb[2 * i + 1];
-      const float2 b01 = make_float2(b0.z, b0.w), b10 = make_float2(b1.x, b1.y),
-                   b11 = make_float2(b1.z, b1.w);
-      R01 = cadd(R01, cmul(b01, cr));
-      R10 = cadd(R10, cmul(b10, cr));
-      R11 = cadd(R11, cmul(b11, cr));
-      m = cadd(m, cadd(cmul(cw01, b01), cadd(cmul(cw10, b10), cmul(cw11, b11))));
+    const dcx cr = dcx{(double)(nre * inv), (double)(y * inv)};   // conj(1 / (i G - Lambda))
+    dcx m = {0.0, 0.0};
+#pragma unroll
+    for (int a = 0; a < NB; ++a) {
+      const dcx b = sb[NB * i + a];
+      R[a] = dmac(R[a], b, cr);
+      m = dmac(m, cw[a], b);
     }
-    const float2 t = cmul(cmul(cr, cr), m);
-    Tn = cadd(Tn, t);
-    En = cadd(En, make_float2(G * t.y, -G * t.x));                // conj(i G) t
+    Tn = dmac(Tn, dmul(cr, cr), m);
   }
-  float* rv = red + 12 * tid;
-  rv[0] = R00.x; rv[1] = R00.y; rv[2] = R01.x; rv[3] = R01.y; rv[4] = R10.x; rv[5] = R10.y;
-  rv[6] = R11.x; rv[7] = R11.y; rv[8] = Tn.x; rv[9] = Tn.y; rv[10] = En.x; rv[11] = En.y;
+  double* rv = red + 2 * kPoleSums * tid;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    rv[2 * a] = R[a].x;
+    rv[2 * a + 1] = R[a].y;
+  }
+  rv[8] = Tn.x;
+  rv[9] = Tn.y;
   __syncthreads();
   if (sub == 0 && n < N) {
-    float s[12];
+    double sv[2 * kPoleSums];
 #pragma unroll
-    for (int c = 0; c < 12; ++c) s[c] = 0.f;
+    for (int c = 0; c < 2 * kPoleSums; ++c) sv[c] = 0.0;
     for (int q = 0; q < sub_n; ++q) {
-      const float* o = red + 12 * (q * npp + n);
+      const double* o = red + 2 * kPoleSums * (q * npp + n);
 #pragma unroll
-      for (int c = 0; c < 12; ++c) s[c] += o[c];
+      for (int c = 0; c < 2 * kPoleSums; ++c) sv[c] += o[c];
     }
-    float2* out = part + 6 * (((size_t)h * gridDim.x + lc) * N + n);
+    dcx* out = part + kPoleSums * (((size_t)h * gridDim.x + lc) * N + n);
 #pragma unroll
-    for (int c = 0; c < 6; ++c) out[c] = make_float2(s[2 * c], s[2 * c + 1]);
+    for (int c = 0; c < kPoleSums; ++c) out[c] = dcx{sv[2 * c], sv[2 * c + 1]};
   }
 }
 
-constexpr int kFinalWaves = 16;   // waves per block of the final combine
+constexpr int kFinalWaves = 8;   // waves per block of the final combine
 
-// Per channel: sums the chunk partials, adds the z = -1 terms, writes the
-// parameter gradients.  With Q tied to P, grad(P) includes the Q path.
-// Each of the block's nw <= 16 waves (one per chunk up to 16) sums every nw-th
+// Per channel: sums the chunk partials (fp64), adds the z = -1 terms, writes
+// the parameter gradients.  With Q tied to P, grad(P) includes the Q path.
+// Each of the block's nw <= 8 waves (one per chunk up to 8) sums every nw-th
 // frequency chunk for 64 poles at a time (lane = pole); the partial sums meet
 // in LDS in a fixed order, so the result does not depend on timing.
+//   dC = conj(B) R00 + conj(P) R01,  dB = conj(C) R00 + Q R10,
+//   dP = conj(C) R01 + Q R11,  dQ = B conj(R10) + P conj(R11),  dLambda = T,
+// plus the z = -1 terms through K-hat(-1) = (dt/2) sum_n C_n B_n.
+// dt: the bilinear kernel (and its z = -1 limit) depends on dt only through
+// dt Lambda, dt P Q^* and dt B, so scaling those three by (1 + eps) is the
+// same as scaling dt:
+//   dt dloss/ddt = Re sum_n [conj(dLambda_n) Lambda_n + conj(dB_n) B_n
+//                            + conj(dP_n) P_n]   (dP through P only).
+// The terms are the gradients themselves, formed and summed in fp64; the
+// equal frequency-domain form, a sum over l of conj(g) conj(r)^2 m, cancels
+// heavily for small dt and would lose several digits in fp32.
 template <bool DIAG>
 __global__ __launch_bounds__(64 * kFinalWaves) void kgen_bwd_final_kernel(
-    ParamPtrs pp, const float2* __restrict__ part, const float2* __restrict__ ghat,
+    ParamPtrs pp, const dcx* __restrict__ part, const float2* __restrict__ ghat,
     float2* __restrict__ dlam, float2* __restrict__ dP, float2* __restrict__ dQ,
     float2* __restrict__ dB, float2* __restrict__ dC, float* __restrict__ ddt, int N, int L,
     int nchunks) {
-  __shared__ float2 acc[kFinalWaves][6][64];
+  __shared__ dcx acc[kFinalWaves][kPoleSums][64];
   const int h = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int nw = blockDim.x >> 6;
-  const float dt = pp.dt[h], half = 0.5f * dt;
-  const float2 gn = ghat[(size_t)h * L + L / 2];
-  float dsum = 0.f;
+  const double dt = (double)pp.dt[h], half = 0.5 * dt;
+  const dcx gn = dc(ghat[(size_t)h * L + L / 2]);
+  auto f2 = [](dcx a) { return make_float2((float)a.x, (float)a.y); };
+  double dsum = 0.0;
   for (int n0 = 0; n0 < N; n0 += 64) {              // uniform over the block
     const int n = n0 + lane;
-    float2 s[6];
+    dcx sv[kPoleSums];
 #pragma unroll
-    for (int c = 0; c < 6; ++c) s[c] = make_float2(0.f, 0.f);
+    for (int c = 0; c < kPoleSums; ++c) sv[c] = dcx{0.0, 0.0};
     if (n < N) {
 #pragma unroll 4
       for (int lc = wave; lc < nchunks; lc += nw) {
-        const float2* o = part + 6 * (((size_t)h * nchunks + lc) * N + n);
+        const dcx* o = part + kPoleSums * (((size_t)h * nchunks + lc) * N + n);
 #pragma unroll
-        for (int c = 0; c < 6; ++c) s[c] = cadd(s[c], o[c]);
+        for (int c = 0; c < kPoleSums; ++c) sv[c] = dadd(sv[c], o[c]);
       }
     }
 #pragma unroll
-    for (int c = 0; c < 6; ++c) acc[wave][c][lane] = s[c];
+    for (int c = 0; c < kPoleSums; ++c) acc[wave][c][lane] = sv[c];
     __syncthreads();
     if (wave == 0 && n < N) {
 #pragma unroll
-      for (int c = 0; c < 6; ++c) {
-        s[c] = acc[0][c][lane];
+      for (int c = 0; c < kPoleSums; ++c) {
+        sv[c] = acc[0][c][lane];
 #pragma unroll
         for (int w = 1; w < kFinalWaves; ++w)
-          if (w < nw) s[c] = cadd(s[c], acc[w][c][lane]);
+          if (w < nw) sv[c] = dadd(sv[c], acc[w][c][lane]);
       }
       const size_t idx = (size_t)h * N + n;
-      const float2 b = pp.B[idx], c = pp.C[idx];
-      float2 gC = cadd(cmul(cconj(b), s[0]), cmul(cconj(make_float2(half * b.x, half * b.y)), gn));
-      float2 gB = cadd(cmul(cconj(c), s[0]), cmul(cconj(make_float2(half * c.x, half * c.y)), gn));
+      const dcx b = dc(pp.B[idx]), c = dc(pp.C[idx]), lam = dc(pp.lam[idx]);
+      dcx gC = dadd(dmul(dconj(b), sv[0]), dmul(dconj(dcx{half * b.x, half * b.y}), gn));
+      dcx gB = dadd(dmul(dconj(c), sv[0]), dmul(dconj(dcx{half * c.x, half * c.y}), gn));
+      double sd = sv[4].x * lam.x + sv[4].y * lam.y;
       if constexpr (!DIAG) {
-        const float2 pv = pp.P[idx], qv = pp.Q ? pp.Q[idx] : pv;
-        gC = cadd(gC, cmul(cconj(pv), s[1]));
-        gB = cadd(gB, cmul(qv, s[2]));
-        float2 gP = cadd(cmul(cconj(c), s[1]), cmul(qv, s[3]));
-        const float2 gQ = cadd(cmul(b, cconj(s[2])), cmul(pv, cconj(s[3])));
+        const dcx pv = dc(pp.P[idx]), qv = pp.Q ? dc(pp.Q[idx]) : pv;
+        gC = dadd(gC, dmul(dconj(pv), sv[1]));
+        gB = dadd(gB, dmul(qv, sv[2]));
+        dcx gP = dadd(dmul(dconj(c), sv[1]), dmul(qv, sv[3]));
+        sd += gP.x * pv.x + gP.y * pv.y;
+        const dcx gQ = dadd(dmul(b, dconj(sv[2])), dmul(pv, dconj(sv[3])));
         if (pp.Q) {
-          if (dQ) dQ[idx] = gQ;
+          if (dQ) dQ[idx] = f2(gQ);
         } else {
-          gP = cadd(gP, gQ);
+          gP = dadd(gP, gQ);
         }
-        if (dP) dP[idx] = gP;
+        if (dP) dP[idx] = f2(gP);
       }
-      if (dC) dC[idx] = gC;
-      if (dB) dB[idx] = gB;
-      if (dlam) dlam[idx] = s[4];
-      // dt: Re(E)/dt, and the z = -1 limit (dt/2) C B
-      dsum += s[5].x / dt + (0.5f * cmul(c, b).x * gn.x + 0.5f * cmul(c, b).y * gn.y);
+      sd += gB.x * b.x + gB.y * b.y;
+      if (dC) dC[idx] = f2(gC);
+      if (dB) dB[idx] = f2(gB);
+      if (dlam) dlam[idx] = f2(sv[4]);
+      dsum += sd;
     }
     __syncthreads();
   }
   if (wave == 0) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) dsum += __shfl_xor(dsum, off);
-    if (lane == 0 && ddt) ddt[h] = dsum;
+    if (lane == 0 && ddt) ddt[h] = (float)(dsum / dt);
   }
 }
 
@@ -855,24 +869,17 @@ hipError_t launch_kernel_gen_bwd(const s4dplr_plan* p, const float* lam, const f
   }
   const float* tanT = at<const float>(ws, p->off_tan);
   const float2* ghat = at<const float2>(ws, p->off_bghat);
-  float4* beta = at<float4>(ws, p->off_bbeta);
-  constexpr int F = 2;
-  const dim3 cgrid((p->L + F * kCauchyThreads - 1) / (F * kCauchyThreads), p->H);
-  if (diag)
-    kgen_bwd_coef_kernel<F, true><<<cgrid, kCauchyThreads, 0, s>>>(pp, tanT, ghat, beta, p->N,
-                                                                   p->NP, p->L);
-  else
-    kgen_bwd_coef_kernel<F, false><<<cgrid, kCauchyThreads, 0, s>>>(pp, tanT, ghat, beta, p->N,
-                                                                    p->NP, p->L);
   int log2npp = 0;
   while ((1 << log2npp) < p->N) ++log2npp;
   const int nchunks = (p->L + kBwdChunk - 1) / kBwdChunk;
-  float2* part = at<float2>(ws, p->off_bpart);
-  const dim3 pgrid(nchunks, p->H);
+  dcx* part = at<dcx>(ws, p->off_bpart);
+  const dim3 grid(nchunks, p->H);
   if (diag)
-    kgen_bwd_pole_kernel<true><<<pgrid, 256, 0, s>>>(pp, tanT, beta, part, p->N, p->L, log2npp);
+    kgen_bwd_chunk_kernel<true><<<grid, 256, 0, s>>>(pp, tanT, ghat, part, p->N, p->NP, p->L,
+                                                     log2npp);
   else
-    kgen_bwd_pole_kernel<false><<<pgrid, 256, 0, s>>>(pp, tanT, beta, part, p->N, p->L, log2npp);
+    kgen_bwd_chunk_kernel<false><<<grid, 256, 0, s>>>(pp, tanT, ghat, part, p->N, p->NP, p->L,
+                                                      log2npp);
   auto c2 = [](float* q) { return reinterpret_cast<float2*>(q); };
   const int fthreads = 64 * (nchunks < kFinalWaves ? nchunks : kFinalWaves);
   if (diag)

@@ -39,9 +39,8 @@ struct s4dplr_plan {
   size_t off_rct;    // recurrent view, chunked: [H][C][N] float2 rows C A-bar^tau, tau < C
   // Backward pass:
   size_t off_bghat;  // [H][L] float2: FFT_L(dK) / L
-  size_t off_bbeta;  // [H][L] x 2 float4: conj(dKhat/dk_ab) * Ghat per frequency
   size_t off_bpart;  // partial sums: correlation spectra [ceil(B/kCorrRows) + 1][H][L+1] float2,
-                     // or per-pole sums [H][ceil(L/kBwdChunk)][N] x 6 float2
+                     // or per-pole sums [H][ceil(L/kBwdChunk)][N] x 5 fp64 complex
   size_t off_bz;     // block (S4DPLR_BLOCK): [batch][H][L] float normalized input
   size_t off_bs;     // block (S4DPLR_BLOCK): [batch][H][L] float layer output
   size_t off_bw;     // block (S4DPLR_BLOCK): [2][2H][H] bf16: W split into hi and lo parts
