@@ -85,6 +85,22 @@ typedef enum s4dplr_status {
 #define S4DPLR_ZOH 2u
 /* Plan flag: reserve the workspace buffers of s4dplr_block_forward. */
 #define S4DPLR_BLOCK 4u
+/* Plan flags, bits 8..11: rank r of the low-rank term ("S4" wiki, "Structured
+ * Transition Matrix": A = Lambda - P Q^* with low-rank P, Q, the correction
+ * handled by the Woodbury identity), 1 <= r <= 4; a zero field means r = 1.
+ * With r > 1, P and Q are [H][r][N] interleaved complex (the r columns of the
+ * N x r factors one after another) and the generating function is
+ *     Khat(z) = 2/(1+z) * (k00 - k01 (I_r + k11)^{-1} k10),
+ * k00 = C R B, k01[j] = C R P_j, k10[i] = Q_i^* R B, k11[i][j] = Q_i^* R P_j,
+ * R = (g(z) - Lambda)^{-1}: (r+1)^2 Cauchy sums and an r x r solve per
+ * frequency.  Rank r > 1 is supported by s4dplr_kernel_gen,
+ * s4dplr_generating_function, s4dplr_forward, s4dplr_forward_noalloc and
+ * s4dplr_block_forward; s4dplr_recurrent_prepare and s4dplr_kernel_gen_bwd
+ * return ERR_UNSUPPORTED for it, and it cannot be combined with
+ * S4DPLR_DIAGONAL (ERR_UNSUPPORTED at plan creation). */
+#define S4DPLR_RANK_SHIFT 8
+#define S4DPLR_RANK_MASK (0xFu << S4DPLR_RANK_SHIFT)
+#define S4DPLR_RANK(r) ((unsigned)(r) << S4DPLR_RANK_SHIFT)
 
 typedef struct s4dplr_plan s4dplr_plan;
 
@@ -101,7 +117,8 @@ int s4dplr_last_hip_error(void);
  * Create a plan for H channels of N poles, sequence length L and `batch`
  * input rows per channel.  Host-only: allocates host memory for the plan and
  * its fp64-derived tables, touches no device.  *out receives the plan, or NULL
- * on error.  Errors: ERR_NULL (out), ERR_SHAPE (sizes), ERR_UNSUPPORTED (flags).
+ * on error.  Errors: ERR_NULL (out), ERR_SHAPE (sizes), ERR_UNSUPPORTED (flags,
+ * including a rank field above 4 or a rank above 1 with S4DPLR_DIAGONAL).
  * The plan is immutable after creation and may be used concurrently from
  * several threads and streams, each with its own workspace.
  */

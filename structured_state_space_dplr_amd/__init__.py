@@ -37,6 +37,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libs4dplr.s
 DIAGONAL = 1
 ZOH = 2
 BLOCK = 4
+RANK_SHIFT = 8
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -144,7 +145,8 @@ def check_preconditions(where: str = "check_preconditions", lam=None, dt=None, *
         if bool(bad.any()):
             idx = tuple(int(i) for i in bad.nonzero()[0])
             raise S4DPLRPreconditionError(
-                where, f"Re(lam) must be < 0 (stable pole); lam{list(idx)} has Re = {float(re[idx]):g}")
+                where, f"Re(lam) must be < 0 (stable pole); lam{list(idx)} has Re = "
+                       f"{float(re[idx]):g}")
     if dt is not None:
         d = _host(dt)
         bad = d <= 0
@@ -219,8 +221,9 @@ def kernel_gen(plan: "Plan | int", lam, P, Q, B, C, dt, K, ws, stream=None) -> N
     _validate("kernel_gen", lam=lam, dt=dt, P=P, Q=Q, B=B, C=C)
     p, (H, N, L, _) = _dims(plan)
     cplx = (H, N, 2)
+    lr = _lowrank_shape(plan)
     _check(_lib.s4dplr_kernel_gen(
-        p, _ptr(lam, "lam", cplx), _ptr(P, "P", cplx), _ptr(Q, "Q", cplx), _ptr(B, "B", cplx),
+        p, _ptr(lam, "lam", cplx), _ptr(P, "P", lr), _ptr(Q, "Q", lr), _ptr(B, "B", cplx),
         _ptr(C, "C", cplx), _ptr(dt, "dt", (H,)), _ptr(K, "K", (H, L)), _ws_ptr(ws),
         _stream(stream)), "kernel_gen")
 
@@ -230,8 +233,9 @@ def generating_function(plan: "Plan | int", lam, P, Q, B, C, dt, khat, ws, strea
     _validate("generating_function", lam=lam, dt=dt, P=P, Q=Q, B=B, C=C)
     p, (H, N, L, _) = _dims(plan)
     cplx = (H, N, 2)
+    lr = _lowrank_shape(plan)
     _check(_lib.s4dplr_generating_function(
-        p, _ptr(lam, "lam", cplx), _ptr(P, "P", cplx), _ptr(Q, "Q", cplx), _ptr(B, "B", cplx),
+        p, _ptr(lam, "lam", cplx), _ptr(P, "P", lr), _ptr(Q, "Q", lr), _ptr(B, "B", cplx),
         _ptr(C, "C", cplx), _ptr(dt, "dt", (H,)), _ptr(khat, "khat", (H, L, 2)), _ws_ptr(ws),
         _stream(stream)), "generating_function")
 
@@ -248,8 +252,9 @@ def forward(plan: "Plan | int", lam, P, Q, B, C, dt, D, u, K, y, ws, stream=None
     _validate("forward", lam=lam, dt=dt, P=P, Q=Q, B=B, C=C, D=D, u=u)
     p, (H, N, L, batch) = _dims(plan)
     cplx = (H, N, 2)
+    lr = _lowrank_shape(plan)
     _check(_lib.s4dplr_forward(
-        p, _ptr(lam, "lam", cplx), _ptr(P, "P", cplx), _ptr(Q, "Q", cplx), _ptr(B, "B", cplx),
+        p, _ptr(lam, "lam", cplx), _ptr(P, "P", lr), _ptr(Q, "Q", lr), _ptr(B, "B", cplx),
         _ptr(C, "C", cplx), _ptr(dt, "dt", (H,)), _ptr(D, "D", (H,)),
         _ptr(u, "u", (batch, H, L)), _ptr(K, "K", (H, L)), _ptr(y, "y", (batch, H, L)),
         _ws_ptr(ws), _stream(stream)), "forward")
@@ -260,8 +265,9 @@ def forward_noalloc(plan: "Plan | int", lam, P, Q, B, C, dt, D, u, K, y, stream=
     _validate("forward_noalloc", lam=lam, dt=dt, P=P, Q=Q, B=B, C=C, D=D, u=u)
     p, (H, N, L, batch) = _dims(plan)
     cplx = (H, N, 2)
+    lr = _lowrank_shape(plan)
     _check(_lib.s4dplr_forward_noalloc(
-        p, _ptr(lam, "lam", cplx), _ptr(P, "P", cplx), _ptr(Q, "Q", cplx), _ptr(B, "B", cplx),
+        p, _ptr(lam, "lam", cplx), _ptr(P, "P", lr), _ptr(Q, "Q", lr), _ptr(B, "B", cplx),
         _ptr(C, "C", cplx), _ptr(dt, "dt", (H,)), _ptr(D, "D", (H,)),
         _ptr(u, "u", (batch, H, L)), _ptr(K, "K", (H, L)), _ptr(y, "y", (batch, H, L)),
         _stream(stream)), "forward_noalloc")
@@ -279,8 +285,9 @@ def recurrent_prepare(plan: "Plan | int", lam, P, Q, B, C, dt, ws, stream=None) 
     _validate("recurrent_prepare", lam=lam, dt=dt, P=P, Q=Q, B=B, C=C)
     p, (H, N, L, _) = _dims(plan)
     cplx = (H, N, 2)
+    lr = _lowrank_shape(plan)
     _check(_lib.s4dplr_recurrent_prepare(
-        p, _ptr(lam, "lam", cplx), _ptr(P, "P", cplx), _ptr(Q, "Q", cplx), _ptr(B, "B", cplx),
+        p, _ptr(lam, "lam", cplx), _ptr(P, "P", lr), _ptr(Q, "Q", lr), _ptr(B, "B", cplx),
         _ptr(C, "C", cplx), _ptr(dt, "dt", (H,)), _ws_ptr(ws), _stream(stream)),
         "recurrent_prepare")
 
@@ -312,10 +319,11 @@ def kernel_gen_bwd(plan: "Plan | int", lam, P, Q, B, C, dt, dK, dlam, dP, dQ, dB
     _validate("kernel_gen_bwd", lam=lam, dt=dt, P=P, Q=Q, B=B, C=C, dK=dK)
     p, (H, N, L, _) = _dims(plan)
     cplx = (H, N, 2)
+    lr = _lowrank_shape(plan)
     _check(_lib.s4dplr_kernel_gen_bwd(
-        p, _ptr(lam, "lam", cplx), _ptr(P, "P", cplx), _ptr(Q, "Q", cplx), _ptr(B, "B", cplx),
+        p, _ptr(lam, "lam", cplx), _ptr(P, "P", lr), _ptr(Q, "Q", lr), _ptr(B, "B", cplx),
         _ptr(C, "C", cplx), _ptr(dt, "dt", (H,)), _ptr(dK, "dK", (H, L)),
-        _ptr(dlam, "dlam", cplx), _ptr(dP, "dP", cplx), _ptr(dQ, "dQ", cplx),
+        _ptr(dlam, "dlam", cplx), _ptr(dP, "dP", lr), _ptr(dQ, "dQ", lr),
         _ptr(dB, "dB", cplx), _ptr(dC, "dC", cplx), _ptr(ddt, "ddt", (H,)), _ws_ptr(ws),
         _stream(stream)), "kernel_gen_bwd")
 
@@ -326,9 +334,10 @@ def block_forward(plan: "Plan | int", x, gamma, beta, lam, P, Q, B, C, dt, D, W,
               D=D, W=W, bias=bias)
     p, (H, N, L, batch) = _dims(plan)
     cplx = (H, N, 2)
+    lr = _lowrank_shape(plan)
     _check(_lib.s4dplr_block_forward(
         p, _ptr(x, "x", (batch, H, L)), _ptr(gamma, "gamma", (H,)), _ptr(beta, "beta", (H,)),
-        _ptr(lam, "lam", cplx), _ptr(P, "P", cplx), _ptr(Q, "Q", cplx), _ptr(B, "B", cplx),
+        _ptr(lam, "lam", cplx), _ptr(P, "P", lr), _ptr(Q, "Q", lr), _ptr(B, "B", cplx),
         _ptr(C, "C", cplx), _ptr(dt, "dt", (H,)), _ptr(D, "D", (H,)), _ptr(W, "W", (2 * H, H)),
         _ptr(bias, "bias", (2 * H,)), _ptr(out, "out", (batch, H, L)), _ws_ptr(ws),
         _stream(stream)), "block_forward")
@@ -340,15 +349,23 @@ def _dims(plan):
     raise TypeError("pass a Plan (its sizes are needed to check tensor shapes)")
 
 
+def _lowrank_shape(plan):
+    """Shape of P and Q: [H, N, 2] at rank 1, [H, r, N, 2] at rank r > 1."""
+    if plan.rank == 1:
+        return (plan.H, plan.N, 2)
+    return (plan.H, plan.rank, plan.N, 2)
+
+
 class Plan:
     """Owns a plan handle and (optionally) a workspace tensor on one device."""
 
     def __init__(self, H: int, N: int, L: int, batch: int, diagonal: bool = False,
-                 device=None, zoh: bool = False, block: bool = False):
+                 device=None, zoh: bool = False, block: bool = False, rank: int = 1):
         self.H, self.N, self.L, self.batch = H, N, L, batch
-        self.diagonal, self.zoh, self.block = diagonal, zoh, block
+        self.diagonal, self.zoh, self.block, self.rank = diagonal, zoh, block, rank
         self.handle = plan_create(H, N, L, batch, (DIAGONAL if diagonal else 0)
-                                  | (ZOH if zoh else 0) | (BLOCK if block else 0))
+                                  | (ZOH if zoh else 0) | (BLOCK if block else 0)
+                                  | ((rank << RANK_SHIFT) if rank != 1 else 0))
         self.workspace_bytes = plan_workspace_bytes(self.handle)
         self.device = torch.device("cuda" if device is None else device)
         self._ws_store = None

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libs4dplr.so")
 SOURCES = ["kernels.hip", "big.hip", "recurrent.hip", "backward.hip", "vandermonde.hip", "block.hip",
-           "noalloc.hip", "api.cpp"]
+           "noalloc.hip", "rank.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

@@ -113,8 +113,13 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
                                  unsigned flags) {
   if (!out) return S4DPLR_ERR_NULL;
   *out = nullptr;
-  if (flags & ~(S4DPLR_DIAGONAL | S4DPLR_ZOH | S4DPLR_BLOCK)) return S4DPLR_ERR_UNSUPPORTED;
+  if (flags & ~(S4DPLR_DIAGONAL | S4DPLR_ZOH | S4DPLR_BLOCK | S4DPLR_RANK_MASK))
+    return S4DPLR_ERR_UNSUPPORTED;
   if ((flags & S4DPLR_ZOH) && !(flags & S4DPLR_DIAGONAL)) return S4DPLR_ERR_UNSUPPORTED;
+  const unsigned rank_field = (flags & S4DPLR_RANK_MASK) >> S4DPLR_RANK_SHIFT;
+  const int rank = rank_field ? (int)rank_field : 1;
+  if (rank > 4) return S4DPLR_ERR_UNSUPPORTED;
+  if (rank > 1 && (flags & S4DPLR_DIAGONAL)) return S4DPLR_ERR_UNSUPPORTED;
   const bool zoh = (flags & S4DPLR_ZOH) != 0;
   if (H < 1 || batch < 1 || N < 1 || N > 256) return S4DPLR_ERR_SHAPE;
   if (!is_pow2(L) || L < 2 || L > 65536) return S4DPLR_ERR_SHAPE;
@@ -129,12 +134,15 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
   p->L = L;
   p->log2L = log2L;
   p->batch = batch;
+  p->rank = rank;
   p->flags = flags;
 
   // Table region.
   size_t off = 0;
   p->off_tan = off;
   off = align_up(off + sizeof(float) * L);
+  p->off_tan2 = off;
+  if (rank > 1) off = align_up(off + 2 * sizeof(float) * L);
   p->off_cs = off;
   off = align_up(off + 2 * sizeof(float) * (L + 1));
   const bool lds = log2L <= S4DPLR_LDS_MAX_LOG2L;
@@ -216,6 +224,17 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
   float* tanT = reinterpret_cast<float*>(p->tables.data() + p->off_tan);
   for (int l = 0; l < L; ++l)
     tanT[l] = (2 * l == L) ? 0.0f : (float)std::tan(M_PI * (double)l / (double)L);
+  if (rank > 1) {
+    // the nodes as two floats: the rank-r Woodbury solve amplifies the
+    // rounding of a single-float node near a sharp pole
+    float* t2 = reinterpret_cast<float*>(p->tables.data() + p->off_tan2);
+    for (int l = 0; l < L; ++l) {
+      const double t = (2 * l == L) ? 0.0 : std::tan(M_PI * (double)l / (double)L);
+      const float hi = (float)t;
+      t2[2 * l + 0] = hi;
+      t2[2 * l + 1] = (float)(t - (double)hi);
+    }
+  }
   float* cs = reinterpret_cast<float*>(p->tables.data() + p->off_cs);
   for (int j = 0; j <= L; ++j) {
     cs[2 * j + 0] = (float)std::cos(M_PI * (double)j / (double)L);
@@ -298,9 +317,10 @@ s4dplr_status s4dplr_generating_function(const s4dplr_plan* p, const float* lamb
   if (p->flags & S4DPLR_ZOH) return S4DPLR_ERR_UNSUPPORTED;
   const size_t kb = 2 * sizeof(float) * (size_t)p->H * p->L;
   const size_t cb = 2 * sizeof(float) * (size_t)p->H * p->N;
+  const size_t rb = cb * (size_t)p->rank;   // P and Q: [H][rank][N] complex
   const size_t hb = sizeof(float) * (size_t)p->H;
   if (overlaps(khat, kb, ws, p->total) || overlaps(khat, kb, lambda, cb) ||
-      overlaps(khat, kb, P, cb) || overlaps(khat, kb, Q, cb) || overlaps(khat, kb, B, cb) ||
+      overlaps(khat, kb, P, rb) || overlaps(khat, kb, Q, rb) || overlaps(khat, kb, B, cb) ||
       overlaps(khat, kb, C, cb) || overlaps(khat, kb, dt, hb))
     return S4DPLR_ERR_ALIAS;
   hipError_t e = s4::launch_generating_function(p, lambda, P, Q, B, C, dt, khat,
@@ -391,6 +411,7 @@ s4dplr_status s4dplr_recurrent_prepare(const s4dplr_plan* p, const float* lambda
   if (!valid_plan(p)) return S4DPLR_ERR_NULL;
   if (s4dplr_status st = check_params(p, lambda, P, B, C, dt)) return st;
   if (s4dplr_status st = check_ws(ws)) return st;
+  if (p->rank > 1) return S4DPLR_ERR_UNSUPPORTED;   // the O(N) step is rank 1
   hipError_t e = s4::launch_recurrent_prepare(p, lambda, P, Q, B, C, dt,
                                               static_cast<unsigned char*>(ws), stream);
   if (e != hipSuccess) return hip_fail(e);
@@ -459,6 +480,7 @@ s4dplr_status s4dplr_kernel_gen_bwd(const s4dplr_plan* p, const float* lambda, c
   if (s4dplr_status st = check_params(p, lambda, P, B, C, dt)) return st;
   if (!dK) return S4DPLR_ERR_NULL;
   if (s4dplr_status st = check_ws(ws)) return st;
+  if (p->rank > 1) return S4DPLR_ERR_UNSUPPORTED;   // gradients are built for rank 1
   const bool zoh = (p->flags & S4DPLR_ZOH) != 0;
   const bool diag = (p->flags & S4DPLR_DIAGONAL) != 0;
   if (diag) dP = dQ = nullptr;
@@ -504,8 +526,9 @@ s4dplr_status s4dplr_block_forward(const s4dplr_plan* p, const float* x, const f
   const size_t cb = 2 * sizeof(float) * (size_t)p->H * p->N;
   const size_t wb = 2 * sizeof(float) * (size_t)p->H * p->H;
   if (out != x && overlaps(out, ub, x, ub)) return S4DPLR_ERR_ALIAS;
+  const size_t rb = cb * (size_t)p->rank;   // P and Q: [H][rank][N] complex
   const void* ins[] = {gamma, beta, lambda, P, Q, B, C, dt, D, W, bias};
-  const size_t inb[] = {hb, hb, cb, cb, cb, cb, cb, hb, hb, wb, 2 * hb};
+  const size_t inb[] = {hb, hb, cb, rb, rb, cb, cb, hb, hb, wb, 2 * hb};
   for (int i = 0; i < 11; ++i)
     if (overlaps(out, ub, ins[i], inb[i])) return S4DPLR_ERR_ALIAS;
   if (overlaps(out, ub, ws, p->total) || overlaps(x, ub, ws, p->total)) return S4DPLR_ERR_ALIAS;

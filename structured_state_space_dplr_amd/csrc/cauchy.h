@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include "device_fft.h"
+#include "internal.h"
 
 namespace s4 {
 
@@ -32,6 +33,11 @@ struct ParamPtrs {
 };
 
 constexpr int kRec = 5;   // float4 per pole record
+
+// Generating function for plans of rank 2 .. 4 (rank.hip): khat [H][L] in
+// natural order (perm_m1 = 0) or the four-step permuted order (perm_m1 = M1).
+hipError_t launch_cauchy_rank(const s4dplr_plan* p, const ParamPtrs& pp, float2* khat,
+                              int perm_m1, unsigned char* ws, hipStream_t s);
 
 // Builds the records of channel h with threads [0, nthr); returns this
 // thread's partial sum of w00 = C B over its poles.

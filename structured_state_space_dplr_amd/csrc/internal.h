@@ -15,9 +15,11 @@
 
 struct s4dplr_plan {
   int H, N, NP, L, log2L, batch;   // NP: N rounded up to the Cauchy loop unroll (4)
+  int rank;                        // columns of the low-rank factors P, Q (1 .. 4)
   unsigned flags;
   // Workspace layout, byte offsets from the 256-byte aligned base.
   size_t off_tan;    // [L] float: tan(pi l / L), 0 at l = L/2
+  size_t off_tan2;   // rank > 1: [L] float2 (hi, lo): tan(pi l / L) = hi + lo to ~48 bits
   size_t off_cs;     // [L+1] float2: (cos(pi j / L), sin(pi j / L))
   size_t off_twL;    // FFT twiddles for transforms of L points
   size_t off_twH;    // FFT twiddles for transforms of L/2 points

@@ -1008,8 +1008,10 @@ hipError_t launch_generating_function(const s4dplr_plan* p, const float* lam, co
                                       const float* Q, const float* B, const float* C,
                                       const float* dt, float* khat, unsigned char* ws,
                                       hipStream_t s) {
-  return launch_cauchy_to(p, param_ptrs(lam, P, Q, B, C, dt), reinterpret_cast<float2*>(khat), 0,
-                          ws, s);
+  const ParamPtrs pp = param_ptrs(lam, P, Q, B, C, dt);
+  float2* out = reinterpret_cast<float2*>(khat);
+  if (p->rank > 1) return launch_cauchy_rank(p, pp, out, 0, ws, s);
+  return launch_cauchy_to(p, pp, out, 0, ws, s);
 }
 
 template <int LOG2L>
@@ -1112,6 +1114,15 @@ hipError_t launch_kernel_gen(const s4dplr_plan* p, const float* lam, const float
     return launch_spectrum_from_time(p, K, D, ws, s, 0);
   }
   const ParamPtrs pp = param_ptrs(lam, P, Q, B, C, dt);
+  if (p->rank > 1) {
+    // rank r: the (r+1)^2 Cauchy sums and the r x r Woodbury solve, then the
+    // kernel spectrum from K-hat (every length, the block-level transform up
+    // to 2^14)
+    hipError_t e = launch_cauchy_rank(p, pp, at<float2>(ws, p->off_khat),
+                                      lds_path(p) ? 0 : p->L / 256, ws, s);
+    if (e != hipSuccess) return e;
+    return launch_kspec(p, nullptr, D, Kout, ws, s, 0);
+  }
   if (fused_path(p)) {
     S4_DISPATCH_LOG2L(kgen_launch, p, pp, D, nullptr, Kout, ws, s, 0);
     return hipGetLastError();

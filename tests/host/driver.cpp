@@ -112,6 +112,45 @@ int main() {
           S4DPLR_OK);
     s4dplr_plan_destroy(big);
   }
+  {
+    // rank-r plans: the forward-side entry points accept them, the recurrent
+    // view and the parameter gradients reject them; invalid rank fields
+    const uintptr_t base = uintptr_t(1) << 40, gap = uintptr_t(1) << 34;
+    const float* f = reinterpret_cast<const float*>(base);
+    float* u = reinterpret_cast<float*>(base + gap);
+    float* y = reinterpret_cast<float*>(base + 2 * gap);
+    float* K = reinterpret_cast<float*>(base + 3 * gap);
+    for (int L : {64, 4096, 65536})
+      for (int r : {2, 3, 4}) {
+        s4dplr_plan* q = nullptr;
+        CHECK(s4dplr_plan_create(&q, 3, 16, L, 2, S4DPLR_RANK(r) | S4DPLR_BLOCK) == S4DPLR_OK);
+        size_t bytes = 0;
+        CHECK(s4dplr_plan_workspace_bytes(q, &bytes) == S4DPLR_OK);
+        std::vector<unsigned char> store(bytes + 256);
+        void* ws = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(store.data()) + 255) & ~uintptr_t(255));
+        CHECK(s4dplr_plan_init(q, ws, nullptr) == S4DPLR_OK);
+        CHECK(s4dplr_kernel_gen(q, f, f, nullptr, f, f, f, K, ws, nullptr) == S4DPLR_OK);
+        CHECK(s4dplr_forward(q, f, f, f, f, f, f, nullptr, u, K, y, ws, nullptr) == S4DPLR_OK);
+        CHECK(s4dplr_forward_noalloc(q, f, f, nullptr, f, f, f, nullptr, u, K, y, nullptr) ==
+              S4DPLR_OK);
+        CHECK(s4dplr_generating_function(q, f, f, nullptr, f, f, f, K, ws, nullptr) == S4DPLR_OK);
+        CHECK(s4dplr_recurrent_prepare(q, f, f, nullptr, f, f, f, ws, nullptr) ==
+              S4DPLR_ERR_UNSUPPORTED);
+        float* outs = reinterpret_cast<float*>(base + 6 * gap);
+        CHECK(s4dplr_kernel_gen_bwd(q, f, f, nullptr, f, f, f, K, outs, nullptr, nullptr, nullptr,
+                                    nullptr, nullptr, ws, nullptr) == S4DPLR_ERR_UNSUPPORTED);
+        float* xo = reinterpret_cast<float*>(base + 7 * gap);
+        CHECK(s4dplr_block_forward(q, xo, f, f, f, f, nullptr, f, f, f, nullptr, f, f, xo, ws,
+                                   nullptr) == S4DPLR_OK);
+        s4dplr_plan_destroy(q);
+      }
+    s4dplr_plan* q = nullptr;
+    CHECK(s4dplr_plan_create(&q, 3, 16, 64, 2, S4DPLR_RANK(5)) == S4DPLR_ERR_UNSUPPORTED && !q);
+    CHECK(s4dplr_plan_create(&q, 3, 16, 64, 2, S4DPLR_RANK(2) | S4DPLR_DIAGONAL) ==
+          S4DPLR_ERR_UNSUPPORTED);
+    CHECK(s4dplr_plan_create(&q, 3, 16, 64, 2, S4DPLR_RANK(1)) == S4DPLR_OK);
+    s4dplr_plan_destroy(q);
+  }
   s4dplr_plan* p = nullptr;
   CHECK(s4dplr_plan_create(&p, 1, 1, 3, 1, 0) == S4DPLR_ERR_SHAPE && !p);
   CHECK(s4dplr_plan_create(&p, 1, 1, 4, 1, 8) == S4DPLR_ERR_UNSUPPORTED);

@@ -404,3 +404,87 @@ def test_generating_function_workload(s4, name):
         # its inverse transform is the kernel the forward writes
         Kr = np.fft.ifft(ref).real
         assert _rel(np.fft.ifft(kh[h]).real, Kr) <= TOL
+
+
+# ---- rank-r low-rank term (plan flag S4DPLR_RANK(r)) --------------------------
+
+def _rank_oracle(x):
+    return o.forward(x["lam"], x["P"], x["Q"], x["B"], x["C"], x["dt"], x["D"], x["u"],
+                     method="cauchy")
+
+
+@pytest.mark.parametrize("r,L,distinct_q", [(2, 2, False), (2, 64, True), (3, 256, False),
+                                            (4, 1024, True), (2, 4096, False), (3, 16384, True),
+                                            (4, 32768, False), (2, 65536, True)])
+def test_rank_r_forward(s4, r, L, distinct_q):
+    # the (r+1)^2 Cauchy sums and the r x r solve per frequency, then every
+    # length class of the kernel spectrum and the convolution
+    import torch
+    print(f"case: rank {r} L={L} distinct_q={distinct_q}", flush=True)
+    H, N, batch = 3, 16, 2
+    x = make_generic_inputs(H=H, N=N, L=L, batch=batch, seed=700 + 10 * r + L % 97,
+                            distinct_q=distinct_q, rank=r)
+    plan = s4.Plan(H, N, L, batch, rank=r)
+    ws = plan.workspace()
+    t = {k: _dev(x[k]) for k in ("lam", "P", "Q", "B", "C", "dt", "D", "u")}
+    K = torch.empty((H, L), dtype=torch.float32, device="cuda")
+    y = torch.empty((batch, H, L), dtype=torch.float32, device="cuda")
+    s4.forward(plan, t["lam"], t["P"], t["Q"], t["B"], t["C"], t["dt"], t["D"], t["u"], K, y, ws)
+    kh = torch.empty((H, L, 2), dtype=torch.float32, device="cuda")
+    s4.generating_function(plan, t["lam"], t["P"], t["Q"], t["B"], t["C"], t["dt"], kh, ws)
+    torch.cuda.synchronize()
+    Kr, yr = _rank_oracle(x)
+    eK, ey = _rel(K.cpu().numpy(), Kr), _rel(y.cpu().numpy(), yr)
+    c = lambda a: a[..., 0].astype(np.float64) + 1j * a[..., 1]
+    kg = kh.cpu().numpy().astype(np.float64)
+    kg = kg[..., 0] + 1j * kg[..., 1]
+    ek = 0.0
+    for h in range(H):
+        Pm = c(x["P"][h]).T
+        Qm = Pm if x["Q"] is None else c(x["Q"][h]).T
+        ref = o.generating_function_lowrank(c(x["lam"][h]), Pm, Qm, c(x["B"][h]), c(x["C"][h]),
+                                            float(x["dt"][h]), L)
+        ek = max(ek, float(np.abs(kg[h] - ref).max() / np.abs(ref).max()))
+    print(f"  rel err K {eK:.2e} y {ey:.2e} K-hat {ek:.2e}", flush=True)
+    assert eK <= TOL and ey <= TOL and ek <= TOL
+    plan.close()
+
+
+def test_rank_r_zero_columns_equal_lower_rank(s4):
+    # a rank-3 plan whose third columns of P and Q are zero gives the rank-2
+    # result; with all columns zero but the first, the rank-1 path's result
+    import torch
+    H, N, L, batch = 2, 16, 512, 2
+    x3 = make_generic_inputs(H=H, N=N, L=L, batch=batch, seed=801, distinct_q=True, rank=3)
+    x3["P"][:, 2] = 0.0
+    x3["Q"][:, 2] = 0.0
+    x2 = dict(x3)
+    x2["P"] = np.ascontiguousarray(x3["P"][:, :2])
+    x2["Q"] = np.ascontiguousarray(x3["Q"][:, :2])
+    outs = []
+    for x, r in ((x3, 3), (x2, 2)):
+        plan = s4.Plan(H, N, L, batch, rank=r)
+        t = {k: _dev(x[k]) for k in ("lam", "P", "Q", "B", "C", "dt", "D", "u")}
+        y = torch.empty((batch, H, L), dtype=torch.float32, device="cuda")
+        s4.forward(plan, t["lam"], t["P"], t["Q"], t["B"], t["C"], t["dt"], t["D"], t["u"], None, y,
+                   plan.workspace())
+        torch.cuda.synchronize()
+        outs.append(y.cpu().numpy())
+        plan.close()
+    assert _rel(outs[0], outs[1].astype(np.float64)) <= TOL
+    assert _rel(outs[1], _rank_oracle(x2)[1]) <= TOL
+
+
+def test_rank_r_unsupported_entry_points(s4):
+    import torch
+    plan = s4.Plan(2, 8, 64, 1, rank=2)
+    z = lambda *s: torch.zeros(s, device="cuda")
+    with pytest.raises(s4.S4DPLRError) as ei:
+        s4.recurrent_prepare(plan, z(2, 8, 2), z(2, 2, 8, 2), None, z(2, 8, 2), z(2, 8, 2), z(2),
+                             plan.workspace())
+    assert ei.value.status == 4
+    with pytest.raises(s4.S4DPLRError) as ei:
+        s4.kernel_gen_bwd(plan, z(2, 8, 2), z(2, 2, 8, 2), None, z(2, 8, 2), z(2, 8, 2), z(2),
+                          z(2, 64), z(2, 8, 2), None, None, None, None, None, plan.workspace())
+    assert ei.value.status == 4
+    plan.close()
