@@ -120,11 +120,12 @@ def backward_counts(w):
     for the Woodbury partials (40 DPLR / 16 diagonal, as in the forward) and
     the transposed per-pole sums: the reciprocal (8), the sums R_ab (8 per
     complex multiply-add: 32 DPLR / 8 diagonal), sum_ab conj(w_ab) beta_ab
-    (32 / 8), conj(r)^2 (6), t = conj(r)^2 m (6), T += t (2), E += conj(g) t (4).
+    (32 / 8), conj(r)^2 (6), t = conj(r)^2 m (6), T += t (2).  (dt comes from
+    the per-pole gradients, not from a frequency sum.)
     """
     bhl, hl = w.batch * w.H * w.L, w.H * w.L
     q_conv = 12 * bhl + 8 * hl + 8 * w.H
-    per_term = (16 + 8 + 8 + 8 + 18) if w.diagonal else (40 + 8 + 32 + 32 + 18)
+    per_term = (16 + 8 + 8 + 8 + 14) if w.diagonal else (40 + 8 + 32 + 32 + 14)
     return q_conv, w.H * w.L * w.N * per_term
 
 
@@ -538,15 +539,21 @@ def _short_name(name: str) -> str:
     return n.split("::")[-1]
 
 
-def summarize_trace(d, label, command):
+def summarize_trace(d, label, command, by_grid=True):
     """Markdown table of per-kernel launch durations from a rocprofv3
-    --kernel-trace run (kernel_trace.csv: end minus start per dispatch)."""
+    --kernel-trace run (kernel_trace.csv: end minus start per dispatch), one
+    row per kernel and grid size (the same kernel serves launches of
+    different sizes, e.g. the four-step kernels in stage 1 and in the
+    convolution)."""
     path = _find_csv(d, "kernel_trace.csv")
     per = {}
     with open(path) as f:
         for r in csv.DictReader(f):
             dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-            per.setdefault(_short_name(r["Kernel_Name"]), []).append(dur)
+            key = _short_name(r["Kernel_Name"])
+            if by_grid and "Grid_Size_X" in r:
+                key += f" (grid {r['Grid_Size_X']}x{r.get('Grid_Size_Y', '1')})"
+            per.setdefault(key, []).append(dur)
     total = sum(sum(v) for v in per.values())
     rows = sorted(per.items(), key=lambda kv: -sum(kv[1]))
     out = [f"# Kernel time per launch: {label}", "", "Command (run from the repository root):",

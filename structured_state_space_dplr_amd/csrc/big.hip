@@ -288,13 +288,21 @@ static int rows_blocks(int rows) {
 // are kept.
 //   CONV:  spectral weights Z'_k = alpha_k Z_k + beta_k conj(Z_{M-k}), the
 //          inverse row DFTs (the lane's bins are exactly its first inverse
-//          pass input) and the inverse twiddle, back into Y.
-//   !CONV: the spectrum of (K + D delta) padded to 2L and the weights
-//          alpha, beta of every bin, written in the permuted layout.
+//          pass input) and the inverse twiddle, back into Y.  The weights of a
+//          bin come from the stored spectrum at the bin and at its partner,
+//          which the lane holds for both of its rows:
+//            alpha_k = ((1 - s_k) S_k + (1 + s_k) conj(S_{M-k})) / (2M),
+//            beta_k  = i c_k (S_k - conj(S_{M-k})) / (2M),
+//          (c_k, s_k) = (cos, sin)(pi k / M).
+//   !CONV: the spectrum S of (K + D delta) padded to 2M (conjugated for the
+//          correlation), one float2 per bin in the permuted layout; bin 0's
+//          slot holds the two real values (S_0, S_M).
+// Storing S (8 B per bin) rather than alpha and beta (16 B) halves the
+// spectrum's traffic in both kernels.
 // ---------------------------------------------------------------------------
 template <int LOG2M, bool CONV>
 __global__ __launch_bounds__(kBigThreads) void big_rows_pair_kernel(
-    float2* __restrict__ Y, float4* __restrict__ coefp, const float* __restrict__ D,
+    float2* __restrict__ Y, float2* __restrict__ specp, const float* __restrict__ D,
     const float2* __restrict__ tw2, const float2* __restrict__ cs,
     const float2* __restrict__ tw4, int nh, int batch, int conj) {
   using S = BigShape<LOG2M>;
@@ -336,15 +344,16 @@ __global__ __launch_bounds__(kBigThreads) void big_rows_pair_kernel(
   dft_dif<16, false>(zb);
   P0::store(za, bufA, lt);
   P0::store(zb, bufB, lb);
-  float4 ca[16], cb[16];
+  float2 sa_[16], sb_[16];
   if constexpr (CONV) {
-    const float4* __restrict__ cfh = coefp + (size_t)h * M;
+    const float2* __restrict__ sph = specp + (size_t)h * M;
 #pragma unroll
     for (int s2 = 0; s2 < 16; ++s2) {
-      ca[s2] = cfh[ka * M2 + lt + 16 * s2];
-      cb[s2] = cfh[kb * M2 + lb + 16 * s2];
+      sa_[s2] = sph[ka * M2 + lt + 16 * s2];
+      sb_[s2] = sph[kb * M2 + lb + 16 * s2];
     }
   }
+  const float2 cs0 = cs[ka + M1 * lt];
   wave_sync();
   P1::load(za, bufA, lt);
   P1::load(zb, bufB, lb);
@@ -360,18 +369,36 @@ __global__ __launch_bounds__(kBigThreads) void big_rows_pair_kernel(
 #pragma unroll
   for (int s2 = 0; s2 < 16; ++s2)
     pz[s2] = sp ? zb[bitrev<4>((16 - s2) & 15)] : zb[bitrev<4>(15 - s2)];
+  // cs_k = (cos, sin)(pi k / M) for k = ka + M1 (lt + 16 s) is cs of the
+  // lane's first bin turned by pi s / 16; cs_{M-k} = (-cos, sin)(pi k / M)
+  float2 csa[16];
+#pragma unroll
+  for (int s2 = 0; s2 < 16; ++s2) csa[s2] = cmul(cs0, make_float2(kCos32[s2], kSin32[s2]));
   if constexpr (CONV) {
     // weighted bins in natural order: oa[s] = Z'(lt + 16 s) of row ka,
     // ob[s] = Z'(lb + 16 s) of row kb (whose partners, for the tasks that
     // keep row kb, are the row-ka bins lt + 16 (15 - s))
+    const float sc = 0.5f / (float)M;
+    // Z'_k from the bin, its partner's bin, S at both and (c, s) of k
+    auto weigh = [sc](float2 z, float2 zp, float2 S, float2 Sp, float2 c) {
+      const float a = sc * (1.0f - c.y), b = sc * (1.0f + c.y), cc = sc * c.x;
+      const float2 al = make_float2(fmaf(a, S.x, b * Sp.x), fmaf(a, S.y, -b * Sp.y));
+      const float2 df = make_float2(S.x - Sp.x, S.y + Sp.y);           // S_k - conj(S_{M-k})
+      const float2 be = make_float2(-cc * df.y, cc * df.x);            // i c (S_k - conj S_{M-k})
+      return cadd(cmul(al, z), cmul(be, cconj(zp)));
+    };
     float2 oa[16], ob[16];
 #pragma unroll
     for (int s2 = 0; s2 < 16; ++s2) {
-      const float4 c = ca[s2], d = cb[s2];
-      oa[s2] = cadd(cmul(make_float2(c.x, c.y), za[bitrev<4>(s2)]),
-                    cmul(make_float2(c.z, c.w), cconj(pz[s2])));
-      ob[s2] = cadd(cmul(make_float2(d.x, d.y), zb[bitrev<4>(s2)]),
-                    cmul(make_float2(d.z, d.w), cconj(za[bitrev<4>(15 - s2)])));
+      const int ps = sp ? ((16 - s2) & 15) : 15 - s2;   // partner of row-ka bin s2 in row kb
+      float2 S = sa_[s2], Sp = sb_[ps];
+      if (sp && s2 == 0) {   // bin 0: the slot holds (S_0, S_M), both real
+        S = make_float2(sa_[0].x, 0.f);
+        Sp = make_float2(sa_[0].y, 0.f);
+      }
+      oa[s2] = weigh(za[bitrev<4>(s2)], pz[s2], S, Sp, csa[s2]);
+      const float2 cb_ = make_float2(-csa[15 - s2].x, csa[15 - s2].y);
+      ob[s2] = weigh(zb[bitrev<4>(s2)], za[bitrev<4>(15 - s2)], sb_[s2], sa_[15 - s2], cb_);
     }
     // inverse pass 0: input x[lt + 16 r] = bin lt + 16 r, already in this lane
     dft_dif<16, true>(oa);
@@ -403,37 +430,26 @@ __global__ __launch_bounds__(kBigThreads) void big_rows_pair_kernel(
       }
     }
   } else {
-    const float sc = 0.5f / (float)M;
     const float Dh = D ? D[h] : 0.f;
-    float4* __restrict__ cfh = coefp + (size_t)h * M;
-    const float2 cs0 = cs[ka + M1 * lt];
+    float2* __restrict__ sph = specp + (size_t)h * M;
 #pragma unroll
     for (int s2 = 0; s2 < 16; ++s2) {
       const int k2 = lt + 16 * s2;
       const int k2p = sp ? ((16 - s2) & 15) * 16 : lb + 16 * (15 - s2);   // partner's k2
       const float2 za_ = za[bitrev<4>(s2)], zb_ = pz[s2];
-      // cs_k = (cos, sin)(pi k / M) for k = ka + M1 (lt + 16 s) is cs of the
-      // lane's first bin turned by pi s / 16; cs_{M-k} = (-cos, sin)(pi k / M)
-      const float2 csa = cmul(cs0, make_float2(kCos32[s2], kSin32[s2]));
-      const float2 csb = make_float2(-csa.x, csa.y);
-      float2 sa = big_rfft_x(za_, zb_, csa), sb = big_rfft_x(zb_, za_, csb);
+      const float2 csb = make_float2(-csa[s2].x, csa[s2].y);
+      float2 sa = big_rfft_x(za_, zb_, csa[s2]), sb = big_rfft_x(zb_, za_, csb);
       sa.x += Dh;
       sb.x += Dh;
-      if (conj) {   // weights of the correlation with (K + D delta)
+      if (conj) {   // the spectrum of the correlation with (K + D delta)
         sa.y = -sa.y;
         sb.y = -sb.y;
       }
-      {
-        const float a = sc * (1.0f - csa.y), bb = sc * (1.0f + csa.y), c = sc * csa.x;
-        const float2 al = make_float2(fmaf(a, sa.x, bb * sb.x), fmaf(a, sa.y, -bb * sb.y));
-        const float2 df = make_float2(sa.x - sb.x, sa.y + sb.y);
-        cfh[ka * M2 + k2] = make_float4(al.x, al.y, -c * df.y, c * df.x);
-      }
-      if (!self) {
-        const float a = sc * (1.0f - csb.y), bb = sc * (1.0f + csb.y), c = sc * csb.x;
-        const float2 al = make_float2(fmaf(a, sb.x, bb * sa.x), fmaf(a, sb.y, -bb * sa.y));
-        const float2 df = make_float2(sb.x - sa.x, sb.y + sa.y);
-        cfh[kb * M2 + k2p] = make_float4(al.x, al.y, -c * df.y, c * df.x);
+      if (sp && s2 == 0) {
+        sph[0] = make_float2(sa.x, sb.x);     // (S_0, S_M): both real
+      } else {
+        sph[ka * M2 + k2] = sa;
+        if (!self) sph[kb * M2 + k2p] = sb;
       }
     }
   }
@@ -465,7 +481,7 @@ static void big_spectrum_from_time(const s4dplr_plan* p, const float* Ktime, con
   big_cols_fwd_kernel<LOG2M><<<col_blocks<LOG2M>(p->H), kBigThreads, 0, s>>>(
       Ktime, Y, wat<const float2>(ws, p->off_tw1), tw4, p->H, p->H, 1);
   big_rows_pair_kernel<LOG2M, false><<<pair_blocks<LOG2M>(p->H), kBigThreads, 0, s>>>(
-      Y, wat<float4>(ws, p->off_coef), D, wat<const float2>(ws, p->off_tw2), cs, tw4, p->H, 1,
+      Y, wat<float2>(ws, p->off_coef), D, wat<const float2>(ws, p->off_tw2), cs, tw4, p->H, 1,
       conj);
 }
 
@@ -505,7 +521,7 @@ static void big_conv(const s4dplr_plan* p, const float* u, float* y, unsigned ch
   big_cols_fwd_kernel<LOG2M><<<col_blocks<LOG2M>(rows), kBigThreads, 0, s>>>(
       u, Y, wat<const float2>(ws, p->off_tw1), tw4, rows, p->H, p->batch);
   big_rows_pair_kernel<LOG2M, true><<<pair_blocks<LOG2M>(rows), kBigThreads, 0, s>>>(
-      Y, wat<float4>(ws, p->off_coef), nullptr, wat<const float2>(ws, p->off_tw2), cs, tw4,
+      Y, wat<float2>(ws, p->off_coef), nullptr, wat<const float2>(ws, p->off_tw2), cs, tw4,
       p->H, p->batch, 0);
   big_cols_inv_kernel<LOG2M, 0><<<col_blocks<LOG2M>(rows), kBigThreads, 0, s>>>(
       Y, y, wat<const float2>(ws, p->off_tw1), rows, p->H, p->batch, 1.0f);
