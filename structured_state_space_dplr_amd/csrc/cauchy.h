@@ -90,7 +90,11 @@ __device__ __forceinline__ float2 block_sum2(float2 v, float2* __restrict__ red,
 }
 
 // acc[f][0..7] += the four Cauchy sums (re, im) at G[f], over poles [0, NP).
-template <int F, bool DIAG>
+// TIED (Q = P): w11 = conj(P) P = |P|^2 is real, so the last sum takes
+// r K11 (one FMA) and -|P|^2 (r y) (one product shared with nothing else and
+// one FMA) instead of two nested FMAs per part: 17 VALU + 1 reciprocal per
+// term instead of 18 + 1.
+template <int F, bool DIAG, bool TIED = false>
 __device__ __forceinline__ void cauchy_sums(const float4* __restrict__ rec, int NP,
                                             const float (&G)[F], float (&acc)[F][8]) {
   for (int n0 = 0; n0 < NP; n0 += kPoleUnroll) {
@@ -117,8 +121,13 @@ __device__ __forceinline__ void cauchy_sums(const float4* __restrict__ rec, int 
           acc[f][3] = fmaf(r, fmaf(-p2.x, yv, p1.w), acc[f][3]);
           acc[f][4] = fmaf(r, fmaf(p3.y, yv, p2.z), acc[f][4]);
           acc[f][5] = fmaf(r, fmaf(-p3.x, yv, p2.w), acc[f][5]);
-          acc[f][6] = fmaf(r, fmaf(p4.y, yv, p3.z), acc[f][6]);
-          acc[f][7] = fmaf(r, fmaf(-p4.x, yv, p3.w), acc[f][7]);
+          if constexpr (TIED) {
+            acc[f][6] = fmaf(r, p3.z, acc[f][6]);
+            acc[f][7] = fmaf(-p4.x, r * yv, acc[f][7]);
+          } else {
+            acc[f][6] = fmaf(r, fmaf(p4.y, yv, p3.z), acc[f][6]);
+            acc[f][7] = fmaf(r, fmaf(-p4.x, yv, p3.w), acc[f][7]);
+          }
         }
       }
     }

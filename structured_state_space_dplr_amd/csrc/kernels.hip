@@ -41,7 +41,7 @@ namespace s4 {
 // channel per blockIdx.y.  perm_m1 > 0 stores the long path's transposed
 // layout: position p = k1*256 + k2 holds frequency l = k1 + perm_m1*k2.
 
-template <int F, bool DIAG>
+template <int F, bool DIAG, bool TIED>
 __global__ __launch_bounds__(kCauchyThreads) void cauchy_kernel(
     ParamPtrs pp, const float* __restrict__ tanT, float2* __restrict__ khat, int N, int NP, int L,
     int perm_m1) {
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_kernel(
 #pragma unroll
     for (int a = 0; a < 8; ++a) acc[f][a] = 0.f;
   }
-  cauchy_sums<F, DIAG>(rec, NP, G, acc);
+  cauchy_sums<F, DIAG, TIED>(rec, NP, G, acc);
 #pragma unroll
   for (int f = 0; f < F; ++f)
     if (pos[f] < L) khat[(size_t)h * L + pos[f]] = cauchy_epilogue<DIAG>(acc[f], T[f], 2 * l[f] == L, nyq);
@@ -128,7 +128,7 @@ __device__ __forceinline__ void weights_pair(const float2* __restrict__ Zb, floa
   }
 }
 
-template <int LOG2L, bool DIAG, bool FROM_TIME>
+template <int LOG2L, bool DIAG, bool FROM_TIME, bool TIED = false>
 __global__ __launch_bounds__(KgenShape<LOG2L>::NTHR) void kgen_wave_kernel(
     ParamPtrs pp, const float* __restrict__ D, const float* __restrict__ Kin,
     float* __restrict__ Kout, float4* __restrict__ coef, const float* __restrict__ tanT,
@@ -182,8 +182,8 @@ __global__ __launch_bounds__(KgenShape<LOG2L>::NTHR) void kgen_wave_kernel(
       }
       if constexpr (S::PS == 2) {
         const int nmid = (NP / 2) / kPoleUnroll * kPoleUnroll;
-        if (ph == 0) cauchy_sums<F, DIAG>(rec, nmid, G, acc);
-        else cauchy_sums<F, DIAG>(rec + kRec * nmid, NP - nmid, G, acc);
+        if (ph == 0) cauchy_sums<F, DIAG, TIED>(rec, nmid, G, acc);
+        else cauchy_sums<F, DIAG, TIED>(rec + kRec * nmid, NP - nmid, G, acc);
         load_tail_tw();
         if (ph == 1) {
 #pragma unroll
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(KgenShape<LOG2L>::NTHR) void kgen_wave_kernel(
             for (int a = 0; a < 8; ++a) acc[f][a] += xs[(f * 8 + a) * NF + ft];
         }
       } else {
-        cauchy_sums<F, DIAG>(rec, NP, G, acc);
+        cauchy_sums<F, DIAG, TIED>(rec, NP, G, acc);
       }
       if (ph == 0) {
 #pragma unroll
@@ -977,6 +977,9 @@ static void kgen_launch(const s4dplr_plan* p, const ParamPtrs& pp, const float* 
     else if (p->flags & S4DPLR_DIAGONAL)
       kgen_wave_kernel<LOG2L, true, false><<<p->H, S::NTHR, 0, s>>>(pp, D, nullptr, Kout, coef,
                                                                   tanT, tw, cs, p->N, p->NP, 0);
+    else if (!pp.Q)   // Q tied to P
+      kgen_wave_kernel<LOG2L, false, false, true><<<p->H, S::NTHR, 0, s>>>(
+          pp, D, nullptr, Kout, coef, tanT, tw, cs, p->N, p->NP, 0);
     else
       kgen_wave_kernel<LOG2L, false, false><<<p->H, S::NTHR, 0, s>>>(pp, D, nullptr, Kout, coef,
                                                                    tanT, tw, cs, p->N, p->NP, 0);
@@ -990,11 +993,14 @@ static hipError_t launch_cauchy_to(const s4dplr_plan* p, const ParamPtrs& pp, fl
   dim3 grid((p->L + per_block - 1) / per_block, p->H);
   const float* tanT = at<const float>(ws, p->off_tan);
   if (p->flags & S4DPLR_DIAGONAL)
-    cauchy_kernel<F, true><<<grid, kCauchyThreads, 0, s>>>(pp, tanT, khat, p->N, p->NP, p->L,
-                                                           perm_m1);
+    cauchy_kernel<F, true, false><<<grid, kCauchyThreads, 0, s>>>(pp, tanT, khat, p->N, p->NP,
+                                                                  p->L, perm_m1);
+  else if (!pp.Q)   // Q tied to P: w11 = |P|^2 is real
+    cauchy_kernel<F, false, true><<<grid, kCauchyThreads, 0, s>>>(pp, tanT, khat, p->N, p->NP,
+                                                                  p->L, perm_m1);
   else
-    cauchy_kernel<F, false><<<grid, kCauchyThreads, 0, s>>>(pp, tanT, khat, p->N, p->NP, p->L,
-                                                            perm_m1);
+    cauchy_kernel<F, false, false><<<grid, kCauchyThreads, 0, s>>>(pp, tanT, khat, p->N, p->NP,
+                                                                   p->L, perm_m1);
   return hipGetLastError();
 }
 
