@@ -622,6 +622,48 @@ def summarize_counters(fetch_dir, write_dir, workload, commands):
     return out
 
 
+SQ_COUNTERS = ("SQ_INSTS_VALU SQ_INSTS_LDS SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES "
+               "SQ_WAIT_INST_LDS SQ_ACTIVE_INST_VALU SQ_WAIT_ANY GRBM_GUI_ACTIVE")
+
+
+def summarize_sq(d, label, command):
+    """Markdown table of the shader-sequencer counters of a --counters run
+    (SQ_COUNTERS in one pass): per kernel, its last dispatch.  VALU issue is
+    SQ_INSTS_VALU (wave instructions, all CUs) per CU per cycle, the cycles
+    being GRBM_GUI_ACTIVE over the 8 XCDs; the wait shares are SQ_WAIT_ANY and
+    SQ_WAIT_INST_LDS over SQ_WAVE_CYCLES."""
+    per, meta = {}, {}
+    for r in _counter_rows(d):
+        key = (_short_name(r["Kernel_Name"]), int(r.get("Dispatch_Id", 0)))
+        per.setdefault(key, {}).setdefault(r["Counter_Name"], 0.0)
+        per[key][r["Counter_Name"]] += float(r["Counter_Value"])
+        meta[key] = r
+    last = {}   # by kernel and grid: one kernel serves launches of several sizes
+    for key in sorted(per, key=lambda k: k[1]):
+        last[(key[0], meta[key].get("Grid_Size", ""))] = key
+    out = [f"# Shader-sequencer counters: {label}", "", "Command (run from the repository root):",
+           "", "```", command, "```", "",
+           "Source: `counter_collection.csv` of one rocprofv3 `--pmc` pass, the last dispatch of "
+           "each kernel, summarized by `python bench.py --summarize-sq`.  VALU issue = "
+           "SQ_INSTS_VALU / (256 CUs x GRBM_GUI_ACTIVE / 8); wait shares = SQ_WAIT_ANY and "
+           "SQ_WAIT_INST_LDS over SQ_WAVE_CYCLES.", "",
+           "| kernel | grid | workgroup | arch VGPRs | scratch (B) | duration (us) | VALU instr "
+           "| VALU issue per CU-cycle | LDS instr | wait any | wait LDS |",
+           "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for (name, _), key in last.items():
+        v, r = per[key], meta[key]
+        cycles = v.get("GRBM_GUI_ACTIVE", 0.0) / 8
+        wc = max(1.0, v.get("SQ_WAVE_CYCLES", 0.0))
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        issue = v.get("SQ_INSTS_VALU", 0.0) / (256 * cycles) if cycles else 0.0
+        out.append(f"| {name} | {r.get('Grid_Size', '')} | {r.get('Workgroup_Size', '')} | "
+                   f"{r.get('VGPR_Count', '')} | {r.get('Scratch_Size', '')} | {dur:.1f} | "
+                   f"{v.get('SQ_INSTS_VALU', 0.0):.3g} | {issue:.2f} | "
+                   f"{v.get('SQ_INSTS_LDS', 0.0):.3g} | {v.get('SQ_WAIT_ANY', 0.0) / wc:.2f} | "
+                   f"{v.get('SQ_WAIT_INST_LDS', 0.0) / wc:.2f} |")
+    return "\n".join(out) + "\n"
+
+
 def counters_sequence(args):
     """The fixed launch sequence of a counter run: one forward pass (set-up),
     five generating-function calls, five convolution launches, then a plain
@@ -668,6 +710,7 @@ def main() -> int:
                     help="run only the counter-collection launch sequence")
     ap.add_argument("--summarize-trace", metavar="DIR")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-sq", metavar="DIR")
     ap.add_argument("--label", default="")
     ap.add_argument("--command", default="")
     ap.add_argument("--out", default="")
@@ -675,6 +718,14 @@ def main() -> int:
 
     if args.summarize_trace:
         text = summarize_trace(args.summarize_trace, args.label or args.workload, args.command)
+        if args.out:
+            with open(args.out, "w") as f:
+                f.write(text)
+        else:
+            sys.stdout.write(text)
+        return 0
+    if args.summarize_sq:
+        text = summarize_sq(args.summarize_sq, args.label or args.workload, args.command)
         if args.out:
             with open(args.out, "w") as f:
                 f.write(text)

@@ -77,3 +77,20 @@ def test_trace_and_counter_summaries(tmp_path):
     k = res["kernels"]["cauchy_kernel"]
     assert math.isclose(res["calibration"]["fetch_scale"], 2.0)
     assert math.isclose(k["bytes_per_launch"], 2.0 * 1024 * 100 + 1.0 * 1024 * 300)
+
+
+def test_sq_summary(tmp_path):
+    d = tmp_path / "sq"
+    d.mkdir()
+    with open(d / "r_counter_collection.csv", "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Grid_Size,Workgroup_Size,VGPR_Count,Scratch_Size,"
+                "Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp\n")
+        vals = {"SQ_INSTS_VALU": 2048.0, "GRBM_GUI_ACTIVE": 16.0, "SQ_WAVE_CYCLES": 100.0,
+                "SQ_WAIT_ANY": 25.0, "SQ_WAIT_INST_LDS": 10.0, "SQ_INSTS_LDS": 7.0}
+        for disp in (1, 2):   # the summary takes the kernel's last dispatch
+            for k, v in vals.items():
+                f.write(f'{disp},"void s4::cauchy_kernel<2, false, true>(x)",1024,256,36,0,{k},'
+                        f'{v * disp},1000,{1000 + 2000 * disp}\n')
+    md = bench.summarize_sq(str(d), "label", "cmd")
+    # 2 x 2048 VALU instructions over 256 CUs x (2 x 16 / 8) cycles = 4.00 per CU-cycle
+    assert "| cauchy_kernel | 1024 | 256 | 36 | 0 | 4.0 | 4.1e+03 | 4.00 | 14 | 0.25 | 0.10 |" in md
