@@ -13,11 +13,12 @@ TOL = 1e-4
 # Per-channel gate: each channel's max error over its own maximum.  The H
 # channels are independent systems; a channel whose kernel is small next to
 # the others could hide a large relative error under the whole-tensor gate.
-# fp32 sums of N Cauchy terms carry about N u (u = 2^-24) of the terms'
-# magnitude and the L-point transforms about log2(L) u; a channel whose
-# spectrum is kappa times larger than its kernel's peak gets kappa times
-# that.  1e-3 allows kappa up to about 100 at N = 64.
-TOL_CHANNEL = 1e-3
+# fp32 sums of N Cauchy terms carry about N u (u = 2^-24; 4e-6 at N = 64) of
+# the terms' magnitude and the L-point transforms about log2(L) u per stage,
+# relative to the channel's own scale unless its spectrum is far larger than
+# its kernel's peak: the task's 1e-4 bar holds per channel with a margin
+# (worst channels measured 6e-7 .. 1.1e-5 over the five workloads).
+TOL_CHANNEL = 1e-4
 
 
 @pytest.fixture(scope="module")
