@@ -201,10 +201,10 @@ s4dplr_status s4dplr_forward(const s4dplr_plan* plan, const float* lambda, const
  * H = 64, L = 65536, batch = 4) are rejected with ERR_TOO_LARGE; the
  * tiny, mid, long and S4D-Lin workload shapes fit.  Computes exactly what
  * s4dplr_forward computes, with the same kernels, on the current device;
- * stream must belong to it.  Every call re-writes the plan's tables into the
- * array (a copy from the plan's host memory, so the plan must outlive the
- * call's completion on the stream), then generates the kernel and applies the
- * convolution.  All calls on one GPU share its array: calls that can overlap
+ * stream must belong to it.  Every call computes the plan's tables into the
+ * array with a small kernel (the same fp64 formulas as the workspace tables,
+ * rounded once; nothing is copied from host memory), then generates the
+ * kernel and applies the convolution.  All calls on one GPU share its array: calls that can overlap
  * in time on one GPU (other streams, other threads) race and must be
  * serialized by the caller.  No device memory is allocated or freed.
  * Errors: ERR_NULL, ERR_ALIAS, ERR_TOO_LARGE, ERR_HIP.

@@ -10,6 +10,7 @@
 #include "fft_sched.h"
 #include "internal.h"
 #include "s4dplr.h"
+#include "tables.h"
 
 namespace {
 
@@ -60,6 +61,21 @@ bool valid_plan(const s4dplr_plan* p) { return p != nullptr; }
 }  // namespace
 
 namespace s4 {
+
+TableSpec plan_table_spec(const s4dplr_plan* p, unsigned char* w) {
+  const bool lds = p->log2L <= S4DPLR_LDS_MAX_LOG2L;
+  TableSpec a;
+  a.tan = reinterpret_cast<float*>(w + p->off_tan);
+  a.tan2 = p->rank > 1 ? reinterpret_cast<float*>(w + p->off_tan2) : nullptr;
+  a.cs = reinterpret_cast<float*>(w + p->off_cs);
+  a.tw_a = reinterpret_cast<float*>(w + (lds ? p->off_twL : p->off_tw1));
+  a.tw_b = reinterpret_cast<float*>(w + (lds ? p->off_twH : p->off_tw2));
+  a.tw4 = lds ? nullptr : reinterpret_cast<float*>(w + p->off_tw4);
+  a.L = p->L;
+  a.log2a = lds ? p->log2L : p->log2L - 8;
+  a.log2b = lds ? (p->log2L > 0 ? p->log2L - 1 : 0) : 8;
+  return a;
+}
 
 void recurrent_shape(int N, long rows, int* ppl_out, int* log2g_out) {
   auto groups_log2 = [N](int ppl) {
@@ -382,10 +398,9 @@ s4dplr_status s4dplr_forward_noalloc(const s4dplr_plan* p, const float* lambda, 
   hipError_t e = s4::noalloc_scratch(&w);
   if (e != hipSuccess) return hip_fail(e);
   // the array keeps whatever the last call on this device left in it: the
-  // tables of this plan are written again by every call
-  if ((e = hipMemcpyAsync(w, p->tables.data(), p->tables_bytes, hipMemcpyHostToDevice,
-                          stream)) != hipSuccess)
-    return hip_fail(e);
+  // tables of this plan are computed into it again by every call, on the
+  // device (no copy from host memory)
+  if ((e = s4::launch_plan_tables(p, w, stream)) != hipSuccess) return hip_fail(e);
   if ((e = s4::launch_kernel_gen(p, lambda, P, Q, B, C, dt, D, K, w, stream)) != hipSuccess)
     return hip_fail(e);
   if ((e = s4::launch_conv(p, u, y, w, stream)) != hipSuccess) return hip_fail(e);

@@ -91,6 +91,12 @@ hipError_t launch_big_ghat(const s4dplr_plan* p, const float* dK, unsigned char*
 // The library's own device scratch for s4dplr_forward_noalloc: its size, and
 // its address on the current device (looked up once per device).
 size_t noalloc_scratch_bytes();
+// The plan's table region computed on the device into w (noalloc.hip).
+hipError_t launch_plan_tables(const s4dplr_plan* p, unsigned char* w, hipStream_t s);
+// Where the entries of the plan's tables go in a buffer laid out like the
+// workspace (tables.h); defined in api.cpp.
+struct TableSpec;
+TableSpec plan_table_spec(const s4dplr_plan* p, unsigned char* w);
 hipError_t noalloc_scratch(unsigned char** out);
 
 // Recurrent view: per-pole step records from the parameters, then T steps of

@@ -12,6 +12,7 @@
 #include <mutex>
 
 #include "internal.h"
+#include "tables.h"
 
 namespace s4 {
 
@@ -29,6 +30,24 @@ unsigned char* g_scratch_ptr[kMaxDevices] = {};
 }  // namespace
 
 size_t noalloc_scratch_bytes() { return kNoallocScratchBytes; }
+
+namespace {
+
+// The plan's table region (tables.h), one entry per thread of a grid-stride
+// loop, so that the no-allocation path copies nothing from host memory.
+__global__ void table_kernel(TableSpec a) {
+  const long total = table_entries(a);
+  for (long g = blockIdx.x * (long)blockDim.x + threadIdx.x; g < total;
+       g += (long)gridDim.x * blockDim.x)
+    table_entry(a, g);
+}
+
+}  // namespace
+
+hipError_t launch_plan_tables(const s4dplr_plan* p, unsigned char* w, hipStream_t s) {
+  table_kernel<<<256, 256, 0, s>>>(plan_table_spec(p, w));
+  return hipGetLastError();
+}
 
 hipError_t noalloc_scratch(unsigned char** out) {
   int dev = -1;

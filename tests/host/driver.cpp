@@ -8,6 +8,7 @@
 
 #include "internal.h"
 #include "s4dplr.h"
+#include "tables.h"
 
 int stub_launch_count();
 
@@ -19,8 +20,32 @@ int stub_launch_count();
     }                                                                  \
   } while (0)
 
+// The per-entry table formulas that the no-allocation path evaluates on the
+// device (tables.h) reproduce the plan's host-built tables bit for bit.
+static int check_table_formulas(const s4dplr_plan* p, const void* ws) {
+  std::vector<unsigned char> store(p->tables_bytes + 256, 0);
+  unsigned char* w = reinterpret_cast<unsigned char*>(
+      (reinterpret_cast<uintptr_t>(store.data()) + 255) & ~uintptr_t(255));
+  const s4::TableSpec a = s4::plan_table_spec(p, w);
+  for (long g = 0; g < s4::table_entries(a); ++g) s4::table_entry(a, g);
+  CHECK(std::memcmp(w, ws, p->tables_bytes) == 0);
+  return 0;
+}
+
 int main() {
   const int Ls[] = {2, 4, 32, 1024, 2048, 16384, 32768, 65536};
+  for (int L : {2, 16, 512, 4096, 32768, 65536})
+    for (unsigned rank : {1u, 2u, 4u}) {
+      s4dplr_plan* p = nullptr;
+      CHECK(s4dplr_plan_create(&p, 2, 8, L, 1, S4DPLR_RANK(rank)) == S4DPLR_OK && p);
+      size_t bytes = 0;
+      CHECK(s4dplr_plan_workspace_bytes(p, &bytes) == S4DPLR_OK);
+      std::vector<unsigned char> store(bytes + 256);
+      void* ws = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(store.data()) + 255) & ~uintptr_t(255));
+      CHECK(s4dplr_plan_init(p, ws, nullptr) == S4DPLR_OK);
+      CHECK(check_table_formulas(p, ws) == 0);
+      s4dplr_plan_destroy(p);
+    }
   const int Ns[] = {1, 3, 64, 256};
   for (int L : Ls)
     for (int N : Ns)
@@ -33,6 +58,7 @@ int main() {
         std::vector<unsigned char> store(bytes + 256);
         void* ws = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(store.data()) + 255) & ~uintptr_t(255));
         CHECK(s4dplr_plan_init(p, ws, nullptr) == S4DPLR_OK);
+        CHECK(check_table_formulas(p, ws) == 0);
         CHECK(s4dplr_plan_init(p, static_cast<char*>(ws) + 8, nullptr) == S4DPLR_ERR_WORKSPACE);
         // compute entry points reach their launchers; the stubs never
         // dereference these synthetic, widely spaced device-style addresses

@@ -7,6 +7,7 @@
 #include <vector>
 
 #include "internal.h"
+#include "tables.h"
 
 static int g_launches = 0;
 int stub_launch_count() { return g_launches; }
@@ -29,6 +30,14 @@ hipError_t noalloc_scratch(unsigned char** out) {
   return hipSuccess;
 }
 bool lds_path(const s4dplr_plan* p) { return p->log2L <= S4DPLR_LDS_MAX_LOG2L; }
+// the device table kernel, played by the same per-entry formulas on the host
+hipError_t launch_plan_tables(const s4dplr_plan* p, unsigned char* w, hipStream_t) {
+  ++g_launches;
+  const TableSpec a = plan_table_spec(p, w);
+  const long n = table_entries(a);
+  for (long g = 0; g < n; ++g) table_entry(a, g);
+  return hipSuccess;
+}
 hipError_t launch_kernel_gen(const s4dplr_plan*, const float*, const float*, const float*,
                              const float*, const float*, const float*, const float*, float*,
                              unsigned char*, hipStream_t) {
