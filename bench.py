@@ -27,11 +27,12 @@ generating function alone (the Cauchy kernel), and the convolution
 bounded sample of the headline workload (a subset of its channels, every
 batch row), on one thread and over a pool of worker processes.
 
-Two more modes turn rocprofv3 output into the summaries under ``profiles/``:
-  python bench.py --summarize-trace DIR --label NAME
-  python bench.py --summarize-counters FETCH_DIR WRITE_DIR --workload NAME
+Three more modes turn rocprofv3 output into the summaries under ``profiles/``:
+  python bench.py --summarize-trace DIR --label NAME --command CMD
+  python bench.py --summarize-counters FETCH_DIR WRITE_DIR --workload NAME --command CMD
+  python bench.py --summarize-sq DIR --workload NAME --command CMD
 and ``--counters`` runs the short, fixed launch sequence those counter runs
-profile (see the design doc for the commands).
+profile; each summary records the rocprofv3 command that produced it.
 """
 from __future__ import annotations
 
