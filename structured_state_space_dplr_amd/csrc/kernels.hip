@@ -128,6 +128,51 @@ __device__ __forceinline__ void weights_pair(const float2* __restrict__ Zb, floa
   }
 }
 
+// exp(-i pi idx / L) from the (cos, sin)(pi j / L) table, 0 <= idx < 2L
+__device__ __forceinline__ float2 wneg(const float2* __restrict__ cs, int L, int idx) {
+  if (idx <= L) {
+    const float2 c = cs[idx];
+    return make_float2(c.x, -c.y);
+  }
+  return cs[2 * L - idx];
+}
+
+// x * i^n (n taken mod 4; n uniform over the wave)
+__device__ __forceinline__ float2 mul_ipow(float2 x, int n) {
+  switch (n & 3) {
+    case 1: return make_float2(-x.y, x.x);
+    case 2: return make_float2(-x.x, -x.y);
+    case 3: return make_float2(x.y, -x.x);
+    default: return x;
+  }
+}
+
+// Pass P of a 256-point Stockham transform held by the 64 lanes of one wave,
+// four points per lane: on entry a[r] = x[lane + 64 r]; the twiddles of pass
+// P >= 1 are tw[r - 1] = W_{4 NS}^{k r}, NS = 4^P, k = lane mod NS (conjugated
+// for the inverse); xb is the wave's own LDS buffer.  After pass 3 the lane
+// holds X[lane + 64 s] in a[bitrev(s)] (no store).
+template <int P, bool INV>
+__device__ __forceinline__ void r4_pass(float2 (&a)[4], float2* __restrict__ xb, int lane,
+                                        const float2 (&tw)[3]) {
+  constexpr int NS = 1 << (2 * P);
+  if constexpr (P > 0) {
+#pragma unroll
+    for (int r = 1; r < 4; ++r) a[r] = INV ? cmulc(a[r], tw[r - 1]) : cmul(a[r], tw[r - 1]);
+  }
+  dft_dif<4, INV>(a);
+  if constexpr (P < 3) {
+    const int k = lane & (NS - 1);
+    const int base = (lane / NS) * 4 * NS + k;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) xb[lds_pad(base + NS * t)] = a[bitrev<2>(t)];
+    wave_sync();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[r] = xb[lds_pad(lane + 64 * r)];
+    wave_sync();
+  }
+}
+
 template <int LOG2L, bool DIAG, bool FROM_TIME, bool TIED = false>
 __global__ __launch_bounds__(KgenShape<LOG2L>::NTHR) void kgen_wave_kernel(
     ParamPtrs pp, const float* __restrict__ D, const float* __restrict__ Kin,
@@ -139,6 +184,12 @@ __global__ __launch_bounds__(KgenShape<LOG2L>::NTHR) void kgen_wave_kernel(
   __shared__ float2 red[NTHR / 64];
   __shared__ float2 buf[S::MP];
   __shared__ float xs[(FROM_TIME || S::PS == 1) ? 1 : S::NF * S::F * 8];
+  // L = 1024: the tail runs on four waves, each a quarter of each transform
+  // (a radix-4 step over the whole transform, then a 256-point transform per
+  // wave), with K in kb and each wave's exchanges in its own slice of xb
+  constexpr bool PAR = LOG2L == 10 && !FROM_TIME;
+  __shared__ float kb[PAR ? L : 1];
+  __shared__ float2 xb[PAR ? 4 * lds_padded_size(256) : 1];
   const int h = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63;
   const bool fft_lane = tid < T;          // lanes of wave 0 that hold the transform
@@ -151,7 +202,23 @@ __global__ __launch_bounds__(KgenShape<LOG2L>::NTHR) void kgen_wave_kernel(
       WPass<LOG2L, P - 1>::load_tw(wB, tw, lane);
     }
   };
-  if constexpr (S::PS == 1 || FROM_TIME) load_tail_tw();
+  // parallel tail (waves 0..3): pre[i] = W_L^{k q} for k = lane + 64 i, the
+  // wave's quarter q; t1..t3 the 256-point passes' W_{4 NS}^{k r}
+  const int tq = tid >> 6;
+  float2 pre[4], t1[3], t2[3], t3[3];
+  auto load_par_tw = [&]() {
+    if (tid < 256) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pre[i] = wneg(cs, L, (2 * (lane + 64 * i) * tq) % (2 * L));
+#pragma unroll
+      for (int r = 1; r < 4; ++r) {
+        t1[r - 1] = wneg(cs, L, (lane & 3) * r * (2 * L / 16));
+        t2[r - 1] = wneg(cs, L, (lane & 15) * r * (2 * L / 64));
+        t3[r - 1] = wneg(cs, L, (lane & 63) * r * (2 * L / 256));
+      }
+    }
+  };
+  if constexpr (!PAR && (S::PS == 1 || FROM_TIME)) load_tail_tw();
   constexpr int NW = (L / 2 + NTHR) / NTHR;     // bin pairs per thread in the weight step
   float2 csj[NW], csm[NW];
 #pragma unroll
@@ -184,7 +251,8 @@ __global__ __launch_bounds__(KgenShape<LOG2L>::NTHR) void kgen_wave_kernel(
         const int nmid = (NP / 2) / kPoleUnroll * kPoleUnroll;
         if (ph == 0) cauchy_sums<F, DIAG, TIED>(rec, nmid, G, acc);
         else cauchy_sums<F, DIAG, TIED>(rec + kRec * nmid, NP - nmid, G, acc);
-        load_tail_tw();
+        if constexpr (PAR) load_par_tw();
+        else load_tail_tw();
         if (ph == 1) {
 #pragma unroll
           for (int f = 0; f < F; ++f)
@@ -210,8 +278,57 @@ __global__ __launch_bounds__(KgenShape<LOG2L>::NTHR) void kgen_wave_kernel(
       }
     }
     __syncthreads();
+    if constexpr (PAR) {
+      // inverse, decimated in frequency by 4: for the wave's quarter q,
+      // y_q[k] = W_L^{-k q} sum_p X[k + 256 p] i^{p q} (k < 256), and
+      // K[4 m + q] = Re IDFT_256(y_q)[m] / L
+      if (tid < 256) {
+        float2* __restrict__ xw = xb + tq * lds_padded_size(256);
+        float2 a[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int k = lane + 64 * i;
+          float2 y = buf[lds_pad(k)];
+#pragma unroll
+          for (int p = 1; p < 4; ++p) y = cadd(y, mul_ipow(buf[lds_pad(k + 256 * p)], p * tq));
+          a[i] = cmulc(y, pre[i]);
+        }
+        r4_pass<0, true>(a, xw, lane, t1);
+        r4_pass<1, true>(a, xw, lane, t1);
+        r4_pass<2, true>(a, xw, lane, t2);
+        r4_pass<3, true>(a, xw, lane, t3);
+        const float invL = 1.0f / (float)L;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int n = 4 * (lane + 64 * t) + tq;
+          const float kv = a[bitrev<2>(t)].x * invL;
+          kb[n] = kv;
+          if (Kout) Kout[(size_t)h * L + n] = kv;
+        }
+      }
+      __syncthreads();
+      // forward transform of the packed zero-padded K (z_k = K_2k + i K_2k+1,
+      // k < L/2), decimated by 4: y_q[j] = W_L^{j q} (z_j + (-i)^q z_{j+256}),
+      // Z[4 k + q] = DFT_256(y_q)[k]
+      if (tid < 256) {
+        float2* __restrict__ xw = xb + tq * lds_padded_size(256);
+        float2 a[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = lane + 64 * i;
+          const float2 z0 = make_float2(kb[2 * j], kb[2 * j + 1]);
+          const float2 z1 = make_float2(kb[2 * j + 512], kb[2 * j + 513]);
+          a[i] = cmul(cadd(z0, mul_ipow(z1, -tq)), pre[i]);
+        }
+        r4_pass<0, false>(a, xw, lane, t1);
+        r4_pass<1, false>(a, xw, lane, t1);
+        r4_pass<2, false>(a, xw, lane, t2);
+        r4_pass<3, false>(a, xw, lane, t3);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) buf[lds_pad(4 * (lane + 64 * t) + tq)] = a[bitrev<2>(t)];
+      }
+    } else if (fft_lane) {
     // inverse transform of length L; K_k = Re / L
-    if (fft_lane) {
       WPass<LOG2L, 0>::load(v, buf, lane);
       WPass<LOG2L, 0>::template compute<true>(v, wA);
       WPass<LOG2L, 0>::store(v, buf, lane);
@@ -245,7 +362,7 @@ __global__ __launch_bounds__(KgenShape<LOG2L>::NTHR) void kgen_wave_kernel(
     __syncthreads();
   }
   // transform of the packed zero-padded kernel z_k = K_2k + i K_2k+1 (k < L/2)
-  if (fft_lane) {
+  if (!PAR && fft_lane) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int k = lane + T * r;
