@@ -32,12 +32,12 @@ def _rel(gpu, ref):
     return float(np.abs(gpu.astype(np.float64) - ref).max() / np.abs(ref).max())
 
 
-def _both(s4, x, diagonal=False):
+def _both(s4, x, diagonal=False, rank=1):
     """(K, y) from the workspace entry point and from the no-allocation one."""
     import torch
     H, N = x["lam"].shape[:2]
     batch, _, L = x["u"].shape
-    plan = s4.Plan(H, N, L, batch, diagonal=diagonal)
+    plan = s4.Plan(H, N, L, batch, diagonal=diagonal, rank=rank)
     t = {k: _dev(x[k]) for k in ("lam", "P", "Q", "B", "C", "dt", "D", "u")}
     P = None if diagonal else t["P"]
     out = []
@@ -79,6 +79,18 @@ def test_length_classes(s4, L, diag):
     assert np.array_equal(Kw, Kn) and np.array_equal(yw, yn)
     Kr, yr = o.forward(x["lam"], x["P"], x["Q"], x["B"], x["C"], x["dt"], x["D"], x["u"],
                        diagonal=diag)
+    assert _rel(Kn, Kr) <= TOL and _rel(yn, yr) <= TOL
+
+
+@pytest.mark.parametrize("L,rank", [(2048, 2), (32768, 3)])
+def test_low_rank_plans(s4, L, rank):
+    # rank r > 1 plans read the two-float frequency nodes, which the
+    # no-allocation path computes on the device like every other table
+    print(f"case: forward_noalloc L={L} rank={rank}", flush=True)
+    x = make_generic_inputs(H=3, N=12, L=L, batch=2, seed=L + rank, distinct_q=True, rank=rank)
+    (Kw, yw), (Kn, yn) = _both(s4, x, rank=rank)
+    assert np.array_equal(Kw, Kn) and np.array_equal(yw, yn)
+    Kr, yr = o.forward(x["lam"], x["P"], x["Q"], x["B"], x["C"], x["dt"], x["D"], x["u"])
     assert _rel(Kn, Kr) <= TOL and _rel(yn, yr) <= TOL
 
 
