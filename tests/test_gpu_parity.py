@@ -107,6 +107,47 @@ def test_workload_parity(s4, name):
 
 # ---- every sequence length, generic DPLR parameters ------------------------
 
+def test_maximum_size_sampled(s4):
+    # the largest problem a plan accepts: L = 65536 and batch * H * L just
+    # under 2^31 elements, so every kernel's row and element offsets reach
+    # beyond 32-bit byte offsets; the output checked on sampled channels and
+    # batch rows (first, middle, last) against the oracle
+    import torch
+    L, H, batch, N = 65536, 4096, 7, 64
+    assert batch * H * L < 2 ** 31
+    plan = s4.Plan(H, N, L, batch)
+    need = plan.workspace_bytes + 4 * (2 * batch * H * L + H * L)
+    free, _ = torch.cuda.mem_get_info()
+    if free < 1.2 * need:
+        plan.close()
+        pytest.skip(f"needs {need / 2 ** 30:.0f} GiB of device memory")
+    print(f"case: maximum size H={H} N={N} L={L} batch={batch}", flush=True)
+    x = make_inputs("waveform", H=H, batch=1, L=2)        # the parameters of H channels
+    t = {k: _dev(x[k]) for k in ("lam", "P", "B", "C", "dt", "D")}
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    u = torch.randn((batch, H, L), generator=g, device="cuda")
+    K = torch.empty((H, L), dtype=torch.float32, device="cuda")
+    y = torch.empty_like(u)
+    ws = plan.workspace()
+    s4.forward(plan, t["lam"], t["P"], None, t["B"], t["C"], t["dt"], t["D"], u, K, y, ws)
+    torch.cuda.synchronize()
+    hs, bs = [0, H // 2 + 1, H - 1], [0, batch // 2, batch - 1]
+    Ks = K[hs].cpu().numpy()
+    ys = y[bs][:, hs].cpu().numpy()
+    us = u[bs][:, hs].cpu().numpy()
+    del u, y, K, ws
+    plan.close()
+    sub = {k: x[k][hs] for k in ("lam", "P", "B", "C", "dt", "D")}
+    Kr, yr = o.forward(sub["lam"], sub["P"], None, sub["B"], sub["C"], sub["dt"], sub["D"], us)
+    eK, ey = _rel(Ks, Kr), _rel(ys, yr)
+    cK, cy = _rel_channels(Ks, Kr, 0), _rel_channels(ys, yr, 1)
+    print(f"  rel err K {eK:.3e} y {ey:.3e}; worst channel K {cK.max():.3e} y {cy.max():.3e}",
+          flush=True)
+    assert eK <= TOL and ey <= TOL
+    assert cK.max() <= TOL_CHANNEL and cy.max() <= TOL_CHANNEL
+
+
 @pytest.mark.parametrize("L", [2 ** k for k in range(1, 17)])
 def test_all_lengths_generic(s4, L):
     print(f"case: generic H=3 N=8 L={L} batch=2", flush=True)
