@@ -71,6 +71,8 @@ TableSpec plan_table_spec(const s4dplr_plan* p, unsigned char* w) {
   a.tw_a = reinterpret_cast<float*>(w + (lds ? p->off_twL : p->off_tw1));
   a.tw_b = reinterpret_cast<float*>(w + (lds ? p->off_twH : p->off_tw2));
   a.tw4 = lds ? nullptr : reinterpret_cast<float*>(w + p->off_tw4);
+  a.tw_c = lds ? nullptr : reinterpret_cast<float*>(w + p->off_tw1h);
+  a.log2c = lds ? 0 : p->log2L - 9;
   a.L = p->L;
   a.log2a = lds ? p->log2L : p->log2L - 8;
   a.log2b = lds ? (p->log2L > 0 ? p->log2L - 1 : 0) : 8;
@@ -172,6 +174,8 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
   if (!lds) off = align_up(off + 2 * sizeof(float) * (size_t)s4::fft_tw_size(8));
   p->off_tw4 = off;
   if (!lds) off = align_up(off + 2 * sizeof(float) * 512);
+  p->off_tw1h = off;
+  if (!lds) off = align_up(off + 2 * sizeof(float) * (size_t)s4::fft_tw_size(log2L - 9));
   p->tables_bytes = off;
   // Scratch region.
   p->off_khat = off;
@@ -264,6 +268,7 @@ s4dplr_status s4dplr_plan_create(s4dplr_plan** out, int H, int N, int L, int bat
   } else {
     fft_twiddles(log2L - 8, reinterpret_cast<float*>(p->tables.data() + p->off_tw1));
     fft_twiddles(8, reinterpret_cast<float*>(p->tables.data() + p->off_tw2));
+    fft_twiddles(log2L - 9, reinterpret_cast<float*>(p->tables.data() + p->off_tw1h));
     float* t4 = reinterpret_cast<float*>(p->tables.data() + p->off_tw4);
     for (int i = 0; i < 512; ++i) {
       const long m = i < 256 ? i : 256L * (i - 256);      // W_L^m

@@ -26,7 +26,7 @@ struct BigShape {
   static constexpr int M = 1 << LOG2M;
   static constexpr int LOG2M2 = 8, M2 = 256;
   static constexpr int LOG2M1 = LOG2M - 8, M1 = M / 256;
-  static_assert(LOG2M >= 15 && LOG2M <= 16, "four-step range");
+  static_assert(LOG2M >= 14 && LOG2M <= 16, "four-step range");
 };
 
 // The four-step twiddles W_M^m (m = n2 k1 < M) from two 256-entry tables
@@ -149,6 +149,9 @@ __global__ __launch_bounds__(kBigThreads, 4) void big_cols_fwd_kernel(
 // Inverse column step: x[M2 n1 + n2] = sum_{k1} Y[k1][n2] W_M1^{-n1 k1}.
 // MODE 0: outputs n < M/2 as (y_2n, y_2n+1) (the kept half of the causal
 // convolution).  MODE 1: all n, real part times `scale` (time-domain kernel).
+// MODE 2: all n, complex, times `scale`, into rows of 2M floats: the packed
+// time-domain kernel z_n = K_2n + i K_2n+1 of a 2M-point kernel, i.e. K in
+// natural order.
 template <int LOG2M, int MODE>
 __global__ __launch_bounds__(kBigThreads, 4) void big_cols_inv_kernel(
     const float2* __restrict__ Y, float* __restrict__ out, const float2* __restrict__ tw1,
@@ -200,12 +203,21 @@ __global__ __launch_bounds__(kBigThreads, 4) void big_cols_inv_kernel(
         const int n1 = la + T * r;     // < M1/2
         yr[M2 * n1] = lds[ca * CP + lds_pad(n1)];
       }
-    } else {
+    } else if constexpr (MODE == 1) {
       float* __restrict__ kr = out + mem_row(lrow, H, batch) * M + n2;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int n1 = la + T * r;
         kr[M2 * n1] = lds[ca * CP + lds_pad(n1)].x * scale;
+      }
+    } else {
+      float2* __restrict__ zr =
+          reinterpret_cast<float2*>(out + mem_row(lrow, H, batch) * (2 * (size_t)M)) + n2;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int n1 = la + T * r;
+        const float2 v = lds[ca * CP + lds_pad(n1)];
+        zr[M2 * n1] = make_float2(v.x * scale, v.y * scale);
       }
     }
     __syncthreads();
@@ -221,8 +233,10 @@ __global__ __launch_bounds__(kBigThreads, 4) void big_cols_inv_kernel(
 //   inverse (INV):  Y[k1][n2] = W_M^{-n2 k1} sum_{k2} X[k1][k2] W_M2^{-n2 k2}
 //                   (X in the permuted layout, e.g. the generating function).
 // Every lane reads and writes the same 16 points of its row, so X may be Y.
+// TWS = 2 takes the four-step twiddles W_M^m of an M-point transform from the
+// table of a 2M-point one (W_M^m = W_2M^(2m)).
 // ---------------------------------------------------------------------------
-template <int LOG2M, bool INV>
+template <int LOG2M, bool INV, int TWS = 1>
 __global__ __launch_bounds__(kBigThreads) void big_rows_kernel(
     const float2* X, float2* Y, const float2* __restrict__ tw2, const float2* __restrict__ tw4,
     int rows) {
@@ -262,7 +276,7 @@ __global__ __launch_bounds__(kBigThreads) void big_rows_kernel(
   for (int s2 = 0; s2 < 16; ++s2) {
     const int n = lt + 16 * s2;
     float2 o = v[bitrev<4>(s2)];
-    if constexpr (INV) o = cmulc(o, w_M(twm, n * k1));
+    if constexpr (INV) o = cmulc(o, w_M(twm, TWS * n * k1));
     Yr[n] = o;
   }
 }
@@ -487,9 +501,21 @@ static void big_spectrum_from_time(const s4dplr_plan* p, const float* Ktime, con
 
 template <int LOG2M>
 static void big_kspec(const s4dplr_plan* p, const float* Ktime, const float* D, float* Kout,
-                      unsigned char* ws, hipStream_t s, int conj) {
+                      unsigned char* ws, hipStream_t s, int conj, bool half) {
   using S = BigShape<LOG2M>;
-  if (!Ktime) {
+  if (!Ktime && half) {
+    // the workspace holds Y (M/2 points, the four-step order of an M/2-point
+    // transform) whose inverse transform, times 1/M, is the packed kernel
+    // z_n = K_2n + i K_2n+1: K in natural order
+    float2* Y = wat<float2>(ws, p->off_big);
+    float* K = Kout ? Kout : wat<float>(ws, p->off_kbuf);
+    big_rows_kernel<LOG2M - 1, true, 2><<<rows_blocks<LOG2M - 1>(p->H), kBigThreads, 0, s>>>(
+        wat<const float2>(ws, p->off_khat), Y, wat<const float2>(ws, p->off_tw2),
+        wat<const float2>(ws, p->off_tw4), p->H);
+    big_cols_inv_kernel<LOG2M - 1, 2><<<col_blocks<LOG2M - 1>(p->H), kBigThreads, 0, s>>>(
+        Y, K, wat<const float2>(ws, p->off_tw1h), p->H, p->H, 1, 1.0f / (float)S::M);
+    Ktime = K;
+  } else if (!Ktime) {
     // inverse transform of the generating function (permuted layout) -> K
     float2* Y = wat<float2>(ws, p->off_big);
     float* K = Kout ? Kout : wat<float>(ws, p->off_kbuf);
@@ -504,9 +530,9 @@ static void big_kspec(const s4dplr_plan* p, const float* Ktime, const float* D, 
 }
 
 hipError_t launch_big_kspec(const s4dplr_plan* p, const float* Ktime, const float* D,
-                            float* Kout, unsigned char* ws, hipStream_t s, int conj) {
-  if (p->log2L == 15) big_kspec<15>(p, Ktime, D, Kout, ws, s, conj);
-  else if (p->log2L == 16) big_kspec<16>(p, Ktime, D, Kout, ws, s, conj);
+                            float* Kout, unsigned char* ws, hipStream_t s, int conj, bool half) {
+  if (p->log2L == 15) big_kspec<15>(p, Ktime, D, Kout, ws, s, conj, half);
+  else if (p->log2L == 16) big_kspec<16>(p, Ktime, D, Kout, ws, s, conj, half);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

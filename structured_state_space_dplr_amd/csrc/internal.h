@@ -26,6 +26,8 @@ struct s4dplr_plan {
   size_t off_tw1;    // long path: FFT twiddles for the column transforms (L/256 points)
   size_t off_tw2;    // long path: FFT twiddles for the row transforms (256 points)
   size_t off_tw4;    // long path: [512] float2, W_L^b (b < 256) then W_L^(256 a) (a < 256)
+  size_t off_tw1h;   // long path: FFT twiddles for the column transforms of L/2 points
+                     // (L/512 points), the half-length inverse of stage 1
   size_t tables_bytes;
   size_t off_khat;   // [H][L] float2: generating function at the roots of unity
   size_t off_coef;   // [H][L] float4: spectral weights (alpha, beta) of bin j
@@ -77,8 +79,11 @@ hipError_t launch_spectrum_from_time(const s4dplr_plan* p, const float* Ktime, c
 hipError_t launch_conv(const s4dplr_plan* p, const float* u, float* y, unsigned char* ws,
                        hipStream_t s);
 // Long sequences (log2 L = 15, 16): four-step transforms through the workspace.
+// Without Ktime the workspace's generating-function region is the input: K-hat
+// (L points, four-step order) or, with `half`, the L/2-point spectrum Y of the
+// packed kernel that the rank-1 Cauchy kernel writes for this path.
 hipError_t launch_big_kspec(const s4dplr_plan* p, const float* Ktime, const float* D,
-                            float* Kout, unsigned char* ws, hipStream_t s, int conj);
+                            float* Kout, unsigned char* ws, hipStream_t s, int conj, bool half);
 hipError_t launch_big_conv(const s4dplr_plan* p, const float* u, float* y, unsigned char* ws,
                            hipStream_t s);
 // Long path backward: dK, dD of the convolution, and Ghat = FFT_L(dK) / L into

@@ -71,6 +71,83 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_kernel(
     if (pos[f] < L) khat[(size_t)h * L + pos[f]] = cauchy_epilogue<DIAG>(acc[f], T[f], 2 * l[f] == L, nyq);
 }
 
+// The generating function reduced to what the time-domain kernel needs, for
+// the four-step path.  K = Re IDFT_L(K-hat) / L depends on K-hat only through
+// its Hermitian part Xh_m = (X_m + conj(X_{L-m})) / 2, and the packed kernel
+// z_n = K_2n + i K_2n+1 (n < L/2) is IDFT_{L/2}(Y) / L with
+//   Y_m = (Xh_m + Xh_{m+L/2}) + i e^{2 pi i m / L} (Xh_m - Xh_{m+L/2}),
+// an L/2-point transform instead of an L-point one.  Y_l and Y_{L/2-l}
+// (0 < l < L/4) both depend on X at l, L - l, L/2 + l and L/2 - l: a lane pair
+// takes them, the even lane l and L - l, the odd lane L/2 - l and L/2 + l,
+// swaps its two values with its partner and stores Y_l (even) or Y_{L/2-l}
+// (odd).  The pair with l = 0 needs no swap: the even lane takes 0 and L/2
+// for Y_0, the odd lane L/4 and 3L/4 for Y_{L/4}.
+// Y is stored in the four-step order of an L/2-point transform: Y_m at
+// (m mod M1) 256 + m / M1, M1 = L / 512.  Pair q = 128 a + b (a < M1,
+// b < 128) takes l = a + M1 b, so Y_l goes to 256 a + b and Y_{L/2-l} to
+// 256 (M1 - a) + 255 - b (256 - b for a = 0): each half of a wave stores
+// one contiguous run.
+// (Seven waves per SIMD, what the pole records' LDS allows: without the
+// bound the scheduler issues all four poles' record reads ahead, 107 VGPRs.)
+template <bool DIAG, bool TIED>
+__global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(7)))
+void cauchy_half_kernel(
+    ParamPtrs pp, const float* __restrict__ tanT, const float2* __restrict__ cs,
+    float2* __restrict__ yhat, int N, int NP, int L) {
+  __shared__ float4 rec[kRec * kMaxPoles];
+  __shared__ float2 red[kCauchyThreads / 64];
+  const int h = blockIdx.y, tid = threadIdx.x;
+  const float2 part = build_pole_records(pp, h, N, NP, DIAG, rec, tid, kCauchyThreads);
+  const float2 sum = block_sum2<kCauchyThreads>(part, red, tid);
+  const float dt = pp.dt[h];
+  const float2 nyq = make_float2(0.5f * dt * sum.x, 0.5f * dt * sum.y);
+  const float two_dt = 2.0f / dt;
+  const int M1 = L / 512, H2 = L / 2, Q = L / 4;
+  const int g = blockIdx.x * kCauchyThreads + tid;          // < L/2 (the grid is exact)
+  const bool odd = g & 1;
+  const int q = g >> 1;
+  const int l = (q >> 7) + M1 * (q & 127);
+  int f[2];
+  if (l == 0) {
+    f[0] = odd ? Q : 0;
+    f[1] = odd ? H2 + Q : H2;
+  } else {
+    f[0] = odd ? H2 - l : l;
+    f[1] = odd ? H2 + l : L - l;
+  }
+  float T[2], G[2], acc[2][8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    T[i] = tanT[f[i]];
+    G[i] = two_dt * T[i];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[i][k] = 0.f;
+  }
+  cauchy_sums<2, DIAG, TIED>(rec, NP, G, acc);
+  const float2 A = cauchy_epilogue<DIAG>(acc[0], T[0], 2 * f[0] == L, nyq);
+  const float2 B = cauchy_epilogue<DIAG>(acc[1], T[1], 2 * f[1] == L, nyq);
+  const float2 pA = make_float2(__shfl_xor(A.x, 1), __shfl_xor(A.y, 1));
+  const float2 pB = make_float2(__shfl_xor(B.x, 1), __shfl_xor(B.y, 1));
+  // Y_m from X at m, L - m, m + L/2 and L/2 - m
+  float2 xm = A, xlm = B, xmh = pB, xlmh = pA;
+  if (l == 0) {
+    if (odd) {
+      xmh = B;
+      xlmh = A;
+    } else {
+      xlm = A;
+      xmh = B;
+      xlmh = B;
+    }
+  }
+  const int m = odd ? (l == 0 ? Q : H2 - l) : l;
+  const float2 h1 = make_float2(0.5f * (xm.x + xlm.x), 0.5f * (xm.y - xlm.y));
+  const float2 h2 = make_float2(0.5f * (xmh.x + xlmh.x), 0.5f * (xmh.y - xlmh.y));
+  const float2 t = cmul(cs[2 * m], csub(h1, h2));           // e^{2 pi i m / L} (Xh_m - Xh_{m+L/2})
+  yhat[(size_t)h * H2 + (m % M1) * 256 + m / M1] =
+      make_float2(h1.x + h2.x - t.y, h1.y + h2.y + t.x);
+}
+
 // ---------------------------------------------------------------------------
 // Stage 1 fused for 32 <= L <= 1024: one block per channel.  All threads form
 // the generating function (one frequency each) in LDS; one wave takes the
@@ -1121,8 +1198,24 @@ static hipError_t launch_cauchy_to(const s4dplr_plan* p, const ParamPtrs& pp, fl
   return hipGetLastError();
 }
 
+template <bool DIAG, bool TIED>
+static void cauchy_half_launch(const s4dplr_plan* p, const ParamPtrs& pp, unsigned char* ws,
+                               hipStream_t s) {
+  const dim3 grid(p->L / 2 / kCauchyThreads, p->H);
+  cauchy_half_kernel<DIAG, TIED><<<grid, kCauchyThreads, 0, s>>>(
+      pp, at<const float>(ws, p->off_tan), at<const float2>(ws, p->off_cs),
+      at<float2>(ws, p->off_khat), p->N, p->NP, p->L);
+}
+
 hipError_t launch_cauchy(const s4dplr_plan* p, const ParamPtrs& pp, unsigned char* ws,
                          hipStream_t s) {
+  if (!lds_path(p)) {
+    // the four-step path: the spectrum of the packed kernel, L/2 points
+    if (p->flags & S4DPLR_DIAGONAL) cauchy_half_launch<true, false>(p, pp, ws, s);
+    else if (!pp.Q) cauchy_half_launch<false, true>(p, pp, ws, s);
+    else cauchy_half_launch<false, false>(p, pp, ws, s);
+    return hipGetLastError();
+  }
   return launch_cauchy_to(p, pp, at<float2>(ws, p->off_khat), lds_path(p) ? 0 : p->L / 256, ws,
                           s);
 }
@@ -1184,7 +1277,10 @@ static void conv_launch(const s4dplr_plan* p, const float* u, float* y, unsigned
     constexpr int by_lds = (160 * 1024) / (R::RPB * R::MP * 8);
     constexpr int by_waves = 32 / (R::NTHR / 64);
     constexpr int per_cu = by_lds < by_waves ? by_lds : by_waves;
-    const int target = 256 * (per_cu > 0 ? per_cu : 1);
+    // Persistent blocks, one round of the resident capacity; at one block per
+    // CU (L = 16384) two rounds: 2 rows per block at 1024 rows ran 3.5% faster
+    // than 4 (one round) and than 1 or 3.
+    const int target = 256 * (per_cu > 1 ? per_cu : 2);
     const int gpb = (ngroups + target - 1) / target;
     const int blocks = (ngroups + gpb - 1) / gpb;
     conv_rows_kernel<LOG2L><<<blocks, R::NTHR, 0, s>>>(
@@ -1220,8 +1316,9 @@ static void conv_launch(const s4dplr_plan* p, const float* u, float* y, unsigned
   }
 
 static hipError_t launch_kspec(const s4dplr_plan* p, const float* Ktime, const float* D,
-                               float* Kout, unsigned char* ws, hipStream_t s, int conj) {
-  if (!lds_path(p)) return launch_big_kspec(p, Ktime, D, Kout, ws, s, conj);
+                               float* Kout, unsigned char* ws, hipStream_t s, int conj,
+                               bool half = false) {
+  if (!lds_path(p)) return launch_big_kspec(p, Ktime, D, Kout, ws, s, conj, half);
   S4_DISPATCH_LOG2L(kspec_launch, p, Ktime, D, Kout, ws, s, conj);
   return hipGetLastError();
 }
@@ -1252,7 +1349,8 @@ hipError_t launch_kernel_gen(const s4dplr_plan* p, const float* lam, const float
   }
   hipError_t e = launch_cauchy(p, pp, ws, s);
   if (e != hipSuccess) return e;
-  return launch_kspec(p, nullptr, D, Kout, ws, s, 0);
+  // L >= 32768: launch_cauchy wrote the half-length spectrum Y
+  return launch_kspec(p, nullptr, D, Kout, ws, s, 0, !lds_path(p));
 }
 
 hipError_t launch_spectrum_from_time(const s4dplr_plan* p, const float* Ktime, const float* D,

@@ -21,14 +21,15 @@ struct TableSpec {
   float* tw_a;      // L <= 16384: twiddles of L-point transforms; else of L/256 points
   float* tw_b;      // L <= 16384: of L/2-point transforms; else of 256 points
   float* tw4;       // L >= 32768: W_L^b (b < 256), then W_L^(256 a) (a < 256); else NULL
-  int L, log2a, log2b;
+  float* tw_c;      // L >= 32768: twiddles of L/512-point transforms; else NULL
+  int L, log2a, log2b, log2c;
 };
 
 constexpr double kTablePi = 3.14159265358979323846;
 
 S4_HD inline long table_entries(const TableSpec& a) {
   return 2L * a.L + (a.L + 1) + fft_tw_size(a.log2a) + fft_tw_size(a.log2b) +
-         (a.tw4 ? 512 : 0);
+         (a.tw4 ? 512 + fft_tw_size(a.log2c) : 0);
 }
 
 // entry e of the pass twiddle table of a 2^log2n-point transform: pass p >= 1
@@ -46,7 +47,7 @@ S4_HD inline void table_twiddle(float* t, int log2n, int e) {
   t[2 * e + 1] = (float)sin(ang);
 }
 
-// entry g of the concatenation tan | tan2 | cs | tw_a | tw_b | tw4
+// entry g of the concatenation tan | tan2 | cs | tw_a | tw_b | tw4 | tw_c
 S4_HD inline void table_entry(const TableSpec& a, long g) {
   const int L = a.L;
   if (g < L) {
@@ -88,11 +89,16 @@ S4_HD inline void table_entry(const TableSpec& a, long g) {
     return;
   }
   g -= nb;
-  const int q = (int)g;             // q < 512
-  const long m = q < 256 ? q : 256L * (q - 256);
-  const double ang = -2.0 * kTablePi * (double)(m % L) / (double)L;
-  a.tw4[2 * q + 0] = (float)cos(ang);
-  a.tw4[2 * q + 1] = (float)sin(ang);
+  if (g < 512) {
+    const int q = (int)g;
+    const long m = q < 256 ? q : 256L * (q - 256);
+    const double ang = -2.0 * kTablePi * (double)(m % L) / (double)L;
+    a.tw4[2 * q + 0] = (float)cos(ang);
+    a.tw4[2 * q + 1] = (float)sin(ang);
+    return;
+  }
+  g -= 512;
+  table_twiddle(a.tw_c, a.log2c, (int)g);
 }
 
 }  // namespace s4
