@@ -64,21 +64,21 @@ __device__ __forceinline__ float2 big_rfft_x(float2 zj, float2 zmj, float2 csj) 
 // while the current one is transformed.  Logical row h*batch + b reads or
 // writes memory row b*H + h of the [batch][H][L] arrays (batch = 1: row h).
 // ---------------------------------------------------------------------------
-template <int LOG2M>
+template <int LOG2M, int NTHR = kBigThreads>
 struct ColShape {
   using S = BigShape<LOG2M>;
   static constexpr int LOG2M1 = S::LOG2M1, M1 = S::M1, M2 = S::M2;
   static constexpr int T = M1 / 16;                  // lanes per column
-  static constexpr int CT = kBigThreads / T;         // columns per task
+  static constexpr int CT = NTHR / T;                // columns per task
   static constexpr int NG = M2 / CT;                 // tasks per logical row
   static constexpr int CP = lds_padded_size(M1);
   static_assert(fft_num_passes(LOG2M1) == 2 && fft_radix_log(LOG2M1, 0) == 4, "two passes");
 };
 constexpr int kColBlocks = 256 * 4;   // four resident blocks per CU (LDS-bound)
 
-template <int LOG2M>
+template <int LOG2M, int NTHR = kBigThreads>
 static int col_blocks(int rows) {
-  const int ntask = rows * ColShape<LOG2M>::NG;
+  const int ntask = rows * ColShape<LOG2M, NTHR>::NG;
   return ntask < kColBlocks ? ntask : kColBlocks;
 }
 
@@ -149,9 +149,6 @@ __global__ __launch_bounds__(kBigThreads, 4) void big_cols_fwd_kernel(
 // Inverse column step: x[M2 n1 + n2] = sum_{k1} Y[k1][n2] W_M1^{-n1 k1}.
 // MODE 0: outputs n < M/2 as (y_2n, y_2n+1) (the kept half of the causal
 // convolution).  MODE 1: all n, real part times `scale` (time-domain kernel).
-// MODE 2: all n, complex, times `scale`, into rows of 2M floats: the packed
-// time-domain kernel z_n = K_2n + i K_2n+1 of a 2M-point kernel, i.e. K in
-// natural order.
 template <int LOG2M, int MODE>
 __global__ __launch_bounds__(kBigThreads, 4) void big_cols_inv_kernel(
     const float2* __restrict__ Y, float* __restrict__ out, const float2* __restrict__ tw1,
@@ -203,21 +200,12 @@ __global__ __launch_bounds__(kBigThreads, 4) void big_cols_inv_kernel(
         const int n1 = la + T * r;     // < M1/2
         yr[M2 * n1] = lds[ca * CP + lds_pad(n1)];
       }
-    } else if constexpr (MODE == 1) {
+    } else {
       float* __restrict__ kr = out + mem_row(lrow, H, batch) * M + n2;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int n1 = la + T * r;
         kr[M2 * n1] = lds[ca * CP + lds_pad(n1)].x * scale;
-      }
-    } else {
-      float2* __restrict__ zr =
-          reinterpret_cast<float2*>(out + mem_row(lrow, H, batch) * (2 * (size_t)M)) + n2;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int n1 = la + T * r;
-        const float2 v = lds[ca * CP + lds_pad(n1)];
-        zr[M2 * n1] = make_float2(v.x * scale, v.y * scale);
       }
     }
     __syncthreads();
@@ -470,6 +458,177 @@ __global__ __launch_bounds__(kBigThreads) void big_rows_pair_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Stage 1 from the half-length spectrum Y (rank 1): the packed kernel
+// z_n = K_2n + i K_2n+1 = IDFT_{L/2}(Y)_n / L (n < L/2) and the padded
+// spectrum S_k = sum_{n<L} K_n W_2L^{kn} + D (k <= L).  The even bins are
+// the Hermitian part of the generating function, S_2m = Xh_m + D, written by
+// the Cauchy kernel.  For the odd bins, with a = K_even, b = K_odd,
+//   S_{2j+1} = E_j + W_2L^{2j+1} O_j + D,
+//   E = DFT_{L/2}(a_m W_L^m),  O = DFT_{L/2}(b_m W_L^m),
+// and F = DFT_{L/2}(z_m W_L^m) = E + i O; a and b are real, so
+// E_{L/2-1-j} = conj E_j (likewise O), which separates the two:
+//   E_j = (F_j + conj F_p) / 2,  O_j = (F_j - conj F_p) / (2i),  p = L/2 - 1 - j.
+// So one L/2-point transform gives all odd bins, where the padded transform
+// of K takes an L-point one ("The S4 kernel, from scratch", section 5: the
+// spectrum of the kernel zero-padded to 2L).
+// ---------------------------------------------------------------------------
+
+// Column step (M = L/2 points per row, four-step M1 x 256): the inverse
+// column DFTs after big_rows_kernel, z times `scale` out as K (natural
+// order), then z_n W_L^n through the forward column DFTs, times the four-step
+// twiddle W_M^{n2 k1}, into F[row][k1][n2].  128-thread blocks: half the
+// columns per task of the other column steps, twice the tasks (the waveform
+// workload's 64 rows give 1024), 3 us faster than 256 threads there.
+template <int LOG2M>
+__global__ __launch_bounds__(128) void big_cols_invfwd_kernel(
+    const float2* __restrict__ X, float* __restrict__ K, float2* __restrict__ F,
+    const float2* __restrict__ tw1, const float2* __restrict__ tw4, int rows, float scale) {
+  using C = ColShape<LOG2M, 128>;
+  using P0 = WPass<C::LOG2M1, 0>;
+  using P1 = WPass<C::LOG2M1, 1>;
+  constexpr int M = BigShape<LOG2M>::M, M2 = C::M2, T = C::T, CT = C::CT, NG = C::NG,
+                CP = C::CP;
+  __shared__ float2 lds[CT * CP];
+  __shared__ TwM twm;   // W_L^m, L = 2M: the twist W_L^n and, at even powers, W_M
+  const int tid = threadIdx.x;
+  const int ca = tid % CT, la = tid / CT;
+  const int cb = tid / T, lb = tid % T;
+  load_twM(twm, tw4, tid, 128);
+  PassTwiddles<C::LOG2M1, 1> pt;
+  pt.load(tw1, lb);
+  const int ntask = rows * NG;
+  float2 pre[16];
+  auto fetch = [&](int task) {
+    const int lrow = task / NG, g = task - lrow * NG;
+    const float2* __restrict__ Xr = X + (size_t)lrow * M + g * CT + ca;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pre[r] = Xr[M2 * (la + T * r)];
+  };
+  int task = blockIdx.x;
+  if (task < ntask) fetch(task);
+  __syncthreads();
+  for (; task < ntask; task += gridDim.x) {
+    float2 v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) v[r] = pre[r];
+    if (task + (int)gridDim.x < ntask) fetch(task + gridDim.x);
+    // inverse column DFT
+    dft_dif<16, true>(v);
+    P0::store(v, lds + ca * CP, la);
+    __syncthreads();
+    P1::load(v, lds + cb * CP, lb);
+    {
+      float2 w1[16];
+      pt.expand(w1);
+      P1::template compute<true>(v, w1);
+    }
+    wave_sync();
+    P1::store(v, lds + cb * CP, lb);
+    __syncthreads();
+    const int lrow = task / NG, n2 = (task - lrow * NG) * CT + ca;
+    float2* __restrict__ zr = reinterpret_cast<float2*>(K + (size_t)lrow * (2 * (size_t)M)) + n2;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int n1 = la + T * r;
+      const float2 zv = lds[ca * CP + lds_pad(n1)];
+      const float2 zs = make_float2(zv.x * scale, zv.y * scale);
+      zr[M2 * n1] = zs;
+      v[r] = cmul(zs, w_M(twm, M2 * n1 + n2));        // z_n W_L^n, the input n1 = la + T r
+    }
+    __syncthreads();                                   // the column is read; reuse its LDS
+    // forward column DFT of the twisted sequence
+    dft_dif<16, false>(v);
+    P0::store(v, lds + ca * CP, la);
+    __syncthreads();
+    P1::load(v, lds + cb * CP, lb);
+    {
+      float2 w1[16];
+      pt.expand(w1);
+      P1::template compute<false>(v, w1);
+    }
+    wave_sync();
+    P1::store(v, lds + cb * CP, lb);
+    __syncthreads();
+    float2* __restrict__ Fr = F + (size_t)lrow * M + n2;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int k1 = la + T * r;
+      Fr[k1 * M2] = cmul(lds[ca * CP + lds_pad(k1)], w_M(twm, 2 * n2 * k1));
+    }
+    __syncthreads();
+  }
+}
+
+// Row step: the row DFTs of F, rows k1 and M1 - 1 - k1 in one 16-lane group
+// (the second with the mirrored lane index 15 - lt), so that bin
+// j = k1 + M1 k2 and its mirror p = L/2 - 1 - j = (M1 - 1 - k1) + M1 (255 - k2)
+// meet in one lane; then the odd bins S_{2j+1} and S_{2p+1} into the padded
+// spectrum's permuted layout (bin k at (k mod L/256) 256 + k div (L/256):
+// row 2 k1 + 1, column k2).
+template <int LOG2M>
+__global__ __launch_bounds__(kBigThreads) void big_rows_odd_kernel(
+    const float2* __restrict__ F, float2* __restrict__ spec, const float* __restrict__ D,
+    const float2* __restrict__ tw2, const float2* __restrict__ cs, int nh) {
+  using S = BigShape<LOG2M>;
+  using P0 = WPass<8, 0>;
+  using P1 = WPass<8, 1>;
+  static_assert(S::M2 == 256 && P0::T == 16 && P1::NS == 16, "256-point rows, 16 lanes");
+  constexpr int M = S::M, M1 = S::M1, M2 = S::M2, L = 2 * M;
+  constexpr int MP = lds_padded_size(M2);
+  constexpr int G = kBigThreads / 16;      // pair tasks per block
+  constexpr int TP = M1 / 2;               // pair tasks per channel
+  __shared__ float2 lds[G * 2 * MP];
+  const int tid = threadIdx.x, grp = tid >> 4, lt = tid & 15;
+  const int task = blockIdx.x * G + grp;
+  if (task >= nh * TP) return;
+  const int t = task % TP, h = task / TP;
+  const int ka = t, kb = M1 - 1 - t, lb = 15 - lt;
+  const float2* __restrict__ Fr = F + (size_t)h * M;
+  float2* __restrict__ bufA = lds + grp * 2 * MP;
+  float2* __restrict__ bufB = bufA + MP;
+  float2 za[16], zb[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    za[r] = Fr[ka * M2 + lt + 16 * r];
+    zb[r] = Fr[kb * M2 + lb + 16 * r];
+  }
+  PassTwiddles<8, 1> pta, ptb;
+  pta.load(tw2, lt);
+  ptb.load(tw2, lb);
+  dft_dif<16, false>(za);
+  dft_dif<16, false>(zb);
+  P0::store(za, bufA, lt);
+  P0::store(zb, bufB, lb);
+  // (cos, sin)(pi (2j + 1) / L) for j = ka + M1 lt; bin lt + 16 s turns it by pi s / 16
+  const float2 cs0 = cs[2 * ka + 1 + 2 * M1 * lt];
+  const float Dh = D ? D[h] : 0.f;
+  wave_sync();
+  P1::load(za, bufA, lt);
+  P1::load(zb, bufB, lb);
+  {
+    float2 w[16];
+    pta.expand(w);
+    P1::template compute<false>(za, w);
+    ptb.expand(w);
+    P1::template compute<false>(zb, w);
+  }
+  float2* __restrict__ sph = spec + (size_t)h * L;
+#pragma unroll
+  for (int s2 = 0; s2 < 16; ++s2) {
+    const int k2 = lt + 16 * s2;
+    const float2 fj = za[bitrev<4>(s2)], fp = zb[bitrev<4>(15 - s2)];
+    const float2 e = make_float2(0.5f * (fj.x + fp.x), 0.5f * (fj.y - fp.y));
+    const float2 o = make_float2(0.5f * (fj.y + fp.y), -0.5f * (fj.x - fp.x));
+    const float2 c = cmul(cs0, make_float2(kCos32[s2], kSin32[s2]));
+    // W_2L^{2j+1} = (cos, -sin); W_2L^{2p+1} = W_2L^{L - (2j+1)} = (-cos, -sin)
+    const float2 sj = cmul(make_float2(c.x, -c.y), o);
+    const float2 sp = cmul(make_float2(-c.x, -c.y), cconj(o));
+    sph[(2 * ka + 1) * M2 + k2] = make_float2(e.x + sj.x + Dh, e.y + sj.y);
+    sph[(2 * kb + 1) * M2 + (255 - k2)] = make_float2(e.x + sp.x + Dh, -e.y + sp.y);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers.  Intermediate rows live in the workspace's big buffer, in
 // logical row order (channel-major for the convolution: row = h*batch + b),
 // while u and y stay in their [batch][H][L] layout: the column kernels map a
@@ -504,18 +663,25 @@ static void big_kspec(const s4dplr_plan* p, const float* Ktime, const float* D, 
                       unsigned char* ws, hipStream_t s, int conj, bool half) {
   using S = BigShape<LOG2M>;
   if (!Ktime && half) {
-    // the workspace holds Y (M/2 points, the four-step order of an M/2-point
-    // transform) whose inverse transform, times 1/M, is the packed kernel
-    // z_n = K_2n + i K_2n+1: K in natural order
-    float2* Y = wat<float2>(ws, p->off_big);
+    // The workspace holds Y (M/2 points, the four-step order of an M/2-point
+    // transform) and the even bins of S; the inverse transform of Y, times
+    // 1/M, is the packed kernel z_n = K_2n + i K_2n+1 (K in natural order),
+    // and one more M/2-point transform of it gives the odd bins.
+    float2* Xr = wat<float2>(ws, p->off_big);
+    float2* F = wat<float2>(ws, p->off_khat);   // Y is consumed by the row step
     float* K = Kout ? Kout : wat<float>(ws, p->off_kbuf);
+    const float2* tw4 = wat<const float2>(ws, p->off_tw4);
     big_rows_kernel<LOG2M - 1, true, 2><<<rows_blocks<LOG2M - 1>(p->H), kBigThreads, 0, s>>>(
-        wat<const float2>(ws, p->off_khat), Y, wat<const float2>(ws, p->off_tw2),
-        wat<const float2>(ws, p->off_tw4), p->H);
-    big_cols_inv_kernel<LOG2M - 1, 2><<<col_blocks<LOG2M - 1>(p->H), kBigThreads, 0, s>>>(
-        Y, K, wat<const float2>(ws, p->off_tw1h), p->H, p->H, 1, 1.0f / (float)S::M);
-    Ktime = K;
-  } else if (!Ktime) {
+        wat<const float2>(ws, p->off_khat), Xr, wat<const float2>(ws, p->off_tw2), tw4, p->H);
+    big_cols_invfwd_kernel<LOG2M - 1><<<col_blocks<LOG2M - 1, 128>(p->H), 128, 0, s>>>(
+        Xr, K, F, wat<const float2>(ws, p->off_tw1h), tw4, p->H, 1.0f / (float)S::M);
+    constexpr int G = kBigThreads / 16, TP = BigShape<LOG2M - 1>::M1 / 2;
+    big_rows_odd_kernel<LOG2M - 1><<<(p->H * TP + G - 1) / G, kBigThreads, 0, s>>>(
+        F, wat<float2>(ws, p->off_coef), D, wat<const float2>(ws, p->off_tw2),
+        wat<const float2>(ws, p->off_cs), p->H);
+    return;
+  }
+  if (!Ktime) {
     // inverse transform of the generating function (permuted layout) -> K
     float2* Y = wat<float2>(ws, p->off_big);
     float* K = Kout ? Kout : wat<float>(ws, p->off_kbuf);

@@ -89,11 +89,15 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_kernel(
 // one contiguous run.
 // (Seven waves per SIMD, what the pole records' LDS allows: without the
 // bound the scheduler issues all four poles' record reads ahead, 107 VGPRs.)
+// The lane also writes the even bin of the padded spectrum that its Hermitian
+// part gives, S_2m = Xh_m + D, into `spec` (bin k at (k mod L/256) 256 +
+// k div (L/256); bin 0's slot holds the real pair (S_0, S_L)).
 template <bool DIAG, bool TIED>
 __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(7)))
 void cauchy_half_kernel(
     ParamPtrs pp, const float* __restrict__ tanT, const float2* __restrict__ cs,
-    float2* __restrict__ yhat, int N, int NP, int L) {
+    float2* __restrict__ yhat, float2* __restrict__ spec, const float* __restrict__ D, int N,
+    int NP, int L) {
   __shared__ float4 rec[kRec * kMaxPoles];
   __shared__ float2 red[kCauchyThreads / 64];
   const int h = blockIdx.y, tid = threadIdx.x;
@@ -146,6 +150,10 @@ void cauchy_half_kernel(
   const float2 t = cmul(cs[2 * m], csub(h1, h2));           // e^{2 pi i m / L} (Xh_m - Xh_{m+L/2})
   yhat[(size_t)h * H2 + (m % M1) * 256 + m / M1] =
       make_float2(h1.x + h2.x - t.y, h1.y + h2.y + t.x);
+  const float Dh = D ? D[h] : 0.f;
+  const int M1L = 2 * M1, k = 2 * m;
+  spec[(size_t)h * L + (k % M1L) * 256 + k / M1L] =
+      (l == 0 && !odd) ? make_float2(h1.x + Dh, h2.x + Dh) : make_float2(h1.x + Dh, h1.y);
 }
 
 // ---------------------------------------------------------------------------
@@ -1199,21 +1207,23 @@ static hipError_t launch_cauchy_to(const s4dplr_plan* p, const ParamPtrs& pp, fl
 }
 
 template <bool DIAG, bool TIED>
-static void cauchy_half_launch(const s4dplr_plan* p, const ParamPtrs& pp, unsigned char* ws,
-                               hipStream_t s) {
+static void cauchy_half_launch(const s4dplr_plan* p, const ParamPtrs& pp, const float* D,
+                               unsigned char* ws, hipStream_t s) {
   const dim3 grid(p->L / 2 / kCauchyThreads, p->H);
   cauchy_half_kernel<DIAG, TIED><<<grid, kCauchyThreads, 0, s>>>(
       pp, at<const float>(ws, p->off_tan), at<const float2>(ws, p->off_cs),
-      at<float2>(ws, p->off_khat), p->N, p->NP, p->L);
+      at<float2>(ws, p->off_khat), at<float2>(ws, p->off_coef), D, p->N, p->NP, p->L);
 }
 
-hipError_t launch_cauchy(const s4dplr_plan* p, const ParamPtrs& pp, unsigned char* ws,
-                         hipStream_t s) {
+// The generating function for stage 1 (rank 1).  L >= 32768: the packed
+// kernel's L/2-point spectrum and the even bins of the padded spectrum (D
+// folded in) instead of K-hat.
+static hipError_t launch_cauchy(const s4dplr_plan* p, const ParamPtrs& pp, const float* D,
+                                unsigned char* ws, hipStream_t s) {
   if (!lds_path(p)) {
-    // the four-step path: the spectrum of the packed kernel, L/2 points
-    if (p->flags & S4DPLR_DIAGONAL) cauchy_half_launch<true, false>(p, pp, ws, s);
-    else if (!pp.Q) cauchy_half_launch<false, true>(p, pp, ws, s);
-    else cauchy_half_launch<false, false>(p, pp, ws, s);
+    if (p->flags & S4DPLR_DIAGONAL) cauchy_half_launch<true, false>(p, pp, D, ws, s);
+    else if (!pp.Q) cauchy_half_launch<false, true>(p, pp, D, ws, s);
+    else cauchy_half_launch<false, false>(p, pp, D, ws, s);
     return hipGetLastError();
   }
   return launch_cauchy_to(p, pp, at<float2>(ws, p->off_khat), lds_path(p) ? 0 : p->L / 256, ws,
@@ -1347,9 +1357,9 @@ hipError_t launch_kernel_gen(const s4dplr_plan* p, const float* lam, const float
     S4_DISPATCH_LOG2L(kgen_launch, p, pp, D, nullptr, Kout, ws, s, 0);
     return hipGetLastError();
   }
-  hipError_t e = launch_cauchy(p, pp, ws, s);
+  hipError_t e = launch_cauchy(p, pp, D, ws, s);
   if (e != hipSuccess) return e;
-  // L >= 32768: launch_cauchy wrote the half-length spectrum Y
+  // L >= 32768: launch_cauchy wrote the half-length spectrum Y and the even bins
   return launch_kspec(p, nullptr, D, Kout, ws, s, 0, !lds_path(p));
 }
 

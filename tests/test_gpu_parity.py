@@ -173,8 +173,10 @@ def test_distinct_q(s4):
     assert _rel(K, Kr) <= TOL and _rel(y, yr) <= TOL
 
 
-def test_no_D_and_no_K_output(s4):
-    x = make_generic_inputs(H=2, N=8, L=1024, batch=3, seed=12)
+@pytest.mark.parametrize("L", [1024, 16384, 32768, 65536])
+def test_no_D_and_no_K_output(s4, L):
+    print(f"case: no D, no K output, L={L}", flush=True)
+    x = make_generic_inputs(H=2, N=8, L=L, batch=2, seed=12)
     K, y = run_forward(s4, x, with_D=False, write_K=False)
     assert K is None
     _, yr = oracle_forward(x, with_D=False)
