@@ -66,8 +66,8 @@ bool lds_path(const s4dplr_plan* p);
 hipError_t launch_kernel_gen(const s4dplr_plan* p, const float* lam, const float* P,
                              const float* Q, const float* B, const float* C, const float* dt,
                              const float* D, float* Kout, unsigned char* ws, hipStream_t s);
-// The generating function at the L roots of unity into khat [H][L] (natural
-// order when natural is set, else the order the plan's kernel spectrum reads).
+// The generating function at the L roots of unity into khat [H][L], natural
+// order.
 hipError_t launch_generating_function(const s4dplr_plan* p, const float* lam, const float* P,
                                       const float* Q, const float* B, const float* C,
                                       const float* dt, float* khat, unsigned char* ws,

@@ -37,14 +37,14 @@
 
 namespace s4 {
 
-// General kernel generation step: F frequencies per thread, 256 threads, one
-// channel per blockIdx.y.  perm_m1 > 0 stores the long path's transposed
-// layout: position p = k1*256 + k2 holds frequency l = k1 + perm_m1*k2.
+// General kernel generation step: the generating function at the L roots of
+// unity in natural order, F frequencies per thread, 256 threads, one channel
+// per blockIdx.y.
 
 template <int F, bool DIAG, bool TIED>
 __global__ __launch_bounds__(kCauchyThreads) void cauchy_kernel(
-    ParamPtrs pp, const float* __restrict__ tanT, float2* __restrict__ khat, int N, int NP, int L,
-    int perm_m1) {
+    ParamPtrs pp, const float* __restrict__ tanT, float2* __restrict__ khat, int N, int NP,
+    int L) {
   __shared__ float4 rec[kRec * kMaxPoles];
   __shared__ float2 red[kCauchyThreads / 64];
   const int h = blockIdx.y, tid = threadIdx.x;
@@ -53,14 +53,13 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_kernel(
   const float dt = pp.dt[h];
   const float2 nyq = make_float2(0.5f * dt * sum.x, 0.5f * dt * sum.y);
   const float two_dt = 2.0f / dt;
-  int l[F], pos[F];
+  int l[F];
   float T[F], G[F];
   float acc[F][8];
 #pragma unroll
   for (int f = 0; f < F; ++f) {
-    pos[f] = (blockIdx.x * F + f) * kCauchyThreads + tid;
-    l[f] = perm_m1 ? ((pos[f] >> 8) + perm_m1 * (pos[f] & 255)) : pos[f];
-    T[f] = pos[f] < L ? tanT[l[f]] : 0.f;
+    l[f] = (blockIdx.x * F + f) * kCauchyThreads + tid;
+    T[f] = l[f] < L ? tanT[l[f]] : 0.f;
     G[f] = two_dt * T[f];
 #pragma unroll
     for (int a = 0; a < 8; ++a) acc[f][a] = 0.f;
@@ -68,7 +67,7 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_kernel(
   cauchy_sums<F, DIAG, TIED>(rec, NP, G, acc);
 #pragma unroll
   for (int f = 0; f < F; ++f)
-    if (pos[f] < L) khat[(size_t)h * L + pos[f]] = cauchy_epilogue<DIAG>(acc[f], T[f], 2 * l[f] == L, nyq);
+    if (l[f] < L) khat[(size_t)h * L + l[f]] = cauchy_epilogue<DIAG>(acc[f], T[f], 2 * l[f] == L, nyq);
 }
 
 // The generating function reduced to what the time-domain kernel needs, for
@@ -1189,20 +1188,20 @@ static void kgen_launch(const s4dplr_plan* p, const ParamPtrs& pp, const float* 
 }
 
 static hipError_t launch_cauchy_to(const s4dplr_plan* p, const ParamPtrs& pp, float2* khat,
-                                   int perm_m1, unsigned char* ws, hipStream_t s) {
+                                   unsigned char* ws, hipStream_t s) {
   constexpr int F = 2;
   const int per_block = F * kCauchyThreads;
   dim3 grid((p->L + per_block - 1) / per_block, p->H);
   const float* tanT = at<const float>(ws, p->off_tan);
   if (p->flags & S4DPLR_DIAGONAL)
     cauchy_kernel<F, true, false><<<grid, kCauchyThreads, 0, s>>>(pp, tanT, khat, p->N, p->NP,
-                                                                  p->L, perm_m1);
+                                                                  p->L);
   else if (!pp.Q)   // Q tied to P: w11 = |P|^2 is real
     cauchy_kernel<F, false, true><<<grid, kCauchyThreads, 0, s>>>(pp, tanT, khat, p->N, p->NP,
-                                                                  p->L, perm_m1);
+                                                                  p->L);
   else
     cauchy_kernel<F, false, false><<<grid, kCauchyThreads, 0, s>>>(pp, tanT, khat, p->N, p->NP,
-                                                                   p->L, perm_m1);
+                                                                   p->L);
   return hipGetLastError();
 }
 
@@ -1226,8 +1225,7 @@ static hipError_t launch_cauchy(const s4dplr_plan* p, const ParamPtrs& pp, const
     else cauchy_half_launch<false, false>(p, pp, D, ws, s);
     return hipGetLastError();
   }
-  return launch_cauchy_to(p, pp, at<float2>(ws, p->off_khat), lds_path(p) ? 0 : p->L / 256, ws,
-                          s);
+  return launch_cauchy_to(p, pp, at<float2>(ws, p->off_khat), ws, s);
 }
 
 hipError_t launch_generating_function(const s4dplr_plan* p, const float* lam, const float* P,
@@ -1237,7 +1235,7 @@ hipError_t launch_generating_function(const s4dplr_plan* p, const float* lam, co
   const ParamPtrs pp = param_ptrs(lam, P, Q, B, C, dt);
   float2* out = reinterpret_cast<float2*>(khat);
   if (p->rank > 1) return launch_cauchy_rank(p, pp, out, 0, ws, s);
-  return launch_cauchy_to(p, pp, out, 0, ws, s);
+  return launch_cauchy_to(p, pp, out, ws, s);
 }
 
 template <int LOG2L>
