@@ -23,7 +23,9 @@ over several input/output buffer sets totalling more than 512 MB, so that the
 workload is launch-bound).  After the K timed steps each stage is timed alone
 with HIP events on the launch stream: kernel generation (stage 1), the
 generating function alone (the Cauchy kernel), and the convolution
-(``conv_apply``).  The CPU baseline runs the fp64 oracle on the host on a
+(``conv_apply``).  By default K = 50 timed steps after W = 5 warmup steps,
+and the per-step median and minimum come from K more steps, each between its
+own pair of events.  The CPU baseline runs the fp64 oracle on the host on a
 bounded sample of the headline workload (a subset of its channels, every
 batch row), on one thread and over a pool of worker processes.
 
@@ -696,7 +698,7 @@ def counters_sequence(args):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE,
                     help="headline workload: tiny | mid | long | s4d_lin | waveform "
@@ -830,7 +832,7 @@ def main() -> int:
             continue
         log(f"[bench] config {cw.describe()}")
         cb = Workbench(s4, torch, cw, dev)
-        configs[name], _ = config_figures(cb, min(args.steps, 20), min(args.warmup, 5))
+        configs[name], _ = config_figures(cb, min(args.steps, 50), min(args.warmup, 5))
         c = configs[name]
         log(f"[bench]   forward {c['forward_us']:.1f} us ({c['samples_per_s']:.3g} samples/s); "
             f"stage 1 {c['stage1_us']:.1f} us (frac {c['stage1_frac_fp32_peak']:.3f}); "
