@@ -86,11 +86,11 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_kernel(
 // b < 128) takes l = a + M1 b, so Y_l goes to 256 a + b and Y_{L/2-l} to
 // 256 (M1 - a) + 255 - b (256 - b for a = 0): each half of a wave stores
 // one contiguous run.
-// (Seven waves per SIMD, what the pole records' LDS allows: without the
-// bound the scheduler issues all four poles' record reads ahead, 107 VGPRs.)
 // The lane also writes the even bin of the padded spectrum that its Hermitian
 // part gives, S_2m = Xh_m + D, into `spec` (bin k at (k mod L/256) 256 +
 // k div (L/256); bin 0's slot holds the real pair (S_0, S_L)).
+// (Seven waves per SIMD, what the pole records' LDS allows: without the
+// bound the scheduler issues all four poles' record reads ahead, 107 VGPRs.)
 template <bool DIAG, bool TIED>
 __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(7)))
 void cauchy_half_kernel(
