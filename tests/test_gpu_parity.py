@@ -291,6 +291,17 @@ def test_pole_counts(s4, N):
     assert _rel(K, Kr) <= TOL and _rel(y, yr) <= TOL
 
 
+@pytest.mark.parametrize("N,L", [(13, 4096), (1, 32768), (256, 32768), (3, 65536)])
+def test_pole_counts_long(s4, N, L):
+    # the frequency-parallel Cauchy kernels (records padded to a multiple of
+    # four poles, up to the 256-pole limit) and the half-length long path
+    print(f"case: generic H=2 N={N} L={L} batch=2", flush=True)
+    x = make_generic_inputs(H=2, N=N, L=L, batch=2, seed=300 + N + L % 89)
+    K, y = run_forward(s4, x)
+    Kr, yr = oracle_forward(x)
+    assert _rel(K, Kr) <= TOL and _rel(y, yr) <= TOL
+
+
 @pytest.mark.parametrize("L", [2048, 16384, 65536])
 def test_diagonal_and_distinct_q_long(s4, L):
     print(f"case: diagonal and distinct-Q L={L}", flush=True)
