@@ -509,6 +509,12 @@ def roofline(w, t_gen, t_cauchy, t_conv):
           "traffic": traffic.get(s1_name), "algorithmic_flops_per_launch": F1,
           "launch_us": s1_t * 1e6,
           "stage1_us": t_gen * 1e6, "stage1_frac": F1 / t_gen / 1e12 / FP32_PEAK_TFLOPS}
+    if w.L >= 32768:
+        s1["note"] = ("launch_us times the generating-function entry point (cauchy_kernel, "
+                      "HIP events). The forward pass runs the same sums in cauchy_half_kernel, "
+                      "which also writes the half-length spectrum and the even spectrum bins "
+                      "and has no entry point of its own; rocprofv3 averages of both kernels "
+                      "are in profiles/<workload>_forward_kernel_trace.md")
     cv = {"kernel": " + ".join(conv_names), "bound": "hbm", "achieved": Q2 / t_conv / 1e9,
           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": Q2 / t_conv / 1e9 / HBM_PEAK_GBS,
           "traffic": conv_traffic, "algorithmic_bytes_per_launch": Q2,
