@@ -73,11 +73,12 @@ def oracle_forward(x, diagonal=False, with_D=True):
 
 # ---- the five workloads at their full sizes --------------------------------
 
+@pytest.mark.parametrize("seed", [0, 1])
 @pytest.mark.parametrize("name", ["tiny", "mid", "long", "s4d_lin", "waveform"])
-def test_workload_parity(s4, name):
+def test_workload_parity(s4, name, seed):
     w = WORKLOADS[name]
-    print(f"case: workload {w.describe()}", flush=True)
-    x = make_inputs(name)
+    print(f"case: workload {w.describe()} seed {seed}", flush=True)
+    x = make_inputs(name, seed=seed)
     K, y = run_forward(s4, x, diagonal=w.diagonal)
     Kr, yr = oracle_forward(x, diagonal=w.diagonal)
     eK, ey = _rel(K, Kr), _rel(y, yr)
