@@ -292,6 +292,18 @@ def test_pole_counts(s4, N):
     assert _rel(K, Kr) <= TOL and _rel(y, yr) <= TOL
 
 
+@pytest.mark.parametrize("L,dt", [(1024, 1e-6), (16384, 1e-5), (65536, 1e-6), (65536, 10.0)])
+def test_extreme_step_sizes(s4, L, dt):
+    # step sizes far outside the workloads' ranges: G = (2/dt) tan(pi l / L)
+    # reaches about 4e10 at dt = 1e-6, and at dt = 10 the poles sit near z = -1
+    print(f"case: HiPPO poles, dt={dt:g}, L={L}", flush=True)
+    x = make_inputs("waveform", H=4, batch=1, L=L, seed=3)
+    x["dt"] = np.full_like(x["dt"], dt)
+    K, y = run_forward(s4, x)
+    Kr, yr = oracle_forward(x)
+    assert _rel(K, Kr) <= TOL and _rel(y, yr) <= TOL
+
+
 @pytest.mark.parametrize("N,L", [(13, 4096), (1, 32768), (256, 32768), (3, 65536)])
 def test_pole_counts_long(s4, N, L):
     # the frequency-parallel Cauchy kernels (records padded to a multiple of
