@@ -304,6 +304,18 @@ def test_extreme_step_sizes(s4, L, dt):
     assert _rel(K, Kr) <= TOL and _rel(y, yr) <= TOL
 
 
+@pytest.mark.parametrize("L,re", [(1024, -1e-4), (65536, -1e-4)])
+def test_poles_near_the_imaginary_axis(s4, L, re):
+    # |Re Lambda| small: r = 1/((Re Lambda)^2 + y^2) reaches 1e8 where the
+    # frequency meets a pole, and the Woodbury denominator is near its bound
+    print(f"case: generic poles with Re Lambda = {re:g}, L={L}", flush=True)
+    x = make_generic_inputs(H=4, N=16, L=L, batch=1, seed=21)
+    x["lam"][..., 0] = re
+    K, y = run_forward(s4, x)
+    Kr, yr = oracle_forward(x)
+    assert _rel(K, Kr) <= TOL and _rel(y, yr) <= TOL
+
+
 @pytest.mark.parametrize("N,L", [(13, 4096), (1, 32768), (256, 32768), (3, 65536)])
 def test_pole_counts_long(s4, N, L):
     # the frequency-parallel Cauchy kernels (records padded to a multiple of
