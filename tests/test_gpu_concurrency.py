@@ -22,7 +22,18 @@ def s4():
     return s4
 
 
-def _forward(s4, plan, x, ws, stream):
+def _workspace(s4, plan, stream):
+    """A workspace of the plan's own (Plan.workspace caches a single one)."""
+    import torch
+    store = torch.empty(plan.workspace_bytes + 256, dtype=torch.uint8, device="cuda")
+    off = (-store.data_ptr()) % 256
+    ws = store[off: off + plan.workspace_bytes]
+    s4.plan_init(plan.handle, ws, stream)
+    return store, ws
+
+
+def _buffers(x):
+    """The inputs on the device and empty K, y for them."""
     import torch
     t = {k: torch.from_numpy(np.ascontiguousarray(x[k])).cuda() for k in
          ("lam", "P", "B", "C", "dt", "D", "u")}
@@ -42,8 +53,8 @@ def test_one_plan_two_threads(s4, H, N, L, batch):
     # reference: the two problems one after the other on the current stream
     ref = []
     for x in xs:
-        ws = plan.workspace()
-        t, K, y = _forward(s4, plan, x, ws, None)
+        _, ws = _workspace(s4, plan, None)
+        t, K, y = _buffers(x)
         s4.forward(plan, t["lam"], t["P"], None, t["B"], t["C"], t["dt"], t["D"], t["u"], K, y,
                    ws, None)
         torch.cuda.synchronize()
@@ -55,8 +66,8 @@ def test_one_plan_two_threads(s4, H, N, L, batch):
         try:
             stream = torch.cuda.Stream()
             with torch.cuda.stream(stream):
-                ws = plan.workspace(stream)
-                t, K, y = _forward(s4, plan, xs[i], ws, stream)
+                store, ws = _workspace(s4, plan, stream)
+                t, K, y = _buffers(xs[i])
                 for rep in range(4):
                     y.fill_(float("nan"))
                     s4.forward(plan, t["lam"], t["P"], None, t["B"], t["C"], t["dt"], t["D"],
