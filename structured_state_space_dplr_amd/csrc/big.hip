@@ -476,14 +476,15 @@ __global__ __launch_bounds__(kBigThreads) void big_rows_pair_kernel(
 // Column step (M = L/2 points per row, four-step M1 x 256): the inverse
 // column DFTs after big_rows_kernel, z times `scale` out as K (natural
 // order), then z_n W_L^n through the forward column DFTs, times the four-step
-// twiddle W_M^{n2 k1}, into F[row][k1][n2].  128-thread blocks: half the
-// columns per task of the other column steps, twice the tasks (the waveform
-// workload's 64 rows give 1024), 3 us faster than 256 threads there.
+// twiddle W_M^{n2 k1}, into F[row][k1][n2].  One-wave blocks, one task each
+// (a quarter of the columns per task of the other column steps; the
+// waveform workload's 64 rows give 2048): at waveform 15.9 us against 17.0
+// with 128 threads and 20.9 with 256.
 template <int LOG2M>
-__global__ __launch_bounds__(128) void big_cols_invfwd_kernel(
+__global__ __launch_bounds__(64) void big_cols_invfwd_kernel(
     const float2* __restrict__ X, float* __restrict__ K, float2* __restrict__ F,
     const float2* __restrict__ tw1, const float2* __restrict__ tw4, int rows, float scale) {
-  using C = ColShape<LOG2M, 128>;
+  using C = ColShape<LOG2M, 64>;
   using P0 = WPass<C::LOG2M1, 0>;
   using P1 = WPass<C::LOG2M1, 1>;
   constexpr int M = BigShape<LOG2M>::M, M2 = C::M2, T = C::T, CT = C::CT, NG = C::NG,
@@ -493,7 +494,7 @@ __global__ __launch_bounds__(128) void big_cols_invfwd_kernel(
   const int tid = threadIdx.x;
   const int ca = tid % CT, la = tid / CT;
   const int cb = tid / T, lb = tid % T;
-  load_twM(twm, tw4, tid, 128);
+  load_twM(twm, tw4, tid, 64);
   PassTwiddles<C::LOG2M1, 1> pt;
   pt.load(tw1, lb);
   const int ntask = rows * NG;
@@ -673,7 +674,7 @@ static void big_kspec(const s4dplr_plan* p, const float* Ktime, const float* D, 
     const float2* tw4 = wat<const float2>(ws, p->off_tw4);
     big_rows_kernel<LOG2M - 1, true, 2><<<rows_blocks<LOG2M - 1>(p->H), kBigThreads, 0, s>>>(
         wat<const float2>(ws, p->off_khat), Xr, wat<const float2>(ws, p->off_tw2), tw4, p->H);
-    big_cols_invfwd_kernel<LOG2M - 1><<<col_blocks<LOG2M - 1, 128>(p->H), 128, 0, s>>>(
+    big_cols_invfwd_kernel<LOG2M - 1><<<(p->H * ColShape<LOG2M - 1, 64>::NG), 64, 0, s>>>(
         Xr, K, F, wat<const float2>(ws, p->off_tw1h), tw4, p->H, 1.0f / (float)S::M);
     constexpr int G = kBigThreads / 16, TP = BigShape<LOG2M - 1>::M1 / 2;
     big_rows_odd_kernel<LOG2M - 1><<<(p->H * TP + G - 1) / G, kBigThreads, 0, s>>>(
