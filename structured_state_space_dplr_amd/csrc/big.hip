@@ -478,8 +478,8 @@ __global__ __launch_bounds__(kBigThreads) void big_rows_pair_kernel(
 // order), then z_n W_L^n through the forward column DFTs, times the four-step
 // twiddle W_M^{n2 k1}, into F[row][k1][n2].  One-wave blocks, one task each
 // (a quarter of the columns per task of the other column steps; the
-// waveform workload's 64 rows give 2048): at waveform 15.9 us against 17.0
-// with 128 threads and 20.9 with 256.
+// waveform workload's 64 rows give 2048): at waveform 16.8 us against
+// 17.1-17.2 with 128 threads and 20.9 with 256.
 template <int LOG2M>
 __global__ __launch_bounds__(64) void big_cols_invfwd_kernel(
     const float2* __restrict__ X, float* __restrict__ K, float2* __restrict__ F,
