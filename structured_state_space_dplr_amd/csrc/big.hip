@@ -301,6 +301,10 @@ static int rows_blocks(int rows) {
 //          slot holds the two real values (S_0, S_M).
 // Storing S (8 B per bin) rather than alpha and beta (16 B) halves the
 // spectrum's traffic in both kernels.
+// Registers and LDS: the two rows go through one LDS buffer per group in
+// turn, and S is read inside the weighting loop, two values per bin pair,
+// so that the kernel stays under 168 VGPRs and 40 KB of LDS per block: three
+// waves per SIMD instead of two.
 // ---------------------------------------------------------------------------
 template <int LOG2M, bool CONV>
 __global__ __launch_bounds__(kBigThreads) void big_rows_pair_kernel(
@@ -315,7 +319,7 @@ __global__ __launch_bounds__(kBigThreads) void big_rows_pair_kernel(
   constexpr int MP = lds_padded_size(M2);
   constexpr int G = kBigThreads / 16;      // pair tasks per block
   constexpr int TP = M1 / 2 + 1;           // pair tasks per logical row
-  __shared__ float2 lds[G * 2 * MP];
+  __shared__ float2 lds[G * MP];
   __shared__ TwM twm;
   const int tid = threadIdx.x, grp = tid >> 4, lt = tid & 15;
   if constexpr (CONV) {
@@ -330,8 +334,7 @@ __global__ __launch_bounds__(kBigThreads) void big_rows_pair_kernel(
   const int lb = (t == 0) ? ((16 - lt) & 15) : 15 - lt;
   const bool sp = (t == 0) && (lt == 0);
   float2* __restrict__ Yr = Y + (size_t)(h * batch + b) * M;
-  float2* __restrict__ bufA = lds + grp * 2 * MP;
-  float2* __restrict__ bufB = bufA + MP;
+  float2* __restrict__ bufA = lds + grp * MP;
   float2 za[16], zb[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -345,20 +348,13 @@ __global__ __launch_bounds__(kBigThreads) void big_rows_pair_kernel(
   dft_dif<16, false>(za);
   dft_dif<16, false>(zb);
   P0::store(za, bufA, lt);
-  P0::store(zb, bufB, lb);
-  float2 sa_[16], sb_[16];
-  if constexpr (CONV) {
-    const float2* __restrict__ sph = specp + (size_t)h * M;
-#pragma unroll
-    for (int s2 = 0; s2 < 16; ++s2) {
-      sa_[s2] = sph[ka * M2 + lt + 16 * s2];
-      sb_[s2] = sph[kb * M2 + lb + 16 * s2];
-    }
-  }
   const float2 cs0 = cs[ka + M1 * lt];
   wave_sync();
   P1::load(za, bufA, lt);
-  P1::load(zb, bufB, lb);
+  wave_sync();
+  P0::store(zb, bufA, lb);
+  wave_sync();
+  P1::load(zb, bufA, lb);
   {
     float2 w[16];
     pta.expand(w);
@@ -390,27 +386,37 @@ __global__ __launch_bounds__(kBigThreads) void big_rows_pair_kernel(
       return cadd(cmul(al, z), cmul(be, cconj(zp)));
     };
     float2 oa[16], ob[16];
+    const float2* __restrict__ spa = specp + (size_t)h * M + ka * M2 + lt;
+    const float2* __restrict__ spb = specp + (size_t)h * M + kb * M2 + lb;
 #pragma unroll
     for (int s2 = 0; s2 < 16; ++s2) {
-      const int ps = sp ? ((16 - s2) & 15) : 15 - s2;   // partner of row-ka bin s2 in row kb
-      float2 S = sa_[s2], Sp = sb_[ps];
+      // row-ka bin s2 and its partner, row-kb bin 15 - s2, give oa[s2] and
+      // ob[15 - s2] from the same four values.  The sp lane's partner of
+      // bin s2 is its own bin (16 - s2) mod 16 of row 0 instead; that task
+      // keeps only row ka, so its ob may take that S value as well.
+      const int ps = sp ? ((16 - s2) & 15) : 15 - s2;
+      const float2 Sa = spa[16 * s2], Sb = spb[16 * ps];
+      const float2 ca = cmul(cs0, make_float2(kCos32[s2], kSin32[s2]));
+      float2 S = Sa, Sp = Sb;
       if (sp && s2 == 0) {   // bin 0: the slot holds (S_0, S_M), both real
-        S = make_float2(sa_[0].x, 0.f);
-        Sp = make_float2(sa_[0].y, 0.f);
+        S = make_float2(Sa.x, 0.f);
+        Sp = make_float2(Sa.y, 0.f);
       }
-      oa[s2] = weigh(za[bitrev<4>(s2)], pz[s2], S, Sp, csa[s2]);
-      const float2 cb_ = make_float2(-csa[15 - s2].x, csa[15 - s2].y);
-      ob[s2] = weigh(zb[bitrev<4>(s2)], za[bitrev<4>(15 - s2)], sb_[s2], sa_[15 - s2], cb_);
+      oa[s2] = weigh(za[bitrev<4>(s2)], pz[s2], S, Sp, ca);
+      ob[15 - s2] = weigh(zb[bitrev<4>(15 - s2)], za[bitrev<4>(s2)], Sb, Sa,
+                          make_float2(-ca.x, ca.y));
     }
     // inverse pass 0: input x[lt + 16 r] = bin lt + 16 r, already in this lane
     dft_dif<16, true>(oa);
     dft_dif<16, true>(ob);
     wave_sync();
     P0::store(oa, bufA, lt);
-    P0::store(ob, bufB, lb);
     wave_sync();
     P1::load(oa, bufA, lt);
-    P1::load(ob, bufB, lb);
+    wave_sync();
+    P0::store(ob, bufA, lb);
+    wave_sync();
+    P1::load(ob, bufA, lb);
     {
       float2 w[16];
       pta.expand(w);
