@@ -37,6 +37,19 @@
 
 namespace s4 {
 
+// Convolution weights of bin j of the padded spectrum from S_j, its partner
+// S_{L-j} and (c, s) = (cos, sin)(pi j / L), with sc = 1 / (2L):
+//   alpha_j = sc ((1 - s) S_j + (1 + s) conj(S_{L-j})),
+//   beta_j  = sc i c (S_j - conj(S_{L-j})),
+// returned as (alpha, beta).  The convolution's spectral step is then
+// Z'_j = alpha_j Z_j + beta_j conj(Z_{L-j}) on the packed row's transform.
+__device__ __forceinline__ float4 bin_weights(float2 sj, float2 sm, float2 csj, float sc) {
+  const float a = sc * (1.0f - csj.y), b = sc * (1.0f + csj.y), c = sc * csj.x;
+  const float2 al = make_float2(fmaf(a, sj.x, b * sm.x), fmaf(a, sj.y, -b * sm.y));
+  const float2 df = make_float2(sj.x - sm.x, sj.y + sm.y);   // S_j - conj(S_{L-j})
+  return make_float4(al.x, al.y, -c * df.y, c * df.x);
+}
+
 // General kernel generation step: the generating function at the L roots of
 // unity in natural order, F frequencies per thread, 256 threads, one channel
 // per blockIdx.y.
@@ -198,18 +211,8 @@ __device__ __forceinline__ void weights_pair(const float2* __restrict__ Zb, floa
     sj.y = -sj.y;
     sm.y = -sm.y;
   }
-  {
-    const float a = sc * (1.0f - csj.y), b = sc * (1.0f + csj.y), c = sc * csj.x;
-    const float2 al = make_float2(fmaf(a, sj.x, b * sm.x), fmaf(a, sj.y, -b * sm.y));
-    const float2 df = make_float2(sj.x - sm.x, sj.y + sm.y);   // S_j - conj(S_m)
-    cf[j] = make_float4(al.x, al.y, -c * df.y, c * df.x);
-  }
-  if (j != 0 && jm != j) {
-    const float a = sc * (1.0f - csm.y), b = sc * (1.0f + csm.y), c = sc * csm.x;
-    const float2 al = make_float2(fmaf(a, sm.x, b * sj.x), fmaf(a, sm.y, -b * sj.y));
-    const float2 df = make_float2(sm.x - sj.x, sm.y + sj.y);
-    cf[jm] = make_float4(al.x, al.y, -c * df.y, c * df.x);
-  }
+  cf[j] = bin_weights(sj, sm, csj, sc);
+  if (j != 0 && jm != j) cf[jm] = bin_weights(sm, sj, csm, sc);
 }
 
 // exp(-i pi idx / L) from the (cos, sin)(pi j / L) table, 0 <= idx < 2L
@@ -560,18 +563,8 @@ __global__ __launch_bounds__(KspecShape<LOG2L>::NT) void kspec_kernel(
       sj.y = -sj.y;
       sm.y = -sm.y;
     }
-    {
-      const float a = sc * (1.0f - csj.y), b = sc * (1.0f + csj.y), c = sc * csj.x;
-      const float2 al = make_float2(fmaf(a, sj.x, b * sm.x), fmaf(a, sj.y, -b * sm.y));
-      const float2 df = make_float2(sj.x - sm.x, sj.y + sm.y);   // S_j - conj(S_m)
-      cf[j] = make_float4(al.x, al.y, -c * df.y, c * df.x);
-    }
-    if (j != 0 && jm != j) {
-      const float a = sc * (1.0f - csm.y), b = sc * (1.0f + csm.y), c = sc * csm.x;
-      const float2 al = make_float2(fmaf(a, sm.x, b * sj.x), fmaf(a, sm.y, -b * sj.y));
-      const float2 df = make_float2(sm.x - sj.x, sm.y + sj.y);
-      cf[jm] = make_float4(al.x, al.y, -c * df.y, c * df.x);
-    }
+    cf[j] = bin_weights(sj, sm, csj, sc);
+    if (j != 0 && jm != j) cf[jm] = bin_weights(sm, sj, csm, sc);
   }
 }
 
