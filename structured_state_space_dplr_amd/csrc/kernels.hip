@@ -1039,8 +1039,12 @@ __global__ __launch_bounds__(RowConvShape<LOG2M>::NTHR) void conv_rows_kernel(
     roff = ((size_t)b * H + h) * M;
     return act;
   };
+  // the next row's input in flight during the inverse transform, except at
+  // M = 4096, where its 16 registers buy a third wave per SIMD instead (161
+  // instead of 178 VGPRs with the weights cached)
+  constexpr bool kPrefetch = LOG2M != 12;
   float2 upre[8];
-  {
+  if constexpr (kPrefetch) {
     int h0;
     size_t r0;
     const bool a0 = row_of(gb * groups_per_block, h0, r0);
@@ -1060,8 +1064,14 @@ __global__ __launch_bounds__(RowConvShape<LOG2M>::NTHR) void conv_rows_kernel(
     size_t roff;
     const bool active = row_of(g, h, roff);
     float2 v[16];
+    if constexpr (kPrefetch) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) v[r] = upre[r];
+      for (int r = 0; r < 8; ++r) v[r] = upre[r];
+    } else {
+      const float2* __restrict__ ur = reinterpret_cast<const float2*>(u + (active ? roff : 0));
+#pragma unroll
+      for (int r = 0; r < 8; ++r) v[r] = active ? ur[lt + T * r] : make_float2(0.f, 0.f);
+    }
     if constexpr (kCache) {
       if (h != hc) {
         const float4* __restrict__ cf = coef + (size_t)h * M;
@@ -1107,7 +1117,7 @@ __global__ __launch_bounds__(RowConvShape<LOG2M>::NTHR) void conv_rows_kernel(
       }
     }
     // next row's input, in flight during the inverse transform
-    if (gi + 1 < groups_per_block && g + 1 < ngroups) {
+    if (kPrefetch && gi + 1 < groups_per_block && g + 1 < ngroups) {
       int hn;
       size_t rn;
       const bool an = row_of(g + 1, hn, rn);
@@ -1274,10 +1284,13 @@ static void conv_launch(const s4dplr_plan* p, const float* u, float* y, unsigned
     using R = RowConvShape<LOG2L>;
     const int rows = p->batch * p->H;
     const int ngroups = (rows + R::RPB - 1) / R::RPB;
-    // blocks resident per CU, limited by LDS (160 KB) and 32 waves
+    // blocks resident per CU, limited by LDS (160 KB) and 32 waves; at
+    // L = 4096 by registers (three waves per SIMD, three blocks per CU):
+    // persistent blocks sized to that ran 2-3% faster than two rounds of
+    // four-per-CU blocks
     constexpr int by_lds = (160 * 1024) / (R::RPB * R::MP * 8);
     constexpr int by_waves = 32 / (R::NTHR / 64);
-    constexpr int per_cu = by_lds < by_waves ? by_lds : by_waves;
+    constexpr int per_cu = LOG2L == 12 ? 3 : (by_lds < by_waves ? by_lds : by_waves);
     // Persistent blocks, one round of the resident capacity; at one block per
     // CU (L = 16384) two rounds: 2 rows per block at 1024 rows ran 3.5% faster
     // than 4 (one round) and than 1 or 3.
