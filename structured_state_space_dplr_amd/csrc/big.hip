@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kBigThreads, 4) void big_cols_fwd_kernel(
     const float2* __restrict__ z =
         reinterpret_cast<const float2*>(x + mem_row(lrow, H, batch) * M) + g * CT + ca;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) pre[r] = z[M2 * (la + T * r)];   // n1 < M1/2
+    for (int r = 0; r < 8; ++r) pre[r] = load_stream(&z[M2 * (la + T * r)]);   // n1 < M1/2
   };
   int task = blockIdx.x;
   if (task < ntask) fetch(task);
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kBigThreads, 4) void big_cols_inv_kernel(
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const int n1 = la + T * r;     // < M1/2
-        yr[M2 * n1] = lds[ca * CP + lds_pad(n1)];
+        store_stream(&yr[M2 * n1], lds[ca * CP + lds_pad(n1)]);
       }
     } else {
       float* __restrict__ kr = out + mem_row(lrow, H, batch) * M + n2;

@@ -112,6 +112,22 @@ __device__ __forceinline__ int pad_shift(int x, int c) {
   return lds_pad(x + c) - lds_pad(x);
 }
 
+// Streaming accesses for data a launch touches once: the convolution's input
+// u and output y.  The non-temporal hint keeps them from displacing what is
+// reused from the caches (the spectral weights, shared by a channel's batch
+// rows, and the four-step intermediate at L >= 32768).
+typedef float f2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float2 load_stream(const float2* p) {
+  const f2v v = __builtin_nontemporal_load(reinterpret_cast<const f2v*>(p));
+  return make_float2(v.x, v.y);
+}
+__device__ __forceinline__ void store_stream(float2* p, float2 x) {
+  f2v v;
+  v.x = x.x;
+  v.y = x.y;
+  __builtin_nontemporal_store(v, reinterpret_cast<f2v*>(p));
+}
+
 // Orders this wave's LDS accesses before and after the call.
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -700,7 +700,7 @@ __global__ __launch_bounds__(kWaveConvThreads) void conv_wave_kernel(
     const bool a0 = row_of(gw * groups_per_wave, h0, r0);
     const float2* __restrict__ ur = reinterpret_cast<const float2*>(u + (a0 ? r0 : 0));
 #pragma unroll
-    for (int r = 0; r < 8; ++r) upre[r] = ur[lt + T * r];
+    for (int r = 0; r < 8; ++r) upre[r] = load_stream(&ur[lt + T * r]);
     if (!a0) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) upre[r] = make_float2(0.f, 0.f);
@@ -771,7 +771,7 @@ __global__ __launch_bounds__(kWaveConvThreads) void conv_wave_kernel(
       const bool an = row_of(g + 1, hn, rn);
       const float2* __restrict__ ur = reinterpret_cast<const float2*>(u + (an ? rn : 0));
 #pragma unroll
-      for (int r = 0; r < 8; ++r) upre[r] = ur[lt + T * r];
+      for (int r = 0; r < 8; ++r) upre[r] = load_stream(&ur[lt + T * r]);
       if (!an) {
 #pragma unroll
         for (int r = 0; r < 8; ++r) upre[r] = make_float2(0.f, 0.f);
@@ -798,7 +798,7 @@ __global__ __launch_bounds__(kWaveConvThreads) void conv_wave_kernel(
       const int j = lt + q * T;                   // j < NS in the last pass
 #pragma unroll
       for (int s2 = 0; s2 < LP::R / 2; ++s2)
-        if (active) yr[j + s2 * LP::NS] = v[q * LP::R + bitrev<LP::RL>(s2)];
+        if (active) store_stream(&yr[j + s2 * LP::NS], v[q * LP::R + bitrev<LP::RL>(s2)]);
     }
     wave_sync();
   }
@@ -864,7 +864,7 @@ __global__ __launch_bounds__(kWaveConvThreads) void conv_pair1024_kernel(
     const bool a0 = row_of(gw * groups_per_wave, h0, r0);
     const float2* __restrict__ ur = reinterpret_cast<const float2*>(u + (a0 ? r0 : 0));
 #pragma unroll
-    for (int r = 0; r < 8; ++r) upre[r] = a0 ? ur[lt + T * r] : make_float2(0.f, 0.f);
+    for (int r = 0; r < 8; ++r) upre[r] = a0 ? load_stream(&ur[lt + T * r]) : make_float2(0.f, 0.f);
   }
   float4 cw[16];
   int hc = -1;
@@ -912,7 +912,7 @@ __global__ __launch_bounds__(kWaveConvThreads) void conv_pair1024_kernel(
       const bool an = row_of(g + 1, hn, rn);
       const float2* __restrict__ ur = reinterpret_cast<const float2*>(u + (an ? rn : 0));
 #pragma unroll
-      for (int r = 0; r < 8; ++r) upre[r] = an ? ur[lt + T * r] : make_float2(0.f, 0.f);
+      for (int r = 0; r < 8; ++r) upre[r] = an ? load_stream(&ur[lt + T * r]) : make_float2(0.f, 0.f);
     }
     // spectral weights in registers: Z'_j = alpha_j Z_j + beta_j conj(Z_{M-j})
     float2 zs[16];
@@ -973,7 +973,7 @@ __global__ __launch_bounds__(kWaveConvThreads) void conv_pair1024_kernel(
       float2* __restrict__ yr = reinterpret_cast<float2*>(y + roff);
 #pragma unroll
       for (int mp = 0; mp < 8; ++mp)
-        if (active) yr[n1 + 4 * m + 64 * mp] = v[bitrev<4>(mp)];
+        if (active) store_stream(&yr[n1 + 4 * m + 64 * mp], v[bitrev<4>(mp)]);
     }
     wave_sync();
   }
@@ -1050,7 +1050,7 @@ __global__ __launch_bounds__(RowConvShape<LOG2M>::NTHR) void conv_rows_kernel(
     const bool a0 = row_of(gb * groups_per_block, h0, r0);
     const float2* __restrict__ ur = reinterpret_cast<const float2*>(u + (a0 ? r0 : 0));
 #pragma unroll
-    for (int r = 0; r < 8; ++r) upre[r] = a0 ? ur[lt + T * r] : make_float2(0.f, 0.f);
+    for (int r = 0; r < 8; ++r) upre[r] = a0 ? load_stream(&ur[lt + T * r]) : make_float2(0.f, 0.f);
   }
   // weights of the thread's bins, held across the rows of a channel where the
   // registers allow it (M <= 4096)
@@ -1070,7 +1070,7 @@ __global__ __launch_bounds__(RowConvShape<LOG2M>::NTHR) void conv_rows_kernel(
     } else {
       const float2* __restrict__ ur = reinterpret_cast<const float2*>(u + (active ? roff : 0));
 #pragma unroll
-      for (int r = 0; r < 8; ++r) v[r] = active ? ur[lt + T * r] : make_float2(0.f, 0.f);
+      for (int r = 0; r < 8; ++r) v[r] = active ? load_stream(&ur[lt + T * r]) : make_float2(0.f, 0.f);
     }
     if constexpr (kCache) {
       if (h != hc) {
@@ -1123,7 +1123,7 @@ __global__ __launch_bounds__(RowConvShape<LOG2M>::NTHR) void conv_rows_kernel(
       const bool an = row_of(g + 1, hn, rn);
       const float2* __restrict__ ur = reinterpret_cast<const float2*>(u + (an ? rn : 0));
 #pragma unroll
-      for (int r = 0; r < 8; ++r) upre[r] = an ? ur[lt + T * r] : make_float2(0.f, 0.f);
+      for (int r = 0; r < 8; ++r) upre[r] = an ? load_stream(&ur[lt + T * r]) : make_float2(0.f, 0.f);
     }
     __syncthreads();                             // all partner reads done
     WPass<LOG2M, 0>::template compute<true>(v, z);
@@ -1143,7 +1143,7 @@ __global__ __launch_bounds__(RowConvShape<LOG2M>::NTHR) void conv_rows_kernel(
       const int j = lt + q * T;                   // j < NS in the last pass
 #pragma unroll
       for (int s2 = 0; s2 < FL::R / 2; ++s2)
-        if (active) yr[j + s2 * FL::NS] = v[q * FL::R + bitrev<FL::RL>(s2)];
+        if (active) store_stream(&yr[j + s2 * FL::NS], v[q * FL::R + bitrev<FL::RL>(s2)]);
     }
   }
 }
