@@ -36,7 +36,10 @@
  *
  * Limits: L a power of two in [2, 65536] (so 2L <= 131072); 1 <= N <= 256;
  * H >= 1; batch >= 1; batch * H * L < 2^31.  The workspace is at least
- * s4dplr_plan_workspace_bytes() bytes and 256-byte aligned.
+ * s4dplr_plan_workspace_bytes() bytes and 256-byte aligned.  Every other
+ * device buffer is 8-byte aligned (the kernels move complex values and real
+ * samples in pairs); an entry point that gets one that is not returns
+ * S4DPLR_ERR_ALIGN before enqueueing anything.
  *
  * Preconditions not checked on the device: Re(Lambda_n) < 0 (a stable
  * system: "The S4 kernel, from scratch", section 6 keeps the real parts
@@ -71,7 +74,8 @@ typedef enum s4dplr_status {
   S4DPLR_ERR_UNSUPPORTED = 4, /* unknown flag bits                               */
   S4DPLR_ERR_HIP = 5,         /* HIP runtime error while enqueueing              */
   S4DPLR_ERR_ALIAS = 6,       /* output buffer overlaps an input it must not     */
-  S4DPLR_ERR_TOO_LARGE = 7    /* plan exceeds the static scratch of *_noalloc    */
+  S4DPLR_ERR_TOO_LARGE = 7,   /* plan exceeds the static scratch of *_noalloc    */
+  S4DPLR_ERR_ALIGN = 8        /* a device buffer is not 8-byte aligned           */
 } s4dplr_status;
 
 /* Plan flag: diagonal state matrix (S4D).  P and Q are ignored (may be NULL). */

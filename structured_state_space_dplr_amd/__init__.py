@@ -3,7 +3,8 @@
 Argument marshalling only: every step of the computation runs in the HIP
 kernels of ``libs4dplr.so``.  The functions carry the names of the C entry
 points in ``include/s4dplr.h`` (without the ``s4dplr_`` prefix).  Tensors are
-float32, contiguous and on the GPU; complex parameters are [H, N, 2]
+float32, contiguous, on the GPU and 8-byte aligned (a view that starts at an
+odd element is refused with status 8); complex parameters are [H, N, 2]
 (interleaved re, im).  PyTorch supplies device memory and the current stream.
 
 There is no fallback: if the library is missing or fails to load, importing

@@ -31,6 +31,13 @@ s4dplr_status hip_fail(hipError_t e) {
   return S4DPLR_ERR_HIP;
 }
 
+// The kernels read and write complex values and pairs of real samples as
+// 8-byte words, so every device buffer must be 8-byte aligned (NULL passes).
+template <typename... Ts>
+static bool misaligned(const Ts*... ps) {
+  return ((ps != nullptr && (reinterpret_cast<uintptr_t>(ps) & 7u) != 0) || ...);
+}
+
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   if (!a || !b || na == 0 || nb == 0) return false;
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
@@ -123,6 +130,7 @@ const char* s4dplr_status_string(s4dplr_status s) {
     case S4DPLR_ERR_ALIAS: return "an output buffer overlaps an input or the workspace";
     case S4DPLR_ERR_TOO_LARGE:
       return "the plan needs more scratch than the library's static device array holds";
+    case S4DPLR_ERR_ALIGN: return "a device buffer is not 8-byte aligned";
   }
   return "unknown status";
 }
@@ -320,6 +328,7 @@ s4dplr_status s4dplr_kernel_gen(const s4dplr_plan* p, const float* lambda, const
   if (s4dplr_status st = check_ws(ws)) return st;
   const size_t kb = sizeof(float) * (size_t)p->H * p->L;
   if (overlaps(K, kb, ws, p->total)) return S4DPLR_ERR_ALIAS;
+  if (misaligned(lambda, P, Q, B, C, dt, K)) return S4DPLR_ERR_ALIGN;
   unsigned char* w = static_cast<unsigned char*>(ws);
   hipError_t e;
   if ((e = s4::launch_kernel_gen(p, lambda, P, Q, B, C, dt, nullptr, K, w, stream)) != hipSuccess)
@@ -344,6 +353,7 @@ s4dplr_status s4dplr_generating_function(const s4dplr_plan* p, const float* lamb
       overlaps(khat, kb, P, rb) || overlaps(khat, kb, Q, rb) || overlaps(khat, kb, B, cb) ||
       overlaps(khat, kb, C, cb) || overlaps(khat, kb, dt, hb))
     return S4DPLR_ERR_ALIAS;
+  if (misaligned(lambda, P, Q, B, C, dt, khat)) return S4DPLR_ERR_ALIGN;
   hipError_t e = s4::launch_generating_function(p, lambda, P, Q, B, C, dt, khat,
                                                 static_cast<unsigned char*>(ws), stream);
   if (e != hipSuccess) return hip_fail(e);
@@ -359,6 +369,7 @@ s4dplr_status s4dplr_conv_fwd(const s4dplr_plan* p, const float* u, const float*
   const size_t kb = sizeof(float) * (size_t)p->H * p->L;
   if (overlaps(y, ub, u, ub) || overlaps(y, ub, K, kb) || overlaps(y, ub, ws, p->total))
     return S4DPLR_ERR_ALIAS;
+  if (misaligned(u, K, D, y)) return S4DPLR_ERR_ALIGN;
   unsigned char* w = static_cast<unsigned char*>(ws);
   hipError_t e;
   if ((e = s4::launch_spectrum_from_time(p, K, D, w, stream, 0)) != hipSuccess) return hip_fail(e);
@@ -379,6 +390,7 @@ s4dplr_status s4dplr_forward(const s4dplr_plan* p, const float* lambda, const fl
   if (overlaps(y, ub, u, ub) || overlaps(y, ub, ws, p->total)) return S4DPLR_ERR_ALIAS;
   if (K && (overlaps(K, kb, u, ub) || overlaps(K, kb, y, ub) || overlaps(K, kb, ws, p->total)))
     return S4DPLR_ERR_ALIAS;
+  if (misaligned(lambda, P, Q, B, C, dt, D, u, K, y)) return S4DPLR_ERR_ALIGN;
   unsigned char* w = static_cast<unsigned char*>(ws);
   hipError_t e;
   if ((e = s4::launch_kernel_gen(p, lambda, P, Q, B, C, dt, D, K, w, stream)) != hipSuccess)
@@ -398,6 +410,7 @@ s4dplr_status s4dplr_forward_noalloc(const s4dplr_plan* p, const float* lambda, 
   const size_t kb = sizeof(float) * (size_t)p->H * p->L;
   if (overlaps(y, ub, u, ub)) return S4DPLR_ERR_ALIAS;
   if (K && (overlaps(K, kb, u, ub) || overlaps(K, kb, y, ub))) return S4DPLR_ERR_ALIAS;
+  if (misaligned(lambda, P, Q, B, C, dt, D, u, K, y)) return S4DPLR_ERR_ALIGN;
   if (p->fwd_bytes > s4::noalloc_scratch_bytes()) return S4DPLR_ERR_TOO_LARGE;
   unsigned char* w = nullptr;
   hipError_t e = s4::noalloc_scratch(&w);
@@ -419,6 +432,7 @@ s4dplr_status s4dplr_conv_apply(const s4dplr_plan* p, const float* u, float* y, 
   if (s4dplr_status st = check_ws(ws)) return st;
   const size_t ub = sizeof(float) * (size_t)p->batch * p->H * p->L;
   if (overlaps(y, ub, u, ub) || overlaps(y, ub, ws, p->total)) return S4DPLR_ERR_ALIAS;
+  if (misaligned(u, y)) return S4DPLR_ERR_ALIGN;
   hipError_t e = s4::launch_conv(p, u, y, static_cast<unsigned char*>(ws), stream);
   if (e != hipSuccess) return hip_fail(e);
   return S4DPLR_OK;
@@ -432,6 +446,7 @@ s4dplr_status s4dplr_recurrent_prepare(const s4dplr_plan* p, const float* lambda
   if (s4dplr_status st = check_params(p, lambda, P, B, C, dt)) return st;
   if (s4dplr_status st = check_ws(ws)) return st;
   if (p->rank > 1) return S4DPLR_ERR_UNSUPPORTED;   // the O(N) step is rank 1
+  if (misaligned(lambda, P, Q, B, C, dt)) return S4DPLR_ERR_ALIGN;
   hipError_t e = s4::launch_recurrent_prepare(p, lambda, P, Q, B, C, dt,
                                               static_cast<unsigned char*>(ws), stream);
   if (e != hipSuccess) return hip_fail(e);
@@ -452,6 +467,7 @@ s4dplr_status s4dplr_recurrent_scan(const s4dplr_plan* p, const float* D, const 
   if (overlaps(y, ub, u, ub) || overlaps(y, ub, state, sb) || overlaps(y, ub, ws, p->total) ||
       overlaps(state, sb, u, ub) || overlaps(state, sb, ws, p->total))
     return S4DPLR_ERR_ALIAS;
+  if (misaligned(D, u, state, y)) return S4DPLR_ERR_ALIGN;
   if (T == 0) return S4DPLR_OK;
   hipError_t e = s4::launch_recurrent_scan(p, D, u, state, y, T,
                                            static_cast<unsigned char*>(ws), stream);
@@ -479,6 +495,7 @@ s4dplr_status s4dplr_conv_bwd(const s4dplr_plan* p, const float* u, const float*
   if (dD && (overlaps(dD, db, dy, ub) || overlaps(dD, db, u, ub) || overlaps(dD, db, du, ub) ||
              overlaps(dD, db, dK, kb) || overlaps(dD, db, ws, p->total)))
     return S4DPLR_ERR_ALIAS;
+  if (misaligned(u, K, D, dy, du, dK, dD)) return S4DPLR_ERR_ALIGN;
   unsigned char* w = static_cast<unsigned char*>(ws);
   hipError_t e;
   if (du) {
@@ -521,6 +538,8 @@ s4dplr_status s4dplr_kernel_gen_bwd(const s4dplr_plan* p, const float* lambda, c
     for (int j = 0; j < i; ++j)
       if (overlaps(outs[i], outb[i], outs[j], outb[j])) return S4DPLR_ERR_ALIAS;
   }
+  if (misaligned(lambda, P, Q, B, C, dt, dK) || misaligned(dlambda, dP, dQ, dB, dC, ddt))
+    return S4DPLR_ERR_ALIGN;
   hipError_t e = zoh ? s4::launch_vandermonde_bwd(p, lambda, B, C, dt, dK, dlambda, dB, dC, ddt,
                                                   static_cast<unsigned char*>(ws), stream)
                      : s4::launch_kernel_gen_bwd(p, lambda, P, Q, B, C, dt, dK, dlambda, dP, dQ,
@@ -552,6 +571,8 @@ s4dplr_status s4dplr_block_forward(const s4dplr_plan* p, const float* x, const f
   for (int i = 0; i < 11; ++i)
     if (overlaps(out, ub, ins[i], inb[i])) return S4DPLR_ERR_ALIAS;
   if (overlaps(out, ub, ws, p->total) || overlaps(x, ub, ws, p->total)) return S4DPLR_ERR_ALIAS;
+  if (misaligned(x, gamma, beta, lambda, P, Q, B, C, dt, D, W, bias, out))
+    return S4DPLR_ERR_ALIGN;
   unsigned char* w = static_cast<unsigned char*>(ws);
   float* z = reinterpret_cast<float*>(w + p->off_bz);
   float* sv = reinterpret_cast<float*>(w + p->off_bs);

@@ -13,6 +13,7 @@ HEADER = os.path.join(ROOT, "include", "s4dplr.h")
 LIB = os.path.join(ROOT, "structured_state_space_dplr_amd", "libs4dplr.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP, ERR_ALIAS = range(7)
+ERR_TOO_LARGE, ERR_ALIGN = 7, 8
 
 
 @pytest.fixture(scope="module")
@@ -68,8 +69,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.s4dplr_abi_version() == 1
-    for s in range(8):
-        assert len(lib.s4dplr_status_string(s)) > 0
+    for s in range(9):
+        assert lib.s4dplr_status_string(s) != b"unknown status"
     assert lib.s4dplr_status_string(99) == b"unknown status"
 
 
@@ -178,6 +179,36 @@ def test_aliasing_is_rejected_before_launch(lib):
     assert lib.s4dplr_forward(h, 1, 1, None, 1, 1, 1, None, u, y, y, ws, None) == ERR_ALIAS
     assert lib.s4dplr_forward(h, 1, 1, None, 1, 1, 1, None, u, ws, y, ws, None) == ERR_ALIAS
     assert lib.s4dplr_kernel_gen(h, 1, 1, None, 1, 1, 1, ws + 512, ws, None) == ERR_ALIAS
+    lib.s4dplr_plan_destroy(h)
+
+
+def test_misaligned_buffers_are_rejected_before_launch(lib):
+    """Every device buffer is 8-byte aligned (the kernels move float pairs):
+    one buffer off by 4 bytes returns ERR_ALIGN before anything is enqueued.
+    Each call below has exactly one misaligned pointer, so none reaches a
+    launch."""
+    H, N, L, B = 4, 16, 256, 2
+    st, h = _create(lib, H, N, L, B)
+    n = ctypes.c_size_t()
+    lib.s4dplr_plan_workspace_bytes(h, ctypes.byref(n))
+    ws = 1 << 32
+    a = [(1 << 20) * (i + 1) for i in range(16)]       # disjoint, aligned, never read
+    lam, P, Bv, C, dt, D, u, K, y = a[:9]
+    for i in [0, 1, 3, 4, 5, 6]:                        # every buffer but the absent Q
+        args = [lam, P, None, Bv, C, dt, K]
+        args[i] += 4
+        assert lib.s4dplr_kernel_gen(h, *args, ws, None) == ERR_ALIGN
+    for i in range(4):
+        args = [u, K, D, y]
+        args[i] += 4
+        assert lib.s4dplr_conv_fwd(h, *args, ws, None) == ERR_ALIGN
+    fwd = [lam, P, None, Bv, C, dt, D, u, K, y]
+    for i in [0, 1, 3, 4, 5, 6, 7, 8, 9]:
+        args = list(fwd)
+        args[i] += 4
+        assert lib.s4dplr_forward(h, *args, ws, None) == ERR_ALIGN
+    assert lib.s4dplr_conv_apply(h, u + 4, y, ws, None) == ERR_ALIGN
+    assert lib.s4dplr_conv_apply(h, u, y + 4, ws, None) == ERR_ALIGN
     lib.s4dplr_plan_destroy(h)
 
 

@@ -116,3 +116,35 @@ def test_gpu_entry_points_with_and_without_flag(s4, case, monkeypatch):
     s4.forward(plan, v["lam"], v["P"], None, v["B"], v["C"], v["dt"], v["D"], v["u"], K, y, ws)
     torch.cuda.synchronize()
     plan.close()
+
+
+@pytest.mark.gpu
+def test_gpu_misaligned_buffer_is_rejected(s4):
+    """A contiguous float32 view 4 bytes past an 8-byte boundary is refused by
+    the C ABI (status 8, ERR_ALIGN) before anything is enqueued; the same
+    values at an aligned address go through."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    print("case: misaligned u and y views", flush=True)
+    t = {k: v.cuda() for k, v in _params().items()}
+    plan = s4.Plan(3, 8, 64, 2)
+    ws = plan.workspace()
+    K = torch.empty((3, 64), device="cuda")
+    y = torch.empty((2, 3, 64), device="cuda")
+    store = torch.empty(t["u"].numel() + 1, device="cuda")
+    u_odd = store[1:].view(2, 3, 64)
+    u_odd.copy_(t["u"])
+    assert u_odd.is_contiguous() and u_odd.data_ptr() % 8 == 4
+    with pytest.raises(s4.S4DPLRError) as ei:
+        s4.forward(plan, t["lam"], t["P"], None, t["B"], t["C"], t["dt"], t["D"], u_odd, K, y, ws)
+    assert ei.value.status == 8
+    ystore = torch.empty(y.numel() + 1, device="cuda")
+    y_odd = ystore[1:].view(2, 3, 64)
+    with pytest.raises(s4.S4DPLRError) as ei:
+        s4.conv_apply(plan, t["u"], y_odd, ws)
+    assert ei.value.status == 8
+    s4.forward(plan, t["lam"], t["P"], None, t["B"], t["C"], t["dt"], t["D"], t["u"], K, y, ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y).all()
+    plan.close()
